@@ -1,0 +1,156 @@
+"""CPU fp64 oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the package smoke check (``__graft_entry__.smoke``) and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library never
+imports, links or calls it, and it shares no code with the GPU path.
+
+``fwd`` / ``bwd`` wrap ``liboracle.so`` (built from ``gdn_oracle.c`` with gcc):
+the plain token-by-token recurrence of the Day-1 page ("Research Sprint Day 1",
+section "The GDN update": forget, read, write the error, read with the query),
+in double precision, and its reverse mode.  Every input is widened to float64
+exactly as given (bf16 and fp32 values are exactly representable).
+
+Array conventions (numpy):
+  dense  : q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H); cu_seqlens None
+  packed : q, k (Ttot, H, Dk); v (Ttot, H, Dv); g, beta (Ttot, H); cu_seqlens (N+1,)
+  S0, S_final, dS_final, dS0 : (N, H, Dk, Dv), N = B for dense inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# x86-64-v3 (AVX2 + FMA) rather than -march=native: the library is built on one
+# host and may run on another.
+GCC_CMD = ["gcc", "-O3", "-march=x86-64-v3", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", "-Wno-unused-parameter", "-pthread",
+           _SRC, "-o", _LIB, "-lm"]
+
+
+def build() -> str:
+    """Compile liboracle.so in place (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = list(GCC_CMD)
+    cmd[cmd.index(_LIB)] = tmp
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_fwd.argtypes = [I, P, I, I, I, P, P, P, P, P, P, D, P, P, I]
+    lib.oracle_fwd.restype = I
+    lib.oracle_bwd.argtypes = [I, P, I, I, I, P, P, P, P, P, P, D, P, P, P, P, P, P, P, P, I]
+    lib.oracle_bwd.restype = I
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _pack(q, k, v, g, beta, cu_seqlens):
+    """Bring dense (B,T,...) inputs to the packed layout with uniform cu_seqlens."""
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    if cu_seqlens is None:
+        if q.ndim != 4:
+            raise ValueError("dense inputs must be (B, T, H, D)")
+        B, T, H, _ = q.shape
+        cu = np.arange(B + 1, dtype=np.int64) * T
+        shape = (B, T)
+        q, k, v = (x.reshape(B * T, H, x.shape[-1]) for x in (q, k, v))
+        g, beta = (x.reshape(B * T, H) for x in (g, beta))
+    else:
+        if q.ndim == 4 and q.shape[0] == 1:  # (1, Ttot, H, D): one packed row
+            q, k, v = (x[0] for x in (q, k, v))
+            g, beta = (x.reshape(x.shape[-2:]) for x in (g, beta))
+        if q.ndim != 3:
+            raise ValueError("packed inputs must be (Ttot, H, D) or (1, Ttot, H, D)")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        shape = (q.shape[0],)
+        if cu[0] != 0 or cu[-1] != q.shape[0] or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at Ttot")
+    return q, k, v, g, beta, cu, shape
+
+
+def fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0, nthreads=None):
+    """Return (o, S_final) in float64; o has v's leading shape."""
+    lib = _load()
+    q, k, v, g, beta, cu, shape = _pack(q, k, v, g, beta, cu_seqlens)
+    N = len(cu) - 1
+    H, Dk = q.shape[1], q.shape[2]
+    Dv = v.shape[2]
+    S0 = _f64(S0)
+    if S0 is not None and S0.shape != (N, H, Dk, Dv):
+        raise ValueError(f"S0 must be {(N, H, Dk, Dv)}")
+    o = np.zeros((q.shape[0], H, Dv))
+    Sf = np.zeros((N, H, Dk, Dv))
+    rc = lib.oracle_fwd(N, _ptr(cu), H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                        _ptr(beta), _ptr(S0), float(scale), _ptr(o), _ptr(Sf),
+                        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_fwd failed with code {rc}")
+    return o.reshape(shape + (H, Dv)), Sf
+
+
+def bwd(q, k, v, g, beta, dO, cu_seqlens=None, S0=None, dS_final=None, scale=1.0,
+        nthreads=None):
+    """Return dict dq, dk, dv, dg, dbeta, dS0 (float64) of L = <o, dO> + <S_final, dS_final>."""
+    lib = _load()
+    q, k, v, g, beta, cu, shape = _pack(q, k, v, g, beta, cu_seqlens)
+    N = len(cu) - 1
+    H, Dk = q.shape[1], q.shape[2]
+    Dv = v.shape[2]
+    dO = _f64(dO).reshape(q.shape[0], H, Dv)
+    S0 = _f64(S0)
+    dSf = _f64(dS_final)
+    out = {
+        "dq": np.zeros((q.shape[0], H, Dk)),
+        "dk": np.zeros((q.shape[0], H, Dk)),
+        "dv": np.zeros((q.shape[0], H, Dv)),
+        "dg": np.zeros((q.shape[0], H)),
+        "dbeta": np.zeros((q.shape[0], H)),
+        "dS0": np.zeros((N, H, Dk, Dv)),
+    }
+    rc = lib.oracle_bwd(N, _ptr(cu), H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                        _ptr(beta), _ptr(S0), float(scale), _ptr(dO), _ptr(dSf),
+                        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                        _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd failed with code {rc}")
+    for name in ("dq", "dk", "dv"):
+        out[name] = out[name].reshape(shape + out[name].shape[1:])
+    for name in ("dg", "dbeta"):
+        out[name] = out[name].reshape(shape + (H,))
+    return out
