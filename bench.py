@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated-delta-rule forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train_bf16]
+
+A step is one gdn_chunk_fwd call (every stage of the forward hot path: cumsum of
+g, K K^T and the triangular solve, the WY errors, the state pass, the causal
+output and the final state) over one batch of seeded synthetic input already
+resident in HBM.  Four independent input/output sets are rotated so that the
+256 MB on-package cache cannot hold the working set between steps.  Prints one
+JSON line.
+
+Roofline (the forward pass is HBM-bound at this shape: ~134 algorithmic FLOP per
+byte, below MI355X's bf16-MFMA/HBM ridge):
+  algorithmic bytes per launch = token-heads * ((2 Dk + Dv) + Dv) * s_io + 8
+                                 + N H Dk Dv 4 (final state) [+ the same for S0]
+  achieved = those bytes / mean kernel duration (HIP events on the launch stream).
+The CPU baseline times the fp64 oracle on the host cores (bench-only use).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunked GDN fwd tokens/s + % MFMA/HBM roofline (B4 H8 T4096 d128 bf16)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CHUNK = 64
+
+
+def alg_bytes(w, s_io: int) -> int:
+    th = w.B * w.T * w.H
+    per_th = (2 * w.Dk + w.Dv) * s_io + w.Dv * s_io + 8
+    state = w.num_seqs * w.H * w.Dk * w.Dv * 4
+    return th * per_th + state * (2 if w.s0_std is not None else 1)
+
+
+def alg_flops(w) -> float:
+    th = w.B * w.T * w.H
+    per_th = 6 * w.Dk * w.Dv + 3 * CHUNK * w.Dk + 2 * CHUNK * w.Dv + CHUNK * CHUNK / 3
+    return th * per_th
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="train_bf16")
+    ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(d, w, budget_s: float):
+    """Time the fp64 oracle on the host on the same workload (whole passes,
+    repeated until about `budget_s` seconds have passed, at most 20)."""
+    import oracle
+
+    threads = oracle.default_threads()
+    reps, t_total = 0, 0.0
+    while reps < 20 and (reps == 0 or t_total < budget_s):
+        t0 = time.perf_counter()
+        oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                   S0=d["S0"], scale=d["scale"], nthreads=threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    tokens = w.B * w.T * reps
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full forward pass(es) of workload {w.name} "
+                      f"({w.B * w.T} tokens x {w.H} heads each), fp64 C oracle, "
+                      f"{t_total:.2f} s total"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_chunked_gdn_amd as gdn
+    from gated_deltanet_chunked_gdn_amd.workloads import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    d = generate(w)
+    io = torch.bfloat16 if w.io == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name} generated", file=sys.stderr, flush=True)
+
+    sets = []
+    for s in range(args.sets):
+        # independent copies (identical values) at distinct addresses
+        t = {key: torch.from_numpy(d[key]).to(dev).to(io) for key in ("q", "k", "v")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+        t["S0"] = None if d["S0"] is None else torch.from_numpy(d["S0"]).to(dev)
+        t["o"] = torch.empty_like(t["v"])
+        t["Sf"] = torch.empty((w.num_seqs, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+        sets.append(t)
+    seqs = None if d["cu_seqlens"] is None else gdn.SeqLens(d["cu_seqlens"], dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"], cu_seqlens=seqs,
+                      scale=d["scale"], out=t["o"], final_state_out=t["Sf"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per launch
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    s_io = 2 if w.io == "bf16" else 4
+    nbytes = alg_bytes(w, s_io)
+    flops = alg_flops(w)
+    k_mean = float(kt.mean())
+    achieved_gbs = nbytes / k_mean / 1e9
+    tokens = w.B * w.T
+    result = {
+        "metric": METRIC,
+        "value": tokens * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io,
+        "data": "synthetic (seeded numpy generator; random inputs of the named shape)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv,
+                   "chunk": CHUNK, "io": w.io, "state": "fp32", "num_segments": 1,
+                   "packed": d["cu_seqlens"] is not None},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": nbytes,
+                     "kernel_ms_mean": k_mean * 1e3,
+                     "kernel_ms_p10": float(np.percentile(kt, 10)) * 1e3,
+                     "kernel_ms_p90": float(np.percentile(kt, 90)) * 1e3},
+        "extras": {"alg_tflops": flops / k_mean / 1e12,
+                   "alg_flops_per_launch": flops,
+                   "mfma_bf16_frac_of_peak": flops / k_mean / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                   "recurrence_tflops_6DkDv": w.B * w.T * w.H * 6 * w.Dk * w.Dv / k_mean / 1e12,
+                   "token_heads_per_s": w.B * w.T * w.H / k_mean},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,8 @@
+"""Chunked gated delta rule (Gated DeltaNet) for AMD Instinct MI355X (gfx950).
+
+The computation lives in libgdn.so (HIP kernels behind the C ABI of
+include/gdn.h); this package is its Python binding plus the seeded synthetic
+input generators.
+"""
+from .ops import SeqLens, chunk_bwd, chunk_fwd, make_problem, recurrent_ref  # noqa: F401
+from ._native import GdnError, GdnLibraryMissing  # noqa: F401

@@ -1,0 +1,238 @@
+// C ABI of libgdn: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before the first launch (see include/gdn.h).
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+};
+
+Range span(const void* p, size_t bytes) {
+  Range r;
+  if (p && bytes) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + bytes;
+  }
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Checked {
+  int64_t tokens = 0;    // B * T
+  int64_t max_len = 0;   // longest sequence
+  int32_t N = 0;
+  bool bf16 = false;
+  size_t io = 4;         // bytes per io element
+};
+
+enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd };
+
+gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->io_dtype != GDN_FP32 && p->io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (p->B < 0 || p->T < 0 || p->H <= 0 || p->Dk <= 0 || p->Dv <= 0 || p->num_seqs < 0)
+    return GDN_ERR_SHAPE;
+  if (p->Dk != 64 && p->Dk != 128) return GDN_ERR_UNSUPPORTED;
+  if (p->Dv % 16 != 0 || p->Dv < 16 || p->Dv > 256) return GDN_ERR_UNSUPPORTED;
+  if (p->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  const bool chunked = kind == Kind::ChunkFwd || kind == Kind::ChunkBwd;
+  if (chunked) {
+    const int G = p->num_segments;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
+    if (G != 1) return GDN_ERR_UNSUPPORTED;  // segment split not built yet
+    if (kind == Kind::ChunkBwd) return GDN_ERR_UNSUPPORTED;  // chunked backward not built yet
+    if (p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
+  }
+  if (kind == Kind::RecBwd && static_cast<size_t>(2) * p->Dk * (p->Dv + 1) * 4 +
+                                      (2 * gdn::kRecBlock * p->Dk + 2 * gdn::kRecBlock + 8) * 4 >
+                                  160 * 1024)
+    return GDN_ERR_UNSUPPORTED;
+
+  const bool packed = p->cu_seqlens_host || p->cu_seqlens_dev;
+  if (packed) {
+    if (!p->cu_seqlens_host || !p->cu_seqlens_dev) return GDN_ERR_NULL;
+    if (p->B != 1) return GDN_ERR_SHAPE;
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0 || cu[p->num_seqs] != p->T) return GDN_ERR_SEQLENS;
+    int64_t mx = 0;
+    for (int32_t n = 0; n < p->num_seqs; ++n) {
+      if (cu[n + 1] < cu[n]) return GDN_ERR_SEQLENS;
+      mx = std::max<int64_t>(mx, cu[n + 1] - cu[n]);
+    }
+    c->max_len = mx;
+  } else {
+    if (p->num_seqs != p->B) return GDN_ERR_SHAPE;
+    c->max_len = p->T;
+  }
+  if (p->num_seqs > 65535) return GDN_ERR_UNSUPPORTED;
+  c->tokens = static_cast<int64_t>(p->B) * p->T;
+  c->N = p->num_seqs;
+  c->bf16 = p->io_dtype == GDN_BF16;
+  c->io = c->bf16 ? 2 : 4;
+  return GDN_OK;
+}
+
+size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
+  if (kind == Kind::RecBwd)
+    return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
+  return 0;
+}
+
+struct Tensor {
+  const void* ptr;
+  size_t bytes;
+  size_t align;
+  bool required;
+};
+
+// Checks NULL / alignment of every tensor and that no output overlaps another
+// tensor.  `ins` are read-only, `outs` are written.
+gdn_status check_tensors(const std::vector<Tensor>& ins, const std::vector<Tensor>& outs) {
+  for (const auto* set : {&ins, &outs})
+    for (const Tensor& t : *set) {
+      if (!t.ptr) {
+        if (t.required && t.bytes) return GDN_ERR_NULL;
+        continue;
+      }
+      if (!aligned(t.ptr, t.align)) return GDN_ERR_ALIGN;
+    }
+  for (size_t i = 0; i < outs.size(); ++i) {
+    const Range ro = span(outs[i].ptr, outs[i].bytes);
+    for (const Tensor& t : ins)
+      if (overlap(ro, span(t.ptr, t.bytes))) return GDN_ERR_ALIAS;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(ro, span(outs[j].ptr, outs[j].bytes))) return GDN_ERR_ALIAS;
+  }
+  return GDN_OK;
+}
+
+gdn::SeqInfo seq_info(const gdn_problem* p) { return gdn::SeqInfo{p->cu_seqlens_dev, p->T}; }
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(int32_t s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "required pointer is NULL";
+    case GDN_ERR_SHAPE: return "size out of range or inconsistent";
+    case GDN_ERR_DTYPE: return "io_dtype is not a gdn_dtype";
+    case GDN_ERR_UNSUPPORTED: return "unsupported Dk, Dv, chunk, num_segments or pass";
+    case GDN_ERR_WORKSPACE: return "workspace NULL or too small";
+    case GDN_ERR_ALIAS: return "an output overlaps another tensor";
+    case GDN_ERR_HIP: return "HIP launch failed";
+    case GDN_ERR_SEQLENS: return "cu_seqlens not a non-decreasing 0..T sequence";
+    case GDN_ERR_ALIGN: return "tensor pointer misaligned";
+    default: return "unknown status";
+  }
+}
+
+gdn_status gdn_workspace_size(const gdn_problem* p, int32_t pass, size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  Kind kind;
+  switch (pass) {
+    case GDN_PASS_CHUNK_FWD: kind = Kind::ChunkFwd; break;
+    case GDN_PASS_CHUNK_BWD: kind = Kind::ChunkBwd; break;
+    case GDN_PASS_RECURRENT_FWD: kind = Kind::RecFwd; break;
+    case GDN_PASS_RECURRENT_BWD: kind = Kind::RecBwd; break;
+    default: return GDN_ERR_UNSUPPORTED;
+  }
+  Checked c;
+  const gdn_status st = check_problem(p, kind, &c);
+  if (st != GDN_OK) return st;
+  *bytes = workspace_bytes(p, kind, c);
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* S0, void* o,
+                         float* S_final, void* workspace, size_t ws_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::ChunkFwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false},
+                      {workspace, ws_bytes, 16, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::ChunkFwd, c);
+  if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  gdn::FwdParams fp{q, k, v, g, beta, S0, o, S_final, seq_info(p), p->H, p->Dv, p->scale};
+  return hip_status(gdn::launch_chunk_fwd(fp, c.N, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* S0, const void* dO,
+                         const float* dS_final, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, float* dS0, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  Checked c;
+  return check_problem(p, Kind::ChunkBwd, &c);
+}
+
+gdn_status gdn_recurrent_ref(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* S0, void* o,
+                             float* S_final, const void* dO, const float* dS_final, void* dq,
+                             void* dk, void* dv, float* dg, float* dbeta, float* dS0,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  const bool bwd = dO != nullptr;
+  const Kind kind = bwd ? Kind::RecBwd : Kind::RecFwd;
+  Checked c;
+  gdn_status st = check_problem(p, kind, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  std::vector<Tensor> ins = {{q, nk * c.io, 16, true},   {k, nk * c.io, 16, true},
+                             {v, nv * c.io, 16, true},   {g, ng * 4, 4, true},
+                             {beta, ng * 4, 4, true},    {S0, ns * 4, 4, false},
+                             {workspace, ws_bytes, 16, false}};
+  std::vector<Tensor> outs = {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false}};
+  if (bwd) {
+    ins.push_back({dO, nv * c.io, 16, true});
+    ins.push_back({dS_final, ns * 4, 4, false});
+    outs.push_back({dq, nk * c.io, 16, true});
+    outs.push_back({dk, nk * c.io, 16, true});
+    outs.push_back({dv, nv * c.io, 16, true});
+    outs.push_back({dg, ng * 4, 4, true});
+    outs.push_back({dbeta, ng * 4, 4, true});
+    outs.push_back({dS0, ns * 4, 4, false});
+  }
+  st = check_tensors(ins, outs);
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, kind, c);
+  if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  gdn::RecParams rp{};
+  rp.q = q; rp.k = k; rp.v = v; rp.g = g; rp.beta = beta; rp.S0 = S0; rp.o = o;
+  rp.S_final = S_final; rp.dO = dO; rp.dS_final = dS_final; rp.dq = dq; rp.dk = dk; rp.dv = dv;
+  rp.dg = dg; rp.dbeta = dbeta; rp.dS0 = dS0;
+  rp.ws = static_cast<float*>(workspace);
+  rp.ckpt_stride = ((c.max_len + gdn::kRecBlock - 1) / gdn::kRecBlock) * p->Dk * p->Dv;
+  rp.seq = seq_info(p);
+  rp.N = c.N; rp.H = p->H; rp.Dv = p->Dv; rp.scale = p->scale;
+  return hip_status(gdn::launch_recurrent(rp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

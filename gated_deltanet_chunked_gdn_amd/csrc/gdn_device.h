@@ -1,0 +1,125 @@
+// Device-side building blocks for the gfx950 kernels of libgdn: number
+// conversions, MFMA operand fragments and 16x16 tile products.
+//
+// MFMA conventions used throughout (CDNA3/CDNA4 matrix-core register layout for
+// the 16x16 output shapes):
+//   * the 16x16 fp32 accumulator of a wave64 holds C[4*(lane/16) + r][lane%16]
+//     in element r (r = 0..3) of lane `lane`;
+//   * an A operand fragment of v_mfma_f32_16x16x32_bf16 is A[lane%16][8*(lane/16) + 0..7]
+//     and a B fragment is B[8*(lane/16) + 0..7][lane%16];
+//   * v_mfma_f32_16x16x4_f32 takes A[lane%16][lane/16] and B[lane/16][lane%16].
+// Both operands are therefore read the same way from LDS when the A operand is
+// stored row-major (M x K) and the B operand is stored transposed (N x K), the
+// reduction index contiguous: `frag(buf, ld, lane, k0)` reads row lane%16 from
+// column k0 + (lane/16) * KPL on.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ----------------------------------------------------------------------------------
+// Operand policies.  `elem` is what operand tiles hold in LDS.
+// ----------------------------------------------------------------------------------
+struct OpBf16 {
+  using elem = uint16_t;
+  static constexpr int KSTEP = 32;  // reduction depth of one MFMA
+  static constexpr int KPL = 8;     // reduction elements per lane
+  static __device__ __forceinline__ elem cvt(float x) { return f32_to_bf16(x); }
+  static __device__ __forceinline__ float widen(elem x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ bf16x8_t frag(const elem* buf, int ld, int lane, int k0) {
+    const uint4 u = *reinterpret_cast<const uint4*>(buf + (lane & 15) * ld + k0 + (lane >> 4) * 8);
+    return __builtin_bit_cast(bf16x8_t, u);
+  }
+  static __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct OpF32 {
+  using elem = float;
+  static constexpr int KSTEP = 4;
+  static constexpr int KPL = 1;
+  static __device__ __forceinline__ elem cvt(float x) { return x; }
+  static __device__ __forceinline__ float widen(elem x) { return x; }
+  static __device__ __forceinline__ float frag(const elem* buf, int ld, int lane, int k0) {
+    return buf[(lane & 15) * ld + k0 + (lane >> 4)];
+  }
+  static __device__ __forceinline__ f32x4_t mma(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// acc += A(16 x K) * B(K x 16): A row-major at `a` (leading dim lda), B stored
+// transposed (16 x K) at `bt` (leading dim ldb); K a multiple of Op::KSTEP.
+template <typename Op, int K>
+__device__ __forceinline__ void tile_mma(f32x4_t& acc, const typename Op::elem* a, int lda,
+                                         const typename Op::elem* bt, int ldb, int lane) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Op::KSTEP)
+    acc = Op::mma(Op::frag(a, lda, lane, k0), Op::frag(bt, ldb, lane, k0), acc);
+}
+
+// fp32 tile product with a row-major B (used by the triangular solve):
+// acc += A(16 x K) * B(K x 16), both fp32 row-major.
+template <int K>
+__device__ __forceinline__ void tile_mma_f32_rowmajor(f32x4_t& acc, const float* a, int lda,
+                                                      const float* b, int ldb, int lane) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(lane & 15) * lda + k0 + (lane >> 4)],
+                                               b[(k0 + (lane >> 4)) * ldb + (lane & 15)], acc,
+                                               0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Load/store of io-dtype values.
+template <typename IO>
+struct IoT;
+template <>
+struct IoT<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+template <>
+struct IoT<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float x) { *p = x; }
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+}  // namespace gdn

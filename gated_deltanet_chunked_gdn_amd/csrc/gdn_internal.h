@@ -1,0 +1,62 @@
+// Host-visible kernel parameter blocks and launchers of libgdn (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Sequence n covers packed rows [bos, bos + len): from cu (device) when given,
+// else the dense batch row n * T .. n * T + T.
+struct SeqInfo {
+  const int32_t* cu;  // device offsets or nullptr
+  int32_t T;          // dense sequence length (unused when cu != nullptr)
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* S0;  // [N, H, Dk, Dv] or nullptr
+  void* o;
+  float* S_final;   // [N, H, Dk, Dv] or nullptr
+  SeqInfo seq;
+  int32_t H, Dv;
+  float scale;
+};
+
+struct RecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* S0;
+  void* o;
+  float* S_final;
+  const void* dO;        // nullptr: forward only
+  const float* dS_final;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dS0;
+  float* ws;             // workspace (backward: checkpoints and replay buffers)
+  int64_t ckpt_stride;   // floats of checkpoints per (sequence, head)
+  SeqInfo seq;
+  int32_t N, H, Dv;
+  float scale;
+};
+
+constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backward
+
+// Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
+// `bf16` selects the io dtype.
+hipError_t launch_chunk_fwd(const FwdParams& p, int N, int Dk, bool bf16, hipStream_t s);
+hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
+size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
+
+}  // namespace gdn

@@ -1,0 +1,207 @@
+"""Python entry points over libgdn's C ABI (include/gdn.h).
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in libgdn's HIP kernels.  There is no CPU fallback: without the
+built library every call raises ``GdnLibraryMissing``.
+
+    o, S_final = chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale=1.0)
+    grads      = chunk_bwd(q, k, v, g, beta, dO, S0=..., dS_final=None)
+    out        = recurrent_ref(q, k, v, g, beta, ..., dO=None)
+
+Shapes: q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H) fp32;
+S0 / S_final (N, H, Dk, Dv) fp32.  q, k, v share the io dtype (bf16 or fp32).
+Packed sequences: B == 1 and ``cu_seqlens`` the N + 1 offsets.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _native as nat
+
+_IO = {torch.bfloat16: nat.GDN_BF16, torch.float32: nat.GDN_FP32}
+
+
+class SeqLens:
+    """Packed-sequence offsets held twice: host int32 (validated by the library
+    before launching) and a device copy (read by the kernels)."""
+
+    def __init__(self, offsets, device):
+        host = np.ascontiguousarray(np.asarray(
+            offsets.cpu().numpy() if isinstance(offsets, torch.Tensor) else offsets,
+            dtype=np.int32))
+        if host.ndim != 1 or host.size < 1:
+            raise ValueError("cu_seqlens must be a 1-D sequence of N + 1 offsets")
+        self.host = host
+        self.dev = torch.from_numpy(host.copy()).to(device)
+        self.num_seqs = host.size - 1
+
+    @property
+    def max_len(self) -> int:
+        return int(np.max(np.diff(self.host))) if self.num_seqs else 0
+
+
+def _seqlens(cu_seqlens, device) -> Optional[SeqLens]:
+    if cu_seqlens is None or isinstance(cu_seqlens, SeqLens):
+        return cu_seqlens
+    return SeqLens(cu_seqlens, device)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_inputs(q, k, v, g, beta):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _IO or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one io dtype: bfloat16 or float32")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be (B, T, H, Dk) and v (B, T, H, Dv)")
+    if g.shape != q.shape[:3] or beta.shape != q.shape[:3]:
+        raise ValueError("g and beta must be (B, T, H)")
+
+
+def _fp32_state(t, N, H, Dk, Dv, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (N, H, Dk, Dv):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {(N, H, Dk, Dv)}")
+    return t
+
+
+def make_problem(q, v, seqs: Optional[SeqLens], scale: float, num_segments: int = 1) -> nat.Problem:
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    p = nat.Problem()
+    p.B, p.T, p.H, p.Dk, p.Dv = B, T, H, Dk, Dv
+    if seqs is None:
+        p.num_seqs = B
+        p.cu_seqlens_host = None
+        p.cu_seqlens_dev = None
+    else:
+        p.num_seqs = seqs.num_seqs
+        p.cu_seqlens_host = seqs.host.ctypes.data
+        p.cu_seqlens_dev = seqs.dev.data_ptr()
+    p.io_dtype = _IO[q.dtype]
+    p.scale = float(scale)
+    p.chunk = 64
+    p.num_segments = int(num_segments)
+    return p
+
+
+def _workspace(problem, pass_, device):
+    n = nat.workspace_size(problem, pass_)
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
+              num_segments: int = 1, output_final_state: bool = True, out=None,
+              final_state_out=None, workspace=None):
+    """Chunked forward pass.  Returns (o, S_final or None).
+
+    ``out`` / ``final_state_out`` / ``workspace`` may supply preallocated
+    buffers (o shaped like v; S_final (N, H, Dk, Dv) fp32; a uint8 device
+    tensor of at least the size the library asks for)."""
+    lib = nat.load()
+    _check_inputs(q, k, v, g, beta)
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, num_segments)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    if out is None:
+        o = torch.empty_like(v)
+    else:
+        if out.dtype != v.dtype or out.shape != v.shape or not out.is_contiguous():
+            raise ValueError("out must be contiguous, shaped and typed like v")
+        o = out
+    if final_state_out is not None:
+        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out")
+    elif output_final_state:
+        Sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    else:
+        Sf = None
+    if workspace is not None:
+        ws, nws = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws, nws = _workspace(prob, nat.GDN_PASS_CHUNK_FWD, q.device)
+    st = lib.gdn_chunk_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(S0), _ptr(o), _ptr(Sf), _ptr(ws), nws, _stream(q.device))
+    nat.check(st, "gdn_chunk_fwd")
+    return o, Sf
+
+
+def chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,
+              scale: float = 1.0, want_dS0: bool = True):
+    """Chunked backward pass.  Returns dict dq, dk, dv, dg, dbeta, dS0."""
+    lib = nat.load()
+    _check_inputs(q, k, v, g, beta)
+    if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
+        raise ValueError("dO must be contiguous, shaped and typed like v")
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final")
+    out = {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+        "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+        "dS0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_dS0 else None,
+    }
+    ws, nws = _workspace(prob, nat.GDN_PASS_CHUNK_BWD, q.device)
+    st = lib.gdn_chunk_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                           _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                           _ptr(ws), nws, _stream(q.device))
+    nat.check(st, "gdn_chunk_bwd")
+    return out
+
+
+def recurrent_ref(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0, dO=None,
+                  dS_final=None, want_dS0: bool = True):
+    """fp32 token-loop reference on the GPU.  Returns dict o, S_final (+ gradients if dO)."""
+    lib = nat.load()
+    _check_inputs(q, k, v, g, beta)
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    out = {"o": torch.empty_like(v),
+           "S_final": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)}
+    grads = dict.fromkeys(("dq", "dk", "dv", "dg", "dbeta", "dS0"))
+    pass_ = nat.GDN_PASS_RECURRENT_FWD
+    if dO is not None:
+        if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
+            raise ValueError("dO must be contiguous, shaped and typed like v")
+        dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final")
+        grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+                 "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+                 "dS0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+                 if want_dS0 else None}
+        pass_ = nat.GDN_PASS_RECURRENT_BWD
+    ws, nws = _workspace(prob, pass_, q.device)
+    st = lib.gdn_recurrent_ref(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(S0), _ptr(out["o"]), _ptr(out["S_final"]), _ptr(dO),
+                               _ptr(dS_final), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                               _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]),
+                               _ptr(grads["dS0"]), _ptr(ws), nws, _stream(q.device))
+    nat.check(st, "gdn_recurrent_ref")
+    if dO is not None:
+        out.update(grads)
+    return out

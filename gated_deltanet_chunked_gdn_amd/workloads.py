@@ -35,9 +35,14 @@ import numpy as np
 def round_bf16(x) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # add 0x7FFF plus the lowest kept bit, then clear the 16 dropped bits; the
+    # sum cannot wrap for finite inputs (it carries into the exponent at most)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 def _normalize(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,169 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the chunked gated delta rule (Gated DeltaNet) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Per sequence and head, with a d_k x d_v state S (initial
+ * value S0, or zero) and for every token t in order:
+ *
+ *     S <- exp(g_t) * S                         forget
+ *     e  = beta_t * (v_t - S^T k_t)             error of what is stored under k_t
+ *     S <- S + k_t e^T                          write
+ *     o_t = scale * S^T q_t                     read with the query, after the write
+ *
+ * This is the update of "Research Sprint Day 1 - Verifying the
+ * flash-linear-attention Gated DeltaNet kernel on GB10", section "The GDN update",
+ * with alpha = exp(g) kept in log space as on "Research Sprint Day 2 - Rooflines",
+ * section "Building some intuition" (gates, step 5).  Its closed form on the
+ * Day-2 page is S'_t = S'_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ * with S' = S^T.  `scale` is the query scale that the cuLA issue #126 page
+ * ("Minimal public reproduction") passes to its kernels as a separate argument.
+ *
+ * gdn_chunk_fwd / gdn_chunk_bwd evaluate this in chunks of 64 tokens (the
+ * "chunk_gated_delta_rule" of the Day-1 page, "Conclusion"; intermediates of the
+ * fla issue #1550 page, "Intermediate rounding diagnosis").  gdn_recurrent_ref
+ * runs the token loop itself in IEEE fp32 (the "fused recurrent operator" of the
+ * fla issue #1550 page, "Reproduction and evidence").
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Tensors are dense, row-major, last dimension contiguous, on the device:
+ *      q, k              [B, T, H, Dk]     io dtype
+ *      v, o, dO, dv      [B, T, H, Dv]     io dtype
+ *      dq, dk            [B, T, H, Dk]     io dtype
+ *      g, beta, dg, dbeta[B, T, H]         fp32
+ *      S0, S_final, dS_final, dS0
+ *                        [N, H, Dk, Dv]    fp32  (N = number of sequences)
+ *  - Packed variable-length sequences (fla issue #1550 page: sequence lengths
+ *    [5120, 5120] in one row): B must be 1 and sequence n is tokens
+ *    [cu[n], cu[n+1]) of the row.  Chunks restart at every sequence start; each
+ *    sequence has its own S0 / S_final.  The caller passes the offsets twice:
+ *    on the host (validated before any launch) and as a device copy holding the
+ *    same values (read by the kernels).  Dense input: both NULL, N = B.
+ *  - The value domain is documented, not checked: g <= 0 (alpha = exp(g) in
+ *    (0, 1]), beta in (0, 2) (Day-2 page: beta = 2 sigmoid(.) under
+ *    allow_neg_eigval), k rows L2-normalised.  NaN and Inf propagate.
+ *  - Ownership: the caller allocates every buffer, including the workspace
+ *    sized by gdn_workspace_size.  The library allocates nothing, keeps no state
+ *    between calls and never synchronises the host.
+ *  - Execution: asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Outputs are always overwritten, never accumulated.
+ *  - Errors: every shape, pointer, dtype, support and workspace check happens on
+ *    the host before the first launch, so an error leaves every output untouched.
+ *    GDN_ERR_HIP reports a failed launch (hipGetLastError).  There is no silent
+ *    fallback: an unsupported case is an error.
+ *  - Precision (explicit, never switched by environment variables):
+ *      io dtype GDN_FP32: every product in IEEE fp32 (fp32 MFMA), fp32 state.
+ *      io dtype GDN_BF16: bf16 MFMA operands with fp32 accumulation; the state,
+ *        the decay factors, the triangular solve and all gradients' reductions
+ *        are fp32; outputs are rounded to bf16 (round to nearest even) once.
+ *  - Supported: Dk in {64, 128} (io GDN_FP32: chunked passes Dk == 64 only);
+ *    Dv a multiple of 16 with 16 <= Dv <= 256; chunk == 64; num_segments in
+ *    {1, 2, 4, 8, 16}; N <= 65535.  The recurrent backward needs
+ *    2 * Dk * (Dv + 1) * 4 bytes of LDS and so Dk * Dv <= 128 * 128.
+ *  - All entry points are thread-safe.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                               */
+  GDN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent                   */
+  GDN_ERR_DTYPE = 3,       /* io_dtype is not a gdn_dtype                              */
+  GDN_ERR_UNSUPPORTED = 4, /* valid but not built: Dk, Dv, chunk or num_segments       */
+  GDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than gdn_workspace_size        */
+  GDN_ERR_ALIAS = 6,       /* an output overlaps an input or another output            */
+  GDN_ERR_HIP = 7,         /* a HIP launch failed                                      */
+  GDN_ERR_SEQLENS = 8,     /* cu_seqlens not 0 = cu[0] <= cu[1] <= ... <= cu[N] = T     */
+  GDN_ERR_ALIGN = 9        /* q, k, v, o, dO, dq, dk, dv not 16-byte aligned, or an fp32
+                              tensor not 4-byte aligned                                 */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_FP32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_pass {
+  GDN_PASS_CHUNK_FWD = 0,
+  GDN_PASS_CHUNK_BWD = 1,
+  GDN_PASS_RECURRENT_FWD = 2,
+  GDN_PASS_RECURRENT_BWD = 3
+} gdn_pass;
+
+typedef struct gdn_problem {
+  int32_t B, T, H, Dk, Dv;         /* sizes; T may be 0                                     */
+  int32_t num_seqs;                /* N: == B for dense input, else len(cu_seqlens) - 1     */
+  const int32_t* cu_seqlens_host;  /* host, N + 1 offsets, or NULL (dense)                  */
+  const int32_t* cu_seqlens_dev;   /* device copy of the same N + 1 values, or NULL         */
+  int32_t io_dtype;                /* gdn_dtype of q, k, v, o, dO, dq, dk, dv               */
+  float scale;                     /* output scale: o_t = scale * S_t^T q_t                 */
+  int32_t chunk;                   /* tokens per chunk; must be 64                          */
+  int32_t num_segments;            /* 1: serial over chunks; G > 1: segment split (fwd)     */
+} gdn_problem;
+
+/* Version of this ABI (GDN_ABI_VERSION). */
+int32_t gdn_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* gdn_status_str(int32_t status);
+
+/* Bytes of device workspace that `pass` needs for `problem` (0 is possible; the
+ * workspace pointer may then be NULL).  Validates the problem like the entry
+ * point it sizes for. */
+gdn_status gdn_workspace_size(const gdn_problem* problem, int32_t pass, size_t* bytes);
+
+/* Forward pass of the chunked gated delta rule.
+ *   in : q, k, v, g, beta; S0 (NULL = zero initial state)
+ *   out: o; S_final (NULL = not wanted)
+ * Chunk algebra per (sequence, head), chunk of n <= 64 tokens, state S_c before it:
+ *   gamma = cumsum(g) within the chunk; D_ij = exp(gamma_i - gamma_j) (j <= i)
+ *   A = strict_lower(diag(beta) (K K^T) o D); T = (I + A)^-1 (unit lower triangular)
+ *   E = T diag(beta) (V - diag(exp(gamma)) K S_c)      (the errors e_t of the chunk)
+ *   O = scale (diag(exp(gamma)) Q S_c + lower_incl(Q K^T o D) E)
+ *   S_{c+1} = exp(gamma_n) S_c + (diag(exp(gamma_n - gamma)) K)^T E
+ * num_segments = G > 1 splits every sequence into G runs of whole chunks whose
+ * affine state maps S -> M S + b are formed in fp32 and composed (cuLA issue
+ * #126 page, "Summary" and "Hypothesis": segment affine transforms and carries).
+ * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...). */
+gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, const float* S0,
+                         void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Backward pass of the chunked gated delta rule: gradients of
+ *   L = <o, dO> + <S_final, dS_final>
+ * with respect to q, k, v, g, beta and S0 (the six gradients of the Day-1 page's
+ * "Results" tables plus the initial-state gradient).
+ *   in : q, k, v, g, beta, S0 (NULL = zero), dO, dS_final (NULL = zero)
+ *   out: dq, dk, dv (io dtype), dg, dbeta (fp32), dS0 (fp32; NULL = not wanted)
+ * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD. */
+gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, const float* S0,
+                         const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
+                         float* dg, float* dbeta, float* dS0, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Token-by-token recurrence in IEEE fp32 on the GPU: the full-length second
+ * reference (not the fast path).  Forward always (o, S_final as gdn_chunk_fwd).
+ * If dO is non-NULL it also runs the token-level reverse mode and writes dq, dk,
+ * dv, dg, dbeta (all required then) and dS0 (optional), like gdn_chunk_bwd.
+ * num_segments is ignored.  Workspace: GDN_PASS_RECURRENT_FWD when dO == NULL,
+ * else GDN_PASS_RECURRENT_BWD. */
+gdn_status gdn_recurrent_ref(const gdn_problem* problem, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const float* S0, void* o, float* S_final, const void* dO,
+                             const float* dS_final, void* dq, void* dk, void* dv, float* dg,
+                             float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

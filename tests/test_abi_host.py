@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function include/gdn.h declares, and reject
+every bad argument on the host before any launch.  Pointers passed here are
+never dereferenced: each call fails validation first.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_deltanet_chunked_gdn_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nat.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert declared_functions() == sorted(nat.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {nat.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for s in range(10):
+        assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
+    assert lib.gdn_status_str(99).decode() == "unknown status"
+
+
+def problem(**kw):
+    p = nat.Problem()
+    d = dict(B=2, T=100, H=3, Dk=128, Dv=128, num_seqs=2, io_dtype=nat.GDN_BF16, scale=1.0,
+             chunk=64, num_segments=1)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def ws(p, pass_=nat.GDN_PASS_CHUNK_FWD):
+    n = ctypes.c_size_t(12345)
+    st = nat.load().gdn_workspace_size(ctypes.byref(p), pass_, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(io_dtype=7), nat.GDN_ERR_DTYPE),
+    (dict(H=0), nat.GDN_ERR_SHAPE),
+    (dict(T=-1), nat.GDN_ERR_SHAPE),
+    (dict(Dk=96), nat.GDN_ERR_UNSUPPORTED),
+    (dict(Dv=40), nat.GDN_ERR_UNSUPPORTED),
+    (dict(Dv=512), nat.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=32), nat.GDN_ERR_UNSUPPORTED),
+    (dict(num_segments=3), nat.GDN_ERR_UNSUPPORTED),
+    (dict(num_seqs=3), nat.GDN_ERR_SHAPE),
+    (dict(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_ERR_UNSUPPORTED),
+])
+def test_problem_validation(kw, status):
+    assert ws(problem(**kw))[0] == status
+
+
+def test_workspace_sizes():
+    assert ws(problem()) == (nat.GDN_OK, 0)
+    assert ws(problem(), nat.GDN_PASS_RECURRENT_FWD) == (nat.GDN_OK, 0)
+    st, n = ws(problem(Dk=64), nat.GDN_PASS_RECURRENT_BWD)
+    assert st == nat.GDN_OK and n > 0
+    assert ws(problem(), 17)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert nat.load().gdn_workspace_size(ctypes.byref(problem()), 0, None) == nat.GDN_ERR_NULL
+    assert nat.load().gdn_workspace_size(None, 0, ctypes.byref(ctypes.c_size_t())) == nat.GDN_ERR_NULL
+
+
+def test_recurrent_backward_lds_limit():
+    assert ws(problem(Dk=128, Dv=256), nat.GDN_PASS_RECURRENT_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(Dk=128, Dv=128), nat.GDN_PASS_RECURRENT_BWD)[0] == nat.GDN_OK
+
+
+def test_cu_seqlens_validation():
+    keep = []
+
+    def packed(cu, T=None, **kw):
+        host = np.asarray(cu, dtype=np.int32)
+        keep.append(host)
+        args = dict(B=1, T=int(host[-1]) if T is None else T, num_seqs=len(cu) - 1,
+                    cu_seqlens_host=host.ctypes.data, cu_seqlens_dev=0x1000)
+        args.update(kw)
+        return problem(**args)
+
+    assert ws(packed([0, 5, 5, 9]))[0] == nat.GDN_OK
+    assert ws(packed([0, 5, 3, 9]))[0] == nat.GDN_ERR_SEQLENS
+    assert ws(packed([1, 5, 9]))[0] == nat.GDN_ERR_SEQLENS
+    assert ws(packed([0, 5, 9], T=10))[0] == nat.GDN_ERR_SEQLENS
+    assert ws(packed([0, 5, 9], B=2))[0] == nat.GDN_ERR_SHAPE
+    p = packed([0, 5, 9])
+    p.cu_seqlens_dev = None
+    assert ws(p)[0] == nat.GDN_ERR_NULL
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation
+
+
+def fwd_call(p, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             beta=FAKE + (4 << 30), S0=None, o=FAKE + (5 << 30), Sf=None):
+    P = ctypes.c_void_p
+    return nat.load().gdn_chunk_fwd(ctypes.byref(p), P(q), P(k), P(v), P(g), P(beta), P(S0), P(o),
+                                    P(Sf), None, 0, None)
+
+
+def test_forward_pointer_checks():
+    p = problem()
+    assert fwd_call(p, q=None) == nat.GDN_ERR_NULL
+    assert fwd_call(p, o=None) == nat.GDN_ERR_NULL
+    assert fwd_call(p, q=FAKE + 8) == nat.GDN_ERR_ALIGN
+    assert fwd_call(p, g=FAKE + (3 << 30) + 2) == nat.GDN_ERR_ALIGN
+    assert fwd_call(p, o=FAKE + 4096) == nat.GDN_ERR_ALIAS          # o inside q
+    assert fwd_call(p, Sf=FAKE + (5 << 30) + 64) == nat.GDN_ERR_ALIAS  # S_final inside o
+    assert fwd_call(problem(Dk=80)) == nat.GDN_ERR_UNSUPPORTED
+
+
+def test_backward_entry_validates():
+    P = ctypes.c_void_p
+    z = [P(None)] * 15
+    assert nat.load().gdn_chunk_bwd(ctypes.byref(problem(chunk=16)), *z, 0, None) == nat.GDN_ERR_UNSUPPORTED
+
+
+def test_recurrent_backward_needs_workspace():
+    p = problem(Dk=64)
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE + (i << 30)) for i in range(16)]
+    ptrs[5] = P(None)   # S0
+    ptrs[9] = P(None)   # dS_final
+    ptrs[15] = P(None)  # dS0
+    st = nat.load().gdn_recurrent_ref(ctypes.byref(p), *ptrs, None, 0, None)
+    assert st == nat.GDN_ERR_WORKSPACE
