@@ -89,6 +89,11 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
 size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::RecBwd)
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
+  if (kind == Kind::ChunkFwd) {
+    if (c.N == 0) return 0;
+    // one 64 x 64 triangular inverse per (chunk slot, head), io element type
+    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 64 * 64 * c.io;
+  }
   return 0;
 }
 
@@ -172,15 +177,20 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
   const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
   st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
-                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false},
-                      {workspace, ws_bytes, 16, false}},
-                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false}});
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false},
+                      {workspace, ws_bytes, 16, false}});
   if (st != GDN_OK) return st;
   const size_t need = workspace_bytes(p, Kind::ChunkFwd, c);
   if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
   if (c.N == 0) return GDN_OK;
-  gdn::FwdParams fp{q, k, v, g, beta, S0, o, S_final, seq_info(p), p->H, p->Dv, p->scale};
-  return hip_status(gdn::launch_chunk_fwd(fp, c.N, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+  gdn::FwdParams fp{};
+  fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0; fp.o = o;
+  fp.S_final = S_final; fp.tws = workspace; fp.seq = seq_info(p);
+  fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
+  fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  fp.scale = p->scale;
+  return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
@@ -206,9 +216,9 @@ gdn_status gdn_recurrent_ref(const gdn_problem* p, const void* q, const void* k,
   const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
   std::vector<Tensor> ins = {{q, nk * c.io, 16, true},   {k, nk * c.io, 16, true},
                              {v, nv * c.io, 16, true},   {g, ng * 4, 4, true},
-                             {beta, ng * 4, 4, true},    {S0, ns * 4, 4, false},
-                             {workspace, ws_bytes, 16, false}};
-  std::vector<Tensor> outs = {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false}};
+                             {beta, ng * 4, 4, true},    {S0, ns * 4, 4, false}};
+  std::vector<Tensor> outs = {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false},
+                              {workspace, ws_bytes, 16, false}};
   if (bwd) {
     ins.push_back({dO, nv * c.io, 16, true});
     ins.push_back({dS_final, ns * 4, 4, false});

@@ -28,12 +28,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two values packed into one dword, `a` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // ----------------------------------------------------------------------------------
@@ -41,29 +45,56 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // ----------------------------------------------------------------------------------
 struct OpBf16 {
   using elem = uint16_t;
+  using frag_t = bf16x8_t;
   static constexpr int KSTEP = 32;  // reduction depth of one MFMA
   static constexpr int KPL = 8;     // reduction elements per lane
   static __device__ __forceinline__ elem cvt(float x) { return f32_to_bf16(x); }
   static __device__ __forceinline__ float widen(elem x) { return bf16_to_f32(x); }
-  static __device__ __forceinline__ bf16x8_t frag(const elem* buf, int ld, int lane, int k0) {
+  // Fragment of row (lane % 16) of `buf`, reduction columns k0 + 8 (lane / 16) + 0..7.
+  static __device__ __forceinline__ frag_t frag(const elem* buf, int ld, int lane, int k0) {
     const uint4 u = *reinterpret_cast<const uint4*>(buf + (lane & 15) * ld + k0 + (lane >> 4) * 8);
     return __builtin_bit_cast(bf16x8_t, u);
   }
-  static __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  // The same fragment read from memory where `row` already points at this lane's row.
+  static __device__ __forceinline__ frag_t frag_row(const elem* row, int lane, int k0) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + k0 + (lane >> 4) * 8);
+    return __builtin_bit_cast(bf16x8_t, u);
+  }
+  // Multiply element m of a fragment by s[k0 + 8 (lane / 16) + m] and re-round.
+  static __device__ __forceinline__ frag_t scale(frag_t f, const float* s, int lane, int k0) {
+    uint4 u = __builtin_bit_cast(uint4, f);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const float* sc = s + k0 + (lane >> 4) * 8;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float lo = __uint_as_float(w[m] << 16) * sc[2 * m];
+      const float hi = __uint_as_float(w[m] & 0xffff0000u) * sc[2 * m + 1];
+      w[m] = pack_bf16x2(lo, hi);
+    }
+    return __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]});
+  }
+  static __device__ __forceinline__ f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 
 struct OpF32 {
   using elem = float;
+  using frag_t = float;
   static constexpr int KSTEP = 4;
   static constexpr int KPL = 1;
   static __device__ __forceinline__ elem cvt(float x) { return x; }
   static __device__ __forceinline__ float widen(elem x) { return x; }
-  static __device__ __forceinline__ float frag(const elem* buf, int ld, int lane, int k0) {
+  static __device__ __forceinline__ frag_t frag(const elem* buf, int ld, int lane, int k0) {
     return buf[(lane & 15) * ld + k0 + (lane >> 4)];
   }
-  static __device__ __forceinline__ f32x4_t mma(float a, float b, f32x4_t c) {
+  static __device__ __forceinline__ frag_t frag_row(const elem* row, int lane, int k0) {
+    return row[k0 + (lane >> 4)];
+  }
+  static __device__ __forceinline__ frag_t scale(frag_t f, const float* s, int lane, int k0) {
+    return f * s[k0 + (lane >> 4)];
+  }
+  static __device__ __forceinline__ f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
 };
@@ -106,13 +137,23 @@ struct IoT<float> {
   static __device__ __forceinline__ void st(float* p, float x) { *p = x; }
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+// Lane shift within rows of 16 lanes / row broadcasts (DPP; gfx9 encodings).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: a shift-and-add
+// scan inside each row of 16 lanes, then the row totals are carried across rows
+// by the row_bcast:15 / row_bcast:31 broadcasts.  Lanes whose DPP source lies
+// outside the row (or whose row is masked off) add 0.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int /*lane*/) {
+  x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 

@@ -22,10 +22,18 @@ struct FwdParams {
   const float* S0;  // [N, H, Dk, Dv] or nullptr
   void* o;
   float* S_final;   // [N, H, Dk, Dv] or nullptr
+  void* tws;        // workspace: per-chunk triangular inverses T (io element type)
   SeqInfo seq;
-  int32_t H, Dv;
+  int32_t N, H, Dv;
+  int32_t max_chunks;  // chunks of the longest sequence
   float scale;
 };
+
+// Chunk slots of the T workspace.  Chunk c of sequence n (first row bos) uses
+// slot bos / 64 + n + c; slots of different sequences never overlap because a
+// sequence of len rows has at most floor((bos + len) / 64) - floor(bos / 64) + 1
+// chunks.  Total slots: floor(total_rows / 64) + N + 1.
+inline int64_t chunk_slots(int64_t total_rows, int64_t N) { return total_rows / 64 + N + 1; }
 
 struct RecParams {
   const void* q;
@@ -55,7 +63,7 @@ constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backw
 
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
-hipError_t launch_chunk_fwd(const FwdParams& p, int N, int Dk, bool bf16, hipStream_t s);
+hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 

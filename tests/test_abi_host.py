@@ -80,7 +80,9 @@ def test_problem_validation(kw, status):
 
 
 def test_workspace_sizes():
-    assert ws(problem()) == (nat.GDN_OK, 0)
+    # forward: one 64 x 64 io-typed inverse per (chunk slot, head); slots = rows // 64 + N + 1
+    assert ws(problem()) == (nat.GDN_OK, (200 // 64 + 2 + 1) * 3 * 64 * 64 * 2)
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (nat.GDN_OK, (200 // 64 + 2 + 1) * 3 * 4096 * 4)
     assert ws(problem(), nat.GDN_PASS_RECURRENT_FWD) == (nat.GDN_OK, 0)
     st, n = ws(problem(Dk=64), nat.GDN_PASS_RECURRENT_BWD)
     assert st == nat.GDN_OK and n > 0
@@ -127,6 +129,7 @@ def fwd_call(p, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 3
 
 def test_forward_pointer_checks():
     p = problem()
+    assert fwd_call(p) == nat.GDN_ERR_WORKSPACE
     assert fwd_call(p, q=None) == nat.GDN_ERR_NULL
     assert fwd_call(p, o=None) == nat.GDN_ERR_NULL
     assert fwd_call(p, q=FAKE + 8) == nat.GDN_ERR_ALIGN
