@@ -49,6 +49,21 @@ def alg_flops(w) -> float:
     return th * per_th
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per forward call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel source has changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"chunk_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["kernel_source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,7 +74,52 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--micro", choices=("copy", "gemm"), default=None,
+                    help="run a roofline microbenchmark instead: a 2 GiB device copy "
+                         "(bytes counted as read + write) or 8192^3 bf16/fp32 GEMMs")
     return ap.parse_args()
+
+
+def micro(kind: str, steps: int, warmup: int):
+    """Measured peaks, as the Day-2 page measures its GB10 ("Rooflines": a copy of a
+    2 GB tensor and (8192, 8192) x (8192, 8192) matmuls).  The library is only run."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    out = {"micro": kind}
+    if kind == "copy":
+        n = 2 * 1024 ** 3 // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        out.update({"bytes_per_copy": 2 * a.numel() * 4, "copy_GBps": 2 * a.numel() * 4 / t / 1e9,
+                    "frac_of_8TBps": 2 * a.numel() * 4 / t / 8e12, "ms": t * 1e3})
+    else:
+        for dt, peak in ((torch.bfloat16, 2.5e15), (torch.float32, 157.3e12)):
+            x = torch.randn(8192, 8192, device=dev).to(dt)
+            y = torch.randn(8192, 8192, device=dev).to(dt)
+            for _ in range(warmup):
+                torch.matmul(x, y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                torch.matmul(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / steps
+            fl = 2 * 8192 ** 3 / t
+            out[str(dt).split(".")[-1]] = {"TFLOPs": fl / 1e12, "frac_of_peak": fl / peak, "ms": t * 1e3}
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(d, w, budget_s: float):
@@ -88,6 +148,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.micro:
+        micro(args.micro, args.steps, args.warmup)
+        return
 
     import torch
 
@@ -161,8 +225,10 @@ def main():
                    "chunk": CHUNK, "io": w.io, "state": "fp32", "num_segments": 1,
                    "packed": d["cu_seqlens"] is not None},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": nbytes,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name),
+                     "kernel": "gdn_chunk_fwd = chunk_prep_kernel + chunk_state_kernel",
+                     "alg_bytes_per_launch": nbytes,
                      "kernel_ms_mean": k_mean * 1e3,
                      "kernel_ms_p10": float(np.percentile(kt, 10)) * 1e3,
                      "kernel_ms_p90": float(np.percentile(kt, 90)) * 1e3},

@@ -234,8 +234,8 @@ struct StateSmem {
   float Gam[2][64];         // exp(gamma)
   float Dec[2][64];         // exp(gamma_n - gamma)
   // producer private
-  E Ks[64 * LDK];
-  E Qs[2][64 * LDK];        // Q, token-major (consumers read the previous chunk's)
+  E Ks[64 * LDK];           // K, token-major
+  E Qs[2][64 * LDK];        // Q, token-major: staged by the consumers one chunk ahead
   E Vt[16 * LDC];           // V tile transposed
   E Tm[64 * LDC];           // T of the chunk being prepared (row-major, upper blocks zero)
   float gam[64], bg[64], bet[64];
@@ -296,7 +296,22 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
 
   if (consumer) {
     // ===================== consumers: the state recurrence =====================
+    // Besides the recurrence of chunk s-1, the consumers stage Q of chunk s
+    // (first half) and compute its causal score P (second half).
     f32x4_t Sacc[SRB];
+    const int tp = tid & 31, ds = tid >> 5;
+    u32x4_t qreg[2 * UPT];
+    auto load_q = [&](int c) {  // rows of Q of chunk c (clamped into the sequence)
+      const int64_t c0 = static_cast<int64_t>(c) * 64;
+      const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const E* qr = q + ((bos + c0 + min(2 * tp + tt, nv - 1)) * H + h) * DK + ds * EPT;
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) qreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(qr + u * EPV);
+      }
+    };
+    if (nch > 0) load_q(0);
 #pragma unroll
     for (int sr = 0; sr < SRB; ++sr) {
       const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
@@ -312,6 +327,19 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       F pf[tsteps<Op>(3)];
       float gam_o = 0.f, gam_n = 0.f;
       const int c = s - 1, b = c & 1;
+      if (s < nch) {  // stage Q of chunk s, padded rows as zeros; prefetch the next
+        const int nv = static_cast<int>(len - static_cast<int64_t>(s) * 64 < 64 ? len - static_cast<int64_t>(s) * 64 : 64);
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = 2 * tp + tt;
+#pragma unroll
+          for (int u = 0; u < UPT; ++u)
+            *reinterpret_cast<u32x4_t*>(sm.Qs[s & 1] + t * LDK + ds * EPT + u * EPV) =
+                t < nv ? qreg[tt * UPT + u] : z;
+        }
+        load_q(s + 1 < nch ? s + 1 : s);
+      }
       if (s >= 1) {
         // X = W S (rows of this wave), Y^T = S^T Q^T
         f32x4_t xacc = zero4();
@@ -368,6 +396,36 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           store4<E>(sm.St + (lane & 15) * LDK + 16 * sb + 4 * (lane >> 4), acc[0], acc[1], acc[2], acc[3]);
         }
       }
+      if (s < nch) {
+        // P = lower_incl(Q K^T o D) of chunk s, computed transposed so rows of P
+        // store contiguously.  Blocks (bi, bj) by wave:
+        //   0: (0,0) (1,0) (1,1)   1: (2,0) (2,1) (2,2)   2: (3,0) (3,1)   3: (3,2) (3,3)
+        const int bq = s & 1;
+        auto pblock = [&](int bi, int bj) {
+          f32x4_t acc = zero4();
+          tile_mma<Op, DK>(acc, sm.Ks + 16 * bj * LDK, LDK, sm.Qs[bq] + 16 * bi * LDK, LDK, lane);
+          const int i = 16 * bi + (lane & 15), jb = 16 * bj + 4 * (lane >> 4);
+          const float gi = sm.gam[i];
+          const float4 gj = *reinterpret_cast<const float4*>(sm.gam + jb);
+          const float gjj[4] = {gj.x, gj.y, gj.z, gj.w};
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float d = exp2f(fminf(gi - gjj[r], 0.f));
+            pv[r] = jb + r <= i ? acc[r] * d : 0.f;
+          }
+          store4<E>(sm.Pm + i * LDC + jb, pv[0], pv[1], pv[2], pv[3]);
+        };
+        if (w == 0) {
+          pblock(0, 0); pblock(1, 0); pblock(1, 1);
+        } else if (w == 1) {
+          pblock(2, 0); pblock(2, 1); pblock(2, 2);
+        } else if (w == 2) {
+          pblock(3, 0); pblock(3, 1);
+        } else {
+          pblock(3, 2); pblock(3, 3);
+        }
+      }
       __syncthreads();
     }
     if (p.S_final) {
@@ -384,7 +442,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     // into the sequence, padded rows zeroed when used), so the compiler can wait
     // for exactly the loads it needs.
     const int ptid = tid - 256, tp = ptid & 31, ds = ptid >> 5;
-    u32x4_t kreg[2 * UPT], qreg[2 * UPT], vreg[2];
+    u32x4_t kreg[2 * UPT], vreg[2];
     float greg = 0.f, breg = 0.f;
     // W and U work split by row blocks of T: waves 0, 1 take row blocks {0, 3},
     // waves 2, 3 take {1, 2} (three k-steps each), each wave half of W's columns.
@@ -405,12 +463,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       for (int tt = 0; tt < 2; ++tt) {
         const int t = min(2 * tp + tt, nv - 1);
         const E* kr = k + ((row0 + t) * H + h) * DK + ds * EPT;
-        const E* qr = q + ((row0 + t) * H + h) * DK + ds * EPT;
 #pragma unroll
-        for (int u = 0; u < UPT; ++u) {
-          kreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(kr + u * EPV);
-          qreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(qr + u * EPV);
-        }
+        for (int u = 0; u < UPT; ++u) kreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(kr + u * EPV);
         if (w < NVS / 2)  // wave-uniform: the threads that store the v tile
           vreg[tt] = *reinterpret_cast<const u32x4_t*>(v + ((row0 + t) * H + h) * Dv + j0 + ds * EPV);
       }
@@ -441,9 +495,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
 #pragma unroll
           for (int u = 0; u < UPT; ++u) {
             kreg[tt * UPT + u] = ok ? kreg[tt * UPT + u] : z;
-            qreg[tt * UPT + u] = ok ? qreg[tt * UPT + u] : z;
             *reinterpret_cast<u32x4_t*>(sm.Ks + t * LDK + ds * EPT + u * EPV) = kreg[tt * UPT + u];
-            *reinterpret_cast<u32x4_t*>(sm.Qs[b] + t * LDK + ds * EPT + u * EPV) = qreg[tt * UPT + u];
           }
           vreg[tt] = ok ? vreg[tt] : z;
         }
@@ -480,33 +532,6 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       }
       __syncthreads();
       if (s < nch) {
-        // P = lower_incl(Q K^T o D), computed transposed so rows of P store contiguously.
-        // Blocks (bi, bj) by wave: 0: (0,0) (1,0) (1,1)   1: (2,0) (2,1) (2,2)
-        //                          2: (3,0) (3,1)         3: (3,2) (3,3)
-        auto pblock = [&](int bi, int bj) {
-          f32x4_t acc = zero4();
-          tile_mma<Op, DK>(acc, sm.Ks + 16 * bj * LDK, LDK, sm.Qs[b] + 16 * bi * LDK, LDK, lane);
-          const int i = 16 * bi + (lane & 15), jb = 16 * bj + 4 * (lane >> 4);
-          const float gi = sm.gam[i];
-          const float4 gj = *reinterpret_cast<const float4*>(sm.gam + jb);
-          const float gjj[4] = {gj.x, gj.y, gj.z, gj.w};
-          float pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float d = exp2f(fminf(gi - gjj[r], 0.f));
-            pv[r] = jb + r <= i ? acc[r] * d : 0.f;
-          }
-          store4<E>(sm.Pm + i * LDC + jb, pv[0], pv[1], pv[2], pv[3]);
-        };
-        if (w == 0) {
-          pblock(0, 0); pblock(1, 0); pblock(1, 1);
-        } else if (w == 1) {
-          pblock(2, 0); pblock(2, 1); pblock(2, 2);
-        } else if (w == 2) {
-          pblock(3, 0); pblock(3, 1);
-        } else {
-          pblock(3, 2); pblock(3, 3);
-        }
         // W^T = K^T (T diag(beta Gamma))^T, transposed so rows of W store contiguously;
         // U = T diag(beta) V for one row block, in the consumers' accumulator order
         for_rowblocks([&](auto R0, auto R1) {
