@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="train_bf16")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
+    ap.add_argument("--num-segments", type=int, default=1,
+                    help="segments per sequence (1: serial over chunks; 2..16: segment split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -177,11 +179,14 @@ def main():
         t["Sf"] = torch.empty((w.num_seqs, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
         sets.append(t)
     seqs = None if d["cu_seqlens"] is None else gdn.SeqLens(d["cu_seqlens"], dev)
+    for t in sets:  # workspaces allocated before the timed region
+        t["ws"] = gdn.forward_workspace(t["q"], t["v"], seqs, args.num_segments)
 
     def step(i):
         t = sets[i % len(sets)]
         gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"], cu_seqlens=seqs,
-                      scale=d["scale"], out=t["o"], final_state_out=t["Sf"])
+                      scale=d["scale"], num_segments=args.num_segments, out=t["o"],
+                      final_state_out=t["Sf"], workspace=t["ws"])
 
     for i in range(args.warmup):
         step(i)
@@ -222,7 +227,7 @@ def main():
         "dtype": w.io,
         "data": "synthetic (seeded numpy generator; random inputs of the named shape)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv,
-                   "chunk": CHUNK, "io": w.io, "state": "fp32", "num_segments": 1,
+                   "chunk": CHUNK, "io": w.io, "state": "fp32", "num_segments": args.num_segments,
                    "packed": d["cu_seqlens"] is not None},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,

@@ -4,5 +4,6 @@ The computation lives in libgdn.so (HIP kernels behind the C ABI of
 include/gdn.h); this package is its Python binding plus the seeded synthetic
 input generators.
 """
-from .ops import SeqLens, chunk_bwd, chunk_fwd, make_problem, recurrent_ref  # noqa: F401
+from .ops import (SeqLens, chunk_bwd, chunk_fwd, forward_workspace, make_problem,  # noqa: F401
+                  recurrent_ref)
 from ._native import GdnError, GdnLibraryMissing  # noqa: F401

@@ -53,7 +53,6 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (chunked) {
     const int G = p->num_segments;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
-    if (G != 1) return GDN_ERR_UNSUPPORTED;  // segment split not built yet
     if (kind == Kind::ChunkBwd) return GDN_ERR_UNSUPPORTED;  // chunked backward not built yet
     if (p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
   }
@@ -78,7 +77,11 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
     if (p->num_seqs != p->B) return GDN_ERR_SHAPE;
     c->max_len = p->T;
   }
-  if (p->num_seqs > 65535) return GDN_ERR_UNSUPPORTED;
+  if (p->num_seqs > 65535 || p->H > 65535) return GDN_ERR_UNSUPPORTED;
+  // one state-kernel launch has num_segments * N * H * (Dv / 16) blocks
+  if (static_cast<int64_t>(chunked && p->num_segments > 1 ? p->num_segments : 1) * p->num_seqs * p->H *
+          (p->Dv / 16) > INT32_MAX)
+    return GDN_ERR_UNSUPPORTED;
   c->tokens = static_cast<int64_t>(p->B) * p->T;
   c->N = p->num_seqs;
   c->bf16 = p->io_dtype == GDN_BF16;
@@ -86,13 +89,20 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   return GDN_OK;
 }
 
+size_t t_slot_bytes(const gdn_problem* p, const Checked& c) {
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 64 * 64 * c.io;
+  return (b + 255) / 256 * 256;
+}
+
 size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::RecBwd)
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
   if (kind == Kind::ChunkFwd) {
     if (c.N == 0) return 0;
-    // one 64 x 64 triangular inverse per (chunk slot, head), io element type
-    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 64 * 64 * c.io;
+    // one 64 x 64 triangular inverse per (chunk slot, head), io element type,
+    // then (num_segments > 1) the fp32 segment end states, start states and maps
+    return t_slot_bytes(p, c) +
+           gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
   }
   return 0;
 }
@@ -190,6 +200,9 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
   fp.scale = p->scale;
+  fp.G = p->num_segments;
+  fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + t_slot_bytes(p, c))
+                       : nullptr;
   return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 

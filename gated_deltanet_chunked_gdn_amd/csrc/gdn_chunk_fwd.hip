@@ -270,23 +270,31 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool consumer = wave < 4;
   const int w = wave & 3;
-  const int H = p.H, Dv = p.Dv, NT = Dv / 16;
+  const int H = p.H, Dv = p.Dv, NC = p.ncol, NT = NC / 16;
   // XCD-aware block order: consecutive virtual blocks (the tiles of one head)
   // land on the same XCD, which the hardware picks as blockIdx % 8.
   const int NB = gridDim.x, L = blockIdx.x;
   const int vb = (NB % 8 == 0) ? (L % 8) * (NB / 8) + L / 8 : L;
-  const int tile = vb % NT, nh = vb / NT, h = nh % H, n = nh / H;
+  const int tile = vb % NT, nh = (vb / NT) % (p.N * H), h = nh % H, n = nh / H;
+  const int seg = p.seg_base + vb / NT / (p.N * H);
   const int j0 = tile * 16;
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
-  const int nch = static_cast<int>((len + 63) / 64);
-  const int64_t slot0 = bos / 64 + n;
+  // this block's chunks: segment `seg` of the sequence (all of it when G == 1)
+  const int nch_all = static_cast<int>((len + 63) / 64);
+  const int seg_len = (nch_all + p.G - 1) / p.G;
+  const int cb = min(seg * seg_len, nch_all);
+  const int nch = min(cb + seg_len, nch_all) - cb;
+  const int64_t slot0 = bos / 64 + n + cb;
+  const bool write_o = p.write_o == kOutAll || (p.write_o == kOutSeg0 && seg == 0);
+  const bool use_v = !p.zero_u;
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
   const E* v = static_cast<const E*>(p.v);
   const E* tws = static_cast<const E*>(p.tws);
   E* o = static_cast<E*>(p.o);
   const int64_t nhS = (static_cast<int64_t>(n) * H + h) * DK;
+  const int64_t segS = (static_cast<int64_t>(seg) * p.N * H + nh) * DK;  // [G][N][H][DK][NC] buffers
 
   // upper blocks of P are never written
   for (int x = tid; x < 64 * LDC; x += 512) {
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     const int tp = tid & 31, ds = tid >> 5;
     u32x4_t qreg[2 * UPT];
     auto load_q = [&](int c) {  // rows of Q of chunk c (clamped into the sequence)
-      const int64_t c0 = static_cast<int64_t>(c) * 64;
+      const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
       const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -311,13 +319,22 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         for (int u = 0; u < UPT; ++u) qreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(qr + u * EPV);
       }
     };
-    if (nch > 0) load_q(0);
+    if (nch > 0 && write_o) load_q(0);
 #pragma unroll
     for (int sr = 0; sr < SRB; ++sr) {
       const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = p.S0 ? p.S0[(nhS + i + r) * Dv + j0 + j] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        if (p.start_mode == kStartCarry)
+          x[r] = p.carry[(segS + i + r) * NC + j0 + j];
+        else if (p.start_mode == kStartIdentity)
+          x[r] = i + r == j0 + j ? 1.f : 0.f;
+        else if (p.start_mode == kStartS0 && seg == 0 && p.S0)
+          x[r] = p.S0[(nhS + i + r) * Dv + j0 + j];
+        else
+          x[r] = 0.f;
+      }
       Sacc[sr] = f32x4_t{x[0], x[1], x[2], x[3]};
       store4<E>(sm.St + j * LDK + i, x[0], x[1], x[2], x[3]);
     }
@@ -327,8 +344,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       F pf[tsteps<Op>(3)];
       float gam_o = 0.f, gam_n = 0.f;
       const int c = s - 1, b = c & 1;
-      if (s < nch) {  // stage Q of chunk s, padded rows as zeros; prefetch the next
-        const int nv = static_cast<int>(len - static_cast<int64_t>(s) * 64 < 64 ? len - static_cast<int64_t>(s) * 64 : 64);
+      if (s < nch && write_o) {  // stage Q of chunk s, padded rows as zeros; prefetch the next
+        const int64_t cs0 = static_cast<int64_t>(cb + s) * 64;
+        const int nv = static_cast<int>(len - cs0 < 64 ? len - cs0 : 64);
         const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -347,10 +365,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         for (int ks = 0; ks < NKQ; ++ks) {
           const F st = Op::frag(sm.St, LDK, lane, ks * KS);
           xacc = Op::mma(Op::frag(sm.Ws + 16 * w * LDK, LDK, lane, ks * KS), st, xacc);
-          yacc = Op::mma(st, Op::frag(sm.Qs[b] + 16 * w * LDK, LDK, lane, ks * KS), yacc);
+          if (write_o) yacc = Op::mma(st, Op::frag(sm.Qs[b] + 16 * w * LDK, LDK, lane, ks * KS), yacc);
         }
         // E = U - X; E^T and the decayed E^T go to LDS for every consumer
-        const float4 u = *reinterpret_cast<const float4*>(sm.Us + (w * 64 + lane) * 4);
+        const float4 u = use_v ? *reinterpret_cast<const float4*>(sm.Us + (w * 64 + lane) * 4)
+                               : float4{0.f, 0.f, 0.f, 0.f};
         const float uu[4] = {u.x, u.y, u.z, u.w};
         const int t0 = 16 * w + 4 * (lane >> 4), j = lane & 15;
         float e[4], ed[4];
@@ -364,13 +383,13 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         // this wave's rows of P and the decays it needs after the barrier
 #pragma unroll
         for (int ks = 0; ks < tsteps<Op>(3); ++ks)
-          pf[ks] = ks < tsteps<Op>(w) ? Op::frag(sm.Pm + 16 * w * LDC, LDC, lane, ks * KS) : F{};
+          pf[ks] = write_o && ks < tsteps<Op>(w) ? Op::frag(sm.Pm + 16 * w * LDC, LDC, lane, ks * KS) : F{};
         gam_o = sm.Gam[b][16 * w + (lane & 15)];
         gam_n = sm.Gam[b][63];
       }
       __syncthreads();
       if (s >= 1) {
-        const int64_t c0 = static_cast<int64_t>(c) * 64;
+        const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
         const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
         // O^T = E^T P^T + Y^T scaled by Gamma  (rows j, columns t)
         f32x4_t oacc = zero4();
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         for (int ks = 0; ks < tsteps<Op>(3); ++ks)
           oacc = Op::mma(Op::frag(sm.Et, LDC, lane, ks * KS), pf[ks], oacc);
         const int t = 16 * w + (lane & 15), jj = 4 * (lane >> 4);
-        if (t < nv) {
+        if (write_o && t < nv) {
           E* dst = o + ((bos + c0 + t) * H + h) * Dv + j0 + jj;
           store4<E>(dst, p.scale * (gam_o * yacc[0] + oacc[0]), p.scale * (gam_o * yacc[1] + oacc[1]),
                     p.scale * (gam_o * yacc[2] + oacc[2]), p.scale * (gam_o * yacc[3] + oacc[3]));
@@ -396,7 +415,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           store4<E>(sm.St + (lane & 15) * LDK + 16 * sb + 4 * (lane >> 4), acc[0], acc[1], acc[2], acc[3]);
         }
       }
-      if (s < nch) {
+      if (s < nch && write_o) {
         // P = lower_incl(Q K^T o D) of chunk s, computed transposed so rows of P
         // store contiguously.  Blocks (bi, bj) by wave:
         //   0: (0,0) (1,0) (1,1)   1: (2,0) (2,1) (2,2)   2: (3,0) (3,1)   3: (3,2) (3,3)
@@ -428,12 +447,18 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       }
       __syncthreads();
     }
-    if (p.S_final) {
+    const bool to_final = p.final_to_sfinal && seg == p.G - 1;
+    if (to_final ? p.S_final != nullptr : p.seg_out != nullptr) {
 #pragma unroll
       for (int sr = 0; sr < SRB; ++sr) {
         const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p.S_final[(nhS + i + r) * Dv + j0 + j] = Sacc[sr][r];
+        for (int r = 0; r < 4; ++r) {
+          if (to_final)
+            p.S_final[(nhS + i + r) * Dv + j0 + j] = Sacc[sr][r];
+          else
+            p.seg_out[(segS + i + r) * NC + j0 + j] = Sacc[sr][r];
+        }
       }
     }
   } else {
@@ -456,7 +481,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         fn(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
     };
     auto load_chunk = [&](int c) {  // raw rows of chunk c and its T into registers
-      const int64_t c0 = static_cast<int64_t>(c) * 64;
+      const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
       const int64_t row0 = bos + c0;
       const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
 #pragma unroll
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         const E* kr = k + ((row0 + t) * H + h) * DK + ds * EPT;
 #pragma unroll
         for (int u = 0; u < UPT; ++u) kreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(kr + u * EPV);
-        if (w < NVS / 2)  // wave-uniform: the threads that store the v tile
+        if (use_v && w < NVS / 2)  // wave-uniform: the threads that store the v tile
           vreg[tt] = *reinterpret_cast<const u32x4_t*>(v + ((row0 + t) * H + h) * Dv + j0 + ds * EPV);
       }
       if (w == 0) {
@@ -484,7 +509,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     auto step = [&](int s) {
       const int b = s & 1;
       if (s < nch) {
-        const int64_t c0 = static_cast<int64_t>(s) * 64;
+        const int64_t c0 = static_cast<int64_t>(cb + s) * 64;
         const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
         const u32x4_t z = {0u, 0u, 0u, 0u};
         // rows of chunk s: K, Q token-major; K^T; V^T (padded rows as zeros)
@@ -546,15 +571,16 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
               tw[ks] = Op::scale(Op::frag(sm.Tm + 16 * rb[x] * LDC, LDC, lane, ks * KS), sm.bg, lane, ks * KS);
 #pragma unroll
             for (int cj = 0; cj < NCW; ++cj) {
-              const int cb = (w & 1) * NCW + cj;
+              const int cw = (w & 1) * NCW + cj;
               f32x4_t acc = zero4();
 #pragma unroll
               for (int ks = 0; ks < tsteps<Op>(rb[x]); ++ks)
-                acc = Op::mma(Op::frag(sm.Kt[b] + 16 * cb * LDC, LDC, lane, ks * KS), tw[ks], acc);
-              store4<E>(sm.Ws + (16 * ri + (lane & 15)) * LDK + 16 * cb + 4 * (lane >> 4), acc[0],
+                acc = Op::mma(Op::frag(sm.Kt[b] + 16 * cw * LDC, LDC, lane, ks * KS), tw[ks], acc);
+              store4<E>(sm.Ws + (16 * ri + (lane & 15)) * LDK + 16 * cw + 4 * (lane >> 4), acc[0],
                         acc[1], acc[2], acc[3]);
             }
           }
+          if (!use_v) return;  // transition maps: U = 0, read as zeros by the consumers
           const int x = w & 1;
           const int ri = x ? rb[1] : rb[0];
           f32x4_t acc = zero4();
@@ -580,6 +606,47 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   }
 }
 
+// Segment carries (sequential in the segment index, parallel over sequences,
+// heads and 16-column tiles): start(1) = end(0), and
+// start(sigma + 1) = M_sigma start(sigma) + b_sigma for sigma = 1 .. G-2, in fp32,
+// with a fixed summation order.  One block of 256 threads per 16-column tile.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_carry_kernel(CarryParams c) {
+  __shared__ float cur[DK][17];
+  const int NT = c.Dv / 16;
+  const int tile = blockIdx.x % NT, nh = blockIdx.x / NT;
+  const int j0 = tile * 16, tid = threadIdx.x, jj = tid & 15, i0 = tid >> 4;
+  const int64_t NHD = static_cast<int64_t>(c.N) * c.H * DK;
+  auto at = [&](int sigma, int i) {  // element offset in a [G][N][H][DK][Dv] buffer
+    return (sigma * NHD + static_cast<int64_t>(nh) * DK + i) * c.Dv + j0 + jj;
+  };
+  for (int i = i0; i < DK; i += 16) {
+    const float x = c.ends[at(0, i)];
+    cur[i][jj] = x;
+    c.starts[at(1, i)] = x;
+  }
+  __syncthreads();
+  for (int sg = 1; sg + 1 < c.G; ++sg) {
+    float nxt[DK / 16];
+    const float* M = c.maps + (sg * NHD + static_cast<int64_t>(nh) * DK) * DK;  // [G][N][H][DK][DK]
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r) {
+      const int i = i0 + 16 * r;
+      float acc = c.ends[at(sg, i)];
+      for (int k = 0; k < DK; ++k) acc = fmaf(M[static_cast<int64_t>(i) * DK + k], cur[k][jj], acc);
+      nxt[r] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r) {
+      const int i = i0 + 16 * r;
+      cur[i][jj] = nxt[r];
+      c.starts[at(sg + 1, i)] = nxt[r];
+    }
+    __syncthreads();
+  }
+}
+
 template <int DK, typename Op>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   constexpr size_t prep_smem = sizeof(PrepSmem<DK, Op>);
@@ -599,8 +666,42 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(p.N * p.H * (p.Dv / 16)), dim3(512), state_smem, s, p);
-  return hipGetLastError();
+  auto run_state = [&](const FwdParams& q) {
+    hipLaunchKernelGGL(state, dim3(q.nseg * q.N * q.H * (q.ncol / 16)), dim3(512), state_smem, s, q);
+    return hipGetLastError();
+  };
+  FwdParams q = p;
+  q.ncol = p.Dv;
+  q.zero_u = 0;
+  q.carry = nullptr;
+  if (p.G == 1) {
+    q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
+    q.seg_out = nullptr; q.final_to_sfinal = 1;
+    return run_state(q);
+  }
+  // G segments per sequence: (1) segment 0 from S0 with its outputs, and the
+  // segments 1 .. G-2 from zero (their offsets b); (2) the transition maps M of
+  // segments 1 .. G-2 (the same pass with U = 0, started from the identity);
+  // (3) the carries; (4) segments 1 .. G-1 again from their carried start states.
+  const size_t ends_floats = static_cast<size_t>(p.G) * p.N * p.H * DK * p.Dv;
+  float* ends = p.seg_ws;
+  float* starts = ends + ends_floats;
+  float* maps = starts + ends_floats;
+  q.seg_base = 0; q.nseg = p.G - 1; q.start_mode = kStartS0; q.write_o = kOutSeg0;
+  q.seg_out = ends; q.final_to_sfinal = 0;
+  if ((e = run_state(q)) != hipSuccess) return e;
+  if (p.G > 2) {
+    FwdParams m = q;
+    m.ncol = DK; m.seg_base = 1; m.nseg = p.G - 2; m.start_mode = kStartIdentity;
+    m.write_o = kOutNone; m.zero_u = 1; m.seg_out = maps;
+    if ((e = run_state(m)) != hipSuccess) return e;
+  }
+  CarryParams c{ends, maps, starts, p.G, p.N, p.H, DK, p.Dv};
+  hipLaunchKernelGGL(seg_carry_kernel<DK>, dim3(p.N * p.H * (p.Dv / 16)), dim3(256), 0, s, c);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  q.seg_base = 1; q.nseg = p.G - 1; q.start_mode = kStartCarry; q.write_o = kOutAll;
+  q.carry = starts; q.seg_out = nullptr; q.final_to_sfinal = 1;
+  return run_state(q);
 }
 
 }  // namespace

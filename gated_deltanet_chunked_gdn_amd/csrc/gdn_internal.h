@@ -27,6 +27,28 @@ struct FwdParams {
   int32_t N, H, Dv;
   int32_t max_chunks;  // chunks of the longest sequence
   float scale;
+  // Segment split: every sequence is cut into G runs of whole chunks; segment
+  // sigma covers chunks [sigma L, min((sigma + 1) L, nch)), L = ceil(nch / G).
+  // One launch of the state kernel covers segments seg_base .. seg_base + nseg - 1.
+  int32_t G, seg_base, nseg;
+  int32_t start_mode;  // kStartS0 / kStartZero / kStartIdentity / kStartCarry
+  int32_t write_o;     // kOutNone / kOutAll / kOutSeg0
+  int32_t zero_u;      // U = 0: propagate transition maps instead of states
+  int32_t ncol;        // state columns: Dv, or Dk for transition maps
+  const float* carry;  // [G][N][H][Dk][ncol] start states (kStartCarry)
+  float* seg_out;      // [G][N][H][Dk][ncol] end states, or nullptr
+  int32_t final_to_sfinal;  // segment G - 1 writes S_final (layout [N][H][Dk][Dv])
+  float* seg_ws;       // G > 1: ends, starts ([G][N][H][Dk][Dv] each), maps ([G][N][H][Dk][Dk])
+};
+
+enum : int32_t { kStartS0 = 0, kStartZero = 1, kStartIdentity = 2, kStartCarry = 3 };
+enum : int32_t { kOutNone = 0, kOutAll = 1, kOutSeg0 = 2 };
+
+struct CarryParams {
+  const float* ends;   // [G][N][H][Dk][Dv]: end state of each segment run from its own start
+  const float* maps;   // [G][N][H][Dk][Dk]: transition map of each segment
+  float* starts;       // [G][N][H][Dk][Dv]: start states, written for sigma = 1 .. G - 1
+  int32_t G, N, H, Dk, Dv;
 };
 
 // Chunk slots of the T workspace.  Chunk c of sequence n (first row bos) uses
@@ -64,6 +86,12 @@ constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backw
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
+// Bytes of forward workspace beyond the T slots for G segments (0 for G = 1).
+inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
+  if (G <= 1) return 0;
+  const size_t nh = static_cast<size_t>(G) * N * H * Dk;
+  return (2 * nh * Dv + nh * Dk) * sizeof(float);
+}
 hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 

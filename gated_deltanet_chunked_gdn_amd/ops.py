@@ -111,6 +111,13 @@ def _workspace(problem, pass_, device):
     return torch.empty(n, dtype=torch.uint8, device=device), n
 
 
+def forward_workspace(q, v, cu_seqlens=None, num_segments: int = 1):
+    """A uint8 device tensor of the size gdn_chunk_fwd asks for (None if 0 bytes)."""
+    seqs = _seqlens(cu_seqlens, q.device)
+    return _workspace(make_problem(q, v, seqs, 1.0, num_segments), nat.GDN_PASS_CHUNK_FWD,
+                      q.device)[0]
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
               num_segments: int = 1, output_final_state: bool = True, out=None,
               final_state_out=None, workspace=None):

@@ -128,10 +128,16 @@ gdn_status gdn_workspace_size(const gdn_problem* problem, int32_t pass, size_t* 
  *   E = T diag(beta) (V - diag(exp(gamma)) K S_c)      (the errors e_t of the chunk)
  *   O = scale (diag(exp(gamma)) Q S_c + lower_incl(Q K^T o D) E)
  *   S_{c+1} = exp(gamma_n) S_c + (diag(exp(gamma_n - gamma)) K)^T E
- * num_segments = G > 1 splits every sequence into G runs of whole chunks whose
- * affine state maps S -> M S + b are formed in fp32 and composed (cuLA issue
- * #126 page, "Summary" and "Hypothesis": segment affine transforms and carries).
- * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...). */
+ * num_segments = G > 1 splits every sequence of nch chunks into G runs of whole
+ * chunks (segment s covers chunks [s L, min((s + 1) L, nch)), L = ceil(nch / G))
+ * that run in parallel: each segment's state map S -> M S + b is taken by the
+ * same chunk pass (b from a zero start, M from the identity with V = 0), the
+ * start states are composed in fp32 in segment order, and the segments are run
+ * again from them with their outputs (cuLA issue #126 page, "Summary" and
+ * "Hypothesis": segment affine transforms and carries).  G = 2 gives results
+ * bit-identical to G = 1; G > 2 agrees to the bf16 rounding of M's operands.
+ * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...): the per-chunk
+ * inverses, plus for G > 1 fp32 buffers of 2 G N H Dk Dv + G N H Dk Dk floats. */
 gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,
                          void* o, float* S_final, void* workspace, size_t workspace_bytes,

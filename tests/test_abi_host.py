@@ -72,6 +72,8 @@ def ws(p, pass_=nat.GDN_PASS_CHUNK_FWD):
     (dict(Dv=512), nat.GDN_ERR_UNSUPPORTED),
     (dict(chunk=32), nat.GDN_ERR_UNSUPPORTED),
     (dict(num_segments=3), nat.GDN_ERR_UNSUPPORTED),
+    (dict(num_segments=0), nat.GDN_ERR_UNSUPPORTED),
+    (dict(num_segments=32), nat.GDN_ERR_UNSUPPORTED),
     (dict(num_seqs=3), nat.GDN_ERR_SHAPE),
     (dict(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_ERR_UNSUPPORTED),
 ])
@@ -83,6 +85,12 @@ def test_workspace_sizes():
     # forward: one 64 x 64 io-typed inverse per (chunk slot, head); slots = rows // 64 + N + 1
     assert ws(problem()) == (nat.GDN_OK, (200 // 64 + 2 + 1) * 3 * 64 * 64 * 2)
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (nat.GDN_OK, (200 // 64 + 2 + 1) * 3 * 4096 * 4)
+    # segment split: the inverses (rounded up to 256 bytes), then fp32 end and
+    # start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
+    t_bytes = (200 // 64 + 2 + 1) * 3 * 64 * 64 * 2
+    for G in (2, 4, 16):
+        seg = (2 * G * 2 * 3 * 128 * 96 + G * 2 * 3 * 128 * 128) * 4
+        assert ws(problem(num_segments=G, Dv=96)) == (nat.GDN_OK, t_bytes + seg)
     assert ws(problem(), nat.GDN_PASS_RECURRENT_FWD) == (nat.GDN_OK, 0)
     st, n = ws(problem(Dk=64), nat.GDN_PASS_RECURRENT_BWD)
     assert st == nat.GDN_OK and n > 0
