@@ -53,7 +53,7 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (chunked) {
     const int G = p->num_segments;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
-    if (kind == Kind::ChunkBwd) return GDN_ERR_UNSUPPORTED;  // chunked backward not built yet
+    if (kind == Kind::ChunkBwd && G != 1) return GDN_ERR_UNSUPPORTED;
     if (p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
   }
   if (kind == Kind::RecBwd && static_cast<size_t>(2) * p->Dk * (p->Dv + 1) * 4 +
@@ -94,6 +94,10 @@ size_t t_slot_bytes(const gdn_problem* p, const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
+size_t state_slot_bytes(const gdn_problem* p, const Checked& c) {
+  return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * sizeof(float);
+}
+
 size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::RecBwd)
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
@@ -103,6 +107,12 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
     // then (num_segments > 1) the fp32 segment end states, start states and maps
     return t_slot_bytes(p, c) +
            gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
+  }
+  if (kind == Kind::ChunkBwd) {
+    if (c.N == 0) return 0;
+    // the inverses, then the fp32 state before and the state gradient after
+    // every chunk, [slot][H][Dk][Dv] each
+    return t_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
   }
   return 0;
 }
@@ -212,7 +222,38 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
                          float* dbeta, float* dS0, void* workspace, size_t ws_bytes,
                          void* stream) {
   Checked c;
-  return check_problem(p, Kind::ChunkBwd, &c);
+  gdn_status st = check_problem(p, Kind::ChunkBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false},
+                      {dO, nv * c.io, 16, true}, {dS_final, ns * 4, 4, false}},
+                     {{dq, nk * c.io, 16, true}, {dk, nk * c.io, 16, true}, {dv, nv * c.io, 16, true},
+                      {dg, ng * 4, 4, true}, {dbeta, ng * 4, 4, true}, {dS0, ns * 4, 4, false},
+                      {workspace, ws_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::ChunkBwd, c);
+  if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* states = reinterpret_cast<float*>(static_cast<char*>(workspace) + t_slot_bytes(p, c));
+  float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + state_slot_bytes(p, c));
+  gdn::FwdParams fp{};
+  fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0;
+  fp.tws = workspace; fp.states = states; fp.seq = seq_info(p);
+  fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
+  fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  fp.scale = p->scale;
+  fp.G = 1;
+  st = hip_status(gdn::launch_chunk_fwd_states(fp, p->Dk, c.bf16, s));
+  if (st != GDN_OK) return st;
+  gdn::BwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
+  bp.tws = workspace; bp.states = states; bp.dstates = dstates; bp.seq = seq_info(p);
+  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv; bp.max_chunks = fp.max_chunks; bp.scale = p->scale;
+  return hip_status(gdn::launch_chunk_bwd(bp, p->Dk, c.bf16, s));
 }
 
 gdn_status gdn_recurrent_ref(const gdn_problem* p, const void* q, const void* k, const void* v,

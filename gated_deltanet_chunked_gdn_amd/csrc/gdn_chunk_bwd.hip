@@ -1,0 +1,852 @@
+// Chunked backward pass of the gated delta rule on gfx950.
+//
+// Gradients of L = <o, dO> + <S_final, dS_final> (the six gradients of the
+// "Research Sprint Day 1" page, "Results", plus dS0).  With the chunk algebra of
+// the forward (gamma, Gamma, D, T, W, U, E, P and K~ = diag(exp(gamma_n - gamma)) K
+// for one chunk of n <= 64 tokens, state S_c before it) and dOs = scale dO, the
+// reverse mode of one chunk, given dS_{c+1}, is
+//   dE  = K~ dS_{c+1} + P^T dOs
+//   dS_c = Gamma_n dS_{c+1} + (diag(Gamma) Q)^T dOs - W^T dE        [state pass]
+//   dK~ = E dS_{c+1}^T,  dQ = diag(Gamma) dOs S_c^T + (dP o D) K,  dP = lower(dOs E^T)
+//   dW  = -dE S_c^T,  dT = dE (diag(beta) V)^T + dW (diag(beta Gamma) K)^T
+//   dA  = strict_lower(-T^T dT T^T),  dV = diag(beta) T^T dE
+//   dK  = diag(exp(gamma_n - gamma)) dK~ + (dP o D)^T Q + (dKK + dKK^T) K
+//         + diag(beta Gamma) T^T dW,   dKK = dA o beta_i D
+//   dbeta, dgamma: the row sums of the terms above that carry beta, Gamma or D;
+//   dg = reverse cumsum of dgamma within the chunk (gamma = cumsum g).
+//
+// Kernels (the forward states come from the forward state kernel run with a
+// per-chunk state output):
+//   chunk_dstate_kernel: one workgroup per (sequence, head, 16-column tile of
+//     d_v), sequential over the chunks in reverse; holds the d_k x 16 slice of
+//     dS in fp32 MFMA accumulators, stores dS_{c+1} of every chunk and dS0.
+//   chunk_grad_kernel: one workgroup per (chunk, head, sequence), fully
+//     parallel; loops over d_v in tiles for every product that reduces over d_v
+//     (fp32 accumulators held across tiles), then the 64 x 64 and 64 x d_k
+//     stages, and writes dq, dk, dv, dg, dbeta.  Per-token sums are taken per
+//     wave and added in a fixed order, so the results are deterministic.
+//
+// Every product is a 16x16-block MFMA product whose operands are read from LDS
+// with the reduction index contiguous; a block is computed either as X or as
+// X^T so that its store to LDS or HBM is contiguous along the 4 accumulator
+// rows of a lane.  Precision as in the forward: bf16 io -> bf16 MFMA operands,
+// fp32 accumulation, fp32 states, decays, sums and dS; fp32 io -> fp32 MFMA.
+#include <type_traits>
+
+#include "gdn_chunk_common.h"
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+using namespace chunk;
+
+template <typename E>
+__device__ __forceinline__ u32x4_t ld16(const E* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+template <typename E>
+__device__ __forceinline__ void st16(E* p, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Element e of a 16-byte vector, as stored / widened to fp32.
+template <typename E>
+__device__ __forceinline__ E raw_elem(const u32x4_t& v, int e);
+template <>
+__device__ __forceinline__ uint16_t raw_elem<uint16_t>(const u32x4_t& v, int e) {
+  return static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+}
+template <>
+__device__ __forceinline__ float raw_elem<float>(const u32x4_t& v, int e) {
+  return __uint_as_float(v[e]);
+}
+template <typename E>
+__device__ __forceinline__ float wide_elem(const u32x4_t& v, int e);
+template <>
+__device__ __forceinline__ float wide_elem<uint16_t>(const u32x4_t& v, int e) {
+  return __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16));
+}
+template <>
+__device__ __forceinline__ float wide_elem<float>(const u32x4_t& v, int e) {
+  return __uint_as_float(v[e]);
+}
+
+template <typename E>
+__device__ __forceinline__ void store2(E* dst, float a, float b);
+template <>
+__device__ __forceinline__ void store2<uint16_t>(uint16_t* dst, float a, float b) {
+  *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a, b);
+}
+template <>
+__device__ __forceinline__ void store2<float>(float* dst, float a, float b) {
+  *reinterpret_cast<float2*>(dst) = float2{a, b};
+}
+
+// Store a 16x16 accumulator block C (C[4 (lane/16) + r][lane % 16] in element r)
+// transposed, dst[(lane % 16) * ld + 4 (lane/16) + r]: contiguous per lane.
+template <typename E>
+__device__ __forceinline__ void store_t(E* dst, int ld, const f32x4_t& c, int lane) {
+  store4<E>(dst + (lane & 15) * ld + 4 * (lane >> 4), c[0], c[1], c[2], c[3]);
+}
+// ... and as is, dst[(4 (lane/16) + r) * ld + lane % 16] (four scalar stores).
+template <typename E, typename Op>
+__device__ __forceinline__ void store_n(E* dst, int ld, const f32x4_t& c, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(4 * (lane >> 4) + r) * ld + (lane & 15)] = Op::cvt(c[r]);
+}
+
+// Sum over the four 16-lane groups: lanes l, l+16, l+32, l+48 all end with the total.
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+// Sum over the 16 lanes of a group: every lane of the group ends with the total.
+__device__ __forceinline__ float sum_in_group(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+template <int DK, typename Op>
+__device__ __forceinline__ void stage_gates(const BwdParams& p, int64_t row0, int nv, int h, int lane,
+                                            float* gam, float* Gam, float* dec, float* bet,
+                                            float* bg) {
+  // gamma by an in-register scan (log2 units); padded rows: g = 0, beta = 0
+  const bool ok = lane < nv;
+  const float gv = ok ? p.g[(row0 + lane) * p.H + h] : 0.f;
+  const float bv = ok ? p.beta[(row0 + lane) * p.H + h] : 0.f;
+  const float g2 = wave_inclusive_scan(gv * kLog2e, lane);
+  const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
+  const float G = exp2f(g2);
+  gam[lane] = g2;
+  Gam[lane] = G;
+  dec[lane] = exp2f(gl2 - g2);
+  if (bet) bet[lane] = bv;
+  bg[lane] = bv * G;
+}
+
+// ===================================================================================
+// Reverse state-gradient pass
+// ===================================================================================
+template <int DK, typename Op>
+struct DStateSmem {
+  using E = typename Op::elem;
+  static constexpr int PADE = sizeof(E) == 2 ? 8 : 4;
+  static constexpr int LDK = DK + PADE;   // rows of length d_k
+  static constexpr int LDC = 64 + PADE;   // rows of length 64
+  static constexpr int LDB = 128 + PADE;  // rows of length 128
+  E Ks[64 * LDK];   // K rows
+  E Qs[64 * LDK];   // Q rows
+  E Kt[DK * LDC];   // K^T
+  E Tm[64 * LDC];   // T rows
+  E Pt[64 * LDC];   // P^T
+  E QW[DK * LDB];   // [ (diag(Gamma) Q)^T | -W^T ]
+  E dB[16 * LDB];   // [ dOs^T | dE^T ] of this tile
+  E dSt[16 * LDK];  // dS^T of this tile
+  float gam[64], Gam[64], dec[64], bg[64];
+};
+
+template <int DK, typename Op>
+__global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
+  using E = typename Op::elem;
+  using SM = DStateSmem<DK, Op>;
+  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDB = SM::LDB, KS = Op::KSTEP;
+  constexpr int EPV = 16 / sizeof(E);
+  constexpr int SRB = DK / 64;  // 16-row blocks of dS per wave
+  extern __shared__ __align__(16) char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const E* __restrict__ q = static_cast<const E*>(p.q);
+  const E* __restrict__ k = static_cast<const E*>(p.k);
+  const E* __restrict__ dO = static_cast<const E*>(p.dO);
+  const E* __restrict__ tws = static_cast<const E*>(p.tws);
+
+  const int H = p.H, Dv = p.Dv, NT = Dv / 16;
+  const int NB = gridDim.x, L = blockIdx.x;
+  const int vb = (NB % 8 == 0) ? (L % 8) * (NB / 8) + L / 8 : L;  // tiles of a head share an XCD
+  const int tile = vb % NT, nh = vb / NT, h = nh % H, n = nh / H;
+  const int j0 = tile * 16;
+  int64_t bos, len;
+  seq_range(p.seq, n, bos, len);
+  const int nch = static_cast<int>((len + 63) / 64);
+  const int64_t slot0 = bos / 64 + n;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t nhS = (static_cast<int64_t>(n) * H + h) * DK;
+
+  // P^T: blocks below the diagonal stay zero
+  for (int x = tid; x < 64 * LDC; x += 256) {
+    const int r = x / LDC, c = x % LDC;
+    if ((c >> 4) < (r >> 4)) sm.Pt[x] = Op::cvt(0.f);
+  }
+  f32x4_t dS[SRB];
+#pragma unroll
+  for (int sr = 0; sr < SRB; ++sr) {
+    const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = p.dS_final ? p.dS_final[(nhS + i + r) * Dv + j0 + j] : 0.f;
+    dS[sr] = f32x4_t{x[0], x[1], x[2], x[3]};
+    store4<E>(sm.dSt + j * LDK + i, x[0], x[1], x[2], x[3]);
+  }
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t c0 = static_cast<int64_t>(c) * 64, row0 = bos + c0;
+    const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+    {  // dS_{c+1}, the gradient of the state after chunk c
+      float* dst = p.dstates + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv;
+#pragma unroll
+      for (int sr = 0; sr < SRB; ++sr) {
+        const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = dS[sr][r];
+      }
+    }
+    // ---- stage K, Q (rows), K^T, T and dOs^T of this tile ----
+    for (int x = tid; x < 64 * (DK / EPV); x += 256) {
+      const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      u32x4_t kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+      if (t < nv) {
+        kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
+        qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
+      }
+      st16(sm.Ks + t * LDK + cv, kv);
+      st16(sm.Qs + t * LDK + cv, qv);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) sm.Kt[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
+    }
+    {
+      const E* T = tws + ((slot0 + c) * H + h) * 4096;
+      for (int x = tid; x < 64 * 64 / EPV; x += 256) {
+        const int t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+        st16(sm.Tm + t * LDC + cv, ld16(T + t * 64 + cv));
+      }
+    }
+    {
+      const int t = tid >> 2, cq = (tid & 3) * 4;
+      float vals[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < nv) {
+        const E* src = dO + ((row0 + t) * H + h) * Dv + j0 + cq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = Op::widen(src[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * vals[e]);
+    }
+    if (w == 0) stage_gates<DK, Op>(p, row0, nv, h, lane, sm.gam, sm.Gam, sm.dec, nullptr, sm.bg);
+    __syncthreads();
+
+    // ---- (diag(Gamma) Q)^T, -W^T and P^T ----
+    for (int x = tid; x < 32 * (DK / EPV); x += 256) {
+      const int t = 2 * (x / (DK / EPV)), cv = (x % (DK / EPV)) * EPV;
+      const u32x4_t a = ld16(sm.Qs + t * LDK + cv), b = ld16(sm.Qs + (t + 1) * LDK + cv);
+      const float ga = sm.Gam[t], gb = sm.Gam[t + 1];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e)
+        store2<E>(sm.QW + (cv + e) * LDB + t, ga * wide_elem<E>(a, e), gb * wide_elem<E>(b, e));
+    }
+    for (int cb = w; cb < DK / 16; cb += 4) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        // W[16 rb + .][16 cb + .] = (T diag(beta Gamma)) K
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < tsteps<Op>(rb); ++ks)
+          acc = Op::mma(Op::scale(Op::frag(sm.Tm + 16 * rb * LDC, LDC, lane, ks * KS), sm.bg, lane, ks * KS),
+                        Op::frag(sm.Kt + 16 * cb * LDC, LDC, lane, ks * KS), acc);
+        store_t<E>(sm.QW + 16 * cb * LDB + 64 + 16 * rb, LDB, -acc, lane);
+      }
+    }
+    {
+      auto pblock = [&](int bi, int bt) {  // P[16 bi + .][16 bt + .] -> P^T
+        f32x4_t acc = zero4();
+        tile_mma<Op, DK>(acc, sm.Qs + 16 * bi * LDK, LDK, sm.Ks + 16 * bt * LDK, LDK, lane);
+        const int t = 16 * bt + (lane & 15), ib = 16 * bi + 4 * (lane >> 4);
+        const float gt = sm.gam[t];
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pv[r] = ib + r >= t ? acc[r] * exp2f(fminf(sm.gam[ib + r] - gt, 0.f)) : 0.f;
+        store4<E>(sm.Pt + t * LDC + ib, pv[0], pv[1], pv[2], pv[3]);
+      };
+      if (w == 0) {
+        pblock(0, 0); pblock(1, 0); pblock(1, 1);
+      } else if (w == 1) {
+        pblock(2, 0); pblock(2, 1); pblock(2, 2);
+      } else if (w == 2) {
+        pblock(3, 0); pblock(3, 1);
+      } else {
+        pblock(3, 2); pblock(3, 3);
+      }
+    }
+    __syncthreads();
+
+    // ---- dE = diag(decay) K dS + P^T dOs, token block w ----
+    {
+      f32x4_t acc = zero4();
+      tile_mma<Op, DK>(acc, sm.Ks + 16 * w * LDK, LDK, sm.dSt, LDK, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.dec[16 * w + 4 * (lane >> 4) + r];
+      for (int ks = (16 * w) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag(sm.Pt + 16 * w * LDC, LDC, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
+      store_t<E>(sm.dB + 64 + 16 * w, LDB, acc, lane);
+    }
+    __syncthreads();
+
+    // ---- dS <- Gamma_n dS + [(diag(Gamma) Q)^T | -W^T] [dOs ; dE] ----
+    {
+      const float gn = sm.Gam[63];
+#pragma unroll
+      for (int sr = 0; sr < SRB; ++sr) {
+        const int rb = w * SRB + sr;
+        f32x4_t acc = dS[sr] * gn;
+#pragma unroll
+        for (int ks = 0; ks < 128 / KS; ++ks)
+          acc = Op::mma(Op::frag(sm.QW + 16 * rb * LDB, LDB, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
+        dS[sr] = acc;
+        store_t<E>(sm.dSt + 16 * rb, LDK, acc, lane);
+      }
+    }
+    __syncthreads();
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int sr = 0; sr < SRB; ++sr) {
+      const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.dS0[(nhS + i + r) * Dv + j0 + j] = dS[sr][r];
+    }
+  }
+}
+
+// ===================================================================================
+// Per-chunk gradients
+// ===================================================================================
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// LDS plan (element offsets; E = io element type).  Persistent: K rows, T, T^T.
+// Region U is reused: first the pre-chunk products and the d_v tiles, then the
+// 64 x 64 / 64 x d_k stages.
+template <int DK, typename Op>
+struct GradLayout {
+  using E = typename Op::elem;
+  static constexpr int DVT = sizeof(E) == 2 ? 32 : 16;  // d_v tile (one bf16 MFMA depth)
+  static constexpr int PADE = sizeof(E) == 2 ? 8 : 4;
+  static constexpr int LDK = DK + PADE, LDC = 64 + PADE, LDV = DVT + PADE;
+  static constexpr int nK = 64 * LDK, nC = 64 * LDC, nKT = DK * LDC, nV = 64 * LDV;
+  static constexpr int nVT = DVT * LDC, nS = DK * LDV, nST = DVT * LDK;
+  static constexpr int oKs = 0, oTm = oKs + nK, oTt = oTm + nC, oU = oTt + nC;
+  // pre-chunk and d_v tiles
+  static constexpr int aWn = 0, aPt = aWn + nK, aTile = aPt + nC;
+  static constexpr int aKt = aTile, aQs = aKt + nKT, aPreEnd = aQs + nK;
+  static constexpr int aVt = aTile, aVr = aVt + nVT, aSt = aVr + nV, aSr = aSt + nST;
+  static constexpr int adSt = aSr + nS, adSr = adSt + nST, adOr = adSr + nS, adOt = adOr + nV;
+  static constexpr int aEr = adOt + nVT, adEr = aEr + nV, adEt = adEr + nV, aEnd = adEt + nVT;
+  // 64 x 64 and 64 x d_k stages
+  static constexpr int bQKr = 0, bQKt = bQKr + nC, bWt = bQKt + nC, bWr = bWt + nKT;
+  static constexpr int bTb = bWr + nK, bXt = bTb + nC, bEnd1 = bXt + nC;
+  static constexpr int bKtmp = bWr, bKKs = bWt, bQt = bWr, bKt2 = bQt + nKT, bEnd2 = bKt2 + nKT;
+  static constexpr int nU = cmax(cmax(aEnd, aPreEnd), cmax(bEnd1, bEnd2));
+  static constexpr int nElem = oU + nU;
+  static constexpr int fOff = (nElem * static_cast<int>(sizeof(E)) + 15) / 16 * 16;
+  // fp32 arrays: gam, Gam, dec, bet, bg [64]; pb, pg [8][64]; pn, sdot [8]
+  static constexpr int nFloat = 5 * 64 + 2 * 8 * 64 + 16;
+  static constexpr size_t bytes = static_cast<size_t>(fOff) + nFloat * 4;
+};
+
+template <int DK, typename Op>
+__global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
+  using E = typename Op::elem;
+  using GL = GradLayout<DK, Op>;
+  constexpr int LDK = GL::LDK, LDC = GL::LDC, LDV = GL::LDV, DVT = GL::DVT, KS = Op::KSTEP;
+  constexpr int EPV = 16 / sizeof(E);
+  constexpr int NKS = DK / 32;  // 64 x d_k blocks per wave (4 * DK / 16 over 8 waves)
+  constexpr int NBT = DVT / 16 * 4;  // (d_v, token) blocks of one tile
+  extern __shared__ __align__(16) char smem_raw[];
+  E* const base = reinterpret_cast<E*>(smem_raw);
+  E* const Ks = base + GL::oKs;
+  E* const Tm = base + GL::oTm;
+  E* const Tt = base + GL::oTt;
+  E* const U = base + GL::oU;
+  float* const fl = reinterpret_cast<float*>(smem_raw + GL::fOff);
+  float* const gam = fl;
+  float* const Gam = fl + 64;
+  float* const dec = fl + 128;
+  float* const bet = fl + 192;
+  float* const bg = fl + 256;
+  float* const pb = fl + 320;        // [8][64] per-wave partial dbeta
+  float* const pg = fl + 320 + 512;  // [8][64] per-wave partial dgamma
+  float* const pn = fl + 320 + 1024;      // [8] per-wave partial dgamma_n
+  float* const sdot = fl + 320 + 1024 + 8;  // [8] per-wave <dS_{c+1}, S_c>
+
+  const E* __restrict__ q = static_cast<const E*>(p.q);
+  const E* __restrict__ k = static_cast<const E*>(p.k);
+  const E* __restrict__ v = static_cast<const E*>(p.v);
+  const E* __restrict__ dO = static_cast<const E*>(p.dO);
+  const E* __restrict__ tws = static_cast<const E*>(p.tws);
+  E* __restrict__ dq = static_cast<E*>(p.dq);
+  E* __restrict__ dk = static_cast<E*>(p.dk);
+  E* __restrict__ dvo = static_cast<E*>(p.dv);
+
+  const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  const int H = p.H, Dv = p.Dv;
+  int64_t bos, len;
+  seq_range(p.seq, n, bos, len);
+  const int64_t c0 = static_cast<int64_t>(c) * 64;
+  if (c0 >= len) return;
+  const int64_t row0 = bos + c0;
+  const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+  const int64_t slot = bos / 64 + n + c;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const float* Sg = p.states + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+  const float* dSg = p.dstates + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+
+  // ---------------- stage K, Q, K^T, T, T^T; gates ----------------
+  E* const Wn = U + GL::aWn;
+  E* const Pt = U + GL::aPt;
+  {
+    E* const Kt = U + GL::aKt;
+    E* const Qs = U + GL::aQs;
+    for (int x = tid; x < 64 * (DK / EPV); x += 512) {
+      const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      u32x4_t kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+      if (t < nv) {
+        kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
+        qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
+      }
+      st16(Ks + t * LDK + cv, kv);
+      st16(Qs + t * LDK + cv, qv);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) Kt[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
+    }
+    const E* T = tws + (slot * H + h) * 4096;
+    for (int x = tid; x < 64 * 64 / EPV; x += 512) {
+      const int t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+      const u32x4_t tv = ld16(T + t * 64 + cv);
+      st16(Tm + t * LDC + cv, tv);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) Tt[(cv + e) * LDC + t] = raw_elem<E>(tv, e);
+    }
+    for (int x = tid; x < 64 * LDC; x += 512) {  // P^T: blocks below the diagonal are zero
+      const int r = x / LDC, cc = x % LDC;
+      if ((cc >> 4) < (r >> 4)) Pt[x] = Op::cvt(0.f);
+    }
+    for (int x = tid; x < 2 * 8 * 64 + 16; x += 512) pb[x] = 0.f;  // pb, pg, pn, sdot
+    if (w == 0) stage_gates<DK, Op>(p, row0, nv, h, lane, gam, Gam, dec, bet, bg);
+    __syncthreads();
+
+    // -W (rows t) from W^T = K^T (T diag(beta Gamma))^T; blocks (a: d_k, b: tokens)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+      f32x4_t acc = zero4();
+      for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
+        acc = Op::mma(Op::frag(Kt + 16 * a * LDC, LDC, lane, ks * KS),
+                      Op::scale(Op::frag(Tm + 16 * b * LDC, LDC, lane, ks * KS), bg, lane, ks * KS), acc);
+      store_t<E>(Wn + 16 * b * LDK + 16 * a, LDK, -acc, lane);
+    }
+  }
+  // Lower 16x16 blocks (bi >= bj) owned by this wave: blk w, and 8 + w for w < 2.
+  const int nlow = w < 2 ? 2 : 1;
+  int lbi[2], lbj[2];
+  lower_block(w, lbi[0], lbj[0]);
+  lower_block(w < 2 ? 8 + w : w, lbi[1], lbj[1]);
+  f32x4_t QKr[2], KKr[2];
+  {
+    const E* Qs = U + GL::aQs;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      QKr[s] = zero4();
+      KKr[s] = zero4();
+      if (s < nlow) {
+        const int bi = lbi[s], bj = lbj[s];
+        tile_mma<Op, DK>(QKr[s], Qs + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+        tile_mma<Op, DK>(KKr[s], Ks + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+        // P = lower_incl(QK o D) -> P^T
+        const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pv[r] = i0 + r >= j ? QKr[s][r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
+        store4<E>(Pt + j * LDC + i0, pv[0], pv[1], pv[2], pv[3]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- d_v tiles ----------------
+  f32x4_t dKtT[NKS], dQ6T[NKS], dWT[NKS], dP[2], dT1T[2];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) dKtT[s] = dQ6T[s] = dWT[s] = zero4();
+  dP[0] = dP[1] = dT1T[0] = dT1T[1] = zero4();
+  float sdot_acc = 0.f;
+  E* const Vt = U + GL::aVt;
+  E* const Vr = U + GL::aVr;
+  E* const St = U + GL::aSt;
+  E* const Sr = U + GL::aSr;
+  E* const dSt = U + GL::adSt;
+  E* const dSr = U + GL::adSr;
+  E* const dOr = U + GL::adOr;
+  E* const dOt = U + GL::adOt;
+  E* const Er = U + GL::aEr;
+  E* const dEr = U + GL::adEr;
+  E* const dEt = U + GL::adEt;
+  for (int v0 = 0; v0 < Dv; v0 += DVT) {
+    // stage V and dOs (rows and transposed), S_c and dS_{c+1} (rows and transposed)
+    for (int x = tid; x < 64 * (DVT / EPV); x += 512) {
+      const int t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
+      u32x4_t vv = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
+      if (t < nv && v0 + cv < Dv) {
+        vv = ld16(v + ((row0 + t) * H + h) * Dv + v0 + cv);
+        ov = ld16(dO + ((row0 + t) * H + h) * Dv + v0 + cv);
+      }
+      st16(Vr + t * LDV + cv, vv);
+      float os[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        Vt[(cv + e) * LDC + t] = raw_elem<E>(vv, e);
+        os[e] = p.scale * wide_elem<E>(ov, e);
+        const E oe = Op::cvt(os[e]);
+        dOt[(cv + e) * LDC + t] = oe;
+        dOr[t * LDV + cv + e] = oe;
+      }
+    }
+    for (int x = tid; x < DK * (DVT / 4); x += 512) {
+      const int i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
+      float4 sv = {0.f, 0.f, 0.f, 0.f}, dv4 = {0.f, 0.f, 0.f, 0.f};
+      if (v0 + cv < Dv) {
+        sv = *reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(i) * Dv + v0 + cv);
+        dv4 = *reinterpret_cast<const float4*>(dSg + static_cast<int64_t>(i) * Dv + v0 + cv);
+      }
+      sdot_acc += sv.x * dv4.x + sv.y * dv4.y + sv.z * dv4.z + sv.w * dv4.w;
+      store4<E>(Sr + i * LDV + cv, sv.x, sv.y, sv.z, sv.w);
+      store4<E>(dSr + i * LDV + cv, dv4.x, dv4.y, dv4.z, dv4.w);
+      const float s4[4] = {sv.x, sv.y, sv.z, sv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        St[(cv + e) * LDK + i] = Op::cvt(s4[e]);
+        dSt[(cv + e) * LDK + i] = Op::cvt(d4[e]);
+      }
+    }
+    __syncthreads();
+    // E^T and dE^T, block (bdv, bt) per wave
+    if (w < NBT) {
+      const int bdv = w >> 2, bt = w & 3;
+      f32x4_t e = zero4();
+      for (int ks = 0; ks < (16 * (bt + 1) + KS - 1) / KS; ++ks)
+        e = Op::mma(Op::frag(Vt + 16 * bdv * LDC, LDC, lane, ks * KS),
+                    Op::scale(Op::frag(Tm + 16 * bt * LDC, LDC, lane, ks * KS), bet, lane, ks * KS), e);
+      tile_mma<Op, DK>(e, St + 16 * bdv * LDK, LDK, Wn + 16 * bt * LDK, LDK, lane);
+      store_t<E>(Er + 16 * bt * LDV + 16 * bdv, LDV, e, lane);
+      f32x4_t de = zero4();
+      tile_mma<Op, DK>(de, dSt + 16 * bdv * LDK, LDK, Ks + 16 * bt * LDK, LDK, lane);
+      const float dc = dec[16 * bt + (lane & 15)];
+      de = de * dc;
+      for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
+        de = Op::mma(Op::frag(dOt + 16 * bdv * LDC, LDC, lane, ks * KS),
+                     Op::frag(Pt + 16 * bt * LDC, LDC, lane, ks * KS), de);
+      store_t<E>(dEr + 16 * bt * LDV + 16 * bdv, LDV, de, lane);
+      store_n<E, Op>(dEt + 16 * bdv * LDC + 16 * bt, LDC, de, lane);
+    }
+    __syncthreads();
+    // accumulate the d_v reductions
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+      tile_mma<Op, DVT>(dKtT[s], dSr + 16 * a * LDV, LDV, Er + 16 * b * LDV, LDV, lane);
+      tile_mma<Op, DVT>(dQ6T[s], Sr + 16 * a * LDV, LDV, dOr + 16 * b * LDV, LDV, lane);
+      tile_mma<Op, DVT>(dWT[s], Sr + 16 * a * LDV, LDV, dEr + 16 * b * LDV, LDV, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nlow) {
+        const int bi = lbi[s], bj = lbj[s];
+        tile_mma<Op, DVT>(dP[s], dOr + 16 * bi * LDV, LDV, Er + 16 * bj * LDV, LDV, lane);
+        tile_mma<Op, DVT>(dT1T[s], Vr + 16 * bj * LDV, LDV, dEr + 16 * bi * LDV, LDV, lane);
+      }
+    }
+    // dV^T block = (T^T dE)^T; dv = beta dVb; dbeta += rowsum(dVb o V)
+    if (w < NBT) {
+      const int bdv = w >> 2, bt = w & 3;
+      f32x4_t acc = zero4();
+      for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag(dEt + 16 * bdv * LDC, LDC, lane, ks * KS),
+                      Op::frag(Tt + 16 * bt * LDC, LDC, lane, ks * KS), acc);
+      const int t = 16 * bt + (lane & 15), cl = 16 * bdv + 4 * (lane >> 4);
+      const float bt_ = bet[t];
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += acc[r] * Op::widen(Vr[t * LDV + cl + r]);
+      part = sum_groups(part);
+      if (lane < 16) pb[w * 64 + t] += part;
+      if (t < nv && v0 + cl < Dv)
+        store4<E>(dvo + ((row0 + t) * H + h) * Dv + v0 + cl, bt_ * acc[0], bt_ * acc[1], bt_ * acc[2],
+                  bt_ * acc[3]);
+    }
+    __syncthreads();
+  }
+  sdot_acc = wave_sum(sdot_acc);
+  if (lane == 0) sdot[w] = sdot_acc;
+
+  // ---------------- 64 x 64 and 64 x d_k stages ----------------
+  E* const dQKr = U + GL::bQKr;
+  E* const dQKt = U + GL::bQKt;
+  E* const dWt = U + GL::bWt;
+  E* const dWr = U + GL::bWr;
+  E* const dTb = U + GL::bTb;
+  E* const Xt = U + GL::bXt;
+  // dW (rows and transposed); dQK = dP o D (rows and transposed); dD = dP o QK
+  f32x4_t dD[2];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+    const f32x4_t dw = -dWT[s];  // dW^T block (a, b)
+    store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, dw, lane);
+    store_n<E, Op>(dWt + 16 * a * LDC + 16 * b, LDC, dw, lane);
+  }
+  for (int x = tid; x < 64 * 64; x += 512) {  // zero the blocks no owner writes
+    const int r = x >> 6, cc = x & 63;
+    if ((cc >> 4) > (r >> 4)) {
+      dQKr[r * LDC + cc] = Op::cvt(0.f);
+      dTb[r * LDC + cc] = Op::cvt(0.f);
+    }
+    if ((cc >> 4) < (r >> 4)) dQKt[r * LDC + cc] = Op::cvt(0.f);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    dD[s] = zero4();
+    if (s < nlow) {
+      const int bi = lbi[s], bj = lbj[s];
+      const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
+      f32x4_t dqk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool on = i0 + r >= j;
+        const float d = on ? exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
+        dqk[r] = dP[s][r] * d;
+        dD[s][r] = on ? dP[s][r] * QKr[s][r] : 0.f;
+      }
+      store_n<E, Op>(dQKr + 16 * bi * LDC + 16 * bj, LDC, dqk, lane);
+      store_t<E>(dQKt + 16 * bj * LDC + 16 * bi, LDC, dqk, lane);
+    }
+  }
+  __syncthreads();
+  // dT^T = diag(beta) dT1^T + diag(beta Gamma) (K dW^T), strictly lower part of dT
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s < nlow) {
+      const int bi = lbi[s], bj = lbj[s];
+      f32x4_t acc = zero4();
+      tile_mma<Op, DK>(acc, Ks + 16 * bj * LDK, LDK, dWr + 16 * bi * LDK, LDK, lane);
+      const int j0 = 16 * bj + 4 * (lane >> 4), i = 16 * bi + (lane & 15);
+      f32x4_t dt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dt[r] = i > j0 + r ? bet[j0 + r] * dT1T[s][r] + bg[j0 + r] * acc[r] : 0.f;
+      store_t<E>(dTb + 16 * bi * LDC + 16 * bj, LDC, dt, lane);
+    }
+  }
+  __syncthreads();
+  // X = dT T^T (all 16 blocks, two per wave), stored transposed
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
+    f32x4_t acc = zero4();
+    const int kb = bk < bj ? bk : bj;
+    for (int ks = 0; ks < (16 * (kb + 1) + KS - 1) / KS; ++ks)
+      acc = Op::mma(Op::frag(dTb + 16 * bk * LDC, LDC, lane, ks * KS),
+                    Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
+    store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
+  }
+  __syncthreads();
+  // dA = strict_lower(-T^T X); dbeta, dKK, dD; dDD row and column sums.
+  // dKb^T = dW^T T (kept in registers for the final stage).
+  E* const dKtmp = U + GL::bKtmp;
+  f32x4_t dKbT[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+    dKbT[s] = zero4();
+    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+      dKbT[s] = Op::mma(Op::frag(dWt + 16 * a * LDC, LDC, lane, ks * KS),
+                        Op::frag(Tt + 16 * b * LDC, LDC, lane, ks * KS), dKbT[s]);
+  }
+  for (int x = tid; x < 64 * 64; x += 512) {
+    const int r = x >> 6, cc = x & 63;
+    if ((cc >> 4) > (r >> 4)) dKtmp[r * LDC + cc] = Op::cvt(0.f);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s < nlow) {
+      const int bi = lbi[s], bj = lbj[s];
+      f32x4_t acc = zero4();
+      for (int ks = (16 * bi) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag(Tt + 16 * bi * LDC, LDC, lane, ks * KS),
+                      Op::frag(Xt + 16 * bj * LDC, LDC, lane, ks * KS), acc);
+      const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
+      f32x4_t dkk;
+      float rows[4], colp = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        const bool lo = i > j;
+        const float d = i >= j ? exp2f(fminf(gam[i] - gam[j], 0.f)) : 0.f;
+        const float da = lo ? -acc[r] : 0.f;
+        const float b_i = bet[i];
+        const float kk = KKr[s][r];
+        rows[r] = da * kk * d;                 // dbeta_i
+        dkk[r] = da * b_i * d;                 // dKK
+        const float ddd = (dD[s][r] + da * b_i * kk) * d;  // dD o D
+        dD[s][r] = ddd;
+        colp += ddd;
+      }
+      store_n<E, Op>(dKtmp + 16 * bi * LDC + 16 * bj, LDC, dkk, lane);
+      // row sums over the 16 lanes of a group; column sums over the four groups
+      float rs[4], rd[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rs[r] = sum_in_group(rows[r]);
+        rd[r] = sum_in_group(dD[s][r]);
+      }
+      colp = sum_groups(colp);
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[w * 64 + i0 + r] += rs[r];
+          pg[w * 64 + i0 + r] += rd[r];
+        }
+      }
+      if (lane < 16) pg[w * 64 + j] -= colp;
+    }
+  }
+  __syncthreads();
+  E* const dKKs = U + GL::bKKs;
+  for (int x = tid; x < 64 * 64; x += 512) {
+    const int r = x >> 6, cc = x & 63;
+    dKKs[r * LDC + cc] = Op::cvt(Op::widen(dKtmp[r * LDC + cc]) + Op::widen(dKtmp[cc * LDC + r]));
+  }
+  __syncthreads();
+  E* const Qt = U + GL::bQt;
+  E* const Kt2 = U + GL::bKt2;
+  for (int x = tid; x < 64 * (DK / EPV); x += 512) {
+    const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+    u32x4_t qv = {0u, 0u, 0u, 0u};
+    if (t < nv) qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
+    const u32x4_t kv = ld16(Ks + t * LDK + cv);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      Qt[(cv + e) * LDC + t] = raw_elem<E>(qv, e);
+      Kt2[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
+    }
+  }
+  __syncthreads();
+  // dq^T, dk^T blocks (a: d_k, b: tokens) and the per-token terms they carry
+  float pn_acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+    const int t = 16 * b + (lane & 15), d0 = 16 * a + 4 * (lane >> 4);
+    // dq^T = Gamma o (dOs S_c^T)^T + K^T dQK^T
+    const f32x4_t q6 = dQ6T[s] * Gam[t];
+    f32x4_t dqa = q6;
+    for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
+      dqa = Op::mma(Op::frag(Kt2 + 16 * a * LDC, LDC, lane, ks * KS),
+                    Op::frag(dQKr + 16 * b * LDC, LDC, lane, ks * KS), dqa);
+    // dk^T = decay o dK~^T + Q^T dQK + K^T (dKK + dKK^T) + (beta Gamma) o dKb^T
+    f32x4_t dka = zero4();
+    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+      dka = Op::mma(Op::frag(Qt + 16 * a * LDC, LDC, lane, ks * KS),
+                    Op::frag(dQKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
+#pragma unroll
+    for (int ks = 0; ks < 64 / KS; ++ks)
+      dka = Op::mma(Op::frag(Kt2 + 16 * a * LDC, LDC, lane, ks * KS),
+                    Op::frag(dKKs + 16 * b * LDC, LDC, lane, ks * KS), dka);
+    const float dct = dec[t], bgt = bg[t];
+    float qd = 0.f, rk = 0.f, tj = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float kv = Op::widen(Ks[t * LDK + d0 + r]);
+      qd += Op::widen(Qt[(d0 + r) * LDC + t]) * q6[r];
+      rk += dKbT[s][r] * kv;
+      tj += dKtT[s][r] * dct * kv;
+      dka[r] += dct * dKtT[s][r] + bgt * dKbT[s][r];
+    }
+    qd = sum_groups(qd);
+    rk = sum_groups(rk);
+    tj = sum_groups(tj);
+    if (lane < 16) {
+      pg[w * 64 + t] += qd + bet[t] * Gam[t] * rk - tj;
+      pb[w * 64 + t] += Gam[t] * rk;
+      pn_acc += tj;
+    }
+    if (t < nv) {
+      store4<E>(dq + ((row0 + t) * H + h) * DK + d0, dqa[0], dqa[1], dqa[2], dqa[3]);
+      store4<E>(dk + ((row0 + t) * H + h) * DK + d0, dka[0], dka[1], dka[2], dka[3]);
+    }
+  }
+  pn_acc = wave_sum(pn_acc);
+  if (lane == 0) pn[w] = pn_acc;
+  __syncthreads();
+  if (w == 0) {
+    float db = 0.f, dgm = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      db += pb[x * 64 + lane];
+      dgm += pg[x * 64 + lane];
+    }
+    if (lane == 63) {
+      float sd = 0.f, sn = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        sd += sdot[x];
+        sn += pn[x];
+      }
+      dgm += Gam[63] * sd + sn;
+    }
+    // dg_t = sum of dgamma_u over u >= t: a forward scan of the reversed lanes
+    const float rev = __shfl(dgm, 63 - lane, 64);
+    const float sc = wave_inclusive_scan(rev, lane);
+    const float dgt = __shfl(sc, 63 - lane, 64);
+    if (lane < nv) {
+      p.dg[(row0 + lane) * H + h] = dgt;
+      p.dbeta[(row0 + lane) * H + h] = db;
+    }
+  }
+}
+
+template <int DK, typename Op>
+hipError_t launch_bwd_t(const BwdParams& b, hipStream_t s) {
+  constexpr size_t ds_smem = sizeof(DStateSmem<DK, Op>);
+  constexpr size_t gr_smem = GradLayout<DK, Op>::bytes;
+  static_assert(ds_smem <= 160 * 1024 && gr_smem <= 160 * 1024, "LDS budget exceeded");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_dstate_kernel<DK, Op>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ds_smem));
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_grad_kernel<DK, Op>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gr_smem));
+  if (e != hipSuccess) return e;
+  auto dstate = chunk_dstate_kernel<DK, Op>;
+  auto grad = chunk_grad_kernel<DK, Op>;
+  hipLaunchKernelGGL(dstate, dim3(b.N * b.H * (b.Dv / 16)), dim3(256), ds_smem, s, b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (b.max_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(grad, dim3(b.max_chunks, b.H, b.N), dim3(512), gr_smem, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bwd(const BwdParams& b, int Dk, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (Dk == 64) return launch_bwd_t<64, OpBf16>(b, s);
+    if (Dk == 128) return launch_bwd_t<128, OpBf16>(b, s);
+  } else {
+    if (Dk == 64) return launch_bwd_t<64, OpF32>(b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -39,63 +39,14 @@
 // runs every product on v_mfma_f32_16x16x4_f32 (IEEE fp32).
 #include <type_traits>
 
+#include "gdn_chunk_common.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ void seq_range(const SeqInfo& s, int n, int64_t& bos, int64_t& len) {
-  if (s.cu) {
-    bos = s.cu[n];
-    len = s.cu[n + 1] - bos;
-  } else {
-    bos = static_cast<int64_t>(n) * s.T;
-    len = s.T;
-  }
-}
-
-// Lower-triangular 16x16 block (bi >= bj) of a 4x4 block grid, by index 0..9.
-__device__ __forceinline__ void lower_block(int b, int& bi, int& bj) {
-  bi = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
-  bj = b - bi * (bi + 1) / 2;
-}
-
-// 16 bytes in four registers (a native vector type, so selects stay in registers)
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t u4_word(const u32x4_t& v, int i) { return v[i]; }
-
-// Element e of two row vectors a, b (16 bytes each), paired for a transposed
-// store: {a[e], b[e]}.  Register-only (e is a compile-time index after unrolling).
-template <typename E>
-struct Pair;
-template <>
-struct Pair<uint16_t> {
-  static __device__ __forceinline__ void store(uint16_t* dst, const u32x4_t& a, const u32x4_t& b, int e) {
-    const uint32_t wa = u4_word(a, e >> 1), wb = u4_word(b, e >> 1);
-    *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
-  }
-};
-template <>
-struct Pair<float> {
-  static __device__ __forceinline__ void store(float* dst, const u32x4_t& a, const u32x4_t& b, int e) {
-    *reinterpret_cast<uint2*>(dst) = uint2{u4_word(a, e), u4_word(b, e)};
-  }
-};
-
-template <typename E>
-__device__ __forceinline__ void store4(E* dst, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
-}
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(dst) = float4{a, b, c, d};
-}
+using namespace chunk;
 
 // ===================================================================================
 // Kernel 1: per-chunk T = (I + A)^-1
@@ -245,11 +196,6 @@ struct StateSmem {
   E Ett[16 * LDC];          // (diag(exp(gamma_n - gamma)) E)^T
 };
 
-template <typename Op>
-__host__ __device__ constexpr int tsteps(int ri) {  // k-steps covering T row block ri
-  return (16 * (ri + 1) + Op::KSTEP - 1) / Op::KSTEP;
-}
-
 template <int DK, typename Op>
 __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   using E = typename Op::elem;
@@ -359,6 +305,15 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         load_q(s + 1 < nch ? s + 1 : s);
       }
       if (s >= 1) {
+        if (p.states) {  // S_c, the state before chunk c, kept for the backward
+          float* dst = p.states + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv;
+#pragma unroll
+          for (int sr = 0; sr < SRB; ++sr) {
+            const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = Sacc[sr][r];
+          }
+        }
         // X = W S (rows of this wave), Y^T = S^T Q^T
         f32x4_t xacc = zero4();
 #pragma unroll
@@ -648,6 +603,36 @@ __global__ __launch_bounds__(256) void seg_carry_kernel(CarryParams c) {
 }
 
 template <int DK, typename Op>
+hipError_t set_fwd_attributes() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel<DK, Op>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(sizeof(PrepSmem<DK, Op>)));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_state_kernel<DK, Op>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(sizeof(StateSmem<DK, Op>)));
+}
+
+template <int DK, typename Op>
+hipError_t launch_states_t(const FwdParams& p, hipStream_t s) {
+  hipError_t e = set_fwd_attributes<DK, Op>();
+  if (e != hipSuccess) return e;
+  if (p.max_chunks == 0) return hipSuccess;
+  auto prep = chunk_prep_kernel<DK, Op>;
+  auto state = chunk_state_kernel<DK, Op>;
+  constexpr size_t prep_smem = sizeof(PrepSmem<DK, Op>);
+  constexpr size_t state_smem = sizeof(StateSmem<DK, Op>);
+  hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), prep_smem, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  FwdParams q = p;
+  q.G = 1; q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutNone;
+  q.zero_u = 0; q.ncol = p.Dv; q.carry = nullptr; q.seg_out = nullptr; q.final_to_sfinal = 0;
+  q.S_final = nullptr;
+  hipLaunchKernelGGL(state, dim3(p.N * p.H * (p.Dv / 16)), dim3(512), state_smem, s, q);
+  return hipGetLastError();
+}
+
+template <int DK, typename Op>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   constexpr size_t prep_smem = sizeof(PrepSmem<DK, Op>);
   constexpr size_t state_smem = sizeof(StateSmem<DK, Op>);
@@ -705,6 +690,16 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (Dk == 64) return launch_states_t<64, OpBf16>(p, s);
+    if (Dk == 128) return launch_states_t<128, OpBf16>(p, s);
+  } else {
+    if (Dk == 64) return launch_states_t<64, OpF32>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
   if (bf16) {

@@ -39,6 +39,7 @@ struct FwdParams {
   float* seg_out;      // [G][N][H][Dk][ncol] end states, or nullptr
   int32_t final_to_sfinal;  // segment G - 1 writes S_final (layout [N][H][Dk][Dv])
   float* seg_ws;       // G > 1: ends, starts ([G][N][H][Dk][Dv] each), maps ([G][N][H][Dk][Dk])
+  float* states;       // or nullptr: S_c before every chunk, [chunk slot][H][Dk][Dv] fp32
 };
 
 enum : int32_t { kStartS0 = 0, kStartZero = 1, kStartIdentity = 2, kStartCarry = 3 };
@@ -56,6 +57,29 @@ struct CarryParams {
 // sequence of len rows has at most floor((bos + len) / 64) - floor(bos / 64) + 1
 // chunks.  Total slots: floor(total_rows / 64) + N + 1.
 inline int64_t chunk_slots(int64_t total_rows, int64_t N) { return total_rows / 64 + N + 1; }
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const void* dO;
+  const float* dS_final;  // or nullptr (zero)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dS0;             // or nullptr (not wanted)
+  const void* tws;        // T of every chunk slot (io element type, 64 x 64)
+  const float* states;    // S_c before every chunk, [slot][H][Dk][Dv]
+  float* dstates;         // dS_{c+1} after every chunk, [slot][H][Dk][Dv]
+  SeqInfo seq;
+  int32_t N, H, Dv;
+  int32_t max_chunks;
+  float scale;
+};
 
 struct RecParams {
   const void* q;
@@ -86,12 +110,18 @@ constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backw
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
+// The T slots and the per-chunk states only (no outputs): the forward half of the
+// chunked backward.  Uses p.tws and p.states; G must be 1.
+hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
 // Bytes of forward workspace beyond the T slots for G segments (0 for G = 1).
 inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
   if (G <= 1) return 0;
   const size_t nh = static_cast<size_t>(G) * N * H * Dk;
   return (2 * nh * Dv + nh * Dk) * sizeof(float);
 }
+// Reverse state-gradient pass and per-chunk gradients; needs b.tws and b.states
+// filled by launch_chunk_fwd_states.
+hipError_t launch_chunk_bwd(const BwdParams& b, int Dk, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 

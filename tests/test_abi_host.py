@@ -149,8 +149,33 @@ def test_forward_pointer_checks():
 
 def test_backward_entry_validates():
     P = ctypes.c_void_p
+    lib = nat.load()
     z = [P(None)] * 15
-    assert nat.load().gdn_chunk_bwd(ctypes.byref(problem(chunk=16)), *z, 0, None) == nat.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem(chunk=16)), *z, 0, None) == nat.GDN_ERR_UNSUPPORTED
+    # the segment split is a forward-only option
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem(num_segments=2)), *z, 0, None) == nat.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem()), *z, 0, None) == nat.GDN_ERR_NULL
+    # q k v g beta S0 dO dS_final dq dk dv dg dbeta dS0 ws
+    ptrs = [P(FAKE + (i << 30)) for i in range(14)]
+    for i in (5, 7, 13):  # S0, dS_final, dS0 optional
+        ptrs[i] = P(None)
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem()), *ptrs, P(None), 0, None) == nat.GDN_ERR_WORKSPACE
+    bad = list(ptrs)
+    bad[8] = P(FAKE + (6 << 30) + 64)  # dq inside dO
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem()), *bad, P(None), 0, None) == nat.GDN_ERR_ALIAS
+    bad = list(ptrs)
+    bad[11] = P(FAKE + (11 << 30) + 2)  # misaligned dg
+    assert lib.gdn_chunk_bwd(ctypes.byref(problem()), *bad, P(None), 0, None) == nat.GDN_ERR_ALIGN
+
+
+def test_backward_workspace_size():
+    # inverses (io type), then fp32 states before and state gradients after every chunk slot
+    slots = 200 // 64 + 2 + 1
+    st, n = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
+    assert st == nat.GDN_OK
+    assert n == slots * 3 * 64 * 64 * 2 + 2 * slots * 3 * 128 * 96 * 4
+    assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
 
 
 def test_recurrent_backward_needs_workspace():
