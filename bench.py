@@ -49,6 +49,78 @@ def alg_flops(w) -> float:
     return th * per_th
 
 
+def bwd_alg_bytes(w, s_io: int) -> int:
+    """Reads q, k, v, dO, g, beta; writes dq, dk, dv, dg, dbeta; reads S0 and writes dS0."""
+    th = w.B * w.T * w.H
+    per_th = (2 * w.Dk + 2 * w.Dv) * s_io + 8 + (2 * w.Dk + w.Dv) * s_io + 8
+    return th * per_th + 2 * w.num_seqs * w.H * w.Dk * w.Dv * 4
+
+
+def event_times(call, n_calls, warmup, stream):
+    """Per-call durations (s) of `call(i)` from HIP events on `stream`."""
+    import torch
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_calls)]
+    for i in range(n_calls):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+
+
+def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
+    """Backward of the training shape and the segment split of the long sequence
+    (reported beside the headline forward number, not in it)."""
+    import torch
+
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    # backward, B=32 T=1024 H=16 d_k=64 d_v=128
+    w = WORKLOADS["fwdbwd_bf16"]
+    d = generate(w)
+    sets = []
+    for _ in range(2):
+        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v", "dO")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta", "S0")})
+        sets.append(t)
+
+    def bwd(i):
+        t = sets[i % len(sets)]
+        gdn.chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], S0=t["S0"], scale=d["scale"])
+
+    kt = event_times(bwd, steps, warmup, stream)
+    nb = bwd_alg_bytes(w, 2)
+    out["bwd"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3,
+                  "tokens_per_s": w.B * w.T / float(kt.mean()),
+                  "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
+                  "kernels": "prep + state (with per-chunk states) + chunk_dstate + chunk_grad"}
+    del sets
+    # segment split, B=1 T=65536 H=1 d=128
+    w = WORKLOADS["long_bf16"]
+    d = generate(w)
+    t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+    t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+    seg = {}
+    for G in (1, 2, 4, 8, 16):
+        ws = gdn.forward_workspace(t["q"], t["v"], None, G)
+        o = torch.empty_like(t["v"])
+        Sf = torch.empty((1, 1, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+        def fwd(i, G=G, ws=ws, o=o, Sf=Sf):
+            gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], num_segments=G,
+                          out=o, final_state_out=Sf, workspace=ws)
+
+        kt = event_times(fwd, max(5, steps // 4), 2, stream)
+        seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
+    out["segment_split"] = {"workload": w.name, "by_num_segments": seg}
+    return out
+
+
 def measured_traffic(workload: str):
     """HBM bytes per forward call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary, or None when the kernel source has changed since it was taken."""
@@ -74,6 +146,8 @@ def parse():
     ap.add_argument("--num-segments", type=int, default=1,
                     help="segments per sequence (1: serial over chunks; 2..16: segment split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the backward and segment-split measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--micro", choices=("copy", "gemm"), default=None,
@@ -243,6 +317,10 @@ def main():
                    "recurrence_tflops_6DkDv": w.B * w.T * w.H * 6 * w.Dk * w.Dv / k_mean / 1e12,
                    "token_heads_per_s": w.B * w.T * w.H / k_mean},
     }
+    if not args.no_extras and args.workload == "train_bf16":
+        print("[bench] extras: backward, segment split ...", file=sys.stderr, flush=True)
+        result["extras"].update(extra_measurements(gdn, generate, WORKLOADS, dev, args.steps,
+                                                   args.warmup))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds)

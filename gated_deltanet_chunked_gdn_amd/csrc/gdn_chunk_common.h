@@ -67,5 +67,33 @@ __host__ __device__ constexpr int tsteps(int ri) {  // k-steps covering T row bl
   return (16 * (ri + 1) + Op::KSTEP - 1) / Op::KSTEP;
 }
 
+// Buffer resource over `bytes` bytes at `base` (gfx9 raw buffer: stride 0, 32-bit
+// data format).  Stores at offsets past `bytes` are dropped by the hardware's
+// range check, which lets a loop store conditionally without branching; with
+// bytes = 0 every store is dropped and `base` is never dereferenced.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+typedef uint32_t u32x2v_t __attribute__((vector_size(8)));
+typedef uint32_t u32x4v_t __attribute__((vector_size(16)));
+template <typename E>
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float a, float b, float c,
+                                              float d);
+template <>
+__device__ __forceinline__ void buffer_store4<uint16_t>(__amdgpu_buffer_rsrc_t r, int off, float a, float b,
+                                                        float c, float d) {
+  const u32x2v_t v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void buffer_store4<float>(__amdgpu_buffer_rsrc_t r, int off, float a, float b,
+                                                     float c, float d) {
+  const u32x4v_t v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, int off, float a) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
+}
+
 }  // namespace chunk
 }  // namespace gdn

@@ -59,7 +59,8 @@ struct PrepSmem {
   static constexpr int LDF = 64 + 4;
   static constexpr int LDM = 20;
   E Ks[64 * LDK];
-  float Af[64 * LDF];
+  E Qs[64 * LDK];
+  float Af[64 * LDF];  // A, then P
   float Tf[64 * LDF];
   float Mt[4 * 16 * LDM];
   float gam[64], bet[64];
@@ -82,21 +83,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
   const int64_t row0 = bos + c0;
   const int64_t slot = bos / 64 + n + c;
-  E* Tout = static_cast<E*>(p.tws) + (slot * H + h) * 4096;
+  const int64_t moff = (slot * H + h) * 4096;
   const E* k = static_cast<const E*>(p.k);
+  const E* q = static_cast<const E*>(p.q);
+  const bool want_p = p.pws != nullptr;
 
   if (wave == 0) {
     const float gv = lane < nv ? p.g[(row0 + lane) * H + h] * kLog2e : 0.f;
-    sm.gam[lane] = wave_inclusive_scan(gv, lane);  // gamma * log2(e)
+    const float g2 = wave_inclusive_scan(gv, lane);  // gamma * log2(e)
+    sm.gam[lane] = g2;
+    if (p.gws) {  // Gamma and the decays to the chunk end, for the state pass
+      const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
+      float* gr = p.gws + (slot * H + h) * 128;
+      gr[lane] = exp2f(g2);
+      gr[64 + lane] = exp2f(gl2 - g2);
+    }
   } else if (wave == 1) {
     sm.bet[lane] = lane < nv ? p.beta[(row0 + lane) * H + h] : 0.f;
   }
   constexpr int VPR = DK / EPV;
   for (int x = tid; x < 64 * VPR; x += 256) {
     const int t = x / VPR, cc = x % VPR;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (t < nv) val = *reinterpret_cast<const uint4*>(k + ((row0 + t) * H + h) * DK + cc * EPV);
+    uint4 val = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (t < nv) {
+      val = *reinterpret_cast<const uint4*>(k + ((row0 + t) * H + h) * DK + cc * EPV);
+      if (want_p) qv = *reinterpret_cast<const uint4*>(q + ((row0 + t) * H + h) * DK + cc * EPV);
+    }
     *reinterpret_cast<uint4*>(sm.Ks + t * LDK + cc * EPV) = val;
+    if (want_p) *reinterpret_cast<uint4*>(sm.Qs + t * LDK + cc * EPV) = qv;
   }
   __syncthreads();
 
@@ -154,68 +168,111 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  // store T row-major, blocks above the diagonal as zeros
-  constexpr int VPT = 64 / EPV;
-  for (int x = tid; x < 64 * VPT; x += 256) {
-    const int i = x / VPT, jb = (x % VPT) * EPV;
-    E vals[EPV];
+  // P = lower_incl((Q K^T) o D) into Af (A is no longer needed)
+  if (want_p) {
+    for (int b = wave; b < 10; b += 4) {
+      int bi, bj;
+      lower_block(b, bi, bj);
+      f32x4_t acc = zero4();
+      tile_mma<Op, DK>(acc, sm.Qs + 16 * bi * LDK, LDK, sm.Ks + 16 * bj * LDK, LDK, lane);
 #pragma unroll
-    for (int m = 0; m < EPV; ++m) {
-      const int j = jb + m;
-      vals[m] = Op::cvt((j >> 4) <= (i >> 4) ? sm.Tf[i * LDF + j] : 0.f);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * bi + 4 * (lane >> 4) + r, j = 16 * bj + (lane & 15);
+        const float d = exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f));
+        sm.Af[i * LDF + j] = i >= j ? acc[r] * d : 0.f;
+      }
     }
-    *reinterpret_cast<uint4*>(Tout + i * 64 + jb) = *reinterpret_cast<const uint4*>(vals);
+    __syncthreads();
   }
+
+  // store T, T diag(beta) and P row-major (io type), blocks above the diagonal as zeros
+  constexpr int VPT = 64 / EPV;
+  auto store_mat = [&](E* dst, const float* src, bool by_beta) {
+    for (int x = tid; x < 64 * VPT; x += 256) {
+      const int i = x / VPT, jb = (x % VPT) * EPV;
+      E vals[EPV];
+#pragma unroll
+      for (int m = 0; m < EPV; ++m) {
+        const int j = jb + m;
+        const float t = (j >> 4) <= (i >> 4) ? src[i * LDF + j] : 0.f;
+        vals[m] = Op::cvt(by_beta ? t * sm.bet[j] : t);
+      }
+      *reinterpret_cast<uint4*>(dst + i * 64 + jb) = *reinterpret_cast<const uint4*>(vals);
+    }
+  };
+  if (p.tws) store_mat(static_cast<E*>(p.tws) + moff, sm.Tf, false);
+  if (p.tbws) store_mat(static_cast<E*>(p.tbws) + moff, sm.Tf, true);
+  if (want_p) store_mat(static_cast<E*>(p.pws) + moff, sm.Af, false);
 }
 
 // ===================================================================================
-// Kernel 2: the state pass with output, producer/consumer waves
+// Kernel 2: the state pass with output
 // ===================================================================================
+// Ring of per-chunk operands staged in LDS by the output waves (three chunks:
+// the one in use, the next one, and the one being written).
+constexpr int kRing = 3;
+
 template <int DK, typename Op>
 struct StateSmem {
   using E = typename Op::elem;
   static constexpr int PADE = sizeof(E) == 2 ? 8 : 4;
   static constexpr int LDK = DK + PADE;  // rows of length d_k
   static constexpr int LDC = 64 + PADE;  // rows of length 64 (one chunk)
-  // producer -> consumer
-  E Ws[64 * LDK];           // W, token-major (consumers read it before the mid barrier)
-  E Pm[64 * LDC];           // P, row-major; upper blocks stay zero
-  E Kt[2][DK * LDC];        // K^T, d_k-major (consumers read it after the mid barrier)
-  float Us[4 * 64 * 4];     // U in the consumers' accumulator order [row block][lane][r]
-  float Gam[2][64];         // exp(gamma)
-  float Dec[2][64];         // exp(gamma_n - gamma)
-  // producer private
-  E Ks[64 * LDK];           // K, token-major
-  E Qs[2][64 * LDK];        // Q, token-major: staged by the consumers one chunk ahead
-  E Vt[16 * LDC];           // V tile transposed
-  E Tm[64 * LDC];           // T of the chunk being prepared (row-major, upper blocks zero)
-  float gam[64], bg[64], bet[64];
-  // consumer private
-  E St[16 * LDK];           // S^T (16 columns x d_k)
-  E Et[16 * LDC];           // E^T
-  E Ett[16 * LDC];          // (diag(exp(gamma_n - gamma)) E)^T
+  static constexpr int LDR = 16 + PADE;  // rows of length 16 (one tile)
+  E Ks[kRing][64 * LDK];  // K rows of a chunk (padded tokens as zeros)
+  E Tb[kRing][64 * LDC];  // T diag(beta) of a chunk
+  E Vs[kRing][64 * 16];   // the v tile of a chunk
+  float Gs[kRing][128];   // Gamma and exp(gamma_n - gamma) of a chunk
+  E Sb[16 * LDK];         // S^T of this tile as an MFMA operand, [j][d_k]
+  E Rr[64 * LDR];         // R = V - diag(Gamma) K S, [t][j]
+  E Et[16 * LDC];         // E^T
+  E Ett[16 * LDC];        // (diag(exp(gamma_n - gamma)) E)^T
 };
 
-template <int DK, typename Op>
+// Four consecutive io values, widened when used.
+template <typename E>
+struct Raw4;
+template <>
+struct Raw4<uint16_t> {
+  uint2 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint2*>(p) = u; }
+  __device__ __forceinline__ float operator[](int r) const {
+    const uint32_t w = r < 2 ? u.x : u.y;
+    return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct Raw4<float> {
+  float4 u;
+  __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<float4*>(p) = u; }
+  __device__ __forceinline__ float operator[](int r) const {
+    return r == 0 ? u.x : r == 1 ? u.y : r == 2 ? u.z : u.w;
+  }
+};
+
+// STATES: also store S_c before every chunk (the backward's forward half).
+// OUT: compute and store the output (stores are further masked per segment).
+template <int DK, typename Op, bool STATES, bool OUT>
 __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   using E = typename Op::elem;
   using F = typename Op::frag_t;
   using SM = StateSmem<DK, Op>;
-  constexpr int LDK = SM::LDK, LDC = SM::LDC;
-  constexpr int KS = Op::KSTEP;
-  constexpr int NKQ = DK / KS;               // k-steps over d_k
-  constexpr int SRB = DK / 64;               // 16-row blocks of S per consumer wave
-  constexpr int EPV = 16 / static_cast<int>(sizeof(E));
-  constexpr int EPT = DK / 8;                // k/q elements per producer thread per token
-  constexpr int UPT = EPT / EPV;             // 16-byte vectors per token
-  constexpr int NVS = 16 / EPV;              // 16-byte vectors per row of a v tile
-  static_assert(EPT % EPV == 0, "thread slice must be whole vectors");
+  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDR = SM::LDR, KS = Op::KSTEP, KPL = Op::KPL;
+  constexpr int NKK = DK / KS;  // k-steps over d_k
+  constexpr int NTS = 64 / KS;  // k-steps over one chunk
+  constexpr int DPW = DK / 64;  // 16-row blocks of S per state wave
   extern __shared__ __align__(16) char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const E* __restrict__ q = static_cast<const E*>(p.q);
+  const E* __restrict__ k = static_cast<const E*>(p.k);
+  const E* __restrict__ v = static_cast<const E*>(p.v);
+  const E* __restrict__ tbw = static_cast<const E*>(p.tbws);
+  const E* __restrict__ pw = static_cast<const E*>(p.pws);
+  const float* __restrict__ gw = p.gws;
+  E* __restrict__ o = static_cast<E*>(p.o);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool consumer = wave < 4;
-  const int w = wave & 3;
   const int H = p.H, Dv = p.Dv, NC = p.ncol, NT = NC / 16;
   // XCD-aware block order: consecutive virtual blocks (the tiles of one head)
   // land on the same XCD, which the hardware picks as blockIdx % 8.
@@ -232,332 +289,228 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   const int cb = min(seg * seg_len, nch_all);
   const int nch = min(cb + seg_len, nch_all) - cb;
   const int64_t slot0 = bos / 64 + n + cb;
-  const bool write_o = p.write_o == kOutAll || (p.write_o == kOutSeg0 && seg == 0);
+  const bool store_o = p.write_o == kOutAll || (p.write_o == kOutSeg0 && seg == 0);
   const bool use_v = !p.zero_u;
-  const E* q = static_cast<const E*>(p.q);
-  const E* k = static_cast<const E*>(p.k);
-  const E* v = static_cast<const E*>(p.v);
-  const E* tws = static_cast<const E*>(p.tws);
-  E* o = static_cast<E*>(p.o);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wr = w & 3, lr = lane & 15, lg = lane >> 4;
+  const int tc = 16 * wr + lr;  // this lane's token row / column
+  const bool state_wave = w < 4;
   const int64_t nhS = (static_cast<int64_t>(n) * H + h) * DK;
   const int64_t segS = (static_cast<int64_t>(seg) * p.N * H + nh) * DK;  // [G][N][H][DK][NC] buffers
 
-  // upper blocks of P are never written
-  for (int x = tid; x < 64 * LDC; x += 512) {
-    const int i = x / LDC, j = x % LDC;
-    if ((j >> 4) > (i >> 4)) sm.Pm[x] = Op::cvt(0.f);
-  }
+  auto chunk_rows = [&](int c) {  // valid rows of chunk c
+    const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
+    return static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+  };
+  // Rows past the end of the sequence repeat its last row (every load stays in
+  // bounds); K rows of padded tokens are staged as zeros, R rows are zeroed and
+  // output rows are not stored, so padded tokens never reach a result.
+  auto row_of = [&](int c, int t) { return bos + static_cast<int64_t>(cb + c) * 64 + min(t, chunk_rows(c) - 1); };
+  auto clampc = [&](int c) { return c < nch ? c : nch - 1; };
 
-  if (consumer) {
-    // ===================== consumers: the state recurrence =====================
-    // Besides the recurrence of chunk s-1, the consumers stage Q of chunk s
-    // (first half) and compute its causal score P (second half).
-    f32x4_t Sacc[SRB];
-    const int tp = tid & 31, ds = tid >> 5;
-    u32x4_t qreg[2 * UPT];
-    auto load_q = [&](int c) {  // rows of Q of chunk c (clamped into the sequence)
-      const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
-      const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+  f32x4_t Sacc[DPW];
+  if (state_wave) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const E* qr = q + ((bos + c0 + min(2 * tp + tt, nv - 1)) * H + h) * DK + ds * EPT;
-#pragma unroll
-        for (int u = 0; u < UPT; ++u) qreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(qr + u * EPV);
-      }
-    };
-    if (nch > 0 && write_o) load_q(0);
-#pragma unroll
-    for (int sr = 0; sr < SRB; ++sr) {
-      const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
-      float x[4];
+    for (int x = 0; x < DPW; ++x) {
+      const int i = 16 * (wr * DPW + x) + 4 * lg;
+      float s4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (p.start_mode == kStartCarry)
-          x[r] = p.carry[(segS + i + r) * NC + j0 + j];
+          s4[r] = p.carry[(segS + i + r) * NC + j0 + lr];
         else if (p.start_mode == kStartIdentity)
-          x[r] = i + r == j0 + j ? 1.f : 0.f;
+          s4[r] = i + r == j0 + lr ? 1.f : 0.f;
         else if (p.start_mode == kStartS0 && seg == 0 && p.S0)
-          x[r] = p.S0[(nhS + i + r) * Dv + j0 + j];
+          s4[r] = p.S0[(nhS + i + r) * Dv + j0 + lr];
         else
-          x[r] = 0.f;
+          s4[r] = 0.f;
       }
-      Sacc[sr] = f32x4_t{x[0], x[1], x[2], x[3]};
-      store4<E>(sm.St + j * LDK + i, x[0], x[1], x[2], x[3]);
+      Sacc[x] = f32x4_t{s4[0], s4[1], s4[2], s4[3]};
+      store4<E>(sm.Sb + lr * LDK + i, s4[0], s4[1], s4[2], s4[3]);
     }
-    __syncthreads();
-    for (int s = 0; s <= nch; ++s) {
-      f32x4_t yacc = zero4();
-      F pf[tsteps<Op>(3)];
-      float gam_o = 0.f, gam_n = 0.f;
-      const int c = s - 1, b = c & 1;
-      if (s < nch && write_o) {  // stage Q of chunk s, padded rows as zeros; prefetch the next
-        const int64_t cs0 = static_cast<int64_t>(cb + s) * 64;
-        const int nv = static_cast<int>(len - cs0 < 64 ? len - cs0 : 64);
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * tp + tt;
-#pragma unroll
-          for (int u = 0; u < UPT; ++u)
-            *reinterpret_cast<u32x4_t*>(sm.Qs[s & 1] + t * LDK + ds * EPT + u * EPV) =
-                t < nv ? qreg[tt * UPT + u] : z;
-        }
-        load_q(s + 1 < nch ? s + 1 : s);
-      }
-      if (s >= 1) {
-        if (p.states) {  // S_c, the state before chunk c, kept for the backward
-          float* dst = p.states + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv;
-#pragma unroll
-          for (int sr = 0; sr < SRB; ++sr) {
-            const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = Sacc[sr][r];
-          }
-        }
-        // X = W S (rows of this wave), Y^T = S^T Q^T
-        f32x4_t xacc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKQ; ++ks) {
-          const F st = Op::frag(sm.St, LDK, lane, ks * KS);
-          xacc = Op::mma(Op::frag(sm.Ws + 16 * w * LDK, LDK, lane, ks * KS), st, xacc);
-          if (write_o) yacc = Op::mma(st, Op::frag(sm.Qs[b] + 16 * w * LDK, LDK, lane, ks * KS), yacc);
-        }
-        // E = U - X; E^T and the decayed E^T go to LDS for every consumer
-        const float4 u = use_v ? *reinterpret_cast<const float4*>(sm.Us + (w * 64 + lane) * 4)
-                               : float4{0.f, 0.f, 0.f, 0.f};
-        const float uu[4] = {u.x, u.y, u.z, u.w};
-        const int t0 = 16 * w + 4 * (lane >> 4), j = lane & 15;
-        float e[4], ed[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = uu[r] - xacc[r];
-          ed[r] = e[r] * sm.Dec[b][t0 + r];
-        }
-        store4<E>(sm.Et + j * LDC + t0, e[0], e[1], e[2], e[3]);
-        store4<E>(sm.Ett + j * LDC + t0, ed[0], ed[1], ed[2], ed[3]);
-        // this wave's rows of P and the decays it needs after the barrier
-#pragma unroll
-        for (int ks = 0; ks < tsteps<Op>(3); ++ks)
-          pf[ks] = write_o && ks < tsteps<Op>(w) ? Op::frag(sm.Pm + 16 * w * LDC, LDC, lane, ks * KS) : F{};
-        gam_o = sm.Gam[b][16 * w + (lane & 15)];
-        gam_n = sm.Gam[b][63];
-      }
-      __syncthreads();
-      if (s >= 1) {
-        const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
-        const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
-        // O^T = E^T P^T + Y^T scaled by Gamma  (rows j, columns t)
-        f32x4_t oacc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < tsteps<Op>(3); ++ks)
-          oacc = Op::mma(Op::frag(sm.Et, LDC, lane, ks * KS), pf[ks], oacc);
-        const int t = 16 * w + (lane & 15), jj = 4 * (lane >> 4);
-        if (write_o && t < nv) {
-          E* dst = o + ((bos + c0 + t) * H + h) * Dv + j0 + jj;
-          store4<E>(dst, p.scale * (gam_o * yacc[0] + oacc[0]), p.scale * (gam_o * yacc[1] + oacc[1]),
-                    p.scale * (gam_o * yacc[2] + oacc[2]), p.scale * (gam_o * yacc[3] + oacc[3]));
-        }
-        // S <- Gamma_n S + K^T (decayed E)
-#pragma unroll
-        for (int sr = 0; sr < SRB; ++sr) {
-          const int sb = w * SRB + sr;
-          f32x4_t acc = Sacc[sr] * gam_n;
-#pragma unroll
-          for (int ks = 0; ks < 64 / KS; ++ks)
-            acc = Op::mma(Op::frag(sm.Kt[b] + 16 * sb * LDC, LDC, lane, ks * KS),
-                          Op::frag(sm.Ett, LDC, lane, ks * KS), acc);
-          Sacc[sr] = acc;
-          store4<E>(sm.St + (lane & 15) * LDK + 16 * sb + 4 * (lane >> 4), acc[0], acc[1], acc[2], acc[3]);
-        }
-      }
-      if (s < nch && write_o) {
-        // P = lower_incl(Q K^T o D) of chunk s, computed transposed so rows of P
-        // store contiguously.  Blocks (bi, bj) by wave:
-        //   0: (0,0) (1,0) (1,1)   1: (2,0) (2,1) (2,2)   2: (3,0) (3,1)   3: (3,2) (3,3)
-        const int bq = s & 1;
-        auto pblock = [&](int bi, int bj) {
-          f32x4_t acc = zero4();
-          tile_mma<Op, DK>(acc, sm.Ks + 16 * bj * LDK, LDK, sm.Qs[bq] + 16 * bi * LDK, LDK, lane);
-          const int i = 16 * bi + (lane & 15), jb = 16 * bj + 4 * (lane >> 4);
-          const float gi = sm.gam[i];
-          const float4 gj = *reinterpret_cast<const float4*>(sm.gam + jb);
-          const float gjj[4] = {gj.x, gj.y, gj.z, gj.w};
-          float pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float d = exp2f(fminf(gi - gjj[r], 0.f));
-            pv[r] = jb + r <= i ? acc[r] * d : 0.f;
-          }
-          store4<E>(sm.Pm + i * LDC + jb, pv[0], pv[1], pv[2], pv[3]);
-        };
-        if (w == 0) {
-          pblock(0, 0); pblock(1, 0); pblock(1, 1);
-        } else if (w == 1) {
-          pblock(2, 0); pblock(2, 1); pblock(2, 2);
-        } else if (w == 2) {
-          pblock(3, 0); pblock(3, 1);
-        } else {
-          pblock(3, 2); pblock(3, 3);
-        }
-      }
-      __syncthreads();
-    }
+  }
+  auto write_state = [&](void) {
     const bool to_final = p.final_to_sfinal && seg == p.G - 1;
     if (to_final ? p.S_final != nullptr : p.seg_out != nullptr) {
 #pragma unroll
-      for (int sr = 0; sr < SRB; ++sr) {
-        const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+      for (int x = 0; x < DPW; ++x) {
+        const int i = 16 * (wr * DPW + x) + 4 * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (to_final)
-            p.S_final[(nhS + i + r) * Dv + j0 + j] = Sacc[sr][r];
+            p.S_final[(nhS + i + r) * Dv + j0 + lr] = Sacc[x][r];
           else
-            p.seg_out[(segS + i + r) * NC + j0 + j] = Sacc[sr][r];
+            p.seg_out[(segS + i + r) * NC + j0 + lr] = Sacc[x][r];
         }
       }
     }
+  };
+  if (nch == 0) {  // empty segment (uniform over the workgroup): the state passes through
+    if (state_wave) write_state();
+    return;
+  }
+  // The chunk loop is unrolled by the ring size and has no tail branch: steps
+  // past the last chunk run on clamped data and change nothing.  Straight-line
+  // bodies let the compiler wait for exactly the loads each step consumes.
+  const int nsteps = (nch + kRing - 1) / kRing * kRing;
+
+  if (state_wave) {
+    // ===================== state waves: the recurrence (LDS and MFMA only) =====================
+    __syncthreads();  // chunk 0 staged
+    int c0 = 0;
+    do {
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) {
+        const int c = c0 + u;
+        const bool active = c < nch;
+        const E* Ks = sm.Ks[u];
+        const float* Gs = sm.Gs[u];
+        // phase 1: R = V - Gamma o (K S), via Z^T = S^T K^T (rows j, column tc)
+        if (STATES) {  // S_c, the state before chunk c, kept for the backward
+          const auto rs = buffer_rsrc(p.states + ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
+                                      active ? DK * Dv * 4 : 0);
+#pragma unroll
+          for (int x = 0; x < DPW; ++x) {
+            const int i = 16 * (wr * DPW + x) + 4 * lg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) buffer_store1(rs, ((i + r) * Dv + j0 + lr) * 4, Sacc[x][r]);
+          }
+        }
+        f32x4_t z = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks)
+          z = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), Op::frag(Ks + 16 * wr * LDK, LDK, lane, ks * KS), z);
+        Raw4<E> vv;
+        vv.load(sm.Vs[u] + tc * 16 + 4 * lg);
+        const float gt = Gs[tc];
+        const bool real = tc < chunk_rows(clampc(c));
+        float rr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rr[r] = real ? (use_v ? vv[r] : 0.f) - gt * z[r] : 0.f;
+        store4<E>(sm.Rr + tc * LDR + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
+        __syncthreads();
+        // phase 2: E = (T diag(beta)) R
+        f32x4_t e = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NTS; ++ks)
+          e = Op::mma(Op::frag(sm.Tb[u] + 16 * wr * LDC, LDC, lane, ks * KS), Op::frag_tr(sm.Rr, LDR, lane, ks * KS), e);
+        const int t0 = 16 * wr + 4 * lg;
+        const float4 dc = *reinterpret_cast<const float4*>(Gs + 64 + t0);
+        store4<E>(sm.Et + lr * LDC + t0, e[0], e[1], e[2], e[3]);
+        store4<E>(sm.Ett + lr * LDC + t0, e[0] * dc.x, e[1] * dc.y, e[2] * dc.z, e[3] * dc.w);
+        __syncthreads();
+        // phase 3: S <- Gamma_n S + K^T (decayed E)
+        const float gn = Gs[63];
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+          const int db = wr * DPW + x;
+          f32x4_t acc = Sacc[x] * gn;
+#pragma unroll
+          for (int ks = 0; ks < NTS; ++ks)
+            acc = Op::mma(Op::frag_tr(Ks + 16 * db, LDK, lane, ks * KS), Op::frag(sm.Ett, LDC, lane, ks * KS), acc);
+          Sacc[x] = active ? acc : Sacc[x];
+          store4<E>(sm.Sb + lr * LDK + 16 * db + 4 * lg, Sacc[x][0], Sacc[x][1], Sacc[x][2], Sacc[x][3]);
+        }
+        __syncthreads();
+      }
+      c0 += kRing;
+    } while (c0 < nsteps);
+    write_state();
   } else {
-    // ===================== producers: chunk c+1 while consumers run chunk c =====================
-    // Prefetches are issued one chunk ahead and unconditionally (rows clamped
-    // into the sequence, padded rows zeroed when used), so the compiler can wait
-    // for exactly the loads it needs.
-    const int ptid = tid - 256, tp = ptid & 31, ds = ptid >> 5;
-    u32x4_t kreg[2 * UPT], vreg[2];
-    float greg = 0.f, breg = 0.f;
-    // W and U work split by row blocks of T: waves 0, 1 take row blocks {0, 3},
-    // waves 2, 3 take {1, 2} (three k-steps each), each wave half of W's columns.
-    constexpr int TS = tsteps<Op>(3);
-    constexpr int TPT = 64 * 64 / 256 / EPV;  // 16-byte vectors of T per producer thread
-    u32x4_t treg[TPT];
-    auto for_rowblocks = [&](auto&& fn) {  // fn(integral_constant<R0>, integral_constant<R1>)
-      if (w < 2)
-        fn(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
-      else
-        fn(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    // ===================== output waves: staging, and O = Gamma o (Q S) + P E =====================
+    // Staged operands of chunk c (rows tc): loaded two steps before they are
+    // written to LDS, which is one step before the state waves read them.
+    struct Stage {
+      u32x4_t kv[DK * static_cast<int>(sizeof(E)) / 64];  // K row tc (KPL-wide fragments)
+      u32x4_t tv[64 * static_cast<int>(sizeof(E)) / 64];  // T diag(beta) row tc
+      Raw4<E> vv;                                         // v[tc][j0 + 4 lg .. + 3]
+      float2 gv;                                          // decays (wave 4 only)
     };
-    auto load_chunk = [&](int c) {  // raw rows of chunk c and its T into registers
-      const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
-      const int64_t row0 = bos + c0;
-      const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+    constexpr int NKV = DK * static_cast<int>(sizeof(E)) / 64;
+    constexpr int NTV = 64 * static_cast<int>(sizeof(E)) / 64;
+    Stage stg[kRing];
+    F qf[kRing][NKK], pf[kRing][NTS];
+    auto load_stage = [&](Stage& st, int c) {
+      const E* krow = k + (row_of(c, tc) * H + h) * DK;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = min(2 * tp + tt, nv - 1);
-        const E* kr = k + ((row0 + t) * H + h) * DK + ds * EPT;
+      for (int x = 0; x < NKV; ++x) st.kv[x] = *reinterpret_cast<const u32x4_t*>(krow + (x * 4 + lg) * (16 / sizeof(E)));
+      const E* trow = tbw + ((slot0 + c) * H + h) * 4096 + tc * 64;
 #pragma unroll
-        for (int u = 0; u < UPT; ++u) kreg[tt * UPT + u] = *reinterpret_cast<const u32x4_t*>(kr + u * EPV);
-        if (use_v && w < NVS / 2)  // wave-uniform: the threads that store the v tile
-          vreg[tt] = *reinterpret_cast<const u32x4_t*>(v + ((row0 + t) * H + h) * Dv + j0 + ds * EPV);
-      }
-      if (w == 0) {
-        const int tl = min(lane, nv - 1);
-        greg = p.g[(row0 + tl) * H + h];
-        breg = p.beta[(row0 + tl) * H + h];
-      }
-      const E* T = tws + ((slot0 + c) * H + h) * 4096 + ptid * TPT * EPV;
-#pragma unroll
-      for (int x = 0; x < TPT; ++x) treg[x] = *reinterpret_cast<const u32x4_t*>(T + x * EPV);
+      for (int x = 0; x < NTV; ++x) st.tv[x] = *reinterpret_cast<const u32x4_t*>(trow + (x * 4 + lg) * (16 / sizeof(E)));
+      // (a pass without V still loads, from a column clamped into the row, and discards it)
+      st.vv.load(v + (row_of(c, tc) * H + h) * Dv + min(j0 + 4 * lg, Dv - 4));
+      st.gv = *reinterpret_cast<const float2*>(gw + ((slot0 + c) * H + h) * 128 + 2 * lane);
     };
-    // One pipeline step: stage chunk s in LDS (first half), then build its W, U
-    // and P (second half).  Every prefetched register is consumed in the first
-    // half, before the next chunk's loads are issued into it, so the loads stay
-    // in flight across a whole step.
-    auto step = [&](int s) {
-      const int b = s & 1;
-      if (s < nch) {
-        const int64_t c0 = static_cast<int64_t>(cb + s) * 64;
-        const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        // rows of chunk s: K, Q token-major; K^T; V^T (padded rows as zeros)
+    auto write_stage = [&](const Stage& st, int c, int slot) {
+      const bool real = tc < chunk_rows(c);
+      const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * tp + tt;
-          const bool ok = t < nv;
+      for (int x = 0; x < NKV; ++x)
+        *reinterpret_cast<u32x4_t*>(sm.Ks[slot] + tc * LDK + (x * 4 + lg) * (16 / sizeof(E))) = real ? st.kv[x] : z;
 #pragma unroll
-          for (int u = 0; u < UPT; ++u) {
-            kreg[tt * UPT + u] = ok ? kreg[tt * UPT + u] : z;
-            *reinterpret_cast<u32x4_t*>(sm.Ks + t * LDK + ds * EPT + u * EPV) = kreg[tt * UPT + u];
-          }
-          vreg[tt] = ok ? vreg[tt] : z;
-        }
-        {
-          E* kt = sm.Kt[b] + (ds * EPT) * LDC + 2 * tp;
-#pragma unroll
-          for (int e = 0; e < EPT; ++e)
-            Pair<E>::store(kt + e * LDC, kreg[e / EPV], kreg[UPT + e / EPV], e % EPV);
-        }
-        if (ptid < 32 * NVS) {
-          E* vt = sm.Vt + (ds * EPV) * LDC + 2 * tp;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) Pair<E>::store(vt + e * LDC, vreg[0], vreg[1], e);
-        }
-#pragma unroll
-        for (int x = 0; x < TPT; ++x) {
-          const int e0 = (ptid * TPT + x) * EPV;  // element of the 64 x 64 T
-          *reinterpret_cast<u32x4_t*>(sm.Tm + (e0 / 64) * LDC + e0 % 64) = treg[x];
-        }
-        if (w == 0) {
-          // gamma by an in-register scan; decays as exp2 of log2(e)-scaled values
-          const bool ok = lane < nv;
-          const float g2 = wave_inclusive_scan(ok ? greg * kLog2e : 0.f, lane);
-          const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
-          const float G = exp2f(g2);
-          const float bt = ok ? breg : 0.f;
-          sm.gam[lane] = g2;
-          sm.Gam[b][lane] = G;
-          sm.Dec[b][lane] = exp2f(gl2 - g2);
-          sm.bet[lane] = bt;
-          sm.bg[lane] = bt * G;
-        }
-        load_chunk(s + 1 < nch ? s + 1 : s);
-      }
-      __syncthreads();
-      if (s < nch) {
-        // W^T = K^T (T diag(beta Gamma))^T, transposed so rows of W store contiguously;
-        // U = T diag(beta) V for one row block, in the consumers' accumulator order
-        for_rowblocks([&](auto R0, auto R1) {
-          constexpr int rb[2] = {decltype(R0)::value, decltype(R1)::value};
-          constexpr int NCW = DK / 32;  // 16-column blocks of W per wave
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int ri = rb[x];
-            F tw[TS];
-#pragma unroll
-            for (int ks = 0; ks < tsteps<Op>(rb[x]); ++ks)
-              tw[ks] = Op::scale(Op::frag(sm.Tm + 16 * rb[x] * LDC, LDC, lane, ks * KS), sm.bg, lane, ks * KS);
-#pragma unroll
-            for (int cj = 0; cj < NCW; ++cj) {
-              const int cw = (w & 1) * NCW + cj;
-              f32x4_t acc = zero4();
-#pragma unroll
-              for (int ks = 0; ks < tsteps<Op>(rb[x]); ++ks)
-                acc = Op::mma(Op::frag(sm.Kt[b] + 16 * cw * LDC, LDC, lane, ks * KS), tw[ks], acc);
-              store4<E>(sm.Ws + (16 * ri + (lane & 15)) * LDK + 16 * cw + 4 * (lane >> 4), acc[0],
-                        acc[1], acc[2], acc[3]);
-            }
-          }
-          if (!use_v) return;  // transition maps: U = 0, read as zeros by the consumers
-          const int x = w & 1;
-          const int ri = x ? rb[1] : rb[0];
-          f32x4_t acc = zero4();
-          if (x == 0) {
-#pragma unroll
-            for (int ks = 0; ks < tsteps<Op>(rb[0]); ++ks)
-              acc = Op::mma(Op::scale(Op::frag(sm.Tm + 16 * rb[0] * LDC, LDC, lane, ks * KS), sm.bet, lane, ks * KS),
-                            Op::frag(sm.Vt, LDC, lane, ks * KS), acc);
-          } else {
-#pragma unroll
-            for (int ks = 0; ks < tsteps<Op>(rb[1]); ++ks)
-              acc = Op::mma(Op::scale(Op::frag(sm.Tm + 16 * rb[1] * LDC, LDC, lane, ks * KS), sm.bet, lane, ks * KS),
-                            Op::frag(sm.Vt, LDC, lane, ks * KS), acc);
-          }
-          *reinterpret_cast<float4*>(sm.Us + (ri * 64 + lane) * 4) = float4{acc[0], acc[1], acc[2], acc[3]};
-        });
-      }
-      __syncthreads();
+      for (int x = 0; x < NTV; ++x)
+        *reinterpret_cast<u32x4_t*>(sm.Tb[slot] + tc * LDC + (x * 4 + lg) * (16 / sizeof(E))) = st.tv[x];
+      st.vv.store(sm.Vs[slot] + tc * 16 + 4 * lg);
+      if (w == 4) *reinterpret_cast<float2*>(sm.Gs[slot] + 2 * lane) = st.gv;
     };
-    if (nch > 0) load_chunk(0);
+    auto load_q = [&](F (&f)[NKK], int c) {
+      const E* row = q + (row_of(c, tc) * H + h) * DK;
+#pragma unroll
+      for (int ks = 0; ks < NKK; ++ks) f[ks] = Op::frag_row(row, lane, ks * KS);
+    };
+    auto load_p = [&](F (&f)[NTS], int c) {
+      const E* row = pw + ((slot0 + c) * H + h) * 4096 + tc * 64;
+#pragma unroll
+      for (int ks = 0; ks < NTS; ++ks) f[ks] = Op::frag_row(row, lane, ks * KS);
+    };
+    // prologue: chunks 0, 1, 2 in flight; chunk 0 staged
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      load_stage(stg[u], clampc(u));
+      if (OUT) {
+        load_q(qf[u], clampc(u));
+        load_p(pf[u], clampc(u));
+      }
+    }
+    write_stage(stg[0], 0, 0);
     __syncthreads();
-    for (int s = 0; s <= nch; ++s) step(s);
+    int c0 = 0;
+    do {
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) {
+        const int c = c0 + u;
+        const int un = (u + 1) % kRing;
+        // phase 1: stage chunk c + 1 (loaded two steps ago) into its ring slot
+        write_stage(stg[un], clampc(c + 1), un);
+        __syncthreads();
+        // phase 2: Y^T = S^T Q^T; load the staging operands of chunk c + 3
+        f32x4_t yacc = zero4();
+        if (OUT) {
+#pragma unroll
+          for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), qf[u][ks], yacc);
+          load_q(qf[u], clampc(c + kRing));
+        }
+        load_stage(stg[u], clampc(c + kRing));
+        __syncthreads();
+        // phase 3: O^T = Gamma o Y^T + E^T P^T
+        if (OUT) {
+          f32x4_t oacc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < NTS; ++ks) oacc = Op::mma(Op::frag(sm.Et, LDC, lane, ks * KS), pf[u][ks], oacc);
+          const float gt = sm.Gs[u][tc];
+          // rows of padded tokens and steps past the last chunk fall outside the range
+          const int cc = clampc(c), nv = chunk_rows(cc);
+          const auto ro = buffer_rsrc(o + ((bos + static_cast<int64_t>(cb + cc) * 64) * H + h) * Dv + j0,
+                                      store_o && c < nch ? ((nv - 1) * H * Dv + 16) * static_cast<int>(sizeof(E)) : 0);
+          buffer_store4<E>(ro, (tc * H * Dv + 4 * lg) * static_cast<int>(sizeof(E)),
+                           p.scale * (gt * yacc[0] + oacc[0]), p.scale * (gt * yacc[1] + oacc[1]),
+                           p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
+          load_p(pf[u], clampc(c + kRing));
+        }
+        __syncthreads();
+      }
+      c0 += kRing;
+    } while (c0 < nsteps);
   }
 }
 
@@ -602,59 +555,49 @@ __global__ __launch_bounds__(256) void seg_carry_kernel(CarryParams c) {
   }
 }
 
-template <int DK, typename Op>
-hipError_t set_fwd_attributes() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel<DK, Op>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(sizeof(PrepSmem<DK, Op>)));
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_state_kernel<DK, Op>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(sizeof(StateSmem<DK, Op>)));
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(bytes));
 }
 
 template <int DK, typename Op>
-hipError_t launch_states_t(const FwdParams& p, hipStream_t s) {
-  hipError_t e = set_fwd_attributes<DK, Op>();
-  if (e != hipSuccess) return e;
-  if (p.max_chunks == 0) return hipSuccess;
+hipError_t launch_prep(const FwdParams& p, hipStream_t s) {
+  constexpr size_t smem = sizeof(PrepSmem<DK, Op>);
+  static_assert(smem <= 160 * 1024, "LDS budget exceeded");
   auto prep = chunk_prep_kernel<DK, Op>;
-  auto state = chunk_state_kernel<DK, Op>;
-  constexpr size_t prep_smem = sizeof(PrepSmem<DK, Op>);
-  constexpr size_t state_smem = sizeof(StateSmem<DK, Op>);
-  hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), prep_smem, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  FwdParams q = p;
-  q.G = 1; q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutNone;
-  q.zero_u = 0; q.ncol = p.Dv; q.carry = nullptr; q.seg_out = nullptr; q.final_to_sfinal = 0;
-  q.S_final = nullptr;
-  hipLaunchKernelGGL(state, dim3(p.N * p.H * (p.Dv / 16)), dim3(512), state_smem, s, q);
+  hipError_t e = allow_lds(prep, smem);
+  if (e != hipSuccess || p.max_chunks == 0) return e;
+  hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int DK, typename Op, bool STATES, bool OUT>
+hipError_t launch_state(const FwdParams& q, hipStream_t s) {
+  constexpr size_t smem = sizeof(StateSmem<DK, Op>);
+  static_assert(smem <= 160 * 1024, "LDS budget exceeded");
+  auto state = chunk_state_kernel<DK, Op, STATES, OUT>;
+  hipError_t e = allow_lds(state, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(state, dim3(q.nseg * q.N * q.H * (q.ncol / 16)), dim3(512), smem, s, q);
   return hipGetLastError();
 }
 
 template <int DK, typename Op>
+hipError_t launch_states_t(const FwdParams& p, hipStream_t s) {
+  hipError_t e = launch_prep<DK, Op>(p, s);
+  if (e != hipSuccess) return e;
+  FwdParams q = p;
+  q.G = 1; q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutNone;
+  q.zero_u = 0; q.ncol = p.Dv; q.carry = nullptr; q.seg_out = nullptr; q.final_to_sfinal = 0;
+  q.S_final = nullptr;
+  return launch_state<DK, Op, true, false>(q, s);
+}
+
+template <int DK, typename Op>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  constexpr size_t prep_smem = sizeof(PrepSmem<DK, Op>);
-  constexpr size_t state_smem = sizeof(StateSmem<DK, Op>);
-  static_assert(prep_smem <= 160 * 1024 && state_smem <= 160 * 1024, "LDS budget exceeded");
-  auto prep = chunk_prep_kernel<DK, Op>;
-  auto state = chunk_state_kernel<DK, Op>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(prep_smem));
+  hipError_t e = launch_prep<DK, Op>(p, s);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(state),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(state_smem));
-  if (e != hipSuccess) return e;
-  if (p.max_chunks > 0) {
-    hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), prep_smem, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  auto run_state = [&](const FwdParams& q) {
-    hipLaunchKernelGGL(state, dim3(q.nseg * q.N * q.H * (q.ncol / 16)), dim3(512), state_smem, s, q);
-    return hipGetLastError();
-  };
   FwdParams q = p;
   q.ncol = p.Dv;
   q.zero_u = 0;
@@ -662,7 +605,7 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   if (p.G == 1) {
     q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
     q.seg_out = nullptr; q.final_to_sfinal = 1;
-    return run_state(q);
+    return launch_state<DK, Op, false, true>(q, s);
   }
   // G segments per sequence: (1) segment 0 from S0 with its outputs, and the
   // segments 1 .. G-2 from zero (their offsets b); (2) the transition maps M of
@@ -674,19 +617,19 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   float* maps = starts + ends_floats;
   q.seg_base = 0; q.nseg = p.G - 1; q.start_mode = kStartS0; q.write_o = kOutSeg0;
   q.seg_out = ends; q.final_to_sfinal = 0;
-  if ((e = run_state(q)) != hipSuccess) return e;
+  if ((e = launch_state<DK, Op, false, true>(q, s)) != hipSuccess) return e;
   if (p.G > 2) {
     FwdParams m = q;
     m.ncol = DK; m.seg_base = 1; m.nseg = p.G - 2; m.start_mode = kStartIdentity;
     m.write_o = kOutNone; m.zero_u = 1; m.seg_out = maps;
-    if ((e = run_state(m)) != hipSuccess) return e;
+    if ((e = launch_state<DK, Op, false, false>(m, s)) != hipSuccess) return e;
   }
   CarryParams c{ends, maps, starts, p.G, p.N, p.H, DK, p.Dv};
   hipLaunchKernelGGL(seg_carry_kernel<DK>, dim3(p.N * p.H * (p.Dv / 16)), dim3(256), 0, s, c);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   q.seg_base = 1; q.nseg = p.G - 1; q.start_mode = kStartCarry; q.write_o = kOutAll;
   q.carry = starts; q.seg_out = nullptr; q.final_to_sfinal = 1;
-  return run_state(q);
+  return launch_state<DK, Op, false, true>(q, s);
 }
 
 }  // namespace

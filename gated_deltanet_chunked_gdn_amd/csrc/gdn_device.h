@@ -43,6 +43,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // ----------------------------------------------------------------------------------
 // Operand policies.  `elem` is what operand tiles hold in LDS.
 // ----------------------------------------------------------------------------------
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
 struct OpBf16 {
   using elem = uint16_t;
   using frag_t = bf16x8_t;
@@ -59,6 +62,19 @@ struct OpBf16 {
   static __device__ __forceinline__ frag_t frag_row(const elem* row, int lane, int k0) {
     const uint4 u = *reinterpret_cast<const uint4*>(row + k0 + (lane >> 4) * 8);
     return __builtin_bit_cast(bf16x8_t, u);
+  }
+  // Fragment of the transpose of a row-major LDS buffer: element m of lane `lane`
+  // is buf[k0 + 8 (lane / 16) + m][lane % 16].  Two ds_read_b64_tr_b16: within each
+  // 16-lane group, lane s supplies row k0 + 8 g + s / 4 (+4), columns 4 (s % 4) .. +3,
+  // and lane i receives column i of the four rows.
+  static __device__ __forceinline__ frag_t frag_tr(const elem* buf, int ld, int lane, int k0) {
+    const int s = lane & 15;
+    const elem* p0 = buf + (k0 + 8 * (lane >> 4) + (s >> 2)) * ld + 4 * (s & 3);
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 4 * ld));
+    typedef short i16x8_t __attribute__((ext_vector_type(8)));
+    const i16x8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, ab);
   }
   // Multiply element m of a fragment by s[k0 + 8 (lane / 16) + m] and re-round.
   static __device__ __forceinline__ frag_t scale(frag_t f, const float* s, int lane, int k0) {
@@ -90,6 +106,9 @@ struct OpF32 {
   }
   static __device__ __forceinline__ frag_t frag_row(const elem* row, int lane, int k0) {
     return row[k0 + (lane >> 4)];
+  }
+  static __device__ __forceinline__ frag_t frag_tr(const elem* buf, int ld, int lane, int k0) {
+    return buf[(k0 + (lane >> 4)) * ld + (lane & 15)];
   }
   static __device__ __forceinline__ frag_t scale(frag_t f, const float* s, int lane, int k0) {
     return f * s[k0 + (lane >> 4)];

@@ -22,7 +22,10 @@ struct FwdParams {
   const float* S0;  // [N, H, Dk, Dv] or nullptr
   void* o;
   float* S_final;   // [N, H, Dk, Dv] or nullptr
-  void* tws;        // workspace: per-chunk triangular inverses T (io element type)
+  void* tws;        // per-chunk T = (I + A)^-1 (io element type, 64 x 64 per slot), or nullptr
+  void* tbws;       // per-chunk T diag(beta) (written by the prep kernel, read by the state pass)
+  void* pws;        // per-chunk P = lower_incl((Q K^T) o D) (likewise)
+  float* gws;       // per-chunk Gamma and exp(gamma_n - gamma), [slot][H][128] fp32 (likewise)
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;  // chunks of the longest sequence
@@ -113,7 +116,7 @@ hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s
 // The T slots and the per-chunk states only (no outputs): the forward half of the
 // chunked backward.  Uses p.tws and p.states; G must be 1.
 hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
-// Bytes of forward workspace beyond the T slots for G segments (0 for G = 1).
+// Bytes of forward workspace beyond the per-chunk records for G segments (0 for G = 1).
 inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
   if (G <= 1) return 0;
   const size_t nh = static_cast<size_t>(G) * N * H * Dk;
