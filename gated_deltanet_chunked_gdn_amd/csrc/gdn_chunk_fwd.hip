@@ -49,7 +49,7 @@ namespace {
 using namespace chunk;
 
 // ===================================================================================
-// Kernel 1: per-chunk T = (I + A)^-1
+// Kernel 1: per-chunk T = (I + A)^-1, T diag(beta), P and the decays
 // ===================================================================================
 template <int DK, typename Op>
 struct PrepSmem {
@@ -58,22 +58,27 @@ struct PrepSmem {
   static constexpr int LDK = DK + PADE;
   static constexpr int LDF = 64 + 4;
   static constexpr int LDM = 20;
-  E Ks[64 * LDK];
-  E Qs[64 * LDK];
-  float Af[64 * LDF];  // A, then P
-  float Tf[64 * LDF];
-  float Mt[4 * 16 * LDM];
+  static constexpr size_t kBytes = 64 * LDK * sizeof(E);                      // K rows
+  static constexpr size_t tBytes = (64 * LDF + 4 * 16 * LDM) * sizeof(float);  // T, block temps
+  static constexpr size_t uBytes = kBytes > tBytes ? kBytes : tBytes;
+  alignas(16) char U[uBytes];  // K rows, then (once A and P are formed) T and the block temps
+  float Af[64 * LDF];
   float gam[64], bet[64];
 };
 
 template <int DK, typename Op>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   using E = typename Op::elem;
+  using F = typename Op::frag_t;
   using SM = PrepSmem<DK, Op>;
-  constexpr int LDK = SM::LDK, LDF = SM::LDF, LDM = SM::LDM;
+  constexpr int LDK = SM::LDK, LDF = SM::LDF, LDM = SM::LDM, KS = Op::KSTEP;
   constexpr int EPV = 16 / sizeof(E);
+  constexpr int NKK = DK / KS;
   extern __shared__ __align__(16) char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  E* const Ks = reinterpret_cast<E*>(sm.U);
+  float* const Tf = reinterpret_cast<float*>(sm.U);
+  float* const Mts = Tf + 64 * LDF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z, H = p.H;
   int64_t bos, len;
@@ -87,7 +92,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   const E* k = static_cast<const E*>(p.k);
   const E* q = static_cast<const E*>(p.q);
   const bool want_p = p.pws != nullptr;
+  // Each wave forms the A blocks of row block `wave` and the P blocks of row block
+  // 3 - wave: five 16x16 blocks per wave.
+  const int ai = wave, pi = 3 - wave;
 
+  // Q rows of row block pi, as MFMA fragments straight from memory (zero past the end)
+  F qf[NKK];
+  if (want_p) {
+    const int t = 16 * pi + (lane & 15);
+    const E* row = q + ((row0 + min(t, nv - 1)) * H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks) qf[ks] = Op::frag_row(row, lane, ks * KS);
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks) qf[ks] = t < nv ? qf[ks] : F{};
+  }
   if (wave == 0) {
     const float gv = lane < nv ? p.g[(row0 + lane) * H + h] * kLog2e : 0.f;
     const float g2 = wave_inclusive_scan(gv, lane);  // gamma * log2(e)
@@ -104,30 +122,50 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   constexpr int VPR = DK / EPV;
   for (int x = tid; x < 64 * VPR; x += 256) {
     const int t = x / VPR, cc = x % VPR;
-    uint4 val = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (t < nv) {
-      val = *reinterpret_cast<const uint4*>(k + ((row0 + t) * H + h) * DK + cc * EPV);
-      if (want_p) qv = *reinterpret_cast<const uint4*>(q + ((row0 + t) * H + h) * DK + cc * EPV);
-    }
-    *reinterpret_cast<uint4*>(sm.Ks + t * LDK + cc * EPV) = val;
-    if (want_p) *reinterpret_cast<uint4*>(sm.Qs + t * LDK + cc * EPV) = qv;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (t < nv) val = *reinterpret_cast<const uint4*>(k + ((row0 + t) * H + h) * DK + cc * EPV);
+    *reinterpret_cast<uint4*>(Ks + t * LDK + cc * EPV) = val;
   }
   __syncthreads();
 
-  // A = strict_lower(diag(beta) (K K^T) o D), fp32
-  for (int b = wave; b < 10; b += 4) {
-    int bi, bj;
-    lower_block(b, bi, bj);
-    f32x4_t acc = zero4();
-    tile_mma<Op, DK>(acc, sm.Ks + 16 * bi * LDK, LDK, sm.Ks + 16 * bj * LDK, LDK, lane);
+  // A = strict_lower(diag(beta) (K K^T) o D) (fp32, row block ai), and
+  // P = lower_incl((Q K^T) o D) (row block pi), formed as P^T blocks and stored
+  // row-major straight to the workspace.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * bi + 4 * (lane >> 4) + r, j = 16 * bj + (lane & 15);
-      const float d = exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f));
-      sm.Af[i * LDF + j] = i > j ? sm.bet[i] * acc[r] * d : 0.f;
+  for (int bj = 0; bj < 4; ++bj) {
+    if (bj <= ai) {
+      f32x4_t acc = zero4();
+      tile_mma<Op, DK>(acc, Ks + 16 * ai * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ai + 4 * (lane >> 4) + r, j = 16 * bj + (lane & 15);
+        const float d = exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f));
+        sm.Af[i * LDF + j] = i > j ? sm.bet[i] * acc[r] * d : 0.f;
+      }
     }
   }
-  __syncthreads();
+  if (want_p) {
+    E* P = static_cast<E*>(p.pws) + moff;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      // block (pi, bj) of P, as P^T: C[j][i] = K_j . Q_i
+      f32x4_t acc = zero4();
+      if (bj <= pi) {
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks)
+          acc = Op::mma(Op::frag(Ks + 16 * bj * LDK, LDK, lane, ks * KS), qf[ks], acc);
+      }
+      const int i = 16 * pi + (lane & 15), jb = 16 * bj + 4 * (lane >> 4);
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + r;
+        pv[r] = j <= i ? acc[r] * exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f)) : 0.f;
+      }
+      store4<E>(P + i * 64 + jb, pv[0], pv[1], pv[2], pv[3]);
+    }
+  }
+  __syncthreads();  // A complete; K rows no longer needed (their space becomes T)
 
   // T = (I + A)^-1: diagonal blocks by forward substitution (wave w, lane = column)
   if (lane < 16) {
@@ -141,68 +179,48 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
       tcol[r] = r == cc ? 1.f : (r < cc ? 0.f : -s);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.Tf[(16 * w + r) * LDF + 16 * w + cc] = tcol[r];
+    for (int r = 0; r < 16; ++r) Tf[(16 * w + r) * LDF + 16 * w + cc] = tcol[r];
   }
   __syncthreads();
   // then the block diagonals below: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
   for (int d = 1; d < 4; ++d) {
     const bool act = wave < 4 - d;
     const int bj = wave, bi = wave + d;
-    float* Mt = sm.Mt + wave * 16 * LDM;
+    float* Mt = Mts + wave * 16 * LDM;
     if (act) {
       f32x4_t m = zero4();
       for (int kb = bj; kb < bi; ++kb)
-        tile_mma_f32_rowmajor<16>(m, sm.Af + 16 * bi * LDF + 16 * kb, LDF,
-                                  sm.Tf + 16 * kb * LDF + 16 * bj, LDF, lane);
+        tile_mma_f32_rowmajor<16>(m, sm.Af + 16 * bi * LDF + 16 * kb, LDF, Tf + 16 * kb * LDF + 16 * bj, LDF, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Mt[(4 * (lane >> 4) + r) * LDM + (lane & 15)] = m[r];
     }
     __syncthreads();
     if (act) {
       f32x4_t x = zero4();
-      tile_mma_f32_rowmajor<16>(x, sm.Tf + 16 * bi * LDF + 16 * bi, LDF, Mt, LDM, lane);
+      tile_mma_f32_rowmajor<16>(x, Tf + 16 * bi * LDF + 16 * bi, LDF, Mt, LDM, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.Tf[(16 * bi + 4 * (lane >> 4) + r) * LDF + 16 * bj + (lane & 15)] = -x[r];
+      for (int r = 0; r < 4; ++r) Tf[(16 * bi + 4 * (lane >> 4) + r) * LDF + 16 * bj + (lane & 15)] = -x[r];
     }
     __syncthreads();
   }
 
-  // P = lower_incl((Q K^T) o D) into Af (A is no longer needed)
-  if (want_p) {
-    for (int b = wave; b < 10; b += 4) {
-      int bi, bj;
-      lower_block(b, bi, bj);
-      f32x4_t acc = zero4();
-      tile_mma<Op, DK>(acc, sm.Qs + 16 * bi * LDK, LDK, sm.Ks + 16 * bj * LDK, LDK, lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * bi + 4 * (lane >> 4) + r, j = 16 * bj + (lane & 15);
-        const float d = exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f));
-        sm.Af[i * LDF + j] = i >= j ? acc[r] * d : 0.f;
-      }
-    }
-    __syncthreads();
-  }
-
-  // store T, T diag(beta) and P row-major (io type), blocks above the diagonal as zeros
+  // store T and T diag(beta) row-major (io type), blocks above the diagonal as zeros
   constexpr int VPT = 64 / EPV;
-  auto store_mat = [&](E* dst, const float* src, bool by_beta) {
+  auto store_mat = [&](E* dst, bool by_beta) {
     for (int x = tid; x < 64 * VPT; x += 256) {
       const int i = x / VPT, jb = (x % VPT) * EPV;
       E vals[EPV];
 #pragma unroll
       for (int m = 0; m < EPV; ++m) {
         const int j = jb + m;
-        const float t = (j >> 4) <= (i >> 4) ? src[i * LDF + j] : 0.f;
+        const float t = (j >> 4) <= (i >> 4) ? Tf[i * LDF + j] : 0.f;
         vals[m] = Op::cvt(by_beta ? t * sm.bet[j] : t);
       }
       *reinterpret_cast<uint4*>(dst + i * 64 + jb) = *reinterpret_cast<const uint4*>(vals);
     }
   };
-  if (p.tws) store_mat(static_cast<E*>(p.tws) + moff, sm.Tf, false);
-  if (p.tbws) store_mat(static_cast<E*>(p.tbws) + moff, sm.Tf, true);
-  if (want_p) store_mat(static_cast<E*>(p.pws) + moff, sm.Af, false);
+  if (p.tws) store_mat(static_cast<E*>(p.tws) + moff, false);
+  if (p.tbws) store_mat(static_cast<E*>(p.tbws) + moff, true);
 }
 
 // ===================================================================================
@@ -354,6 +372,12 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   // bodies let the compiler wait for exactly the loads each step consumes.
   const int nsteps = (nch + kRing - 1) / kRing * kRing;
 
+  // Row-contiguous staging of [token][width] rows by 256 threads (index st):
+  // vector x * 256 + st is row (x * 256 + st) / VPR, column ((x * 256 + st) % VPR) * EPV.
+  constexpr int EPV = 16 / static_cast<int>(sizeof(E));
+  constexpr int KVR = DK / EPV, TVR = 64 / EPV;            // 16-byte vectors per K / per T row
+  constexpr int NKV = 64 * KVR / 256, NTV = 64 * TVR / 256;  // vectors per thread
+
   if (state_wave) {
     // ===================== state waves: the recurrence (LDS and MFMA only) =====================
     __syncthreads();  // chunk 0 staged
@@ -418,40 +442,54 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     write_state();
   } else {
     // ===================== output waves: staging, and O = Gamma o (Q S) + P E =====================
-    // Staged operands of chunk c (rows tc): loaded two steps before they are
-    // written to LDS, which is one step before the state waves read them.
+    // Staged operands of chunk c: loaded two steps before they are written to LDS,
+    // which is one step before the state waves read them.  The loads run along
+    // whole rows (every 16-byte vector of a row by consecutive lanes), so each
+    // load instruction covers whole cache lines.
+    const int ot = tid - 256;                            // 0 .. 255 over the output waves
+    constexpr int VVR = static_cast<int>(sizeof(E));     // 16-byte vectors per v-tile row
     struct Stage {
-      u32x4_t kv[DK * static_cast<int>(sizeof(E)) / 64];  // K row tc (KPL-wide fragments)
-      u32x4_t tv[64 * static_cast<int>(sizeof(E)) / 64];  // T diag(beta) row tc
-      Raw4<E> vv;                                         // v[tc][j0 + 4 lg .. + 3]
-      float2 gv;                                          // decays (wave 4 only)
+      u32x4_t kv[NKV];  // K, rows (x * 256 + ot) / KVR
+      u32x4_t tv[NTV];  // T diag(beta), rows (x * 256 + ot) / TVR
+      u32x4_t vv;       // the v tile: vector min(ot, 64 VVR - 1)
+      float4 gv;        // decays: floats 4 min(ot, 31) .. + 3
     };
-    constexpr int NKV = DK * static_cast<int>(sizeof(E)) / 64;
-    constexpr int NTV = 64 * static_cast<int>(sizeof(E)) / 64;
     Stage stg[kRing];
     F qf[kRing][NKK], pf[kRing][NTS];
-    auto load_stage = [&](Stage& st, int c) {
-      const E* krow = k + (row_of(c, tc) * H + h) * DK;
+    auto load_stage_k = [&](Stage& st, int c) {
 #pragma unroll
-      for (int x = 0; x < NKV; ++x) st.kv[x] = *reinterpret_cast<const u32x4_t*>(krow + (x * 4 + lg) * (16 / sizeof(E)));
-      const E* trow = tbw + ((slot0 + c) * H + h) * 4096 + tc * 64;
+      for (int x = 0; x < NKV; ++x) {
+        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
+        st.kv[x] = *reinterpret_cast<const u32x4_t*>(k + (row_of(c, t) * H + h) * DK + cv);
+      }
+    };
+    auto load_stage_rest = [&](Stage& st, int c) {
+      const E* T = tbw + ((slot0 + c) * H + h) * 4096;
 #pragma unroll
-      for (int x = 0; x < NTV; ++x) st.tv[x] = *reinterpret_cast<const u32x4_t*>(trow + (x * 4 + lg) * (16 / sizeof(E)));
-      // (a pass without V still loads, from a column clamped into the row, and discards it)
-      st.vv.load(v + (row_of(c, tc) * H + h) * Dv + min(j0 + 4 * lg, Dv - 4));
-      st.gv = *reinterpret_cast<const float2*>(gw + ((slot0 + c) * H + h) * 128 + 2 * lane);
+      for (int x = 0; x < NTV; ++x) st.tv[x] = *reinterpret_cast<const u32x4_t*>(T + (x * 256 + ot) * EPV);
+      // (a pass without V still loads, from columns clamped into the row, and discards them)
+      const int vi = min(ot, 64 * VVR - 1), t = vi / VVR, cpos = (vi % VVR) * EPV;
+      st.vv = *reinterpret_cast<const u32x4_t*>(v + (row_of(c, t) * H + h) * Dv + min(j0 + cpos, Dv - EPV));
+      st.gv = *reinterpret_cast<const float4*>(gw + ((slot0 + c) * H + h) * 128 + 4 * min(ot, 31));
     };
     auto write_stage = [&](const Stage& st, int c, int slot) {
-      const bool real = tc < chunk_rows(c);
+      const int nv = chunk_rows(c);
       const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int x = 0; x < NKV; ++x)
-        *reinterpret_cast<u32x4_t*>(sm.Ks[slot] + tc * LDK + (x * 4 + lg) * (16 / sizeof(E))) = real ? st.kv[x] : z;
+      for (int x = 0; x < NKV; ++x) {
+        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
+        *reinterpret_cast<u32x4_t*>(sm.Ks[slot] + t * LDK + cv) = t < nv ? st.kv[x] : z;
+      }
 #pragma unroll
-      for (int x = 0; x < NTV; ++x)
-        *reinterpret_cast<u32x4_t*>(sm.Tb[slot] + tc * LDC + (x * 4 + lg) * (16 / sizeof(E))) = st.tv[x];
-      st.vv.store(sm.Vs[slot] + tc * 16 + 4 * lg);
-      if (w == 4) *reinterpret_cast<float2*>(sm.Gs[slot] + 2 * lane) = st.gv;
+      for (int x = 0; x < NTV; ++x) {
+        const int vi = x * 256 + ot, t = vi / TVR, cv = (vi % TVR) * EPV;
+        *reinterpret_cast<u32x4_t*>(sm.Tb[slot] + t * LDC + cv) = st.tv[x];
+      }
+      {
+        const int vi = min(ot, 64 * VVR - 1);
+        *reinterpret_cast<u32x4_t*>(sm.Vs[slot] + (vi / VVR) * 16 + (vi % VVR) * EPV) = st.vv;
+      }
+      *reinterpret_cast<float4*>(sm.Gs[slot] + 4 * min(ot, 31)) = st.gv;
     };
     auto load_q = [&](F (&f)[NKK], int c) {
       const E* row = q + (row_of(c, tc) * H + h) * DK;
@@ -466,7 +504,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     // prologue: chunks 0, 1, 2 in flight; chunk 0 staged
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      load_stage(stg[u], clampc(u));
+      load_stage_k(stg[u], clampc(u));
+      load_stage_rest(stg[u], clampc(u));
       if (OUT) {
         load_q(qf[u], clampc(u));
         load_p(pf[u], clampc(u));
@@ -480,8 +519,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       for (int u = 0; u < kRing; ++u) {
         const int c = c0 + u;
         const int un = (u + 1) % kRing;
-        // phase 1: stage chunk c + 1 (loaded two steps ago) into its ring slot
+        // phase 1: stage chunk c + 1 (loaded two steps ago) into its ring slot; the
+        // loads of chunk c + 3 are spread over the three phases
         write_stage(stg[un], clampc(c + 1), un);
+        load_stage_k(stg[u], clampc(c + kRing));
         __syncthreads();
         // phase 2: Y^T = S^T Q^T; load the staging operands of chunk c + 3
         f32x4_t yacc = zero4();
@@ -490,7 +531,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), qf[u][ks], yacc);
           load_q(qf[u], clampc(c + kRing));
         }
-        load_stage(stg[u], clampc(c + kRing));
+        load_stage_rest(stg[u], clampc(c + kRing));
         __syncthreads();
         // phase 3: O^T = Gamma o Y^T + E^T P^T
         if (OUT) {
