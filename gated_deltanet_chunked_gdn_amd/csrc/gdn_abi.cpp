@@ -96,6 +96,11 @@ size_t t_slot_bytes(const gdn_problem* p, const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
+size_t packed_slot_bytes(const gdn_problem* p, const Checked& c) {
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kLPack * c.io;
+  return (b + 255) / 256 * 256;
+}
+
 size_t gate_slot_bytes(const gdn_problem* p, const Checked& c) {
   const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 128 * sizeof(float);
   return (b + 255) / 256 * 256;
@@ -110,17 +115,18 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
   if (kind == Kind::ChunkFwd) {
     if (c.N == 0) return 0;
-    // two 64 x 64 matrices per (chunk slot, head), io element type: T diag(beta)
-    // and the causal score P; the chunk's decays (128 fp32); then
+    // per (chunk slot, head): T diag(beta) and the causal score P (lower 16x16
+    // blocks packed, io element type) and the chunk's decays (128 fp32); then
     // (num_segments > 1) the fp32 segment end states, start states and maps
-    return 2 * t_slot_bytes(p, c) + gate_slot_bytes(p, c) +
+    return 2 * packed_slot_bytes(p, c) + gate_slot_bytes(p, c) +
            gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
-    // T, T diag(beta) and P per (chunk slot, head), the chunk's decays, then the
-    // fp32 state before and the state gradient after every chunk, [slot][H][Dk][Dv] each
-    return 3 * t_slot_bytes(p, c) + gate_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
+    // T (64 x 64), T diag(beta) (packed) and the decays per (chunk slot, head),
+    // then the fp32 state before and the state gradient after every chunk,
+    // [slot][H][Dk][Dv] each
+    return t_slot_bytes(p, c) + packed_slot_bytes(p, c) + gate_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
   }
   return 0;
 }
@@ -216,16 +222,16 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0; fp.o = o;
   fp.S_final = S_final; fp.seq = seq_info(p);
   fp.tws = nullptr;
-  fp.tbws = workspace;
-  fp.pws = static_cast<char*>(workspace) + t_slot_bytes(p, c);
-  fp.gws = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * t_slot_bytes(p, c));
+  char* const wsb = static_cast<char*>(workspace);
+  const size_t pb = packed_slot_bytes(p, c);
+  fp.tbws = wsb;
+  fp.pws = wsb + pb;
+  fp.gws = reinterpret_cast<float*>(wsb + 2 * pb);
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
   fp.scale = p->scale;
   fp.G = p->num_segments;
-  fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * t_slot_bytes(p, c) +
-                                                   gate_slot_bytes(p, c))
-                       : nullptr;
+  fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(wsb + 2 * pb + gate_slot_bytes(p, c)) : nullptr;
   return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
@@ -252,12 +258,13 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* const wsb = static_cast<char*>(workspace);
   const size_t tb = t_slot_bytes(p, c);
-  float* states = reinterpret_cast<float*>(wsb + 3 * tb + gate_slot_bytes(p, c));
+  const size_t pb = packed_slot_bytes(p, c);
+  float* states = reinterpret_cast<float*>(wsb + tb + pb + gate_slot_bytes(p, c));
   float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + state_slot_bytes(p, c));
   gdn::FwdParams fp{};
   fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0;
-  fp.tws = wsb; fp.tbws = wsb + tb; fp.pws = wsb + 2 * tb;
-  fp.gws = reinterpret_cast<float*>(wsb + 3 * tb);
+  fp.tws = wsb; fp.tbws = wsb + tb; fp.pws = nullptr;
+  fp.gws = reinterpret_cast<float*>(wsb + tb + pb);
   fp.states = states; fp.seq = seq_info(p);
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);

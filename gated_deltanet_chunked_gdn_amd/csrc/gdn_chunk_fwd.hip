@@ -8,8 +8,8 @@
 //       [cumsum of g instead of a product of alpha: "Research Sprint Day 2",
 //        "Building some intuition", gates step 5]
 //   A = strict_lower(diag(beta) (K K^T) o D),  T = (I + A)^-1   [triangular inverse]
-//   W = T diag(beta Gamma) K,  U = T diag(beta) V                [WY tensors w, u]
-//   E = U - W S                 (the chunk's errors e_t: the "write" of the update)
+//   E = U - W S with the WY tensors U = T diag(beta) V, W = T diag(beta Gamma) K
+//     = (T diag(beta)) (V - diag(Gamma) K S)      (the chunk's errors e_t)
 //   P = lower_incl((Q K^T) o D)                                 [causal QK score]
 //   O = scale (diag(Gamma) Q S + P E)
 //   S <- Gamma_n S + K^T diag(exp(gamma_n - gamma)) E
@@ -18,25 +18,25 @@
 // harmlessly and nothing is divided by a decay.
 //
 // Kernel 1, chunk_prep_kernel: one workgroup per (chunk, head, sequence), fully
-//   parallel.  Computes A with MFMA and T = (I + A)^-1 in fp32 in LDS (16x16
-//   diagonal blocks by forward substitution, the blocks below by
-//   T_ij = -T_ii sum_k A_ik T_kj with fp32 MFMA), stores T (upper blocks zero)
-//   in the workspace.
-// Kernel 2, chunk_state_kernel: one workgroup per (sequence, head, 16-column
-//   tile of d_v); column j of S only mixes with column j of v, so tiles are
-//   independent.  Eight waves in two roles, pipelined one chunk apart:
-//     producers (waves 4-7) turn chunk c+1 into W, U, P, K^T and the decays,
-//       reading q/k/v/g/beta/T straight from HBM (one chunk of prefetch);
-//     consumers (waves 0-3) hold the d_k x 16 fp32 slice of S in MFMA
-//       accumulators and run chunk c: E = U - W S, O, and the state update.
-//   Two workgroup barriers per chunk; the producer/consumer hand-off is
-//   double-buffered where a buffer is read across the mid-chunk barrier.
-//   Blocks are mapped so that the tiles of one head share an XCD (and its L2).
+//   parallel.  gamma and the decays, A and P with MFMA, T = (I + A)^-1 in fp32
+//   (16x16 diagonal blocks by forward substitution, the blocks below by
+//   T_ij = -T_ii sum_k A_ik T_kj with fp32 MFMA); stores T diag(beta) and P
+//   (lower blocks only), the decays, and for the backward T itself.
+// Kernel 2, chunk_state_kernel: one workgroup per (segment, sequence, head,
+//   16-column tile of d_v); column j of S only mixes with column j of v, so
+//   tiles are independent.  Eight waves in two roles:
+//     state waves (0-3) hold the d_k x 16 fp32 slice of S in MFMA accumulators
+//       and run chunk c: R = V - diag(Gamma) K S, E = (T diag(beta)) R, the
+//       state update; they touch only LDS;
+//     output waves (4-7) load chunk c + 2 along whole rows, stage chunk c + 1
+//       into LDS and form the output of chunk c.
+//   Three workgroup barriers per chunk.  The tiles of one head share an XCD (and
+//   its L2), so each input byte comes from HBM once per head.
 //
 // Precision: bf16 io feeds bf16 MFMA operands (v_mfma_f32_16x16x32_bf16) with
-// fp32 accumulation; S, gamma, the decays, A and the solve are fp32; T, W, U,
-// P, E and the state operand are rounded to bf16 only as MFMA inputs.  fp32 io
-// runs every product on v_mfma_f32_16x16x4_f32 (IEEE fp32).
+// fp32 accumulation; S, gamma, the decays, A and the inverse are fp32; T
+// diag(beta), P, R, E and the state operand are rounded to bf16 only as MFMA
+// inputs.  fp32 io runs every product on v_mfma_f32_16x16x4_f32 (IEEE fp32).
 #include <type_traits>
 
 #include "gdn_chunk_common.h"
@@ -47,6 +47,33 @@ namespace gdn {
 namespace {
 
 using namespace chunk;
+
+// Orders this wave's LDS accesses around a hand-off between its own lanes (the
+// LDS executes one wave's instructions in order; the fences keep the compiler
+// from moving accesses across the hand-off).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+// An offset that every buffer range check rejects: the load returns zeros and
+// moves no data.
+constexpr int kNoLoad = 0x7ffffff0;
+
+// Row block, row and column of element e of a packed lower-block matrix.
+__device__ __forceinline__ void lpack_pos(int e, int& i, int& j) {
+  const int rb = e < lpack_base(1) ? 0 : e < lpack_base(2) ? 1 : e < lpack_base(3) ? 2 : 3;
+  const int w = 16 * (rb + 1), rel = e - lpack_base(rb);
+  i = 16 * rb + rel / w;
+  j = rel % w;
+}
 
 // ===================================================================================
 // Kernel 1: per-chunk T = (I + A)^-1, T diag(beta), P and the decays
@@ -88,26 +115,50 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
   const int64_t row0 = bos + c0;
   const int64_t slot = bos / 64 + n + c;
-  const int64_t moff = (slot * H + h) * 4096;
-  const E* k = static_cast<const E*>(p.k);
-  const E* q = static_cast<const E*>(p.q);
+  const E* __restrict__ k = static_cast<const E*>(p.k);
+  const E* __restrict__ q = static_cast<const E*>(p.q);
   const bool want_p = p.pws != nullptr;
   // Each wave forms the A blocks of row block `wave` and the P blocks of row block
   // 3 - wave: five 16x16 blocks per wave.
   const int ai = wave, pi = 3 - wave;
 
-  // Q rows of row block pi, as MFMA fragments straight from memory (zero past the end)
+  // Every load is issued up front, through buffer resources bounded to the
+  // chunk's valid rows (padded rows read as zeros): Q rows of row block pi as
+  // MFMA fragments, K rows, g and beta.
+  const int s_e = static_cast<int>(sizeof(E));
+  const int rows_bytes = ((nv - 1) * H * DK + DK) * s_e;
   F qf[NKK];
   if (want_p) {
+    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rows_bytes);
     const int t = 16 * pi + (lane & 15);
-    const E* row = q + ((row0 + min(t, nv - 1)) * H + h) * DK;
 #pragma unroll
-    for (int ks = 0; ks < NKK; ++ks) qf[ks] = Op::frag_row(row, lane, ks * KS);
+    for (int ks = 0; ks < NKK; ++ks) {
+      const int off = (t * H * DK + ks * KS + (lane >> 4) * Op::KPL) * s_e;
+      if constexpr (sizeof(E) == 2)
+        qf[ks] = __builtin_bit_cast(F, buffer_load16(rq, off));
+      else
+        qf[ks] = buffer_load1(rq, off);
+    }
+  }
+  constexpr int VPR = DK / EPV;
+  constexpr int NKV = 64 * VPR / 256;
+  const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, rows_bytes);
+  u32x4_t kv[NKV];
 #pragma unroll
-    for (int ks = 0; ks < NKK; ++ks) qf[ks] = t < nv ? qf[ks] : F{};
+  for (int x = 0; x < NKV; ++x) {
+    const int vi = x * 256 + tid, t = vi / VPR, cc = vi % VPR;
+    kv[x] = buffer_load16(rk, (t * H * DK + cc * EPV) * s_e);
+  }
+  const auto rg = buffer_rsrc(p.g + row0 * H + h, ((nv - 1) * H + 1) * 4);
+  const auto rb = buffer_rsrc(p.beta + row0 * H + h, ((nv - 1) * H + 1) * 4);
+  const float gv = buffer_load1(rg, lane * H * 4) * kLog2e;
+  const float bv = buffer_load1(rb, lane * H * 4);
+#pragma unroll
+  for (int x = 0; x < NKV; ++x) {
+    const int vi = x * 256 + tid, t = vi / VPR, cc = vi % VPR;
+    *reinterpret_cast<u32x4_t*>(Ks + t * LDK + cc * EPV) = kv[x];
   }
   if (wave == 0) {
-    const float gv = lane < nv ? p.g[(row0 + lane) * H + h] * kLog2e : 0.f;
     const float g2 = wave_inclusive_scan(gv, lane);  // gamma * log2(e)
     sm.gam[lane] = g2;
     if (p.gws) {  // Gamma and the decays to the chunk end, for the state pass
@@ -117,20 +168,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
       gr[64 + lane] = exp2f(gl2 - g2);
     }
   } else if (wave == 1) {
-    sm.bet[lane] = lane < nv ? p.beta[(row0 + lane) * H + h] : 0.f;
-  }
-  constexpr int VPR = DK / EPV;
-  for (int x = tid; x < 64 * VPR; x += 256) {
-    const int t = x / VPR, cc = x % VPR;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (t < nv) val = *reinterpret_cast<const uint4*>(k + ((row0 + t) * H + h) * DK + cc * EPV);
-    *reinterpret_cast<uint4*>(Ks + t * LDK + cc * EPV) = val;
+    sm.bet[lane] = bv;
   }
   __syncthreads();
 
   // A = strict_lower(diag(beta) (K K^T) o D) (fp32, row block ai), and
   // P = lower_incl((Q K^T) o D) (row block pi), formed as P^T blocks and stored
-  // row-major straight to the workspace.
+  // packed straight to the workspace.
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
     if (bj <= ai) {
@@ -145,24 +189,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
     }
   }
   if (want_p) {
-    E* P = static_cast<E*>(p.pws) + moff;
+    E* P = static_cast<E*>(p.pws) + (slot * H + h) * kLPack + lpack_base(pi);
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-      // block (pi, bj) of P, as P^T: C[j][i] = K_j . Q_i
-      f32x4_t acc = zero4();
       if (bj <= pi) {
+        // block (pi, bj) of P, as P^T: C[j][i] = K_j . Q_i
+        f32x4_t acc = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKK; ++ks)
           acc = Op::mma(Op::frag(Ks + 16 * bj * LDK, LDK, lane, ks * KS), qf[ks], acc);
-      }
-      const int i = 16 * pi + (lane & 15), jb = 16 * bj + 4 * (lane >> 4);
-      float pv[4];
+        const int il = lane & 15, i = 16 * pi + il, jb = 16 * bj + 4 * (lane >> 4);
+        float pv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jb + r;
-        pv[r] = j <= i ? acc[r] * exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f)) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb + r;
+          pv[r] = j <= i ? acc[r] * exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f)) : 0.f;
+        }
+        store4<E>(P + il * 16 * (pi + 1) + jb, pv[0], pv[1], pv[2], pv[3]);
       }
-      store4<E>(P + i * 64 + jb, pv[0], pv[1], pv[2], pv[3]);
     }
   }
   __syncthreads();  // A complete; K rows no longer needed (their space becomes T)
@@ -204,32 +248,42 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  // store T and T diag(beta) row-major (io type), blocks above the diagonal as zeros
-  constexpr int VPT = 64 / EPV;
-  auto store_mat = [&](E* dst, bool by_beta) {
+  // T diag(beta), packed (the entries above the diagonal inside the diagonal
+  // blocks are exact zeros), and T row-major for the backward
+  const int64_t sh = slot * H + h;
+  if (p.tbws) {
+    E* dst = static_cast<E*>(p.tbws) + sh * kLPack;
+    for (int x = tid; x < kLPack / EPV; x += 256) {
+      int i, jb;
+      lpack_pos(x * EPV, i, jb);
+      E vals[EPV];
+#pragma unroll
+      for (int m = 0; m < EPV; ++m) vals[m] = Op::cvt(Tf[i * LDF + jb + m] * sm.bet[jb + m]);
+      *reinterpret_cast<uint4*>(dst + x * EPV) = *reinterpret_cast<const uint4*>(vals);
+    }
+  }
+  if (p.tws) {
+    E* dst = static_cast<E*>(p.tws) + sh * 4096;
+    constexpr int VPT = 64 / EPV;
     for (int x = tid; x < 64 * VPT; x += 256) {
       const int i = x / VPT, jb = (x % VPT) * EPV;
       E vals[EPV];
 #pragma unroll
       for (int m = 0; m < EPV; ++m) {
         const int j = jb + m;
-        const float t = (j >> 4) <= (i >> 4) ? Tf[i * LDF + j] : 0.f;
-        vals[m] = Op::cvt(by_beta ? t * sm.bet[j] : t);
+        vals[m] = Op::cvt((j >> 4) <= (i >> 4) ? Tf[i * LDF + j] : 0.f);
       }
       *reinterpret_cast<uint4*>(dst + i * 64 + jb) = *reinterpret_cast<const uint4*>(vals);
     }
-  };
-  if (p.tws) store_mat(static_cast<E*>(p.tws) + moff, false);
-  if (p.tbws) store_mat(static_cast<E*>(p.tbws) + moff, true);
+  }
 }
 
 // ===================================================================================
 // Kernel 2: the state pass with output
 // ===================================================================================
-// Ring of per-chunk operands staged in LDS by the output waves (three chunks:
-// the one in use, the next one, and the one being written).
-constexpr int kRing = 3;
-
+// LDS of one workgroup: the per-chunk operands of the state waves in two ring
+// slots (the chunk in use and the next one, being staged), private relayout
+// space of each output wave, and the hand-off buffers between the roles.
 template <int DK, typename Op>
 struct StateSmem {
   using E = typename Op::elem;
@@ -237,14 +291,16 @@ struct StateSmem {
   static constexpr int LDK = DK + PADE;  // rows of length d_k
   static constexpr int LDC = 64 + PADE;  // rows of length 64 (one chunk)
   static constexpr int LDR = 16 + PADE;  // rows of length 16 (one tile)
-  E Ks[kRing][64 * LDK];  // K rows of a chunk (padded tokens as zeros)
-  E Tb[kRing][64 * LDC];  // T diag(beta) of a chunk
-  E Vs[kRing][64 * 16];   // the v tile of a chunk
-  float Gs[kRing][128];   // Gamma and exp(gamma_n - gamma) of a chunk
-  E Sb[16 * LDK];         // S^T of this tile as an MFMA operand, [j][d_k]
-  E Rr[64 * LDR];         // R = V - diag(Gamma) K S, [t][j]
-  E Et[16 * LDC];         // E^T
-  E Ett[16 * LDC];        // (diag(exp(gamma_n - gamma)) E)^T
+  alignas(16) E Ks[2][64 * LDK];   // K rows (rows of padded tokens are zero)
+  alignas(16) E Tb[2][64 * LDC];   // T diag(beta); the blocks above the diagonal stay zero
+  alignas(16) E Vs[2][64 * 16];    // the v tile
+  alignas(16) float Gs[2][128];    // Gamma and exp(gamma_n - gamma)
+  alignas(16) E Qv[4][16 * LDK];   // output wave w: its 16 Q rows
+  alignas(16) E Pv[4][16 * LDC];   // output wave w: its 16 P rows (the blocks above the diagonal stay zero)
+  alignas(16) E Sb[16 * LDK];      // S^T of this tile as an MFMA operand, [j][d_k]
+  alignas(16) E Rr[64 * LDR];      // R = V - diag(Gamma) K S, [t][j]
+  alignas(16) E Et[16 * LDC];      // E^T
+  alignas(16) E Ett[16 * LDC];     // (diag(exp(gamma_n - gamma)) E)^T
 };
 
 // Four consecutive io values, widened when used.
@@ -254,7 +310,6 @@ template <>
 struct Raw4<uint16_t> {
   uint2 u;
   __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint2*>(p) = u; }
   __device__ __forceinline__ float operator[](int r) const {
     const uint32_t w = r < 2 ? u.x : u.y;
     return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -264,7 +319,6 @@ template <>
 struct Raw4<float> {
   float4 u;
   __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
-  __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<float4*>(p) = u; }
   __device__ __forceinline__ float operator[](int r) const {
     return r == 0 ? u.x : r == 1 ? u.y : r == 2 ? u.z : u.w;
   }
@@ -277,7 +331,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   using E = typename Op::elem;
   using F = typename Op::frag_t;
   using SM = StateSmem<DK, Op>;
-  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDR = SM::LDR, KS = Op::KSTEP, KPL = Op::KPL;
+  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDR = SM::LDR;
+  constexpr int KS = Op::KSTEP;
   constexpr int NKK = DK / KS;  // k-steps over d_k
   constexpr int NTS = 64 / KS;  // k-steps over one chunk
   constexpr int DPW = DK / 64;  // 16-row blocks of S per state wave
@@ -309,7 +364,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   const int64_t slot0 = bos / 64 + n + cb;
   const bool store_o = p.write_o == kOutAll || (p.write_o == kOutSeg0 && seg == 0);
   const bool use_v = !p.zero_u;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int wr = w & 3, lr = lane & 15, lg = lane >> 4;
   const int tc = 16 * wr + lr;  // this lane's token row / column
   const bool state_wave = w < 4;
@@ -320,10 +376,6 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     const int64_t c0 = static_cast<int64_t>(cb + c) * 64;
     return static_cast<int>(len - c0 < 64 ? len - c0 : 64);
   };
-  // Rows past the end of the sequence repeat its last row (every load stays in
-  // bounds); K rows of padded tokens are staged as zeros, R rows are zeroed and
-  // output rows are not stored, so padded tokens never reach a result.
-  auto row_of = [&](int c, int t) { return bos + static_cast<int64_t>(cb + c) * 64 + min(t, chunk_rows(c) - 1); };
   auto clampc = [&](int c) { return c < nch ? c : nch - 1; };
 
   f32x4_t Sacc[DPW];
@@ -367,16 +419,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     if (state_wave) write_state();
     return;
   }
-  // The chunk loop is unrolled by the ring size and has no tail branch: steps
-  // past the last chunk run on clamped data and change nothing.  Straight-line
-  // bodies let the compiler wait for exactly the loads each step consumes.
-  const int nsteps = (nch + kRing - 1) / kRing * kRing;
-
-  // Row-contiguous staging of [token][width] rows by 256 threads (index st):
-  // vector x * 256 + st is row (x * 256 + st) / VPR, column ((x * 256 + st) % VPR) * EPV.
-  constexpr int EPV = 16 / static_cast<int>(sizeof(E));
-  constexpr int KVR = DK / EPV, TVR = 64 / EPV;            // 16-byte vectors per K / per T row
-  constexpr int NKV = 64 * KVR / 256, NTV = 64 * TVR / 256;  // vectors per thread
+  // The chunk loop is unrolled by two (the ring slots) and has no tail branch:
+  // steps past the last chunk run on clamped data and change nothing.
+  // Straight-line bodies let the compiler wait for exactly the loads each step
+  // consumes.
+  const int nsteps = (nch + 1) / 2 * 2;
 
   if (state_wave) {
     // ===================== state waves: the recurrence (LDS and MFMA only) =====================
@@ -384,7 +431,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     int c0 = 0;
     do {
 #pragma unroll
-      for (int u = 0; u < kRing; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
         const bool active = c < nch;
         const E* Ks = sm.Ks[u];
@@ -437,103 +484,159 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         }
         __syncthreads();
       }
-      c0 += kRing;
+      c0 += 2;
     } while (c0 < nsteps);
     write_state();
   } else {
-    // ===================== output waves: staging, and O = Gamma o (Q S) + P E =====================
-    // Staged operands of chunk c: loaded two steps before they are written to LDS,
-    // which is one step before the state waves read them.  The loads run along
-    // whole rows (every 16-byte vector of a row by consecutive lanes), so each
-    // load instruction covers whole cache lines.
-    const int ot = tid - 256;                            // 0 .. 255 over the output waves
-    constexpr int VVR = static_cast<int>(sizeof(E));     // 16-byte vectors per v-tile row
-    struct Stage {
-      u32x4_t kv[NKV];  // K, rows (x * 256 + ot) / KVR
-      u32x4_t tv[NTV];  // T diag(beta), rows (x * 256 + ot) / TVR
-      u32x4_t vv;       // the v tile: vector min(ot, 64 VVR - 1)
-      float4 gv;        // decays: floats 4 min(ot, 31) .. + 3
+    // ============ output waves: loads, staging, O = Gamma o (Q S) + P E ============
+    // In step c (the state waves on chunk c): phase 1 issues the loads of chunk
+    // c + 2 and forms Y^T = S_c^T Q_c^T; phase 2 turns the Q and P rows of chunk
+    // c + 1 into operand fragments and stages its T diag(beta); phase 3 forms
+    // the output of chunk c and stages K, v and the decays of chunk c + 1.  Loads
+    // run along whole rows (consecutive lanes read consecutive 16-byte vectors),
+    // through buffer resources that bound them to the chunk's valid rows (rows
+    // of padded tokens read as zeros).
+    const int wo = w - 4, ot = tid - 256;
+    constexpr int EPV = 16 / static_cast<int>(sizeof(E));
+    constexpr int KVR = DK / EPV;                     // 16-byte vectors per K / Q row
+    constexpr int NKV = 64 * KVR / 256;               // K vectors per output thread
+    constexpr int NQV = 16 * KVR / 64;                // Q vectors per lane (the wave's 16 rows)
+    constexpr int VVR = static_cast<int>(sizeof(E));  // 16-byte vectors per v-tile row
+    constexpr int TVN = kLPack / EPV;                 // vectors of a packed T diag(beta)
+    constexpr int NTV = (TVN + 255) / 256;
+    constexpr int NPV = (16 * 64 / EPV + 63) / 64;    // P vectors per lane (row block 3)
+    const int prow = 16 * (wo + 1);                   // length of this wave's P rows
+    const int pvn = 16 * prow / EPV;                  // its vectors
+    // Lanes past the end of a short array load nothing (kNoLoad) and write nothing.
+    struct LoadSet {
+      u32x4_t kv[NKV];  // K: vector x * 256 + ot is row (x * 256 + ot) / KVR
+      u32x4_t qv[NQV];  // Q rows 16 wo .. 16 wo + 15: vector x * 64 + lane
+      u32x4_t tv[NTV];  // T diag(beta): packed vector x * 256 + ot (< TVN)
+      u32x4_t pv[NPV];  // P row block wo: packed vector x * 64 + lane (< pvn)
+      u32x4_t vv;       // the v tile: vector ot (< 64 VVR)
+      u32x4_t gv;       // decays: floats 4 ot .. 4 ot + 3 (ot < 32)
     };
-    Stage stg[kRing];
-    F qf[kRing][NKK], pf[kRing][NTS];
-    auto load_stage_k = [&](Stage& st, int c) {
-#pragma unroll
-      for (int x = 0; x < NKV; ++x) {
-        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
-        st.kv[x] = *reinterpret_cast<const u32x4_t*>(k + (row_of(c, t) * H + h) * DK + cv);
-      }
-    };
-    auto load_stage_rest = [&](Stage& st, int c) {
-      const E* T = tbw + ((slot0 + c) * H + h) * 4096;
-#pragma unroll
-      for (int x = 0; x < NTV; ++x) st.tv[x] = *reinterpret_cast<const u32x4_t*>(T + (x * 256 + ot) * EPV);
-      // (a pass without V still loads, from columns clamped into the row, and discards them)
-      const int vi = min(ot, 64 * VVR - 1), t = vi / VVR, cpos = (vi % VVR) * EPV;
-      st.vv = *reinterpret_cast<const u32x4_t*>(v + (row_of(c, t) * H + h) * Dv + min(j0 + cpos, Dv - EPV));
-      st.gv = *reinterpret_cast<const float4*>(gw + ((slot0 + c) * H + h) * 128 + 4 * min(ot, 31));
-    };
-    auto write_stage = [&](const Stage& st, int c, int slot) {
+    LoadSet ls[2];
+    F qf[2][NKK], pf[2][NTS];
+    E* const qvE = sm.Qv[wo];
+    E* const pvE = sm.Pv[wo];
+
+    auto load_set = [&](LoadSet& s, int c) {
       const int nv = chunk_rows(c);
-      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
+      const int64_t sh = (slot0 + c) * H + h;
+      const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
 #pragma unroll
       for (int x = 0; x < NKV; ++x) {
         const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
-        *reinterpret_cast<u32x4_t*>(sm.Ks[slot] + t * LDK + cv) = t < nv ? st.kv[x] : z;
+        s.kv[x] = buffer_load16(rk, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
       }
+      if (OUT) {
+        const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
+#pragma unroll
+        for (int x = 0; x < NQV; ++x) {
+          const int vi = x * 64 + lane, t = 16 * wo + vi / KVR, cv = (vi % KVR) * EPV;
+          s.qv[x] = buffer_load16(rq, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
+        }
+        const auto rp = buffer_rsrc(pw + sh * kLPack + lpack_base(wo), pvn * 16);
+#pragma unroll
+        for (int x = 0; x < NPV; ++x) s.pv[x] = buffer_load16(rp, (x * 64 + lane) * 16);
+      }
+      const auto rt = buffer_rsrc(tbw + sh * kLPack, kLPack * static_cast<int>(sizeof(E)));
+#pragma unroll
+      for (int x = 0; x < NTV; ++x) s.tv[x] = buffer_load16(rt, (x * 256 + ot) * 16);
+      // (a pass without V still loads, from columns clamped into the row, and discards them)
+      const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, ((nv - 1) * H * Dv + Dv) * static_cast<int>(sizeof(E)));
+      const int t = ot / VVR, cpos = (ot % VVR) * EPV;
+      s.vv = buffer_load16(rv, ot < 64 * VVR ? (t * H * Dv + min(j0 + cpos, Dv - EPV)) * static_cast<int>(sizeof(E))
+                                             : kNoLoad);
+      s.gv = buffer_load16(buffer_rsrc(gw + sh * 128, 512), ot * 16);
+    };
+    // the wave's 16 Q rows as MFMA operand fragments (through its private LDS)
+    auto stage_q = [&](const LoadSet& s, F (&f)[NKK]) {
+#pragma unroll
+      for (int x = 0; x < NQV; ++x) {
+        const int vi = x * 64 + lane, t = vi / KVR, cv = (vi % KVR) * EPV;
+        *reinterpret_cast<u32x4_t*>(qvE + t * LDK + cv) = s.qv[x];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int ks = 0; ks < NKK; ++ks) f[ks] = Op::frag(qvE, LDK, lane, ks * KS);
+      wave_lds_sync();
+    };
+    // likewise the wave's 16 P rows (P^T as the B operand of O^T = E^T P^T)
+    auto stage_p = [&](const LoadSet& s, F (&f)[NTS]) {
+#pragma unroll
+      for (int x = 0; x < NPV; ++x) {
+        const int e = (x * 64 + lane) * EPV, t = e / prow, cc = e - t * prow;
+        if (x * 64 + lane < pvn) *reinterpret_cast<u32x4_t*>(pvE + t * LDC + cc) = s.pv[x];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int ks = 0; ks < NTS; ++ks) f[ks] = Op::frag(pvE, LDC, lane, ks * KS);
+      wave_lds_sync();
+    };
+    auto stage_t = [&](const LoadSet& s, int sl) {
 #pragma unroll
       for (int x = 0; x < NTV; ++x) {
-        const int vi = x * 256 + ot, t = vi / TVR, cv = (vi % TVR) * EPV;
-        *reinterpret_cast<u32x4_t*>(sm.Tb[slot] + t * LDC + cv) = st.tv[x];
+        int i, jb;
+        lpack_pos(min(x * 256 + ot, TVN - 1) * EPV, i, jb);
+        if (x * 256 + ot < TVN) *reinterpret_cast<u32x4_t*>(sm.Tb[sl] + i * LDC + jb) = s.tv[x];
       }
-      {
-        const int vi = min(ot, 64 * VVR - 1);
-        *reinterpret_cast<u32x4_t*>(sm.Vs[slot] + (vi / VVR) * 16 + (vi % VVR) * EPV) = st.vv;
+    };
+    auto stage_kvg = [&](const LoadSet& s, int sl) {
+#pragma unroll
+      for (int x = 0; x < NKV; ++x) {
+        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
+        *reinterpret_cast<u32x4_t*>(sm.Ks[sl] + t * LDK + cv) = s.kv[x];
       }
-      *reinterpret_cast<float4*>(sm.Gs[slot] + 4 * min(ot, 31)) = st.gv;
+      if (ot < 64 * VVR) *reinterpret_cast<u32x4_t*>(sm.Vs[sl] + (ot / VVR) * 16 + (ot % VVR) * EPV) = s.vv;
+      if (ot < 32) *reinterpret_cast<u32x4_t*>(sm.Gs[sl] + 4 * ot) = s.gv;
     };
-    auto load_q = [&](F (&f)[NKK], int c) {
-      const E* row = q + (row_of(c, tc) * H + h) * DK;
-#pragma unroll
-      for (int ks = 0; ks < NKK; ++ks) f[ks] = Op::frag_row(row, lane, ks * KS);
-    };
-    auto load_p = [&](F (&f)[NTS], int c) {
-      const E* row = pw + ((slot0 + c) * H + h) * 4096 + tc * 64;
-#pragma unroll
-      for (int ks = 0; ks < NTS; ++ks) f[ks] = Op::frag_row(row, lane, ks * KS);
-    };
-    // prologue: chunks 0, 1, 2 in flight; chunk 0 staged
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-      load_stage_k(stg[u], clampc(u));
-      load_stage_rest(stg[u], clampc(u));
-      if (OUT) {
-        load_q(qf[u], clampc(u));
-        load_p(pf[u], clampc(u));
+
+    // prologue: the blocks above the diagonal of both T diag(beta) slots and of the
+    // private P rows are zero for good; chunk 0 staged, chunk 1 loading
+    {
+      constexpr int VPT = 64 / EPV;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      for (int x = ot; x < 2 * 64 * VPT; x += 256) {
+        const int sl = x / (64 * VPT), rem = x % (64 * VPT), i = rem / VPT, jv = (rem % VPT) * EPV;
+        if ((jv >> 4) > (i >> 4)) *reinterpret_cast<u32x4_t*>(sm.Tb[sl] + i * LDC + jv) = z;
       }
+      for (int x = lane; x < 16 * VPT; x += 64)
+        *reinterpret_cast<u32x4_t*>(pvE + (x / VPT) * LDC + (x % VPT) * EPV) = z;
+      wave_lds_sync();
     }
-    write_stage(stg[0], 0, 0);
+    load_set(ls[0], 0);
+    load_set(ls[1], clampc(1));
+    stage_t(ls[0], 0);
+    stage_kvg(ls[0], 0);
+    if (OUT) {
+      stage_q(ls[0], qf[0]);
+      stage_p(ls[0], pf[0]);
+    }
     __syncthreads();
     int c0 = 0;
     do {
 #pragma unroll
-      for (int u = 0; u < kRing; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
-        const int un = (u + 1) % kRing;
-        // phase 1: stage chunk c + 1 (loaded two steps ago) into its ring slot; the
-        // loads of chunk c + 3 are spread over the three phases
-        write_stage(stg[un], clampc(c + 1), un);
-        load_stage_k(stg[u], clampc(c + kRing));
-        __syncthreads();
-        // phase 2: Y^T = S^T Q^T; load the staging operands of chunk c + 3
+        // phase 1
+        load_set(ls[u], clampc(c + 2));
         f32x4_t yacc = zero4();
         if (OUT) {
 #pragma unroll
           for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), qf[u][ks], yacc);
-          load_q(qf[u], clampc(c + kRing));
         }
-        load_stage_rest(stg[u], clampc(c + kRing));
         __syncthreads();
-        // phase 3: O^T = Gamma o Y^T + E^T P^T
+        // phase 2
+        if (OUT) {
+          stage_q(ls[u ^ 1], qf[u ^ 1]);
+          stage_p(ls[u ^ 1], pf[u ^ 1]);
+        }
+        stage_t(ls[u ^ 1], u ^ 1);
+        __syncthreads();
+        // phase 3: O^T = scale (Gamma o Y^T + E^T P^T) (columns j, token tc)
         if (OUT) {
           f32x4_t oacc = zero4();
 #pragma unroll
@@ -546,11 +649,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           buffer_store4<E>(ro, (tc * H * Dv + 4 * lg) * static_cast<int>(sizeof(E)),
                            p.scale * (gt * yacc[0] + oacc[0]), p.scale * (gt * yacc[1] + oacc[1]),
                            p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
-          load_p(pf[u], clampc(c + kRing));
         }
+        stage_kvg(ls[u ^ 1], u ^ 1);
         __syncthreads();
       }
-      c0 += kRing;
+      c0 += 2;
     } while (c0 < nsteps);
   }
 }
@@ -650,7 +753,7 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   }
   // G segments per sequence: (1) segment 0 from S0 with its outputs, and the
   // segments 1 .. G-2 from zero (their offsets b); (2) the transition maps M of
-  // segments 1 .. G-2 (the same pass with U = 0, started from the identity);
+  // segments 1 .. G-2 (the same pass with V = 0, started from the identity);
   // (3) the carries; (4) segments 1 .. G-1 again from their carried start states.
   const size_t ends_floats = static_cast<size_t>(p.G) * p.N * p.H * DK * p.Dv;
   float* ends = p.seg_ws;

@@ -23,9 +23,9 @@ struct FwdParams {
   void* o;
   float* S_final;   // [N, H, Dk, Dv] or nullptr
   void* tws;        // per-chunk T = (I + A)^-1 (io element type, 64 x 64 per slot), or nullptr
-  void* tbws;       // per-chunk T diag(beta) (written by the prep kernel, read by the state pass)
-  void* pws;        // per-chunk P = lower_incl((Q K^T) o D) (likewise)
-  float* gws;       // per-chunk Gamma and exp(gamma_n - gamma), [slot][H][128] fp32 (likewise)
+  void* tbws;       // per-chunk T diag(beta), lower blocks packed (kLPack io elements per slot)
+  void* pws;        // per-chunk P = lower_incl((Q K^T) o D), packed likewise, or nullptr
+  float* gws;       // per-chunk Gamma and exp(gamma_n - gamma), [slot][H][128] fp32
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;  // chunks of the longest sequence
@@ -60,6 +60,11 @@ struct CarryParams {
 // sequence of len rows has at most floor((bos + len) / 64) - floor(bos / 64) + 1
 // chunks.  Total slots: floor(total_rows / 64) + N + 1.
 inline int64_t chunk_slots(int64_t total_rows, int64_t N) { return total_rows / 64 + N + 1; }
+
+// A 64 x 64 matrix that is zero above its 16x16 block diagonal, stored packed:
+// row block rb (16 rows of 16 (rb + 1) entries, row-major) at element 128 rb (rb + 1).
+constexpr int kLPack = 2560;
+__host__ __device__ constexpr int lpack_base(int rb) { return 128 * rb * (rb + 1); }
 
 struct BwdParams {
   const void* q;
@@ -113,8 +118,9 @@ constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backw
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
-// The T slots and the per-chunk states only (no outputs): the forward half of the
-// chunked backward.  Uses p.tws and p.states; G must be 1.
+// T, T diag(beta) and the decays of every chunk slot, and the per-chunk states
+// (no outputs): the forward half of the chunked backward.  Uses p.tws, p.tbws,
+// p.gws and p.states; G must be 1.
 hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
 // Bytes of forward workspace beyond the per-chunk records for G segments (0 for G = 1).
 inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {

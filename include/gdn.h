@@ -136,8 +136,10 @@ gdn_status gdn_workspace_size(const gdn_problem* problem, int32_t pass, size_t* 
  * again from them with their outputs (cuLA issue #126 page, "Summary" and
  * "Hypothesis": segment affine transforms and carries).  G = 2 gives results
  * bit-identical to G = 1; G > 2 agrees to the bf16 rounding of M's operands.
- * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...): the per-chunk
- * inverses, plus for G > 1 fp32 buffers of 2 G N H Dk Dv + G N H Dk Dk floats. */
+ * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...): per chunk and
+ * head, T diag(beta) and the causal score (their 16x16 blocks on and below the
+ * diagonal) and the chunk's decays, plus for G > 1 fp32 buffers of
+ * 2 G N H Dk Dv + G N H Dk Dk floats. */
 gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,
                          void* o, float* S_final, void* workspace, size_t workspace_bytes,
@@ -149,7 +151,9 @@ gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* 
  * "Results" tables plus the initial-state gradient).
  *   in : q, k, v, g, beta, S0 (NULL = zero), dO, dS_final (NULL = zero)
  *   out: dq, dk, dv (io dtype), dg, dbeta (fp32), dS0 (fp32; NULL = not wanted)
- * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD. */
+ * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD (T, T diag(beta) and
+ * the decays of every chunk, and the fp32 state before and its gradient after
+ * every chunk). */
 gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,
                          const void* dO, const float* dS_final, void* dq, void* dk, void* dv,

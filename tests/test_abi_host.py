@@ -82,19 +82,18 @@ def test_problem_validation(kw, status):
 
 
 def test_workspace_sizes():
-    # forward: two 64 x 64 io-typed matrices (T diag(beta), P) and 128 fp32 decays
-    # per (chunk slot, head), each array rounded up to 256 bytes; slots = rows // 64 + N + 1
+    # forward: per (chunk slot, head) T diag(beta) and P with their lower 16x16
+    # blocks packed (2560 io elements each) and 128 fp32 decays, each array
+    # rounded up to 256 bytes; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     gates = up(slots * 3 * 128 * 4)
-    assert ws(problem()) == (nat.GDN_OK, 2 * slots * 3 * 64 * 64 * 2 + gates)
-    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (nat.GDN_OK, 2 * slots * 3 * 4096 * 4 + gates)
-    # segment split: the inverses (rounded up to 256 bytes), then fp32 end and
-    # start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
-    t_bytes = (200 // 64 + 2 + 1) * 3 * 64 * 64 * 2
+    assert ws(problem()) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 2) + gates)
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 4) + gates)
+    # segment split: then fp32 end and start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
     for G in (2, 4, 16):
         seg = (2 * G * 2 * 3 * 128 * 96 + G * 2 * 3 * 128 * 128) * 4
-        assert ws(problem(num_segments=G, Dv=96)) == (nat.GDN_OK, 2 * t_bytes + gates + seg)
+        assert ws(problem(num_segments=G, Dv=96)) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 2) + gates + seg)
     assert ws(problem(), nat.GDN_PASS_RECURRENT_FWD) == (nat.GDN_OK, 0)
     st, n = ws(problem(Dk=64), nat.GDN_PASS_RECURRENT_BWD)
     assert st == nat.GDN_OK and n > 0
@@ -173,13 +172,15 @@ def test_backward_entry_validates():
 
 
 def test_backward_workspace_size():
-    # T, T diag(beta), P (io type), then fp32 states before and state gradients
-    # after every chunk slot
+    # T (64 x 64), packed T diag(beta) (io type) and the decays, each rounded up
+    # to 256 bytes, then fp32 states before and state gradients after every
+    # chunk slot; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
+    up = lambda b: (b + 255) // 256 * 256
     st, n = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
     assert st == nat.GDN_OK
-    gates = (slots * 3 * 128 * 4 + 255) // 256 * 256
-    assert n == 3 * slots * 3 * 64 * 64 * 2 + gates + 2 * slots * 3 * 128 * 96 * 4
+    assert n == (up(slots * 3 * 4096 * 2) + up(slots * 3 * 2560 * 2) + up(slots * 3 * 128 * 4)
+                 + 2 * slots * 3 * 128 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
 
