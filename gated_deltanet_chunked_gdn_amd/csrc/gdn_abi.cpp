@@ -115,10 +115,11 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
   if (kind == Kind::ChunkFwd) {
     if (c.N == 0) return 0;
-    // per (chunk slot, head): T diag(beta) and the causal score P (lower 16x16
-    // blocks packed, io element type) and the chunk's decays (128 fp32); then
-    // (num_segments > 1) the fp32 segment end states, start states and maps
-    return 2 * packed_slot_bytes(p, c) + gate_slot_bytes(p, c) +
+    // per (chunk slot, head): T diag(beta) (lower 16x16 blocks packed, io element
+    // type), the causal score P (64 x 64 in MFMA operand order) and the chunk's
+    // decays (128 fp32); then (num_segments > 1) the fp32 segment end states,
+    // start states and maps
+    return packed_slot_bytes(p, c) + t_slot_bytes(p, c) + gate_slot_bytes(p, c) +
            gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
   }
   if (kind == Kind::ChunkBwd) {
@@ -226,12 +227,12 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   const size_t pb = packed_slot_bytes(p, c);
   fp.tbws = wsb;
   fp.pws = wsb + pb;
-  fp.gws = reinterpret_cast<float*>(wsb + 2 * pb);
+  fp.gws = reinterpret_cast<float*>(wsb + pb + t_slot_bytes(p, c));
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
   fp.scale = p->scale;
   fp.G = p->num_segments;
-  fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(wsb + 2 * pb + gate_slot_bytes(p, c)) : nullptr;
+  fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(wsb + pb + t_slot_bytes(p, c) + gate_slot_bytes(p, c)) : nullptr;
   return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 

@@ -20,8 +20,8 @@
 // Kernel 1, chunk_prep_kernel: one workgroup per (chunk, head, sequence), fully
 //   parallel.  gamma and the decays, A and P with MFMA, T = (I + A)^-1 in fp32
 //   (16x16 diagonal blocks by forward substitution, the blocks below by
-//   T_ij = -T_ii sum_k A_ik T_kj with fp32 MFMA); stores T diag(beta) and P
-//   (lower blocks only), the decays, and for the backward T itself.
+//   T_ij = -T_ii sum_k A_ik T_kj with fp32 MFMA); stores T diag(beta) (lower
+//   blocks only), P (in MFMA operand order), the decays, and for the backward T.
 // Kernel 2, chunk_state_kernel: one workgroup per (segment, sequence, head,
 //   16-column tile of d_v); column j of S only mixes with column j of v, so
 //   tiles are independent.  Eight waves in two roles:
@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   E* const Ks = reinterpret_cast<E*>(sm.U);
   float* const Tf = reinterpret_cast<float*>(sm.U);
   float* const Mts = Tf + 64 * LDF;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z, H = p.H;
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
@@ -174,38 +175,70 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
 
   // A = strict_lower(diag(beta) (K K^T) o D) (fp32, row block ai), and
   // P = lower_incl((Q K^T) o D) (row block pi), formed as P^T blocks and stored
-  // packed straight to the workspace.
+  // straight to the workspace in MFMA operand order: fragment (pi, ks) holds, in
+  // lane 16 g + t, the KPL entries P[16 pi + t][ks KSTEP + g KPL ..], so that a
+  // plain load of 64 consecutive lanes yields the operand (the blocks above the
+  // diagonal as zeros).
+  {
+    // K fragments of row block ai (the A operand of the A blocks), and the gates
+    // each lane needs, read once
+    const int lr = lane & 15, lg = lane >> 4;
+    F ka[NKK];
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    if (bj <= ai) {
-      f32x4_t acc = zero4();
-      tile_mma<Op, DK>(acc, Ks + 16 * ai * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ai + 4 * (lane >> 4) + r, j = 16 * bj + (lane & 15);
-        const float d = exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f));
-        sm.Af[i * LDF + j] = i > j ? sm.bet[i] * acc[r] * d : 0.f;
-      }
-    }
-  }
-  if (want_p) {
-    E* P = static_cast<E*>(p.pws) + (slot * H + h) * kLPack + lpack_base(pi);
+    for (int ks = 0; ks < NKK; ++ks) ka[ks] = Op::frag(Ks + 16 * ai * LDK, LDK, lane, ks * KS);
+    const float4 gA = *reinterpret_cast<const float4*>(sm.gam + 16 * ai + 4 * lg);  // rows i of A
+    const float4 bA = *reinterpret_cast<const float4*>(sm.bet + 16 * ai + 4 * lg);
+    const float gAr[4] = {gA.x, gA.y, gA.z, gA.w}, bAr[4] = {bA.x, bA.y, bA.z, bA.w};
+    const float gP = sm.gam[16 * pi + lr];  // row i of P
+    constexpr int NTS = 64 / KS, KPL = Op::KPL;
+    E* P = want_p ? static_cast<E*>(p.pws) + (slot * H + h) * 4096 + pi * NTS * 64 * KPL : nullptr;
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-      if (bj <= pi) {
-        // block (pi, bj) of P, as P^T: C[j][i] = K_j . Q_i
+      if (!want_p && bj > ai) continue;
+      F kb[NKK];  // K fragments of row block bj: B operand of A block (ai, bj), A operand of P^T block (bj, pi)
+      if (bj <= ai || bj <= pi) {
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks) kb[ks] = Op::frag(Ks + 16 * bj * LDK, LDK, lane, ks * KS);
+      }
+      if (bj <= ai) {
         f32x4_t acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < NKK; ++ks)
-          acc = Op::mma(Op::frag(Ks + 16 * bj * LDK, LDK, lane, ks * KS), qf[ks], acc);
-        const int il = lane & 15, i = 16 * pi + il, jb = 16 * bj + 4 * (lane >> 4);
+        for (int ks = 0; ks < NKK; ++ks) acc = Op::mma(ka[ks], kb[ks], acc);
+        const int j = 16 * bj + lr;
+        const float gj = sm.gam[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ai + 4 * lg + r;
+          const float x = bAr[r] * acc[r] * __builtin_amdgcn_exp2f(fminf(gAr[r] - gj, 0.f));
+          sm.Af[i * LDF + j] = i > j ? x : 0.f;
+        }
+      }
+      if (want_p) {
+        // block (pi, bj) of P, as P^T: C[j][i] = K_j . Q_i; stored in operand
+        // order (the blocks above the diagonal as zeros)
+        f32x4_t acc = zero4();
+        if (bj <= pi) {
+#pragma unroll
+          for (int ks = 0; ks < NKK; ++ks) acc = Op::mma(kb[ks], qf[ks], acc);
+        }
+        const int i = 16 * pi + lr, jb = 16 * bj + 4 * lg;
+        const float4 gj = *reinterpret_cast<const float4*>(sm.gam + jb);
+        const float gjr[4] = {gj.x, gj.y, gj.z, gj.w};
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = jb + r;
-          pv[r] = j <= i ? acc[r] * exp2f(fminf(sm.gam[i] - sm.gam[j], 0.f)) : 0.f;
+          const float x = acc[r] * __builtin_amdgcn_exp2f(fminf(gP - gjr[r], 0.f));
+          pv[r] = jb + r <= i ? x : 0.f;
         }
-        store4<E>(P + il * 16 * (pi + 1) + jb, pv[0], pv[1], pv[2], pv[3]);
+        // (fragments entirely above the diagonal are never read and not stored)
+        if ((jb / KS) * KS < 16 * (pi + 1)) {
+          if constexpr (KPL == 8) {  // the four columns are consecutive entries of one lane
+            store4<E>(P + ((jb / KS) * 64 + 16 * ((jb % KS) / KPL) + lr) * KPL + jb % KPL, pv[0], pv[1], pv[2], pv[3]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[((jb + r) / KS) * 64 + 16 * ((jb + r) % KS) + lr] = Op::cvt(pv[r]);
+          }
+        }
       }
     }
   }
@@ -282,8 +315,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
 // Kernel 2: the state pass with output
 // ===================================================================================
 // LDS of one workgroup: the per-chunk operands of the state waves in two ring
-// slots (the chunk in use and the next one, being staged), private relayout
-// space of each output wave, and the hand-off buffers between the roles.
+// slots (the chunk in use and the next one, being staged) and the hand-off
+// buffers between the roles.
 template <int DK, typename Op>
 struct StateSmem {
   using E = typename Op::elem;
@@ -295,8 +328,6 @@ struct StateSmem {
   alignas(16) E Tb[2][64 * LDC];   // T diag(beta); the blocks above the diagonal stay zero
   alignas(16) E Vs[2][64 * 16];    // the v tile
   alignas(16) float Gs[2][128];    // Gamma and exp(gamma_n - gamma)
-  alignas(16) E Qv[4][16 * LDK];   // output wave w: its 16 Q rows
-  alignas(16) E Pv[4][16 * LDC];   // output wave w: its 16 P rows (the blocks above the diagonal stay zero)
   alignas(16) E Sb[16 * LDK];      // S^T of this tile as an MFMA operand, [j][d_k]
   alignas(16) E Rr[64 * LDR];      // R = V - diag(Gamma) K S, [t][j]
   alignas(16) E Et[16 * LDC];      // E^T
@@ -472,16 +503,20 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         __syncthreads();
         // phase 3: S <- Gamma_n S + K^T (decayed E)
         const float gn = Gs[63];
+        F ef[NTS];
+#pragma unroll
+        for (int ks = 0; ks < NTS; ++ks) ef[ks] = Op::frag(sm.Ett, LDC, lane, ks * KS);
 #pragma unroll
         for (int x = 0; x < DPW; ++x) {
           const int db = wr * DPW + x;
           f32x4_t acc = Sacc[x] * gn;
 #pragma unroll
-          for (int ks = 0; ks < NTS; ++ks)
-            acc = Op::mma(Op::frag_tr(Ks + 16 * db, LDK, lane, ks * KS), Op::frag(sm.Ett, LDC, lane, ks * KS), acc);
+          for (int ks = 0; ks < NTS; ++ks) acc = Op::mma(Op::frag_tr(Ks + 16 * db, LDK, lane, ks * KS), ef[ks], acc);
           Sacc[x] = active ? acc : Sacc[x];
-          store4<E>(sm.Sb + lr * LDK + 16 * db + 4 * lg, Sacc[x][0], Sacc[x][1], Sacc[x][2], Sacc[x][3]);
         }
+#pragma unroll
+        for (int x = 0; x < DPW; ++x)
+          store4<E>(sm.Sb + lr * LDK + 16 * (wr * DPW + x) + 4 * lg, Sacc[x][0], Sacc[x][1], Sacc[x][2], Sacc[x][3]);
         __syncthreads();
       }
       c0 += 2;
@@ -489,59 +524,65 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     write_state();
   } else {
     // ============ output waves: loads, staging, O = Gamma o (Q S) + P E ============
-    // In step c (the state waves on chunk c): phase 1 issues the loads of chunk
-    // c + 2 and forms Y^T = S_c^T Q_c^T; phase 2 turns the Q and P rows of chunk
-    // c + 1 into operand fragments and stages its T diag(beta); phase 3 forms
-    // the output of chunk c and stages K, v and the decays of chunk c + 1.  Loads
-    // run along whole rows (consecutive lanes read consecutive 16-byte vectors),
-    // through buffer resources that bound them to the chunk's valid rows (rows
-    // of padded tokens read as zeros).
+    // In step c (the state waves on chunk c): phase 1 forms Y^T = S_c^T Q_c^T and
+    // loads Q of chunk c + 2 and P of chunk c + 1; phase 2 stages T diag(beta) of
+    // chunk c + 1 and loads K of chunk c + 2; phase 3 forms the output of chunk c,
+    // stages K, v and the decays of chunk c + 1 and loads those of chunk c + 2.  Staged operands are loaded along whole rows
+    // (consecutive lanes read consecutive 16-byte vectors); Q and P, which only
+    // this wave uses, load straight into MFMA operand fragments (P comes in
+    // operand order from the prep kernel).  Buffer resources bound the loads to
+    // the chunk's valid rows (rows of padded tokens read as zeros).
     const int wo = w - 4, ot = tid - 256;
     constexpr int EPV = 16 / static_cast<int>(sizeof(E));
     constexpr int KVR = DK / EPV;                     // 16-byte vectors per K / Q row
     constexpr int NKV = 64 * KVR / 256;               // K vectors per output thread
-    constexpr int NQV = 16 * KVR / 64;                // Q vectors per lane (the wave's 16 rows)
     constexpr int VVR = static_cast<int>(sizeof(E));  // 16-byte vectors per v-tile row
     constexpr int TVN = kLPack / EPV;                 // vectors of a packed T diag(beta)
     constexpr int NTV = (TVN + 255) / 256;
-    constexpr int NPV = (16 * 64 / EPV + 63) / 64;    // P vectors per lane (row block 3)
-    const int prow = 16 * (wo + 1);                   // length of this wave's P rows
-    const int pvn = 16 * prow / EPV;                  // its vectors
     // Lanes past the end of a short array load nothing (kNoLoad) and write nothing.
     struct LoadSet {
       u32x4_t kv[NKV];  // K: vector x * 256 + ot is row (x * 256 + ot) / KVR
-      u32x4_t qv[NQV];  // Q rows 16 wo .. 16 wo + 15: vector x * 64 + lane
+      F qf[NKK];        // Q rows tc as MFMA operand fragments
       u32x4_t tv[NTV];  // T diag(beta): packed vector x * 256 + ot (< TVN)
-      u32x4_t pv[NPV];  // P row block wo: packed vector x * 64 + lane (< pvn)
       u32x4_t vv;       // the v tile: vector ot (< 64 VVR)
       u32x4_t gv;       // decays: floats 4 ot .. 4 ot + 3 (ot < 32)
     };
     LoadSet ls[2];
-    F qf[2][NKK], pf[2][NTS];
-    E* const qvE = sm.Qv[wo];
-    E* const pvE = sm.Pv[wo];
+    F pf[2][NTS];  // P rows tc as MFMA operand fragments (stored in that order by the prep kernel)
+    auto frag_load = [](__amdgpu_buffer_rsrc_t r, int off) -> F {
+      if constexpr (sizeof(E) == 2)
+        return __builtin_bit_cast(F, buffer_load16(r, off));
+      else
+        return buffer_load1(r, off);
+    };
 
-    auto load_set = [&](LoadSet& s, int c) {
+    // The loads of one chunk come in three groups, issued in different phases so
+    // that the texture-address unit (about one 1 KB wave load per 16 cycles) works
+    // through them while the waves compute.
+    auto load_q = [&](LoadSet& s, int c) {  // Q rows tc as operand fragments
+      if (OUT) {
+        const int nv = chunk_rows(c);
+        const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
+        const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks)
+          s.qf[ks] = frag_load(rq, (tc * H * DK + ks * KS + lg * Op::KPL) * static_cast<int>(sizeof(E)));
+      }
+    };
+    auto load_k = [&](LoadSet& s, int c) {
       const int nv = chunk_rows(c);
       const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
-      const int64_t sh = (slot0 + c) * H + h;
       const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
 #pragma unroll
       for (int x = 0; x < NKV; ++x) {
         const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
         s.kv[x] = buffer_load16(rk, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
       }
-      if (OUT) {
-        const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
-#pragma unroll
-        for (int x = 0; x < NQV; ++x) {
-          const int vi = x * 64 + lane, t = 16 * wo + vi / KVR, cv = (vi % KVR) * EPV;
-          s.qv[x] = buffer_load16(rq, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
-        }
-        const auto rp = buffer_rsrc(pw + sh * kLPack + lpack_base(wo), pvn * 16);
-#pragma unroll
-        for (int x = 0; x < NPV; ++x) s.pv[x] = buffer_load16(rp, (x * 64 + lane) * 16);
-      }
+    };
+    auto load_rest = [&](LoadSet& s, int c) {  // T diag(beta), the v tile, the decays
+      const int nv = chunk_rows(c);
+      const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
+      const int64_t sh = (slot0 + c) * H + h;
       const auto rt = buffer_rsrc(tbw + sh * kLPack, kLPack * static_cast<int>(sizeof(E)));
 #pragma unroll
       for (int x = 0; x < NTV; ++x) s.tv[x] = buffer_load16(rt, (x * 256 + ot) * 16);
@@ -552,29 +593,18 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
                                              : kNoLoad);
       s.gv = buffer_load16(buffer_rsrc(gw + sh * 128, 512), ot * 16);
     };
-    // the wave's 16 Q rows as MFMA operand fragments (through its private LDS)
-    auto stage_q = [&](const LoadSet& s, F (&f)[NKK]) {
-#pragma unroll
-      for (int x = 0; x < NQV; ++x) {
-        const int vi = x * 64 + lane, t = vi / KVR, cv = (vi % KVR) * EPV;
-        *reinterpret_cast<u32x4_t*>(qvE + t * LDK + cv) = s.qv[x];
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int ks = 0; ks < NKK; ++ks) f[ks] = Op::frag(qvE, LDK, lane, ks * KS);
-      wave_lds_sync();
+    auto load_set = [&](LoadSet& s, int c) {
+      load_q(s, c);
+      load_k(s, c);
+      load_rest(s, c);
     };
-    // likewise the wave's 16 P rows (P^T as the B operand of O^T = E^T P^T)
-    auto stage_p = [&](const LoadSet& s, F (&f)[NTS]) {
+    // P rows tc of chunk c: fragment ks only where it meets the blocks on or below the diagonal
+    auto load_p = [&](F (&f)[NTS], int c) {
+      const auto rp = buffer_rsrc(pw + ((slot0 + c) * H + h) * 4096, 4096 * static_cast<int>(sizeof(E)));
 #pragma unroll
-      for (int x = 0; x < NPV; ++x) {
-        const int e = (x * 64 + lane) * EPV, t = e / prow, cc = e - t * prow;
-        if (x * 64 + lane < pvn) *reinterpret_cast<u32x4_t*>(pvE + t * LDC + cc) = s.pv[x];
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int ks = 0; ks < NTS; ++ks) f[ks] = Op::frag(pvE, LDC, lane, ks * KS);
-      wave_lds_sync();
+      for (int ks = 0; ks < NTS; ++ks)
+        f[ks] = frag_load(rp, ks * KS < 16 * (wo + 1) ? ((wo * NTS + ks) * 64 + lane) * Op::KPL * static_cast<int>(sizeof(E))
+                                                      : kNoLoad);
     };
     auto stage_t = [&](const LoadSet& s, int sl) {
 #pragma unroll
@@ -594,8 +624,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       if (ot < 32) *reinterpret_cast<u32x4_t*>(sm.Gs[sl] + 4 * ot) = s.gv;
     };
 
-    // prologue: the blocks above the diagonal of both T diag(beta) slots and of the
-    // private P rows are zero for good; chunk 0 staged, chunk 1 loading
+    // prologue: the blocks above the diagonal of both T diag(beta) slots are zero
+    // for good; chunk 0 staged, chunk 1 loading
     {
       constexpr int VPT = 64 / EPV;
       const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -603,38 +633,30 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         const int sl = x / (64 * VPT), rem = x % (64 * VPT), i = rem / VPT, jv = (rem % VPT) * EPV;
         if ((jv >> 4) > (i >> 4)) *reinterpret_cast<u32x4_t*>(sm.Tb[sl] + i * LDC + jv) = z;
       }
-      for (int x = lane; x < 16 * VPT; x += 64)
-        *reinterpret_cast<u32x4_t*>(pvE + (x / VPT) * LDC + (x % VPT) * EPV) = z;
-      wave_lds_sync();
     }
     load_set(ls[0], 0);
     load_set(ls[1], clampc(1));
+    if (OUT) load_p(pf[0], 0);
     stage_t(ls[0], 0);
     stage_kvg(ls[0], 0);
-    if (OUT) {
-      stage_q(ls[0], qf[0]);
-      stage_p(ls[0], pf[0]);
-    }
     __syncthreads();
     int c0 = 0;
     do {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
-        // phase 1
-        load_set(ls[u], clampc(c + 2));
+        // phase 1 (Q of chunk c is in ls[u] until the loads of chunk c + 2 replace it)
         f32x4_t yacc = zero4();
         if (OUT) {
 #pragma unroll
-          for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), qf[u][ks], yacc);
+          for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), ls[u].qf[ks], yacc);
         }
+        load_q(ls[u], clampc(c + 2));
+        if (OUT) load_p(pf[u ^ 1], clampc(c + 1));
         __syncthreads();
         // phase 2
-        if (OUT) {
-          stage_q(ls[u ^ 1], qf[u ^ 1]);
-          stage_p(ls[u ^ 1], pf[u ^ 1]);
-        }
         stage_t(ls[u ^ 1], u ^ 1);
+        load_k(ls[u], clampc(c + 2));
         __syncthreads();
         // phase 3: O^T = scale (Gamma o Y^T + E^T P^T) (columns j, token tc)
         if (OUT) {
@@ -651,6 +673,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
                            p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
         }
         stage_kvg(ls[u ^ 1], u ^ 1);
+        load_rest(ls[u], clampc(c + 2));
         __syncthreads();
       }
       c0 += 2;

@@ -24,7 +24,8 @@ struct FwdParams {
   float* S_final;   // [N, H, Dk, Dv] or nullptr
   void* tws;        // per-chunk T = (I + A)^-1 (io element type, 64 x 64 per slot), or nullptr
   void* tbws;       // per-chunk T diag(beta), lower blocks packed (kLPack io elements per slot)
-  void* pws;        // per-chunk P = lower_incl((Q K^T) o D), packed likewise, or nullptr
+  void* pws;        // per-chunk P = lower_incl((Q K^T) o D) in MFMA operand order (4096 io
+                    // elements per slot: fragment (row block, k-step) of 64 lanes each), or nullptr
   float* gws;       // per-chunk Gamma and exp(gamma_n - gamma), [slot][H][128] fp32
   SeqInfo seq;
   int32_t N, H, Dv;

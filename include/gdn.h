@@ -137,8 +137,8 @@ gdn_status gdn_workspace_size(const gdn_problem* problem, int32_t pass, size_t* 
  * "Hypothesis": segment affine transforms and carries).  G = 2 gives results
  * bit-identical to G = 1; G > 2 agrees to the bf16 rounding of M's operands.
  * Workspace: gdn_workspace_size(..., GDN_PASS_CHUNK_FWD, ...): per chunk and
- * head, T diag(beta) and the causal score (their 16x16 blocks on and below the
- * diagonal) and the chunk's decays, plus for G > 1 fp32 buffers of
+ * head, T diag(beta) (its 16x16 blocks on and below the diagonal), the causal
+ * score and the chunk's decays, plus for G > 1 fp32 buffers of
  * 2 G N H Dk Dv + G N H Dk Dk floats. */
 gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,

@@ -82,18 +82,20 @@ def test_problem_validation(kw, status):
 
 
 def test_workspace_sizes():
-    # forward: per (chunk slot, head) T diag(beta) and P with their lower 16x16
-    # blocks packed (2560 io elements each) and 128 fp32 decays, each array
-    # rounded up to 256 bytes; slots = rows // 64 + N + 1
+    # forward: per (chunk slot, head) T diag(beta) with its lower 16x16 blocks
+    # packed (2560 io elements), P (4096 io elements) and 128 fp32 decays, each
+    # array rounded up to 256 bytes; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     gates = up(slots * 3 * 128 * 4)
-    assert ws(problem()) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 2) + gates)
-    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 4) + gates)
+    recs = up(slots * 3 * 2560 * 2) + up(slots * 3 * 4096 * 2) + gates
+    assert ws(problem()) == (nat.GDN_OK, recs)
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (
+        nat.GDN_OK, up(slots * 3 * 2560 * 4) + up(slots * 3 * 4096 * 4) + gates)
     # segment split: then fp32 end and start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
     for G in (2, 4, 16):
         seg = (2 * G * 2 * 3 * 128 * 96 + G * 2 * 3 * 128 * 128) * 4
-        assert ws(problem(num_segments=G, Dv=96)) == (nat.GDN_OK, 2 * up(slots * 3 * 2560 * 2) + gates + seg)
+        assert ws(problem(num_segments=G, Dv=96)) == (nat.GDN_OK, recs + seg)
     assert ws(problem(), nat.GDN_PASS_RECURRENT_FWD) == (nat.GDN_OK, 0)
     st, n = ws(problem(Dk=64), nat.GDN_PASS_RECURRENT_BWD)
     assert st == nat.GDN_OK and n > 0
