@@ -332,6 +332,7 @@ struct StateSmem {
   alignas(16) E Rr[64 * LDR];      // R = V - diag(Gamma) K S, [t][j]
   alignas(16) E Et[16 * LDC];      // E^T
   alignas(16) E Ett[16 * LDC];     // (diag(exp(gamma_n - gamma)) E)^T
+  alignas(16) float Ys[64 * 20];   // Y = Q S (fp32), [t][j]
 };
 
 // Four consecutive io values, widened when used.
@@ -456,8 +457,42 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   // consumes.
   const int nsteps = (nch + 1) / 2 * 2;
 
+  // Q and P rows tc of a chunk straight into MFMA operand fragments: Q from the
+  // chunk's rows, P in the operand order the prep kernel stores (fragment ks only
+  // where it meets the blocks on or below the diagonal).  Padded rows read as zeros.
+  auto frag_load = [](__amdgpu_buffer_rsrc_t r, int off) -> F {
+    if constexpr (sizeof(E) == 2)
+      return __builtin_bit_cast(F, buffer_load16(r, off));
+    else
+      return buffer_load1(r, off);
+  };
+  auto load_q = [&](F (&f)[NKK], int c) {
+    const int nv = chunk_rows(c);
+    const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
+    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks)
+      f[ks] = frag_load(rq, (tc * H * DK + ks * KS + lg * Op::KPL) * static_cast<int>(sizeof(E)));
+  };
+  auto load_p = [&](F (&f)[NTS], int c) {
+    const auto rp = buffer_rsrc(pw + ((slot0 + c) * H + h) * 4096, 4096 * static_cast<int>(sizeof(E)));
+#pragma unroll
+    for (int ks = 0; ks < NTS; ++ks)
+      f[ks] = frag_load(rp, ks * KS < 16 * (wr + 1) ? ((wr * NTS + ks) * 64 + lane) * Op::KPL * static_cast<int>(sizeof(E))
+                                                    : kNoLoad);
+  };
+
   if (state_wave) {
-    // ===================== state waves: the recurrence (LDS and MFMA only) =====================
+    // ============ state waves: the recurrence and the output of their 16 tokens ============
+    // In step c: phase 1 forms Z^T = S^T K^T and Y^T = S^T Q^T from the same S^T
+    // fragments (Y goes to the loader waves, which form the output), loads Q of
+    // chunk c + 2, then R; phase 2 E = (T diag(beta)) R; phase 3 the state update.
+    // Only the Q loads touch memory.
+    F qf[2][NKK];
+    if (OUT) {
+      load_q(qf[0], 0);
+      load_q(qf[1], clampc(1));
+    }
     __syncthreads();  // chunk 0 staged
     int c0 = 0;
     do {
@@ -467,7 +502,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         const bool active = c < nch;
         const E* Ks = sm.Ks[u];
         const float* Gs = sm.Gs[u];
-        // phase 1: R = V - Gamma o (K S), via Z^T = S^T K^T (rows j, column tc)
+        // phase 1
         if (STATES) {  // S_c, the state before chunk c, kept for the backward
           const auto rs = buffer_rsrc(p.states + ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
                                       active ? DK * Dv * 4 : 0);
@@ -478,10 +513,19 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
             for (int r = 0; r < 4; ++r) buffer_store1(rs, ((i + r) * Dv + j0 + lr) * 4, Sacc[x][r]);
           }
         }
-        f32x4_t z = zero4();
+        F sa[NKK];
 #pragma unroll
-        for (int ks = 0; ks < NKK; ++ks)
-          z = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), Op::frag(Ks + 16 * wr * LDK, LDK, lane, ks * KS), z);
+        for (int ks = 0; ks < NKK; ++ks) sa[ks] = Op::frag(sm.Sb, LDK, lane, ks * KS);
+        f32x4_t z = zero4(), yacc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks) {
+          z = Op::mma(sa[ks], Op::frag(Ks + 16 * wr * LDK, LDK, lane, ks * KS), z);
+          if (OUT) yacc = Op::mma(sa[ks], qf[u][ks], yacc);
+        }
+        if (OUT) {
+          *reinterpret_cast<f32x4_t*>(sm.Ys + tc * 20 + 4 * lg) = yacc;
+          load_q(qf[u], clampc(c + 2));
+        }
         Raw4<E> vv;
         vv.load(sm.Vs[u] + tc * 16 + 4 * lg);
         const float gt = Gs[tc];
@@ -523,52 +567,32 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     } while (c0 < nsteps);
     write_state();
   } else {
-    // ============ output waves: loads, staging, O = Gamma o (Q S) + P E ============
-    // In step c (the state waves on chunk c): phase 1 forms Y^T = S_c^T Q_c^T and
-    // loads Q of chunk c + 2 and P of chunk c + 1; phase 2 stages T diag(beta) of
-    // chunk c + 1 and loads K of chunk c + 2; phase 3 forms the output of chunk c,
-    // stages K, v and the decays of chunk c + 1 and loads those of chunk c + 2.  Staged operands are loaded along whole rows
-    // (consecutive lanes read consecutive 16-byte vectors); Q and P, which only
-    // this wave uses, load straight into MFMA operand fragments (P comes in
-    // operand order from the prep kernel).  Buffer resources bound the loads to
-    // the chunk's valid rows (rows of padded tokens read as zeros).
-    const int wo = w - 4, ot = tid - 256;
+    // ============ loader waves: the LDS ring, and the output ============
+    // In step c (the state waves on chunk c): phase 1 stages K, v and the decays
+    // of chunk c + 1 and loads K of chunk c + 2; phase 2 stages T diag(beta) of
+    // chunk c + 1 and loads the rest of chunk c + 2; phase 3 forms the output of
+    // chunk c (O^T = scale (Gamma o Y^T + E^T P^T), Y from the state waves) and
+    // loads P of chunk c + 1 straight into operand fragments.  Loads run along
+    // whole rows (consecutive lanes read consecutive 16-byte vectors), in groups
+    // spread over the phases so that the texture-address unit (about one 1 KB
+    // wave load per 16 cycles) works through them behind the compute; buffer
+    // resources bound them to the chunk's valid rows (rows of padded tokens read
+    // as zeros), and lanes past the end of a short array load nothing (kNoLoad)
+    // and write nothing.
+    const int ot = tid - 256;
     constexpr int EPV = 16 / static_cast<int>(sizeof(E));
-    constexpr int KVR = DK / EPV;                     // 16-byte vectors per K / Q row
-    constexpr int NKV = 64 * KVR / 256;               // K vectors per output thread
+    constexpr int KVR = DK / EPV;                     // 16-byte vectors per K row
+    constexpr int NKV = 64 * KVR / 256;               // K vectors per loader thread
     constexpr int VVR = static_cast<int>(sizeof(E));  // 16-byte vectors per v-tile row
     constexpr int TVN = kLPack / EPV;                 // vectors of a packed T diag(beta)
     constexpr int NTV = (TVN + 255) / 256;
-    // Lanes past the end of a short array load nothing (kNoLoad) and write nothing.
     struct LoadSet {
       u32x4_t kv[NKV];  // K: vector x * 256 + ot is row (x * 256 + ot) / KVR
-      F qf[NKK];        // Q rows tc as MFMA operand fragments
       u32x4_t tv[NTV];  // T diag(beta): packed vector x * 256 + ot (< TVN)
       u32x4_t vv;       // the v tile: vector ot (< 64 VVR)
       u32x4_t gv;       // decays: floats 4 ot .. 4 ot + 3 (ot < 32)
     };
     LoadSet ls[2];
-    F pf[2][NTS];  // P rows tc as MFMA operand fragments (stored in that order by the prep kernel)
-    auto frag_load = [](__amdgpu_buffer_rsrc_t r, int off) -> F {
-      if constexpr (sizeof(E) == 2)
-        return __builtin_bit_cast(F, buffer_load16(r, off));
-      else
-        return buffer_load1(r, off);
-    };
-
-    // The loads of one chunk come in three groups, issued in different phases so
-    // that the texture-address unit (about one 1 KB wave load per 16 cycles) works
-    // through them while the waves compute.
-    auto load_q = [&](LoadSet& s, int c) {  // Q rows tc as operand fragments
-      if (OUT) {
-        const int nv = chunk_rows(c);
-        const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
-        const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
-#pragma unroll
-        for (int ks = 0; ks < NKK; ++ks)
-          s.qf[ks] = frag_load(rq, (tc * H * DK + ks * KS + lg * Op::KPL) * static_cast<int>(sizeof(E)));
-      }
-    };
     auto load_k = [&](LoadSet& s, int c) {
       const int nv = chunk_rows(c);
       const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
@@ -593,19 +617,6 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
                                              : kNoLoad);
       s.gv = buffer_load16(buffer_rsrc(gw + sh * 128, 512), ot * 16);
     };
-    auto load_set = [&](LoadSet& s, int c) {
-      load_q(s, c);
-      load_k(s, c);
-      load_rest(s, c);
-    };
-    // P rows tc of chunk c: fragment ks only where it meets the blocks on or below the diagonal
-    auto load_p = [&](F (&f)[NTS], int c) {
-      const auto rp = buffer_rsrc(pw + ((slot0 + c) * H + h) * 4096, 4096 * static_cast<int>(sizeof(E)));
-#pragma unroll
-      for (int ks = 0; ks < NTS; ++ks)
-        f[ks] = frag_load(rp, ks * KS < 16 * (wo + 1) ? ((wo * NTS + ks) * 64 + lane) * Op::KPL * static_cast<int>(sizeof(E))
-                                                      : kNoLoad);
-    };
     auto stage_t = [&](const LoadSet& s, int sl) {
 #pragma unroll
       for (int x = 0; x < NTV; ++x) {
@@ -628,14 +639,17 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     // for good; chunk 0 staged, chunk 1 loading
     {
       constexpr int VPT = 64 / EPV;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t zv = {0u, 0u, 0u, 0u};
       for (int x = ot; x < 2 * 64 * VPT; x += 256) {
         const int sl = x / (64 * VPT), rem = x % (64 * VPT), i = rem / VPT, jv = (rem % VPT) * EPV;
-        if ((jv >> 4) > (i >> 4)) *reinterpret_cast<u32x4_t*>(sm.Tb[sl] + i * LDC + jv) = z;
+        if ((jv >> 4) > (i >> 4)) *reinterpret_cast<u32x4_t*>(sm.Tb[sl] + i * LDC + jv) = zv;
       }
     }
-    load_set(ls[0], 0);
-    load_set(ls[1], clampc(1));
+    F pf[2][NTS];
+    load_k(ls[0], 0);
+    load_rest(ls[0], 0);
+    load_k(ls[1], clampc(1));
+    load_rest(ls[1], clampc(1));
     if (OUT) load_p(pf[0], 0);
     stage_t(ls[0], 0);
     stage_kvg(ls[0], 0);
@@ -645,24 +659,20 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
-        // phase 1 (Q of chunk c is in ls[u] until the loads of chunk c + 2 replace it)
-        f32x4_t yacc = zero4();
-        if (OUT) {
-#pragma unroll
-          for (int ks = 0; ks < NKK; ++ks) yacc = Op::mma(Op::frag(sm.Sb, LDK, lane, ks * KS), ls[u].qf[ks], yacc);
-        }
-        load_q(ls[u], clampc(c + 2));
-        if (OUT) load_p(pf[u ^ 1], clampc(c + 1));
+        // phase 1
+        stage_kvg(ls[u ^ 1], u ^ 1);
+        load_k(ls[u], clampc(c + 2));
         __syncthreads();
         // phase 2
         stage_t(ls[u ^ 1], u ^ 1);
-        load_k(ls[u], clampc(c + 2));
+        load_rest(ls[u], clampc(c + 2));
         __syncthreads();
-        // phase 3: O^T = scale (Gamma o Y^T + E^T P^T) (columns j, token tc)
-        if (OUT) {
+        // phase 3
+        if (OUT) {  // O^T = scale (Gamma o Y^T + E^T P^T), columns j, token tc
           f32x4_t oacc = zero4();
 #pragma unroll
           for (int ks = 0; ks < NTS; ++ks) oacc = Op::mma(Op::frag(sm.Et, LDC, lane, ks * KS), pf[u][ks], oacc);
+          const f32x4_t yacc = *reinterpret_cast<const f32x4_t*>(sm.Ys + tc * 20 + 4 * lg);
           const float gt = sm.Gs[u][tc];
           // rows of padded tokens and steps past the last chunk fall outside the range
           const int cc = clampc(c), nv = chunk_rows(cc);
@@ -671,9 +681,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           buffer_store4<E>(ro, (tc * H * Dv + 4 * lg) * static_cast<int>(sizeof(E)),
                            p.scale * (gt * yacc[0] + oacc[0]), p.scale * (gt * yacc[1] + oacc[1]),
                            p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
+          load_p(pf[u ^ 1], clampc(c + 1));
         }
-        stage_kvg(ls[u ^ 1], u ^ 1);
-        load_rest(ls[u], clampc(c + 2));
         __syncthreads();
       }
       c0 += 2;
@@ -739,14 +748,31 @@ hipError_t launch_prep(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    counts[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return counts[dev];
+}
+
 template <int DK, typename Op, bool STATES, bool OUT>
 hipError_t launch_state(const FwdParams& q, hipStream_t s) {
-  constexpr size_t smem = sizeof(StateSmem<DK, Op>);
-  static_assert(smem <= 160 * 1024, "LDS budget exceeded");
+  constexpr size_t need = sizeof(StateSmem<DK, Op>);
+  static_assert(need <= 160 * 1024, "LDS budget exceeded");
+  // A grid with fewer than two workgroups per compute unit asks for more than
+  // half of a CU's 160 KB of LDS, so that no CU holds two of them while another
+  // stays idle; larger grids pack two per CU where they fit.
+  const int blocks = q.nseg * q.N * q.H * (q.ncol / 16);
+  const size_t smem = blocks < 2 * cu_count() && need < 82 * 1024 ? 82 * 1024 : need;
   auto state = chunk_state_kernel<DK, Op, STATES, OUT>;
   hipError_t e = allow_lds(state, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(state, dim3(q.nseg * q.N * q.H * (q.ncol / 16)), dim3(512), smem, s, q);
+  hipLaunchKernelGGL(state, dim3(blocks), dim3(512), smem, s, q);
   return hipGetLastError();
 }
 
