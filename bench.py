@@ -200,12 +200,12 @@ def micro(kind: str, steps: int, warmup: int):
 
 def cpu_baseline(d, w, budget_s: float):
     """Time the fp64 oracle on the host on the same workload (whole passes,
-    repeated until about `budget_s` seconds have passed, at most 20)."""
+    repeated until about `budget_s` seconds have passed, at most 500)."""
     import oracle
 
     threads = oracle.default_threads()
     reps, t_total = 0, 0.0
-    while reps < 20 and (reps == 0 or t_total < budget_s):
+    while reps < 500 and (reps == 0 or t_total < budget_s):
         t0 = time.perf_counter()
         oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
                    S0=d["S0"], scale=d["scale"], nthreads=threads)
