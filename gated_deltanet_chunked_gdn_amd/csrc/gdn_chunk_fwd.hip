@@ -485,9 +485,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   if (state_wave) {
     // ============ state waves: the recurrence and the output of their 16 tokens ============
     // In step c: phase 1 forms Z^T = S^T K^T and Y^T = S^T Q^T from the same S^T
-    // fragments (Y goes to the loader waves, which form the output), loads Q of
-    // chunk c + 2, then R; phase 2 E = (T diag(beta)) R; phase 3 the state update.
-    // Only the Q loads touch memory.
+    // fragments (Y goes to the loader waves, which form the output), then R;
+    // phase 2 E = (T diag(beta)) R; phase 3 the state update, and loads Q of
+    // chunk c + 2 (phase 3 is the one with the least memory traffic).  Only the
+    // Q loads touch memory.
     F qf[2][NKK];
     if (OUT) {
       load_q(qf[0], 0);
@@ -522,10 +523,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           z = Op::mma(sa[ks], Op::frag(Ks + 16 * wr * LDK, LDK, lane, ks * KS), z);
           if (OUT) yacc = Op::mma(sa[ks], qf[u][ks], yacc);
         }
-        if (OUT) {
-          *reinterpret_cast<f32x4_t*>(sm.Ys + tc * 20 + 4 * lg) = yacc;
-          load_q(qf[u], clampc(c + 2));
-        }
+        if (OUT) *reinterpret_cast<f32x4_t*>(sm.Ys + tc * 20 + 4 * lg) = yacc;
         Raw4<E> vv;
         vv.load(sm.Vs[u] + tc * 16 + 4 * lg);
         const float gt = Gs[tc];
@@ -561,6 +559,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < DPW; ++x)
           store4<E>(sm.Sb + lr * LDK + 16 * (wr * DPW + x) + 4 * lg, Sacc[x][0], Sacc[x][1], Sacc[x][2], Sacc[x][3]);
+        if (OUT) load_q(qf[u], clampc(c + 2));
         __syncthreads();
       }
       c0 += 2;
@@ -569,10 +568,12 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   } else {
     // ============ loader waves: the LDS ring, and the output ============
     // In step c (the state waves on chunk c): phase 1 stages K, v and the decays
-    // of chunk c + 1 and loads K of chunk c + 2; phase 2 stages T diag(beta) of
-    // chunk c + 1 and loads the rest of chunk c + 2; phase 3 forms the output of
-    // chunk c (O^T = scale (Gamma o Y^T + E^T P^T), Y from the state waves) and
-    // loads P of chunk c + 1 straight into operand fragments.  Loads run along
+    // of chunk c + 1 and refills the freed registers with K of chunk c + 3; phase
+    // 2 stages T diag(beta) of chunk c + 1 and loads the rest of chunk c + 3;
+    // phase 3 forms the output of chunk c (O^T = scale (Gamma o Y^T + E^T P^T), Y
+    // from the state waves) and loads P of chunk c + 2 straight into the operand
+    // fragments it has just used.  Every load thus has two steps to arrive, with
+    // two register sets.  Loads run along
     // whole rows (consecutive lanes read consecutive 16-byte vectors), in groups
     // spread over the phases so that the texture-address unit (about one 1 KB
     // wave load per 16 cycles) works through them behind the compute; buffer
@@ -653,6 +654,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     if (OUT) load_p(pf[0], 0);
     stage_t(ls[0], 0);
     stage_kvg(ls[0], 0);
+    load_k(ls[0], clampc(2));
+    load_rest(ls[0], clampc(2));
+    if (OUT) load_p(pf[1], clampc(1));
     __syncthreads();
     int c0 = 0;
     do {
@@ -661,11 +665,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         const int c = c0 + u;
         // phase 1
         stage_kvg(ls[u ^ 1], u ^ 1);
-        load_k(ls[u], clampc(c + 2));
+        load_k(ls[u ^ 1], clampc(c + 3));
         __syncthreads();
         // phase 2
         stage_t(ls[u ^ 1], u ^ 1);
-        load_rest(ls[u], clampc(c + 2));
+        load_rest(ls[u ^ 1], clampc(c + 3));
         __syncthreads();
         // phase 3
         if (OUT) {  // O^T = scale (Gamma o Y^T + E^T P^T), columns j, token tc
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           buffer_store4<E>(ro, (tc * H * Dv + 4 * lg) * static_cast<int>(sizeof(E)),
                            p.scale * (gt * yacc[0] + oacc[0]), p.scale * (gt * yacc[1] + oacc[1]),
                            p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
-          load_p(pf[u ^ 1], clampc(c + 1));
+          load_p(pf[u], clampc(c + 2));
         }
         __syncthreads();
       }
