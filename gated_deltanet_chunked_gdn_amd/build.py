@@ -21,15 +21,20 @@ OUT = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gdn_abi.cpp", "gdn_chunk_fwd.hip", "gdn_chunk_bwd.hip", "gdn_recurrent.hip"]
+SOURCES = ["gdn_abi.cpp", "gdn_chunk_fwd.hip", "gdn_chunk_chain.hip", "gdn_chunk_bwd.hip", "gdn_recurrent.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# The state pass keeps its MFMA accumulators in VGPRs: it touches them with VALU
+# code between products, which AGPR accumulators would turn into copies.
+EXTRA = {"gdn_chunk_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -97,7 +97,7 @@ size_t t_slot_bytes(const gdn_problem* p, const Checked& c) {
 }
 
 size_t packed_slot_bytes(const gdn_problem* p, const Checked& c) {
-  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kLPack * c.io;
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kTbSlot * c.io;
   return (b + 255) / 256 * 256;
 }
 

@@ -285,14 +285,32 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   // blocks are exact zeros), and T row-major for the backward
   const int64_t sh = slot * H + h;
   if (p.tbws) {
-    E* dst = static_cast<E*>(p.tbws) + sh * kLPack;
-    for (int x = tid; x < kLPack / EPV; x += 256) {
-      int i, jb;
-      lpack_pos(x * EPV, i, jb);
-      E vals[EPV];
+    E* dst = static_cast<E*>(p.tbws) + sh * kTbSlot;
+    if constexpr (sizeof(E) == 2) {
+      // bf16: six operand fragments (row block mb, reduction step s <= mb / 2); lane
+      // (m, g) holds row 32 (mb / 2) + 8 (m / 4) + 4 (mb % 2) + m % 4 (the row order of
+      // the state pass's accumulators), columns 32 s + 8 g + 0..7
+      for (int x = tid; x < 6 * 64; x += 256) {
+        const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4;
+        const int mb = f < 2 ? f : 2 + (f - 2) / 2, s = f < 2 ? 0 : (f - 2) % 2;
+        const int i = 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3), jb = 32 * s + 8 * g;
+        E vals[8];
 #pragma unroll
-      for (int m = 0; m < EPV; ++m) vals[m] = Op::cvt(Tf[i * LDF + jb + m] * sm.bet[jb + m]);
-      *reinterpret_cast<uint4*>(dst + x * EPV) = *reinterpret_cast<const uint4*>(vals);
+        for (int e = 0; e < 8; ++e) {
+          const int j = jb + e;
+          vals[e] = Op::cvt((j >> 4) <= (i >> 4) ? Tf[i * LDF + j] * sm.bet[j] : 0.f);
+        }
+        *reinterpret_cast<uint4*>(dst + x * 8) = *reinterpret_cast<const uint4*>(vals);
+      }
+    } else {
+      for (int x = tid; x < kLPack / EPV; x += 256) {
+        int i, jb;
+        lpack_pos(x * EPV, i, jb);
+        E vals[EPV];
+#pragma unroll
+        for (int m = 0; m < EPV; ++m) vals[m] = Op::cvt(Tf[i * LDF + jb + m] * sm.bet[jb + m]);
+        *reinterpret_cast<uint4*>(dst + x * EPV) = *reinterpret_cast<const uint4*>(vals);
+      }
     }
   }
   if (p.tws) {
@@ -608,7 +626,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
       const int nv = chunk_rows(c);
       const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
       const int64_t sh = (slot0 + c) * H + h;
-      const auto rt = buffer_rsrc(tbw + sh * kLPack, kLPack * static_cast<int>(sizeof(E)));
+      const auto rt = buffer_rsrc(tbw + sh * kTbSlot, kLPack * static_cast<int>(sizeof(E)));
 #pragma unroll
       for (int x = 0; x < NTV; ++x) s.tv[x] = buffer_load16(rt, (x * 256 + ot) * 16);
       // (a pass without V still loads, from columns clamped into the row, and discards them)
@@ -766,18 +784,22 @@ int cu_count() {
 
 template <int DK, typename Op, bool STATES, bool OUT>
 hipError_t launch_state(const FwdParams& q, hipStream_t s) {
-  constexpr size_t need = sizeof(StateSmem<DK, Op>);
-  static_assert(need <= 160 * 1024, "LDS budget exceeded");
-  // A grid with fewer than two workgroups per compute unit asks for more than
-  // half of a CU's 160 KB of LDS, so that no CU holds two of them while another
-  // stays idle; larger grids pack two per CU where they fit.
-  const int blocks = q.nseg * q.N * q.H * (q.ncol / 16);
-  const size_t smem = blocks < 2 * cu_count() && need < 82 * 1024 ? 82 * 1024 : need;
-  auto state = chunk_state_kernel<DK, Op, STATES, OUT>;
-  hipError_t e = allow_lds(state, smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(state, dim3(blocks), dim3(512), smem, s, q);
-  return hipGetLastError();
+  if constexpr (std::is_same<Op, OpBf16>::value) {
+    return launch_state_chain(q, DK, STATES, OUT, s);
+  } else {
+    constexpr size_t need = sizeof(StateSmem<DK, Op>);
+    static_assert(need <= 160 * 1024, "LDS budget exceeded");
+    // A grid with fewer than two workgroups per compute unit asks for more than
+    // half of a CU's 160 KB of LDS, so that no CU holds two of them while another
+    // stays idle; larger grids pack two per CU where they fit.
+    const int blocks = q.nseg * q.N * q.H * (q.ncol / 16);
+    const size_t smem = blocks < 2 * cu_count() && need < 82 * 1024 ? 82 * 1024 : need;
+    auto state = chunk_state_kernel<DK, Op, STATES, OUT>;
+    hipError_t e = allow_lds(state, smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(state, dim3(blocks), dim3(512), smem, s, q);
+    return hipGetLastError();
+  }
 }
 
 template <int DK, typename Op>

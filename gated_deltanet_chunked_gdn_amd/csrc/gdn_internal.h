@@ -66,6 +66,11 @@ inline int64_t chunk_slots(int64_t total_rows, int64_t N) { return total_rows / 
 // row block rb (16 rows of 16 (rb + 1) entries, row-major) at element 128 rb (rb + 1).
 constexpr int kLPack = 2560;
 __host__ __device__ constexpr int lpack_base(int rb) { return 128 * rb * (rb + 1); }
+// Elements of the per-chunk T diag(beta) record: the packed lower blocks (fp32 io),
+// or, for bf16 io, six MFMA operand fragments of 64 lanes x 8 entries: fragment
+// (row block mb, reduction step s), s <= mb / 2, lane (m, g) = (lane % 16, lane / 16)
+// holding row 32 (mb / 2) + 8 (m / 4) + 4 (mb % 2) + m % 4, columns 32 s + 8 g + 0..7.
+constexpr int kTbSlot = 3072;
 
 struct BwdParams {
   const void* q;
@@ -119,6 +124,9 @@ constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backw
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
+// The bf16 state pass (one launch): `states` stores S_c before every chunk, `out`
+// forms the output.  Reads the bf16 T diag(beta) fragments, P and the decays.
+hipError_t launch_state_chain(const FwdParams& p, int Dk, bool states, bool out, hipStream_t s);
 // T, T diag(beta) and the decays of every chunk slot, and the per-chunk states
 // (no outputs): the forward half of the chunked backward.  Uses p.tws, p.tbws,
 // p.gws and p.states; G must be 1.
