@@ -82,16 +82,17 @@ def test_problem_validation(kw, status):
 
 
 def test_workspace_sizes():
-    # forward: per (chunk slot, head) T diag(beta) with its lower 16x16 blocks
-    # packed (2560 io elements), P (4096 io elements) and 128 fp32 decays, each
-    # array rounded up to 256 bytes; slots = rows // 64 + N + 1
+    # forward: per (chunk slot, head) a T diag(beta) record of 3072 io elements
+    # (six bf16 operand fragments, or the 2560 entries of its lower 16x16 blocks
+    # for fp32), P (4096 io elements) and 128 fp32 decays, each array rounded up
+    # to 256 bytes; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     gates = up(slots * 3 * 128 * 4)
-    recs = up(slots * 3 * 2560 * 2) + up(slots * 3 * 4096 * 2) + gates
+    recs = up(slots * 3 * 3072 * 2) + up(slots * 3 * 4096 * 2) + gates
     assert ws(problem()) == (nat.GDN_OK, recs)
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (
-        nat.GDN_OK, up(slots * 3 * 2560 * 4) + up(slots * 3 * 4096 * 4) + gates)
+        nat.GDN_OK, up(slots * 3 * 3072 * 4) + up(slots * 3 * 4096 * 4) + gates)
     # segment split: then fp32 end and start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
     for G in (2, 4, 16):
         seg = (2 * G * 2 * 3 * 128 * 96 + G * 2 * 3 * 128 * 128) * 4
@@ -174,14 +175,14 @@ def test_backward_entry_validates():
 
 
 def test_backward_workspace_size():
-    # T (64 x 64), packed T diag(beta) (io type) and the decays, each rounded up
+    # T (64 x 64), the T diag(beta) record (3072 io elements) and the decays, each rounded up
     # to 256 bytes, then fp32 states before and state gradients after every
     # chunk slot; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     st, n = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
     assert st == nat.GDN_OK
-    assert n == (up(slots * 3 * 4096 * 2) + up(slots * 3 * 2560 * 2) + up(slots * 3 * 128 * 4)
+    assert n == (up(slots * 3 * 4096 * 2) + up(slots * 3 * 3072 * 2) + up(slots * 3 * 128 * 4)
                  + 2 * slots * 3 * 128 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
