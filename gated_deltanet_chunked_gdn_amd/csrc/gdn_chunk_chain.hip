@@ -23,15 +23,20 @@
 // from memory absorb the order: the Z operand reads K rows tau(mb, m), T diag(beta)
 // is stored by the preparation kernel as operand fragments with rows in tau order.
 //
-// Waves of a workgroup (one per SIMD; one workgroup per (segment, sequence, head,
-// 16-column tile)):
-//   wave 0 (state):  the recurrence of chunk c; hands S_c and E_c (bf16 operand
-//                    fragments) to wave 1 through LDS;
-//   wave 1 (output): O of chunk c - 1 as O^T = scale (Gamma o (S^T Q^T) + E^T P^T),
-//                    with Q and P loaded from memory straight into operand fragments;
-//   waves 2-3:       stage K, the v tile (transposed) and the decays of chunk c + 1
-//                    into the LDS ring and load chunk c + 3.
-// One workgroup barrier per chunk.
+// Waves of a workgroup (one workgroup per (segment, sequence, head, 16-column tile)):
+//   waves 0-1 (state): the recurrence of chunk c, split by halves of d_k: wave h
+//                      holds rows [d_k h / 2, d_k (h + 1) / 2) of the tile of S,
+//                      forms its partial Z, and the two partials are summed through
+//                      LDS; both waves then form R and E, and each updates its half
+//                      of S.  They hand S_c and E_c to wave 2;
+//   waves 2-3 (output): O of chunk c - 1 as O^T = scale (Gamma o (S^T Q^T) + E^T P^T),
+//                      token row blocks 0-1 and 2-3, with Q and P loaded from memory
+//                      straight into operand fragments;
+//   waves 4-5:         stage K, the v tile (transposed, fp32), T diag(beta) and the
+//                      decays of chunk c + 1 into the LDS ring and load chunk c + 3.
+// Two workgroup barriers per chunk: X (the partial Z exchanged) and Y (end of step);
+// the output and staging work is spread over both intervals.  (Waves are placed on
+// the SIMDs round robin: each state wave shares its SIMD with a staging wave.)
 #include "gdn_chunk_common.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -76,32 +81,27 @@ __device__ __forceinline__ int ksw(int t) {
 template <int DK>
 __device__ __forceinline__ int kpos(int t, int u) { return t * DK + 8 * (u ^ ksw<DK>(t)); }
 
-template <int DK, int NCH>
+template <int DK>
 struct ChainSmem {
-  static constexpr int TW = 16 * NCH;  // state columns of the workgroup
-  static constexpr int LDV = 64 + 4;   // rows of the transposed v tile
+  static constexpr int LDV = 64 + 4;  // rows of the transposed v tile
   static constexpr int NKS = DK / 32;
   alignas(16) uint16_t Ks[2][64 * DK];          // K rows, swizzled pieces (kpos)
-  alignas(16) float Vt[2][TW * LDV];            // the v tile, transposed (fp32)
+  alignas(16) float Vt[2][16 * LDV];            // the v tile, transposed (fp32)
   alignas(16) float Gs[2][128];                 // Gamma, exp(gamma_n - gamma)
   alignas(16) bf16x8_t Tb[2][6][64];            // T diag(beta) operand fragments
-  alignas(16) bf16x8_t hand[3][NCH][NKS][64];   // S_c operand fragments (ring of 3: S_c is
+  alignas(16) bf16x8_t hand[3][NKS][64];        // S_c operand fragments (ring of 3: S_c is
                                                 // written in step c - 1, read in step c + 1)
-  alignas(16) f32x4_t handE[2][NCH][4][64];     // E_c (fp32, accumulator layout)
+  alignas(16) f32x4_t handE[2][4][64];          // E_c (fp32, accumulator layout)
+  alignas(16) f32x4_t zx[2][4][64];             // partial Z of each state wave
 };
 
-// Fragment f of T diag(beta) (and of P) covers row block mb and reduction step s
-// with s <= mb / 2: f = 0 (0,0), 1 (1,0), 2 (2,0), 3 (2,1), 4 (3,0), 5 (3,1).
-__device__ __forceinline__ constexpr int frag_of(int mb, int s) { return mb < 2 ? mb : 2 + 2 * (mb - 2) + s; }
-
-// NCH 16-column tiles of one head per workgroup: the state wave runs their NCH
-// independent chains side by side, sharing every K operand fragment.
-template <int DK, int NCH, bool STATES, bool OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_chain_kernel(FwdParams p) {
-  using SM = ChainSmem<DK, NCH>;
-  constexpr int LDV = SM::LDV, TW = SM::TW;
+template <int DK, bool STATES, bool OUT>
+__global__ __launch_bounds__(384) void chunk_chain_kernel(FwdParams p) {
+  using SM = ChainSmem<DK>;
+  constexpr int LDV = SM::LDV;
   constexpr int NKS = DK / 32;  // reduction steps over d_k
-  constexpr int NSB = DK / 16;  // 16-row blocks of the state tile
+  constexpr int HS = NKS / 2;   // ... over the half of d_k a state wave holds
+  constexpr int HB = DK / 32;   // 16-row blocks of S per state wave
   extern __shared__ __align__(16) char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(p.q);
@@ -112,14 +112,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float* __restrict__ gw = p.gws;
   uint16_t* __restrict__ o = static_cast<uint16_t*>(p.o);
 
-  const int H = p.H, Dv = p.Dv, NC = p.ncol, NT = NC / TW;
+  const int H = p.H, Dv = p.Dv, NC = p.ncol, NT = NC / 16;
   // XCD-aware order: the workgroups of one head land on one XCD (blockIdx % 8),
   // whose L2 then serves their shared per-chunk reads.
   const int NB = gridDim.x, L = blockIdx.x;
   const int vb = (NB % 8 == 0) ? (L % 8) * (NB / 8) + L / 8 : L;
   const int tile = vb % NT, nh = (vb / NT) % (p.N * H), h = nh % H, n = nh / H;
   const int seg = p.seg_base + vb / NT / (p.N * H);
-  const int j0 = tile * TW;
+  const int j0 = tile * 16;
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
   const int nch_all = static_cast<int>((len + 63) / 64);
@@ -142,59 +142,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto row0_of = [&](int c) { return bos + static_cast<int64_t>(cb + c) * 64; };
   const int nsteps = (nch + 1) / 2 * 2;
 
-  if (w == 0) {
-    // ================= state wave =================
-    // S[ch]: the d_k x 16 fp32 slice of tile ch (columns j0 + 16 ch + j), rows of
-    // d_k in tau order
-    f32x4_t S[NCH][NSB];
+  if (w < 2) {
+    // ================= state waves: half hh of d_k =================
+    const int hh = w;
+    // S: blocks hh HB .. hh HB + HB - 1 of the d_k x 16 fp32 tile (rows in tau order)
+    f32x4_t S[HB];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
+    for (int i = 0; i < HB; ++i) {
 #pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d = tau(b, lg, r), j = j0 + 16 * ch + lr;
-          float x;
-          if (p.start_mode == kStartCarry)
-            x = p.carry[(segS + d) * NC + j];
-          else if (p.start_mode == kStartIdentity)
-            x = d == j ? 1.f : 0.f;
-          else if (p.start_mode == kStartS0 && seg == 0 && p.S0)
-            x = p.S0[(nhS + d) * Dv + j];
-          else
-            x = 0.f;
-          S[ch][b][r] = x;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int d = tau(hh * HB + i, lg, r), j = j0 + lr;
+        float x;
+        if (p.start_mode == kStartCarry)
+          x = p.carry[(segS + d) * NC + j];
+        else if (p.start_mode == kStartIdentity)
+          x = d == j ? 1.f : 0.f;
+        else if (p.start_mode == kStartS0 && seg == 0 && p.S0)
+          x = p.S0[(nhS + d) * Dv + j];
+        else
+          x = 0.f;
+        S[i][r] = x;
       }
+    }
     auto write_state = [&]() {
       const bool to_final = p.final_to_sfinal && seg == p.G - 1;
       if (to_final ? p.S_final != nullptr : p.seg_out != nullptr) {
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
+        for (int i = 0; i < HB; ++i)
 #pragma unroll
-          for (int b = 0; b < NSB; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int d = tau(b, lg, r), j = j0 + 16 * ch + lr;
-              if (to_final)
-                p.S_final[(nhS + d) * Dv + j] = S[ch][b][r];
-              else
-                p.seg_out[(segS + d) * NC + j] = S[ch][b][r];
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int d = tau(hh * HB + i, lg, r), j = j0 + lr;
+            if (to_final)
+              p.S_final[(nhS + d) * Dv + j] = S[i][r];
+            else
+              p.seg_out[(segS + d) * NC + j] = S[i][r];
+          }
       }
     };
     if (nch == 0) {
       write_state();
       return;
     }
-    bf16x8_t Sf[NCH][NKS];
+    // Sf[i]: the B operand of reduction step hh HS + i (rows 32 s + 8 g + 0..7)
+    bf16x8_t Sf[HS];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        Sf[ch][s] = pack_pair(S[ch][2 * s], S[ch][2 * s + 1]);
-        sm.hand[0][ch][s][lane] = Sf[ch][s];
-      }
+    for (int i = 0; i < HS; ++i) {
+      Sf[i] = pack_pair(S[2 * i], S[2 * i + 1]);
+      sm.hand[0][hh * HS + i][lane] = Sf[i];
+    }
     __syncthreads();  // chunk 0 staged
     int c0 = 0;
     do {
@@ -208,262 +203,235 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const auto rs = buffer_rsrc(p.states + ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
                                       active ? DK * Dv * 4 : 0);
 #pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
+          for (int i = 0; i < HB; ++i)
 #pragma unroll
-            for (int b = 0; b < NSB; ++b)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                buffer_store1(rs, (tau(b, lg, r) * Dv + j0 + 16 * ch + lr) * 4, S[ch][b][r]);
+            for (int r = 0; r < 4; ++r) buffer_store1(rs, (tau(hh * HB + i, lg, r) * Dv + j0 + lr) * 4, S[i][r]);
         }
-        // The step is ordered so that the vector ALU work of one part overlaps
-        // the matrix products of another: Z for row blocks 0-1, then 2-3 while R
-        // of blocks 0-1 forms; E from the first half of R while the second half
-        // forms; the update's first reduction step while the second half of the
-        // decayed E forms.  LDS operands are read ahead of the products that use
-        // them (the reads retire in order): the K fragments of Z (rows in tau
-        // order), the v tile, the decays and T diag(beta) first, then the K^T
-        // fragments of the update (rows in tau order, via ds_read_b64_tr_b16: lane
-        // s of each 16-lane group supplies token row 8 g + s / 4 (+ 4) of the step
-        // and the four columns 32 (b / 2) + 8 (s % 4) + 4 (b % 2) + 0..3, i.e. half
-        // b % 2 of piece 4 (b / 2) + s % 4).
-        bf16x8_t ka[NKS][4];
-        auto read_ka = [&](int s, int mb) {
-          ka[s][mb] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(Ks + kpos<DK>(tau(mb, lr >> 2, lr & 3), 4 * s + lg)));
-        };
+        // ---- interval A: partial Z = K[:, half] S[half] (token rows in tau order) ----
+        bf16x8_t ka[HS][4];
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
+        for (int i = 0; i < HS; ++i)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) read_ka(s, mb);
+          for (int mb = 0; mb < 4; ++mb)
+            ka[i][mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                         Ks + kpos<DK>(tau(mb, lr >> 2, lr & 3), 4 * (hh * HS + i) + lg)));
+        f32x4_t Zp[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
+        for (int i = 0; i < HS; ++i)
 #pragma unroll
-          for (int mb = 2; mb < 4; ++mb) read_ka(s, mb);
-        float4 v4[NCH][4], g4[4];
+          for (int mb = 0; mb < 4; ++mb) Zp[mb] = mma(ka[i][mb], Sf[i], Zp[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int t0 = tau(mb, lg, 0);
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
-            v4[ch][mb] = *reinterpret_cast<const float4*>(sm.Vt[u] + (16 * ch + lr) * LDV + t0);
-          g4[mb] = *reinterpret_cast<const float4*>(Gs + t0);
-        }
+        for (int mb = 0; mb < 4; ++mb) sm.zx[hh][mb][lane] = Zp[mb];
         // (a step past the last chunk finds its decays staged as zero and Gamma_n
         // as 1, and leaves S unchanged)
         const float gn = Gs[63];
+#pragma unroll
+        for (int i = 0; i < HB; ++i) S[i] = S[i] * gn;
+        __syncthreads();  // X: both partials of Z written
+        // ---- interval B: R, E, and the update of this half of S ----
+        // LDS reads go out in batches of at most 15 (the depth the LDS wait
+        // counter can name), each ahead of the products that use it: the
+        // partials of Z and T diag(beta); the v tile and Gamma; the decays to the
+        // chunk end and the K^T fragments of the update (rows in tau order, via
+        // ds_read_b64_tr_b16: lane s of each 16-lane group supplies token row
+        // 8 g + s / 4 (+ 4) of the step and the four columns 32 (b / 2) + 8 (s % 4) +
+        // 4 (b % 2) + 0..3, i.e. half b % 2 of piece 4 (b / 2) + s % 4).
+        f32x4_t zp0[4], zp1[4];
         bf16x8_t tb[6];
 #pragma unroll
-        for (int f = 0; f < 6; ++f) tb[f] = sm.Tb[u][f][lane];
-        // Z = K S, row blocks 0-1 (2 NCH interleaved chains), then 2-3, with Gamma_n S
-        f32x4_t Z[NCH][4];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) Z[ch][mb] = zero4();
-#pragma unroll
-        for (int s = 0; s < NKS; ++s)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) Z[ch][mb] = mma(ka[s][mb], Sf[ch][s], Z[ch][mb]);
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-          for (int b = 0; b < NSB; ++b) S[ch][b] = S[ch][b] * gn;
-#pragma unroll
-        for (int s = 0; s < NKS; ++s)
-#pragma unroll
-          for (int mb = 2; mb < 4; ++mb)
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) Z[ch][mb] = mma(ka[s][mb], Sf[ch][s], Z[ch][mb]);
-        // Issue order: the first K reads, then each product of Z behind the reads
-        // it needs, the remaining reads (K, v tile, decays, T diag(beta)) between
-        // the products, and the scaling of S behind the second half of Z.
-        constexpr int NRD = 4 * NKS + 4 * NCH + 4 + 1 + 6;  // LDS reads above
-        constexpr int NZ = 4 * NKS * NCH;                   // products of Z
-        constexpr int RPM = (NRD - 4 + NZ / 2 - 1) / (NZ / 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int x = 0; x < NZ / 2; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        for (int mb = 0; mb < 4; ++mb) {
+          zp0[mb] = sm.zx[0][mb][lane];
+          zp1[mb] = sm.zx[1][mb][lane];
         }
 #pragma unroll
-        for (int x = 0; x < NZ / 2; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        for (int f = 0; f < 6; ++f) tb[f] = sm.Tb[u][f][lane];
+        __builtin_amdgcn_sched_barrier(0);
+        float4 v4[4], g4[4], d4[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int t0 = tau(mb, lg, 0);
+          v4[mb] = *reinterpret_cast<const float4*>(sm.Vt[u] + lr * LDV + t0);
+          g4[mb] = *reinterpret_cast<const float4*>(Gs + t0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // the same sum, in the same order, in both waves
+        f32x4_t Z[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) Z[mb] = zp0[mb] + zp1[mb];
         // R = V - diag(Gamma) Z (the v tile reads as zeros in a pass without V)
-        auto r_of = [&](int ch, int mb) {
-          const float vv[4] = {v4[ch][mb].x, v4[ch][mb].y, v4[ch][mb].z, v4[ch][mb].w};
+        auto r_of = [&](int mb) {
+          const float vv[4] = {v4[mb].x, v4[mb].y, v4[mb].z, v4[mb].w};
           const float gg[4] = {g4[mb].x, g4[mb].y, g4[mb].z, g4[mb].w};
           f32x4_t r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = vv[e] - gg[e] * Z[ch][mb][e];
+          for (int e = 0; e < 4; ++e) r[e] = vv[e] - gg[e] * Z[mb][e];
           return r;
         };
-        bf16x8_t Rf0[NCH], Rf1[NCH];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) Rf0[ch] = pack_pair(r_of(ch, 0), r_of(ch, 1));
+        const bf16x8_t Rf0 = pack_pair(r_of(0), r_of(1));
+        // E = (T diag(beta)) R (the blocks above the diagonal skipped)
+        f32x4_t E[4];
+        E[0] = mma(tb[0], Rf0, zero4());
+        E[1] = mma(tb[1], Rf0, zero4());
+        E[2] = mma(tb[2], Rf0, zero4());
+        E[3] = mma(tb[4], Rf0, zero4());
+        const bf16x8_t Rf1 = pack_pair(r_of(2), r_of(3));
+        E[2] = mma(tb[3], Rf1, E[2]);
+        E[3] = mma(tb[5], Rf1, E[3]);
         __builtin_amdgcn_sched_barrier(0);
-        bf16x8_t kt[2][NSB];
-        auto read_kt = [&](int s) {
 #pragma unroll
-          for (int b = 0; b < NSB; ++b) {
+        for (int mb = 0; mb < 4; ++mb) d4[mb] = *reinterpret_cast<const float4*>(Gs + 64 + tau(mb, lg, 0));
+        bf16x8_t kt[2][HB];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < HB; ++i) {
+            const int b = hh * HB + i;
             const int t = 32 * s + 8 * lg + (lr >> 2), pc = 4 * (b >> 1) + (lr & 3);
             const uint16_t* p0 = Ks + kpos<DK>(t, pc) + 4 * (b & 1);
             const uint16_t* p1 = Ks + kpos<DK>(t + 4, pc) + 4 * (b & 1);
             const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
             const i16x4_t bb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
-            kt[s][b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
+            kt[s][i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-        };
-        read_kt(0);
-        // E = (T diag(beta)) R (the blocks above the diagonal skipped): the terms of
-        // the first half of R, while the second half forms
-        f32x4_t E[NCH][4];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          E[ch][0] = mma(tb[0], Rf0[ch], zero4());
-          E[ch][1] = mma(tb[1], Rf0[ch], zero4());
-          E[ch][2] = mma(tb[2], Rf0[ch], zero4());
-          E[ch][3] = mma(tb[4], Rf0[ch], zero4());
-        }
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) Rf1[ch] = pack_pair(r_of(ch, 2), r_of(ch, 3));
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          E[ch][2] = mma(tb[3], Rf1[ch], E[ch][2]);
-          E[ch][3] = mma(tb[5], Rf1[ch], E[ch][3]);
-        }
         __builtin_amdgcn_sched_barrier(0);
-        read_kt(1);
-        // E (fp32) to the output wave; decayed E as the B operand of the update
-        float4 d4[4];
+        // decayed E as the B operand of the update; E (fp32) to the output wave
+        auto ed_of = [&](int mb) { return E[mb] * f32x4_t{d4[mb].x, d4[mb].y, d4[mb].z, d4[mb].w}; };
+        const bf16x8_t Edf0 = pack_pair(ed_of(0), ed_of(1));
+        if (hh == 0) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) d4[mb] = *reinterpret_cast<const float4*>(Gs + 64 + tau(mb, lg, 0));
-        auto ed_of = [&](int ch, int mb) { return E[ch][mb] * f32x4_t{d4[mb].x, d4[mb].y, d4[mb].z, d4[mb].w}; };
-        bf16x8_t Edf0[NCH], Edf1[NCH];
+          for (int mb = 0; mb < 4; ++mb) sm.handE[u][mb][lane] = E[mb];
+        }
+        // S <- Gamma_n S + K^T (decayed E) on this half: HB independent chains
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) Edf0[ch] = pack_pair(ed_of(ch, 0), ed_of(ch, 1));
+        for (int i = 0; i < HB; ++i) S[i] = mma(kt[0][i], Edf0, S[i]);
+        const bf16x8_t Edf1 = pack_pair(ed_of(2), ed_of(3));
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
+        for (int i = 0; i < HB; ++i) S[i] = mma(kt[1][i], Edf1, S[i]);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) sm.handE[u][ch][mb][lane] = E[ch][mb];
-        // S <- Gamma_n S + K^T (decayed E): 8 NCH independent chains
-#pragma unroll
-        for (int b = 0; b < NSB; ++b)
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) S[ch][b] = mma(kt[0][b], Edf0[ch], S[ch][b]);
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) Edf1[ch] = pack_pair(ed_of(ch, 2), ed_of(ch, 3));
-#pragma unroll
-        for (int b = 0; b < NSB; ++b)
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) S[ch][b] = mma(kt[1][b], Edf1[ch], S[ch][b]);
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            Sf[ch][s] = pack_pair(S[ch][2 * s], S[ch][2 * s + 1]);
-            sm.hand[(c + 1) % 3][ch][s][lane] = Sf[ch][s];  // S_{c+1}, for the output wave
-          }
-        __syncthreads();
+        for (int i = 0; i < HS; ++i) {
+          Sf[i] = pack_pair(S[2 * i], S[2 * i + 1]);
+          sm.hand[(c + 1) % 3][hh * HS + i][lane] = Sf[i];  // S_{c+1}, for the output wave
+        }
+        __syncthreads();  // Y: end of step
       }
       c0 += 2;
     } while (c0 < nsteps);
     write_state();
-  } else if (w == 1) {
-    // ================= output wave =================
+  } else if (w < 4) {
+    // ================= output waves: token row blocks 2 ow, 2 ow + 1 =================
     if (nch == 0) return;
+    const int ow = w - 2;
     // Q rows 16 nb + j (B operand of S^T Q^T), P rows 16 nb + j in the operand
     // order the preparation kernel stores (fragment (nb, s) of 64 lanes), Gamma.
     struct OutSet {
-      bf16x8_t qf[4][NKS];
-      bf16x8_t pf[6];
-      float gq[4];
+      bf16x8_t qf[2][NKS];
+      bf16x8_t pf[2][2];  // [block][reduction step], step 1 only for blocks 2-3
+      float gq[2];
     };
     OutSet os[2];
-    auto load_set = [&](OutSet& st, int c) {
+    auto load_q = [&](OutSet& st, int c) {
       if (!OUT) return;
       const int nv = chunk_rows(c);
       const int64_t row0 = row0_of(c);
       const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * 2);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
-          st.qf[nb][s] = __builtin_bit_cast(bf16x8_t, buf_load16(rq, ((16 * nb + lr) * H * DK + 32 * s + 8 * lg) * 2));
+          st.qf[i][s] = __builtin_bit_cast(
+              bf16x8_t, buf_load16(rq, ((16 * (2 * ow + i) + lr) * H * DK + 32 * s + 8 * lg) * 2));
+    };
+    auto load_p = [&](OutSet& st, int c) {
+      if (!OUT) return;
       const int64_t sh = (slot0 + c) * H + h;
       const auto rp = buffer_rsrc(pw + sh * 4096, 4096 * 2);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int s = 0; s <= nb / 2; ++s)
-          st.pf[frag_of(nb, s)] = __builtin_bit_cast(bf16x8_t, buf_load16(rp, ((nb * 2 + s) * 64 + lane) * 16));
+        for (int s = 0; s < 2; ++s)
+          if (s == 0 || ow == 1)
+            st.pf[i][s] = __builtin_bit_cast(bf16x8_t, buf_load16(rp, (((2 * ow + i) * 2 + s) * 64 + lane) * 16));
       const auto rg = buffer_rsrc(gw + sh * 128, 256);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) st.gq[nb] = buf_load1(rg, (16 * nb + lr) * 4);
+      for (int i = 0; i < 2; ++i) st.gq[i] = buf_load1(rg, (16 * (2 * ow + i) + lr) * 4);
     };
-    load_set(os[0], 0);
-    load_set(os[1], clampc(1));
+    // Output of chunk c in two parts: Y^T = S_c^T Q^T (interval A of step c + 1),
+    // then E_c^T P^T and the store (interval B of step c + 1).
+    f32x4_t y[2];
+    auto part_y = [&](int c, const OutSet& st) {
+      bf16x8_t sf[NKS];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) sf[s] = sm.hand[c % 3][s][lane];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        y[i] = zero4();
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) y[i] = mma(sf[s], st.qf[i][s], y[i]);
+      }
+    };
+    auto part_pe = [&](int c, int ue, OutSet& st) {
+      const bf16x8_t ef0 = pack_pair(sm.handE[ue][0][lane], sm.handE[ue][1][lane]);
+      bf16x8_t ef1 = ef0;
+      if (ow == 1) ef1 = pack_pair(sm.handE[ue][2][lane], sm.handE[ue][3][lane]);
+      const int cc = clampc(c), nv = chunk_rows(cc);
+      const auto ro = buffer_rsrc(o + (row0_of(cc) * H + h) * Dv + j0,
+                                  store_o && c < nch ? ((nv - 1) * H * Dv + 16) * 2 : 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x4_t pe = mma(ef0, st.pf[i][0], zero4());
+        if (ow == 1) pe = mma(ef1, st.pf[i][1], pe);
+        const float gt = st.gq[i];
+        buffer_store4<uint16_t>(ro, ((16 * (2 * ow + i) + lr) * H * Dv + 4 * lg) * 2,
+                                p.scale * (gt * y[i][0] + pe[0]), p.scale * (gt * y[i][1] + pe[1]),
+                                p.scale * (gt * y[i][2] + pe[2]), p.scale * (gt * y[i][3] + pe[3]));
+      }
+    };
+    load_q(os[0], 0);
+    load_p(os[0], 0);
+    load_q(os[1], clampc(1));
+    load_p(os[1], clampc(1));
     __syncthreads();
     int c0 = 0;
     do {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
-        __syncthreads();  // S_c and E_c handed over
-        if (OUT) {
-          const int cc = clampc(c), nv = chunk_rows(cc);
-          const auto ro = buffer_rsrc(o + (row0_of(cc) * H + h) * Dv + j0,
-                                      store_o && c < nch ? ((nv - 1) * H * Dv + TW) * 2 : 0);
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) {
-            bf16x8_t sf[NKS], ef[2];
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) sf[s] = sm.hand[c % 3][ch][s][lane];
-            ef[0] = pack_pair(sm.handE[u][ch][0][lane], sm.handE[u][ch][1][lane]);
-            ef[1] = pack_pair(sm.handE[u][ch][2][lane], sm.handE[u][ch][3][lane]);
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              f32x4_t y = zero4(), pe = zero4();
-#pragma unroll
-              for (int s = 0; s < NKS; ++s) y = mma(sf[s], os[u].qf[nb][s], y);
-#pragma unroll
-              for (int s = 0; s <= nb / 2; ++s) pe = mma(ef[s], os[u].pf[frag_of(nb, s)], pe);
-              const float gt = os[u].gq[nb];
-              buffer_store4<uint16_t>(ro, ((16 * nb + lr) * H * Dv + 16 * ch + 4 * lg) * 2,
-                                      p.scale * (gt * y[0] + pe[0]), p.scale * (gt * y[1] + pe[1]),
-                                      p.scale * (gt * y[2] + pe[2]), p.scale * (gt * y[3] + pe[3]));
-            }
-          }
-          load_set(os[u], clampc(c + 2));
+        // interval A of step c: Y^T of chunk c - 1, then Q of chunk c + 1
+        if (OUT && c > 0) {
+          part_y(c - 1, os[u ^ 1]);
+          load_q(os[u ^ 1], clampc(c + 1));
         }
+        __syncthreads();  // X
+        // interval B: the rest of chunk c - 1's output, then P and Gamma of chunk c + 1
+        if (OUT && c > 0) {
+          part_pe(c - 1, u ^ 1, os[u ^ 1]);
+          load_p(os[u ^ 1], clampc(c + 1));
+        }
+        __syncthreads();  // Y: S_c and E_c handed over
       }
       c0 += 2;
     } while (c0 < nsteps);
+    if (OUT) {  // the last step's chunk
+      part_y(nsteps - 1, os[1]);
+      part_pe(nsteps - 1, 1, os[1]);
+    }
   } else {
     // ================= loader waves =================
     if (nch == 0) return;
-    const int lt = tid - 128;               // 0..127
+    const int lt = tid - 256;               // 0..127
     constexpr int KVR = DK / 8;             // 16-byte vectors per K row
     constexpr int NKV = 64 * KVR / 128;     // K vectors per loader thread
-    constexpr int VVR = TW / 8;             // 16-byte vectors per v-tile row
-    constexpr int NVV = 64 * VVR / 128;     // v vectors per loader thread
     struct LoadSet {
       u32x4_t kv[NKV];
-      u32x4_t tv[3];    // T diag(beta) fragments: 16-byte vectors lt, lt + 128, lt + 256
-      u32x4_t vv[NVV];  // v tile: vector x 128 + lt is row (x 128 + lt) / VVR
-      u32x4_t gv;       // decays: floats 4 lt .. 4 lt + 3 (lt < 32)
-      bool past;        // a step past the last chunk
+      u32x4_t tv[3];  // T diag(beta) fragments: 16-byte vectors lt, lt + 128, lt + 256
+      u32x4_t vv;     // v tile: row lt / 2, columns j0 + 8 (lt % 2) .. + 7
+      u32x4_t gv;     // decays: floats 4 lt .. 4 lt + 3 (lt < 32)
+      bool past;      // a step past the last chunk
     };
     LoadSet ls[2];
     const bool use_v = !p.zero_u;
-    auto load = [&](LoadSet& s, int cu) {
+    auto load_k = [&](LoadSet& s, int cu) {
       const int c = clampc(cu);
-      s.past = cu >= nch;
       const int nv = chunk_rows(c);
       const int64_t row0 = row0_of(c);
       const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * 2);
@@ -472,13 +440,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int vi = x * 128 + lt, t = vi / KVR, cv = (vi % KVR) * 8;
         s.kv[x] = buf_load16(rk, (t * H * DK + cv) * 2);
       }
+    };
+    auto load_rest = [&](LoadSet& s, int cu) {
+      const int c = clampc(cu);
+      s.past = cu >= nch;
+      const int nv = chunk_rows(c);
+      const int64_t row0 = row0_of(c);
       // (a pass without V loads nothing: the range is empty and the tile reads as zeros)
       const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, use_v ? ((nv - 1) * H * Dv + Dv) * 2 : 0);
-#pragma unroll
-      for (int x = 0; x < NVV; ++x) {
-        const int vi = x * 128 + lt, t = vi / VVR, pc = vi % VVR;
-        s.vv[x] = buf_load16(rv, (t * H * Dv + min(j0 + 8 * pc, Dv - 8)) * 2);
-      }
+      s.vv = buf_load16(rv, ((lt >> 1) * H * Dv + min(j0 + 8 * (lt & 1), Dv - 8)) * 2);
       const int64_t sh = (slot0 + c) * H + h;
       const auto rt = buffer_rsrc(tbw + sh * kTbSlot, 6 * 1024);
 #pragma unroll
@@ -486,20 +456,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const auto rg = buffer_rsrc(gw + sh * 128, 512);
       s.gv = buf_load16(rg, lt < 32 ? lt * 16 : kNoLoad);
     };
-    auto stage = [&](const LoadSet& s, int sl) {
+    auto stage_k = [&](const LoadSet& s, int sl) {
 #pragma unroll
       for (int x = 0; x < NKV; ++x) {
         const int vi = x * 128 + lt, t = vi / KVR;
         *reinterpret_cast<u32x4_t*>(sm.Ks[sl] + kpos<DK>(t, vi % KVR)) = s.kv[x];
       }
+    };
+    auto stage_rest = [&](const LoadSet& s, int sl) {
+      const int t = lt >> 1, cbase = 8 * (lt & 1);
 #pragma unroll
-      for (int x = 0; x < NVV; ++x) {
-        const int vi = x * 128 + lt, t = vi / VVR, pc = vi % VVR;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wd = s.vv[x][e >> 1];
-          sm.Vt[sl][(8 * pc + e) * LDV + t] = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-        }
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wd = s.vv[e >> 1];
+        sm.Vt[sl][(cbase + e) * LDV + t] = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
       }
 #pragma unroll
       for (int x = 0; x < 3; ++x) {
@@ -514,19 +483,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         *reinterpret_cast<u32x4_t*>(sm.Gs[sl] + 4 * lt) = gv;
       }
     };
-    load(ls[0], 0);
-    load(ls[1], 1);
-    stage(ls[0], 0);
-    load(ls[0], 2);
+    load_k(ls[0], 0);
+    load_rest(ls[0], 0);
+    load_k(ls[1], 1);
+    load_rest(ls[1], 1);
+    stage_k(ls[0], 0);
+    stage_rest(ls[0], 0);
+    load_k(ls[0], 2);
+    load_rest(ls[0], 2);
     __syncthreads();
     int c0 = 0;
     do {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = c0 + u;
-        stage(ls[u ^ 1], u ^ 1);
-        load(ls[u ^ 1], c + 3);
-        __syncthreads();
+        // interval A of step c: K of chunk c + 1 staged; interval B: the v tile,
+        // T diag(beta) and the decays staged, then chunk c + 3 loaded
+        stage_k(ls[u ^ 1], u ^ 1);
+        __syncthreads();  // X
+        stage_rest(ls[u ^ 1], u ^ 1);
+        load_k(ls[u ^ 1], c + 3);
+        load_rest(ls[u ^ 1], c + 3);
+        __syncthreads();  // Y
       }
       c0 += 2;
     } while (c0 < nsteps);
@@ -544,44 +522,33 @@ int cu_count_chain() {
   return counts[dev];
 }
 
-template <int DK, int NCH, bool STATES, bool OUT>
+template <int DK, bool STATES, bool OUT>
 hipError_t launch_chain_t(const FwdParams& q, hipStream_t s) {
-  constexpr size_t need = sizeof(ChainSmem<DK, NCH>);
+  constexpr size_t need = sizeof(ChainSmem<DK>);
   static_assert(DK == 64 || DK == 128, "K swizzle defined for 8 or 16 pieces per row");
   static_assert(need <= 160 * 1024, "LDS budget exceeded");
   // A grid with fewer than two workgroups per compute unit asks for more than half
   // of a CU's LDS so that no CU holds two while another idles.
-  const int blocks = q.nseg * q.N * q.H * (q.ncol / (16 * NCH));
+  const int blocks = q.nseg * q.N * q.H * (q.ncol / 16);
   const size_t smem = blocks < 2 * cu_count_chain() && need < 82 * 1024 ? 82 * 1024 : need;
-  auto kern = chunk_chain_kernel<DK, NCH, STATES, OUT>;
+  auto kern = chunk_chain_kernel<DK, STATES, OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), smem, s, q);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(384), smem, s, q);
   return hipGetLastError();
-}
-
-template <int DK, bool STATES, bool OUT>
-hipError_t launch_chain_cols(const FwdParams& q, hipStream_t s) {
-  // Two 16-column tiles per workgroup (one state wave runs both chains, sharing
-  // the K operands: fewer LDS reads per tile, but a longer step) only where the
-  // grid of single tiles would hold at least two workgroups per compute unit;
-  // otherwise the chains are the critical path and one tile per wave is faster.
-  const int single = q.nseg * q.N * q.H * (q.ncol / 16);
-  if (q.ncol % 32 == 0 && single >= 2 * cu_count_chain()) return launch_chain_t<DK, 2, STATES, OUT>(q, s);
-  return launch_chain_t<DK, 1, STATES, OUT>(q, s);
 }
 
 }  // namespace
 
 hipError_t launch_state_chain(const FwdParams& p, int Dk, bool states, bool out, hipStream_t s) {
   if (Dk == 128) {
-    if (states) return out ? hipErrorInvalidValue : launch_chain_cols<128, true, false>(p, s);
-    return out ? launch_chain_cols<128, false, true>(p, s) : launch_chain_cols<128, false, false>(p, s);
+    if (states) return out ? hipErrorInvalidValue : launch_chain_t<128, true, false>(p, s);
+    return out ? launch_chain_t<128, false, true>(p, s) : launch_chain_t<128, false, false>(p, s);
   }
   if (Dk == 64) {
-    if (states) return out ? hipErrorInvalidValue : launch_chain_cols<64, true, false>(p, s);
-    return out ? launch_chain_cols<64, false, true>(p, s) : launch_chain_cols<64, false, false>(p, s);
+    if (states) return out ? hipErrorInvalidValue : launch_chain_t<64, true, false>(p, s);
+    return out ? launch_chain_t<64, false, true>(p, s) : launch_chain_t<64, false, false>(p, s);
   }
   return hipErrorInvalidValue;
 }
