@@ -121,19 +121,63 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
     return out
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per forward call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the kernel source has changed since it was taken."""
+FWD_KERNEL_SOURCES = ("gated_deltanet_chunked_gdn_amd/csrc/gdn_chunk_fwd.hip",
+                      "gated_deltanet_chunked_gdn_amd/csrc/gdn_chunk_chain.hip")
+
+
+def _source_hashes():
     import hashlib
 
+    return {src: hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+            for src in FWD_KERNEL_SOURCES}
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per forward call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record, or None when a kernel source has changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"chunk_fwd_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["kernel_source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+    if rec.get("kernel_sources_sha256") != _source_hashes():
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+def write_traffic_record(fwd_fetch, fwd_write, copy_fetch, copy_write, workload="train_bf16"):
+    """Write profiles/chunk_fwd_<workload>_traffic.json from four rocprofv3 --pmc
+    counter_collection CSV files: FETCH_SIZE and WRITE_SIZE of a bench.py run, and
+    of a `bench.py --micro copy` run (2 GiB read + 2 GiB written, which calibrates
+    each counter to bytes).  Counters are in KiB per dispatch."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    copy_bytes = 2 * 1024 ** 3
+    cf = [v for k, v in per_kernel(copy_fetch, "FETCH_SIZE").items() if "copy" in k.lower()]
+    cw = [v for k, v in per_kernel(copy_write, "WRITE_SIZE").items() if "copy" in k.lower()]
+    f_scale = copy_bytes / (max(cf) * 1024)
+    w_scale = copy_bytes / (max(cw) * 1024)
+    ff = per_kernel(fwd_fetch, "FETCH_SIZE")
+    fw = per_kernel(fwd_write, "WRITE_SIZE")
+    kernels = sorted(k for k in ff if "gdn::" in k and ("prep" in k or "chain" in k))
+    rows = {k.split("(anonymous namespace)::")[-1][:60]: {
+        "fetch_KiB": ff[k], "write_KiB": fw.get(k, 0.0),
+        "read_bytes": ff[k] * 1024 * f_scale, "written_bytes": fw.get(k, 0.0) * 1024 * w_scale}
+        for k in kernels}
+    total = sum(r["read_bytes"] + r["written_bytes"] for r in rows.values())
+    rec = {"workload": workload, "kernels": rows, "kernel_sources_sha256": _source_hashes(),
+           "traffic_bytes_per_launch": int(total), "fetch_size_scale": f_scale,
+           "write_size_scale": w_scale, "summary": f"chunk_fwd_{workload}_hbm_traffic.md"}
+    out = os.path.join(ROOT, "profiles", f"chunk_fwd_{workload}_traffic.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def parse():
@@ -150,6 +194,8 @@ def parse():
                     help="skip the backward and segment-split measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the HBM-traffic record from four rocprofv3 --pmc CSV files and exit")
     ap.add_argument("--micro", choices=("copy", "gemm"), default=None,
                     help="run a roofline microbenchmark instead: a 2 GiB device copy "
                          "(bytes counted as read + write) or 8192^3 bf16/fp32 GEMMs")
@@ -225,6 +271,9 @@ def main():
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from, workload=args.workload)
+        return
     if args.micro:
         micro(args.micro, args.steps, args.warmup)
         return
@@ -306,7 +355,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w.name),
-                     "kernel": "gdn_chunk_fwd = chunk_prep_kernel + chunk_state_kernel",
+                     "kernel": "gdn_chunk_fwd = chunk_prep_kernel + chunk_chain_kernel",
                      "alg_bytes_per_launch": nbytes,
                      "kernel_ms_mean": k_mean * 1e3,
                      "kernel_ms_p10": float(np.percentile(kt, 10)) * 1e3,
