@@ -7,6 +7,7 @@
 // reverse mode of one chunk, given dS_{c+1}, is
 //   dE  = K~ dS_{c+1} + P^T dOs
 //   dS_c = Gamma_n dS_{c+1} + (diag(Gamma) Q)^T dOs - W^T dE        [state pass]
+//        = Gamma_n dS_{c+1} + Q^T diag(Gamma) dOs - K^T diag(beta Gamma) T^T dE
 //   dK~ = E dS_{c+1}^T,  dQ = diag(Gamma) dOs S_c^T + (dP o D) K,  dP = lower(dOs E^T)
 //   dW  = -dE S_c^T,  dT = dE (diag(beta) V)^T + dW (diag(beta Gamma) K)^T
 //   dA  = strict_lower(-T^T dT T^T),  dV = diag(beta) T^T dE
@@ -19,7 +20,9 @@
 // per-chunk state output):
 //   chunk_dstate_kernel: one workgroup per (sequence, head, 16-column tile of
 //     d_v), sequential over the chunks in reverse; holds the d_k x 16 slice of
-//     dS in fp32 MFMA accumulators, stores dS_{c+1} of every chunk and dS0.
+//     dS in fp32 MFMA accumulators, stores dS_{c+1} of every chunk and dS0.  The
+//     operands of chunk c - 1 are loaded while chunk c is processed; W is never
+//     formed (the second form of the state pass above).
 //   chunk_grad_kernel: one workgroup per (chunk, head, sequence), fully
 //     parallel; loops over d_v in tiles for every product that reduces over d_v
 //     (fp32 accumulators held across tiles), then the 64 x 64 and 64 x d_k
@@ -71,17 +74,6 @@ __device__ __forceinline__ float wide_elem<uint16_t>(const u32x4_t& v, int e) {
 template <>
 __device__ __forceinline__ float wide_elem<float>(const u32x4_t& v, int e) {
   return __uint_as_float(v[e]);
-}
-
-template <typename E>
-__device__ __forceinline__ void store2(E* dst, float a, float b);
-template <>
-__device__ __forceinline__ void store2<uint16_t>(uint16_t* dst, float a, float b) {
-  *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a, b);
-}
-template <>
-__device__ __forceinline__ void store2<float>(float* dst, float a, float b) {
-  *reinterpret_cast<float2*>(dst) = float2{a, b};
 }
 
 // Store a 16x16 accumulator block C (C[4 (lane/16) + r][lane % 16] in element r)
@@ -142,11 +134,10 @@ struct DStateSmem {
   static constexpr int LDB = 128 + PADE;  // rows of length 128
   E Ks[64 * LDK];   // K rows
   E Qs[64 * LDK];   // Q rows
-  E Kt[DK * LDC];   // K^T
   E Tm[64 * LDC];   // T rows
   E Pt[64 * LDC];   // P^T
-  E QW[DK * LDB];   // [ (diag(Gamma) Q)^T | -W^T ]
   E dB[16 * LDB];   // [ dOs^T | dE^T ] of this tile
+  E dU[16 * LDB];   // [ (diag(Gamma) dOs)^T | (-diag(beta Gamma) T^T dE)^T ] of this tile
   E dSt[16 * LDK];  // dS^T of this tile
   float gam[64], Gam[64], dec[64], bg[64];
 };
@@ -193,9 +184,87 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     store4<E>(sm.dSt + j * LDK + i, x[0], x[1], x[2], x[3]);
   }
 
-  for (int c = nch - 1; c >= 0; --c) {
+  // The global operands of chunk c - 1 (K, Q, T, dOs, the gates) are loaded into
+  // registers while chunk c is processed, and staged into LDS at the start of
+  // the next step: the load latency hides behind the products.
+  constexpr int NSV = 64 * (DK / EPV) / 256;  // K (and Q) vectors per thread
+  constexpr int NTV = 64 * 64 / EPV / 256;    // T vectors per thread
+  struct Pre {
+    u32x4_t kv[NSV], qv[NSV], tv[NTV];
+    float dov[4];
+    float gv, bv;
+  };
+  auto load_pre = [&](Pre& pr, int c) {
     const int64_t c0 = static_cast<int64_t>(c) * 64, row0 = bos + c0;
     const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) {
+      const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      pr.kv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      pr.qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t < nv) {
+        pr.kv[i] = ld16(k + ((row0 + t) * H + h) * DK + cv);
+        pr.qv[i] = ld16(q + ((row0 + t) * H + h) * DK + cv);
+      }
+    }
+    const E* T = tws + ((slot0 + c) * H + h) * 4096;
+#pragma unroll
+    for (int i = 0; i < NTV; ++i) {
+      const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+      pr.tv[i] = ld16(T + t * 64 + cv);
+    }
+    {
+      const int t = tid >> 2, cq = (tid & 3) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr.dov[e] = 0.f;
+      if (t < nv) {
+        const E* src = dO + ((row0 + t) * H + h) * Dv + j0 + cq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr.dov[e] = Op::widen(src[e]);
+      }
+    }
+    {  // padded rows: g = 0, beta = 0 (every wave loads the gates)
+      const bool ok = lane < nv;
+      pr.gv = ok ? p.g[(row0 + lane) * H + h] : 0.f;
+      pr.bv = ok ? p.beta[(row0 + lane) * H + h] : 0.f;
+    }
+  };
+  auto stage_pre = [&](const Pre& pr) {
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) {
+      const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      st16(sm.Ks + t * LDK + cv, pr.kv[i]);
+      st16(sm.Qs + t * LDK + cv, pr.qv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NTV; ++i) {
+      const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+      st16(sm.Tm + t * LDC + cv, pr.tv[i]);
+    }
+    // gamma by an in-register scan (log2 units), in every wave; wave 0 stores it
+    const float g2 = wave_inclusive_scan(pr.gv * kLog2e, lane);
+    const float G = exp2f(g2);
+    if (w == 0) {
+      const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
+      sm.gam[lane] = g2;
+      sm.Gam[lane] = G;
+      sm.dec[lane] = exp2f(gl2 - g2);
+      sm.bg[lane] = pr.bv * G;
+    }
+    {
+      const int t = tid >> 2, cq = (tid & 3) * 4;
+      const float Gt = __shfl(G, t, 64);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * pr.dov[e]);
+        sm.dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * pr.dov[e]);
+      }
+    }
+  };
+  Pre pre;
+  if (nch > 0) load_pre(pre, nch - 1);
+
+  for (int c = nch - 1; c >= 0; --c) {
     {  // dS_{c+1}, the gradient of the state after chunk c
       float* dst = p.dstates + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv;
 #pragma unroll
@@ -205,61 +274,12 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = dS[sr][r];
       }
     }
-    // ---- stage K, Q (rows), K^T, T and dOs^T of this tile ----
-    for (int x = tid; x < 64 * (DK / EPV); x += 256) {
-      const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      u32x4_t kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-      if (t < nv) {
-        kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
-        qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
-      }
-      st16(sm.Ks + t * LDK + cv, kv);
-      st16(sm.Qs + t * LDK + cv, qv);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) sm.Kt[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
-    }
-    {
-      const E* T = tws + ((slot0 + c) * H + h) * 4096;
-      for (int x = tid; x < 64 * 64 / EPV; x += 256) {
-        const int t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
-        st16(sm.Tm + t * LDC + cv, ld16(T + t * 64 + cv));
-      }
-    }
-    {
-      const int t = tid >> 2, cq = (tid & 3) * 4;
-      float vals[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < nv) {
-        const E* src = dO + ((row0 + t) * H + h) * Dv + j0 + cq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vals[e] = Op::widen(src[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * vals[e]);
-    }
-    if (w == 0) stage_gates<DK, Op>(p, row0, nv, h, lane, sm.gam, sm.Gam, sm.dec, nullptr, sm.bg);
+    // ---- stage K, Q (rows), T, dOs^T of this tile and the gates; load chunk c - 1 ----
+    stage_pre(pre);
+    if (c > 0) load_pre(pre, c - 1);
     __syncthreads();
 
-    // ---- (diag(Gamma) Q)^T, -W^T and P^T ----
-    for (int x = tid; x < 32 * (DK / EPV); x += 256) {
-      const int t = 2 * (x / (DK / EPV)), cv = (x % (DK / EPV)) * EPV;
-      const u32x4_t a = ld16(sm.Qs + t * LDK + cv), b = ld16(sm.Qs + (t + 1) * LDK + cv);
-      const float ga = sm.Gam[t], gb = sm.Gam[t + 1];
-#pragma unroll
-      for (int e = 0; e < EPV; ++e)
-        store2<E>(sm.QW + (cv + e) * LDB + t, ga * wide_elem<E>(a, e), gb * wide_elem<E>(b, e));
-    }
-    for (int cb = w; cb < DK / 16; cb += 4) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        // W[16 rb + .][16 cb + .] = (T diag(beta Gamma)) K
-        f32x4_t acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < tsteps<Op>(rb); ++ks)
-          acc = Op::mma(Op::scale(Op::frag(sm.Tm + 16 * rb * LDC, LDC, lane, ks * KS), sm.bg, lane, ks * KS),
-                        Op::frag(sm.Kt + 16 * cb * LDC, LDC, lane, ks * KS), acc);
-        store_t<E>(sm.QW + 16 * cb * LDB + 64 + 16 * rb, LDB, -acc, lane);
-      }
-    }
+    // ---- P^T ----
     {
       auto pblock = [&](int bi, int bt) {  // P[16 bi + .][16 bt + .] -> P^T
         f32x4_t acc = zero4();
@@ -296,7 +316,19 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    // ---- dS <- Gamma_n dS + [(diag(Gamma) Q)^T | -W^T] [dOs ; dE] ----
+    // ---- F = T^T dE (token block w; T is lower triangular), scaled to -beta Gamma F ----
+    // (-W^T dE = K^T diag(-beta Gamma) T^T dE, so W itself is never formed)
+    {
+      f32x4_t acc = zero4();
+      for (int ks = (16 * w) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag_tr(sm.Tm + 16 * w, LDC, lane, ks * KS), Op::frag(sm.dB + 64, LDB, lane, ks * KS), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= -sm.bg[16 * w + 4 * (lane >> 4) + r];
+      store_t<E>(sm.dU + 64 + 16 * w, LDB, acc, lane);
+    }
+    __syncthreads();
+
+    // ---- dS <- Gamma_n dS + [Q^T | K^T] [diag(Gamma) dOs ; -diag(beta Gamma) F] ----
     {
       const float gn = sm.Gam[63];
 #pragma unroll
@@ -304,8 +336,12 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
         const int rb = w * SRB + sr;
         f32x4_t acc = dS[sr] * gn;
 #pragma unroll
-        for (int ks = 0; ks < 128 / KS; ++ks)
-          acc = Op::mma(Op::frag(sm.QW + 16 * rb * LDB, LDB, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
+        for (int ks = 0; ks < 64 / KS; ++ks)
+          acc = Op::mma(Op::frag_tr(sm.Qs + 16 * rb, LDK, lane, ks * KS), Op::frag(sm.dU, LDB, lane, ks * KS), acc);
+#pragma unroll
+        for (int ks = 0; ks < 64 / KS; ++ks)
+          acc = Op::mma(Op::frag_tr(sm.Ks + 16 * rb, LDK, lane, ks * KS), Op::frag(sm.dU + 64, LDB, lane, ks * KS),
+                        acc);
         dS[sr] = acc;
         store_t<E>(sm.dSt + 16 * rb, LDK, acc, lane);
       }

@@ -48,15 +48,6 @@ namespace {
 
 using namespace chunk;
 
-// Orders this wave's LDS accesses around a hand-off between its own lanes (the
-// LDS executes one wave's instructions in order; the fences keep the compiler
-// from moving accesses across the hand-off).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
