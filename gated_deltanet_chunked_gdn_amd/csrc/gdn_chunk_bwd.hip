@@ -440,6 +440,38 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   const float* Sg = p.states + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
   const float* dSg = p.dstates + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
 
+  // Global operands of one d_v tile (V and dO rows, S_c and dS_{c+1}), loaded into
+  // registers one tile ahead of their use.
+  constexpr int NVX = (64 * (DVT / EPV) + 511) / 512;
+  constexpr int NSX = (DK * (DVT / 4) + 511) / 512;
+  struct TileLd {
+    u32x4_t vv[NVX], ov[NVX];
+    float4 sv[NSX], dv[NSX];
+  };
+  TileLd tl;
+  auto load_tile = [&](TileLd& L, int v0) {
+#pragma unroll
+    for (int ix = 0; ix < NVX; ++ix) {
+      const int x = tid + 512 * ix, t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
+      L.vv[ix] = u32x4_t{0u, 0u, 0u, 0u};
+      L.ov[ix] = u32x4_t{0u, 0u, 0u, 0u};
+      if (x < 64 * (DVT / EPV) && t < nv && v0 + cv < Dv) {
+        L.vv[ix] = ld16(v + ((row0 + t) * H + h) * Dv + v0 + cv);
+        L.ov[ix] = ld16(dO + ((row0 + t) * H + h) * Dv + v0 + cv);
+      }
+    }
+#pragma unroll
+    for (int ix = 0; ix < NSX; ++ix) {
+      const int x = tid + 512 * ix, i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
+      L.sv[ix] = float4{0.f, 0.f, 0.f, 0.f};
+      L.dv[ix] = float4{0.f, 0.f, 0.f, 0.f};
+      if (x < DK * (DVT / 4) && v0 + cv < Dv) {
+        L.sv[ix] = *reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(i) * Dv + v0 + cv);
+        L.dv[ix] = *reinterpret_cast<const float4*>(dSg + static_cast<int64_t>(i) * Dv + v0 + cv);
+      }
+    }
+  };
+
   // ---------------- stage K, Q, K^T, T, T^T; gates ----------------
   E* const Wn = U + GL::aWn;
   E* const Pt = U + GL::aPt;
@@ -472,6 +504,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     }
     for (int x = tid; x < 2 * 8 * 64 + 16; x += 512) pb[x] = 0.f;  // pb, pg, pn, sdot
     if (w == 0) stage_gates<DK, Op>(p, row0, nv, h, lane, gam, Gam, dec, bet, bg);
+    load_tile(tl, 0);  // the first d_v tile's operands, while the pre-tile products run
     __syncthreads();
 
     // -W (rows t) from W^T = K^T (T diag(beta Gamma))^T; blocks (a: d_k, b: tokens)
@@ -530,43 +563,43 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   E* const Er = U + GL::aEr;
   E* const dEr = U + GL::adEr;
   E* const dEt = U + GL::adEt;
+  auto stage_tile = [&](const TileLd& L, int v0) {
+#pragma unroll
+    for (int ix = 0; ix < NVX; ++ix) {
+      const int x = tid + 512 * ix, t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
+      if (x < 64 * (DVT / EPV)) {
+        st16(Vr + t * LDV + cv, L.vv[ix]);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          Vt[(cv + e) * LDC + t] = raw_elem<E>(L.vv[ix], e);
+          const E oe = Op::cvt(p.scale * wide_elem<E>(L.ov[ix], e));
+          dOt[(cv + e) * LDC + t] = oe;
+          dOr[t * LDV + cv + e] = oe;
+        }
+      }
+    }
+#pragma unroll
+    for (int ix = 0; ix < NSX; ++ix) {
+      const int x = tid + 512 * ix, i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
+      if (x < DK * (DVT / 4)) {
+        const float4 sv = L.sv[ix], dv4 = L.dv[ix];
+        sdot_acc += sv.x * dv4.x + sv.y * dv4.y + sv.z * dv4.z + sv.w * dv4.w;
+        store4<E>(Sr + i * LDV + cv, sv.x, sv.y, sv.z, sv.w);
+        store4<E>(dSr + i * LDV + cv, dv4.x, dv4.y, dv4.z, dv4.w);
+        const float s4[4] = {sv.x, sv.y, sv.z, sv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          St[(cv + e) * LDK + i] = Op::cvt(s4[e]);
+          dSt[(cv + e) * LDK + i] = Op::cvt(d4[e]);
+        }
+      }
+    }
+  };
   for (int v0 = 0; v0 < Dv; v0 += DVT) {
-    // stage V and dOs (rows and transposed), S_c and dS_{c+1} (rows and transposed)
-    for (int x = tid; x < 64 * (DVT / EPV); x += 512) {
-      const int t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
-      u32x4_t vv = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
-      if (t < nv && v0 + cv < Dv) {
-        vv = ld16(v + ((row0 + t) * H + h) * Dv + v0 + cv);
-        ov = ld16(dO + ((row0 + t) * H + h) * Dv + v0 + cv);
-      }
-      st16(Vr + t * LDV + cv, vv);
-      float os[EPV];
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        Vt[(cv + e) * LDC + t] = raw_elem<E>(vv, e);
-        os[e] = p.scale * wide_elem<E>(ov, e);
-        const E oe = Op::cvt(os[e]);
-        dOt[(cv + e) * LDC + t] = oe;
-        dOr[t * LDV + cv + e] = oe;
-      }
-    }
-    for (int x = tid; x < DK * (DVT / 4); x += 512) {
-      const int i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
-      float4 sv = {0.f, 0.f, 0.f, 0.f}, dv4 = {0.f, 0.f, 0.f, 0.f};
-      if (v0 + cv < Dv) {
-        sv = *reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(i) * Dv + v0 + cv);
-        dv4 = *reinterpret_cast<const float4*>(dSg + static_cast<int64_t>(i) * Dv + v0 + cv);
-      }
-      sdot_acc += sv.x * dv4.x + sv.y * dv4.y + sv.z * dv4.z + sv.w * dv4.w;
-      store4<E>(Sr + i * LDV + cv, sv.x, sv.y, sv.z, sv.w);
-      store4<E>(dSr + i * LDV + cv, dv4.x, dv4.y, dv4.z, dv4.w);
-      const float s4[4] = {sv.x, sv.y, sv.z, sv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        St[(cv + e) * LDK + i] = Op::cvt(s4[e]);
-        dSt[(cv + e) * LDK + i] = Op::cvt(d4[e]);
-      }
-    }
+    // stage V and dOs (rows and transposed), S_c and dS_{c+1} (rows and transposed);
+    // load the next tile meanwhile
+    stage_tile(tl, v0);
+    if (v0 + DVT < Dv) load_tile(tl, v0 + DVT);
     __syncthreads();
     // E^T and dE^T, block (bdv, bt) per wave
     if (w < NBT) {
