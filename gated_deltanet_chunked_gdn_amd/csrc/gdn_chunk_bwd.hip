@@ -104,6 +104,17 @@ __device__ __forceinline__ float sum_in_group(float x) {
   return x;
 }
 
+// acc += A(16 x K) * B(K x 16) with A given transposed: At row-major (K x 16 block
+// at `at`, leading dim lda), B stored transposed (16 x K) at `bt`.  The A operand is
+// read with a transposing LDS read, so no transposed copy of At is staged.
+template <typename Op, int K>
+__device__ __forceinline__ void tile_mma_ta(f32x4_t& acc, const typename Op::elem* at, int lda,
+                                            const typename Op::elem* bt, int ldb, int lane) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Op::KSTEP)
+    acc = Op::mma(Op::frag_tr(at, lda, lane, k0), Op::frag(bt, ldb, lane, k0), acc);
+}
+
 template <int DK, typename Op>
 __device__ __forceinline__ void stage_gates(const BwdParams& p, int64_t row0, int nv, int h, int lane,
                                             float* gam, float* Gam, float* dec, float* bet,
@@ -363,7 +374,8 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 // ===================================================================================
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// LDS plan (element offsets; E = io element type).  Persistent: K rows, T, T^T.
+// LDS plan (element offsets; E = io element type).  Persistent: K rows, T (its
+// transpose, and those of V, dOs, S and dS, are read with transposing LDS reads).
 // Region U is reused: first the pre-chunk products and the d_v tiles, then the
 // 64 x 64 / 64 x d_k stages.
 template <int DK, typename Op>
@@ -374,13 +386,12 @@ struct GradLayout {
   static constexpr int LDK = DK + PADE, LDC = 64 + PADE, LDV = DVT + PADE;
   static constexpr int nK = 64 * LDK, nC = 64 * LDC, nKT = DK * LDC, nV = 64 * LDV;
   static constexpr int nVT = DVT * LDC, nS = DK * LDV, nST = DVT * LDK;
-  static constexpr int oKs = 0, oTm = oKs + nK, oTt = oTm + nC, oU = oTt + nC;
+  static constexpr int oKs = 0, oTm = oKs + nK, oU = oTm + nC;
   // pre-chunk and d_v tiles
   static constexpr int aWn = 0, aPt = aWn + nK, aTile = aPt + nC;
-  static constexpr int aKt = aTile, aQs = aKt + nKT, aPreEnd = aQs + nK;
-  static constexpr int aVt = aTile, aVr = aVt + nVT, aSt = aVr + nV, aSr = aSt + nST;
-  static constexpr int adSt = aSr + nS, adSr = adSt + nST, adOr = adSr + nS, adOt = adOr + nV;
-  static constexpr int aEr = adOt + nVT, adEr = aEr + nV, adEt = adEr + nV, aEnd = adEt + nVT;
+  static constexpr int aQs = aTile, aPreEnd = aQs + nK;
+  static constexpr int aVr = aTile, aSr = aVr + nV, adSr = aSr + nS, adOr = adSr + nS;
+  static constexpr int aEr = adOr + nV, adEr = aEr + nV, adEt = adEr + nV, aEnd = adEt + nVT;
   // 64 x 64 and 64 x d_k stages
   static constexpr int bQKr = 0, bQKt = bQKr + nC, bWt = bQKt + nC, bWr = bWt + nKT;
   static constexpr int bTb = bWr + nK, bXt = bTb + nC, bEnd1 = bXt + nC;
@@ -405,7 +416,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   E* const base = reinterpret_cast<E*>(smem_raw);
   E* const Ks = base + GL::oKs;
   E* const Tm = base + GL::oTm;
-  E* const Tt = base + GL::oTt;
   E* const U = base + GL::oU;
   float* const fl = reinterpret_cast<float*>(smem_raw + GL::fOff);
   float* const gam = fl;
@@ -476,7 +486,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   E* const Wn = U + GL::aWn;
   E* const Pt = U + GL::aPt;
   {
-    E* const Kt = U + GL::aKt;
     E* const Qs = U + GL::aQs;
     for (int x = tid; x < 64 * (DK / EPV); x += 512) {
       const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
@@ -487,16 +496,14 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       }
       st16(Ks + t * LDK + cv, kv);
       st16(Qs + t * LDK + cv, qv);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) Kt[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
+
     }
     const E* T = tws + (slot * H + h) * 4096;
     for (int x = tid; x < 64 * 64 / EPV; x += 512) {
       const int t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
       const u32x4_t tv = ld16(T + t * 64 + cv);
       st16(Tm + t * LDC + cv, tv);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) Tt[(cv + e) * LDC + t] = raw_elem<E>(tv, e);
+
     }
     for (int x = tid; x < 64 * LDC; x += 512) {  // P^T: blocks below the diagonal are zero
       const int r = x / LDC, cc = x % LDC;
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
       f32x4_t acc = zero4();
       for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
-        acc = Op::mma(Op::frag(Kt + 16 * a * LDC, LDC, lane, ks * KS),
+        acc = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
                       Op::scale(Op::frag(Tm + 16 * b * LDC, LDC, lane, ks * KS), bg, lane, ks * KS), acc);
       store_t<E>(Wn + 16 * b * LDK + 16 * a, LDK, -acc, lane);
     }
@@ -552,14 +559,10 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   for (int s = 0; s < NKS; ++s) dKtT[s] = dQ6T[s] = dWT[s] = zero4();
   dP[0] = dP[1] = dT1T[0] = dT1T[1] = zero4();
   float sdot_acc = 0.f;
-  E* const Vt = U + GL::aVt;
   E* const Vr = U + GL::aVr;
-  E* const St = U + GL::aSt;
   E* const Sr = U + GL::aSr;
-  E* const dSt = U + GL::adSt;
   E* const dSr = U + GL::adSr;
   E* const dOr = U + GL::adOr;
-  E* const dOt = U + GL::adOt;
   E* const Er = U + GL::aEr;
   E* const dEr = U + GL::adEr;
   E* const dEt = U + GL::adEt;
@@ -569,13 +572,10 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       const int x = tid + 512 * ix, t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
       if (x < 64 * (DVT / EPV)) {
         st16(Vr + t * LDV + cv, L.vv[ix]);
+        E os[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          Vt[(cv + e) * LDC + t] = raw_elem<E>(L.vv[ix], e);
-          const E oe = Op::cvt(p.scale * wide_elem<E>(L.ov[ix], e));
-          dOt[(cv + e) * LDC + t] = oe;
-          dOr[t * LDV + cv + e] = oe;
-        }
+        for (int e = 0; e < EPV; ++e) os[e] = Op::cvt(p.scale * wide_elem<E>(L.ov[ix], e));
+        st16(dOr + t * LDV + cv, *reinterpret_cast<const u32x4_t*>(os));
       }
     }
 #pragma unroll
@@ -586,12 +586,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
         sdot_acc += sv.x * dv4.x + sv.y * dv4.y + sv.z * dv4.z + sv.w * dv4.w;
         store4<E>(Sr + i * LDV + cv, sv.x, sv.y, sv.z, sv.w);
         store4<E>(dSr + i * LDV + cv, dv4.x, dv4.y, dv4.z, dv4.w);
-        const float s4[4] = {sv.x, sv.y, sv.z, sv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          St[(cv + e) * LDK + i] = Op::cvt(s4[e]);
-          dSt[(cv + e) * LDK + i] = Op::cvt(d4[e]);
-        }
       }
     }
   };
@@ -606,16 +600,16 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       const int bdv = w >> 2, bt = w & 3;
       f32x4_t e = zero4();
       for (int ks = 0; ks < (16 * (bt + 1) + KS - 1) / KS; ++ks)
-        e = Op::mma(Op::frag(Vt + 16 * bdv * LDC, LDC, lane, ks * KS),
+        e = Op::mma(Op::frag_tr(Vr + 16 * bdv, LDV, lane, ks * KS),
                     Op::scale(Op::frag(Tm + 16 * bt * LDC, LDC, lane, ks * KS), bet, lane, ks * KS), e);
-      tile_mma<Op, DK>(e, St + 16 * bdv * LDK, LDK, Wn + 16 * bt * LDK, LDK, lane);
+      tile_mma_ta<Op, DK>(e, Sr + 16 * bdv, LDV, Wn + 16 * bt * LDK, LDK, lane);
       store_t<E>(Er + 16 * bt * LDV + 16 * bdv, LDV, e, lane);
       f32x4_t de = zero4();
-      tile_mma<Op, DK>(de, dSt + 16 * bdv * LDK, LDK, Ks + 16 * bt * LDK, LDK, lane);
+      tile_mma_ta<Op, DK>(de, dSr + 16 * bdv, LDV, Ks + 16 * bt * LDK, LDK, lane);
       const float dc = dec[16 * bt + (lane & 15)];
       de = de * dc;
       for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
-        de = Op::mma(Op::frag(dOt + 16 * bdv * LDC, LDC, lane, ks * KS),
+        de = Op::mma(Op::frag_tr(dOr + 16 * bdv, LDV, lane, ks * KS),
                      Op::frag(Pt + 16 * bt * LDC, LDC, lane, ks * KS), de);
       store_t<E>(dEr + 16 * bt * LDV + 16 * bdv, LDV, de, lane);
       store_n<E, Op>(dEt + 16 * bdv * LDC + 16 * bt, LDC, de, lane);
@@ -643,7 +637,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       f32x4_t acc = zero4();
       for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
         acc = Op::mma(Op::frag(dEt + 16 * bdv * LDC, LDC, lane, ks * KS),
-                      Op::frag(Tt + 16 * bt * LDC, LDC, lane, ks * KS), acc);
+                      Op::frag_tr(Tm + 16 * bt, LDC, lane, ks * KS), acc);
       const int t = 16 * bt + (lane & 15), cl = 16 * bdv + 4 * (lane >> 4);
       const float bt_ = bet[t];
       float part = 0.f;
@@ -741,7 +735,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     dKbT[s] = zero4();
     for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
       dKbT[s] = Op::mma(Op::frag(dWt + 16 * a * LDC, LDC, lane, ks * KS),
-                        Op::frag(Tt + 16 * b * LDC, LDC, lane, ks * KS), dKbT[s]);
+                        Op::frag_tr(Tm + 16 * b, LDC, lane, ks * KS), dKbT[s]);
   }
   for (int x = tid; x < 64 * 64; x += 512) {
     const int r = x >> 6, cc = x & 63;
@@ -753,7 +747,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       const int bi = lbi[s], bj = lbj[s];
       f32x4_t acc = zero4();
       for (int ks = (16 * bi) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag(Tt + 16 * bi * LDC, LDC, lane, ks * KS),
+        acc = Op::mma(Op::frag_tr(Tm + 16 * bi, LDC, lane, ks * KS),
                       Op::frag(Xt + 16 * bj * LDC, LDC, lane, ks * KS), acc);
       const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
       f32x4_t dkk;
