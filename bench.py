@@ -118,6 +118,21 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
         kt = event_times(fwd, max(5, steps // 4), 2, stream)
         seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
     out["segment_split"] = {"workload": w.name, "by_num_segments": seg}
+    # fused input prologue (normalised q, k; g; beta) on the training shape
+    w = WORKLOADS["train_bf16"]
+    rng = np.random.default_rng(11)
+    shape = (w.B, w.T, w.H, w.Dk)
+    qr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    kr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    a = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
+    b = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
+    A_log = torch.from_numpy(rng.uniform(0.0, 1.5, size=(w.H,)).astype(np.float32)).to(dev)
+    dt = torch.from_numpy((0.5 * rng.standard_normal(w.H)).astype(np.float32)).to(dev)
+    kt = event_times(lambda i: gdn.prologue(qr, kr, a, b, A_log, dt), steps, warmup, stream)
+    th = w.B * w.T * w.H
+    nb = th * (2 * w.Dk * 2 * 2 + 4 * 4)  # q, k read and written (bf16); a, b read, g, beta written
+    out["prologue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
+                       "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
     return out
 
 

@@ -5,5 +5,5 @@ include/gdn.h); this package is its Python binding plus the seeded synthetic
 input generators.
 """
 from .ops import (SeqLens, chunk_bwd, chunk_fwd, forward_workspace, make_problem,  # noqa: F401
-                  recurrent_ref)
+                  prologue, recurrent_ref)
 from ._native import GdnError, GdnLibraryMissing  # noqa: F401

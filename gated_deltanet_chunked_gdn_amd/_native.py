@@ -27,6 +27,9 @@ GDN_ERR_ALIGN = 9
 # gdn_dtype
 GDN_FP32 = 0
 GDN_BF16 = 1
+# gdn_gate_kind
+GDN_GATE_GDN = 0
+GDN_GATE_BOUNDED5 = 1
 # gdn_pass
 GDN_PASS_CHUNK_FWD = 0
 GDN_PASS_CHUNK_BWD = 1
@@ -35,7 +38,7 @@ GDN_PASS_RECURRENT_BWD = 3
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
-            "gdn_chunk_bwd", "gdn_recurrent_ref")
+            "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -90,6 +93,8 @@ def load():
     lib.gdn_recurrent_ref.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                       ctypes.c_size_t, P]
     lib.gdn_recurrent_ref.restype = ctypes.c_int
+    lib.gdn_prologue.argtypes = [PP, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+    lib.gdn_prologue.restype = ctypes.c_int
     _lib = lib
     return lib
 

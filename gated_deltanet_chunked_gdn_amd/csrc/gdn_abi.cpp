@@ -324,4 +324,27 @@ gdn_status gdn_recurrent_ref(const gdn_problem* p, const void* q, const void* k,
   return hip_status(gdn::launch_recurrent(rp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_prologue(const gdn_problem* p, const void* q, const void* k, const float* a, const float* b,
+                        const float* A_log, const float* dt_bias, int32_t gate_kind, int32_t allow_neg_eigval,
+                        void* q_out, void* k_out, float* g, float* beta, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::RecFwd, &c);
+  if (st != GDN_OK) return st;
+  if (gate_kind != GDN_GATE_GDN && gate_kind != GDN_GATE_BOUNDED5) return GDN_ERR_UNSUPPORTED;
+  const size_t nk = c.tokens * p->H * p->Dk, ng = c.tokens * p->H;
+  const bool gdn_gate = gate_kind == GDN_GATE_GDN;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {a, ng * 4, 4, true},
+                      {b, ng * 4, 4, true}, {A_log, static_cast<size_t>(p->H) * 4, 4, gdn_gate},
+                      {dt_bias, static_cast<size_t>(p->H) * 4, 4, gdn_gate}},
+                     {{q_out, nk * c.io, 16, true}, {k_out, nk * c.io, 16, true}, {g, ng * 4, 4, true},
+                      {beta, ng * 4, 4, true}});
+  if (st != GDN_OK) return st;
+  if (ng == 0) return GDN_OK;
+  gdn::PrologueParams pp{};
+  pp.q = q; pp.k = k; pp.a = a; pp.b = b; pp.A_log = A_log; pp.dt_bias = dt_bias;
+  pp.q_out = q_out; pp.k_out = k_out; pp.g = g; pp.beta = beta;
+  pp.rows = static_cast<int64_t>(ng); pp.H = p->H; pp.gate_kind = gate_kind; pp.allow_neg = allow_neg_eigval != 0;
+  return hip_status(gdn::launch_prologue(pp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

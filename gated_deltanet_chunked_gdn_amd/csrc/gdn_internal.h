@@ -121,6 +121,23 @@ struct RecParams {
 
 constexpr int kRecBlock = 16;  // tokens per replay block of the recurrent backward
 
+struct PrologueParams {
+  const void* q;
+  const void* k;
+  const float* a;
+  const float* b;
+  const float* A_log;    // [H] (gate_kind 0)
+  const float* dt_bias;  // [H] (gate_kind 0)
+  void* q_out;
+  void* k_out;
+  float* g;
+  float* beta;
+  int64_t rows;          // B * T * H token-heads
+  int32_t H;
+  int32_t gate_kind;     // 0: -exp(A_log) softplus(a + dt_bias); 1: -5 sigmoid(a)
+  int32_t allow_neg;     // beta = 2 sigmoid(b)
+};
+
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
@@ -141,6 +158,7 @@ inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
 // filled by launch_chunk_fwd_states.
 hipError_t launch_chunk_bwd(const BwdParams& b, int Dk, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
+hipError_t launch_prologue(const PrologueParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 
 }  // namespace gdn

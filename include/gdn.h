@@ -173,6 +173,37 @@ gdn_status gdn_recurrent_ref(const gdn_problem* problem, const void* q, const vo
                              float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Gate forms of gdn_prologue. */
+typedef enum {
+  GDN_GATE_GDN = 0,      /* g = -exp(A_log[h]) * softplus(a + dt_bias[h]) */
+  GDN_GATE_BOUNDED5 = 1  /* g = -5 * sigmoid(a), in (-5, 0)               */
+} gdn_gate_kind;
+
+/* Fused input prologue: the elementwise step that produces the operator's inputs
+ * from the raw projections, in one pass over HBM.
+ *   q_out = q / max(||q||_2, 1e-30), k_out = k / max(||k||_2, 1e-30): norms over
+ *           the last dimension in fp32 from the io-dtype inputs, then rounded to
+ *           the io dtype (round to nearest even).  The fla issue #1550 page
+ *           ("Proposed scope") asks for exactly this order: normalise in FP32,
+ *           then cast.
+ *   beta  = sigmoid(b), or 2 sigmoid(b) when allow_neg_eigval != 0 (the range
+ *           (0, 2) of the Day-2 page, "Building some intuition", gates).
+ *   g     = -exp(A_log[h]) softplus(a + dt_bias[h])   (GDN_GATE_GDN: the gate
+ *           formula of the Day-2 page, "Building some intuition", steps 4-5), or
+ *           -5 sigmoid(a)                              (GDN_GATE_BOUNDED5: the
+ *           bounded gates of the fla issue #1550 workload).
+ * Shapes: q, k, q_out, k_out [B, T, H, Dk] io dtype; a, b, g, beta [B, T, H] fp32;
+ * A_log, dt_bias [H] fp32 (required for GDN_GATE_GDN, ignored otherwise).
+ * `problem` is the problem of the chunked call the outputs feed (only B, T, H,
+ * Dk and io_dtype are used; it is validated as for gdn_recurrent_ref).  Outputs
+ * must not overlap inputs (GDN_ERR_ALIAS).  No workspace.  In fp32 the results
+ * are the correctly computed fp32 expressions up to a few units of the last
+ * place (the exponentials and the division). */
+gdn_status gdn_prologue(const gdn_problem* problem, const void* q, const void* k, const float* a,
+                        const float* b, const float* A_log, const float* dt_bias, int32_t gate_kind,
+                        int32_t allow_neg_eigval, void* q_out, void* k_out, float* g, float* beta,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

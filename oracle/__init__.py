@@ -4,6 +4,9 @@ Only ``tests/``, the package smoke check (``__graft_entry__.smoke``) and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library never
 imports, links or calls it, and it shares no code with the GPU path.
 
+``prologue`` is the input prologue in float64 numpy (the normalisation and the
+gate formulas written out; pinned in tests/test_oracle_pins.py).
+
 ``fwd`` / ``bwd`` wrap ``liboracle.so`` (built from ``gdn_oracle.c`` with gcc):
 the plain token-by-token recurrence of the Day-1 page ("Research Sprint Day 1",
 section "The GDN update": forget, read, write the error, read with the query),
@@ -154,3 +157,35 @@ def bwd(q, k, v, g, beta, dO, cu_seqlens=None, S0=None, dS_final=None, scale=1.0
     for name in ("dg", "dbeta"):
         out[name] = out[name].reshape(shape + (H,))
     return out
+
+
+def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate="gdn", allow_neg_eigval=False):
+    """The operator's inputs from the raw projections, in float64.
+
+    q = q_raw / ||q_raw||, k = k_raw / ||k_raw|| (L2 over the last axis; the
+    normalisation the fla issue #1550 page, "Proposed scope", places before the
+    cast); beta = sigmoid(b), doubled when negative eigenvalues are allowed (range
+    (0, 2), "Research Sprint Day 2", "Building some intuition", gates); and the
+    log-decay g = -exp(A_log[h]) softplus(a + dt_bias[h]) (the same page's gate
+    formula) or, for gate == "bounded5", g = -5 sigmoid(a).  Returns float64
+    arrays (q, k, g, beta) of the input shapes.
+    """
+    q = _f64(q_raw)
+    k = _f64(k_raw)
+    qn = np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
+    kn = np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    q = q / np.maximum(qn, 1e-30)
+    k = k / np.maximum(kn, 1e-30)
+    a = _f64(a)
+    b = _f64(b)
+    sig_b = 1.0 / (1.0 + np.exp(-b))
+    beta = 2.0 * sig_b if allow_neg_eigval else sig_b
+    if gate == "gdn":
+        x = a + _f64(dt_bias)
+        softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+        g = -np.exp(_f64(A_log)) * softplus
+    elif gate == "bounded5":
+        g = -5.0 / (1.0 + np.exp(-a))
+    else:
+        raise ValueError(gate)
+    return q, k, g, beta

@@ -197,3 +197,26 @@ def test_recurrent_backward_needs_workspace():
     ptrs[15] = P(None)  # dS0
     st = nat.load().gdn_recurrent_ref(ctypes.byref(p), *ptrs, None, 0, None)
     assert st == nat.GDN_ERR_WORKSPACE
+
+
+def prologue_call(p, gate=nat.GDN_GATE_GDN, **kw):
+    """gdn_prologue with fake, well-separated pointers (overridable by name)."""
+    names = ("q", "k", "a", "b", "A_log", "dt_bias", "q_out", "k_out", "g", "beta")
+    ptr = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+    ptr.update(kw)
+    P = ctypes.c_void_p
+    return nat.load().gdn_prologue(ctypes.byref(p), P(ptr["q"]), P(ptr["k"]), P(ptr["a"]), P(ptr["b"]),
+                                   P(ptr["A_log"]), P(ptr["dt_bias"]), gate, 0, P(ptr["q_out"]),
+                                   P(ptr["k_out"]), P(ptr["g"]), P(ptr["beta"]), None)
+
+
+def test_prologue_checks():
+    p = problem()
+    assert prologue_call(p, q=None) == nat.GDN_ERR_NULL
+    assert prologue_call(p, beta=None) == nat.GDN_ERR_NULL
+    assert prologue_call(p, A_log=None) == nat.GDN_ERR_NULL         # required by the GDN gate
+    assert prologue_call(p, gate=7) == nat.GDN_ERR_UNSUPPORTED
+    assert prologue_call(p, k=FAKE + (1 << 30) + 8) == nat.GDN_ERR_ALIGN
+    assert prologue_call(p, q_out=FAKE + 4096) == nat.GDN_ERR_ALIAS  # q_out inside q
+    assert prologue_call(problem(Dk=96)) == nat.GDN_ERR_UNSUPPORTED
+    assert prologue_call(problem(io_dtype=5)) == nat.GDN_ERR_DTYPE
