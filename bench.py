@@ -133,6 +133,15 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
     nb = th * (2 * w.Dk * 2 * 2 + 4 * 4)  # q, k read and written (bf16); a, b read, g, beta written
     out["prologue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
                        "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
+    # output epilogue (RMSNorm(o) * weight * silu(z)) on the training shape
+    shape = (w.B, w.T, w.H, w.Dv)
+    o = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    z = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    wt = torch.ones(w.Dv, dtype=torch.float32, device=dev)
+    kt = event_times(lambda i: gdn.epilogue(o, z, wt), steps, warmup, stream)
+    nb = th * w.Dv * 2 * 3  # o, z read, y written (bf16)
+    out["epilogue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
+                       "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
     return out
 
 

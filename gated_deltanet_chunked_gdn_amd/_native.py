@@ -38,7 +38,7 @@ GDN_PASS_RECURRENT_BWD = 3
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
-            "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue")
+            "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -95,6 +95,8 @@ def load():
     lib.gdn_recurrent_ref.restype = ctypes.c_int
     lib.gdn_prologue.argtypes = [PP, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.gdn_prologue.restype = ctypes.c_int
+    lib.gdn_epilogue.argtypes = [PP, P, P, P, ctypes.c_float, P, P]
+    lib.gdn_epilogue.restype = ctypes.c_int
     _lib = lib
     return lib
 

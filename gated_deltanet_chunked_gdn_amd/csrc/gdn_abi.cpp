@@ -347,4 +347,22 @@ gdn_status gdn_prologue(const gdn_problem* p, const void* q, const void* k, cons
   return hip_status(gdn::launch_prologue(pp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_epilogue(const gdn_problem* p, const void* o, const void* z, const float* weight, float eps,
+                        void* y, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::RecFwd, &c);
+  if (st != GDN_OK) return st;
+  if ((p->Dv & (p->Dv - 1)) != 0) return GDN_ERR_UNSUPPORTED;
+  const size_t nv = c.tokens * p->H * p->Dv;
+  st = check_tensors({{o, nv * c.io, 16, true}, {z, nv * c.io, 16, true},
+                      {weight, static_cast<size_t>(p->Dv) * 4, 16, false}},
+                     {{y, nv * c.io, 16, true}});
+  if (st != GDN_OK) return st;
+  if (nv == 0) return GDN_OK;
+  gdn::EpilogueParams ep{};
+  ep.o = o; ep.z = z; ep.weight = weight; ep.y = y;
+  ep.rows = static_cast<int64_t>(c.tokens) * p->H; ep.eps = eps;
+  return hip_status(gdn::launch_epilogue(ep, p->Dv, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

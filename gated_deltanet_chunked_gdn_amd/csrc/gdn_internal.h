@@ -159,6 +159,16 @@ inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
 hipError_t launch_chunk_bwd(const BwdParams& b, int Dk, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecParams& p, int Dk, bool bf16, hipStream_t s);
 hipError_t launch_prologue(const PrologueParams& p, int Dk, bool bf16, hipStream_t s);
+
+struct EpilogueParams {
+  const void* o;
+  const void* z;
+  const float* weight;  // [Dv] or nullptr (ones)
+  void* y;
+  int64_t rows;         // B * T * H token-heads
+  float eps;
+};
+hipError_t launch_epilogue(const EpilogueParams& p, int Dv, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 
 }  // namespace gdn

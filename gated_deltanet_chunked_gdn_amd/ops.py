@@ -8,6 +8,7 @@ built library every call raises ``GdnLibraryMissing``.
     grads      = chunk_bwd(q, k, v, g, beta, dO, S0=..., dS_final=None)
     out        = recurrent_ref(q, k, v, g, beta, ..., dO=None)
     q, k, g, beta = prologue(q_raw, k_raw, a, b, A_log=..., dt_bias=..., gate="gdn")
+    y          = epilogue(o, z, weight=None, eps=1e-6)
 
 Shapes: q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H) fp32;
 S0 / S_final (N, H, Dk, Dv) fp32.  q, k, v share the io dtype (bf16 or fp32).
@@ -247,3 +248,25 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate: str = "gdn",
                           _ptr(beta), _stream(q_raw.device))
     nat.check(st, "gdn_prologue")
     return q, k, g, beta
+
+
+def epilogue(o, z, weight=None, eps: float = 1e-6):
+    """Output epilogue (gdn_epilogue): y = o / sqrt(mean(o^2) + eps) * weight * silu(z)
+    per (token, head) over the last dimension.  o, z: (B, T, H, Dv) of the io dtype;
+    weight: float32 (Dv,) or None (ones)."""
+    lib = nat.load()
+    if o.dtype not in _IO or z.dtype != o.dtype:
+        raise TypeError("o and z must share the io dtype (bfloat16 or float32)")
+    if o.dim() != 4 or z.shape != o.shape or not o.is_contiguous() or not z.is_contiguous():
+        raise ValueError("o and z must be contiguous (B, T, H, Dv) tensors of one shape")
+    B, T, H, Dv = o.shape
+    if weight is not None and (weight.dtype != torch.float32 or tuple(weight.shape) != (Dv,)
+                               or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous float32 (Dv,) tensor")
+    prob = nat.Problem(B=B, T=T, H=H, Dk=64, Dv=Dv, num_seqs=B, cu_seqlens_host=None, cu_seqlens_dev=None,
+                       io_dtype=_IO[o.dtype], scale=1.0, chunk=64, num_segments=1)
+    y = torch.empty_like(o)
+    st = lib.gdn_epilogue(ctypes.byref(prob), _ptr(o), _ptr(z), _ptr(weight), float(eps), _ptr(y),
+                          _stream(o.device))
+    nat.check(st, "gdn_epilogue")
+    return y

@@ -204,6 +204,20 @@ gdn_status gdn_prologue(const gdn_problem* problem, const void* q, const void* k
                         int32_t allow_neg_eigval, void* q_out, void* k_out, float* g, float* beta,
                         void* stream);
 
+/* Output epilogue: the gated, normalised output the operator's result feeds,
+ * in one pass over HBM ("Research Sprint Day 2", "Building some intuition",
+ * step 7: normalise per head, then gate):
+ *   y = o / sqrt(mean_j(o_j^2) + eps) * weight * silu(z),  silu(z) = z sigmoid(z)
+ * per (token, head) over the Dv values, in fp32, rounded once to the io dtype.
+ * Shapes: o, z, y [B, T, H, Dv] io dtype; weight [Dv] fp32, 16-byte aligned (NULL =
+ * all ones).
+ * eps >= 0 is documented, not checked.  `problem` is that of the chunked call
+ * that produced o (B, T, H, Dv and io_dtype are used; validated as for
+ * gdn_recurrent_ref); Dv must be a power of two (16 .. 256), else
+ * GDN_ERR_UNSUPPORTED.  y must not overlap o or z (GDN_ERR_ALIAS).  No workspace. */
+gdn_status gdn_epilogue(const gdn_problem* problem, const void* o, const void* z, const float* weight,
+                        float eps, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,7 +4,8 @@ Only ``tests/``, the package smoke check (``__graft_entry__.smoke``) and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library never
 imports, links or calls it, and it shares no code with the GPU path.
 
-``prologue`` is the input prologue in float64 numpy (the normalisation and the
+``prologue`` / ``epilogue`` are the input prologue and the output epilogue in
+float64 numpy (the normalisation and the
 gate formulas written out; pinned in tests/test_oracle_pins.py).
 
 ``fwd`` / ``bwd`` wrap ``liboracle.so`` (built from ``gdn_oracle.c`` with gcc):
@@ -189,3 +190,15 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate="gdn", allow_neg
     else:
         raise ValueError(gate)
     return q, k, g, beta
+
+
+def epilogue(o, z, weight=None, eps=1e-6):
+    """The gated, normalised output in float64: per (token, head) over the last
+    axis, y = o / sqrt(mean(o^2) + eps) * weight * silu(z) with silu(z) =
+    z / (1 + exp(-z)) ("Research Sprint Day 2", "Building some intuition", step 7:
+    normalise per head, then gate).  weight None means ones."""
+    o = _f64(o)
+    z = _f64(z)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    w = 1.0 if weight is None else _f64(weight)
+    return o / rms * w * (z / (1.0 + np.exp(-z)))

@@ -220,3 +220,17 @@ def test_prologue_checks():
     assert prologue_call(p, q_out=FAKE + 4096) == nat.GDN_ERR_ALIAS  # q_out inside q
     assert prologue_call(problem(Dk=96)) == nat.GDN_ERR_UNSUPPORTED
     assert prologue_call(problem(io_dtype=5)) == nat.GDN_ERR_DTYPE
+
+
+def test_epilogue_checks():
+    P = ctypes.c_void_p
+    lib = nat.load()
+
+    def call(p, o=FAKE, z=FAKE + (1 << 30), w=FAKE + (2 << 30), y=FAKE + (3 << 30)):
+        return lib.gdn_epilogue(ctypes.byref(p), P(o), P(z), P(w), 1e-6, P(y), None)
+
+    assert call(problem(), o=None) == nat.GDN_ERR_NULL
+    assert call(problem(), y=None) == nat.GDN_ERR_NULL
+    assert call(problem(Dv=96)) == nat.GDN_ERR_UNSUPPORTED          # not a power of two
+    assert call(problem(), y=FAKE + 4096) == nat.GDN_ERR_ALIAS       # y inside o
+    assert call(problem(), z=FAKE + (1 << 30) + 8) == nat.GDN_ERR_ALIGN
