@@ -23,6 +23,10 @@ The five named workloads follow the pages' experiments:
   reproduction"): T=65536, H=1, d=128, slow constant decay.
 * ``fwdbwd_bf16`` -- Day-2 training shape B=32, T=1024, H=16, d_k=64, d_v=128
   (value expansion 2), forward plus backward with upstream dO.
+* ``kda_bf16``    -- the training shape of ``train_bf16`` with one log-decay per
+  (token, head, key channel), the gate layout of the cuLA issue #126 page
+  ("Minimal public reproduction": g shaped like q, dt_bias per head and
+  channel); the values follow the Day-2 gate formula channel by channel.
 """
 from __future__ import annotations
 
@@ -70,7 +74,8 @@ class Workload:
     Dv: int
     io: str = "bf16"                    # "bf16" or "fp32"
     qk: str = "iid"                     # "iid" (q ~ N, k normalised) / "norm_both" / "correlated"
-    gate: str = "gdn"                   # "softplus01" / "gdn" / "bounded5" / "const"
+    gate: str = "gdn"                   # "softplus01" / "gdn" / "bounded5" / "const" /
+                                        # "gdn_channel" (g shaped like q)
     gate_const: float = -1e-3
     cu_seqlens: Optional[Sequence[int]] = None   # packed row (B must be 1)
     s0_std: Optional[float] = None      # None: no initial state; 0.0: explicit zeros
@@ -102,13 +107,16 @@ WORKLOADS = {
                           gate="const", gate_const=-1e-3, seed=3),
     "fwdbwd_bf16": Workload("fwdbwd_bf16", 32, 1024, 16, 64, 128, io="bf16", qk="norm_both",
                             gate="gdn", s0_std=0.0, with_dO=True, seed=4),
+    "kda_bf16": Workload("kda_bf16", 4, 4096, 8, 128, 128, io="bf16", qk="norm_both",
+                         gate="gdn_channel", seed=5),
 }
 
 
 def generate(w: Workload) -> dict:
     """Draw one workload.  Returns float32 arrays (io-dtype-exact) and metadata.
 
-    Shapes: q, k (B, T, H, Dk); v, dO (B, T, H, Dv); g, beta (B, T, H);
+    Shapes: q, k (B, T, H, Dk); v, dO (B, T, H, Dv); g, beta (B, T, H) (g is
+    (B, T, H, Dk) for the per-channel gate);
     S0 (N, H, Dk, Dv) or None; cu_seqlens int32 (N+1,) or None.
     """
     if w.cu_seqlens is not None:
@@ -151,6 +159,11 @@ def generate(w: Workload) -> dict:
         g = (np.float32(-5.0) * _sigmoid(randn(B, T, H))).astype(np.float32)
     elif w.gate == "const":
         g = np.full((B, T, H), w.gate_const, dtype=np.float32)
+    elif w.gate == "gdn_channel":
+        a = randn(B, T, H, Dk)
+        A_log = rng.uniform(0.0, 1.5, size=(H,)).astype(np.float32)
+        dt_bias = (np.float32(0.5) * randn(H, Dk)).astype(np.float32)
+        g = (-np.exp(A_log)[:, None] * _softplus(a + dt_bias)).astype(np.float32)
     else:
         raise ValueError(w.gate)
     beta = _sigmoid(randn(B, T, H))

@@ -8,6 +8,9 @@ imports, links or calls it, and it shares no code with the GPU path.
 float64 numpy (the normalisation and the
 gate formulas written out; pinned in tests/test_oracle_pins.py).
 
+``kda_fwd`` is the same recurrence with one decay per key channel (numpy,
+float64; pinned in tests/test_oracle_kda_pins.py).
+
 ``fwd`` / ``bwd`` wrap ``liboracle.so`` (built from ``gdn_oracle.c`` with gcc):
 the plain token-by-token recurrence of the Day-1 page ("Research Sprint Day 1",
 section "The GDN update": forget, read, write the error, read with the query),
@@ -202,3 +205,55 @@ def epilogue(o, z, weight=None, eps=1e-6):
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
     w = 1.0 if weight is None else _f64(weight)
     return o / rms * w * (z / (1.0 + np.exp(-z)))
+
+
+def kda_fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0):
+    """Gated delta rule with a per-key-channel decay, token by token, in float64.
+
+    The update of "Research Sprint Day 1" ("The GDN update") with the scalar
+    forget factor replaced by a diagonal one: g holds one log-decay per (token,
+    head, key channel), the gate layout of the cuLA issue #126 page ("Minimal
+    public reproduction", g shaped like q).  Per token, with a = exp(g_t) of
+    length Dk:
+        S <- diag(a) S,  r = S^T k_t,  e = beta_t (v_t - r),  S <- S + k_t e^T,
+        o_t = scale S^T q_t.
+    Shapes: q, k, g (B, T, H, Dk) or packed (Ttot, H, Dk); v (..., H, Dv);
+    beta (..., H); S0 / S_final (N, H, Dk, Dv).  Returns (o, S_final) in float64.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    if g.shape != q.shape:
+        raise ValueError("g must be shaped like q (one log-decay per key channel)")
+    if cu_seqlens is None:
+        if q.ndim != 4:
+            raise ValueError("dense inputs must be (B, T, H, D)")
+        B, T = q.shape[:2]
+        cu = np.arange(B + 1, dtype=np.int64) * T
+        lead = (B, T)
+    else:
+        if q.ndim == 4 and q.shape[0] == 1:
+            q, k, v, g, beta = q[0], k[0], v[0], g[0], beta.reshape(beta.shape[-2:])
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        lead = (q.shape[0],)
+        if cu[0] != 0 or cu[-1] != q.shape[0] or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at Ttot")
+    H, Dk = q.shape[-2:]
+    Dv = v.shape[-1]
+    q, k, g = (x.reshape(-1, H, Dk) for x in (q, k, g))
+    v = v.reshape(-1, H, Dv)
+    beta = beta.reshape(-1, H)
+    N = len(cu) - 1
+    S0 = _f64(S0)
+    if S0 is not None and S0.shape != (N, H, Dk, Dv):
+        raise ValueError(f"S0 must be {(N, H, Dk, Dv)}")
+    o = np.zeros((q.shape[0], H, Dv))
+    Sf = np.zeros((N, H, Dk, Dv))
+    for n in range(N):
+        S = np.zeros((H, Dk, Dv)) if S0 is None else S0[n].copy()
+        for t in range(cu[n], cu[n + 1]):
+            S *= np.exp(g[t])[:, :, None]                        # forget, per key channel
+            r = np.einsum("hkv,hk->hv", S, k[t])                 # read the old value
+            e = beta[t][:, None] * (v[t] - r)                    # written error
+            S += k[t][:, :, None] * e[:, None, :]                # write
+            o[t] = scale * np.einsum("hkv,hk->hv", S, q[t])      # read after the write
+        Sf[n] = S
+    return o.reshape(lead + (H, Dv)), Sf

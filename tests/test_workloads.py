@@ -42,3 +42,13 @@ def test_workload_shapes_follow_the_pages():
     assert small["S0"].shape == (2, 12, 128, 128)
     assert abs(float(np.std(small["S0"])) - 0.1) < 0.01
     assert np.all(small["g"] > -5) and np.all(small["g"] < 0)
+
+
+def test_channel_gate_generator():
+    w = WORKLOADS["kda_bf16"]
+    assert (w.B, w.T, w.H, w.Dk, w.Dv) == (4, 4096, 8, 128, 128)
+    d = generate(w.with_(B=1, T=128))
+    assert d["g"].shape == d["q"].shape
+    assert np.all(d["g"] < 0) and np.all(np.isfinite(d["g"]))
+    # channels of one head differ (dt_bias per channel), heads differ (A_log per head)
+    assert np.std(d["g"][0, :, 0, :].mean(axis=0)) > 0.05
