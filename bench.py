@@ -142,7 +142,33 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
     nb = th * w.Dv * 2 * 3  # o, z read, y written (bf16)
     out["epilogue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
                        "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
+    del o, z, qr, kr
+    # per-key-channel decay (gdn_kda_chunk_fwd) on the training shape
+    w = WORKLOADS["kda_bf16"]
+    d = generate(w)
+    t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+    t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+    del d
+    o = torch.empty_like(t["v"])
+    Sf = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    kws = torch.empty(gdn_workspace_bytes(gdn, t["q"], t["v"]), dtype=torch.uint8, device=dev)
+    kt = event_times(lambda i: gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale,
+                                                 out=o, final_state_out=Sf, workspace=kws),
+                     steps, warmup, stream)
+    th = w.B * w.T * w.H
+    # q, k, v read and o written (bf16), g (Dk fp32 per token-head) and beta read, S_final written
+    nb = th * ((2 * w.Dk + 2 * w.Dv) * 2 + w.Dk * 4 + 4) + w.B * w.H * w.Dk * w.Dv * 4
+    out["kda"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
+                  "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
+                  "kernels": "kda_prep_kernel + kda_state_kernel (fp32 arithmetic)"}
     return out
+
+
+def gdn_workspace_bytes(gdn, q, v):
+    """Workspace bytes gdn_kda_chunk_fwd asks for (dense inputs)."""
+    from gated_deltanet_chunked_gdn_amd import _native as nat
+
+    return nat.workspace_size(gdn.make_problem(q, v, None, 1.0, 1), nat.GDN_PASS_KDA_FWD)
 
 
 FWD_KERNEL_SOURCES = ("gated_deltanet_chunked_gdn_amd/csrc/gdn_chunk_fwd.hip",

@@ -5,5 +5,5 @@ include/gdn.h); this package is its Python binding plus the seeded synthetic
 input generators.
 """
 from .ops import (SeqLens, chunk_bwd, chunk_fwd, epilogue, forward_workspace,  # noqa: F401
-                  make_problem, prologue, recurrent_ref)
+                  kda_chunk_fwd, make_problem, prologue, recurrent_ref)
 from ._native import GdnError, GdnLibraryMissing  # noqa: F401

@@ -35,10 +35,12 @@ GDN_PASS_CHUNK_FWD = 0
 GDN_PASS_CHUNK_BWD = 1
 GDN_PASS_RECURRENT_FWD = 2
 GDN_PASS_RECURRENT_BWD = 3
+GDN_PASS_KDA_FWD = 4
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
-            "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue")
+            "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue",
+            "gdn_kda_chunk_fwd")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -97,6 +99,8 @@ def load():
     lib.gdn_prologue.restype = ctypes.c_int
     lib.gdn_epilogue.argtypes = [PP, P, P, P, ctypes.c_float, P, P]
     lib.gdn_epilogue.restype = ctypes.c_int
+    lib.gdn_kda_chunk_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_kda_chunk_fwd.restype = ctypes.c_int
     _lib = lib
     return lib
 

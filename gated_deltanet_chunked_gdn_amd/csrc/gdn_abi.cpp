@@ -39,7 +39,7 @@ struct Checked {
   size_t io = 4;         // bytes per io element
 };
 
-enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd };
+enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd, KdaFwd };
 
 gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (!p) return GDN_ERR_NULL;
@@ -57,6 +57,10 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
     if (p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
     // one chunk of one head's rows is addressed with 32-bit byte offsets
     if (static_cast<int64_t>(64) * p->H * p->Dv * 4 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  }
+  if (kind == Kind::KdaFwd) {
+    if (p->num_segments != 1) return GDN_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(p->num_seqs) * p->H * (p->Dv / 16) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   }
   if (kind == Kind::RecBwd && static_cast<size_t>(2) * p->Dk * (p->Dv + 1) * 4 +
                                       (2 * gdn::kRecBlock * p->Dk + 2 * gdn::kRecBlock + 8) * 4 >
@@ -121,6 +125,11 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
     // start states and maps
     return packed_slot_bytes(p, c) + t_slot_bytes(p, c) + gate_slot_bytes(p, c) +
            gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
+  }
+  if (kind == Kind::KdaFwd) {
+    if (c.N == 0) return 0;
+    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda_rec_floats(p->Dk) *
+           sizeof(float);
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
@@ -194,6 +203,7 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int32_t pass, size_t* bytes)
     case GDN_PASS_CHUNK_BWD: kind = Kind::ChunkBwd; break;
     case GDN_PASS_RECURRENT_FWD: kind = Kind::RecFwd; break;
     case GDN_PASS_RECURRENT_BWD: kind = Kind::RecBwd; break;
+    case GDN_PASS_KDA_FWD: kind = Kind::KdaFwd; break;
     default: return GDN_ERR_UNSUPPORTED;
   }
   Checked c;
@@ -234,6 +244,32 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   fp.G = p->num_segments;
   fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(wsb + pb + t_slot_bytes(p, c) + gate_slot_bytes(p, c)) : nullptr;
   return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* S0, void* o,
+                             float* S_final, void* workspace, size_t ws_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::KdaFwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, nk * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false},
+                      {workspace, ws_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::KdaFwd, c);
+  if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  gdn::KdaParams kp{};
+  kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = o; kp.S_final = S_final;
+  kp.ws = static_cast<float*>(workspace);
+  kp.seq = seq_info(p);
+  kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
+  kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  kp.scale = p->scale;
+  return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,

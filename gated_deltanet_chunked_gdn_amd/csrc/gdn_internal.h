@@ -169,6 +169,27 @@ struct EpilogueParams {
   float eps;
 };
 hipError_t launch_epilogue(const EpilogueParams& p, int Dv, bool bf16, hipStream_t s);
+
+// Chunked forward with one log-decay per key channel (g shaped like q).
+struct KdaParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;        // [rows][H][Dk]
+  const float* beta;     // [rows][H]
+  const float* S0;       // [N, H, Dk, Dv] or nullptr
+  void* o;
+  float* S_final;        // [N, H, Dk, Dv] or nullptr
+  float* ws;             // one record of kda_rec_floats(Dk) floats per (chunk slot, head)
+  SeqInfo seq;
+  int32_t N, H, Dv;
+  int32_t max_chunks;
+  float scale;
+};
+// Per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma, Q o Gamma
+// and (K o exp(gamma_n - gamma))^T (64 x Dk each), Gamma_n (Dk); all fp32.
+inline size_t kda_rec_floats(int Dk) { return 8192 + 3 * 64 * static_cast<size_t>(Dk) + Dk; }
+hipError_t launch_kda_fwd(const KdaParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 
 }  // namespace gdn

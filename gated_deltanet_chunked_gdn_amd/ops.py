@@ -9,6 +9,7 @@ built library every call raises ``GdnLibraryMissing``.
     out        = recurrent_ref(q, k, v, g, beta, ..., dO=None)
     q, k, g, beta = prologue(q_raw, k_raw, a, b, A_log=..., dt_bias=..., gate="gdn")
     y          = epilogue(o, z, weight=None, eps=1e-6)
+    o, S_final = kda_chunk_fwd(q, k, v, g, beta, ...)   # g (B, T, H, Dk): per-channel decay
 
 Shapes: q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H) fp32;
 S0 / S_final (N, H, Dk, Dv) fp32.  q, k, v share the io dtype (bf16 or fp32).
@@ -153,6 +154,42 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
     st = lib.gdn_chunk_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(S0), _ptr(o), _ptr(Sf), _ptr(ws), nws, _stream(q.device))
     nat.check(st, "gdn_chunk_fwd")
+    return o, Sf
+
+
+def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
+                  output_final_state: bool = True, out=None, final_state_out=None, workspace=None):
+    """Chunked forward pass with one log-decay per key channel: g is fp32 and
+    shaped like q.  Returns (o, S_final or None); buffers as for chunk_fwd."""
+    lib = nat.load()
+    _check_inputs(q, k, v, beta, beta)
+    if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
+        raise ValueError("g must be a float32 tensor shaped like q (one log-decay per key channel)")
+    if not g.is_cuda or not g.is_contiguous():
+        raise ValueError("g must be a contiguous GPU tensor")
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    if out is None:
+        o = torch.empty_like(v)
+    else:
+        if out.dtype != v.dtype or out.shape != v.shape or not out.is_contiguous():
+            raise ValueError("out must be contiguous, shaped and typed like v")
+        o = out
+    if final_state_out is not None:
+        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out")
+    elif output_final_state:
+        Sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    else:
+        Sf = None
+    if workspace is not None:
+        ws, nws = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws, nws = _workspace(prob, nat.GDN_PASS_KDA_FWD, q.device)
+    st = lib.gdn_kda_chunk_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(S0), _ptr(o), _ptr(Sf), _ptr(ws), nws, _stream(q.device))
+    nat.check(st, "gdn_kda_chunk_fwd")
     return o, Sf
 
 

@@ -94,7 +94,8 @@ typedef enum gdn_pass {
   GDN_PASS_CHUNK_FWD = 0,
   GDN_PASS_CHUNK_BWD = 1,
   GDN_PASS_RECURRENT_FWD = 2,
-  GDN_PASS_RECURRENT_BWD = 3
+  GDN_PASS_RECURRENT_BWD = 3,
+  GDN_PASS_KDA_FWD = 4
 } gdn_pass;
 
 typedef struct gdn_problem {
@@ -171,6 +172,28 @@ gdn_status gdn_recurrent_ref(const gdn_problem* problem, const void* q, const vo
                              const float* S0, void* o, float* S_final, const void* dO,
                              const float* dS_final, void* dq, void* dk, void* dv, float* dg,
                              float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Chunked forward pass with one log-decay per key channel: the gate layout of
+ * the cuLA issue #126 page ("Minimal public reproduction", where g has the shape
+ * of q and is handed to the KDA kernels).  Per token, with a = exp(g_t) a vector
+ * of Dk factors:  S <- diag(a) S,  e = beta (v - S^T k),  S <- S + k e^T,
+ * o = scale S^T q  (the update of "Research Sprint Day 1", "The GDN update",
+ * with a diagonal forget factor; with equal factors on every channel it is
+ * gdn_chunk_fwd's recurrence).
+ *   in : q, k [B,T,H,Dk] and v [B,T,H,Dv] (io dtype); g [B,T,H,Dk] fp32, finite
+ *        and <= 0; beta [B,T,H] fp32; S0 [N,H,Dk,Dv] fp32 or NULL (zero)
+ *   out: o [B,T,H,Dv] (io dtype), S_final [N,H,Dk,Dv] fp32 or NULL
+ * Packed sequences through cu_seqlens as for gdn_chunk_fwd.  Dk 64 or 128 and
+ * Dv a multiple of 16 up to 256, for both io dtypes; num_segments must be 1.
+ * All arithmetic is fp32 (the io dtype only at loads and the o store).
+ * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_FWD, ...): one fp32 record per
+ * chunk and head (T diag(beta), the causal score, K and Q scaled by the decays,
+ * the decayed keys of the state update).  Errors as gdn_chunk_fwd: every check
+ * runs before the first launch. */
+gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, const float* S0,
+                             void* o, float* S_final, void* workspace, size_t workspace_bytes,
                              void* stream);
 
 /* Gate forms of gdn_prologue. */

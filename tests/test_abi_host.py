@@ -234,3 +234,31 @@ def test_epilogue_checks():
     assert call(problem(Dv=96)) == nat.GDN_ERR_UNSUPPORTED          # not a power of two
     assert call(problem(), y=FAKE + 4096) == nat.GDN_ERR_ALIAS       # y inside o
     assert call(problem(), z=FAKE + (1 << 30) + 8) == nat.GDN_ERR_ALIGN
+
+
+def test_kda_workspace_and_checks():
+    # one fp32 record per (chunk slot, head): T diag(beta) and P (64 x 64 each),
+    # K o Gamma, Q o Gamma and the decayed keys (64 x Dk each), Gamma_n (Dk)
+    slots = 200 // 64 + 2 + 1
+    for Dk in (64, 128):
+        for io in (nat.GDN_BF16, nat.GDN_FP32):
+            rec = 8192 + 3 * 64 * Dk + Dk
+            assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_FWD) == (nat.GDN_OK, slots * 3 * rec * 4)
+    assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(Dk=96), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    P = ctypes.c_void_p
+    lib = nat.load()
+
+    def call(p, q=FAKE, g=FAKE + (3 << 30), o=FAKE + (5 << 30), wsp=None, nws=0):
+        return lib.gdn_kda_chunk_fwd(ctypes.byref(p), P(q), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)), P(g),
+                                     P(FAKE + (4 << 30)), None, P(o), None, P(wsp), nws, None)
+
+    assert call(problem()) == nat.GDN_ERR_WORKSPACE
+    assert call(problem(), q=None) == nat.GDN_ERR_NULL
+    assert call(problem(), g=None) == nat.GDN_ERR_NULL
+    assert call(problem(), g=FAKE + (3 << 30) + 2) == nat.GDN_ERR_ALIGN
+    assert call(problem(), o=FAKE + 4096) == nat.GDN_ERR_ALIAS
+    # g spans B T H Dk floats: an output starting inside that range aliases it
+    assert call(problem(), o=FAKE + (3 << 30) + 2 * 100 * 3 * 128 * 4 - 16) == nat.GDN_ERR_ALIAS
+    assert call(problem(num_segments=4)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched

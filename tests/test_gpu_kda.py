@@ -1,0 +1,122 @@
+"""GPU parity of the per-key-channel-decay forward (gdn_kda_chunk_fwd) against
+the fp64 oracle ``oracle.kda_fwd`` (marked gpu).
+
+Tolerances (each of o and S_final separately): max_rel <= 3e-4 for fp32 io,
+rel_rms <= 8e-3 for bf16 io -- the bars of the scalar-gate path.  Cases: both io
+dtypes and head sizes, ragged tails, packed sequences with an empty one, an
+initial state, strong and slow per-channel decay, equal decays on every channel
+(the scalar-gate recurrence), run-to-run determinism, and the 4 x 4096 x 8 x 128
+training shape in the launch configuration bench.py times (sampled heads).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_chunked_gdn_amd as gdn
+import oracle
+from gated_deltanet_chunked_gdn_amd.workloads import WORKLOADS, Workload, generate
+from oracle.compare import max_rel, rel_rms
+from _helpers import to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 3e-4
+BF16_TOL = 8e-3
+
+
+def _run(d, t):
+    cu = d["cu_seqlens"]
+    o, Sf = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t.get("S0"),
+                              cu_seqlens=cu, scale=d["scale"])
+    torch.cuda.synchronize()
+    return to_np(o), to_np(Sf)
+
+
+def _oracle(d):
+    o, Sf = oracle.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                           S0=d["S0"], scale=d["scale"])
+    return o.reshape(d["v"].shape), Sf
+
+
+def _check(d, got, ref, tag):
+    (o, Sf), (o_ref, Sf_ref) = got, ref
+    assert np.isfinite(o).all() and np.isfinite(Sf).all(), tag
+    if d["io"] == "fp32":
+        eo, es = max_rel(o, o_ref), max_rel(Sf, Sf_ref)
+        print(f"{tag}: max_rel o {eo:.2e} S_final {es:.2e}")
+        assert eo <= FP32_TOL and es <= FP32_TOL, tag
+    else:
+        eo, es = rel_rms(o, o_ref), rel_rms(Sf, Sf_ref)
+        print(f"{tag}: rel_rms o {eo:.2e} S_final {es:.2e}")
+        assert eo <= BF16_TOL and es <= BF16_TOL, tag
+
+
+CASES = [
+    Workload("kda_fp32_dk64", 2, 200, 2, 64, 64, io="fp32", qk="iid", gate="gdn_channel", s0_std=0.1,
+             scale=0.7, seed=51),
+    Workload("kda_fp32_dk128", 1, 130, 3, 128, 32, io="fp32", qk="norm_both", gate="gdn_channel", seed=52),
+    Workload("kda_bf16_dk128", 2, 257, 2, 128, 128, io="bf16", qk="norm_both", gate="gdn_channel",
+             s0_std=0.1, seed=53),
+    Workload("kda_bf16_dk64_dv128", 1, 300, 4, 64, 128, io="bf16", qk="norm_both", gate="gdn_channel",
+             cu_seqlens=(0, 70, 70, 300), s0_std=0.1, seed=54),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_kda_matches_oracle(w):
+    d = generate(w)
+    _check(d, _run(d, to_device(d)), _oracle(d), w.name)
+
+
+@pytest.mark.parametrize("kind", ["strong", "slow"])
+def test_kda_decay_extremes(kind):
+    w = Workload(f"kda_{kind}", 1, 260, 2, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel",
+                 s0_std=0.1, seed=55)
+    d = generate(w)
+    rng = np.random.default_rng(56)
+    if kind == "strong":
+        # per-channel log-decays down to -5 per token: exp(gamma) underflows within a chunk
+        d["g"] = (-5.0 / (1.0 + np.exp(-rng.standard_normal(d["q"].shape)))).astype(np.float32)
+    else:
+        d["g"] = (-1e-3 * rng.random(d["q"].shape)).astype(np.float32)
+    _check(d, _run(d, to_device(d)), _oracle(d), w.name)
+
+
+def test_kda_equal_channel_decays_is_the_scalar_gate_recurrence():
+    w = Workload("kda_equal", 2, 190, 2, 128, 128, io="bf16", qk="norm_both", gate="gdn", s0_std=0.1,
+                 seed=57)
+    d = generate(w)
+    t = to_device(d)
+    t["g"] = t["g"][..., None].expand(*d["q"].shape).contiguous()
+    got = _run(d, t)
+    o_ref, Sf_ref = oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], scale=d["scale"])
+    _check(d, got, (o_ref.reshape(d["v"].shape), Sf_ref), "equal channel decays vs scalar-gate oracle")
+
+
+def test_kda_deterministic():
+    d = generate(CASES[2])
+    t = to_device(d)
+    a = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"])
+    b = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_kda_training_shape_sampled_heads():
+    # the 4 x 4096 x 8 x 128 bf16 shape with per-channel gates, as bench.py runs it;
+    # the oracle recomputes three (sequence, head) pairs in full
+    w = WORKLOADS["kda_bf16"]
+    d = generate(w)
+    t = to_device(d)
+    o, Sf = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale)
+    torch.cuda.synchronize()
+    o, Sf = to_np(o), to_np(Sf)
+    assert np.isfinite(o).all() and np.isfinite(Sf).all()
+    for b, h in ((0, 0), (1, 5), (3, 7)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        o_ref, Sf_ref = oracle.kda_fwd(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["beta"][sl],
+                                       scale=w.scale)
+        eo = rel_rms(o[sl], o_ref)
+        es = rel_rms(Sf[b, h], Sf_ref[0, 0])
+        print(f"kda_bf16 (b={b}, h={h}): rel_rms o {eo:.2e} S_final {es:.2e}")
+        assert eo <= BF16_TOL and es <= BF16_TOL
