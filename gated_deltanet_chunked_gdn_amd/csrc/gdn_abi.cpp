@@ -128,8 +128,7 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   }
   if (kind == Kind::KdaFwd) {
     if (c.N == 0) return 0;
-    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda_rec_floats(p->Dk) *
-           sizeof(float);
+    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda_rec_bytes(p->Dk, c.bf16);
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
@@ -264,7 +263,7 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   if (c.N == 0) return GDN_OK;
   gdn::KdaParams kp{};
   kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = o; kp.S_final = S_final;
-  kp.ws = static_cast<float*>(workspace);
+  kp.ws = workspace;
   kp.seq = seq_info(p);
   kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
   kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);

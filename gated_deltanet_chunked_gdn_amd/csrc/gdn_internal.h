@@ -180,15 +180,18 @@ struct KdaParams {
   const float* S0;       // [N, H, Dk, Dv] or nullptr
   void* o;
   float* S_final;        // [N, H, Dk, Dv] or nullptr
-  float* ws;             // one record of kda_rec_floats(Dk) floats per (chunk slot, head)
+  void* ws;              // one record of kda_rec_bytes(Dk, bf16) bytes per (chunk slot, head)
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;
   float scale;
 };
 // Per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma, Q o Gamma
-// and (K o exp(gamma_n - gamma))^T (64 x Dk each), Gamma_n (Dk); all fp32.
-inline size_t kda_rec_floats(int Dk) { return 8192 + 3 * 64 * static_cast<size_t>(Dk) + Dk; }
+// and (K o exp(gamma_n - gamma))^T (64 x Dk each) in the io element type (the
+// MFMA operand type), then Gamma_n (Dk fp32).
+inline size_t kda_rec_bytes(int Dk, bool bf16) {
+  return (8192 + 3 * 64 * static_cast<size_t>(Dk)) * (bf16 ? 2 : 4) + 4 * static_cast<size_t>(Dk);
+}
 hipError_t launch_kda_fwd(const KdaParams& p, int Dk, bool bf16, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 

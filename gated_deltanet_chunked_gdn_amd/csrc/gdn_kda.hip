@@ -23,6 +23,8 @@
 //                       walks the chunks in order with its state tile in fp32
 //                       MFMA accumulators (v_mfma_f32_16x16x4_f32); four of its
 //                       eight waves load the next chunk's record meanwhile.
+#include <type_traits>
+
 #include "gdn_chunk_common.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -32,16 +34,20 @@ namespace {
 
 using chunk::seq_range;
 
-// Offsets (floats) inside one (chunk slot, head) record.
-template <int DK>
+// One (chunk slot, head) record: five matrices in the MFMA operand type EL
+// (bf16 for bf16 io, fp32 for fp32 io; element offsets below), then Gamma_n as
+// DK floats at byte kGnByte.
+template <int DK, typename EL>
 struct KdaRec {
   static constexpr int kTb = 0;               // T diag(beta), 64 x 64, zero above the diagonal
   static constexpr int kP = 4096;             // P, 64 x 64, zero above the diagonal
   static constexpr int kKG = 8192;            // K o Gamma, 64 x DK
   static constexpr int kQG = kKG + 64 * DK;   // Q o Gamma, 64 x DK
   static constexpr int kKDt = kQG + 64 * DK;  // (K o exp(gamma_n - gamma))^T, DK x 64
-  static constexpr int kGn = kKDt + 64 * DK;  // Gamma_n, DK
-  static constexpr int kSize = kGn + DK;
+  static constexpr int kElems = kKDt + 64 * DK;
+  static constexpr int kGnByte = kElems * static_cast<int>(sizeof(EL));
+  static constexpr int kBytes = kGnByte + DK * 4;
+  static_assert(kGnByte % 4096 == 0 && kBytes % 16 == 0, "record alignment");
 };
 
 // Eight consecutive io elements: raw load, widening store of eight floats to LDS.
@@ -85,8 +91,10 @@ constexpr size_t prep_smem_bytes() {
 }
 
 template <int DK, typename E>
-__global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
-  using R = KdaRec<DK>;
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
+  using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
+  using EL = typename Op::elem;
+  using R = KdaRec<DK, EL>;
   constexpr int LD = DK + 4;  // 16-byte rows: four channels per LDS read
   extern __shared__ __align__(16) float sm[];
   float* ks = sm;             // [64][LD] keys
@@ -104,7 +112,8 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
   if (r0 >= len) return;
   const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
   const int64_t slot = bos / 64 + n + c;
-  float* rec = p.ws + (slot * p.H + h) * static_cast<int64_t>(R::kSize);
+  char* const recb = static_cast<char*>(p.ws) + (slot * p.H + h) * static_cast<int64_t>(R::kBytes);
+  EL* const rec = reinterpret_cast<EL*>(recb);
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
 
@@ -113,12 +122,12 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
   // channels per load; every load of the thread is issued before the first store.
   {
     constexpr int VPR = DK / 8;             // vectors per row
-    constexpr int NV = 64 * VPR / 256;      // vectors per thread
+    constexpr int NV = 64 * VPR / 512;      // vectors per thread
     typename Vec8<E>::raw kr[NV], qr[NV];
     float4 ga[NV], gb[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int x = tid + 256 * u, i = x / VPR, ch = 8 * (x % VPR);
+      const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
       const int64_t off = ((bos + r0 + i) * p.H + h) * DK + ch;
       if (i < nr) {
         kr[u] = Vec8<E>::load(k + off);
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int x = tid + 256 * u, i = x / VPR, ch = 8 * (x % VPR);
+      const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
       Vec8<E>::store(ks + i * LD + ch, kr[u]);
       Vec8<E>::store(qs + i * LD + ch, qr[u]);
       *reinterpret_cast<float4*>(gs + i * LD + ch) = ga[u];
@@ -151,36 +160,62 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
   }
   __syncthreads();
 
-  // A and P over the 2080 pairs j <= i, one pair per thread at a time
-  for (int pi = tid; pi < 64 * 65 / 2; pi += 256) {
-    int i = static_cast<int>((sqrtf(8.f * pi + 1.f) - 1.f) * 0.5f);
-    if (i * (i + 1) / 2 > pi) --i;
-    if ((i + 1) * (i + 2) / 2 <= pi) ++i;
-    const int j = pi - i * (i + 1) / 2;
-    const float* ki = ks + i * LD;
-    const float* kj = ks + j * LD;
-    const float* qi = qs + i * LD;
-    const float* gi = gs + i * LD;
-    const float* gj = gs + j * LD;
-    float a = 0.f, s = 0.f;
-#pragma unroll 4
+  // A and P over the pairs j <= i in 2 x 2 tiles (rows i0, i0 + 1; columns j0,
+  // j0 + 1): 528 tiles on or below the diagonal; each channel quad of the four
+  // rows is read from LDS once per tile.  The pair above the diagonal of a
+  // diagonal tile is computed and dropped.
+  for (int t = tid; t < 32 * 33 / 2; t += 512) {
+    int ti = static_cast<int>((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+    if (ti * (ti + 1) / 2 > t) --ti;
+    if ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    const int tj = t - ti * (ti + 1) / 2;
+    const int i0 = 2 * ti, j0 = 2 * tj;
+    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+    float s00 = 0.f, s01 = 0.f, s10 = 0.f, s11 = 0.f;
+#pragma unroll 2
     for (int ch = 0; ch < DK; ch += 4) {
-      const float4 k4i = *reinterpret_cast<const float4*>(ki + ch);
-      const float4 k4j = *reinterpret_cast<const float4*>(kj + ch);
-      const float4 q4i = *reinterpret_cast<const float4*>(qi + ch);
-      const float4 g4i = *reinterpret_cast<const float4*>(gi + ch);
-      const float4 g4j = *reinterpret_cast<const float4*>(gj + ch);
-      const float d0 = k4j.x * __expf(g4i.x - g4j.x), d1 = k4j.y * __expf(g4i.y - g4j.y);
-      const float d2 = k4j.z * __expf(g4i.z - g4j.z), d3 = k4j.w * __expf(g4i.w - g4j.w);
-      a = fmaf(k4i.x, d0, fmaf(k4i.y, d1, fmaf(k4i.z, d2, fmaf(k4i.w, d3, a))));
-      s = fmaf(q4i.x, d0, fmaf(q4i.y, d1, fmaf(q4i.z, d2, fmaf(q4i.w, d3, s))));
+      const f32x4_t ki0 = *reinterpret_cast<const f32x4_t*>(ks + i0 * LD + ch);
+      const f32x4_t ki1 = *reinterpret_cast<const f32x4_t*>(ks + (i0 + 1) * LD + ch);
+      const f32x4_t qi0 = *reinterpret_cast<const f32x4_t*>(qs + i0 * LD + ch);
+      const f32x4_t qi1 = *reinterpret_cast<const f32x4_t*>(qs + (i0 + 1) * LD + ch);
+      const f32x4_t gi0 = *reinterpret_cast<const f32x4_t*>(gs + i0 * LD + ch);
+      const f32x4_t gi1 = *reinterpret_cast<const f32x4_t*>(gs + (i0 + 1) * LD + ch);
+      const f32x4_t kj0 = *reinterpret_cast<const f32x4_t*>(ks + j0 * LD + ch);
+      const f32x4_t kj1 = *reinterpret_cast<const f32x4_t*>(ks + (j0 + 1) * LD + ch);
+      const f32x4_t gj0 = *reinterpret_cast<const f32x4_t*>(gs + j0 * LD + ch);
+      const f32x4_t gj1 = *reinterpret_cast<const f32x4_t*>(gs + (j0 + 1) * LD + ch);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float d00 = kj0[x] * __expf(gi0[x] - gj0[x]);
+        const float d01 = kj1[x] * __expf(gi0[x] - gj1[x]);
+        const float d10 = kj0[x] * __expf(gi1[x] - gj0[x]);
+        const float d11 = kj1[x] * __expf(gi1[x] - gj1[x]);
+        a00 = fmaf(ki0[x], d00, a00);
+        a01 = fmaf(ki0[x], d01, a01);
+        a10 = fmaf(ki1[x], d10, a10);
+        a11 = fmaf(ki1[x], d11, a11);
+        s00 = fmaf(qi0[x], d00, s00);
+        s01 = fmaf(qi0[x], d01, s01);
+        s10 = fmaf(qi1[x], d10, s10);
+        s11 = fmaf(qi1[x], d11, s11);
+      }
     }
-    As[i * 65 + j] = j < i ? bs[i] * a : 0.f;
-    rec[R::kP + i * 64 + j] = s;
+    const float av[2][2] = {{a00, a01}, {a10, a11}};
+    const float sv[2][2] = {{s00, s01}, {s10, s11}};
+#pragma unroll
+    for (int di = 0; di < 2; ++di)
+#pragma unroll
+      for (int dj = 0; dj < 2; ++dj) {
+        const int i = i0 + di, j = j0 + dj;
+        if (j <= i) {
+          As[i * 65 + j] = j < i ? bs[i] * av[di][dj] : 0.f;
+          rec[R::kP + i * 64 + j] = Op::cvt(sv[di][dj]);
+        }
+      }
   }
-  for (int x = tid; x < 64 * 64; x += 256) {
+  for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
-    if (j > i) rec[R::kP + x] = 0.f;
+    if (j > i) rec[R::kP + x] = Op::cvt(0.f);
     if (j / 16 > i / 16) Ts[i * 65 + j] = 0.f;  // T is zero above its diagonal blocks
   }
   __syncthreads();
@@ -188,7 +223,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
   // T = (I + A)^-1: the 16x16 diagonal blocks by forward substitution (wave w
   // inverts block w, one column per lane), then the blocks below, band by band:
   // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (fp32 MFMA)
-  if (lane < 16) {
+  if (wave < 4 && lane < 16) {
     const int b = wave, cc = lane;
     float tcol[16];
 #pragma unroll
@@ -223,29 +258,52 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p) {
     __syncthreads();
   }
 
-  for (int x = tid; x < 64 * 64; x += 256) {
+  for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
-    rec[R::kTb + x] = Ts[i * 65 + j] * bs[j];
+    rec[R::kTb + x] = Op::cvt(Ts[i * 65 + j] * bs[j]);
   }
   const float* gn = gs + (nr - 1) * LD;
-  for (int x = tid; x < 64 * DK; x += 256) {
+  for (int x = tid; x < 64 * DK; x += 512) {
     const int i = x / DK, ch = x % DK;
     const float e = __expf(gs[i * LD + ch]);
-    rec[R::kKG + x] = ks[i * LD + ch] * e;
-    rec[R::kQG + x] = qs[i * LD + ch] * e;
+    rec[R::kKG + x] = Op::cvt(ks[i * LD + ch] * e);
+    rec[R::kQG + x] = Op::cvt(qs[i * LD + ch] * e);
   }
-  for (int x = tid; x < 64 * DK; x += 256) {
+  for (int x = tid; x < 64 * DK; x += 512) {
     const int ch = x / 64, i = x % 64;
-    rec[R::kKDt + x] = ks[i * LD + ch] * __expf(gn[ch] - gs[i * LD + ch]);
+    rec[R::kKDt + x] = Op::cvt(ks[i * LD + ch] * __expf(gn[ch] - gs[i * LD + ch]));
   }
-  if (tid < DK) rec[R::kGn + tid] = __expf(gn[tid]);
+  if (tid < DK) reinterpret_cast<float*>(recb + R::kGnByte)[tid] = __expf(gn[tid]);
 }
 
-// LDS of the state kernel (floats): row strides keep 16-byte aligned rows.
-template <int DK>
+// acc += A(16 x K) B(K x 16) (A row-major, B stored transposed, as tile_mma),
+// the k-steps dealt round-robin to up to four accumulators so that independent
+// chains are in flight instead of one dependent chain.
+template <typename Op, int K>
+__device__ __forceinline__ void tile_mma_split(f32x4_t& acc, const typename Op::elem* a, int lda,
+                                               const typename Op::elem* bt, int ldb, int lane) {
+  constexpr int NS = K / Op::KSTEP;
+  constexpr int NA = NS < 4 ? NS : 4;
+  static_assert(NS * Op::KSTEP == K, "K must be a multiple of the MFMA depth");
+  f32x4_t x[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) x[j] = zero4();
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    x[st % NA] = Op::mma(Op::frag(a, lda, lane, st * Op::KSTEP), Op::frag(bt, ldb, lane, st * Op::KSTEP), x[st % NA]);
+  f32x4_t t = x[0];
+#pragma unroll
+  for (int j = 1; j < NA; ++j) t += x[j];
+  acc += t;
+}
+
+// LDS of the state kernel, in elements of the operand type EL (row strides keep
+// 16-byte aligned rows), then Gamma_n as DK floats.
+template <int DK, typename EL>
 struct StateLds {
-  static constexpr int LK = DK + 4;  // rows of K o Gamma, Q o Gamma and the transposed state
-  static constexpr int L64 = 68;     // rows of 64-wide matrices
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(EL));
+  static constexpr int LK = DK + PAD;  // rows of K o Gamma, Q o Gamma and the transposed state
+  static constexpr int L64 = 64 + PAD; // rows of 64-wide matrices
   static constexpr int kKG = 0;
   static constexpr int kQG = kKG + 64 * LK;
   static constexpr int kKDt = kQG + 64 * LK;
@@ -254,61 +312,71 @@ struct StateLds {
   static constexpr int kSt = kP + 64 * L64;   // [16][LK]: S^T of the tile
   static constexpr int kRt = kSt + 16 * LK;   // [16][L64]: (V - (K o Gamma) S)^T
   static constexpr int kEt = kRt + 16 * L64;  // [16][L64]: E^T
-  static constexpr int kGn = kEt + 16 * L64;  // [DK]
-  static constexpr int kFloats = kGn + DK;
+  static constexpr int kElems = kEt + 16 * L64;
+  static constexpr int kGnByte = (kElems * static_cast<int>(sizeof(EL)) + 15) / 16 * 16;
+  static constexpr int kBytes = kGnByte + DK * 4;
 };
 
-// One chunk record in registers: the matrices (T diag(beta), P, K o Gamma,
-// Q o Gamma, the decayed keys; contiguous in the record) as 16-byte vectors
-// tid + 256 u, and Gamma_n[tid].  Region boundaries are multiples of 256
-// vectors, so each u belongs to one matrix at compile time.  (A native vector
-// type: arrays of HIP's float4 struct are kept in scratch memory when they live
-// across a barrier.)
-template <int DK>
+// One chunk record in registers: the five matrices (contiguous at the start of
+// the record) as 16-byte vectors tid + 256 u, and Gamma_n[tid].  Every matrix
+// spans a multiple of 256 vectors, so each u belongs to one matrix at compile
+// time.  (A native vector type: arrays of HIP's float4 struct are kept in
+// scratch memory when they live across a barrier.)
+template <int DK, typename EL>
 struct Stager {
-  using L = StateLds<DK>;
-  static constexpr int NV = (8192 + 3 * 64 * DK) / 4 / 256;
-  static constexpr int kUP = 4096 / 4 / 256;                // first u of P
-  static constexpr int kUKG = 8192 / 4 / 256;               // first u of K o Gamma
-  static constexpr int kUQG = kUKG + 64 * DK / 4 / 256;     // first u of Q o Gamma
-  static constexpr int kUKD = kUQG + 64 * DK / 4 / 256;     // first u of the decayed keys
+  using L = StateLds<DK, EL>;
+  using R = KdaRec<DK, EL>;
+  static constexpr int EPV = 16 / static_cast<int>(sizeof(EL));   // elements per vector
+  static constexpr int NV = R::kGnByte / 16 / 256;
+  static constexpr int kUP = 4096 / EPV / 256;                     // first u of P
+  static constexpr int kUKG = 2 * kUP;                             // first u of K o Gamma
+  static constexpr int kUQG = kUKG + 64 * DK / EPV / 256;          // first u of Q o Gamma
+  static constexpr int kUKD = kUQG + 64 * DK / EPV / 256;          // first u of the decayed keys
+  static_assert(kUKD + 64 * DK / EPV / 256 == NV, "record layout");
 
-  static __device__ __forceinline__ void load(f32x4_t (&r)[NV], float& gn, const float* rec, int tid) {
+  static __device__ __forceinline__ void load(f32x4_t (&r)[NV], float& gn, const char* rec, int tid) {
 #pragma unroll
-    for (int u = 0; u < NV; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(rec + 4 * (tid + 256 * u));
-    gn = tid < DK ? rec[8192 + 3 * 64 * DK + tid] : 0.f;
+    for (int u = 0; u < NV; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(rec + 16 * (tid + 256 * u));
+    gn = tid < DK ? reinterpret_cast<const float*>(rec + R::kGnByte)[tid] : 0.f;
   }
-  static __device__ __forceinline__ void store(const f32x4_t (&r)[NV], float gn, float* sm, int tid) {
+  static __device__ __forceinline__ void store(const f32x4_t (&r)[NV], float gn, char* smb, int tid) {
+    EL* const sm = reinterpret_cast<EL*>(smb);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      float* dst;
+      EL* dst;
       if (u < kUKG) {  // T diag(beta) or P: 64-wide rows
-        const int f = 4 * (tid + 256 * (u < kUP ? u : u - kUP));
+        const int f = EPV * (tid + 256 * (u < kUP ? u : u - kUP));
         dst = sm + (u < kUP ? L::kTb : L::kP) + (f / 64) * L::L64 + f % 64;
       } else if (u < kUKD) {  // K o Gamma or Q o Gamma: DK-wide rows
-        const int f = 4 * (tid + 256 * (u < kUQG ? u - kUKG : u - kUQG));
+        const int f = EPV * (tid + 256 * (u < kUQG ? u - kUKG : u - kUQG));
         dst = sm + (u < kUQG ? L::kKG : L::kQG) + (f / DK) * L::LK + f % DK;
       } else {  // decayed keys, transposed: DK rows of 64
-        const int f = 4 * (tid + 256 * (u - kUKD));
+        const int f = EPV * (tid + 256 * (u - kUKD));
         dst = sm + L::kKDt + (f / 64) * L::L64 + f % 64;
       }
       *reinterpret_cast<f32x4_t*>(dst) = r[u];
     }
-    if (tid < DK) sm[L::kGn + tid] = gn;
+    if (tid < DK) reinterpret_cast<float*>(smb + L::kGnByte)[tid] = gn;
   }
 };
 
 // Eight waves: waves 0-3 compute (wave w owns rows 16 w .. 16 w + 15 of the
 // chunk and state row blocks w, w + 4), waves 4-7 load the next chunk's record
 // into registers while the current one is computed and write it to LDS at the
-// top of the next step.
+// top of the next step.  The state stays fp32 in accumulators; for bf16 io the
+// products take bf16 operands (the record, S, R and E rounded to bf16) with
+// fp32 accumulation, for fp32 io every product is IEEE fp32.
 template <int DK, typename E>
 __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
-  using R = KdaRec<DK>;
-  using L = StateLds<DK>;
-  using St8 = Stager<DK>;
+  using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
+  using EL = typename Op::elem;
+  using R = KdaRec<DK, EL>;
+  using L = StateLds<DK, EL>;
+  using St8 = Stager<DK, EL>;
   constexpr int RB = DK / 64;  // state row blocks per compute wave
-  extern __shared__ __align__(16) float sm[];
+  extern __shared__ __align__(16) char smb[];
+  EL* const sm = reinterpret_cast<EL*>(smb);
+  const float* const gn_s = reinterpret_cast<const float*>(smb + L::kGnByte);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool loader = tid >= 256;
   const int lt = tid - 256;
@@ -325,11 +393,11 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   const int c0 = tile * 16 + col;
   const E* v = static_cast<const E*>(p.v);
   E* o = static_cast<E*>(p.o);
-  float* St = sm + L::kSt;
-  float* Rt = sm + L::kRt;
-  float* Et = sm + L::kEt;
-  const float* rec0 = p.ws + ((bos / 64 + n) * p.H + h) * static_cast<int64_t>(R::kSize);
-  const int64_t rec_step = static_cast<int64_t>(p.H) * R::kSize;  // next chunk slot, same head
+  EL* St = sm + L::kSt;
+  EL* Rt = sm + L::kRt;
+  EL* Et = sm + L::kEt;
+  const char* rec0 = static_cast<const char*>(p.ws) + ((bos / 64 + n) * p.H + h) * static_cast<int64_t>(R::kBytes);
+  const int64_t rec_step = static_cast<int64_t>(p.H) * R::kBytes;  // next chunk slot, same head
 
   // The two roles run separate loops with the same four barriers per chunk, so
   // the loaders' prefetch registers and the compute waves' operands never have
@@ -340,7 +408,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
     if (nch > 0) St8::load(pre, pre_gn, rec0, lt);
     for (int c = 0; c < nch; ++c) {
       __syncthreads();  // the previous chunk's reads of the staged record are done
-      St8::store(pre, pre_gn, sm, lt);
+      St8::store(pre, pre_gn, smb, lt);
       __syncthreads();
       if (c + 1 < nch) St8::load(pre, pre_gn, rec0 + (c + 1) * rec_step, lt);
       __syncthreads();
@@ -358,38 +426,49 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * (w + 4 * b) + 4 * g4 + r;
       S[b][r] = p.S0 ? p.S0[(sbase + row) * Dv + c0] : 0.f;
-      St[col * L::LK + row] = S[b][r];
+      St[col * L::LK + row] = Op::cvt(S[b][r]);
     }
   }
+  // this lane's four values of v (rows 16 w + 4 g4 + r, column c0), one chunk ahead
+  float vnext[4];
+  auto load_v = [&](int c) {
+    const int64_t r0 = 64LL * c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * w + 4 * g4 + r;
+      vnext[r] = r0 + row < len ? IoT<E>::ld(v + ((bos + r0 + row) * p.H + h) * Dv + c0) : 0.f;
+    }
+  };
+  if (nch > 0) load_v(0);
   for (int c = 0; c < nch; ++c) {
     const int64_t r0 = 64LL * c;
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
+    float vcur[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vcur[r] = vnext[r];
+    if (c + 1 < nch) load_v(c + 1);
     __syncthreads();
     __syncthreads();  // the record of chunk c is in LDS
-    {
-      // R = V - (K o Gamma) S for rows 16 w .. 16 w + 15
-      f32x4_t ks = zero4();
-      tile_mma<OpF32, DK>(ks, sm + L::kKG + 16 * w * L::LK, L::LK, St, L::LK, lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w + 4 * g4 + r;
-        const float vv = row < nr ? IoT<E>::ld(v + ((bos + r0 + row) * p.H + h) * Dv + c0) : 0.f;
-        Rt[col * L::L64 + row] = vv - ks[r];
-      }
-    }
-    __syncthreads();
-    // E = T diag(beta) R, then (Q o Gamma) S while E is published
+    // R = V - (K o Gamma) S and (Q o Gamma) S for rows 16 w .. 16 w + 15
     f32x4_t qsacc = zero4();
     {
-      f32x4_t e = zero4();
-      tile_mma<OpF32, 64>(e, sm + L::kTb + 16 * w * L::L64, L::L64, Rt, L::L64, lane);
+      f32x4_t ks = zero4();
+      tile_mma_split<Op, DK>(ks, sm + L::kKG + 16 * w * L::LK, L::LK, St, L::LK, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Et[col * L::L64 + 16 * w + 4 * g4 + r] = e[r];
-      tile_mma<OpF32, DK>(qsacc, sm + L::kQG + 16 * w * L::LK, L::LK, St, L::LK, lane);
+      for (int r = 0; r < 4; ++r) Rt[col * L::L64 + 16 * w + 4 * g4 + r] = Op::cvt(vcur[r] - ks[r]);
+      tile_mma_split<Op, DK>(qsacc, sm + L::kQG + 16 * w * L::LK, L::LK, St, L::LK, lane);
+    }
+    __syncthreads();
+    // E = T diag(beta) R
+    {
+      f32x4_t e = zero4();
+      tile_mma_split<Op, 64>(e, sm + L::kTb + 16 * w * L::L64, L::L64, Rt, L::L64, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Et[col * L::L64 + 16 * w + 4 * g4 + r] = Op::cvt(e[r]);
     }
     __syncthreads();
     // O = scale ((Q o Gamma) S + P E)
-    tile_mma<OpF32, 64>(qsacc, sm + L::kP + 16 * w * L::L64, L::L64, Et, L::L64, lane);
+    tile_mma_split<Op, 64>(qsacc, sm + L::kP + 16 * w * L::L64, L::L64, Et, L::L64, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * w + 4 * g4 + r;
@@ -400,15 +479,15 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
     for (int b = 0; b < RB; ++b) {
       const int rb = w + 4 * b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[b][r] *= sm[L::kGn + 16 * rb + 4 * g4 + r];
-      tile_mma<OpF32, 64>(S[b], sm + L::kKDt + 16 * rb * L::L64, L::L64, Et, L::L64, lane);
+      for (int r = 0; r < 4; ++r) S[b][r] *= gn_s[16 * rb + 4 * g4 + r];
+      tile_mma_split<Op, 64>(S[b], sm + L::kKDt + 16 * rb * L::L64, L::L64, Et, L::L64, lane);
     }
     // every compute wave has finished reading St (before the previous barrier),
     // so the new state can replace it now
 #pragma unroll
     for (int b = 0; b < RB; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) St[col * L::LK + 16 * (w + 4 * b) + 4 * g4 + r] = S[b][r];
+      for (int r = 0; r < 4; ++r) St[col * L::LK + 16 * (w + 4 * b) + 4 * g4 + r] = Op::cvt(S[b][r]);
   }
 
   if (p.S_final) {
@@ -422,10 +501,11 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
 
 template <int DK, typename E>
 hipError_t launch_kda_t(const KdaParams& p, hipStream_t s) {
-  static_assert(StateLds<DK>::kFloats * sizeof(float) <= 160 * 1024, "LDS budget exceeded");
+  using EL = typename std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>::elem;
+  static_assert(StateLds<DK, EL>::kBytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(prep_smem_bytes<DK>() <= 160 * 1024, "LDS budget exceeded");
   constexpr size_t prep_smem = prep_smem_bytes<DK>();
-  constexpr size_t state_smem = StateLds<DK>::kFloats * sizeof(float);
+  constexpr size_t state_smem = StateLds<DK, EL>::kBytes;
   auto prep = kda_prep_kernel<DK, E>;
   auto state = kda_state_kernel<DK, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
@@ -435,7 +515,7 @@ hipError_t launch_kda_t(const KdaParams& p, hipStream_t s) {
                           static_cast<int>(state_smem));
   if (e != hipSuccess) return e;
   if (p.max_chunks > 0) {
-    hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), prep_smem, s, p);
+    hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(512), prep_smem, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -186,10 +186,11 @@ gdn_status gdn_recurrent_ref(const gdn_problem* problem, const void* q, const vo
  *   out: o [B,T,H,Dv] (io dtype), S_final [N,H,Dk,Dv] fp32 or NULL
  * Packed sequences through cu_seqlens as for gdn_chunk_fwd.  Dk 64 or 128 and
  * Dv a multiple of 16 up to 256, for both io dtypes; num_segments must be 1.
- * All arithmetic is fp32 (the io dtype only at loads and the o store).
- * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_FWD, ...): one fp32 record per
- * chunk and head (T diag(beta), the causal score, K and Q scaled by the decays,
- * the decayed keys of the state update).  Errors as gdn_chunk_fwd: every check
+ * Precision: decays, A, the inverse and the state are fp32; the products take
+ * bf16 operands with fp32 accumulation for bf16 io and are IEEE fp32 for fp32 io.
+ * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_FWD, ...): one record per chunk
+ * and head (T diag(beta), the causal score, K and Q scaled by the decays, the
+ * decayed keys of the state update, in the io element type; the chunk's decay).  Errors as gdn_chunk_fwd: every check
  * runs before the first launch. */
 gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
                              const void* v, const float* g, const float* beta, const float* S0,

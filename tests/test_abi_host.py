@@ -237,13 +237,14 @@ def test_epilogue_checks():
 
 
 def test_kda_workspace_and_checks():
-    # one fp32 record per (chunk slot, head): T diag(beta) and P (64 x 64 each),
-    # K o Gamma, Q o Gamma and the decayed keys (64 x Dk each), Gamma_n (Dk)
+    # one record per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma,
+    # Q o Gamma and the decayed keys (64 x Dk each) in the io element type, then
+    # Gamma_n (Dk fp32)
     slots = 200 // 64 + 2 + 1
     for Dk in (64, 128):
-        for io in (nat.GDN_BF16, nat.GDN_FP32):
-            rec = 8192 + 3 * 64 * Dk + Dk
-            assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_FWD) == (nat.GDN_OK, slots * 3 * rec * 4)
+        for io, size in ((nat.GDN_BF16, 2), (nat.GDN_FP32, 4)):
+            rec = (8192 + 3 * 64 * Dk) * size + 4 * Dk
+            assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_FWD) == (nat.GDN_OK, slots * 3 * rec)
     assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(Dk=96), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
     P = ctypes.c_void_p
