@@ -361,9 +361,9 @@ struct Stager {
 };
 
 // Eight waves: waves 0-3 compute (wave w owns rows 16 w .. 16 w + 15 of the
-// chunk and state row blocks w, w + 4), waves 4-7 load the next chunk's record
-// into registers while the current one is computed and write it to LDS at the
-// top of the next step.  The state stays fp32 in accumulators; for bf16 io the
+// chunk and state row blocks w, w + 4), waves 4-7 keep the records of the next
+// two chunks (one for fp32 records) in registers while the current one is
+// computed and write each to LDS at the top of its step.  The state stays fp32 in accumulators; for bf16 io the
 // products take bf16 operands (the record, S, R and E rounded to bf16) with
 // fp32 accumulation, for fp32 io every product is IEEE fp32.
 template <int DK, typename E>
@@ -403,16 +403,41 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   // the loaders' prefetch registers and the compute waves' operands never have
   // to be allocated side by side.
   if (loader) {
-    f32x4_t pre[St8::NV];
-    float pre_gn = 0.f;
-    if (nch > 0) St8::load(pre, pre_gn, rec0, lt);
-    for (int c = 0; c < nch; ++c) {
-      __syncthreads();  // the previous chunk's reads of the staged record are done
-      St8::store(pre, pre_gn, smb, lt);
-      __syncthreads();
-      if (c + 1 < nch) St8::load(pre, pre_gn, rec0 + (c + 1) * rec_step, lt);
-      __syncthreads();
-      __syncthreads();
+    if constexpr (St8::NV <= 16) {
+      // two records in flight: chunk c + 2 is requested as chunk c is staged
+      f32x4_t pa[St8::NV], pb[St8::NV];
+      float ga = 0.f, gb = 0.f;
+      if (nch > 0) St8::load(pa, ga, rec0, lt);
+      if (nch > 1) St8::load(pb, gb, rec0 + rec_step, lt);
+      for (int c = 0; c < nch; c += 2) {
+        __syncthreads();  // the previous chunk's reads of the staged record are done
+        St8::store(pa, ga, smb, lt);
+        __syncthreads();
+        if (c + 2 < nch) St8::load(pa, ga, rec0 + (c + 2) * rec_step, lt);
+        __syncthreads();
+        __syncthreads();
+        if (c + 1 < nch) {
+          __syncthreads();
+          St8::store(pb, gb, smb, lt);
+          __syncthreads();
+          if (c + 3 < nch) St8::load(pb, gb, rec0 + (c + 3) * rec_step, lt);
+          __syncthreads();
+          __syncthreads();
+        }
+      }
+    } else {
+      // fp32 records (twice the registers): one record in flight
+      f32x4_t pa[St8::NV];
+      float ga = 0.f;
+      if (nch > 0) St8::load(pa, ga, rec0, lt);
+      for (int c = 0; c < nch; ++c) {
+        __syncthreads();
+        St8::store(pa, ga, smb, lt);
+        __syncthreads();
+        if (c + 1 < nch) St8::load(pa, ga, rec0 + (c + 1) * rec_step, lt);
+        __syncthreads();
+        __syncthreads();
+      }
     }
     return;
   }
