@@ -73,94 +73,107 @@ def event_times(call, n_calls, warmup, stream):
     return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
 
-def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup):
-    """Backward of the training shape and the segment split of the long sequence
-    (reported beside the headline forward number, not in it)."""
+EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda")
+
+
+def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRAS):
+    """The other passes, reported beside the headline forward number (not in it):
+    backward of the training shape, the segment split of the long sequence, the
+    input prologue and output epilogue, and the per-key-channel-decay forward."""
     import torch
 
     out = {}
     stream = torch.cuda.current_stream(dev)
-    # backward, B=32 T=1024 H=16 d_k=64 d_v=128
-    w = WORKLOADS["fwdbwd_bf16"]
-    d = generate(w)
-    sets = []
-    for _ in range(2):
-        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v", "dO")}
-        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta", "S0")})
-        sets.append(t)
+    if "bwd" in which:
+        # backward, B=32 T=1024 H=16 d_k=64 d_v=128
+        w = WORKLOADS["fwdbwd_bf16"]
+        d = generate(w)
+        sets = []
+        for _ in range(2):
+            t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v", "dO")}
+            t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta", "S0")})
+            sets.append(t)
 
-    def bwd(i):
-        t = sets[i % len(sets)]
-        gdn.chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], S0=t["S0"], scale=d["scale"])
+        def bwd(i):
+            t = sets[i % len(sets)]
+            gdn.chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], S0=t["S0"], scale=d["scale"])
 
-    kt = event_times(bwd, steps, warmup, stream)
-    nb = bwd_alg_bytes(w, 2)
-    out["bwd"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3,
-                  "tokens_per_s": w.B * w.T / float(kt.mean()),
-                  "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
-                  "kernels": "prep + state (with per-chunk states) + chunk_dstate + chunk_grad"}
-    del sets
-    # segment split, B=1 T=65536 H=1 d=128
-    w = WORKLOADS["long_bf16"]
-    d = generate(w)
-    t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
-    t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
-    seg = {}
-    for G in (1, 2, 4, 8, 16):
-        ws = gdn.forward_workspace(t["q"], t["v"], None, G)
+        kt = event_times(bwd, steps, warmup, stream)
+        nb = bwd_alg_bytes(w, 2)
+        out["bwd"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3,
+                      "tokens_per_s": w.B * w.T / float(kt.mean()),
+                      "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
+                      "kernels": "prep + state (with per-chunk states) + chunk_dstate + chunk_grad"}
+        del sets
+    if "segment_split" in which:
+        # segment split, B=1 T=65536 H=1 d=128
+        w = WORKLOADS["long_bf16"]
+        d = generate(w)
+        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+        seg = {}
+        for G in (1, 2, 4, 8, 16):
+            ws = gdn.forward_workspace(t["q"], t["v"], None, G)
+            o = torch.empty_like(t["v"])
+            Sf = torch.empty((1, 1, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+            def fwd(i, G=G, ws=ws, o=o, Sf=Sf):
+                gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], num_segments=G,
+                              out=o, final_state_out=Sf, workspace=ws)
+
+            kt = event_times(fwd, max(5, steps // 4), 2, stream)
+            seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
+        out["segment_split"] = {"workload": w.name, "by_num_segments": seg}
+    if "prologue" in which:
+        # fused input prologue (normalised q, k; g; beta) on the training shape
+        w = WORKLOADS["train_bf16"]
+        rng = np.random.default_rng(11)
+        shape = (w.B, w.T, w.H, w.Dk)
+        qr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+        kr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+        a = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
+        b = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
+        A_log = torch.from_numpy(rng.uniform(0.0, 1.5, size=(w.H,)).astype(np.float32)).to(dev)
+        dt = torch.from_numpy((0.5 * rng.standard_normal(w.H)).astype(np.float32)).to(dev)
+        kt = event_times(lambda i: gdn.prologue(qr, kr, a, b, A_log, dt), steps, warmup, stream)
+        th = w.B * w.T * w.H
+        nb = th * (2 * w.Dk * 2 * 2 + 4 * 4)  # q, k read and written (bf16); a, b read, g, beta written
+        out["prologue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
+                           "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
+        del qr, kr
+    if "epilogue" in which:
+        # output epilogue (RMSNorm(o) * weight * silu(z)) on the training shape
+        w = WORKLOADS["train_bf16"]
+        rng = np.random.default_rng(12)
+        th = w.B * w.T * w.H
+        shape = (w.B, w.T, w.H, w.Dv)
+        o = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+        z = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
+        wt = torch.ones(w.Dv, dtype=torch.float32, device=dev)
+        kt = event_times(lambda i: gdn.epilogue(o, z, wt), steps, warmup, stream)
+        nb = th * w.Dv * 2 * 3  # o, z read, y written (bf16)
+        out["epilogue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
+                           "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
+        del o, z
+    if "kda" in which:
+        # per-key-channel decay (gdn_kda_chunk_fwd) on the training shape
+        w = WORKLOADS["kda_bf16"]
+        d = generate(w)
+        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+        del d
         o = torch.empty_like(t["v"])
-        Sf = torch.empty((1, 1, w.Dk, w.Dv), dtype=torch.float32, device=dev)
-
-        def fwd(i, G=G, ws=ws, o=o, Sf=Sf):
-            gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], num_segments=G,
-                          out=o, final_state_out=Sf, workspace=ws)
-
-        kt = event_times(fwd, max(5, steps // 4), 2, stream)
-        seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
-    out["segment_split"] = {"workload": w.name, "by_num_segments": seg}
-    # fused input prologue (normalised q, k; g; beta) on the training shape
-    w = WORKLOADS["train_bf16"]
-    rng = np.random.default_rng(11)
-    shape = (w.B, w.T, w.H, w.Dk)
-    qr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
-    kr = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
-    a = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
-    b = torch.from_numpy(rng.standard_normal(shape[:3], dtype=np.float32)).to(dev)
-    A_log = torch.from_numpy(rng.uniform(0.0, 1.5, size=(w.H,)).astype(np.float32)).to(dev)
-    dt = torch.from_numpy((0.5 * rng.standard_normal(w.H)).astype(np.float32)).to(dev)
-    kt = event_times(lambda i: gdn.prologue(qr, kr, a, b, A_log, dt), steps, warmup, stream)
-    th = w.B * w.T * w.H
-    nb = th * (2 * w.Dk * 2 * 2 + 4 * 4)  # q, k read and written (bf16); a, b read, g, beta written
-    out["prologue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
-                       "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
-    # output epilogue (RMSNorm(o) * weight * silu(z)) on the training shape
-    shape = (w.B, w.T, w.H, w.Dv)
-    o = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
-    z = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(dev).to(torch.bfloat16)
-    wt = torch.ones(w.Dv, dtype=torch.float32, device=dev)
-    kt = event_times(lambda i: gdn.epilogue(o, z, wt), steps, warmup, stream)
-    nb = th * w.Dv * 2 * 3  # o, z read, y written (bf16)
-    out["epilogue"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "bytes_per_launch": nb,
-                       "GBps": nb / float(kt.mean()) / 1e9, "frac_of_8TBps": nb / float(kt.mean()) / 8e12}
-    del o, z, qr, kr
-    # per-key-channel decay (gdn_kda_chunk_fwd) on the training shape
-    w = WORKLOADS["kda_bf16"]
-    d = generate(w)
-    t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
-    t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
-    del d
-    o = torch.empty_like(t["v"])
-    Sf = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
-    kws = torch.empty(gdn_workspace_bytes(gdn, t["q"], t["v"]), dtype=torch.uint8, device=dev)
-    kt = event_times(lambda i: gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale,
-                                                 out=o, final_state_out=Sf, workspace=kws),
-                     steps, warmup, stream)
-    th = w.B * w.T * w.H
-    # q, k, v read and o written (bf16), g (Dk fp32 per token-head) and beta read, S_final written
-    nb = th * ((2 * w.Dk + 2 * w.Dv) * 2 + w.Dk * 4 + 4) + w.B * w.H * w.Dk * w.Dv * 4
-    out["kda"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
-                  "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
-                  "kernels": "kda_prep_kernel + kda_state_kernel (fp32 arithmetic)"}
+        Sf = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+        kws = torch.empty(gdn_workspace_bytes(gdn, t["q"], t["v"]), dtype=torch.uint8, device=dev)
+        kt = event_times(lambda i: gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale,
+                                                     out=o, final_state_out=Sf, workspace=kws),
+                         steps, warmup, stream)
+        th = w.B * w.T * w.H
+        # q, k, v read and o written (bf16), g (Dk fp32 per token-head) and beta read, S_final written
+        nb = th * ((2 * w.Dk + 2 * w.Dv) * 2 + w.Dk * 4 + 4) + w.B * w.H * w.Dk * w.Dv * 4
+        out["kda"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
+                      "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
+                      "kernels": "kda_prep_kernel + kda_state_kernel"}
     return out
 
 
@@ -241,7 +254,9 @@ def parse():
                     help="segments per sequence (1: serial over chunks; 2..16: segment split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the backward and segment-split measurements")
+                    help="skip the measurements of the other passes")
+    ap.add_argument("--extra", choices=EXTRAS, default=None,
+                    help="time only this other pass (HIP events) and print its JSON object")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -336,6 +351,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.extra:
+        dev = torch.device("cuda:0")
+        res = extra_measurements(gdn, generate, WORKLOADS, dev, args.steps, args.warmup, (args.extra,))
+        print(json.dumps({"extra": args.extra, **res[args.extra]}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     d = generate(w)
     io = torch.bfloat16 if w.io == "bf16" else torch.float32
