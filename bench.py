@@ -73,7 +73,7 @@ def event_times(call, n_calls, warmup, stream):
     return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
 
-EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda")
+EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda", "policy")
 
 
 def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRAS):
@@ -174,6 +174,31 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
         out["kda"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
                       "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
                       "kernels": "kda_prep_kernel + kda_state_kernel"}
+    if "policy" in which:
+        # latency and peak device memory of one forward call per precision policy:
+        # bf16 io (bf16 MFMA operands, fp32 accumulation and state) and fp32 io (IEEE
+        # fp32 products), on the d_k = 64 / d_v = 128 training shape both support
+        w = WORKLOADS["fwdbwd_bf16"]
+        d = generate(w.with_(io="fp32"))
+        pol = {}
+        for name, io in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+            t = {key: torch.from_numpy(d[key]).to(dev).to(io) for key in ("q", "k", "v")}
+            t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+            kt = event_times(lambda i: gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale),
+                             max(5, steps // 2), 2, stream)
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            o, Sf = gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            ws = gdn.forward_workspace(t["q"], t["v"])
+            pol[name] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
+                         "workspace_bytes": 0 if ws is None else ws.numel(),
+                         "peak_call_bytes": int(peak),
+                         "input_bytes": int(sum(x.numel() * x.element_size() for x in t.values()))}
+            del t, o, Sf, ws
+        out["policy"] = {"workload": "fwdbwd_bf16 shape, forward", "by_io_dtype": pol}
     return out
 
 
