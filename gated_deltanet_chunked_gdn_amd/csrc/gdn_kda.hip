@@ -128,33 +128,41 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
-      const int64_t off = ((bos + r0 + i) * p.H + h) * DK + ch;
-      if (i < nr) {
-        kr[u] = Vec8<E>::load(k + off);
-        qr[u] = Vec8<E>::load(q + off);
-        ga[u] = *reinterpret_cast<const float4*>(p.g + off);
-        gb[u] = *reinterpret_cast<const float4*>(p.g + off + 4);
-      } else {
-        kr[u] = Vec8<E>::zero();
-        qr[u] = Vec8<E>::zero();
-        ga[u] = gb[u] = float4{0.f, 0.f, 0.f, 0.f};
-      }
+      // rows past the chunk load its last row (no branch around the loads) and
+      // are zeroed when stored below
+      const int64_t off = ((bos + r0 + (i < nr ? i : nr - 1)) * p.H + h) * DK + ch;
+      kr[u] = Vec8<E>::load(k + off);
+      qr[u] = Vec8<E>::load(q + off);
+      ga[u] = *reinterpret_cast<const float4*>(p.g + off);
+      gb[u] = *reinterpret_cast<const float4*>(p.g + off + 4);
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
+      if (i >= nr) {
+        kr[u] = Vec8<E>::zero();
+        qr[u] = Vec8<E>::zero();
+        ga[u] = gb[u] = float4{0.f, 0.f, 0.f, 0.f};
+      }
       Vec8<E>::store(ks + i * LD + ch, kr[u]);
       Vec8<E>::store(qs + i * LD + ch, qr[u]);
       *reinterpret_cast<float4*>(gs + i * LD + ch) = ga[u];
       *reinterpret_cast<float4*>(gs + i * LD + ch + 4) = gb[u];
     }
   }
-  if (tid < 64) bs[tid] = tid < nr ? p.beta[(bos + r0 + tid) * p.H + h] : 0.f;
+  if (tid < 64) {
+    const float bv = p.beta[(bos + r0 + (tid < nr ? tid : nr - 1)) * p.H + h];
+    bs[tid] = tid < nr ? bv : 0.f;
+  }
   __syncthreads();
-  if (tid < DK) {
+  if (tid < DK) {  // channel tid: its 64 values are read at once, summed in registers
+    float col[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) col[i] = gs[i * LD + tid];
     float acc = 0.f;
+#pragma unroll
     for (int i = 0; i < 64; ++i) {
-      acc += gs[i * LD + tid];
+      acc += col[i];
       gs[i * LD + tid] = acc;
     }
   }
@@ -312,7 +320,9 @@ struct StateLds {
   static constexpr int kSt = kP + 64 * L64;   // [16][LK]: S^T of the tile
   static constexpr int kRt = kSt + 16 * LK;   // [16][L64]: (V - (K o Gamma) S)^T
   static constexpr int kEt = kRt + 16 * L64;  // [16][L64]: E^T
-  static constexpr int kElems = kEt + 16 * L64;
+  static constexpr int LV = 16 + PAD;         // rows of the v tile
+  static constexpr int kVs = kEt + 16 * L64;  // [64][LV]: the chunk's v tile (io element type)
+  static constexpr int kElems = kVs + 64 * LV;
   static constexpr int kGnByte = (kElems * static_cast<int>(sizeof(EL)) + 15) / 16 * 16;
   static constexpr int kBytes = kGnByte + DK * 4;
 };
@@ -403,24 +413,56 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   // the loaders' prefetch registers and the compute waves' operands never have
   // to be allocated side by side.
   if (loader) {
+    // the chunk's v tile (64 rows x 16 columns) travels with its record: one
+    // 16-byte vector per loader lane (rows past the sequence load its last row
+    // and are zeroed; lanes past the tile load a valid row and keep nothing)
+    constexpr int VPR = 16 * static_cast<int>(sizeof(E)) / 16;  // vectors per tile row
+    constexpr int EPV = 16 / static_cast<int>(sizeof(E));
+    const int vrow = lt / VPR < 64 ? lt / VPR : 63, vcol = (lt % VPR) * EPV;
+    const bool vlane = lt < 64 * VPR;
+    auto load_vt = [&](int c) {
+      const int64_t row = 64LL * c + vrow;
+      f32x4_t x = *reinterpret_cast<const f32x4_t*>(v + ((bos + (row < len ? row : len - 1)) * p.H + h) * Dv +
+                                                    tile * 16 + vcol);
+      if (row >= len) x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      return x;
+    };
+    auto store_vt = [&](const f32x4_t& x) {
+      if (vlane) *reinterpret_cast<f32x4_t*>(sm + L::kVs + vrow * L::LV + vcol) = x;
+    };
     if constexpr (St8::NV <= 16) {
       // two records in flight: chunk c + 2 is requested as chunk c is staged
       f32x4_t pa[St8::NV], pb[St8::NV];
+      f32x4_t va = {0.f, 0.f, 0.f, 0.f}, vb2 = {0.f, 0.f, 0.f, 0.f};
       float ga = 0.f, gb = 0.f;
-      if (nch > 0) St8::load(pa, ga, rec0, lt);
-      if (nch > 1) St8::load(pb, gb, rec0 + rec_step, lt);
+      if (nch > 0) {
+        St8::load(pa, ga, rec0, lt);
+        va = load_vt(0);
+      }
+      if (nch > 1) {
+        St8::load(pb, gb, rec0 + rec_step, lt);
+        vb2 = load_vt(1);
+      }
       for (int c = 0; c < nch; c += 2) {
         __syncthreads();  // the previous chunk's reads of the staged record are done
         St8::store(pa, ga, smb, lt);
+        store_vt(va);
         __syncthreads();
-        if (c + 2 < nch) St8::load(pa, ga, rec0 + (c + 2) * rec_step, lt);
+        if (c + 2 < nch) {
+          St8::load(pa, ga, rec0 + (c + 2) * rec_step, lt);
+          va = load_vt(c + 2);
+        }
         __syncthreads();
         __syncthreads();
         if (c + 1 < nch) {
           __syncthreads();
           St8::store(pb, gb, smb, lt);
+          store_vt(vb2);
           __syncthreads();
-          if (c + 3 < nch) St8::load(pb, gb, rec0 + (c + 3) * rec_step, lt);
+          if (c + 3 < nch) {
+            St8::load(pb, gb, rec0 + (c + 3) * rec_step, lt);
+            vb2 = load_vt(c + 3);
+          }
           __syncthreads();
           __syncthreads();
         }
@@ -428,13 +470,21 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
     } else {
       // fp32 records (twice the registers): one record in flight
       f32x4_t pa[St8::NV];
+      f32x4_t va = {0.f, 0.f, 0.f, 0.f};
       float ga = 0.f;
-      if (nch > 0) St8::load(pa, ga, rec0, lt);
+      if (nch > 0) {
+        St8::load(pa, ga, rec0, lt);
+        va = load_vt(0);
+      }
       for (int c = 0; c < nch; ++c) {
         __syncthreads();
         St8::store(pa, ga, smb, lt);
+        store_vt(va);
         __syncthreads();
-        if (c + 1 < nch) St8::load(pa, ga, rec0 + (c + 1) * rec_step, lt);
+        if (c + 1 < nch) {
+          St8::load(pa, ga, rec0 + (c + 1) * rec_step, lt);
+          va = load_vt(c + 1);
+        }
         __syncthreads();
         __syncthreads();
       }
@@ -450,30 +500,22 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * (w + 4 * b) + 4 * g4 + r;
-      S[b][r] = p.S0 ? p.S0[(sbase + row) * Dv + c0] : 0.f;
-      St[col * L::LK + row] = Op::cvt(S[b][r]);
+      S[b][r] = 0.f;
+      if (p.S0) S[b][r] = p.S0[(sbase + row) * Dv + c0];
     }
   }
-  // this lane's four values of v (rows 16 w + 4 g4 + r, column c0), one chunk ahead
-  float vnext[4];
-  auto load_v = [&](int c) {
-    const int64_t r0 = 64LL * c;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * g4 + r;
-      vnext[r] = r0 + row < len ? IoT<E>::ld(v + ((bos + r0 + row) * p.H + h) * Dv + c0) : 0.f;
-    }
-  };
-  if (nch > 0) load_v(0);
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) St[col * L::LK + 16 * (w + 4 * b) + 4 * g4 + r] = Op::cvt(S[b][r]);
   for (int c = 0; c < nch; ++c) {
     const int64_t r0 = 64LL * c;
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
+    __syncthreads();
+    __syncthreads();  // the record and the v tile of chunk c are in LDS
     float vcur[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vcur[r] = vnext[r];
-    if (c + 1 < nch) load_v(c + 1);
-    __syncthreads();
-    __syncthreads();  // the record of chunk c is in LDS
+    for (int r = 0; r < 4; ++r) vcur[r] = IoT<EL>::ld(sm + L::kVs + (16 * w + 4 * g4 + r) * L::LV + col);
     // R = V - (K o Gamma) S and (Q o Gamma) S for rows 16 w .. 16 w + 15
     f32x4_t qsacc = zero4();
     {
