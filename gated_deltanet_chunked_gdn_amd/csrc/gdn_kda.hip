@@ -12,13 +12,16 @@
 //   O = scale ((Q o Gamma) S + P E)
 //   S <- diag(Gamma_n) S + (K o exp(gamma_n - gamma))^T E
 // Every exponent above is <= 0 (g <= 0, j <= i), so nothing overflows however
-// strong the decay; the per-channel factor cannot be pulled out of K K^T as a
-// rank-one mask, which is why A and P are summed channel by channel.
+// strong the decay.  The per-channel factor cannot be pulled out of K K^T as one
+// rank-one mask, but for rows i > r >= j it splits as exp(gamma_ic - gamma_rc)
+// exp(gamma_rc - gamma_jc) with both exponents <= 0.
 //
 // Two kernels, all arithmetic in fp32 (io dtype only at the loads and the o store):
 //   kda_prep_kernel  -- one workgroup per (chunk, head, sequence); writes the
 //                       chunk's record: T diag(beta), P, K o Gamma, Q o Gamma,
-//                       (K o exp(gamma_n - gamma))^T and Gamma_n.
+//                       (K o exp(gamma_n - gamma))^T and Gamma_n.  A and P below
+//                       the diagonal blocks are MFMA products of rows decayed to
+//                       a reference row between the two blocks.
 //   kda_state_kernel -- one workgroup per (sequence, head, 16 value columns);
 //                       walks the chunks in order with its state tile in fp32
 //                       MFMA accumulators (v_mfma_f32_16x16x4_f32); four of its
@@ -168,58 +171,61 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   }
   __syncthreads();
 
-  // A and P over the pairs j <= i in 2 x 2 tiles (rows i0, i0 + 1; columns j0,
-  // j0 + 1): 528 tiles on or below the diagonal; each channel quad of the four
-  // rows is read from LDS once per tile.  The pair above the diagonal of a
-  // diagonal tile is computed and dropped.
-  for (int t = tid; t < 32 * 33 / 2; t += 512) {
-    int ti = static_cast<int>((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
-    if (ti * (ti + 1) / 2 > t) --ti;
-    if ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    const int tj = t - ti * (ti + 1) / 2;
-    const int i0 = 2 * ti, j0 = 2 * tj;
-    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-    float s00 = 0.f, s01 = 0.f, s10 = 0.f, s11 = 0.f;
-#pragma unroll 2
+  // A and P.  Below the 16x16 diagonal blocks, block (bi, bj) factors through the
+  // last row r = 16 bj + 15 of block bj: exp(gamma_i - gamma_j) =
+  // exp(gamma_i - gamma_r) exp(gamma_r - gamma_j) channel by channel, both factors
+  // <= 1 (j <= r < i), so A and P there are fp32 MFMA products of decayed rows;
+  // waves 0-5 take one such block each.  The diagonal blocks (pairs j <= i inside
+  // a block) are summed pair by pair, one exponential per channel, by all threads.
+  if (wave < 6) {
+    const int bi = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;  // (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
+    const int bj = wave < 3 ? 0 : wave < 5 ? 1 : 2;
+    const int ia = 16 * bi + (lane & 15), jb = 16 * bj + (lane & 15), r = 16 * bj + 15;
+    f32x4_t accA = zero4(), accP = zero4();
+#pragma unroll 4
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+      const int ch = k0 + (lane >> 4);
+      const float gr = gs[r * LD + ch];
+      const float ei = __expf(gs[ia * LD + ch] - gr);
+      const float bk = ks[jb * LD + ch] * __expf(gr - gs[jb * LD + ch]);
+      accA = __builtin_amdgcn_mfma_f32_16x16x4f32(ks[ia * LD + ch] * ei, bk, accA, 0, 0, 0);
+      accP = __builtin_amdgcn_mfma_f32_16x16x4f32(qs[ia * LD + ch] * ei, bk, accP, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i = 16 * bi + 4 * (lane >> 4) + q4, j = 16 * bj + (lane & 15);
+      As[i * 65 + j] = bs[i] * accA[q4];
+      rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
+    }
+  }
+  for (int t = tid; t < 4 * 136; t += 512) {
+    const int b = t / 136, tl = t % 136;
+    int il = static_cast<int>((sqrtf(8.f * tl + 1.f) - 1.f) * 0.5f);
+    if (il * (il + 1) / 2 > tl) --il;
+    if ((il + 1) * (il + 2) / 2 <= tl) ++il;
+    const int i = 16 * b + il, j = 16 * b + tl - il * (il + 1) / 2;
+    const float* ki = ks + i * LD;
+    const float* kj = ks + j * LD;
+    const float* qi = qs + i * LD;
+    const float* gi = gs + i * LD;
+    const float* gj = gs + j * LD;
+    float a = 0.f, sc = 0.f;
+#pragma unroll 4
     for (int ch = 0; ch < DK; ch += 4) {
-      const f32x4_t ki0 = *reinterpret_cast<const f32x4_t*>(ks + i0 * LD + ch);
-      const f32x4_t ki1 = *reinterpret_cast<const f32x4_t*>(ks + (i0 + 1) * LD + ch);
-      const f32x4_t qi0 = *reinterpret_cast<const f32x4_t*>(qs + i0 * LD + ch);
-      const f32x4_t qi1 = *reinterpret_cast<const f32x4_t*>(qs + (i0 + 1) * LD + ch);
-      const f32x4_t gi0 = *reinterpret_cast<const f32x4_t*>(gs + i0 * LD + ch);
-      const f32x4_t gi1 = *reinterpret_cast<const f32x4_t*>(gs + (i0 + 1) * LD + ch);
-      const f32x4_t kj0 = *reinterpret_cast<const f32x4_t*>(ks + j0 * LD + ch);
-      const f32x4_t kj1 = *reinterpret_cast<const f32x4_t*>(ks + (j0 + 1) * LD + ch);
-      const f32x4_t gj0 = *reinterpret_cast<const f32x4_t*>(gs + j0 * LD + ch);
-      const f32x4_t gj1 = *reinterpret_cast<const f32x4_t*>(gs + (j0 + 1) * LD + ch);
+      const f32x4_t k4i = *reinterpret_cast<const f32x4_t*>(ki + ch);
+      const f32x4_t k4j = *reinterpret_cast<const f32x4_t*>(kj + ch);
+      const f32x4_t q4i = *reinterpret_cast<const f32x4_t*>(qi + ch);
+      const f32x4_t g4i = *reinterpret_cast<const f32x4_t*>(gi + ch);
+      const f32x4_t g4j = *reinterpret_cast<const f32x4_t*>(gj + ch);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float d00 = kj0[x] * __expf(gi0[x] - gj0[x]);
-        const float d01 = kj1[x] * __expf(gi0[x] - gj1[x]);
-        const float d10 = kj0[x] * __expf(gi1[x] - gj0[x]);
-        const float d11 = kj1[x] * __expf(gi1[x] - gj1[x]);
-        a00 = fmaf(ki0[x], d00, a00);
-        a01 = fmaf(ki0[x], d01, a01);
-        a10 = fmaf(ki1[x], d10, a10);
-        a11 = fmaf(ki1[x], d11, a11);
-        s00 = fmaf(qi0[x], d00, s00);
-        s01 = fmaf(qi0[x], d01, s01);
-        s10 = fmaf(qi1[x], d10, s10);
-        s11 = fmaf(qi1[x], d11, s11);
+        const float kd = k4j[x] * __expf(g4i[x] - g4j[x]);
+        a = fmaf(k4i[x], kd, a);
+        sc = fmaf(q4i[x], kd, sc);
       }
     }
-    const float av[2][2] = {{a00, a01}, {a10, a11}};
-    const float sv[2][2] = {{s00, s01}, {s10, s11}};
-#pragma unroll
-    for (int di = 0; di < 2; ++di)
-#pragma unroll
-      for (int dj = 0; dj < 2; ++dj) {
-        const int i = i0 + di, j = j0 + dj;
-        if (j <= i) {
-          As[i * 65 + j] = j < i ? bs[i] * av[di][dj] : 0.f;
-          rec[R::kP + i * 64 + j] = Op::cvt(sv[di][dj]);
-        }
-      }
+    As[i * 65 + j] = j < i ? bs[i] * a : 0.f;
+    rec[R::kP + i * 64 + j] = Op::cvt(sc);
   }
   for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
