@@ -198,7 +198,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
       rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
     }
   }
-  for (int t = tid; t < 4 * 136; t += 512) {
+  // waves 6-7 (no MFMA block) take pairs 0..127 and the 32 past 511
+  for (int t = tid >= 384 ? tid - 384 : tid + 128; t < 4 * 136; t += 512) {
     const int b = t / 136, tl = t % 136;
     int il = static_cast<int>((sqrtf(8.f * tl + 1.f) - 1.f) * 0.5f);
     if (il * (il + 1) / 2 > tl) --il;
@@ -353,7 +354,9 @@ struct Stager {
   static __device__ __forceinline__ void load(f32x4_t (&r)[NV], float& gn, const char* rec, int tid) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(rec + 16 * (tid + 256 * u));
-    gn = tid < DK ? reinterpret_cast<const float*>(rec + R::kGnByte)[tid] : 0.f;
+    // every lane loads (lanes past DK re-read entry 0): a branch around the load
+    // would make the wave wait for all of its loads right here
+    gn = reinterpret_cast<const float*>(rec + R::kGnByte)[tid < DK ? tid : 0];
   }
   static __device__ __forceinline__ void store(const f32x4_t (&r)[NV], float gn, char* smb, int tid) {
     EL* const sm = reinterpret_cast<EL*>(smb);
@@ -426,15 +429,16 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
     constexpr int EPV = 16 / static_cast<int>(sizeof(E));
     const int vrow = lt / VPR < 64 ? lt / VPR : 63, vcol = (lt % VPR) * EPV;
     const bool vlane = lt < 64 * VPR;
+    // (the zeroing of rows past the sequence waits for the store: a select right
+    // after the load would make the wave wait for every load issued before it)
     auto load_vt = [&](int c) {
       const int64_t row = 64LL * c + vrow;
-      f32x4_t x = *reinterpret_cast<const f32x4_t*>(v + ((bos + (row < len ? row : len - 1)) * p.H + h) * Dv +
-                                                    tile * 16 + vcol);
-      if (row >= len) x = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      return x;
+      return *reinterpret_cast<const f32x4_t*>(v + ((bos + (row < len ? row : len - 1)) * p.H + h) * Dv +
+                                               tile * 16 + vcol);
     };
-    auto store_vt = [&](const f32x4_t& x) {
-      if (vlane) *reinterpret_cast<f32x4_t*>(sm + L::kVs + vrow * L::LV + vcol) = x;
+    auto store_vt = [&](const f32x4_t& x, int c) {
+      const f32x4_t y = 64LL * c + vrow < len ? x : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (vlane) *reinterpret_cast<f32x4_t*>(sm + L::kVs + vrow * L::LV + vcol) = y;
     };
     if constexpr (St8::NV <= 16) {
       // two records in flight: chunk c + 2 is requested as chunk c is staged
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
       for (int c = 0; c < nch; c += 2) {
         __syncthreads();  // the previous chunk's reads of the staged record are done
         St8::store(pa, ga, smb, lt);
-        store_vt(va);
+        store_vt(va, c);
         __syncthreads();
         if (c + 2 < nch) {
           St8::load(pa, ga, rec0 + (c + 2) * rec_step, lt);
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
         if (c + 1 < nch) {
           __syncthreads();
           St8::store(pb, gb, smb, lt);
-          store_vt(vb2);
+          store_vt(vb2, c + 1);
           __syncthreads();
           if (c + 3 < nch) {
             St8::load(pb, gb, rec0 + (c + 3) * rec_step, lt);
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
       for (int c = 0; c < nch; ++c) {
         __syncthreads();
         St8::store(pa, ga, smb, lt);
-        store_vt(va);
+        store_vt(va, c);
         __syncthreads();
         if (c + 1 < nch) {
           St8::load(pa, ga, rec0 + (c + 1) * rec_step, lt);
