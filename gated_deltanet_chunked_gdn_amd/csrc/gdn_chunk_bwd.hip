@@ -200,23 +200,25 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   // the next step: the load latency hides behind the products.
   constexpr int NSV = 64 * (DK / EPV) / 256;  // K (and Q) vectors per thread
   constexpr int NTV = 64 * 64 / EPV / 256;    // T vectors per thread
+  // Rows past the chunk's end load its last row and are zeroed when staged: a
+  // branch around a load, or a select right after it, would make the wave wait
+  // for every load in flight at that point.
   struct Pre {
     u32x4_t kv[NSV], qv[NSV], tv[NTV];
-    float dov[4];
+    u32x4_t dor;  // four dO values of row tid / 4 (raw io elements)
     float gv, bv;
+    int nv;
   };
   auto load_pre = [&](Pre& pr, int c) {
     const int64_t c0 = static_cast<int64_t>(c) * 64, row0 = bos + c0;
     const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
+    pr.nv = nv;
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
       const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      pr.kv[i] = u32x4_t{0u, 0u, 0u, 0u};
-      pr.qv[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t < nv) {
-        pr.kv[i] = ld16(k + ((row0 + t) * H + h) * DK + cv);
-        pr.qv[i] = ld16(q + ((row0 + t) * H + h) * DK + cv);
-      }
+      const int tt = t < nv ? t : nv - 1;
+      pr.kv[i] = ld16(k + ((row0 + tt) * H + h) * DK + cv);
+      pr.qv[i] = ld16(q + ((row0 + tt) * H + h) * DK + cv);
     }
     const E* T = tws + ((slot0 + c) * H + h) * 4096;
 #pragma unroll
@@ -226,26 +228,27 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     }
     {
       const int t = tid >> 2, cq = (tid & 3) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr.dov[e] = 0.f;
-      if (t < nv) {
-        const E* src = dO + ((row0 + t) * H + h) * Dv + j0 + cq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr.dov[e] = Op::widen(src[e]);
+      const E* src = dO + ((row0 + (t < nv ? t : nv - 1)) * H + h) * Dv + j0 + cq;
+      if constexpr (sizeof(E) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src);
+        pr.dor = u32x4_t{u.x, u.y, 0u, 0u};
+      } else {
+        pr.dor = *reinterpret_cast<const u32x4_t*>(src);
       }
     }
-    {  // padded rows: g = 0, beta = 0 (every wave loads the gates)
-      const bool ok = lane < nv;
-      pr.gv = ok ? p.g[(row0 + lane) * H + h] : 0.f;
-      pr.bv = ok ? p.beta[(row0 + lane) * H + h] : 0.f;
+    {  // every wave loads the gates
+      const int ll = lane < nv ? lane : nv - 1;
+      pr.gv = p.g[(row0 + ll) * H + h];
+      pr.bv = p.beta[(row0 + ll) * H + h];
     }
   };
   auto stage_pre = [&](const Pre& pr) {
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
       const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      st16(sm.Ks + t * LDK + cv, pr.kv[i]);
-      st16(sm.Qs + t * LDK + cv, pr.qv[i]);
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      st16(sm.Ks + t * LDK + cv, t < pr.nv ? pr.kv[i] : z);
+      st16(sm.Qs + t * LDK + cv, t < pr.nv ? pr.qv[i] : z);
     }
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
@@ -253,22 +256,34 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       st16(sm.Tm + t * LDC + cv, pr.tv[i]);
     }
     // gamma by an in-register scan (log2 units), in every wave; wave 0 stores it
-    const float g2 = wave_inclusive_scan(pr.gv * kLog2e, lane);
+    // (padded rows: g = 0, beta = 0)
+    const float gv = lane < pr.nv ? pr.gv : 0.f, bv = lane < pr.nv ? pr.bv : 0.f;
+    const float g2 = wave_inclusive_scan(gv * kLog2e, lane);
     const float G = exp2f(g2);
     if (w == 0) {
       const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
       sm.gam[lane] = g2;
       sm.Gam[lane] = G;
       sm.dec[lane] = exp2f(gl2 - g2);
-      sm.bg[lane] = pr.bv * G;
+      sm.bg[lane] = bv * G;
     }
     {
       const int t = tid >> 2, cq = (tid & 3) * 4;
       const float Gt = __shfl(G, t, 64);
+      float dov[4];
+      if constexpr (sizeof(E) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dov[e] = __uint_as_float((e & 1) ? (pr.dor[e >> 1] & 0xffff0000u) : (pr.dor[e >> 1] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dov[e] = __uint_as_float(pr.dor[e]);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * pr.dov[e]);
-        sm.dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * pr.dov[e]);
+        const float x = t < pr.nv ? dov[e] : 0.f;
+        sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * x);
+        sm.dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * x);
       }
     }
   };
