@@ -1,5 +1,5 @@
-"""HIP-graph capture and replay of the chunked forward and backward passes
-(marked gpu).
+"""HIP-graph capture and replay of the chunked forward and backward passes and
+of the per-key-channel-decay forward (marked gpu).
 
 The library allocates nothing and issues no memset, so a call can be captured
 into a graph.  Each test captures one call, then replays the graph several times
@@ -99,3 +99,47 @@ def test_backward_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
             assert torch.equal(got[name], ref[name]), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_kda_forward_graph_replays_match_eager():
+    # the per-key-channel-decay forward, captured once and replayed on new inputs
+    wk = Workload("graph_kda", 2, 300, 3, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel", s0_std=0.1,
+                  scale=0.5, seed=51)
+
+    def inputs(seed):
+        return to_device(generate(Workload(**{**wk.__dict__, "seed": seed})))
+
+    t = inputs(51)
+    dev = t["q"].device
+    o = torch.empty_like(t["v"])
+    Sf = torch.empty((wk.B, wk.H, wk.Dk, wk.Dv), dtype=torch.float32, device=dev)
+    from gated_deltanet_chunked_gdn_amd import _native as nat
+    ws = torch.empty(nat.workspace_size(gdn.make_problem(t["q"], t["v"], None, 1.0, 1), nat.GDN_PASS_KDA_FWD),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"], scale=wk.scale, out=o,
+                          final_state_out=Sf, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((52, 53, 54)):
+        fresh = inputs(seed)
+        _copy_into(t, fresh)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_graph, S_graph = o.clone(), Sf.clone()
+        o_eager, S_eager = gdn.kda_chunk_fwd(fresh["q"], fresh["k"], fresh["v"], fresh["g"], fresh["beta"],
+                                             S0=fresh["S0"], scale=wk.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, o_eager), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(S_graph, S_eager), f"replay {rep}: final state differs from the eager call"
