@@ -116,12 +116,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
 
   // Every load is issued up front, through buffer resources bounded to the
   // chunk's valid rows (padded rows read as zeros): Q rows of row block pi as
-  // MFMA fragments, K rows, g and beta.
+  // MFMA fragments, K rows, g and beta.  No load sits inside a branch and every
+  // loaded value is used by every wave: a load in a branch, or one sunk into
+  // the only branch that uses it, is waited for where that branch ends.
   const int s_e = static_cast<int>(sizeof(E));
   const int rows_bytes = ((nv - 1) * H * DK + DK) * s_e;
   F qf[NKK];
-  if (want_p) {
-    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rows_bytes);
+  {
+    // without P the resource covers no bytes: the loads return zeros and read nothing
+    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, want_p ? rows_bytes : 0);
     const int t = 16 * pi + (lane & 15);
 #pragma unroll
     for (int ks = 0; ks < NKK; ++ks) {
@@ -150,17 +153,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
     const int vi = x * 256 + tid, t = vi / VPR, cc = vi % VPR;
     *reinterpret_cast<u32x4_t*>(Ks + t * LDK + cc * EPV) = kv[x];
   }
-  if (wave == 0) {
+  {
+    // every wave scans g and writes beta (identical values); wave 0 also stores the decays
     const float g2 = wave_inclusive_scan(gv, lane);  // gamma * log2(e)
     sm.gam[lane] = g2;
-    if (p.gws) {  // Gamma and the decays to the chunk end, for the state pass
+    sm.bet[lane] = bv;
+    if (wave == 0 && p.gws) {  // Gamma and the decays to the chunk end, for the state pass
       const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
       float* gr = p.gws + (slot * H + h) * 128;
       gr[lane] = exp2f(g2);
       gr[64 + lane] = exp2f(gl2 - g2);
     }
-  } else if (wave == 1) {
-    sm.bet[lane] = bv;
   }
   __syncthreads();
 
