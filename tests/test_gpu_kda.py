@@ -59,6 +59,11 @@ CASES = [
              s0_std=0.1, seed=53),
     Workload("kda_bf16_dk64_dv128", 1, 300, 4, 64, 128, io="bf16", qk="norm_both", gate="gdn_channel",
              cu_seqlens=(0, 70, 70, 300), s0_std=0.1, seed=54),
+    # a one-token sequence, one of exactly one chunk, one with a ragged tail; the widest d_v
+    Workload("kda_fp32_dk64_dv256_edges", 1, 200, 2, 64, 256, io="fp32", qk="norm_both", gate="gdn_channel",
+             cu_seqlens=(0, 1, 65, 200), s0_std=0.1, scale=0.3, seed=58),
+    Workload("kda_bf16_dk128_dv16_edges", 1, 130, 2, 128, 16, io="bf16", qk="iid", gate="gdn_channel",
+             cu_seqlens=(0, 64, 65, 130), seed=59),
 ]
 
 
