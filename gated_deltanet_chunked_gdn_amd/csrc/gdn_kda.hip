@@ -36,6 +36,7 @@ namespace gdn {
 namespace {
 
 using chunk::seq_range;
+using chunk::u32x4_t;
 
 // One (chunk slot, head) record: five matrices in the MFMA operand type EL
 // (bf16 for bf16 io, fp32 for fp32 io; element offsets below), then Gamma_n as
@@ -53,44 +54,46 @@ struct KdaRec {
   static_assert(kGnByte % 4096 == 0 && kBytes % 16 == 0, "record alignment");
 };
 
-// Eight consecutive io elements: raw load, widening store of eight floats to LDS.
-template <typename E>
-struct Vec8;
-template <>
-struct Vec8<uint16_t> {
-  using raw = uint4;
-  static __device__ __forceinline__ raw load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-  static __device__ __forceinline__ raw zero() { return uint4{0u, 0u, 0u, 0u}; }
-  static __device__ __forceinline__ void store(float* dst, const raw& u) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    float f[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f[2 * m] = __uint_as_float(w[m] << 16);
-      f[2 * m + 1] = __uint_as_float(w[m] & 0xffff0000u);
-    }
-    *reinterpret_cast<float4*>(dst) = float4{f[0], f[1], f[2], f[3]};
-    *reinterpret_cast<float4*>(dst + 4) = float4{f[4], f[5], f[6], f[7]};
-  }
+// LDS of the prep kernel (bytes): K and Q rows in the io element type, gamma in
+// fp32, A in fp32 (beta on its unused diagonal), all rows unpadded and swizzled
+// in 16-byte units so that the 16 rows an MFMA fragment reads sit in distinct
+// banks.  Once the record's K, Q and decay parts are written, the K, Q and
+// gamma rows are dead and the solve's T and block products reuse their space.  For bf16
+// io this is 80 KiB: two workgroups per CU.
+template <int DK, typename E>
+struct PrepLds {
+  static constexpr int kK = 0;                                    // E [64][DK]
+  static constexpr int kQ = kK + 64 * DK * static_cast<int>(sizeof(E));
+  static constexpr int kG = kQ + 64 * DK * static_cast<int>(sizeof(E));  // float [64][DK]
+  static constexpr int kA = kG + 64 * DK * 4;                     // float [64][64]
+  static constexpr int kBytes = kA + 64 * 64 * 4;
+  static constexpr int kT = 0;                                    // float [64][65], over K, Q, gamma
+  static constexpr int kM = kT + 64 * 65 * 4;                     // float [4][16][17]
+  static_assert(kM + 4 * 16 * 17 * 4 <= kA, "the solve's buffers must fit over K, Q and gamma");
 };
-template <>
-struct Vec8<float> {
-  struct raw {
-    float4 a, b;
-  };
-  static __device__ __forceinline__ raw load(const float* p) {
-    return raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
-  }
-  static __device__ __forceinline__ raw zero() { return raw{float4{0.f, 0.f, 0.f, 0.f}, float4{0.f, 0.f, 0.f, 0.f}}; }
-  static __device__ __forceinline__ void store(float* dst, const raw& u) {
-    *reinterpret_cast<float4*>(dst) = u.a;
-    *reinterpret_cast<float4*>(dst + 4) = u.b;
-  }
-};
+// Swizzled column of channel ch in row i: 16-byte units (EPV elements) XOR-ed
+// with the row's low bits.
+template <int DK, int EPV>
+__device__ __forceinline__ int swz(int i, int ch) {
+  return ch ^ ((EPV * (i & 15)) & (DK - 1));
+}
 
-template <int DK>
+template <int DK, typename E>
 constexpr size_t prep_smem_bytes() {
-  return (3 * 64 * (DK + 4) + 2 * 64 * 65 + 4 * 16 * 17 + 64) * sizeof(float);
+  return PrepLds<DK, E>::kBytes;
+}
+
+template <typename E>
+__device__ __forceinline__ f32x4_t ld4f(const E* p);  // four consecutive io elements, widened
+template <>
+__device__ __forceinline__ f32x4_t ld4f<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4_t ld4f<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
 }
 
 template <int DK, typename E>
@@ -98,15 +101,17 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
   using EL = typename Op::elem;
   using R = KdaRec<DK, EL>;
-  constexpr int LD = DK + 4;  // 16-byte rows: four channels per LDS read
-  extern __shared__ __align__(16) float sm[];
-  float* ks = sm;             // [64][LD] keys
-  float* qs = ks + 64 * LD;   // [64][LD] queries
-  float* gs = qs + 64 * LD;   // [64][LD] g, then gamma = cumsum(g)
-  float* As = gs + 64 * LD;   // [64][65] A (strictly lower)
-  float* Ts = As + 64 * 65;   // [64][65] T = (I + A)^-1
-  float* Ms = Ts + 64 * 65;   // [4][16][17] block products of the solve
-  float* bs = Ms + 4 * 16 * 17;  // [64] beta
+  using PL = PrepLds<DK, E>;
+  constexpr int EPV = 16 / static_cast<int>(sizeof(E));  // io elements per 16 bytes
+  extern __shared__ __align__(16) char smp[];
+  E* const ks = reinterpret_cast<E*>(smp + PL::kK);      // [64][DK] keys (swizzled)
+  E* const qs = reinterpret_cast<E*>(smp + PL::kQ);      // [64][DK] queries (swizzled)
+  float* const gs = reinterpret_cast<float*>(smp + PL::kG);  // [64][DK] g, then gamma (swizzled by 4)
+  float* const As = reinterpret_cast<float*>(smp + PL::kA);  // [64][64] A; beta_i at (i, i)
+  float* const Ts = reinterpret_cast<float*>(smp + PL::kT);  // [64][65] T = (I + A)^-1 (after the outputs)
+  float* const Ms = reinterpret_cast<float*>(smp + PL::kM);  // [4][16][17] block products of the solve
+  auto kidx = [](int i, int ch) { return i * DK + swz<DK, EPV>(i, ch); };
+  auto gidx = [](int i, int ch) { return i * DK + swz<DK, 4>(i, ch); };
   const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   int64_t bos, len;
@@ -120,53 +125,53 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
 
-  // rows past the chunk's end hold zero keys and queries and g = 0, so gamma
-  // stays at the last row's value and those rows contribute nothing.  Eight
-  // channels per load; every load of the thread is issued before the first store.
+  // Every load of the chunk is issued before the first store (eight channels per
+  // vector; native vector types).  Rows past the chunk's end load its last row
+  // (no branch around a load) and are stored as zero keys, queries and g, so
+  // gamma stays at the last row's value and those rows contribute nothing.
   {
-    constexpr int VPR = DK / 8;             // vectors per row
-    constexpr int NV = 64 * VPR / 512;      // vectors per thread
-    typename Vec8<E>::raw kr[NV], qr[NV];
-    float4 ga[NV], gb[NV];
+    constexpr int VPR = DK / 8;          // eight-channel vectors per row
+    constexpr int NV = 64 * VPR / 512;   // vectors per thread
+    constexpr int W = sizeof(E) / 2;     // 16-byte words per eight io elements
+    u32x4_t kr[NV][W], qr[NV][W], gr[NV][2];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
-      // rows past the chunk load its last row (no branch around the loads) and
-      // are zeroed when stored below
       const int64_t off = ((bos + r0 + (i < nr ? i : nr - 1)) * p.H + h) * DK + ch;
-      kr[u] = Vec8<E>::load(k + off);
-      qr[u] = Vec8<E>::load(q + off);
-      ga[u] = *reinterpret_cast<const float4*>(p.g + off);
-      gb[u] = *reinterpret_cast<const float4*>(p.g + off + 4);
+#pragma unroll
+      for (int wd = 0; wd < W; ++wd) {
+        kr[u][wd] = *reinterpret_cast<const u32x4_t*>(k + off + wd * EPV);
+        qr[u][wd] = *reinterpret_cast<const u32x4_t*>(q + off + wd * EPV);
+      }
+      gr[u][0] = *reinterpret_cast<const u32x4_t*>(p.g + off);
+      gr[u][1] = *reinterpret_cast<const u32x4_t*>(p.g + off + 4);
     }
+    const float bv = p.beta[(bos + r0 + (lane < nr ? lane : nr - 1)) * p.H + h];
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int x = tid + 512 * u, i = x / VPR, ch = 8 * (x % VPR);
-      if (i >= nr) {
-        kr[u] = Vec8<E>::zero();
-        qr[u] = Vec8<E>::zero();
-        ga[u] = gb[u] = float4{0.f, 0.f, 0.f, 0.f};
+      const bool ok = i < nr;
+#pragma unroll
+      for (int wd = 0; wd < W; ++wd) {
+        *reinterpret_cast<u32x4_t*>(ks + kidx(i, ch + wd * EPV)) = ok ? kr[u][wd] : z;
+        *reinterpret_cast<u32x4_t*>(qs + kidx(i, ch + wd * EPV)) = ok ? qr[u][wd] : z;
       }
-      Vec8<E>::store(ks + i * LD + ch, kr[u]);
-      Vec8<E>::store(qs + i * LD + ch, qr[u]);
-      *reinterpret_cast<float4*>(gs + i * LD + ch) = ga[u];
-      *reinterpret_cast<float4*>(gs + i * LD + ch + 4) = gb[u];
+      *reinterpret_cast<u32x4_t*>(gs + gidx(i, ch)) = ok ? gr[u][0] : z;
+      *reinterpret_cast<u32x4_t*>(gs + gidx(i, ch + 4)) = ok ? gr[u][1] : z;
     }
-  }
-  if (tid < 64) {
-    const float bv = p.beta[(bos + r0 + (tid < nr ? tid : nr - 1)) * p.H + h];
-    bs[tid] = tid < nr ? bv : 0.f;
+    if (tid < 64) As[tid * 64 + tid] = tid < nr ? bv : 0.f;
   }
   __syncthreads();
   if (tid < DK) {  // channel tid: its 64 values are read at once, summed in registers
     float col[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) col[i] = gs[i * LD + tid];
+    for (int i = 0; i < 64; ++i) col[i] = gs[gidx(i, tid)];
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       acc += col[i];
-      gs[i * LD + tid] = acc;
+      gs[gidx(i, tid)] = acc;
     }
   }
   __syncthreads();
@@ -185,16 +190,16 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
 #pragma unroll 4
     for (int k0 = 0; k0 < DK; k0 += 4) {
       const int ch = k0 + (lane >> 4);
-      const float gr = gs[r * LD + ch];
-      const float ei = __expf(gs[ia * LD + ch] - gr);
-      const float bk = ks[jb * LD + ch] * __expf(gr - gs[jb * LD + ch]);
-      accA = __builtin_amdgcn_mfma_f32_16x16x4f32(ks[ia * LD + ch] * ei, bk, accA, 0, 0, 0);
-      accP = __builtin_amdgcn_mfma_f32_16x16x4f32(qs[ia * LD + ch] * ei, bk, accP, 0, 0, 0);
+      const float gr = gs[gidx(r, ch)];
+      const float ei = __expf(gs[gidx(ia, ch)] - gr);
+      const float bk = IoT<E>::ld(ks + kidx(jb, ch)) * __expf(gr - gs[gidx(jb, ch)]);
+      accA = __builtin_amdgcn_mfma_f32_16x16x4f32(IoT<E>::ld(ks + kidx(ia, ch)) * ei, bk, accA, 0, 0, 0);
+      accP = __builtin_amdgcn_mfma_f32_16x16x4f32(IoT<E>::ld(qs + kidx(ia, ch)) * ei, bk, accP, 0, 0, 0);
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int i = 16 * bi + 4 * (lane >> 4) + q4, j = 16 * bj + (lane & 15);
-      As[i * 65 + j] = bs[i] * accA[q4];
+      As[i * 64 + j] = As[i * 64 + i] * accA[q4];
       rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
     }
   }
@@ -205,19 +210,14 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     if (il * (il + 1) / 2 > tl) --il;
     if ((il + 1) * (il + 2) / 2 <= tl) ++il;
     const int i = 16 * b + il, j = 16 * b + tl - il * (il + 1) / 2;
-    const float* ki = ks + i * LD;
-    const float* kj = ks + j * LD;
-    const float* qi = qs + i * LD;
-    const float* gi = gs + i * LD;
-    const float* gj = gs + j * LD;
     float a = 0.f, sc = 0.f;
 #pragma unroll 4
     for (int ch = 0; ch < DK; ch += 4) {
-      const f32x4_t k4i = *reinterpret_cast<const f32x4_t*>(ki + ch);
-      const f32x4_t k4j = *reinterpret_cast<const f32x4_t*>(kj + ch);
-      const f32x4_t q4i = *reinterpret_cast<const f32x4_t*>(qi + ch);
-      const f32x4_t g4i = *reinterpret_cast<const f32x4_t*>(gi + ch);
-      const f32x4_t g4j = *reinterpret_cast<const f32x4_t*>(gj + ch);
+      const f32x4_t k4i = ld4f<E>(ks + kidx(i, ch));
+      const f32x4_t k4j = ld4f<E>(ks + kidx(j, ch));
+      const f32x4_t q4i = ld4f<E>(qs + kidx(i, ch));
+      const f32x4_t g4i = *reinterpret_cast<const f32x4_t*>(gs + gidx(i, ch));
+      const f32x4_t g4j = *reinterpret_cast<const f32x4_t*>(gs + gidx(j, ch));
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const float kd = k4j[x] * __expf(g4i[x] - g4j[x]);
@@ -225,15 +225,35 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         sc = fmaf(q4i[x], kd, sc);
       }
     }
-    As[i * 65 + j] = j < i ? bs[i] * a : 0.f;
+    if (j < i) As[i * 64 + j] = As[i * 64 + i] * a;
     rec[R::kP + i * 64 + j] = Op::cvt(sc);
   }
   for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
     if (j > i) rec[R::kP + x] = Op::cvt(0.f);
-    if (j / 16 > i / 16) Ts[i * 65 + j] = 0.f;  // T is zero above its diagonal blocks
+  }
+
+  // the record's K o Gamma, Q o Gamma, decayed keys and Gamma_n (K, Q and gamma
+  // are dead afterwards: T and the block products take their place)
+  {
+    const int rl = nr - 1;
+    for (int x = tid; x < 64 * DK; x += 512) {
+      const int i = x / DK, ch = x % DK;
+      const float e = __expf(gs[gidx(i, ch)]);
+      rec[R::kKG + x] = Op::cvt(IoT<E>::ld(ks + kidx(i, ch)) * e);
+      rec[R::kQG + x] = Op::cvt(IoT<E>::ld(qs + kidx(i, ch)) * e);
+    }
+    for (int x = tid; x < 64 * DK; x += 512) {
+      const int ch = x / 64, i = x % 64;
+      rec[R::kKDt + x] = Op::cvt(IoT<E>::ld(ks + kidx(i, ch)) * __expf(gs[gidx(rl, ch)] - gs[gidx(i, ch)]));
+    }
+    if (tid < DK) reinterpret_cast<float*>(recb + R::kGnByte)[tid] = __expf(gs[gidx(rl, tid)]);
   }
   __syncthreads();
+  for (int x = tid; x < 64 * 64; x += 512) {
+    const int i = x / 64, j = x % 64;
+    if (j / 16 > i / 16) Ts[i * 65 + j] = 0.f;  // T is zero above its diagonal blocks
+  }
 
   // T = (I + A)^-1: the 16x16 diagonal blocks by forward substitution (wave w
   // inverts block w, one column per lane), then the blocks below, band by band:
@@ -245,7 +265,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     for (int r = 0; r < 16; ++r) {
       float acc = 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) acc = fmaf(As[(16 * b + r) * 65 + 16 * b + m], tcol[m], acc);
+      for (int m = 0; m < r; ++m) acc = fmaf(As[(16 * b + r) * 64 + 16 * b + m], tcol[m], acc);
       tcol[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
     }
 #pragma unroll
@@ -259,7 +279,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     if (act) {
       f32x4_t m = zero4();
       for (int kb = bj; kb < bi; ++kb)
-        tile_mma_f32_rowmajor<16>(m, As + 16 * bi * 65 + 16 * kb, 65, Ts + 16 * kb * 65 + 16 * bj, 65, lane);
+        tile_mma_f32_rowmajor<16>(m, As + 16 * bi * 64 + 16 * kb, 64, Ts + 16 * kb * 65 + 16 * bj, 65, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Mt[(4 * (lane >> 4) + r) * 17 + (lane & 15)] = m[r];
     }
@@ -275,20 +295,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
 
   for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
-    rec[R::kTb + x] = Op::cvt(Ts[i * 65 + j] * bs[j]);
+    rec[R::kTb + x] = Op::cvt(Ts[i * 65 + j] * As[j * 64 + j]);
   }
-  const float* gn = gs + (nr - 1) * LD;
-  for (int x = tid; x < 64 * DK; x += 512) {
-    const int i = x / DK, ch = x % DK;
-    const float e = __expf(gs[i * LD + ch]);
-    rec[R::kKG + x] = Op::cvt(ks[i * LD + ch] * e);
-    rec[R::kQG + x] = Op::cvt(qs[i * LD + ch] * e);
-  }
-  for (int x = tid; x < 64 * DK; x += 512) {
-    const int ch = x / 64, i = x % 64;
-    rec[R::kKDt + x] = Op::cvt(ks[i * LD + ch] * __expf(gn[ch] - gs[i * LD + ch]));
-  }
-  if (tid < DK) reinterpret_cast<float*>(recb + R::kGnByte)[tid] = __expf(gn[tid]);
 }
 
 // acc += A(16 x K) B(K x 16) (A row-major, B stored transposed, as tile_mma),
@@ -580,8 +588,8 @@ template <int DK, typename E>
 hipError_t launch_kda_t(const KdaParams& p, hipStream_t s) {
   using EL = typename std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>::elem;
   static_assert(StateLds<DK, EL>::kBytes <= 160 * 1024, "LDS budget exceeded");
-  static_assert(prep_smem_bytes<DK>() <= 160 * 1024, "LDS budget exceeded");
-  constexpr size_t prep_smem = prep_smem_bytes<DK>();
+  static_assert(prep_smem_bytes<DK, E>() <= 160 * 1024, "LDS budget exceeded");
+  constexpr size_t prep_smem = prep_smem_bytes<DK, E>();
   constexpr size_t state_smem = StateLds<DK, EL>::kBytes;
   auto prep = kda_prep_kernel<DK, E>;
   auto state = kda_state_kernel<DK, E>;
