@@ -348,10 +348,27 @@ def cpu_baseline(d, w, budget_s: float):
         t_total += time.perf_counter() - t0
         reps += 1
     tokens = w.B * w.T * reps
+    # one pass on a single thread as well (the oracle's parallel speed-up is printed beside it)
+    t0 = time.perf_counter()
+    oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+               S0=d["S0"], scale=d["scale"], nthreads=1)
+    t1 = time.perf_counter() - t0
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full forward pass(es) of workload {w.name} "
                       f"({w.B * w.T} tokens x {w.H} heads each), fp64 C oracle, "
-                      f"{t_total:.2f} s total"}
+                      f"{t_total:.2f} s total",
+            "single_thread_value": w.B * w.T / t1,
+            "host_cpu": _host_cpu()}
+
+
+def _host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return f"{line.split(':', 1)[1].strip()}, {os.cpu_count()} logical CPUs visible"
+    except OSError:
+        pass
+    return f"{os.cpu_count()} logical CPUs visible"
 
 
 def main():
