@@ -16,16 +16,19 @@
 // rank-one mask, but for rows i > r >= j it splits as exp(gamma_ic - gamma_rc)
 // exp(gamma_rc - gamma_jc) with both exponents <= 0.
 //
-// Two kernels, all arithmetic in fp32 (io dtype only at the loads and the o store):
+// Two kernels.  Decays, A, the inverse and the state are fp32; the chunk record
+// is stored in the io element type, so that the state pass multiplies bf16
+// operands with fp32 accumulation for bf16 io and runs IEEE fp32 products for
+// fp32 io.
 //   kda_prep_kernel  -- one workgroup per (chunk, head, sequence); writes the
 //                       chunk's record: T diag(beta), P, K o Gamma, Q o Gamma,
 //                       (K o exp(gamma_n - gamma))^T and Gamma_n.  A and P below
-//                       the diagonal blocks are MFMA products of rows decayed to
-//                       a reference row between the two blocks.
+//                       the diagonal blocks are fp32 MFMA products of rows decayed
+//                       to a reference row between the two blocks.
 //   kda_state_kernel -- one workgroup per (sequence, head, 16 value columns);
 //                       walks the chunks in order with its state tile in fp32
-//                       MFMA accumulators (v_mfma_f32_16x16x4_f32); four of its
-//                       eight waves load the next chunk's record meanwhile.
+//                       MFMA accumulators; four of its eight waves load the next
+//                       chunks' records meanwhile.
 #include <type_traits>
 
 #include "gdn_chunk_common.h"
