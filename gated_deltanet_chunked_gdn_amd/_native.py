@@ -30,6 +30,7 @@ GDN_BF16 = 1
 # gdn_gate_kind
 GDN_GATE_GDN = 0
 GDN_GATE_BOUNDED5 = 1
+GDN_GATE_GDN_CHANNEL = 2
 # gdn_pass
 GDN_PASS_CHUNK_FWD = 0
 GDN_PASS_CHUNK_BWD = 1

@@ -365,13 +365,17 @@ gdn_status gdn_prologue(const gdn_problem* p, const void* q, const void* k, cons
   Checked c;
   gdn_status st = check_problem(p, Kind::RecFwd, &c);
   if (st != GDN_OK) return st;
-  if (gate_kind != GDN_GATE_GDN && gate_kind != GDN_GATE_BOUNDED5) return GDN_ERR_UNSUPPORTED;
+  if (gate_kind != GDN_GATE_GDN && gate_kind != GDN_GATE_BOUNDED5 && gate_kind != GDN_GATE_GDN_CHANNEL)
+    return GDN_ERR_UNSUPPORTED;
   const size_t nk = c.tokens * p->H * p->Dk, ng = c.tokens * p->H;
-  const bool gdn_gate = gate_kind == GDN_GATE_GDN;
-  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {a, ng * 4, 4, true},
+  const bool chan = gate_kind == GDN_GATE_GDN_CHANNEL;
+  const bool gdn_gate = gate_kind != GDN_GATE_BOUNDED5;
+  const size_t na = chan ? nk : ng;                                      // a and g elements
+  const size_t nbias = static_cast<size_t>(p->H) * (chan ? p->Dk : 1);  // dt_bias elements
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {a, na * 4, chan ? 16u : 4u, true},
                       {b, ng * 4, 4, true}, {A_log, static_cast<size_t>(p->H) * 4, 4, gdn_gate},
-                      {dt_bias, static_cast<size_t>(p->H) * 4, 4, gdn_gate}},
-                     {{q_out, nk * c.io, 16, true}, {k_out, nk * c.io, 16, true}, {g, ng * 4, 4, true},
+                      {dt_bias, nbias * 4, chan ? 16u : 4u, gdn_gate}},
+                     {{q_out, nk * c.io, 16, true}, {k_out, nk * c.io, 16, true}, {g, na * 4, chan ? 16u : 4u, true},
                       {beta, ng * 4, 4, true}});
   if (st != GDN_OK) return st;
   if (ng == 0) return GDN_OK;

@@ -134,7 +134,8 @@ struct PrologueParams {
   float* beta;
   int64_t rows;          // B * T * H token-heads
   int32_t H;
-  int32_t gate_kind;     // 0: -exp(A_log) softplus(a + dt_bias); 1: -5 sigmoid(a)
+  int32_t gate_kind;     // 0: -exp(A_log) softplus(a + dt_bias); 1: -5 sigmoid(a);
+                         // 2: form 0 per key channel (a, g [rows][Dk], dt_bias [H][Dk])
   int32_t allow_neg;     // beta = 2 sigmoid(b)
 };
 

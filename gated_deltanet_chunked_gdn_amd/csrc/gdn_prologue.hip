@@ -6,13 +6,15 @@
 //       (normalise in FP32, then cast: fla issue #1550 page, "Proposed scope")
 //   beta  = sigmoid(b)  (x 2 with negative eigenvalues allowed)
 //   g     = -exp(A_log[h]) softplus(a + dt_bias[h])  or  -5 sigmoid(a)
-//       ("Research Sprint Day 2", "Building some intuition", the gate steps)
+//       ("Research Sprint Day 2", "Building some intuition", the gate steps),
+//       or the first form per key channel (the KDA gate layout of the cuLA
+//       issue #126 page: a, g shaped like q, dt_bias per head and channel)
 //
 // The work is HBM-bound elementwise: each row of d_k values is read by a group of
 // lanes (one 16-byte vector per lane), its sum of squares reduced across the group
 // with lane shuffles, and written back once; the first lane of each group also
-// forms the gates of its (token, head).  Rows of q and k are handled by the same
-// lanes.
+// forms the gates of its (token, head); with per-channel gates every lane forms
+// those of its channels.  Rows of q and k are handled by the same lanes.
 #include <hip/hip_runtime.h>
 
 #include "gdn_chunk_common.h"
@@ -39,10 +41,18 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   const int64_t off = (live ? th : 0) * DK + sub * EPV;
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
-  u32x4_t qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
-  if (live) {
-    qv = *reinterpret_cast<const u32x4_t*>(q + off);
-    kv = *reinterpret_cast<const u32x4_t*>(k + off);
+  // every lane loads (rows past the end re-read row 0): no branch around a load
+  const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(q + off);
+  const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(k + off);
+  const bool chan = p.gate_kind == 2;
+  f32x4_t ca[EPV / 4], cb[EPV / 4];  // per-channel gates: a and dt_bias of this lane's channels
+  if (chan) {
+    const int h0 = static_cast<int>((live ? th : 0) % p.H);
+#pragma unroll
+    for (int u = 0; u < EPV / 4; ++u) {
+      ca[u] = *reinterpret_cast<const f32x4_t*>(p.a + off + 4 * u);
+      cb[u] = *reinterpret_cast<const f32x4_t*>(p.dt_bias + h0 * DK + sub * EPV + 4 * u);
+    }
   }
   float qf[EPV], kf[EPV];
   float sq = 0.f, sk = 0.f;
@@ -80,12 +90,24 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
     }
     *reinterpret_cast<u32x4_t*>(static_cast<E*>(p.q_out) + off) = *reinterpret_cast<const u32x4_t*>(qo);
     *reinterpret_cast<u32x4_t*>(static_cast<E*>(p.k_out) + off) = *reinterpret_cast<const u32x4_t*>(ko);
+    const int h = static_cast<int>(th % p.H);
     if (sub == 0) {
-      const int h = static_cast<int>(th % p.H);
       const float bs = sigmoidf_(p.b[th]);
       p.beta[th] = p.allow_neg ? 2.f * bs : bs;
-      const float a = p.a[th];
-      p.g[th] = p.gate_kind == 0 ? -__expf(p.A_log[h]) * softplusf_(a + p.dt_bias[h]) : -5.f * sigmoidf_(a);
+      if (!chan) {
+        const float a = p.a[th];
+        p.g[th] = p.gate_kind == 0 ? -__expf(p.A_log[h]) * softplusf_(a + p.dt_bias[h]) : -5.f * sigmoidf_(a);
+      }
+    }
+    if (chan) {
+      const float ea = -__expf(p.A_log[h]);
+#pragma unroll
+      for (int u = 0; u < EPV / 4; ++u) {
+        f32x4_t gv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv[e] = ea * softplusf_(ca[u][e] + cb[u][e]);
+        *reinterpret_cast<f32x4_t*>(p.g + off + 4 * u) = gv;
+      }
     }
   }
 }

@@ -258,28 +258,33 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate: str = "gdn",
     """Fused input prologue (gdn_prologue): L2-normalised q and k (fp32 norms, one
     rounding to the io dtype), g and beta from the raw projections.  Returns
     (q, k, g, beta).  gate: "gdn" (g = -exp(A_log) softplus(a + dt_bias); A_log and
-    dt_bias of shape (H,)) or "bounded5" (g = -5 sigmoid(a))."""
+    dt_bias of shape (H,)), "bounded5" (g = -5 sigmoid(a)), or "gdn_channel" (the
+    first form per key channel, for kda_chunk_fwd: a and g shaped like q, dt_bias
+    (H, Dk))."""
     lib = nat.load()
     if q_raw.dtype not in _IO or k_raw.dtype != q_raw.dtype:
         raise TypeError("q_raw and k_raw must share the io dtype (bfloat16 or float32)")
     if q_raw.dim() != 4 or k_raw.shape != q_raw.shape or not q_raw.is_contiguous() or not k_raw.is_contiguous():
         raise ValueError("q_raw and k_raw must be contiguous (B, T, H, Dk) tensors of one shape")
     B, T, H, Dk = q_raw.shape
-    for name, t in (("a", a), ("b", b)):
-        if t.dtype != torch.float32 or tuple(t.shape) != (B, T, H) or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 (B, T, H) tensor")
-    kind = {"gdn": nat.GDN_GATE_GDN, "bounded5": nat.GDN_GATE_BOUNDED5}[gate]
-    if kind == nat.GDN_GATE_GDN:
-        for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
-            if t is None or t.dtype != torch.float32 or tuple(t.shape) != (H,) or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous float32 (H,) tensor for gate='gdn'")
+    kind = {"gdn": nat.GDN_GATE_GDN, "bounded5": nat.GDN_GATE_BOUNDED5,
+            "gdn_channel": nat.GDN_GATE_GDN_CHANNEL}[gate]
+    chan = kind == nat.GDN_GATE_GDN_CHANNEL
+    a_shape = (B, T, H, Dk) if chan else (B, T, H)
+    for name, t, shape in (("a", a, a_shape), ("b", b, (B, T, H))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 {shape} tensor")
+    if kind != nat.GDN_GATE_BOUNDED5:
+        for name, t, shape in (("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, Dk) if chan else (H,))):
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 {shape} tensor for gate='{gate}'")
     prob = nat.Problem(B=B, T=T, H=H, Dk=Dk, Dv=Dv if Dv is not None else 16, num_seqs=B,
                        cu_seqlens_host=None, cu_seqlens_dev=None, io_dtype=_IO[q_raw.dtype],
                        scale=1.0, chunk=64, num_segments=1)
     q = torch.empty_like(q_raw)
     k = torch.empty_like(k_raw)
-    g = torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device)
-    beta = torch.empty_like(g)
+    g = torch.empty(a_shape, dtype=torch.float32, device=q_raw.device)
+    beta = torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device)
     st = lib.gdn_prologue(ctypes.byref(prob), _ptr(q_raw), _ptr(k_raw), _ptr(a), _ptr(b), _ptr(A_log),
                           _ptr(dt_bias), kind, int(bool(allow_neg_eigval)), _ptr(q), _ptr(k), _ptr(g),
                           _ptr(beta), _stream(q_raw.device))

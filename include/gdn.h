@@ -199,8 +199,9 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const vo
 
 /* Gate forms of gdn_prologue. */
 typedef enum {
-  GDN_GATE_GDN = 0,      /* g = -exp(A_log[h]) * softplus(a + dt_bias[h]) */
-  GDN_GATE_BOUNDED5 = 1  /* g = -5 * sigmoid(a), in (-5, 0)               */
+  GDN_GATE_GDN = 0,         /* g = -exp(A_log[h]) * softplus(a + dt_bias[h])            */
+  GDN_GATE_BOUNDED5 = 1,    /* g = -5 * sigmoid(a), in (-5, 0)                          */
+  GDN_GATE_GDN_CHANNEL = 2  /* g[..., c] = -exp(A_log[h]) * softplus(a[..., c] + dt_bias[h, c]) */
 } gdn_gate_kind;
 
 /* Fused input prologue: the elementwise step that produces the operator's inputs
@@ -215,9 +216,15 @@ typedef enum {
  *   g     = -exp(A_log[h]) softplus(a + dt_bias[h])   (GDN_GATE_GDN: the gate
  *           formula of the Day-2 page, "Building some intuition", steps 4-5), or
  *           -5 sigmoid(a)                              (GDN_GATE_BOUNDED5: the
- *           bounded gates of the fla issue #1550 workload).
- * Shapes: q, k, q_out, k_out [B, T, H, Dk] io dtype; a, b, g, beta [B, T, H] fp32;
- * A_log, dt_bias [H] fp32 (required for GDN_GATE_GDN, ignored otherwise).
+ *           bounded gates of the fla issue #1550 workload), or the first form
+ *           channel by channel, one log-decay per key channel for
+ *           gdn_kda_chunk_fwd (GDN_GATE_GDN_CHANNEL: the gate layout of the cuLA
+ *           issue #126 page, "Minimal public reproduction", dt_bias per head and
+ *           channel).
+ * Shapes: q, k, q_out, k_out [B, T, H, Dk] io dtype; b, beta [B, T, H] fp32; a, g
+ * [B, T, H] fp32, or [B, T, H, Dk] for GDN_GATE_GDN_CHANNEL; A_log [H] fp32 and
+ * dt_bias [H] fp32, or [H, Dk] for GDN_GATE_GDN_CHANNEL (both required for the
+ * two GDN forms, ignored for GDN_GATE_BOUNDED5).
  * `problem` is the problem of the chunked call the outputs feed (only B, T, H,
  * Dk and io_dtype are used; it is validated as for gdn_recurrent_ref).  Outputs
  * must not overlap inputs (GDN_ERR_ALIAS).  No workspace.  In fp32 the results

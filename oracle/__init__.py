@@ -171,8 +171,10 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate="gdn", allow_neg
     cast); beta = sigmoid(b), doubled when negative eigenvalues are allowed (range
     (0, 2), "Research Sprint Day 2", "Building some intuition", gates); and the
     log-decay g = -exp(A_log[h]) softplus(a + dt_bias[h]) (the same page's gate
-    formula) or, for gate == "bounded5", g = -5 sigmoid(a).  Returns float64
-    arrays (q, k, g, beta) of the input shapes.
+    formula) or, for gate == "bounded5", g = -5 sigmoid(a); for gate ==
+    "gdn_channel" the first form channel by channel, a shaped like q and dt_bias
+    (H, Dk) (the KDA gate layout of the cuLA issue #126 page, "Minimal public
+    reproduction").  Returns float64 arrays (q, k, g, beta) of the input shapes.
     """
     q = _f64(q_raw)
     k = _f64(k_raw)
@@ -188,6 +190,10 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate="gdn", allow_neg
         x = a + _f64(dt_bias)
         softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
         g = -np.exp(_f64(A_log)) * softplus
+    elif gate == "gdn_channel":
+        x = a + _f64(dt_bias)                          # (..., H, Dk) + (H, Dk)
+        softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+        g = -np.exp(_f64(A_log))[:, None] * softplus
     elif gate == "bounded5":
         g = -5.0 / (1.0 + np.exp(-a))
     else:

@@ -220,6 +220,13 @@ def test_prologue_checks():
     assert prologue_call(p, q_out=FAKE + 4096) == nat.GDN_ERR_ALIAS  # q_out inside q
     assert prologue_call(problem(Dk=96)) == nat.GDN_ERR_UNSUPPORTED
     assert prologue_call(problem(io_dtype=5)) == nat.GDN_ERR_DTYPE
+    # per-channel gates: dt_bias required, a, g and dt_bias 16-byte aligned, g spans B T H Dk floats
+    ch = nat.GDN_GATE_GDN_CHANNEL
+    assert prologue_call(p, gate=ch, dt_bias=None) == nat.GDN_ERR_NULL
+    assert prologue_call(p, gate=ch, a=FAKE + (2 << 30) + 4) == nat.GDN_ERR_ALIGN
+    assert prologue_call(p, gate=nat.GDN_GATE_GDN, a=FAKE + (2 << 30) + 4) != nat.GDN_ERR_ALIGN
+    assert prologue_call(p, gate=ch, beta=FAKE + (8 << 30) + 2 * 100 * 3 * 4 * 8) == nat.GDN_ERR_ALIAS
+    assert prologue_call(p, gate=3) == nat.GDN_ERR_UNSUPPORTED
 
 
 def test_epilogue_checks():

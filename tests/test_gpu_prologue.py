@@ -72,6 +72,30 @@ def test_prologue_matches_oracle(B, T, H, Dk, io, gate, neg):
     assert (g.cpu().numpy() < 0).all()
 
 
+@pytest.mark.parametrize("B,T,H,Dk,io", [(1, 1, 1, 64, "bf16"), (2, 77, 3, 128, "bf16"), (1, 130, 2, 64, "fp32"),
+                                         (4, 4096, 8, 128, "bf16")])
+def test_channel_gate_prologue_matches_oracle(B, T, H, Dk, io):
+    # one log-decay per key channel (the KDA gate layout): a and g shaped like q, dt_bias (H, Dk)
+    q, k, _, b, A_log, _ = _raw(B, T, H, Dk, io, seed=B * 7 + T)
+    rng = np.random.default_rng(T)
+    a = rng.standard_normal((B, T, H, Dk), dtype=np.float32)
+    dt = (np.float32(0.5) * rng.standard_normal((H, Dk), dtype=np.float32)).astype(np.float32)
+    iot = torch.bfloat16 if io == "bf16" else torch.float32
+    qo, ko, g, beta = gdn.prologue(_dev(q, iot), _dev(k, iot), _dev(a), _dev(b), _dev(A_log), _dev(dt),
+                                   gate="gdn_channel")
+    torch.cuda.synchronize()
+    rq, rk, rg, rb = oracle.prologue(q, k, a, b, A_log, dt, gate="gdn_channel")
+    assert tuple(g.shape) == (B, T, H, Dk)
+    for name, got, ref in (("g", g, rg), ("beta", beta, rb)):
+        x = got.cpu().numpy().astype(np.float64)
+        r = np.max(np.abs(x - ref) / np.maximum(np.abs(ref), 1e-30))
+        report(f"prologue {io} gdn_channel {name}", max_rel=r)
+        assert r <= 1e-5, (name, r)
+    rel = 2.0 ** -8 if io == "bf16" else 4e-7
+    x = ko.float().cpu().numpy().astype(np.float64)
+    assert (np.abs(x - rk) - rel * np.abs(rk)).max() <= 1e-12
+
+
 def test_prologue_feeds_the_chunked_forward():
     B, T, H, Dk, Dv = 2, 257, 3, 128, 64
     q, k, a, b, A_log, dt = _raw(B, T, H, Dk, "bf16", seed=77)

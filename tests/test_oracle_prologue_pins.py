@@ -93,3 +93,37 @@ def test_gates_and_norms_agree_with_the_generators_float32_formulas():
     assert np.allclose(qn, workloads._normalize(q.astype(f)), rtol=0, atol=2e-7)
     g5 = oracle.prologue(q, k, a.astype(f), b, gate="bounded5")[2]
     assert np.allclose(g5, f(-5.0) * workloads._sigmoid(a.astype(f)), rtol=2e-6, atol=0)
+
+
+def test_channel_gate_closed_forms_and_reduction_to_the_head_gate():
+    # per key channel: the same closed forms channel by channel, and with a and
+    # dt_bias equal on every channel it is the head gate repeated over channels
+    A_log = np.array([0.0, 0.7, 1.5])
+    xs = np.array([0.0, math.log(math.e - 1.0), 40.0, -40.0])
+    dt = 0.25 * np.arange(3 * 8).reshape(3, 8) - 2.0            # (H, Dk)
+    a = (xs[:, None, None] - dt[None, :, :]).reshape(1, 4, 3, 8)
+    z = np.zeros((1, 4, 3, 8))
+    _, _, g, _ = oracle.prologue(z, z, a, np.zeros((1, 4, 3)), A_log, dt, gate="gdn_channel")
+    e = np.exp(A_log)[:, None]
+    assert g.shape == (1, 4, 3, 8)
+    assert np.allclose(g[0, 0], -e * math.log(2.0), rtol=1e-14)
+    assert np.allclose(g[0, 1], -e, rtol=1e-14)
+    assert np.allclose(g[0, 2], -e * 40.0, rtol=1e-14)
+    assert np.allclose(g[0, 3], -e * math.exp(-40.0), rtol=1e-12)
+    q, k, a1, b, A_log1, dt1 = _draw(seed=11, shape=(2, 5, 3, 16))
+    _, _, g_head, _ = oracle.prologue(q, k, a1, b, A_log1, dt1)
+    _, _, g_chan, _ = oracle.prologue(q, k, np.repeat(a1[..., None], 16, axis=-1), b, A_log1,
+                                      np.repeat(dt1[:, None], 16, axis=-1), gate="gdn_channel")
+    assert np.allclose(g_chan, g_head[..., None], rtol=0, atol=0)
+    # the seeded per-channel generator of the KDA workload draws the same formula in float32
+    f = np.float32
+    w = workloads.WORKLOADS["kda_bf16"].with_(B=1, T=16, H=2, Dk=8, Dv=8)
+    rng = np.random.default_rng(w.seed)
+    for _ in range(3):   # q_raw, k_raw, v, as the generator draws them
+        rng.standard_normal((1, 16, 2, 8), dtype=f)
+    a_g = rng.standard_normal((1, 16, 2, 8), dtype=f)
+    A_log_g = rng.uniform(0.0, 1.5, size=(2,)).astype(f)
+    dt_g = (f(0.5) * rng.standard_normal((2, 8), dtype=f)).astype(f)
+    g_ref = oracle.prologue(np.zeros((1, 16, 2, 8)), np.zeros((1, 16, 2, 8)), a_g, np.zeros((1, 16, 2)), A_log_g,
+                            dt_g, gate="gdn_channel")[2]
+    assert np.allclose(workloads.generate(w)["g"], g_ref, rtol=3e-6, atol=0)
