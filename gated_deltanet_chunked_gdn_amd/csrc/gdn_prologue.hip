@@ -30,7 +30,7 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf
 // softplus(x) = log(1 + exp(x)) = max(x, 0) + log1p(exp(-|x|)), without overflow
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
 
-template <typename E, int DK>
+template <typename E, int DK, bool CHAN>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   constexpr int EPV = 16 / static_cast<int>(sizeof(E));  // elements per 16-byte vector
   constexpr int LPR = DK / EPV;                          // lanes per row
@@ -44,9 +44,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   // every lane loads (rows past the end re-read row 0): no branch around a load
   const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(q + off);
   const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(k + off);
-  const bool chan = p.gate_kind == 2;
   f32x4_t ca[EPV / 4], cb[EPV / 4];  // per-channel gates: a and dt_bias of this lane's channels
-  if (chan) {
+  if constexpr (CHAN) {
     const int h0 = static_cast<int>((live ? th : 0) % p.H);
 #pragma unroll
     for (int u = 0; u < EPV / 4; ++u) {
@@ -94,12 +93,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
     if (sub == 0) {
       const float bs = sigmoidf_(p.b[th]);
       p.beta[th] = p.allow_neg ? 2.f * bs : bs;
-      if (!chan) {
+      if constexpr (!CHAN) {
         const float a = p.a[th];
         p.g[th] = p.gate_kind == 0 ? -__expf(p.A_log[h]) * softplusf_(a + p.dt_bias[h]) : -5.f * sigmoidf_(a);
       }
     }
-    if (chan) {
+    if constexpr (CHAN) {
       const float ea = -__expf(p.A_log[h]);
 #pragma unroll
       for (int u = 0; u < EPV / 4; ++u) {
@@ -118,7 +117,10 @@ hipError_t launch_t(const PrologueParams& p, hipStream_t s) {
   constexpr int RPB = 256 / LPR;
   const int64_t blocks = (p.rows + RPB - 1) / RPB;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((prologue_kernel<E, DK>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  if (p.gate_kind == 2)
+    hipLaunchKernelGGL((prologue_kernel<E, DK, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((prologue_kernel<E, DK, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
