@@ -110,3 +110,24 @@ def test_prologue_feeds_the_chunked_forward():
     es = rel_rms(Sf.cpu().numpy(), S_ref)
     report("prologue -> chunk_fwd", o_rel_rms=eo, S_rel_rms=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_channel_gate_prologue_feeds_the_kda_forward():
+    # raw projections -> per-channel-gate prologue -> gdn_kda_chunk_fwd, against the
+    # oracle run on the same (prologue-made) inputs
+    B, T, H, Dk, Dv = 2, 200, 2, 128, 64
+    q, k, _, b, A_log, _ = _raw(B, T, H, Dk, "bf16", seed=79)
+    rng = np.random.default_rng(80)
+    a = rng.standard_normal((B, T, H, Dk), dtype=np.float32)
+    dt = (np.float32(0.5) * rng.standard_normal((H, Dk), dtype=np.float32)).astype(np.float32)
+    v = round_bf16(rng.standard_normal((B, T, H, Dv), dtype=np.float32))
+    qo, ko, g, beta = gdn.prologue(_dev(q, torch.bfloat16), _dev(k, torch.bfloat16), _dev(a), _dev(b), _dev(A_log),
+                                   _dev(dt), gate="gdn_channel")
+    o, Sf = gdn.kda_chunk_fwd(qo, ko, _dev(v, torch.bfloat16), g, beta)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_fwd(qo.float().cpu().numpy(), ko.float().cpu().numpy(), v, g.cpu().numpy(),
+                                  beta.cpu().numpy())
+    eo = rel_rms(o.float().cpu().numpy(), o_ref.reshape(o.shape))
+    es = rel_rms(Sf.cpu().numpy(), S_ref)
+    report("prologue (channel gate) -> kda_chunk_fwd", o_rel_rms=eo, S_rel_rms=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
