@@ -61,12 +61,25 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on_device(t, device, name):
+    """Every pointer handed to the library must be device memory of the call's GPU:
+    a host pointer reaching a kernel is a memory fault, which the C ABI (it sees
+    plain addresses) cannot detect."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+
+
 def _check_inputs(q, k, v, g, beta):
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on a GPU device")
+        _on_device(t, q.device, name)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if q.dtype not in _IO or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -79,9 +92,10 @@ def _check_inputs(q, k, v, g, beta):
         raise ValueError("g and beta must be (B, T, H)")
 
 
-def _fp32_state(t, N, H, Dk, Dv, name):
+def _fp32_state(t, N, H, Dk, Dv, name, device):
     if t is None:
         return None
+    _on_device(t, device, name)
     if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (N, H, Dk, Dv):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {(N, H, Dk, Dv)}")
     return t
@@ -134,20 +148,24 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
     seqs = _seqlens(cu_seqlens, q.device)
     prob = make_problem(q, v, seqs, scale, num_segments)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
-    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
     if out is None:
         o = torch.empty_like(v)
     else:
+        _on_device(out, q.device, "out")
         if out.dtype != v.dtype or out.shape != v.shape or not out.is_contiguous():
             raise ValueError("out must be contiguous, shaped and typed like v")
         o = out
     if final_state_out is not None:
-        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out")
+        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out", q.device)
     elif output_final_state:
         Sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     else:
         Sf = None
     if workspace is not None:
+        _on_device(workspace, q.device, "workspace")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         ws, nws = workspace, workspace.numel() * workspace.element_size()
     else:
         ws, nws = _workspace(prob, nat.GDN_PASS_CHUNK_FWD, q.device)
@@ -165,25 +183,30 @@ def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0
     _check_inputs(q, k, v, beta, beta)
     if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
         raise ValueError("g must be a float32 tensor shaped like q (one log-decay per key channel)")
-    if not g.is_cuda or not g.is_contiguous():
+    _on_device(g, q.device, "g")
+    if not g.is_contiguous():
         raise ValueError("g must be a contiguous GPU tensor")
     seqs = _seqlens(cu_seqlens, q.device)
     prob = make_problem(q, v, seqs, scale, 1)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
-    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
     if out is None:
         o = torch.empty_like(v)
     else:
+        _on_device(out, q.device, "out")
         if out.dtype != v.dtype or out.shape != v.shape or not out.is_contiguous():
             raise ValueError("out must be contiguous, shaped and typed like v")
         o = out
     if final_state_out is not None:
-        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out")
+        Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out", q.device)
     elif output_final_state:
         Sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     else:
         Sf = None
     if workspace is not None:
+        _on_device(workspace, q.device, "workspace")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         ws, nws = workspace, workspace.numel() * workspace.element_size()
     else:
         ws, nws = _workspace(prob, nat.GDN_PASS_KDA_FWD, q.device)
@@ -198,13 +221,14 @@ def chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,
     """Chunked backward pass.  Returns dict dq, dk, dv, dg, dbeta, dS0."""
     lib = nat.load()
     _check_inputs(q, k, v, g, beta)
+    _on_device(dO, q.device, "dO")
     if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
         raise ValueError("dO must be contiguous, shaped and typed like v")
     seqs = _seqlens(cu_seqlens, q.device)
     prob = make_problem(q, v, seqs, scale, 1)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
-    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
-    dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final")
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
+    dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final", q.device)
     out = {
         "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
         "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
@@ -227,15 +251,16 @@ def recurrent_ref(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0
     seqs = _seqlens(cu_seqlens, q.device)
     prob = make_problem(q, v, seqs, scale, 1)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
-    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0")
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
     out = {"o": torch.empty_like(v),
            "S_final": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)}
     grads = dict.fromkeys(("dq", "dk", "dv", "dg", "dbeta", "dS0"))
     pass_ = nat.GDN_PASS_RECURRENT_FWD
     if dO is not None:
+        _on_device(dO, q.device, "dO")
         if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
             raise ValueError("dO must be contiguous, shaped and typed like v")
-        dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final")
+        dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final", q.device)
         grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
                  "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
                  "dS0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
@@ -262,6 +287,11 @@ def prologue(q_raw, k_raw, a, b, A_log=None, dt_bias=None, gate: str = "gdn",
     first form per key channel, for kda_chunk_fwd: a and g shaped like q, dt_bias
     (H, Dk))."""
     lib = nat.load()
+    if not isinstance(q_raw, torch.Tensor) or not q_raw.is_cuda:
+        raise ValueError("q_raw must be a GPU tensor")
+    dev = q_raw.device
+    for name, t in (("k_raw", k_raw), ("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias)):
+        _on_device(t, dev, name)
     if q_raw.dtype not in _IO or k_raw.dtype != q_raw.dtype:
         raise TypeError("q_raw and k_raw must share the io dtype (bfloat16 or float32)")
     if q_raw.dim() != 4 or k_raw.shape != q_raw.shape or not q_raw.is_contiguous() or not k_raw.is_contiguous():
@@ -297,6 +327,10 @@ def epilogue(o, z, weight=None, eps: float = 1e-6):
     per (token, head) over the last dimension.  o, z: (B, T, H, Dv) of the io dtype;
     weight: float32 (Dv,) or None (ones)."""
     lib = nat.load()
+    if not isinstance(o, torch.Tensor) or not o.is_cuda:
+        raise ValueError("o must be a GPU tensor")
+    for name, t in (("z", z), ("weight", weight)):
+        _on_device(t, o.device, name)
     if o.dtype not in _IO or z.dtype != o.dtype:
         raise TypeError("o and z must share the io dtype (bfloat16 or float32)")
     if o.dim() != 4 or z.shape != o.shape or not o.is_contiguous() or not z.is_contiguous():
