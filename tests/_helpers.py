@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 import oracle
-from oracle.compare import max_rel, rel_rms
+from oracle.compare import max_rel, rel_rms, worst_head_rel_rms
 
 
 def io_torch(io: str):
@@ -49,4 +49,5 @@ def report(name, **vals):
     print(name, " ".join(f"{k}={v:.3e}" for k, v in vals.items()), flush=True)
 
 
-__all__ = ["io_torch", "to_device", "to_np", "oracle_fwd", "truncate", "max_rel", "rel_rms", "report"]
+__all__ = ["io_torch", "to_device", "to_np", "oracle_fwd", "truncate", "max_rel", "rel_rms", "report",
+           "worst_head_rel_rms"]

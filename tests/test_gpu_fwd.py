@@ -15,7 +15,7 @@ import torch
 
 import gated_deltanet_chunked_gdn_amd as gdn
 from gated_deltanet_chunked_gdn_amd.workloads import WORKLOADS, Workload, generate
-from _helpers import max_rel, oracle_fwd, rel_rms, report, to_device, to_np
+from _helpers import max_rel, oracle_fwd, rel_rms, report, to_device, to_np, worst_head_rel_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +40,12 @@ def check_against_oracle(name, d, o, Sf):
         assert eo <= TOL_FP32 and es <= TOL_FP32
     else:
         eo, es = rel_rms(o, o_ref), rel_rms(Sf, S_ref)
-        report(name, o_rel_rms=eo, S_rel_rms=es)
+        # the worst (sequence, head): a whole-tensor value can hide one bad head
+        ho = worst_head_rel_rms(o, o_ref, cu_seqlens=d["cu_seqlens"])
+        hs = worst_head_rel_rms(Sf, S_ref, token_major=False)
+        report(name, o_rel_rms=eo, S_rel_rms=es, o_worst_head=ho, S_worst_head=hs)
         assert eo <= TOL_BF16 and es <= TOL_BF16
+        assert ho <= TOL_BF16 and hs <= TOL_BF16
     return o_ref, S_ref
 
 

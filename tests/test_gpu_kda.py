@@ -6,7 +6,7 @@ rel_rms <= 8e-3 for bf16 io -- the bars of the scalar-gate path.  Cases: both io
 dtypes and head sizes, ragged tails, packed sequences with an empty one, an
 initial state, strong and slow per-channel decay, equal decays on every channel
 (the scalar-gate recurrence), run-to-run determinism, and the 4 x 4096 x 8 x 128
-training shape in the launch configuration bench.py times (sampled heads).
+training shape in the launch configuration bench.py times (every head).
 """
 import numpy as np
 import pytest
@@ -15,7 +15,7 @@ import torch
 import gated_deltanet_chunked_gdn_amd as gdn
 import oracle
 from gated_deltanet_chunked_gdn_amd.workloads import WORKLOADS, Workload, generate
-from oracle.compare import max_rel, rel_rms
+from oracle.compare import max_rel, rel_rms, worst_head_rel_rms
 from _helpers import to_device, to_np
 
 pytestmark = pytest.mark.gpu
@@ -107,9 +107,9 @@ def test_kda_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_kda_training_shape_sampled_heads():
+def test_kda_training_shape_every_head():
     # the 4 x 4096 x 8 x 128 bf16 shape with per-channel gates, as bench.py runs it;
-    # the oracle recomputes three (sequence, head) pairs in full
+    # the oracle recomputes all 32 (sequence, head) pairs in full (about 10 s)
     w = WORKLOADS["kda_bf16"]
     d = generate(w)
     t = to_device(d)
@@ -117,11 +117,11 @@ def test_kda_training_shape_sampled_heads():
     torch.cuda.synchronize()
     o, Sf = to_np(o), to_np(Sf)
     assert np.isfinite(o).all() and np.isfinite(Sf).all()
-    for b, h in ((0, 0), (1, 5), (3, 7)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        o_ref, Sf_ref = oracle.kda_fwd(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["beta"][sl],
-                                       scale=w.scale)
-        eo = rel_rms(o[sl], o_ref)
-        es = rel_rms(Sf[b, h], Sf_ref[0, 0])
-        print(f"kda_bf16 (b={b}, h={h}): rel_rms o {eo:.2e} S_final {es:.2e}")
-        assert eo <= BF16_TOL and es <= BF16_TOL
+    o_ref, Sf_ref = oracle.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=w.scale)
+    o_ref = o_ref.reshape(o.shape)
+    eo, es = rel_rms(o, o_ref), rel_rms(Sf, Sf_ref)
+    ho = worst_head_rel_rms(o, o_ref)
+    hs = worst_head_rel_rms(Sf, Sf_ref, token_major=False)
+    print(f"kda_bf16: rel_rms o {eo:.2e} S_final {es:.2e}; worst head o {ho:.2e} S_final {hs:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+    assert ho <= BF16_TOL and hs <= BF16_TOL

@@ -19,7 +19,7 @@ import torch
 
 import gated_deltanet_chunked_gdn_amd as gdn
 from gated_deltanet_chunked_gdn_amd.workloads import WORKLOADS, Workload, generate
-from _helpers import max_rel, oracle_fwd, rel_rms, report, to_device, to_np
+from _helpers import max_rel, oracle_fwd, rel_rms, report, to_device, to_np, worst_head_rel_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +106,51 @@ def test_segments_deterministic_and_empty():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     # an empty sequence passes S0 through to its final state
     assert np.array_equal(a[1][0], d["S0"][0]) and np.array_equal(a[1][2], d["S0"][2])
+
+
+@pytest.fixture(scope="module")
+def weak_write_case():
+    """The regime the cuLA issue #126 page blames ("Hypothesis"): slow decay and
+    weak writes, so the segment maps M are close to non-contracting.  65536
+    tokens, two heads with log-decays -1e-4 and -1e-3 per token, beta uniform in
+    [0.02, 0.05)."""
+    w = Workload("weak_write", 1, 65536, 2, 128, 128, io="bf16", qk="iid", gate="const",
+                 gate_const=-1e-3, seed=41)
+    d = generate(w)
+    d["g"][..., 0] = np.float32(-1e-4)
+    rng = np.random.default_rng(4141)
+    d["beta"] = (0.02 + 0.03 * rng.random(d["beta"].shape)).astype(np.float32)
+    o_ref, S_ref = oracle_fwd(d)
+    o1, S1 = run(d, 1)
+    return d, o_ref, S_ref, o1, S1
+
+
+def _worst_head_windows(o, ref):
+    """Per 8192-token window, the largest rel-L2 over the heads."""
+    return [max(rel_rms(o[:, 8192 * w:8192 * (w + 1), h], ref[:, 8192 * w:8192 * (w + 1), h])
+                for h in range(o.shape[2])) for w in range(o.shape[1] // 8192)]
+
+
+def test_weak_write_serial_reference(weak_write_case):
+    d, o_ref, S_ref, o1, S1 = weak_write_case
+    win = _worst_head_windows(o1, o_ref)
+    eS = worst_head_rel_rms(S1, S_ref, token_major=False)
+    report("weak_write G=1", o_worst_head=worst_head_rel_rms(o1, o_ref), S_worst_head=eS,
+           worst_window=max(win))
+    assert max(win) <= TOL_BF16 and eS <= TOL_BF16
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_weak_write_segments_per_window_and_head(weak_write_case, G):
+    d, o_ref, S_ref, o1, S1 = weak_write_case
+    o, Sf = run(d, G)
+    win = _worst_head_windows(o, o_ref)
+    win_vs_serial = _worst_head_windows(o, o1)
+    eS = worst_head_rel_rms(Sf, S_ref, token_major=False)
+    eS1 = worst_head_rel_rms(Sf, S1, token_major=False)
+    report(f"weak_write G={G}", S_worst_head=eS, S_vs_serial=eS1, worst_window=max(win),
+           worst_window_vs_serial=max(win_vs_serial))
+    for w, (e, e1) in enumerate(zip(win, win_vs_serial)):
+        report(f"  window {w}", rel_l2_worst_head=e, vs_serial=e1)
+    assert max(win) <= TOL_BF16 and eS <= TOL_BF16
+    assert max(win_vs_serial) <= TOL_BF16 and eS1 <= TOL_BF16
