@@ -24,6 +24,9 @@ GDN_ERR_ALIAS = 6
 GDN_ERR_HIP = 7
 GDN_ERR_SEQLENS = 8
 GDN_ERR_ALIGN = 9
+GDN_ERR_SCRATCH = 10
+# bytes of the device array gdn_chunk_fwd_noalloc uses as its workspace
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 # gdn_dtype
 GDN_FP32 = 0
 GDN_BF16 = 1
@@ -41,7 +44,7 @@ GDN_PASS_KDA_FWD = 4
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
             "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue",
-            "gdn_kda_chunk_fwd")
+            "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -102,6 +105,8 @@ def load():
     lib.gdn_epilogue.restype = ctypes.c_int
     lib.gdn_kda_chunk_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.gdn_kda_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -174,6 +174,26 @@ gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_
 
 }  // namespace
 
+namespace gdn {
+
+gdn_status check_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* S0, const void* o, const float* S_final,
+                           size_t* ws_need) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::ChunkFwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false}});
+  if (st != GDN_OK) return st;
+  *ws_need = workspace_bytes(p, Kind::ChunkFwd, c);
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
 extern "C" {
 
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
@@ -190,6 +210,7 @@ const char* gdn_status_str(int32_t s) {
     case GDN_ERR_HIP: return "HIP launch failed";
     case GDN_ERR_SEQLENS: return "cu_seqlens not a non-decreasing 0..T sequence";
     case GDN_ERR_ALIGN: return "tensor pointer misaligned";
+    case GDN_ERR_SCRATCH: return "problem needs more workspace than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

@@ -4,7 +4,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
+
+// gdn_chunk_fwd's host checks of the problem and of every tensor except the
+// workspace (include/gdn.h); on success *ws_need is the workspace it needs.
+gdn_status check_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* S0, const void* o, const float* S_final,
+                           size_t* ws_need);
 
 // Sequence n covers packed rows [bos, bos + len): from cu (device) when given,
 // else the dense batch row n * T .. n * T + T.

@@ -175,6 +175,32 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
     return o, Sf
 
 
+def chunk_fwd_noalloc(q, k, v, g, beta, out, final_state_out=None, S0=None, cu_seqlens=None,
+                      scale: float = 1.0, num_segments: int = 1):
+    """gdn_chunk_fwd_noalloc: chunk_fwd with the library's fixed device workspace.
+
+    The caller passes every output (``out`` shaped like v; ``final_state_out``
+    (N, H, Dk, Dv) fp32 or None) and the call allocates nothing, so it can run
+    where allocation is not allowed (e.g. under HIP graph capture).  Calls on one
+    device share the workspace: do not let two of them run concurrently.  With
+    ``cu_seqlens``, pass a SeqLens built beforehand (building one allocates)."""
+    lib = nat.load()
+    _check_inputs(q, k, v, g, beta)
+    if cu_seqlens is not None and not isinstance(cu_seqlens, SeqLens):
+        raise TypeError("chunk_fwd_noalloc takes cu_seqlens as a prebuilt SeqLens")
+    prob = make_problem(q, v, cu_seqlens, scale, num_segments)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
+    _on_device(out, q.device, "out")
+    if out is None or out.dtype != v.dtype or out.shape != v.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous, shaped and typed like v")
+    Sf = _fp32_state(final_state_out, N, H, Dk, Dv, "final_state_out", q.device)
+    st = lib.gdn_chunk_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(S0), _ptr(out), _ptr(Sf), _stream(q.device))
+    nat.check(st, "gdn_chunk_fwd_noalloc")
+    return out, Sf
+
+
 def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
                   output_final_state: bool = True, out=None, final_state_out=None, workspace=None):
     """Chunked forward pass with one log-decay per key channel: g is fp32 and

@@ -44,7 +44,9 @@
  *    allow_neg_eigval), k rows L2-normalised.  NaN and Inf propagate.
  *  - Ownership: the caller allocates every buffer, including the workspace
  *    sized by gdn_workspace_size.  The library allocates nothing, keeps no state
- *    between calls and never synchronises the host.
+ *    between calls and never synchronises the host -- except
+ *    gdn_chunk_fwd_noalloc, whose workspace is a fixed device array the library
+ *    holds (see there).
  *  - Execution: asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Outputs are always overwritten, never accumulated.
  *  - Errors: every shape, pointer, dtype, support and workspace check happens on
@@ -84,8 +86,10 @@ typedef enum gdn_status {
   GDN_ERR_ALIAS = 6,       /* an output overlaps an input or another output            */
   GDN_ERR_HIP = 7,         /* a HIP launch failed                                      */
   GDN_ERR_SEQLENS = 8,     /* cu_seqlens not 0 = cu[0] <= cu[1] <= ... <= cu[N] = T     */
-  GDN_ERR_ALIGN = 9        /* q, k, v, o, dO, dq, dk, dv not 16-byte aligned, or an fp32
+  GDN_ERR_ALIGN = 9,       /* q, k, v, o, dO, dq, dk, dv not 16-byte aligned, or an fp32
                               tensor not 4-byte aligned                                 */
+  GDN_ERR_SCRATCH = 10     /* gdn_chunk_fwd_noalloc: the problem needs more workspace than
+                              GDN_NOALLOC_SCRATCH_BYTES                                 */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_FP32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -145,6 +149,31 @@ gdn_status gdn_chunk_fwd(const gdn_problem* problem, const void* q, const void* 
                          const void* v, const float* g, const float* beta, const float* S0,
                          void* o, float* S_final, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* Size of the device array that gdn_chunk_fwd_noalloc uses as its workspace
+ * (64 MiB: the bf16 forward of 4 x 4096 tokens x 8 heads at Dk = Dv = 128 needs
+ * about 30 MiB). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_chunk_fwd without a caller-provided workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid allocation).  Same arguments, results and kernels as
+ * gdn_chunk_fwd; the workspace is a file-scope device array of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  The call allocates nothing: the array's device
+ * address is looked up once per device (on the first call with that device
+ * current; the current device must be the one `stream` belongs to).
+ *   Errors: as gdn_chunk_fwd, plus GDN_ERR_SCRATCH (before any launch) when
+ *   gdn_workspace_size(problem, GDN_PASS_CHUNK_FWD) exceeds the array, and
+ *   GDN_ERR_HIP if the address lookup fails.
+ *   Concurrency: every call on one device shares that device's array, which
+ *   keeps the last call's contents (nothing in it has to start at zero).  Calls
+ *   whose executions overlap on one device -- different streams, or different
+ *   host threads -- race on the array and give undefined results; serialise
+ *   them (one stream, or events). */
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* problem, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, const float* S0,
+                                 void* o, float* S_final, void* stream);
 
 /* Backward pass of the chunked gated delta rule: gradients of
  *   L = <o, dO> + <S_final, dS_final>

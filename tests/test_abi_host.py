@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.gdn_abi_version() == 1
-    for s in range(10):
+    for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
 
@@ -269,4 +269,30 @@ def test_kda_workspace_and_checks():
     # g spans B T H Dk floats: an output starting inside that range aliases it
     assert call(problem(), o=FAKE + (3 << 30) + 2 * 100 * 3 * 128 * 4 - 16) == nat.GDN_ERR_ALIAS
     assert call(problem(num_segments=4)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
+
+
+def test_noalloc_entry_checks_before_any_launch():
+    """gdn_chunk_fwd_noalloc validates like gdn_chunk_fwd and rejects problems whose
+    workspace exceeds its fixed device array, all before touching a device."""
+    P = ctypes.c_void_p
+    lib = nat.load()
+
+    def call(p, q=FAKE, o=FAKE + (5 << 30)):
+        return lib.gdn_chunk_fwd_noalloc(ctypes.byref(p), P(q), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)),
+                                         P(FAKE + (3 << 30)), P(FAKE + (4 << 30)), None, P(o), None, None)
+
+    # 32 x 1024 tokens x 16 heads at Dk = 64, Dv = 128 needs ~126 MiB of workspace
+    big = problem(B=32, T=1024, H=16, Dk=64, Dv=128, num_seqs=32)
+    st, n = ws(big)
+    assert st == nat.GDN_OK and n > nat.GDN_NOALLOC_SCRATCH_BYTES
+    assert call(big) == nat.GDN_ERR_SCRATCH
+    assert "no-allocation" in lib.gdn_status_str(nat.GDN_ERR_SCRATCH).decode()
+    # the training shape fits
+    st, n = ws(problem(B=4, T=4096, H=8, num_seqs=4))
+    assert st == nat.GDN_OK and 0 < n <= nat.GDN_NOALLOC_SCRATCH_BYTES
+    # ordinary validation comes first
+    assert call(problem(Dk=96)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(), q=None) == nat.GDN_ERR_NULL
+    assert call(problem(num_segments=3)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
