@@ -73,14 +73,17 @@ def event_times(call, n_calls, warmup, stream):
     return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
 
-EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda", "policy")
+EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda", "kda_segment_split", "policy")
 
 
 def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRAS):
     """The other passes, reported beside the headline forward number (not in it):
     backward of the training shape, the segment split of the long sequence, the
-    input prologue and output epilogue, and the per-key-channel-decay forward."""
+    input prologue and output epilogue, and the per-key-channel-decay forward
+    (serial and with the segment split)."""
     import torch
+
+    from gated_deltanet_chunked_gdn_amd import _native as nat
 
     out = {}
     stream = torch.cuda.current_stream(dev)
@@ -124,6 +127,26 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
             kt = event_times(fwd, max(5, steps // 4), 2, stream)
             seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
         out["segment_split"] = {"workload": w.name, "by_num_segments": seg}
+    if "kda_segment_split" in which:
+        # per-key-channel decay, segment split, B=1 T=65536 H=1 d=128 (slow per-channel decay)
+        w = WORKLOADS["kda_long_bf16"]
+        d = generate(w)
+        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+        seg = {}
+        for G in (1, 2, 4, 8, 16):
+            prob = gdn.make_problem(t["q"], t["v"], None, 1.0, G)
+            ws = torch.empty(nat.workspace_size(prob, nat.GDN_PASS_KDA_FWD), dtype=torch.uint8, device=dev)
+            o = torch.empty_like(t["v"])
+            Sf = torch.empty((1, 1, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+            def fwd(i, G=G, ws=ws, o=o, Sf=Sf):
+                gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=d["scale"], num_segments=G,
+                                  out=o, final_state_out=Sf, workspace=ws)
+
+            kt = event_times(fwd, max(5, steps // 4), 2, stream)
+            seg[str(G)] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.T / float(kt.mean())}
+        out["kda_segment_split"] = {"workload": w.name, "by_num_segments": seg}
     if "prologue" in which:
         # fused input prologue (normalised q, k; g; beta) on the training shape
         w = WORKLOADS["train_bf16"]

@@ -59,8 +59,11 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
     if (static_cast<int64_t>(64) * p->H * p->Dv * 4 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   }
   if (kind == Kind::KdaFwd) {
-    if (p->num_segments != 1) return GDN_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(p->num_seqs) * p->H * (p->Dv / 16) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    const int G = p->num_segments;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
+    // one state-kernel launch has up to G * N * H * (max(Dk, Dv) / 16) blocks
+    if (static_cast<int64_t>(G) * p->num_seqs * p->H * (std::max(p->Dk, p->Dv) / 16) > INT32_MAX)
+      return GDN_ERR_UNSUPPORTED;
   }
   if (kind == Kind::RecBwd && static_cast<size_t>(2) * p->Dk * (p->Dv + 1) * 4 +
                                       (2 * gdn::kRecBlock * p->Dk + 2 * gdn::kRecBlock + 8) * 4 >
@@ -114,6 +117,11 @@ size_t state_slot_bytes(const gdn_problem* p, const Checked& c) {
   return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * sizeof(float);
 }
 
+size_t kda_rec_region(const gdn_problem* p, const Checked& c) {
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda_rec_bytes(p->Dk, c.bf16);
+  return (b + 255) / 256 * 256;
+}
+
 size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::RecBwd)
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
@@ -128,7 +136,9 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   }
   if (kind == Kind::KdaFwd) {
     if (c.N == 0) return 0;
-    return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda_rec_bytes(p->Dk, c.bf16);
+    // one record per (chunk slot, head), then (num_segments > 1) the fp32 segment
+    // end states, start states and maps
+    return kda_rec_region(p, c) + gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
@@ -289,6 +299,8 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
   kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
   kp.scale = p->scale;
+  kp.G = p->num_segments;
+  kp.seg_ws = kp.G > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kda_rec_region(p, c)) : nullptr;
   return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 

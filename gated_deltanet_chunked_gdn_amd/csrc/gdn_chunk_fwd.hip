@@ -857,6 +857,18 @@ hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStr
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_segment_carry(const float* ends, const float* maps, float* starts, int G, int N, int H, int Dk,
+                                int Dv, hipStream_t s) {
+  CarryParams c{ends, maps, starts, G, N, H, Dk, Dv};
+  if (Dk == 128)
+    hipLaunchKernelGGL(seg_carry_kernel<128>, dim3(N * H * (Dv / 16)), dim3(256), 0, s, c);
+  else if (Dk == 64)
+    hipLaunchKernelGGL(seg_carry_kernel<64>, dim3(N * H * (Dv / 16)), dim3(256), 0, s, c);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
   if (bf16) {
     if (Dk == 64) return launch_fwd_t<64, OpBf16>(p, s);

@@ -194,6 +194,18 @@ struct KdaParams {
   int32_t N, H, Dv;
   int32_t max_chunks;
   float scale;
+  // Segment split, as FwdParams: segment sigma covers chunks [sigma L, min((sigma +
+  // 1) L, nch)), L = ceil(nch / G); one launch covers segments seg_base ..
+  // seg_base + nseg - 1.
+  int32_t G, seg_base, nseg;
+  int32_t start_mode;       // kStartS0 / kStartZero / kStartIdentity / kStartCarry
+  int32_t write_o;          // kOutNone / kOutAll / kOutSeg0
+  int32_t zero_u;           // V = 0: propagate transition maps instead of states
+  int32_t ncol;             // state columns: Dv, or Dk for transition maps
+  const float* carry;       // [G][N][H][Dk][ncol] start states (kStartCarry)
+  float* seg_out;           // [G][N][H][Dk][ncol] end states, or nullptr
+  int32_t final_to_sfinal;  // segment G - 1 writes S_final
+  float* seg_ws;            // G > 1: end states, start states, maps (segment_ws_bytes)
 };
 // Per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma, Q o Gamma
 // and (K o exp(gamma_n - gamma))^T (64 x Dk each) in the io element type (the
@@ -202,6 +214,12 @@ inline size_t kda_rec_bytes(int Dk, bool bf16) {
   return (8192 + 3 * 64 * static_cast<size_t>(Dk)) * (bf16 ? 2 : 4) + 4 * static_cast<size_t>(Dk);
 }
 hipError_t launch_kda_fwd(const KdaParams& p, int Dk, bool bf16, hipStream_t s);
+// Start states of segments 1 .. G - 1 composed in fp32 from the segments' end
+// states b (ends, from zero; segment 0 from S0) and transition maps M (maps):
+// starts[s + 1] = M_s starts[s] + b_s, starts[1] = ends[0].  Layouts [G][N][H][Dk][Dv]
+// and [G][N][H][Dk][Dk].
+hipError_t launch_segment_carry(const float* ends, const float* maps, float* starts, int G, int N, int H, int Dk,
+                                int Dv, hipStream_t s);
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len);
 
 }  // namespace gdn

@@ -411,14 +411,20 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   const bool loader = tid >= 256;
   const int lt = tid - 256;
   const int col = lane & 15, g4 = lane >> 4;
-  const int ntile = p.Dv / 16;
-  const int nb = p.N * p.H * ntile;
+  const int NC = p.ncol, ntile = NC / 16;
+  const int nb = gridDim.x;
   const int Lb = blockIdx.x;
   const int vb = (nb % 8 == 0) ? (Lb % 8) * (nb / 8) + Lb / 8 : Lb;  // tiles of a head share an XCD
-  const int tile = vb % ntile, nh = vb / ntile, h = nh % p.H, n = nh / p.H;
+  const int tile = vb % ntile, nh = (vb / ntile) % (p.N * p.H), h = nh % p.H, n = nh / p.H;
+  const int seg = p.seg_base + vb / ntile / (p.N * p.H);
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
-  const int nch = static_cast<int>((len + 63) / 64);
+  // this workgroup's segment: chunks [cb, cb + nch) of the sequence
+  const int nch_all = static_cast<int>((len + 63) / 64);
+  const int seg_len = (nch_all + p.G - 1) / p.G;
+  const int cb = min(seg * seg_len, nch_all);
+  const int nch = min(cb + seg_len, nch_all) - cb;
+  const bool store_o = p.write_o == kOutAll || (p.write_o == kOutSeg0 && seg == 0);
   const int Dv = p.Dv;
   const int c0 = tile * 16 + col;
   const E* v = static_cast<const E*>(p.v);
@@ -426,7 +432,8 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   EL* St = sm + L::kSt;
   EL* Rt = sm + L::kRt;
   EL* Et = sm + L::kEt;
-  const char* rec0 = static_cast<const char*>(p.ws) + ((bos / 64 + n) * p.H + h) * static_cast<int64_t>(R::kBytes);
+  const char* rec0 =
+      static_cast<const char*>(p.ws) + ((bos / 64 + n + cb) * p.H + h) * static_cast<int64_t>(R::kBytes);
   const int64_t rec_step = static_cast<int64_t>(p.H) * R::kBytes;  // next chunk slot, same head
 
   // The two roles run separate loops with the same four barriers per chunk, so
@@ -434,22 +441,23 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   // to be allocated side by side.
   if (loader) {
     // the chunk's v tile (64 rows x 16 columns) travels with its record: one
-    // 16-byte vector per loader lane (rows past the sequence load its last row
-    // and are zeroed; lanes past the tile load a valid row and keep nothing)
+    // 16-byte vector per loader lane, through a buffer resource bounded to the
+    // chunk's valid rows (rows past the sequence, and every row of a pass without
+    // V, read as zeros; lanes past the tile load row 63 again and keep nothing)
     constexpr int VPR = 16 * static_cast<int>(sizeof(E)) / 16;  // vectors per tile row
     constexpr int EPV = 16 / static_cast<int>(sizeof(E));
     const int vrow = lt / VPR < 64 ? lt / VPR : 63, vcol = (lt % VPR) * EPV;
     const bool vlane = lt < 64 * VPR;
-    // (the zeroing of rows past the sequence waits for the store: a select right
-    // after the load would make the wave wait for every load issued before it)
     auto load_vt = [&](int c) {
-      const int64_t row = 64LL * c + vrow;
-      return *reinterpret_cast<const f32x4_t*>(v + ((bos + (row < len ? row : len - 1)) * p.H + h) * Dv +
-                                               tile * 16 + vcol);
+      const int64_t r0 = 64LL * (cb + c);
+      const int nv = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
+      const auto rv = chunk::buffer_rsrc(v + ((bos + r0) * p.H + h) * Dv + tile * 16,
+                                  p.zero_u ? 0 : static_cast<int>(((nv - 1) * p.H * Dv + 16) * sizeof(E)));
+      return __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (vrow * p.H * Dv + vcol) * static_cast<int>(sizeof(E)), 0, 0));
     };
-    auto store_vt = [&](const f32x4_t& x, int c) {
-      const f32x4_t y = 64LL * c + vrow < len ? x : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (vlane) *reinterpret_cast<f32x4_t*>(sm + L::kVs + vrow * L::LV + vcol) = y;
+    auto store_vt = [&](const f32x4_t& x, int) {
+      if (vlane) *reinterpret_cast<f32x4_t*>(sm + L::kVs + vrow * L::LV + vcol) = x;
     };
     if constexpr (St8::NV <= 16) {
       // two records in flight: chunk c + 2 is requested as chunk c is staged
@@ -516,13 +524,20 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   // compute waves: state rows 16 rb + 4 g4 + r, rb = w + 4 b, in accumulators
   f32x4_t S[RB];
   const int64_t sbase = (static_cast<int64_t>(n) * p.H + h) * DK;
+  const int64_t segS = (static_cast<int64_t>(seg) * p.N * p.H + nh) * DK;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * (w + 4 * b) + 4 * g4 + r;
-      S[b][r] = 0.f;
-      if (p.S0) S[b][r] = p.S0[(sbase + row) * Dv + c0];
+      float x = 0.f;
+      if (p.start_mode == kStartCarry)
+        x = p.carry[(segS + row) * NC + c0];
+      else if (p.start_mode == kStartIdentity)
+        x = row == c0 ? 1.f : 0.f;
+      else if (p.start_mode == kStartS0 && seg == 0 && p.S0)
+        x = p.S0[(sbase + row) * Dv + c0];
+      S[b][r] = x;
     }
   }
 #pragma unroll
@@ -530,7 +545,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) St[col * L::LK + 16 * (w + 4 * b) + 4 * g4 + r] = Op::cvt(S[b][r]);
   for (int c = 0; c < nch; ++c) {
-    const int64_t r0 = 64LL * c;
+    const int64_t r0 = 64LL * (cb + c);
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
     __syncthreads();
     __syncthreads();  // the record and the v tile of chunk c are in LDS
@@ -560,7 +575,7 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * w + 4 * g4 + r;
-      if (row < nr) IoT<E>::st(o + ((bos + r0 + row) * p.H + h) * Dv + c0, p.scale * qsacc[r]);
+      if (store_o && row < nr) IoT<E>::st(o + ((bos + r0 + row) * p.H + h) * Dv + c0, p.scale * qsacc[r]);
     }
     // S <- diag(Gamma_n) S + (K o exp(gamma_n - gamma))^T E
 #pragma unroll
@@ -578,12 +593,18 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
       for (int r = 0; r < 4; ++r) St[col * L::LK + 16 * (w + 4 * b) + 4 * g4 + r] = Op::cvt(S[b][r]);
   }
 
-  if (p.S_final) {
+  const bool to_final = p.final_to_sfinal && seg == p.G - 1;
+  if (to_final ? p.S_final != nullptr : p.seg_out != nullptr) {
 #pragma unroll
     for (int b = 0; b < RB; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        p.S_final[(sbase + 16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] = S[b][r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (w + 4 * b) + 4 * g4 + r;
+        if (to_final)
+          p.S_final[(sbase + row) * Dv + c0] = S[b][r];
+        else
+          p.seg_out[(segS + row) * NC + c0] = S[b][r];
+      }
   }
 }
 
@@ -607,8 +628,40 @@ hipError_t launch_kda_t(const KdaParams& p, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(p.N * p.H * (p.Dv / 16)), dim3(512), state_smem, s, p);
-  return hipGetLastError();
+  auto run = [&](const KdaParams& q) {
+    hipLaunchKernelGGL(state, dim3(q.nseg * q.N * q.H * (q.ncol / 16)), dim3(512), state_smem, s, q);
+    return hipGetLastError();
+  };
+  KdaParams q = p;
+  q.ncol = p.Dv;
+  q.zero_u = 0;
+  q.carry = nullptr;
+  if (p.G == 1) {
+    q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
+    q.seg_out = nullptr; q.final_to_sfinal = 1;
+    return run(q);
+  }
+  // G segments per sequence, as for the scalar-gate pass: (1) segment 0 from S0
+  // with its outputs and segments 1 .. G-2 from zero (their offsets b); (2) the
+  // transition maps M of segments 1 .. G-2 (V = 0, started from the identity);
+  // (3) the carries, composed in fp32; (4) segments 1 .. G-1 again from them.
+  const size_t ends_floats = static_cast<size_t>(p.G) * p.N * p.H * DK * p.Dv;
+  float* ends = p.seg_ws;
+  float* starts = ends + ends_floats;
+  float* maps = starts + ends_floats;
+  q.seg_base = 0; q.nseg = p.G - 1; q.start_mode = kStartS0; q.write_o = kOutSeg0;
+  q.seg_out = ends; q.final_to_sfinal = 0;
+  if ((e = run(q)) != hipSuccess) return e;
+  if (p.G > 2) {
+    KdaParams m = q;
+    m.ncol = DK; m.seg_base = 1; m.nseg = p.G - 2; m.start_mode = kStartIdentity;
+    m.write_o = kOutNone; m.zero_u = 1; m.seg_out = maps;
+    if ((e = run(m)) != hipSuccess) return e;
+  }
+  if ((e = launch_segment_carry(ends, maps, starts, p.G, p.N, p.H, DK, p.Dv, s)) != hipSuccess) return e;
+  q.seg_base = 1; q.nseg = p.G - 1; q.start_mode = kStartCarry; q.write_o = kOutAll;
+  q.carry = starts; q.seg_out = nullptr; q.final_to_sfinal = 1;
+  return run(q);
 }
 
 }  // namespace

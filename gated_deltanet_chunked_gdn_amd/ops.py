@@ -202,9 +202,11 @@ def chunk_fwd_noalloc(q, k, v, g, beta, out, final_state_out=None, S0=None, cu_s
 
 
 def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
-                  output_final_state: bool = True, out=None, final_state_out=None, workspace=None):
+                  output_final_state: bool = True, out=None, final_state_out=None, workspace=None,
+                  num_segments: int = 1):
     """Chunked forward pass with one log-decay per key channel: g is fp32 and
-    shaped like q.  Returns (o, S_final or None); buffers as for chunk_fwd."""
+    shaped like q.  Returns (o, S_final or None); buffers as for chunk_fwd;
+    num_segments > 1 runs the segment split."""
     lib = nat.load()
     _check_inputs(q, k, v, beta, beta)
     if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
@@ -213,7 +215,7 @@ def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0
     if not g.is_contiguous():
         raise ValueError("g must be a contiguous GPU tensor")
     seqs = _seqlens(cu_seqlens, q.device)
-    prob = make_problem(q, v, seqs, scale, 1)
+    prob = make_problem(q, v, seqs, scale, num_segments)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
     S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
     if out is None:

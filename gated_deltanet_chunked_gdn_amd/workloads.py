@@ -27,6 +27,9 @@ The five named workloads follow the pages' experiments:
   (token, head, key channel), the gate layout of the cuLA issue #126 page
   ("Minimal public reproduction": g shaped like q, dt_bias per head and
   channel); the values follow the Day-2 gate formula channel by channel.
+* ``kda_long_bf16`` -- the cuLA issue #126 synthetic case in its own gate layout:
+  T=65536, H=1, d=128, per-channel log-decays uniform in [-1e-3, -1e-4) (slow
+  decay), for the segment split.
 """
 from __future__ import annotations
 
@@ -109,6 +112,8 @@ WORKLOADS = {
                             gate="gdn", s0_std=0.0, with_dO=True, seed=4),
     "kda_bf16": Workload("kda_bf16", 4, 4096, 8, 128, 128, io="bf16", qk="norm_both",
                          gate="gdn_channel", seed=5),
+    "kda_long_bf16": Workload("kda_long_bf16", 1, 65536, 1, 128, 128, io="bf16", qk="iid",
+                              gate="channel_slow", seed=6),
 }
 
 
@@ -159,6 +164,10 @@ def generate(w: Workload) -> dict:
         g = (np.float32(-5.0) * _sigmoid(randn(B, T, H))).astype(np.float32)
     elif w.gate == "const":
         g = np.full((B, T, H), w.gate_const, dtype=np.float32)
+    elif w.gate == "channel_slow":
+        # slow per-channel decay: log-decay per (token, head, key channel) uniform in
+        # [-1e-3, -1e-4), so the state forgets over thousands of tokens
+        g = (-(1e-4 + 9e-4 * rng.random((B, T, H, Dk)))).astype(np.float32)
     elif w.gate == "gdn_channel":
         a = randn(B, T, H, Dk)
         A_log = rng.uniform(0.0, 1.5, size=(H,)).astype(np.float32)

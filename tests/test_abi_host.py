@@ -252,7 +252,13 @@ def test_kda_workspace_and_checks():
         for io, size in ((nat.GDN_BF16, 2), (nat.GDN_FP32, 4)):
             rec = (8192 + 3 * 64 * Dk) * size + 4 * Dk
             assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_FWD) == (nat.GDN_OK, slots * 3 * rec)
-    assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    # segment split: the fp32 end states, start states (G N H Dk Dv each) and maps (G N H Dk Dk)
+    # after the records
+    for G in (2, 16):
+        rec = slots * 3 * ((8192 + 3 * 64 * 128) * 2 + 4 * 128)
+        seg = (2 * G * 2 * 3 * 128 * 128 + G * 2 * 3 * 128 * 128) * 4
+        assert ws(problem(num_segments=G), nat.GDN_PASS_KDA_FWD) == (nat.GDN_OK, rec + seg)
+    assert ws(problem(num_segments=3), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(Dk=96), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
     P = ctypes.c_void_p
     lib = nat.load()
@@ -268,7 +274,8 @@ def test_kda_workspace_and_checks():
     assert call(problem(), o=FAKE + 4096) == nat.GDN_ERR_ALIAS
     # g spans B T H Dk floats: an output starting inside that range aliases it
     assert call(problem(), o=FAKE + (3 << 30) + 2 * 100 * 3 * 128 * 4 - 16) == nat.GDN_ERR_ALIAS
-    assert call(problem(num_segments=4)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(num_segments=4)) == nat.GDN_ERR_WORKSPACE    # segments need the larger workspace
+    assert call(problem(num_segments=5)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
 
 

@@ -24,10 +24,10 @@ FP32_TOL = 3e-4
 BF16_TOL = 8e-3
 
 
-def _run(d, t):
+def _run(d, t, G=1):
     cu = d["cu_seqlens"]
     o, Sf = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t.get("S0"),
-                              cu_seqlens=cu, scale=d["scale"])
+                              cu_seqlens=cu, scale=d["scale"], num_segments=G)
     torch.cuda.synchronize()
     return to_np(o), to_np(Sf)
 
@@ -125,3 +125,69 @@ def test_kda_training_shape_every_head():
     print(f"kda_bf16: rel_rms o {eo:.2e} S_final {es:.2e}; worst head o {ho:.2e} S_final {hs:.2e}")
     assert eo <= BF16_TOL and es <= BF16_TOL
     assert ho <= BF16_TOL and hs <= BF16_TOL
+
+
+# ---- segment split (cuLA issue #126: "Summary", "Minimal public reproduction") ----
+
+SEG_CASES = [
+    (Workload("kda_seg_fp32", 2, 700, 2, 64, 64, io="fp32", qk="norm_both", gate="gdn_channel", s0_std=0.3,
+              seed=61), 4),
+    (Workload("kda_seg_bf16", 1, 2000, 2, 128, 48, io="bf16", qk="norm_both", gate="gdn_channel",
+              cu_seqlens=(0, 64, 64, 129, 1500, 2000), s0_std=0.2, seed=62), 16),
+    (Workload("kda_seg_bf16_dk64", 2, 1300, 2, 64, 128, io="bf16", qk="norm_both", gate="channel_slow",
+              s0_std=0.1, seed=63), 8),
+    (Workload("kda_seg_few_chunks", 3, 130, 2, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel",
+              s0_std=0.1, seed=64), 16),
+]
+
+
+@pytest.mark.parametrize("w,G", SEG_CASES, ids=lambda x: x.name if hasattr(x, "name") else f"G{x}")
+def test_kda_segments_match_oracle_and_serial(w, G):
+    d = generate(w)
+    t = to_device(d)
+    got = _run(d, t, G)
+    _check(d, got, _oracle(d), f"{w.name} G={G}")
+    # G = 2 and the rows of the first two segments are computed exactly as in the serial pass
+    one, two = _run(d, t, 1), _run(d, t, 2)
+    assert np.array_equal(two[0], one[0]) and np.array_equal(two[1], one[1])
+    if d["cu_seqlens"] is None:
+        L = -(-(-(-w.T // 64)) // G)
+        rows = min(2 * L * 64, w.T)
+        assert np.array_equal(got[0][:, :rows], one[0][:, :rows])
+
+
+@pytest.fixture(scope="module")
+def kda_long():
+    d = generate(WORKLOADS["kda_long_bf16"])
+    t = to_device(d)
+    o_ref, S_ref = _oracle(d)
+    one = _run(d, t, 1)
+    return d, t, o_ref, S_ref, one
+
+
+def test_kda_long_serial(kda_long):
+    d, t, o_ref, S_ref, (o1, S1) = kda_long
+    win = [rel_rms(o1[:, 8192 * i:8192 * (i + 1)], o_ref[:, 8192 * i:8192 * (i + 1)]) for i in range(8)]
+    es = rel_rms(S1, S_ref)
+    print("kda_long G=1: windows " + " ".join(f"{e:.2e}" for e in win) + f"; S_final {es:.2e}")
+    assert max(win) <= BF16_TOL and es <= BF16_TOL
+
+
+@pytest.mark.parametrize("G", [2, 4, 8, 16])
+def test_kda_long_segments_per_window(kda_long, G):
+    """Per-8K-window rel-L2 against the oracle and against the serial pass (the
+    windows of the cuLA issue #126 page's reproduction)."""
+    d, t, o_ref, S_ref, (o1, S1) = kda_long
+    o, Sf = _run(d, t, G)
+    win = [rel_rms(o[:, 8192 * i:8192 * (i + 1)], o_ref[:, 8192 * i:8192 * (i + 1)]) for i in range(8)]
+    win1 = [rel_rms(o[:, 8192 * i:8192 * (i + 1)], o1[:, 8192 * i:8192 * (i + 1)]) for i in range(8)]
+    es, es1 = rel_rms(Sf, S_ref), rel_rms(Sf, S1)
+    print(f"kda_long G={G}: windows vs oracle " + " ".join(f"{e:.2e}" for e in win)
+          + "; vs serial " + " ".join(f"{e:.2e}" for e in win1) + f"; S_final {es:.2e} (vs serial {es1:.2e})")
+    assert max(win) <= BF16_TOL and es <= BF16_TOL
+    assert max(win1) <= BF16_TOL and es1 <= BF16_TOL
+    L = -(-1024 // G)
+    rows = min(2 * L * 64, 65536)
+    assert np.array_equal(o[:, :rows], o1[:, :rows])
+    if G == 2:
+        assert np.array_equal(o, o1) and np.array_equal(Sf, S1)
