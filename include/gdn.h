@@ -214,12 +214,17 @@ gdn_status gdn_recurrent_ref(const gdn_problem* problem, const void* q, const vo
  *        and <= 0; beta [B,T,H] fp32; S0 [N,H,Dk,Dv] fp32 or NULL (zero)
  *   out: o [B,T,H,Dv] (io dtype), S_final [N,H,Dk,Dv] fp32 or NULL
  * Packed sequences through cu_seqlens as for gdn_chunk_fwd.  Dk 64 or 128 and
- * Dv a multiple of 16 up to 256, for both io dtypes; num_segments must be 1.
+ * Dv a multiple of 16 up to 256, for both io dtypes.  num_segments in {1, 2, 4,
+ * 8, 16}: the segment split of gdn_chunk_fwd (segment maps S -> M S + b, M a
+ * Dk x Dk matrix, composed in fp32; G = 2 and the first two segments are
+ * bit-identical to G = 1) -- the intra-card split whose error the cuLA issue
+ * #126 page measures ("Summary").
  * Precision: decays, A, the inverse and the state are fp32; the products take
  * bf16 operands with fp32 accumulation for bf16 io and are IEEE fp32 for fp32 io.
  * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_FWD, ...): one record per chunk
  * and head (T diag(beta), the causal score, K and Q scaled by the decays, the
- * decayed keys of the state update, in the io element type; the chunk's decay).  Errors as gdn_chunk_fwd: every check
+ * decayed keys of the state update, in the io element type; the chunk's decay),
+ * then for G > 1 fp32 buffers of 2 G N H Dk Dv + G N H Dk Dk floats.  Errors as gdn_chunk_fwd: every check
  * runs before the first launch. */
 gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const void* k,
                              const void* v, const float* g, const float* beta, const float* S0,
