@@ -198,30 +198,34 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
                       "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
                       "kernels": "kda_prep_kernel + kda_state_kernel"}
     if "policy" in which:
-        # latency and peak device memory of one forward call per precision policy:
-        # bf16 io (bf16 MFMA operands, fp32 accumulation and state) and fp32 io (IEEE
-        # fp32 products), on the d_k = 64 / d_v = 128 training shape both support
-        w = WORKLOADS["fwdbwd_bf16"]
-        d = generate(w.with_(io="fp32"))
+        # latency, workspace and peak device memory of one forward call per precision
+        # policy on the same bf16 inputs (the metric shape, B=4 T=4096 H=8 d=128):
+        # "io" (bf16 MFMA operands, fp32 accumulation and state) and "fp32" (every
+        # product in IEEE fp32, o rounded to bf16 once); and fp32 io for reference
+        w = WORKLOADS["train_bf16"]
+        d = generate(w)
         pol = {}
-        for name, io in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        for name, io, precision in (("bf16_io", torch.bfloat16, "io"), ("bf16_io_fp32_products", torch.bfloat16, "fp32"),
+                                    ("fp32_io", torch.float32, "io")):
             t = {key: torch.from_numpy(d[key]).to(dev).to(io) for key in ("q", "k", "v")}
             t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
-            kt = event_times(lambda i: gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale),
+            kt = event_times(lambda i: gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale,
+                                                     precision=precision),
                              max(5, steps // 2), 2, stream)
             torch.cuda.synchronize()
             torch.cuda.reset_peak_memory_stats(dev)
             base = torch.cuda.memory_allocated(dev)
-            o, Sf = gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale)
+            o, Sf = gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=w.scale, precision=precision)
             torch.cuda.synchronize()
             peak = torch.cuda.max_memory_allocated(dev) - base
-            ws = gdn.forward_workspace(t["q"], t["v"])
-            pol[name] = {"ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
+            ws = gdn.forward_workspace(t["q"], t["v"], precision=precision)
+            pol[name] = {"precision": precision, "ms_mean": float(kt.mean()) * 1e3,
+                         "tokens_per_s": w.B * w.T / float(kt.mean()),
                          "workspace_bytes": 0 if ws is None else ws.numel(),
                          "peak_call_bytes": int(peak),
                          "input_bytes": int(sum(x.numel() * x.element_size() for x in t.values()))}
             del t, o, Sf, ws
-        out["policy"] = {"workload": "fwdbwd_bf16 shape, forward", "by_io_dtype": pol}
+        out["policy"] = {"workload": "train_bf16 (B4 T4096 H8 d128), forward", "by_policy": pol}
     return out
 
 

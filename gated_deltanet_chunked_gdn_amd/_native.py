@@ -30,6 +30,9 @@ GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 # gdn_dtype
 GDN_FP32 = 0
 GDN_BF16 = 1
+# gdn_precision
+GDN_PRECISION_IO = 0
+GDN_PRECISION_FP32 = 1
 # gdn_gate_kind
 GDN_GATE_GDN = 0
 GDN_GATE_BOUNDED5 = 1
@@ -68,6 +71,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("chunk", ctypes.c_int32),
         ("num_segments", ctypes.c_int32),
+        ("precision", ctypes.c_int32),
     ]
 
 

@@ -37,6 +37,8 @@ struct Checked {
   int32_t N = 0;
   bool bf16 = false;
   size_t io = 4;         // bytes per io element
+  bool fp32_products = false;  // IEEE fp32 products (fp32 io, or GDN_PRECISION_FP32)
+  size_t ce = 4;         // bytes per element of the per-chunk records (the product operand type)
 };
 
 enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd, KdaFwd };
@@ -49,12 +51,15 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (p->Dk != 64 && p->Dk != 128) return GDN_ERR_UNSUPPORTED;
   if (p->Dv % 16 != 0 || p->Dv < 16 || p->Dv > 256) return GDN_ERR_UNSUPPORTED;
   if (p->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (p->precision != GDN_PRECISION_IO && p->precision != GDN_PRECISION_FP32) return GDN_ERR_UNSUPPORTED;
+  const bool fp32_policy_bf16 = p->precision == GDN_PRECISION_FP32 && p->io_dtype == GDN_BF16;
+  if (fp32_policy_bf16 && (kind == Kind::ChunkBwd || kind == Kind::KdaFwd)) return GDN_ERR_UNSUPPORTED;
   const bool chunked = kind == Kind::ChunkFwd || kind == Kind::ChunkBwd;
   if (chunked) {
     const int G = p->num_segments;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
     if (kind == Kind::ChunkBwd && G != 1) return GDN_ERR_UNSUPPORTED;
-    if (p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
+    if (kind == Kind::ChunkBwd && p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
     // one chunk of one head's rows is addressed with 32-bit byte offsets
     if (static_cast<int64_t>(64) * p->H * p->Dv * 4 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   }
@@ -95,16 +100,18 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   c->N = p->num_seqs;
   c->bf16 = p->io_dtype == GDN_BF16;
   c->io = c->bf16 ? 2 : 4;
+  c->fp32_products = !c->bf16 || p->precision == GDN_PRECISION_FP32;
+  c->ce = c->fp32_products ? 4 : 2;
   return GDN_OK;
 }
 
 size_t t_slot_bytes(const gdn_problem* p, const Checked& c) {
-  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 64 * 64 * c.io;
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * 64 * 64 * c.ce;
   return (b + 255) / 256 * 256;
 }
 
 size_t packed_slot_bytes(const gdn_problem* p, const Checked& c) {
-  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kTbSlot * c.io;
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kTbSlot * c.ce;
   return (b + 255) / 256 * 256;
 }
 
@@ -214,7 +221,7 @@ const char* gdn_status_str(int32_t s) {
     case GDN_ERR_NULL: return "required pointer is NULL";
     case GDN_ERR_SHAPE: return "size out of range or inconsistent";
     case GDN_ERR_DTYPE: return "io_dtype is not a gdn_dtype";
-    case GDN_ERR_UNSUPPORTED: return "unsupported Dk, Dv, chunk, num_segments or pass";
+    case GDN_ERR_UNSUPPORTED: return "unsupported Dk, Dv, chunk, num_segments, precision or pass";
     case GDN_ERR_WORKSPACE: return "workspace NULL or too small";
     case GDN_ERR_ALIAS: return "an output overlaps another tensor";
     case GDN_ERR_HIP: return "HIP launch failed";
@@ -273,7 +280,7 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   fp.scale = p->scale;
   fp.G = p->num_segments;
   fp.seg_ws = fp.G > 1 ? reinterpret_cast<float*>(wsb + pb + t_slot_bytes(p, c) + gate_slot_bytes(p, c)) : nullptr;
-  return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+  return hip_status(gdn::launch_chunk_fwd(fp, p->Dk, c.bf16, c.fp32_products, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,

@@ -58,6 +58,29 @@ __device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int off)
 // moves no data.
 constexpr int kNoLoad = 0x7ffffff0;
 
+// One io element at byte offset `off`, widened to fp32 (bf16 widens exactly).
+template <typename IO>
+__device__ __forceinline__ float io_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (sizeof(IO) == 2)
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+  else
+    return buffer_load1(r, off);
+}
+// 16 bytes of io elements into `dst` of compute element type E: a plain copy when
+// the types agree, else 8 bf16 widened to 8 fp32 (two 16-byte stores).
+template <typename E, typename IO>
+__device__ __forceinline__ void io_stage16(E* dst, const u32x4_t& x) {
+  if constexpr (sizeof(E) == sizeof(IO)) {
+    *reinterpret_cast<u32x4_t*>(dst) = x;
+  } else {
+    static_assert(sizeof(E) == 4 && sizeof(IO) == 2, "bf16 io widened to fp32");
+    const u32x4_t lo = {x[0] << 16, x[0] & 0xffff0000u, x[1] << 16, x[1] & 0xffff0000u};
+    const u32x4_t hi = {x[2] << 16, x[2] & 0xffff0000u, x[3] << 16, x[3] & 0xffff0000u};
+    *reinterpret_cast<u32x4_t*>(dst) = lo;
+    *reinterpret_cast<u32x4_t*>(dst + 4) = hi;
+  }
+}
+
 // Row block, row and column of element e of a packed lower-block matrix.
 __device__ __forceinline__ void lpack_pos(int e, int& i, int& j) {
   const int rb = e < lpack_base(1) ? 0 : e < lpack_base(2) ? 1 : e < lpack_base(3) ? 2 : 3;
@@ -84,7 +107,9 @@ struct PrepSmem {
   float gam[64], bet[64];
 };
 
-template <int DK, typename Op>
+// IO: element type of q and k in memory (the compute type, or bf16 widened to
+// fp32 for fp32 products on bf16 inputs).
+template <int DK, typename Op, typename IO>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   using E = typename Op::elem;
   using F = typename Op::frag_t;
@@ -107,8 +132,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
   const int64_t row0 = bos + c0;
   const int64_t slot = bos / 64 + n + c;
-  const E* __restrict__ k = static_cast<const E*>(p.k);
-  const E* __restrict__ q = static_cast<const E*>(p.q);
+  const IO* __restrict__ k = static_cast<const IO*>(p.k);
+  const IO* __restrict__ q = static_cast<const IO*>(p.q);
   const bool want_p = p.pws != nullptr;
   // Each wave forms the A blocks of row block `wave` and the P blocks of row block
   // 3 - wave: five 16x16 blocks per wave.
@@ -119,7 +144,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   // MFMA fragments, K rows, g and beta.  No load sits inside a branch and every
   // loaded value is used by every wave: a load in a branch, or one sunk into
   // the only branch that uses it, is waited for where that branch ends.
-  const int s_e = static_cast<int>(sizeof(E));
+  const int s_e = static_cast<int>(sizeof(IO));
   const int rows_bytes = ((nv - 1) * H * DK + DK) * s_e;
   F qf[NKK];
   {
@@ -132,17 +157,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
       if constexpr (sizeof(E) == 2)
         qf[ks] = __builtin_bit_cast(F, buffer_load16(rq, off));
       else
-        qf[ks] = buffer_load1(rq, off);
+        qf[ks] = io_load1<IO>(rq, off);
     }
   }
-  constexpr int VPR = DK / EPV;
+  constexpr int EPVI = 16 / static_cast<int>(sizeof(IO));  // io elements per 16-byte vector
+  constexpr int VPR = DK / EPVI;
   constexpr int NKV = 64 * VPR / 256;
   const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, rows_bytes);
   u32x4_t kv[NKV];
 #pragma unroll
   for (int x = 0; x < NKV; ++x) {
     const int vi = x * 256 + tid, t = vi / VPR, cc = vi % VPR;
-    kv[x] = buffer_load16(rk, (t * H * DK + cc * EPV) * s_e);
+    kv[x] = buffer_load16(rk, (t * H * DK + cc * EPVI) * s_e);
   }
   const auto rg = buffer_rsrc(p.g + row0 * H + h, ((nv - 1) * H + 1) * 4);
   const auto rb = buffer_rsrc(p.beta + row0 * H + h, ((nv - 1) * H + 1) * 4);
@@ -151,7 +177,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
 #pragma unroll
   for (int x = 0; x < NKV; ++x) {
     const int vi = x * 256 + tid, t = vi / VPR, cc = vi % VPR;
-    *reinterpret_cast<u32x4_t*>(Ks + t * LDK + cc * EPV) = kv[x];
+    io_stage16<E, IO>(Ks + t * LDK + cc * EPVI, kv[x]);
   }
   {
     // every wave scans g and writes beta (identical values); wave 0 also stores the decays
@@ -370,7 +396,7 @@ struct Raw4<float> {
 
 // STATES: also store S_c before every chunk (the backward's forward half).
 // OUT: compute and store the output (stores are further masked per segment).
-template <int DK, typename Op, bool STATES, bool OUT>
+template <int DK, typename Op, typename IO, bool STATES, bool OUT>
 __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   using E = typename Op::elem;
   using F = typename Op::frag_t;
@@ -382,13 +408,14 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   constexpr int DPW = DK / 64;  // 16-row blocks of S per state wave
   extern __shared__ __align__(16) char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const E* __restrict__ q = static_cast<const E*>(p.q);
-  const E* __restrict__ k = static_cast<const E*>(p.k);
-  const E* __restrict__ v = static_cast<const E*>(p.v);
+  const IO* __restrict__ q = static_cast<const IO*>(p.q);
+  const IO* __restrict__ k = static_cast<const IO*>(p.k);
+  const IO* __restrict__ v = static_cast<const IO*>(p.v);
   const E* __restrict__ tbw = static_cast<const E*>(p.tbws);
   const E* __restrict__ pw = static_cast<const E*>(p.pws);
   const float* __restrict__ gw = p.gws;
-  E* __restrict__ o = static_cast<E*>(p.o);
+  IO* __restrict__ o = static_cast<IO*>(p.o);
+  constexpr int SIO = static_cast<int>(sizeof(IO));
 
   const int H = p.H, Dv = p.Dv, NC = p.ncol, NT = NC / 16;
   // XCD-aware block order: consecutive virtual blocks (the tiles of one head)
@@ -481,10 +508,15 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
   auto load_q = [&](F (&f)[NKK], int c) {
     const int nv = chunk_rows(c);
     const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
-    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
+    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * SIO);
 #pragma unroll
-    for (int ks = 0; ks < NKK; ++ks)
-      f[ks] = frag_load(rq, (tc * H * DK + ks * KS + lg * Op::KPL) * static_cast<int>(sizeof(E)));
+    for (int ks = 0; ks < NKK; ++ks) {
+      const int off = (tc * H * DK + ks * KS + lg * Op::KPL) * SIO;
+      if constexpr (sizeof(E) == 2)
+        f[ks] = __builtin_bit_cast(F, buffer_load16(rq, off));
+      else
+        f[ks] = io_load1<IO>(rq, off);
+    }
   };
   auto load_p = [&](F (&f)[NTS], int c) {
     const auto rp = buffer_rsrc(pw + ((slot0 + c) * H + h) * 4096, 4096 * static_cast<int>(sizeof(E)));
@@ -594,9 +626,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     // and write nothing.
     const int ot = tid - 256;
     constexpr int EPV = 16 / static_cast<int>(sizeof(E));
-    constexpr int KVR = DK / EPV;                     // 16-byte vectors per K row
+    constexpr int EPVI = 16 / SIO;                    // io elements per 16-byte vector
+    constexpr int KVR = DK / EPVI;                    // 16-byte vectors per K row (io)
     constexpr int NKV = 64 * KVR / 256;               // K vectors per loader thread
-    constexpr int VVR = static_cast<int>(sizeof(E));  // 16-byte vectors per v-tile row
+    constexpr int VVR = SIO;                          // 16-byte vectors per v-tile row (io)
     constexpr int TVN = kLPack / EPV;                 // vectors of a packed T diag(beta)
     constexpr int NTV = (TVN + 255) / 256;
     struct LoadSet {
@@ -609,11 +642,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     auto load_k = [&](LoadSet& s, int c) {
       const int nv = chunk_rows(c);
       const int64_t row0 = bos + static_cast<int64_t>(cb + c) * 64;
-      const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E)));
+      const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * SIO);
 #pragma unroll
       for (int x = 0; x < NKV; ++x) {
-        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
-        s.kv[x] = buffer_load16(rk, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
+        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPVI;
+        s.kv[x] = buffer_load16(rk, (t * H * DK + cv) * SIO);
       }
     };
     auto load_rest = [&](LoadSet& s, int c) {  // T diag(beta), the v tile, the decays
@@ -624,10 +657,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
 #pragma unroll
       for (int x = 0; x < NTV; ++x) s.tv[x] = buffer_load16(rt, (x * 256 + ot) * 16);
       // (a pass without V still loads, from columns clamped into the row, and discards them)
-      const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, ((nv - 1) * H * Dv + Dv) * static_cast<int>(sizeof(E)));
-      const int t = ot / VVR, cpos = (ot % VVR) * EPV;
-      s.vv = buffer_load16(rv, ot < 64 * VVR ? (t * H * Dv + min(j0 + cpos, Dv - EPV)) * static_cast<int>(sizeof(E))
-                                             : kNoLoad);
+      const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, ((nv - 1) * H * Dv + Dv) * SIO);
+      const int t = ot / VVR, cpos = (ot % VVR) * EPVI;
+      s.vv = buffer_load16(rv, ot < 64 * VVR ? (t * H * Dv + min(j0 + cpos, Dv - EPVI)) * SIO : kNoLoad);
       s.gv = buffer_load16(buffer_rsrc(gw + sh * 128, 512), ot * 16);
     };
     auto stage_t = [&](const LoadSet& s, int sl) {
@@ -641,10 +673,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
     auto stage_kvg = [&](const LoadSet& s, int sl) {
 #pragma unroll
       for (int x = 0; x < NKV; ++x) {
-        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPV;
-        *reinterpret_cast<u32x4_t*>(sm.Ks[sl] + t * LDK + cv) = s.kv[x];
+        const int vi = x * 256 + ot, t = vi / KVR, cv = (vi % KVR) * EPVI;
+        io_stage16<E, IO>(sm.Ks[sl] + t * LDK + cv, s.kv[x]);
       }
-      if (ot < 64 * VVR) *reinterpret_cast<u32x4_t*>(sm.Vs[sl] + (ot / VVR) * 16 + (ot % VVR) * EPV) = s.vv;
+      if (ot < 64 * VVR) io_stage16<E, IO>(sm.Vs[sl] + (ot / VVR) * 16 + (ot % VVR) * EPVI, s.vv);
       if (ot < 32) *reinterpret_cast<u32x4_t*>(sm.Gs[sl] + 4 * ot) = s.gv;
     };
 
@@ -693,8 +725,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
           // rows of padded tokens and steps past the last chunk fall outside the range
           const int cc = clampc(c), nv = chunk_rows(cc);
           const auto ro = buffer_rsrc(o + ((bos + static_cast<int64_t>(cb + cc) * 64) * H + h) * Dv + j0,
-                                      store_o && c < nch ? ((nv - 1) * H * Dv + 16) * static_cast<int>(sizeof(E)) : 0);
-          buffer_store4<E>(ro, (tc * H * Dv + 4 * lg) * static_cast<int>(sizeof(E)),
+                                      store_o && c < nch ? ((nv - 1) * H * Dv + 16) * SIO : 0);
+          buffer_store4<IO>(ro, (tc * H * Dv + 4 * lg) * SIO,
                            p.scale * (gt * yacc[0] + oacc[0]), p.scale * (gt * yacc[1] + oacc[1]),
                            p.scale * (gt * yacc[2] + oacc[2]), p.scale * (gt * yacc[3] + oacc[3]));
           load_p(pf[u], clampc(c + 2));
@@ -753,11 +785,11 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              static_cast<int>(bytes));
 }
 
-template <int DK, typename Op>
+template <int DK, typename Op, typename IO>
 hipError_t launch_prep(const FwdParams& p, hipStream_t s) {
   constexpr size_t smem = sizeof(PrepSmem<DK, Op>);
   static_assert(smem <= 160 * 1024, "LDS budget exceeded");
-  auto prep = chunk_prep_kernel<DK, Op>;
+  auto prep = chunk_prep_kernel<DK, Op, IO>;
   hipError_t e = allow_lds(prep, smem);
   if (e != hipSuccess || p.max_chunks == 0) return e;
   hipLaunchKernelGGL(prep, dim3(p.max_chunks, p.H, p.N), dim3(256), smem, s, p);
@@ -776,7 +808,7 @@ int cu_count() {
   return counts[dev];
 }
 
-template <int DK, typename Op, bool STATES, bool OUT>
+template <int DK, typename Op, typename IO, bool STATES, bool OUT>
 hipError_t launch_state(const FwdParams& q, hipStream_t s) {
   if constexpr (std::is_same<Op, OpBf16>::value) {
     return launch_state_chain(q, DK, STATES, OUT, s);
@@ -788,7 +820,7 @@ hipError_t launch_state(const FwdParams& q, hipStream_t s) {
     // stays idle; larger grids pack two per CU where they fit.
     const int blocks = q.nseg * q.N * q.H * (q.ncol / 16);
     const size_t smem = blocks < 2 * cu_count() && need < 82 * 1024 ? 82 * 1024 : need;
-    auto state = chunk_state_kernel<DK, Op, STATES, OUT>;
+    auto state = chunk_state_kernel<DK, Op, IO, STATES, OUT>;
     hipError_t e = allow_lds(state, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(state, dim3(blocks), dim3(512), smem, s, q);
@@ -796,20 +828,20 @@ hipError_t launch_state(const FwdParams& q, hipStream_t s) {
   }
 }
 
-template <int DK, typename Op>
+template <int DK, typename Op, typename IO>
 hipError_t launch_states_t(const FwdParams& p, hipStream_t s) {
-  hipError_t e = launch_prep<DK, Op>(p, s);
+  hipError_t e = launch_prep<DK, Op, IO>(p, s);
   if (e != hipSuccess) return e;
   FwdParams q = p;
   q.G = 1; q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutNone;
   q.zero_u = 0; q.ncol = p.Dv; q.carry = nullptr; q.seg_out = nullptr; q.final_to_sfinal = 0;
   q.S_final = nullptr;
-  return launch_state<DK, Op, true, false>(q, s);
+  return launch_state<DK, Op, IO, true, false>(q, s);
 }
 
-template <int DK, typename Op>
+template <int DK, typename Op, typename IO>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  hipError_t e = launch_prep<DK, Op>(p, s);
+  hipError_t e = launch_prep<DK, Op, IO>(p, s);
   if (e != hipSuccess) return e;
   FwdParams q = p;
   q.ncol = p.Dv;
@@ -818,7 +850,7 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   if (p.G == 1) {
     q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
     q.seg_out = nullptr; q.final_to_sfinal = 1;
-    return launch_state<DK, Op, false, true>(q, s);
+    return launch_state<DK, Op, IO, false, true>(q, s);
   }
   // G segments per sequence: (1) segment 0 from S0 with its outputs, and the
   // segments 1 .. G-2 from zero (their offsets b); (2) the transition maps M of
@@ -830,29 +862,29 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   float* maps = starts + ends_floats;
   q.seg_base = 0; q.nseg = p.G - 1; q.start_mode = kStartS0; q.write_o = kOutSeg0;
   q.seg_out = ends; q.final_to_sfinal = 0;
-  if ((e = launch_state<DK, Op, false, true>(q, s)) != hipSuccess) return e;
+  if ((e = launch_state<DK, Op, IO, false, true>(q, s)) != hipSuccess) return e;
   if (p.G > 2) {
     FwdParams m = q;
     m.ncol = DK; m.seg_base = 1; m.nseg = p.G - 2; m.start_mode = kStartIdentity;
     m.write_o = kOutNone; m.zero_u = 1; m.seg_out = maps;
-    if ((e = launch_state<DK, Op, false, false>(m, s)) != hipSuccess) return e;
+    if ((e = launch_state<DK, Op, IO, false, false>(m, s)) != hipSuccess) return e;
   }
   CarryParams c{ends, maps, starts, p.G, p.N, p.H, DK, p.Dv};
   hipLaunchKernelGGL(seg_carry_kernel<DK>, dim3(p.N * p.H * (p.Dv / 16)), dim3(256), 0, s, c);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   q.seg_base = 1; q.nseg = p.G - 1; q.start_mode = kStartCarry; q.write_o = kOutAll;
   q.carry = starts; q.seg_out = nullptr; q.final_to_sfinal = 1;
-  return launch_state<DK, Op, false, true>(q, s);
+  return launch_state<DK, Op, IO, false, true>(q, s);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
   if (bf16) {
-    if (Dk == 64) return launch_states_t<64, OpBf16>(p, s);
-    if (Dk == 128) return launch_states_t<128, OpBf16>(p, s);
+    if (Dk == 64) return launch_states_t<64, OpBf16, uint16_t>(p, s);
+    if (Dk == 128) return launch_states_t<128, OpBf16, uint16_t>(p, s);
   } else {
-    if (Dk == 64) return launch_states_t<64, OpF32>(p, s);
+    if (Dk == 64) return launch_states_t<64, OpF32, float>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -869,12 +901,16 @@ hipError_t launch_segment_carry(const float* ends, const float* maps, float* sta
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
-  if (bf16) {
-    if (Dk == 64) return launch_fwd_t<64, OpBf16>(p, s);
-    if (Dk == 128) return launch_fwd_t<128, OpBf16>(p, s);
+hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, bool fp32_products, hipStream_t s) {
+  if (bf16 && !fp32_products) {
+    if (Dk == 64) return launch_fwd_t<64, OpBf16, uint16_t>(p, s);
+    if (Dk == 128) return launch_fwd_t<128, OpBf16, uint16_t>(p, s);
+  } else if (bf16) {  // bf16 inputs and output, every product in IEEE fp32
+    if (Dk == 64) return launch_fwd_t<64, OpF32, uint16_t>(p, s);
+    if (Dk == 128) return launch_fwd_t<128, OpF32, uint16_t>(p, s);
   } else {
-    if (Dk == 64) return launch_fwd_t<64, OpF32>(p, s);
+    if (Dk == 64) return launch_fwd_t<64, OpF32, float>(p, s);
+    if (Dk == 128) return launch_fwd_t<128, OpF32, float>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -149,7 +149,8 @@ struct PrologueParams {
 
 // Launchers; return hipSuccess or the launch error.  `dk`/`dv` are the head sizes,
 // `bf16` selects the io dtype.
-hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
+// fp32_products: IEEE fp32 products for bf16 io (the inputs widened exactly, o rounded once)
+hipError_t launch_chunk_fwd(const FwdParams& p, int Dk, bool bf16, bool fp32_products, hipStream_t s);
 // The bf16 state pass (one launch): `states` stores S_c before every chunk, `out`
 // forms the output.  Reads the bf16 T diag(beta) fragments, P and the decays.
 hipError_t launch_state_chain(const FwdParams& p, int Dk, bool states, bool out, hipStream_t s);

@@ -101,7 +101,11 @@ def _fp32_state(t, N, H, Dk, Dv, name, device):
     return t
 
 
-def make_problem(q, v, seqs: Optional[SeqLens], scale: float, num_segments: int = 1) -> nat.Problem:
+_PRECISION = {"io": nat.GDN_PRECISION_IO, "fp32": nat.GDN_PRECISION_FP32}
+
+
+def make_problem(q, v, seqs: Optional[SeqLens], scale: float, num_segments: int = 1,
+                 precision: str = "io") -> nat.Problem:
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     p = nat.Problem()
@@ -118,6 +122,9 @@ def make_problem(q, v, seqs: Optional[SeqLens], scale: float, num_segments: int 
     p.scale = float(scale)
     p.chunk = 64
     p.num_segments = int(num_segments)
+    if precision not in _PRECISION:
+        raise ValueError(f"precision must be one of {sorted(_PRECISION)}")
+    p.precision = _PRECISION[precision]
     return p
 
 
@@ -128,25 +135,27 @@ def _workspace(problem, pass_, device):
     return torch.empty(n, dtype=torch.uint8, device=device), n
 
 
-def forward_workspace(q, v, cu_seqlens=None, num_segments: int = 1):
+def forward_workspace(q, v, cu_seqlens=None, num_segments: int = 1, precision: str = "io"):
     """A uint8 device tensor of the size gdn_chunk_fwd asks for (None if 0 bytes)."""
     seqs = _seqlens(cu_seqlens, q.device)
-    return _workspace(make_problem(q, v, seqs, 1.0, num_segments), nat.GDN_PASS_CHUNK_FWD,
+    return _workspace(make_problem(q, v, seqs, 1.0, num_segments, precision), nat.GDN_PASS_CHUNK_FWD,
                       q.device)[0]
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0,
               num_segments: int = 1, output_final_state: bool = True, out=None,
-              final_state_out=None, workspace=None):
+              final_state_out=None, workspace=None, precision: str = "io"):
     """Chunked forward pass.  Returns (o, S_final or None).
 
     ``out`` / ``final_state_out`` / ``workspace`` may supply preallocated
     buffers (o shaped like v; S_final (N, H, Dk, Dv) fp32; a uint8 device
-    tensor of at least the size the library asks for)."""
+    tensor of at least the size the library asks for).  ``precision``: "io"
+    (bf16 io: bf16 MFMA operands, fp32 accumulation) or "fp32" (every product in
+    IEEE fp32, also for bf16 inputs and output)."""
     lib = nat.load()
     _check_inputs(q, k, v, g, beta)
     seqs = _seqlens(cu_seqlens, q.device)
-    prob = make_problem(q, v, seqs, scale, num_segments)
+    prob = make_problem(q, v, seqs, scale, num_segments, precision)
     N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
     S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
     if out is None:

@@ -58,7 +58,7 @@
  *      io dtype GDN_BF16: bf16 MFMA operands with fp32 accumulation; the state,
  *        the decay factors, the triangular solve and all gradients' reductions
  *        are fp32; outputs are rounded to bf16 (round to nearest even) once.
- *  - Supported: Dk in {64, 128} (io GDN_FP32: chunked passes Dk == 64 only);
+ *  - Supported: Dk in {64, 128} (fp32 products: gdn_chunk_bwd Dk == 64 only);
  *    Dv a multiple of 16 with 16 <= Dv <= 256; chunk == 64; num_segments in
  *    {1, 2, 4, 8, 16}; N <= 65535.  The recurrent backward needs
  *    2 * Dk * (Dv + 1) * 4 bytes of LDS and so Dk * Dv <= 128 * 128.
@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -94,6 +94,20 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype { GDN_FP32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* Precision policy of the chunked products (the fla issue #1550 page, "Proposed
+ * scope", asks for a policy for the score and WY intermediates that keeps the
+ * public dtypes, chosen on measured latency and memory):
+ *   GDN_PRECISION_IO   the io dtype decides: bf16 io -> bf16 MFMA operands (the
+ *                      inverse T diag(beta), the score P, R, E and the state
+ *                      operand rounded to bf16) with fp32 accumulation, state and
+ *                      decays; fp32 io -> every product in IEEE fp32.
+ *   GDN_PRECISION_FP32 every product in IEEE fp32 (fp32 MFMA) whatever the io
+ *                      dtype: bf16 inputs are widened exactly, o is rounded to
+ *                      bf16 once, the per-chunk workspace records are fp32.
+ *                      gdn_chunk_fwd only (gdn_chunk_bwd and gdn_kda_chunk_fwd
+ *                      with bf16 io return GDN_ERR_UNSUPPORTED for it). */
+typedef enum gdn_precision { GDN_PRECISION_IO = 0, GDN_PRECISION_FP32 = 1 } gdn_precision;
+
 typedef enum gdn_pass {
   GDN_PASS_CHUNK_FWD = 0,
   GDN_PASS_CHUNK_BWD = 1,
@@ -111,6 +125,7 @@ typedef struct gdn_problem {
   float scale;                     /* output scale: o_t = scale * S_t^T q_t                 */
   int32_t chunk;                   /* tokens per chunk; must be 64                          */
   int32_t num_segments;            /* 1: serial over chunks; G > 1: segment split (fwd)     */
+  int32_t precision;               /* gdn_precision of the chunked products                 */
 } gdn_problem;
 
 /* Version of this ABI (GDN_ABI_VERSION). */

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
@@ -75,10 +75,26 @@ def ws(p, pass_=nat.GDN_PASS_CHUNK_FWD):
     (dict(num_segments=0), nat.GDN_ERR_UNSUPPORTED),
     (dict(num_segments=32), nat.GDN_ERR_UNSUPPORTED),
     (dict(num_seqs=3), nat.GDN_ERR_SHAPE),
-    (dict(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_ERR_UNSUPPORTED),
+    (dict(precision=2), nat.GDN_ERR_UNSUPPORTED),
+    (dict(precision=-1), nat.GDN_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
     assert ws(problem(**kw))[0] == status
+
+
+def test_precision_policy_scope():
+    """IEEE fp32 products: the forward at both head sizes and io dtypes; the
+    backward only with fp32 io at Dk = 64; not the per-channel-decay forward with
+    bf16 io."""
+    fp32 = nat.GDN_PRECISION_FP32
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128))[0] == nat.GDN_OK
+    assert ws(problem(precision=fp32))[0] == nat.GDN_OK
+    assert ws(problem(precision=fp32, Dk=64))[0] == nat.GDN_OK
+    assert ws(problem(precision=fp32), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64, precision=fp32), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_OK
+    assert ws(problem(precision=fp32), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(precision=fp32), nat.GDN_PASS_RECURRENT_FWD)[0] == nat.GDN_OK
 
 
 def test_workspace_sizes():
@@ -92,6 +108,9 @@ def test_workspace_sizes():
     recs = up(slots * 3 * 3072 * 2) + up(slots * 3 * 4096 * 2) + gates
     assert ws(problem()) == (nat.GDN_OK, recs)
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64)) == (
+        nat.GDN_OK, up(slots * 3 * 3072 * 4) + up(slots * 3 * 4096 * 4) + gates)
+    # fp32 products on bf16 inputs keep fp32 records
+    assert ws(problem(precision=nat.GDN_PRECISION_FP32)) == (
         nat.GDN_OK, up(slots * 3 * 3072 * 4) + up(slots * 3 * 4096 * 4) + gates)
     # segment split: then fp32 end and start states [G][N][H][Dk][Dv] and maps [G][N][H][Dk][Dk]
     for G in (2, 4, 16):
