@@ -319,6 +319,37 @@ def parse():
     return ap.parse_args()
 
 
+def measure_copy(dev, steps: int, warmup: int, gib: int = 2):
+    """A `gib` GiB device copy, timed with HIP events, bytes counted as read plus
+    written: torch's copy_ and the library's own copy kernel (gdn_device_copy)."""
+    import torch
+
+    import gated_deltanet_chunked_gdn_amd as gdn
+
+    n = gib * 1024 ** 3 // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    res = {"bytes_per_copy": 2 * a.numel() * 4}
+    for name, fn in (("torch_copy", lambda: b.copy_(a)), ("hip_copy_kernel", lambda: gdn.device_copy(b, a))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        res[name] = {"GBps": 2 * a.numel() * 4 / t / 1e9, "frac_of_8TBps": 2 * a.numel() * 4 / t / 8e12,
+                     "ms": t * 1e3}
+    assert bool((b == 1.0).all()), "copy check"
+    res["copy_GBps"] = max(res["torch_copy"]["GBps"], res["hip_copy_kernel"]["GBps"])
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def micro(kind: str, steps: int, warmup: int):
     """Measured peaks, as the Day-2 page measures its GB10 ("Rooflines": a copy of a
     2 GB tensor and (8192, 8192) x (8192, 8192) matmuls).  The library is only run."""
@@ -327,21 +358,7 @@ def micro(kind: str, steps: int, warmup: int):
     dev = torch.device("cuda:0")
     out = {"micro": kind}
     if kind == "copy":
-        n = 2 * 1024 ** 3 // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(warmup):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / steps
-        out.update({"bytes_per_copy": 2 * a.numel() * 4, "copy_GBps": 2 * a.numel() * 4 / t / 1e9,
-                    "frac_of_8TBps": 2 * a.numel() * 4 / t / 8e12, "ms": t * 1e3})
+        out.update(measure_copy(dev, steps, warmup))
     else:
         for dt, peak in ((torch.bfloat16, 2.5e15), (torch.float32, 157.3e12)):
             x = torch.randn(8192, 8192, device=dev).to(dt)
@@ -505,6 +522,14 @@ def main():
                    "recurrence_tflops_6DkDv": w.B * w.T * w.H * 6 * w.Dk * w.Dv / k_mean / 1e12,
                    "token_heads_per_s": w.B * w.T * w.H / k_mean},
     }
+    if not args.no_extras:
+        # the attainable copy bandwidth on this machine (2 GiB, read + write counted):
+        # the forward's fraction of it is reported beside the fraction of 8 TB/s
+        print("[bench] copy ceiling ...", file=sys.stderr, flush=True)
+        cp = measure_copy(dev, 10, 3)
+        result["roofline"]["measured_copy_GBps"] = cp["copy_GBps"]
+        result["roofline"]["frac_of_measured_copy"] = achieved_gbs / cp["copy_GBps"]
+        result["extras"]["copy"] = cp
     if not args.no_extras and args.workload == "train_bf16":
         print("[bench] extras: backward, segment split ...", file=sys.stderr, flush=True)
         result["extras"].update(extra_measurements(gdn, generate, WORKLOADS, dev, args.steps,

@@ -47,7 +47,7 @@ GDN_PASS_KDA_FWD = 4
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
             "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue",
-            "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc")
+            "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_device_copy")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -111,6 +111,8 @@ def load():
     lib.gdn_kda_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_device_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.gdn_device_copy.restype = ctypes.c_int
     _lib = lib
     return lib
 

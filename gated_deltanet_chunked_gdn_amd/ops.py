@@ -383,3 +383,18 @@ def epilogue(o, z, weight=None, eps: float = 1e-6):
                           _stream(o.device))
     nat.check(st, "gdn_epilogue")
     return y
+
+
+def device_copy(dst, src):
+    """gdn_device_copy: copy src into dst (same byte size, device tensors) with the
+    library's copy kernel, the HBM roofline calibration."""
+    lib = nat.load()
+    for name, t in (("dst", dst), ("src", src)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _on_device(dst, src.device, "dst")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("dst and src must have the same size in bytes")
+    nat.check(lib.gdn_device_copy(_ptr(dst), _ptr(src), n, _stream(src.device)), "gdn_device_copy")
+    return dst

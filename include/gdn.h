@@ -298,6 +298,15 @@ gdn_status gdn_prologue(const gdn_problem* problem, const void* q, const void* k
 gdn_status gdn_epilogue(const gdn_problem* problem, const void* o, const void* z, const float* weight,
                         float eps, void* y, void* stream);
 
+/* Measurement helper, not part of the operator: copies `bytes` bytes of device
+ * memory from src to dst (16-byte vectors, non-temporal, grid-strided), the copy
+ * that calibrates the HBM roofline the chunked kernels are measured against
+ * ("Research Sprint Day 2 - Rooflines", section "Rooflines": the bandwidth of a
+ * large copy, bytes read plus bytes written).  dst, src and bytes must be
+ * multiples of 16 (GDN_ERR_ALIGN), the ranges must not overlap (GDN_ERR_ALIAS);
+ * asynchronous on `stream`. */
+gdn_status gdn_device_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -322,3 +322,13 @@ def test_noalloc_entry_checks_before_any_launch():
     assert call(problem(), q=None) == nat.GDN_ERR_NULL
     assert call(problem(num_segments=3)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
+
+
+def test_device_copy_checks():
+    P = ctypes.c_void_p
+    lib = nat.load()
+    assert lib.gdn_device_copy(None, P(FAKE), 64, None) == nat.GDN_ERR_NULL
+    assert lib.gdn_device_copy(P(FAKE + (1 << 30)), P(FAKE), 60, None) == nat.GDN_ERR_ALIGN
+    assert lib.gdn_device_copy(P(FAKE + 8), P(FAKE + (1 << 30)), 64, None) == nat.GDN_ERR_ALIGN
+    assert lib.gdn_device_copy(P(FAKE + 32), P(FAKE), 64, None) == nat.GDN_ERR_ALIAS
+    assert lib.gdn_device_copy(P(FAKE), P(FAKE), 0, None) == nat.GDN_OK   # nothing to do
