@@ -29,10 +29,11 @@
 //     stages, and writes dq, dk, dv, dg, dbeta.  Per-token sums are taken per
 //     wave and added in a fixed order, so the results are deterministic.
 //
-// Every product is a 16x16-block MFMA product whose operands are read from LDS
-// with the reduction index contiguous; a block is computed either as X or as
-// X^T so that its store to LDS or HBM is contiguous along the 4 accumulator
-// rows of a lane.  Precision as in the forward: bf16 io -> bf16 MFMA operands,
+// Every product is a 16x16-block MFMA product whose operands are read from LDS,
+// either with the reduction index contiguous or, for an operand stored the other
+// way round, with transposing reads (ds_read_b64_tr_b16), so each tile is staged
+// in one orientation only; a block is computed either as X or as X^T so that its
+// store to LDS or HBM is contiguous along the 4 accumulator rows of a lane.  Precision as in the forward: bf16 io -> bf16 MFMA operands,
 // fp32 accumulation, fp32 states, decays, sums and dS; fp32 io -> fp32 MFMA.
 #include <type_traits>
 
@@ -54,17 +55,7 @@ __device__ __forceinline__ void st16(E* p, const u32x4_t& v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
-// Element e of a 16-byte vector, as stored / widened to fp32.
-template <typename E>
-__device__ __forceinline__ E raw_elem(const u32x4_t& v, int e);
-template <>
-__device__ __forceinline__ uint16_t raw_elem<uint16_t>(const u32x4_t& v, int e) {
-  return static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
-}
-template <>
-__device__ __forceinline__ float raw_elem<float>(const u32x4_t& v, int e) {
-  return __uint_as_float(v[e]);
-}
+// Element e of a 16-byte vector, widened to fp32.
 template <typename E>
 __device__ __forceinline__ float wide_elem(const u32x4_t& v, int e);
 template <>
@@ -81,12 +72,6 @@ __device__ __forceinline__ float wide_elem<float>(const u32x4_t& v, int e) {
 template <typename E>
 __device__ __forceinline__ void store_t(E* dst, int ld, const f32x4_t& c, int lane) {
   store4<E>(dst + (lane & 15) * ld + 4 * (lane >> 4), c[0], c[1], c[2], c[3]);
-}
-// ... and as is, dst[(4 (lane/16) + r) * ld + lane % 16] (four scalar stores).
-template <typename E, typename Op>
-__device__ __forceinline__ void store_n(E* dst, int ld, const f32x4_t& c, int lane) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dst[(4 * (lane >> 4) + r) * ld + (lane & 15)] = Op::cvt(c[r]);
 }
 
 // Sum over the four 16-lane groups: lanes l, l+16, l+32, l+48 all end with the total.
@@ -389,8 +374,9 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 // ===================================================================================
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// LDS plan (element offsets; E = io element type).  Persistent: K rows, T (its
-// transpose, and those of V, dOs, S and dS, are read with transposing LDS reads).
+// LDS plan (element offsets; E = io element type).  Persistent: K rows, T.  Every
+// transposed operand (of K, Q, T, V, dOs, S, dS, dE, dW, dQK and dKK) is read with
+// transposing LDS reads from the one stored orientation.
 // Region U is reused: first the pre-chunk products and the d_v tiles, then the
 // 64 x 64 / 64 x d_k stages.
 template <int DK, typename Op>
@@ -399,19 +385,17 @@ struct GradLayout {
   static constexpr int DVT = sizeof(E) == 2 ? 32 : 16;  // d_v tile (one bf16 MFMA depth)
   static constexpr int PADE = sizeof(E) == 2 ? 8 : 4;
   static constexpr int LDK = DK + PADE, LDC = 64 + PADE, LDV = DVT + PADE;
-  static constexpr int nK = 64 * LDK, nC = 64 * LDC, nKT = DK * LDC, nV = 64 * LDV;
-  static constexpr int nVT = DVT * LDC, nS = DK * LDV, nST = DVT * LDK;
+  static constexpr int nK = 64 * LDK, nC = 64 * LDC, nV = 64 * LDV, nS = DK * LDV;
   static constexpr int oKs = 0, oTm = oKs + nK, oU = oTm + nC;
   // pre-chunk and d_v tiles
   static constexpr int aWn = 0, aPt = aWn + nK, aTile = aPt + nC;
   static constexpr int aQs = aTile, aPreEnd = aQs + nK;
   static constexpr int aVr = aTile, aSr = aVr + nV, adSr = aSr + nS, adOr = adSr + nS;
-  static constexpr int aEr = adOr + nV, adEr = aEr + nV, adEt = adEr + nV, aEnd = adEt + nVT;
-  // 64 x 64 and 64 x d_k stages
-  static constexpr int bQKr = 0, bQKt = bQKr + nC, bWt = bQKt + nC, bWr = bWt + nKT;
-  static constexpr int bTb = bWr + nK, bXt = bTb + nC, bEnd1 = bXt + nC;
-  static constexpr int bKtmp = bWr, bKKs = bWt, bQt = bWr, bKt2 = bQt + nKT, bEnd2 = bKt2 + nKT;
-  static constexpr int nU = cmax(cmax(aEnd, aPreEnd), cmax(bEnd1, bEnd2));
+  static constexpr int aEr = adOr + nV, adEr = aEr + nV, aEnd = adEr + nV;
+  // 64 x 64 and 64 x d_k stages: dQK^T, dKK^T, dW rows (then Q rows), dT^T, X^T
+  static constexpr int bQKt = 0, bKKt = bQKt + nC, bWr = bKKt + nC, bQr = bWr;
+  static constexpr int bTb = bWr + nK, bXt = bTb + nC, bEnd = bXt + nC;
+  static constexpr int nU = cmax(cmax(aEnd, aPreEnd), bEnd);
   static constexpr int nElem = oU + nU;
   static constexpr int fOff = (nElem * static_cast<int>(sizeof(E)) + 15) / 16 * 16;
   // fp32 arrays: gam, Gam, dec, bet, bg [64]; pb, pg [8][64]; pn, sdot [8]
@@ -580,7 +564,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   E* const dOr = U + GL::adOr;
   E* const Er = U + GL::aEr;
   E* const dEr = U + GL::adEr;
-  E* const dEt = U + GL::adEt;
   auto stage_tile = [&](const TileLd& L, int v0) {
 #pragma unroll
     for (int ix = 0; ix < NVX; ++ix) {
@@ -627,7 +610,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
         de = Op::mma(Op::frag_tr(dOr + 16 * bdv, LDV, lane, ks * KS),
                      Op::frag(Pt + 16 * bt * LDC, LDC, lane, ks * KS), de);
       store_t<E>(dEr + 16 * bt * LDV + 16 * bdv, LDV, de, lane);
-      store_n<E, Op>(dEt + 16 * bdv * LDC + 16 * bt, LDC, de, lane);
     }
     __syncthreads();
     // accumulate the d_v reductions
@@ -651,7 +633,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       const int bdv = w >> 2, bt = w & 3;
       f32x4_t acc = zero4();
       for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag(dEt + 16 * bdv * LDC, LDC, lane, ks * KS),
+        acc = Op::mma(Op::frag_tr(dEr + 16 * bdv, LDV, lane, ks * KS),
                       Op::frag_tr(Tm + 16 * bt, LDC, lane, ks * KS), acc);
       const int t = 16 * bt + (lane & 15), cl = 16 * bdv + 4 * (lane >> 4);
       const float bt_ = bet[t];
@@ -670,28 +652,36 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   if (lane == 0) sdot[w] = sdot_acc;
 
   // ---------------- 64 x 64 and 64 x d_k stages ----------------
-  E* const dQKr = U + GL::bQKr;
   E* const dQKt = U + GL::bQKt;
-  E* const dWt = U + GL::bWt;
+  E* const dKKt = U + GL::bKKt;
   E* const dWr = U + GL::bWr;
+  E* const Qr = U + GL::bQr;
   E* const dTb = U + GL::bTb;
   E* const Xt = U + GL::bXt;
-  // dW (rows and transposed); dQK = dP o D (rows and transposed); dD = dP o QK
+  // Q rows for the last stage (its operand Q^T, read transposed), loaded now and
+  // staged once dW is no longer needed; rows past the chunk's end load its last
+  // row and are stored as zeros.
+  constexpr int NQV = 64 * (DK / EPV) / 512;
+  u32x4_t qpre[NQV];
+#pragma unroll
+  for (int i = 0; i < NQV; ++i) {
+    const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+    qpre[i] = ld16(q + ((row0 + (t < nv ? t : nv - 1)) * H + h) * DK + cv);
+  }
+  // dW rows; dQK = dP o D (stored transposed); dD = dP o QK
   f32x4_t dD[2];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
-    const f32x4_t dw = -dWT[s];  // dW^T block (a, b)
-    store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, dw, lane);
-    store_n<E, Op>(dWt + 16 * a * LDC + 16 * b, LDC, dw, lane);
+    store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, -dWT[s], lane);  // dW^T block (a, b)
   }
   for (int x = tid; x < 64 * 64; x += 512) {  // zero the blocks no owner writes
     const int r = x >> 6, cc = x & 63;
-    if ((cc >> 4) > (r >> 4)) {
-      dQKr[r * LDC + cc] = Op::cvt(0.f);
-      dTb[r * LDC + cc] = Op::cvt(0.f);
+    if ((cc >> 4) > (r >> 4)) dTb[r * LDC + cc] = Op::cvt(0.f);
+    if ((cc >> 4) < (r >> 4)) {
+      dQKt[r * LDC + cc] = Op::cvt(0.f);
+      dKKt[r * LDC + cc] = Op::cvt(0.f);
     }
-    if ((cc >> 4) < (r >> 4)) dQKt[r * LDC + cc] = Op::cvt(0.f);
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -707,7 +697,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
         dqk[r] = dP[s][r] * d;
         dD[s][r] = on ? dP[s][r] * QKr[s][r] : 0.f;
       }
-      store_n<E, Op>(dQKr + 16 * bi * LDC + 16 * bj, LDC, dqk, lane);
       store_t<E>(dQKt + 16 * bj * LDC + 16 * bi, LDC, dqk, lane);
     }
   }
@@ -728,7 +717,8 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  // X = dT T^T (all 16 blocks, two per wave), stored transposed
+  // X = dT T^T (all 16 blocks, two per wave), stored transposed.
+  // dKb^T = dW^T T (the last use of dW; kept in registers for the final stage).
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
@@ -739,22 +729,23 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
                     Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
     store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
   }
-  __syncthreads();
-  // dA = strict_lower(-T^T X); dbeta, dKK, dD; dDD row and column sums.
-  // dKb^T = dW^T T (kept in registers for the final stage).
-  E* const dKtmp = U + GL::bKtmp;
   f32x4_t dKbT[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
     dKbT[s] = zero4();
     for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
-      dKbT[s] = Op::mma(Op::frag(dWt + 16 * a * LDC, LDC, lane, ks * KS),
+      dKbT[s] = Op::mma(Op::frag_tr(dWr + 16 * a, LDK, lane, ks * KS),
                         Op::frag_tr(Tm + 16 * b, LDC, lane, ks * KS), dKbT[s]);
   }
-  for (int x = tid; x < 64 * 64; x += 512) {
-    const int r = x >> 6, cc = x & 63;
-    if ((cc >> 4) > (r >> 4)) dKtmp[r * LDC + cc] = Op::cvt(0.f);
+  __syncthreads();
+  // dA = strict_lower(-T^T X); dbeta, dKK (stored transposed), dD; dDD row and
+  // column sums.  The Q rows go where dW was.
+#pragma unroll
+  for (int i = 0; i < NQV; ++i) {
+    const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    st16(Qr + t * LDK + cv, t < nv ? qpre[i] : z);
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -781,7 +772,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
         dD[s][r] = ddd;
         colp += ddd;
       }
-      store_n<E, Op>(dKtmp + 16 * bi * LDC + 16 * bj, LDC, dkk, lane);
+      store_t<E>(dKKt + 16 * bj * LDC + 16 * bi, LDC, dkk, lane);
       // row sums over the 16 lanes of a group; column sums over the four groups
       float rs[4], rd[4];
 #pragma unroll
@@ -801,26 +792,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  E* const dKKs = U + GL::bKKs;
-  for (int x = tid; x < 64 * 64; x += 512) {
-    const int r = x >> 6, cc = x & 63;
-    dKKs[r * LDC + cc] = Op::cvt(Op::widen(dKtmp[r * LDC + cc]) + Op::widen(dKtmp[cc * LDC + r]));
-  }
-  __syncthreads();
-  E* const Qt = U + GL::bQt;
-  E* const Kt2 = U + GL::bKt2;
-  for (int x = tid; x < 64 * (DK / EPV); x += 512) {
-    const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-    u32x4_t qv = {0u, 0u, 0u, 0u};
-    if (t < nv) qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
-    const u32x4_t kv = ld16(Ks + t * LDK + cv);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      Qt[(cv + e) * LDC + t] = raw_elem<E>(qv, e);
-      Kt2[(cv + e) * LDC + t] = raw_elem<E>(kv, e);
-    }
-  }
-  __syncthreads();
   // dq^T, dk^T blocks (a: d_k, b: tokens) and the per-token terms they carry
   float pn_acc = 0.f;
 #pragma unroll
@@ -831,23 +802,27 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     const f32x4_t q6 = dQ6T[s] * Gam[t];
     f32x4_t dqa = q6;
     for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
-      dqa = Op::mma(Op::frag(Kt2 + 16 * a * LDC, LDC, lane, ks * KS),
-                    Op::frag(dQKr + 16 * b * LDC, LDC, lane, ks * KS), dqa);
-    // dk^T = decay o dK~^T + Q^T dQK + K^T (dKK + dKK^T) + (beta Gamma) o dKb^T
+      dqa = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                    Op::frag_tr(dQKt + 16 * b, LDC, lane, ks * KS), dqa);
+    // dk^T = decay o dK~^T + Q^T dQK + K^T (dKK + dKK^T) + (beta Gamma) o dKb^T;
+    // dKK is strictly lower, so only token blocks >= b of dKK and <= b of dKK^T
+    // reach column block b
     f32x4_t dka = zero4();
     for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
-      dka = Op::mma(Op::frag(Qt + 16 * a * LDC, LDC, lane, ks * KS),
+      dka = Op::mma(Op::frag_tr(Qr + 16 * a, LDK, lane, ks * KS),
                     Op::frag(dQKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
-#pragma unroll
-    for (int ks = 0; ks < 64 / KS; ++ks)
-      dka = Op::mma(Op::frag(Kt2 + 16 * a * LDC, LDC, lane, ks * KS),
-                    Op::frag(dKKs + 16 * b * LDC, LDC, lane, ks * KS), dka);
+    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+      dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                    Op::frag(dKKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
+    for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
+      dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                    Op::frag_tr(dKKt + 16 * b, LDC, lane, ks * KS), dka);
     const float dct = dec[t], bgt = bg[t];
     float qd = 0.f, rk = 0.f, tj = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float kv = Op::widen(Ks[t * LDK + d0 + r]);
-      qd += Op::widen(Qt[(d0 + r) * LDC + t]) * q6[r];
+      qd += Op::widen(Qr[t * LDK + d0 + r]) * q6[r];
       rk += dKbT[s][r] * kv;
       tj += dKtT[s][r] * dct * kv;
       dka[r] += dct * dKtT[s][r] + bgt * dKbT[s][r];

@@ -95,8 +95,12 @@ struct ChainSmem {
   alignas(16) f32x4_t zx[2][4][64];             // partial Z of each state wave
 };
 
+// At d_k = 64 the register budget is held to 128 so that two workgroups share a
+// CU (grids of many heads run several workgroups per CU); at d_k = 128 the chain
+// needs ~170 registers and the train shapes run one workgroup per CU anyway.
 template <int DK, bool STATES, bool OUT>
-__global__ __launch_bounds__(384) void chunk_chain_kernel(FwdParams p) {
+__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 4 : 1))) void chunk_chain_kernel(
+    FwdParams p) {
   using SM = ChainSmem<DK>;
   constexpr int LDV = SM::LDV;
   constexpr int NKS = DK / 32;  // reduction steps over d_k
