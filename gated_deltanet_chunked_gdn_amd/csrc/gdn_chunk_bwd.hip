@@ -403,8 +403,13 @@ struct GradLayout {
   static constexpr size_t bytes = static_cast<size_t>(fOff) + nFloat * 4;
 };
 
+// With bf16 operands at d_k = 64 the kernel is held to 128 registers so that two
+// workgroups share a CU (a few registers spill; measured faster than one
+// workgroup per CU without spills).
 template <int DK, typename Op>
-__global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 4 : 1))) void chunk_grad_kernel(
+    BwdParams p) {
   using E = typename Op::elem;
   using GL = GradLayout<DK, Op>;
   constexpr int LDK = GL::LDK, LDC = GL::LDC, LDV = GL::LDV, DVT = GL::DVT, KS = Op::KSTEP;
@@ -529,23 +534,20 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   int lbi[2], lbj[2];
   lower_block(w, lbi[0], lbj[0]);
   lower_block(w < 2 ? 8 + w : w, lbi[1], lbj[1]);
-  f32x4_t QKr[2], KKr[2];
-  {
+  {  // P = lower_incl(QK o D) -> P^T (QK and KK are formed again for the last stages,
+     // rather than held in registers across the d_v tiles)
     const E* Qs = U + GL::aQs;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      QKr[s] = zero4();
-      KKr[s] = zero4();
       if (s < nlow) {
         const int bi = lbi[s], bj = lbj[s];
-        tile_mma<Op, DK>(QKr[s], Qs + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-        tile_mma<Op, DK>(KKr[s], Ks + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-        // P = lower_incl(QK o D) -> P^T
+        f32x4_t qk = zero4();
+        tile_mma<Op, DK>(qk, Qs + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
         const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pv[r] = i0 + r >= j ? QKr[s][r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
+          pv[r] = i0 + r >= j ? qk[r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
         store4<E>(Pt + j * LDC + i0, pv[0], pv[1], pv[2], pv[3]);
       }
     }
@@ -668,8 +670,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
     const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
     qpre[i] = ld16(q + ((row0 + (t < nv ? t : nv - 1)) * H + h) * DK + cv);
   }
-  // dW rows; dQK = dP o D (stored transposed); dD = dP o QK
-  f32x4_t dD[2];
+  // dW rows; dQK = dP o D (stored transposed)
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
@@ -685,23 +686,19 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    dD[s] = zero4();
     if (s < nlow) {
       const int bi = lbi[s], bj = lbj[s];
       const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
       f32x4_t dqk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool on = i0 + r >= j;
-        const float d = on ? exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
-        dqk[r] = dP[s][r] * d;
-        dD[s][r] = on ? dP[s][r] * QKr[s][r] : 0.f;
-      }
+      for (int r = 0; r < 4; ++r)
+        dqk[r] = i0 + r >= j ? dP[s][r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
       store_t<E>(dQKt + 16 * bj * LDC + 16 * bi, LDC, dqk, lane);
     }
   }
   __syncthreads();
-  // dT^T = diag(beta) dT1^T + diag(beta Gamma) (K dW^T), strictly lower part of dT
+  // dT^T = diag(beta) dT1^T + diag(beta Gamma) (K dW^T), strictly lower part of dT.
+  // dKb^T = dW^T T (the last use of dW; kept in registers for the final stage).
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     if (s < nlow) {
@@ -716,19 +713,6 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
       store_t<E>(dTb + 16 * bi * LDC + 16 * bj, LDC, dt, lane);
     }
   }
-  __syncthreads();
-  // X = dT T^T (all 16 blocks, two per wave), stored transposed.
-  // dKb^T = dW^T T (the last use of dW; kept in registers for the final stage).
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
-    f32x4_t acc = zero4();
-    const int kb = bk < bj ? bk : bj;
-    for (int ks = 0; ks < (16 * (kb + 1) + KS - 1) / KS; ++ks)
-      acc = Op::mma(Op::frag(dTb + 16 * bk * LDC, LDC, lane, ks * KS),
-                    Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
-    store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
-  }
   f32x4_t dKbT[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
@@ -739,24 +723,40 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
                         Op::frag_tr(Tm + 16 * b, LDC, lane, ks * KS), dKbT[s]);
   }
   __syncthreads();
-  // dA = strict_lower(-T^T X); dbeta, dKK (stored transposed), dD; dDD row and
-  // column sums.  The Q rows go where dW was.
+  // X = dT T^T (all 16 blocks, two per wave), stored transposed.  The Q rows go
+  // where dW was.
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
+    f32x4_t acc = zero4();
+    const int kb = bk < bj ? bk : bj;
+    for (int ks = 0; ks < (16 * (kb + 1) + KS - 1) / KS; ++ks)
+      acc = Op::mma(Op::frag(dTb + 16 * bk * LDC, LDC, lane, ks * KS),
+                    Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
+    store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
+  }
 #pragma unroll
   for (int i = 0; i < NQV; ++i) {
     const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
     const u32x4_t z = {0u, 0u, 0u, 0u};
     st16(Qr + t * LDK + cv, t < nv ? qpre[i] : z);
   }
+  __syncthreads();
+  // dA = strict_lower(-T^T X); QK and KK formed again; dbeta, dKK (stored
+  // transposed), dD = dP o QK; dDD row and column sums.
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     if (s < nlow) {
       const int bi = lbi[s], bj = lbj[s];
+      f32x4_t qk = zero4(), kkb = zero4();
+      tile_mma<Op, DK>(qk, Qr + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+      tile_mma<Op, DK>(kkb, Ks + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
       f32x4_t acc = zero4();
       for (int ks = (16 * bi) / KS; ks < 64 / KS; ++ks)
         acc = Op::mma(Op::frag_tr(Tm + 16 * bi, LDC, lane, ks * KS),
                       Op::frag(Xt + 16 * bj * LDC, LDC, lane, ks * KS), acc);
       const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
-      f32x4_t dkk;
+      f32x4_t dkk, dd;
       float rows[4], colp = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -765,12 +765,12 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
         const float d = i >= j ? exp2f(fminf(gam[i] - gam[j], 0.f)) : 0.f;
         const float da = lo ? -acc[r] : 0.f;
         const float b_i = bet[i];
-        const float kk = KKr[s][r];
+        const float kk = kkb[r];
         rows[r] = da * kk * d;                 // dbeta_i
         dkk[r] = da * b_i * d;                 // dKK
-        const float ddd = (dD[s][r] + da * b_i * kk) * d;  // dD o D
-        dD[s][r] = ddd;
-        colp += ddd;
+        const float dd0 = i >= j ? dP[s][r] * qk[r] : 0.f;  // dD = dP o QK
+        dd[r] = (dd0 + da * b_i * kk) * d;     // dD o D
+        colp += dd[r];
       }
       store_t<E>(dKKt + 16 * bj * LDC + 16 * bi, LDC, dkk, lane);
       // row sums over the 16 lanes of a group; column sums over the four groups
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(512) void chunk_grad_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         rs[r] = sum_in_group(rows[r]);
-        rd[r] = sum_in_group(dD[s][r]);
+        rd[r] = sum_in_group(dd[r]);
       }
       colp = sum_groups(colp);
       if ((lane & 15) == 0) {
