@@ -149,10 +149,10 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
-    // T (64 x 64), T diag(beta) (packed) and the decays per (chunk slot, head),
-    // then the fp32 state before and the state gradient after every chunk,
-    // [slot][H][Dk][Dv] each
-    return t_slot_bytes(p, c) + packed_slot_bytes(p, c) + gate_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
+    // T (64 x 64), T diag(beta) (packed), the decays and P (64 x 64) per (chunk
+    // slot, head), then the fp32 state before and the state gradient after every
+    // chunk, [slot][H][Dk][Dv] each
+    return 2 * t_slot_bytes(p, c) + packed_slot_bytes(p, c) + gate_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
   }
   return 0;
 }
@@ -335,12 +335,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
   char* const wsb = static_cast<char*>(workspace);
   const size_t tb = t_slot_bytes(p, c);
   const size_t pb = packed_slot_bytes(p, c);
-  float* states = reinterpret_cast<float*>(wsb + tb + pb + gate_slot_bytes(p, c));
+  char* const prws = wsb + tb + pb + gate_slot_bytes(p, c);
+  float* states = reinterpret_cast<float*>(prws + tb);
   float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + state_slot_bytes(p, c));
   gdn::FwdParams fp{};
   fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0;
   fp.tws = wsb; fp.tbws = wsb + tb; fp.pws = nullptr;
   fp.gws = reinterpret_cast<float*>(wsb + tb + pb);
+  fp.prws = prws;
   fp.states = states; fp.seq = seq_info(p);
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
@@ -351,7 +353,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
   gdn::BwdParams bp{};
   bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
   bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
-  bp.tws = workspace; bp.states = states; bp.dstates = dstates; bp.seq = seq_info(p);
+  bp.tws = workspace; bp.prws = prws; bp.states = states; bp.dstates = dstates; bp.seq = seq_info(p);
   bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv; bp.max_chunks = fp.max_chunks; bp.scale = p->scale;
   return hip_status(gdn::launch_chunk_bwd(bp, p->Dk, c.bf16, s));
 }

@@ -131,7 +131,7 @@ struct DStateSmem {
   E Ks[64 * LDK];   // K rows
   E Qs[64 * LDK];   // Q rows
   E Tm[64 * LDC];   // T rows
-  E Pt[64 * LDC];   // P^T
+  E Pr[64 * LDC];   // P rows (from the preparation kernel)
   E dB[16 * LDB];   // [ dOs^T | dE^T ] of this tile
   E dU[16 * LDB];   // [ (diag(Gamma) dOs)^T | (-diag(beta Gamma) T^T dE)^T ] of this tile
   E dSt[16 * LDK];  // dS^T of this tile
@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   const E* __restrict__ q = static_cast<const E*>(p.q);
   const E* __restrict__ k = static_cast<const E*>(p.k);
   const E* __restrict__ dO = static_cast<const E*>(p.dO);
+  const E* __restrict__ prw = static_cast<const E*>(p.prws);
   const E* __restrict__ tws = static_cast<const E*>(p.tws);
 
   const int H = p.H, Dv = p.Dv, NT = Dv / 16;
@@ -164,11 +165,6 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t nhS = (static_cast<int64_t>(n) * H + h) * DK;
 
-  // P^T: blocks below the diagonal stay zero
-  for (int x = tid; x < 64 * LDC; x += 256) {
-    const int r = x / LDC, c = x % LDC;
-    if ((c >> 4) < (r >> 4)) sm.Pt[x] = Op::cvt(0.f);
-  }
   f32x4_t dS[SRB];
 #pragma unroll
   for (int sr = 0; sr < SRB; ++sr) {
@@ -189,7 +185,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   // branch around a load, or a select right after it, would make the wave wait
   // for every load in flight at that point.
   struct Pre {
-    u32x4_t kv[NSV], qv[NSV], tv[NTV];
+    u32x4_t kv[NSV], qv[NSV], tv[NTV], pv[NTV];
     u32x4_t dor;  // four dO values of row tid / 4 (raw io elements)
     float gv, bv;
     int nv;
@@ -206,10 +202,12 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       pr.qv[i] = ld16(q + ((row0 + tt) * H + h) * DK + cv);
     }
     const E* T = tws + ((slot0 + c) * H + h) * 4096;
+    const E* P = prw + ((slot0 + c) * H + h) * 4096;
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
       const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
       pr.tv[i] = ld16(T + t * 64 + cv);
+      pr.pv[i] = ld16(P + t * 64 + cv);
     }
     {
       const int t = tid >> 2, cq = (tid & 3) * 4;
@@ -239,6 +237,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     for (int i = 0; i < NTV; ++i) {
       const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
       st16(sm.Tm + t * LDC + cv, pr.tv[i]);
+      st16(sm.Pr + t * LDC + cv, pr.pv[i]);
     }
     // gamma by an in-register scan (log2 units), in every wave; wave 0 stores it
     // (padded rows: g = 0, beta = 0)
@@ -285,34 +284,9 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = dS[sr][r];
       }
     }
-    // ---- stage K, Q (rows), T, dOs^T of this tile and the gates; load chunk c - 1 ----
+    // ---- stage K, Q, T, P (rows), dOs^T of this tile and the gates; load chunk c - 1 ----
     stage_pre(pre);
     if (c > 0) load_pre(pre, c - 1);
-    __syncthreads();
-
-    // ---- P^T ----
-    {
-      auto pblock = [&](int bi, int bt) {  // P[16 bi + .][16 bt + .] -> P^T
-        f32x4_t acc = zero4();
-        tile_mma<Op, DK>(acc, sm.Qs + 16 * bi * LDK, LDK, sm.Ks + 16 * bt * LDK, LDK, lane);
-        const int t = 16 * bt + (lane & 15), ib = 16 * bi + 4 * (lane >> 4);
-        const float gt = sm.gam[t];
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          pv[r] = ib + r >= t ? acc[r] * exp2f(fminf(sm.gam[ib + r] - gt, 0.f)) : 0.f;
-        store4<E>(sm.Pt + t * LDC + ib, pv[0], pv[1], pv[2], pv[3]);
-      };
-      if (w == 0) {
-        pblock(0, 0); pblock(1, 0); pblock(1, 1);
-      } else if (w == 1) {
-        pblock(2, 0); pblock(2, 1); pblock(2, 2);
-      } else if (w == 2) {
-        pblock(3, 0); pblock(3, 1);
-      } else {
-        pblock(3, 2); pblock(3, 3);
-      }
-    }
     __syncthreads();
 
     // ---- dE = diag(decay) K dS + P^T dOs, token block w ----
@@ -322,7 +296,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= sm.dec[16 * w + 4 * (lane >> 4) + r];
       for (int ks = (16 * w) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag(sm.Pt + 16 * w * LDC, LDC, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
+        acc = Op::mma(Op::frag_tr(sm.Pr + 16 * w, LDC, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
       store_t<E>(sm.dB + 64 + 16 * w, LDB, acc, lane);
     }
     __syncthreads();
@@ -388,14 +362,13 @@ struct GradLayout {
   static constexpr int nK = 64 * LDK, nC = 64 * LDC, nV = 64 * LDV, nS = DK * LDV;
   static constexpr int oKs = 0, oTm = oKs + nK, oU = oTm + nC;
   // pre-chunk and d_v tiles
-  static constexpr int aWn = 0, aPt = aWn + nK, aTile = aPt + nC;
-  static constexpr int aQs = aTile, aPreEnd = aQs + nK;
+  static constexpr int aWn = 0, aPr = aWn + nK, aTile = aPr + nC;
   static constexpr int aVr = aTile, aSr = aVr + nV, adSr = aSr + nS, adOr = adSr + nS;
   static constexpr int aEr = adOr + nV, adEr = aEr + nV, aEnd = adEr + nV;
   // 64 x 64 and 64 x d_k stages: dQK^T, dKK^T, dW rows (then Q rows), dT^T, X^T
   static constexpr int bQKt = 0, bKKt = bQKt + nC, bWr = bKKt + nC, bQr = bWr;
   static constexpr int bTb = bWr + nK, bXt = bTb + nC, bEnd = bXt + nC;
-  static constexpr int nU = cmax(cmax(aEnd, aPreEnd), bEnd);
+  static constexpr int nU = cmax(aEnd, bEnd);
   static constexpr int nElem = oU + nU;
   static constexpr int fOff = (nElem * static_cast<int>(sizeof(E)) + 15) / 16 * 16;
   // fp32 arrays: gam, Gam, dec, bet, bg [64]; pb, pg [8][64]; pn, sdot [8]
@@ -436,6 +409,7 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   const E* __restrict__ k = static_cast<const E*>(p.k);
   const E* __restrict__ v = static_cast<const E*>(p.v);
   const E* __restrict__ dO = static_cast<const E*>(p.dO);
+  const E* __restrict__ prw = static_cast<const E*>(p.prws);
   const E* __restrict__ tws = static_cast<const E*>(p.tws);
   E* __restrict__ dq = static_cast<E*>(p.dq);
   E* __restrict__ dk = static_cast<E*>(p.dk);
@@ -486,32 +460,23 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
     }
   };
 
-  // ---------------- stage K, Q, K^T, T, T^T; gates ----------------
+  // ---------------- stage K, T, P (rows); gates ----------------
   E* const Wn = U + GL::aWn;
-  E* const Pt = U + GL::aPt;
+  E* const Pr = U + GL::aPr;
   {
-    E* const Qs = U + GL::aQs;
     for (int x = tid; x < 64 * (DK / EPV); x += 512) {
       const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      u32x4_t kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-      if (t < nv) {
-        kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
-        qv = ld16(q + ((row0 + t) * H + h) * DK + cv);
-      }
+      u32x4_t kv = {0u, 0u, 0u, 0u};
+      if (t < nv) kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
       st16(Ks + t * LDK + cv, kv);
-      st16(Qs + t * LDK + cv, qv);
-
     }
     const E* T = tws + (slot * H + h) * 4096;
+    const E* P = prw + (slot * H + h) * 4096;
     for (int x = tid; x < 64 * 64 / EPV; x += 512) {
       const int t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
-      const u32x4_t tv = ld16(T + t * 64 + cv);
+      const u32x4_t tv = ld16(T + t * 64 + cv), pv = ld16(P + t * 64 + cv);
       st16(Tm + t * LDC + cv, tv);
-
-    }
-    for (int x = tid; x < 64 * LDC; x += 512) {  // P^T: blocks below the diagonal are zero
-      const int r = x / LDC, cc = x % LDC;
-      if ((cc >> 4) < (r >> 4)) Pt[x] = Op::cvt(0.f);
+      st16(Pr + t * LDC + cv, pv);
     }
     for (int x = tid; x < 2 * 8 * 64 + 16; x += 512) pb[x] = 0.f;  // pb, pg, pn, sdot
     if (w == 0) stage_gates<DK, Op>(p, row0, nv, h, lane, gam, Gam, dec, bet, bg);
@@ -534,24 +499,6 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   int lbi[2], lbj[2];
   lower_block(w, lbi[0], lbj[0]);
   lower_block(w < 2 ? 8 + w : w, lbi[1], lbj[1]);
-  {  // P = lower_incl(QK o D) -> P^T (QK and KK are formed again for the last stages,
-     // rather than held in registers across the d_v tiles)
-    const E* Qs = U + GL::aQs;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < nlow) {
-        const int bi = lbi[s], bj = lbj[s];
-        f32x4_t qk = zero4();
-        tile_mma<Op, DK>(qk, Qs + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-        const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          pv[r] = i0 + r >= j ? qk[r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
-        store4<E>(Pt + j * LDC + i0, pv[0], pv[1], pv[2], pv[3]);
-      }
-    }
-  }
   __syncthreads();
 
   // ---------------- d_v tiles ----------------
@@ -610,7 +557,7 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
       de = de * dc;
       for (int ks = (16 * bt) / KS; ks < 64 / KS; ++ks)
         de = Op::mma(Op::frag_tr(dOr + 16 * bdv, LDV, lane, ks * KS),
-                     Op::frag(Pt + 16 * bt * LDC, LDC, lane, ks * KS), de);
+                     Op::frag_tr(Pr + 16 * bt, LDC, lane, ks * KS), de);
       store_t<E>(dEr + 16 * bt * LDV + 16 * bdv, LDV, de, lane);
     }
     __syncthreads();

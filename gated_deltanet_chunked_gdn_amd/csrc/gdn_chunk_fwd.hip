@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   const int64_t slot = bos / 64 + n + c;
   const IO* __restrict__ k = static_cast<const IO*>(p.k);
   const IO* __restrict__ q = static_cast<const IO*>(p.q);
-  const bool want_p = p.pws != nullptr;
+  const bool want_p = p.pws != nullptr || p.prws != nullptr;
   // Each wave forms the A blocks of row block `wave` and the P blocks of row block
   // 3 - wave: five 16x16 blocks per wave.
   const int ai = wave, pi = 3 - wave;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
   // straight to the workspace in MFMA operand order: fragment (pi, ks) holds, in
   // lane 16 g + t, the KPL entries P[16 pi + t][ks KSTEP + g KPL ..], so that a
   // plain load of 64 consecutive lanes yields the operand (the blocks above the
-  // diagonal as zeros).
+  // diagonal as zeros); for the backward, row-major instead.
   {
     // K fragments of row block ai (the A operand of the A blocks), and the gates
     // each lane needs, read once
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
     const float gAr[4] = {gA.x, gA.y, gA.z, gA.w}, bAr[4] = {bA.x, bA.y, bA.z, bA.w};
     const float gP = sm.gam[16 * pi + lr];  // row i of P
     constexpr int NTS = 64 / KS, KPL = Op::KPL;
-    E* P = want_p ? static_cast<E*>(p.pws) + (slot * H + h) * 4096 + pi * NTS * 64 * KPL : nullptr;
+    E* P = p.pws ? static_cast<E*>(p.pws) + (slot * H + h) * 4096 + pi * NTS * 64 * KPL : nullptr;
+    E* Prow = p.prws ? static_cast<E*>(p.prws) + (slot * H + h) * 4096 : nullptr;
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
       if (!want_p && bj > ai) continue;
@@ -250,8 +251,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(FwdParams p) {
           const float x = acc[r] * __builtin_amdgcn_exp2f(fminf(gP - gjr[r], 0.f));
           pv[r] = jb + r <= i ? x : 0.f;
         }
+        // row-major for the backward (every block, zeros above the diagonal)
+        if (Prow) store4<E>(Prow + i * 64 + jb, pv[0], pv[1], pv[2], pv[3]);
         // (fragments entirely above the diagonal are never read and not stored)
-        if ((jb / KS) * KS < 16 * (pi + 1)) {
+        if (P && (jb / KS) * KS < 16 * (pi + 1)) {
           if constexpr (KPL == 8) {  // the four columns are consecutive entries of one lane
             store4<E>(P + ((jb / KS) * 64 + 16 * ((jb % KS) / KPL) + lr) * KPL + jb % KPL, pv[0], pv[1], pv[2], pv[3]);
           } else {

@@ -35,6 +35,8 @@ struct FwdParams {
   void* pws;        // per-chunk P = lower_incl((Q K^T) o D) in MFMA operand order (4096 io
                     // elements per slot: fragment (row block, k-step) of 64 lanes each), or nullptr
   float* gws;       // per-chunk Gamma and exp(gamma_n - gamma), [slot][H][128] fp32
+  void* prws;       // per-chunk P row-major for the backward (64 x 64 io elements per slot,
+                    // zeros above the diagonal), or nullptr
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;  // chunks of the longest sequence
@@ -95,6 +97,7 @@ struct BwdParams {
   float* dbeta;
   float* dS0;             // or nullptr (not wanted)
   const void* tws;        // T of every chunk slot (io element type, 64 x 64)
+  const void* prws;       // P of every chunk slot, row-major (io element type, 64 x 64)
   const float* states;    // S_c before every chunk, [slot][H][Dk][Dv]
   float* dstates;         // dS_{c+1} after every chunk, [slot][H][Dk][Dv]
   SeqInfo seq;

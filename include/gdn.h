@@ -196,9 +196,9 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* problem, const void* q, cons
  * "Results" tables plus the initial-state gradient).
  *   in : q, k, v, g, beta, S0 (NULL = zero), dO, dS_final (NULL = zero)
  *   out: dq, dk, dv (io dtype), dg, dbeta (fp32), dS0 (fp32; NULL = not wanted)
- * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD (T, T diag(beta) and
- * the decays of every chunk, and the fp32 state before and its gradient after
- * every chunk). */
+ * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD (T, T diag(beta), the
+ * decays and the causal score P of every chunk, and the fp32 state before and
+ * its gradient after every chunk). */
 gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,
                          const void* dO, const float* dS_final, void* dq, void* dk, void* dv,

@@ -194,14 +194,14 @@ def test_backward_entry_validates():
 
 
 def test_backward_workspace_size():
-    # T (64 x 64), the T diag(beta) record (3072 io elements) and the decays, each rounded up
-    # to 256 bytes, then fp32 states before and state gradients after every
-    # chunk slot; slots = rows // 64 + N + 1
+    # T (64 x 64), the T diag(beta) record (3072 io elements), the decays and P (64 x 64),
+    # each rounded up to 256 bytes, then fp32 states before and state gradients after
+    # every chunk slot; slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     st, n = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
     assert st == nat.GDN_OK
-    assert n == (up(slots * 3 * 4096 * 2) + up(slots * 3 * 3072 * 2) + up(slots * 3 * 128 * 4)
+    assert n == (2 * up(slots * 3 * 4096 * 2) + up(slots * 3 * 3072 * 2) + up(slots * 3 * 128 * 4)
                  + 2 * slots * 3 * 128 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
