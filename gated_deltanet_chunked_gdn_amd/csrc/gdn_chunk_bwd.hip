@@ -46,6 +46,13 @@ namespace {
 
 using namespace chunk;
 
+// 16-byte load through a buffer resource; offsets past its range read zeros.
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// An offset every buffer range check rejects.
+constexpr int kNoLoadB = 0x7ffffff0;
+
 template <typename E>
 __device__ __forceinline__ u32x4_t ld16(const E* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
@@ -437,26 +444,35 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
     float4 sv[NSX], dv[NSX];
   };
   TileLd tl;
+  // Buffer resources bounded to the chunk's valid rows and the state slots: rows
+  // past the chunk's end and columns past d_v read as zeros (and are never
+  // stored), with 32-bit offsets instead of per-lane 64-bit addresses.
+  const int rowb = ((nv - 1) * H * Dv + Dv) * static_cast<int>(sizeof(E));
+  const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, rowb);
+  const auto rdo = buffer_rsrc(dO + (row0 * H + h) * Dv, rowb);
+  const auto rdv = buffer_rsrc(dvo + (row0 * H + h) * Dv, rowb);
+  const auto rs = buffer_rsrc(Sg, DK * Dv * 4);
+  const int rowk = ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E));
+  const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rowk);
+  const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, rowk);
+  const auto rdq = buffer_rsrc(dq + (row0 * H + h) * DK, rowk);
+  const auto rdk = buffer_rsrc(dk + (row0 * H + h) * DK, rowk);
+  const auto rds = buffer_rsrc(dSg, DK * Dv * 4);
   auto load_tile = [&](TileLd& L, int v0) {
 #pragma unroll
     for (int ix = 0; ix < NVX; ++ix) {
       const int x = tid + 512 * ix, t = x / (DVT / EPV), cv = (x % (DVT / EPV)) * EPV;
-      L.vv[ix] = u32x4_t{0u, 0u, 0u, 0u};
-      L.ov[ix] = u32x4_t{0u, 0u, 0u, 0u};
-      if (x < 64 * (DVT / EPV) && t < nv && v0 + cv < Dv) {
-        L.vv[ix] = ld16(v + ((row0 + t) * H + h) * Dv + v0 + cv);
-        L.ov[ix] = ld16(dO + ((row0 + t) * H + h) * Dv + v0 + cv);
-      }
+      const int off = x < 64 * (DVT / EPV) && v0 + cv < Dv ? (t * H * Dv + v0 + cv) * static_cast<int>(sizeof(E))
+                                                             : kNoLoadB;
+      L.vv[ix] = bload16(rv, off);
+      L.ov[ix] = bload16(rdo, off);
     }
 #pragma unroll
     for (int ix = 0; ix < NSX; ++ix) {
       const int x = tid + 512 * ix, i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
-      L.sv[ix] = float4{0.f, 0.f, 0.f, 0.f};
-      L.dv[ix] = float4{0.f, 0.f, 0.f, 0.f};
-      if (x < DK * (DVT / 4) && v0 + cv < Dv) {
-        L.sv[ix] = *reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(i) * Dv + v0 + cv);
-        L.dv[ix] = *reinterpret_cast<const float4*>(dSg + static_cast<int64_t>(i) * Dv + v0 + cv);
-      }
+      const int off = x < DK * (DVT / 4) && v0 + cv < Dv ? (i * Dv + v0 + cv) * 4 : kNoLoadB;
+      L.sv[ix] = __builtin_bit_cast(float4, bload16(rs, off));
+      L.dv[ix] = __builtin_bit_cast(float4, bload16(rds, off));
     }
   };
 
@@ -466,8 +482,7 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   {
     for (int x = tid; x < 64 * (DK / EPV); x += 512) {
       const int t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      u32x4_t kv = {0u, 0u, 0u, 0u};
-      if (t < nv) kv = ld16(k + ((row0 + t) * H + h) * DK + cv);
+      const u32x4_t kv = bload16(rk, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
       st16(Ks + t * LDK + cv, kv);
     }
     const E* T = tws + (slot * H + h) * 4096;
@@ -591,9 +606,8 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
       for (int r = 0; r < 4; ++r) part += acc[r] * Op::widen(Vr[t * LDV + cl + r]);
       part = sum_groups(part);
       if (lane < 16) pb[w * 64 + t] += part;
-      if (t < nv && v0 + cl < Dv)
-        store4<E>(dvo + ((row0 + t) * H + h) * Dv + v0 + cl, bt_ * acc[0], bt_ * acc[1], bt_ * acc[2],
-                  bt_ * acc[3]);
+      buffer_store4<E>(rdv, v0 + cl < Dv ? (t * H * Dv + v0 + cl) * static_cast<int>(sizeof(E)) : kNoLoadB,
+                       bt_ * acc[0], bt_ * acc[1], bt_ * acc[2], bt_ * acc[3]);
     }
     __syncthreads();
   }
@@ -608,14 +622,13 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   E* const dTb = U + GL::bTb;
   E* const Xt = U + GL::bXt;
   // Q rows for the last stage (its operand Q^T, read transposed), loaded now and
-  // staged once dW is no longer needed; rows past the chunk's end load its last
-  // row and are stored as zeros.
+  // staged once dW is no longer needed (rows past the chunk's end read zeros).
   constexpr int NQV = 64 * (DK / EPV) / 512;
   u32x4_t qpre[NQV];
 #pragma unroll
   for (int i = 0; i < NQV; ++i) {
     const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-    qpre[i] = ld16(q + ((row0 + (t < nv ? t : nv - 1)) * H + h) * DK + cv);
+    qpre[i] = bload16(rq, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
   }
   // dW rows; dQK = dP o D (stored transposed)
 #pragma unroll
@@ -685,8 +698,7 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
 #pragma unroll
   for (int i = 0; i < NQV; ++i) {
     const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    st16(Qr + t * LDK + cv, t < nv ? qpre[i] : z);
+    st16(Qr + t * LDK + cv, qpre[i]);
   }
   __syncthreads();
   // dA = strict_lower(-T^T X); QK and KK formed again; dbeta, dKK (stored
@@ -782,9 +794,10 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
       pb[w * 64 + t] += Gam[t] * rk;
       pn_acc += tj;
     }
-    if (t < nv) {
-      store4<E>(dq + ((row0 + t) * H + h) * DK + d0, dqa[0], dqa[1], dqa[2], dqa[3]);
-      store4<E>(dk + ((row0 + t) * H + h) * DK + d0, dka[0], dka[1], dka[2], dka[3]);
+    {
+      const int off = (t * H * DK + d0) * static_cast<int>(sizeof(E));
+      buffer_store4<E>(rdq, off, dqa[0], dqa[1], dqa[2], dqa[3]);
+      buffer_store4<E>(rdk, off, dka[0], dka[1], dka[2], dka[3]);
     }
   }
   pn_acc = wave_sum(pn_acc);
