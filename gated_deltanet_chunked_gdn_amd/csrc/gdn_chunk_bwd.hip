@@ -142,7 +142,7 @@ struct DStateSmem {
   E dB[16 * LDB];   // [ dOs^T | dE^T ] of this tile
   E dU[16 * LDB];   // [ (diag(Gamma) dOs)^T | (-diag(beta Gamma) T^T dE)^T ] of this tile
   E dSt[16 * LDK];  // dS^T of this tile
-  float gam[64], Gam[64], dec[64], bg[64];
+  float Gam[64], dec[64], bg[64];
 };
 
 template <int DK, typename Op>
@@ -188,57 +188,59 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   // the next step: the load latency hides behind the products.
   constexpr int NSV = 64 * (DK / EPV) / 256;  // K (and Q) vectors per thread
   constexpr int NTV = 64 * 64 / EPV / 256;    // T vectors per thread
-  // Rows past the chunk's end load its last row and are zeroed when staged: a
-  // branch around a load, or a select right after it, would make the wave wait
-  // for every load in flight at that point.
+  // Loads go through buffer resources bounded to the chunk's valid rows, so rows
+  // past its end read as zeros without a branch or a select (either would make
+  // the wave wait for every load in flight at that point), and the lane offsets
+  // are 32-bit and the same for every chunk.
+  constexpr int ES = static_cast<int>(sizeof(E));
   struct Pre {
     u32x4_t kv[NSV], qv[NSV], tv[NTV], pv[NTV];
     u32x4_t dor;  // four dO values of row tid / 4 (raw io elements)
     float gv, bv;
-    int nv;
   };
   auto load_pre = [&](Pre& pr, int c) {
     const int64_t c0 = static_cast<int64_t>(c) * 64, row0 = bos + c0;
     const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
-    pr.nv = nv;
+    const int rowk = ((nv - 1) * H * DK + DK) * ES;
+    const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, rowk);
+    const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rowk);
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
       const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      const int tt = t < nv ? t : nv - 1;
-      pr.kv[i] = ld16(k + ((row0 + tt) * H + h) * DK + cv);
-      pr.qv[i] = ld16(q + ((row0 + tt) * H + h) * DK + cv);
+      pr.kv[i] = bload16(rk, (t * H * DK + cv) * ES);
+      pr.qv[i] = bload16(rq, (t * H * DK + cv) * ES);
     }
-    const E* T = tws + ((slot0 + c) * H + h) * 4096;
-    const E* P = prw + ((slot0 + c) * H + h) * 4096;
+    const auto rt = buffer_rsrc(tws + ((slot0 + c) * H + h) * 4096, 4096 * ES);
+    const auto rp = buffer_rsrc(prw + ((slot0 + c) * H + h) * 4096, 4096 * ES);
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
       const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
-      pr.tv[i] = ld16(T + t * 64 + cv);
-      pr.pv[i] = ld16(P + t * 64 + cv);
+      pr.tv[i] = bload16(rt, (t * 64 + cv) * ES);
+      pr.pv[i] = bload16(rp, (t * 64 + cv) * ES);
     }
     {
       const int t = tid >> 2, cq = (tid & 3) * 4;
-      const E* src = dO + ((row0 + (t < nv ? t : nv - 1)) * H + h) * Dv + j0 + cq;
+      const auto ro = buffer_rsrc(dO + (row0 * H + h) * Dv + j0, ((nv - 1) * H * Dv + 16) * ES);
       if constexpr (sizeof(E) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(src);
-        pr.dor = u32x4_t{u.x, u.y, 0u, 0u};
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(ro, (t * H * Dv + cq) * ES, 0, 0);
+        pr.dor = u32x4_t{u[0], u[1], 0u, 0u};
       } else {
-        pr.dor = *reinterpret_cast<const u32x4_t*>(src);
+        pr.dor = bload16(ro, (t * H * Dv + cq) * ES);
       }
     }
-    {  // every wave loads the gates
-      const int ll = lane < nv ? lane : nv - 1;
-      pr.gv = p.g[(row0 + ll) * H + h];
-      pr.bv = p.beta[(row0 + ll) * H + h];
+    {  // every wave loads the gates (zeros past the chunk's end)
+      const int gb = ((nv - 1) * H + 1) * 4;
+      pr.gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.g + row0 * H + h, gb), lane * H * 4, 0, 0));
+      pr.bv = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.beta + row0 * H + h, gb), lane * H * 4, 0, 0));
     }
   };
   auto stage_pre = [&](const Pre& pr) {
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
       const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      st16(sm.Ks + t * LDK + cv, t < pr.nv ? pr.kv[i] : z);
-      st16(sm.Qs + t * LDK + cv, t < pr.nv ? pr.qv[i] : z);
+      st16(sm.Ks + t * LDK + cv, pr.kv[i]);
+      st16(sm.Qs + t * LDK + cv, pr.qv[i]);
     }
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
@@ -246,17 +248,15 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       st16(sm.Tm + t * LDC + cv, pr.tv[i]);
       st16(sm.Pr + t * LDC + cv, pr.pv[i]);
     }
-    // gamma by an in-register scan (log2 units), in every wave; wave 0 stores it
-    // (padded rows: g = 0, beta = 0)
-    const float gv = lane < pr.nv ? pr.gv : 0.f, bv = lane < pr.nv ? pr.bv : 0.f;
-    const float g2 = wave_inclusive_scan(gv * kLog2e, lane);
+    // gamma by an in-register scan (log2 units), in every wave; wave 0 stores the
+    // decays (padded rows: g = 0, beta = 0)
+    const float g2 = wave_inclusive_scan(pr.gv * kLog2e, lane);
     const float G = exp2f(g2);
     if (w == 0) {
       const float gl2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
-      sm.gam[lane] = g2;
       sm.Gam[lane] = G;
       sm.dec[lane] = exp2f(gl2 - g2);
-      sm.bg[lane] = bv * G;
+      sm.bg[lane] = pr.bv * G;
     }
     {
       const int t = tid >> 2, cq = (tid & 3) * 4;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = t < pr.nv ? dov[e] : 0.f;
+        const float x = dov[e];
         sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * x);
         sm.dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * x);
       }
@@ -283,12 +283,12 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 
   for (int c = nch - 1; c >= 0; --c) {
     {  // dS_{c+1}, the gradient of the state after chunk c
-      float* dst = p.dstates + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv;
+      const auto rd = buffer_rsrc(p.dstates + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv, DK * Dv * 4);
 #pragma unroll
       for (int sr = 0; sr < SRB; ++sr) {
         const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(i + r) * Dv + j0 + j] = dS[sr][r];
+        for (int r = 0; r < 4; ++r) buffer_store1(rd, ((i + r) * Dv + j0 + j) * 4, dS[sr][r]);
       }
     }
     // ---- stage K, Q, T, P (rows), dOs^T of this tile and the gates; load chunk c - 1 ----
