@@ -74,6 +74,20 @@ __device__ __forceinline__ float wide_elem<float>(const u32x4_t& v, int e) {
   return __uint_as_float(v[e]);
 }
 
+// Four consecutive io elements (8- or 16-byte aligned) widened to fp32, one LDS read.
+template <typename E>
+__device__ __forceinline__ f32x4_t wide4(const E* p);
+template <>
+__device__ __forceinline__ f32x4_t wide4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4_t wide4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+
 // Store a 16x16 accumulator block C (C[4 (lane/16) + r][lane % 16] in element r)
 // transposed, dst[(lane % 16) * ld + 4 (lane/16) + r]: contiguous per lane.
 template <typename E>
@@ -602,8 +616,9 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
       const int t = 16 * bt + (lane & 15), cl = 16 * bdv + 4 * (lane >> 4);
       const float bt_ = bet[t];
       float part = 0.f;
+      const f32x4_t vrow = wide4<E>(Vr + t * LDV + cl);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += acc[r] * Op::widen(Vr[t * LDV + cl + r]);
+      for (int r = 0; r < 4; ++r) part += acc[r] * vrow[r];
       part = sum_groups(part);
       if (lane < 16) pb[w * 64 + t] += part;
       buffer_store4<E>(rdv, v0 + cl < Dv ? (t * H * Dv + v0 + cl) * static_cast<int>(sizeof(E)) : kNoLoadB,
@@ -636,12 +651,17 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
     const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
     store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, -dWT[s], lane);  // dW^T block (a, b)
   }
-  for (int x = tid; x < 64 * 64; x += 512) {  // zero the blocks no owner writes
-    const int r = x >> 6, cc = x & 63;
-    if ((cc >> 4) > (r >> 4)) dTb[r * LDC + cc] = Op::cvt(0.f);
-    if ((cc >> 4) < (r >> 4)) {
-      dQKt[r * LDC + cc] = Op::cvt(0.f);
-      dKKt[r * LDC + cc] = Op::cvt(0.f);
+  {  // zero the 16x16 blocks no owner writes: above the diagonal in dT^T, below it
+     // in dQK^T and dKK^T (16-byte stores)
+    constexpr int VR = 16 / EPV, NZ = 3 * 6 * 16 * VR;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int x = tid; x < NZ; x += 512) {
+      const int arr = x / (6 * 16 * VR), rem = x % (6 * 16 * VR);
+      const int blk = rem / (16 * VR), rr = (rem / VR) % 16, cv = (rem % VR) * EPV;
+      const int bu = blk < 3 ? 0 : (blk < 5 ? 1 : 2), bl = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      E* const base = arr == 0 ? dTb : (arr == 1 ? dQKt : dKKt);
+      const int rb = arr == 0 ? bu : bl, cb = arr == 0 ? bl : bu;
+      st16(base + (16 * rb + rr) * LDC + 16 * cb + cv, z);
     }
   }
 #pragma unroll
@@ -778,10 +798,11 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
                     Op::frag_tr(dKKt + 16 * b, LDC, lane, ks * KS), dka);
     const float dct = dec[t], bgt = bg[t];
     float qd = 0.f, rk = 0.f, tj = 0.f;
+    const f32x4_t krow = wide4<E>(Ks + t * LDK + d0), qrow = wide4<E>(Qr + t * LDK + d0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float kv = Op::widen(Ks[t * LDK + d0 + r]);
-      qd += Op::widen(Qr[t * LDK + d0 + r]) * q6[r];
+      const float kv = krow[r];
+      qd += qrow[r] * q6[r];
       rk += dKbT[s][r] * kv;
       tj += dKtT[s][r] * dct * kv;
       dka[r] += dct * dKtT[s][r] + bgt * dKbT[s][r];
