@@ -107,7 +107,35 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
                       "tokens_per_s": w.B * w.T / float(kt.mean()),
                       "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
                       "kernels": "prep + state (with per-chunk states) + chunk_dstate + chunk_grad"}
-        del sets
+
+        # retained states (the fla issue #1550 page's retain-or-recompute choice): a
+        # training step as forward + recomputing backward, against the forward that
+        # keeps the backward's records + the backward from them
+        def fwd(i):
+            t = sets[i % len(sets)]
+            gdn.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"], scale=d["scale"])
+
+        saved = [gdn.saved_buffer(t["q"], t["v"]) for t in sets]
+
+        def fsave(i):
+            t = sets[i % len(sets)]
+            gdn.chunk_fwd_save(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t["S0"], scale=d["scale"],
+                               saved=saved[i % len(sets)])
+
+        def bsaved(i):
+            t = sets[i % len(sets)]
+            gdn.chunk_bwd_saved(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], saved[i % len(sets)],
+                                scale=d["scale"])
+
+        tf = event_times(fwd, steps, warmup, stream)
+        ts = event_times(fsave, steps, warmup, stream)  # leaves both buffers filled
+        tb = event_times(bsaved, steps, warmup, stream)
+        f_ms, s_ms, b_ms = (float(x.mean()) * 1e3 for x in (tf, ts, tb))
+        out["bwd"]["recompute"] = {"fwd_ms": f_ms, "bwd_ms": out["bwd"]["ms_mean"],
+                                   "step_ms": f_ms + out["bwd"]["ms_mean"]}
+        out["bwd"]["retain"] = {"fwd_save_ms": s_ms, "bwd_saved_ms": b_ms, "step_ms": s_ms + b_ms,
+                                "saved_bytes": int(saved[0].numel())}
+        del sets, saved
     if "segment_split" in which:
         # segment split, B=1 T=65536 H=1 d=128
         w = WORKLOADS["long_bf16"]

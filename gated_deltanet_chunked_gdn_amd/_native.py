@@ -43,11 +43,13 @@ GDN_PASS_CHUNK_BWD = 1
 GDN_PASS_RECURRENT_FWD = 2
 GDN_PASS_RECURRENT_BWD = 3
 GDN_PASS_KDA_FWD = 4
+GDN_PASS_CHUNK_SAVED = 5
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
             "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue",
-            "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_device_copy")
+            "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_device_copy", "gdn_chunk_fwd_save",
+            "gdn_chunk_bwd_saved")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -112,6 +114,10 @@ def load():
     lib.gdn_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_device_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd_save.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd_save.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_saved.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_bwd_saved.restype = ctypes.c_int
     lib.gdn_device_copy.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -157,6 +157,36 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   return 0;
 }
 
+// The backward's buffer: per (chunk slot, head) T, T diag(beta) (packed), the
+// decays and P row-major; the fp32 state before and the state gradient after
+// every chunk; then (for the forward that keeps them) P in operand order.
+struct BwdLayout {
+  char* tws;
+  char* tbws;
+  float* gws;
+  char* prws;
+  float* states;
+  float* dstates;
+  char* pws;
+};
+BwdLayout bwd_layout(const gdn_problem* p, const Checked& c, void* ws) {
+  char* const b = static_cast<char*>(ws);
+  const size_t tb = t_slot_bytes(p, c), pb = packed_slot_bytes(p, c), gb = gate_slot_bytes(p, c);
+  const size_t sb = state_slot_bytes(p, c);
+  BwdLayout l;
+  l.tws = b;
+  l.tbws = b + tb;
+  l.gws = reinterpret_cast<float*>(b + tb + pb);
+  l.prws = b + tb + pb + gb;
+  l.states = reinterpret_cast<float*>(l.prws + tb);
+  l.dstates = reinterpret_cast<float*>(l.prws + tb + sb);
+  l.pws = l.prws + tb + 2 * sb;
+  return l;
+}
+size_t saved_bytes_needed(const gdn_problem* p, const Checked& c) {
+  return c.N == 0 ? 0 : workspace_bytes(p, Kind::ChunkBwd, c) + t_slot_bytes(p, c);
+}
+
 struct Tensor {
   const void* ptr;
   size_t bytes;
@@ -241,12 +271,13 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int32_t pass, size_t* bytes)
     case GDN_PASS_RECURRENT_FWD: kind = Kind::RecFwd; break;
     case GDN_PASS_RECURRENT_BWD: kind = Kind::RecBwd; break;
     case GDN_PASS_KDA_FWD: kind = Kind::KdaFwd; break;
+    case GDN_PASS_CHUNK_SAVED: kind = Kind::ChunkBwd; break;
     default: return GDN_ERR_UNSUPPORTED;
   }
   Checked c;
   const gdn_status st = check_problem(p, kind, &c);
   if (st != GDN_OK) return st;
-  *bytes = workspace_bytes(p, kind, c);
+  *bytes = pass == GDN_PASS_CHUNK_SAVED ? saved_bytes_needed(p, c) : workspace_bytes(p, kind, c);
   return GDN_OK;
 }
 
@@ -311,6 +342,21 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
+// The reverse passes of the backward on a filled buffer.
+gdn_status launch_bwd_from(const gdn_problem* p, const Checked& c, const BwdLayout& l, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta, const void* dO,
+                           const float* dS_final, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                           float* dS0, hipStream_t s) {
+  gdn::BwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
+  bp.tws = l.tws; bp.prws = l.prws; bp.states = l.states; bp.dstates = l.dstates; bp.seq = seq_info(p);
+  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv;
+  bp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  bp.scale = p->scale;
+  return hip_status(gdn::launch_chunk_bwd(bp, p->Dk, c.bf16, s));
+}
+
 gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* S0, const void* dO,
                          const float* dS_final, void* dq, void* dk, void* dv, float* dg,
@@ -332,30 +378,69 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
   if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
   if (c.N == 0) return GDN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* const wsb = static_cast<char*>(workspace);
-  const size_t tb = t_slot_bytes(p, c);
-  const size_t pb = packed_slot_bytes(p, c);
-  char* const prws = wsb + tb + pb + gate_slot_bytes(p, c);
-  float* states = reinterpret_cast<float*>(prws + tb);
-  float* dstates = reinterpret_cast<float*>(reinterpret_cast<char*>(states) + state_slot_bytes(p, c));
+  const BwdLayout l = bwd_layout(p, c, workspace);
   gdn::FwdParams fp{};
   fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0;
-  fp.tws = wsb; fp.tbws = wsb + tb; fp.pws = nullptr;
-  fp.gws = reinterpret_cast<float*>(wsb + tb + pb);
-  fp.prws = prws;
-  fp.states = states; fp.seq = seq_info(p);
+  fp.tws = l.tws; fp.tbws = l.tbws; fp.pws = nullptr; fp.gws = l.gws; fp.prws = l.prws;
+  fp.states = l.states; fp.seq = seq_info(p);
   fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
   fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
   fp.scale = p->scale;
   fp.G = 1;
   st = hip_status(gdn::launch_chunk_fwd_states(fp, p->Dk, c.bf16, s));
   if (st != GDN_OK) return st;
-  gdn::BwdParams bp{};
-  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
-  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
-  bp.tws = workspace; bp.prws = prws; bp.states = states; bp.dstates = dstates; bp.seq = seq_info(p);
-  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv; bp.max_chunks = fp.max_chunks; bp.scale = p->scale;
-  return hip_status(gdn::launch_chunk_bwd(bp, p->Dk, c.bf16, s));
+  return launch_bwd_from(p, c, l, q, k, v, g, beta, dO, dS_final, dq, dk, dv, dg, dbeta, dS0, s);
+}
+
+gdn_status gdn_chunk_fwd_save(const gdn_problem* p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* S0, void* o,
+                              float* S_final, void* saved, size_t saved_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::ChunkBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false},
+                      {saved, saved_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = saved_bytes_needed(p, c);
+  if (need && (!saved || saved_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  const BwdLayout l = bwd_layout(p, c, saved);
+  gdn::FwdParams fp{};
+  fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta; fp.S0 = S0; fp.o = o; fp.S_final = S_final;
+  fp.tws = l.tws; fp.tbws = l.tbws; fp.pws = l.pws; fp.gws = l.gws; fp.prws = l.prws;
+  fp.states = l.states; fp.seq = seq_info(p);
+  fp.N = c.N; fp.H = p->H; fp.Dv = p->Dv;
+  fp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  fp.scale = p->scale;
+  fp.G = 1;
+  return hip_status(gdn::launch_chunk_fwd_save(fp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const void* dO, const float* dS_final,
+                               void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dS0,
+                               void* saved, size_t saved_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::ChunkBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, ng * 4, 4, true}, {beta, ng * 4, 4, true},
+                      {dO, nv * c.io, 16, true}, {dS_final, ns * 4, 4, false}},
+                     {{dq, nk * c.io, 16, true}, {dk, nk * c.io, 16, true}, {dv, nv * c.io, 16, true},
+                      {dg, ng * 4, 4, true}, {dbeta, ng * 4, 4, true}, {dS0, ns * 4, 4, false},
+                      {saved, saved_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = saved_bytes_needed(p, c);
+  if (need && (!saved || saved_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  return launch_bwd_from(p, c, bwd_layout(p, c, saved), q, k, v, g, beta, dO, dS_final, dq, dk, dv, dg, dbeta,
+                         dS0, static_cast<hipStream_t>(stream));
 }
 
 gdn_status gdn_recurrent_ref(const gdn_problem* p, const void* q, const void* k, const void* v,

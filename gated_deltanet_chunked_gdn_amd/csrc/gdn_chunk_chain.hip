@@ -547,11 +547,11 @@ hipError_t launch_chain_t(const FwdParams& q, hipStream_t s) {
 
 hipError_t launch_state_chain(const FwdParams& p, int Dk, bool states, bool out, hipStream_t s) {
   if (Dk == 128) {
-    if (states) return out ? hipErrorInvalidValue : launch_chain_t<128, true, false>(p, s);
+    if (states) return out ? launch_chain_t<128, true, true>(p, s) : launch_chain_t<128, true, false>(p, s);
     return out ? launch_chain_t<128, false, true>(p, s) : launch_chain_t<128, false, false>(p, s);
   }
   if (Dk == 64) {
-    if (states) return out ? hipErrorInvalidValue : launch_chain_t<64, true, false>(p, s);
+    if (states) return out ? launch_chain_t<64, true, true>(p, s) : launch_chain_t<64, true, false>(p, s);
     return out ? launch_chain_t<64, false, true>(p, s) : launch_chain_t<64, false, false>(p, s);
   }
   return hipErrorInvalidValue;

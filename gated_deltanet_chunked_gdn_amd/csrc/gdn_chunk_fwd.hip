@@ -842,6 +842,20 @@ hipError_t launch_states_t(const FwdParams& p, hipStream_t s) {
   return launch_state<DK, Op, IO, true, false>(q, s);
 }
 
+// Forward that keeps what the backward needs: the preparation writes T, T
+// diag(beta), the decays, P in operand order (for the output) and P row-major
+// (for the backward); the state pass writes o, S_final and the state before every
+// chunk.
+template <int DK, typename Op, typename IO>
+hipError_t launch_save_t(const FwdParams& p, hipStream_t s) {
+  hipError_t e = launch_prep<DK, Op, IO>(p, s);
+  if (e != hipSuccess) return e;
+  FwdParams q = p;
+  q.G = 1; q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
+  q.zero_u = 0; q.ncol = p.Dv; q.carry = nullptr; q.seg_out = nullptr; q.final_to_sfinal = 1;
+  return launch_state<DK, Op, IO, true, true>(q, s);
+}
+
 template <int DK, typename Op, typename IO>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   hipError_t e = launch_prep<DK, Op, IO>(p, s);
@@ -888,6 +902,16 @@ hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStr
     if (Dk == 128) return launch_states_t<128, OpBf16, uint16_t>(p, s);
   } else {
     if (Dk == 64) return launch_states_t<64, OpF32, float>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_fwd_save(const FwdParams& p, int Dk, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (Dk == 64) return launch_save_t<64, OpBf16, uint16_t>(p, s);
+    if (Dk == 128) return launch_save_t<128, OpBf16, uint16_t>(p, s);
+  } else {
+    if (Dk == 64) return launch_save_t<64, OpF32, float>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -161,6 +161,10 @@ hipError_t launch_state_chain(const FwdParams& p, int Dk, bool states, bool out,
 // (no outputs): the forward half of the chunked backward.  Uses p.tws, p.tbws,
 // p.gws and p.states; G must be 1.
 hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
+// Forward with o and S_final that also keeps the backward's records (T, T
+// diag(beta), decays, P row-major in prws; P in operand order in pws) and the
+// state before every chunk (states).
+hipError_t launch_chunk_fwd_save(const FwdParams& p, int Dk, bool bf16, hipStream_t s);
 // Bytes of forward workspace beyond the per-chunk records for G segments (0 for G = 1).
 inline size_t segment_ws_bytes(int G, int N, int H, int Dk, int Dv) {
   if (G <= 1) return 0;

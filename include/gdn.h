@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -113,7 +113,8 @@ typedef enum gdn_pass {
   GDN_PASS_CHUNK_BWD = 1,
   GDN_PASS_RECURRENT_FWD = 2,
   GDN_PASS_RECURRENT_BWD = 3,
-  GDN_PASS_KDA_FWD = 4
+  GDN_PASS_KDA_FWD = 4,
+  GDN_PASS_CHUNK_SAVED = 5  /* the buffer of gdn_chunk_fwd_save / gdn_chunk_bwd_saved */
 } gdn_pass;
 
 typedef struct gdn_problem {
@@ -204,6 +205,36 @@ gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* 
                          const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
                          float* dg, float* dbeta, float* dS0, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Training with retained states: the forward keeps what the backward needs, so
+ * the backward does not run the forward's state pass again (the fla issue #1550
+ * page, "Proposed scope", asks for retained or recomputed states as a measured
+ * choice; gdn_chunk_bwd is the recomputing one).
+ *
+ * gdn_chunk_fwd_save computes exactly what gdn_chunk_fwd computes (o, S_final;
+ * the same arithmetic, so bit-identical results) and also fills `saved` with
+ * T, T diag(beta), the decays and the causal score P of every chunk and the fp32
+ * state before every chunk.  gdn_chunk_bwd_saved then runs only the reverse
+ * passes of gdn_chunk_bwd and gives bit-identical gradients, provided q, k, v, g,
+ * beta, S0 and the problem are the same as in the gdn_chunk_fwd_save call and
+ * `saved` was not modified in between (neither is checked: other contents give
+ * undefined gradients, not an error).  gdn_chunk_bwd_saved writes the state
+ * gradients into `saved` as well; `saved` may be reused for the next step.
+ *   saved: caller-allocated device buffer of gdn_workspace_size(problem,
+ *          GDN_PASS_CHUNK_SAVED) bytes (the backward workspace plus P in the
+ *          forward's operand order), 16-byte aligned.
+ *   Supported and errors: as gdn_chunk_bwd (num_segments 1, precision IO).
+ *   S0 is not an argument of gdn_chunk_bwd_saved (the saved states carry it);
+ *   dS0 is still produced. */
+gdn_status gdn_chunk_fwd_save(const gdn_problem* problem, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta, const float* S0,
+                              void* o, float* S_final, void* saved, size_t saved_bytes,
+                              void* stream);
+gdn_status gdn_chunk_bwd_saved(const gdn_problem* problem, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, const void* dO,
+                               const float* dS_final, void* dq, void* dk, void* dv, float* dg,
+                               float* dbeta, float* dS0, void* saved, size_t saved_bytes,
+                               void* stream);
 
 /* Token-by-token recurrence in IEEE fp32 on the GPU: the full-length second
  * reference (not the fast path).  Forward always (o, S_final as gdn_chunk_fwd).

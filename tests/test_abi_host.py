@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
@@ -205,6 +205,39 @@ def test_backward_workspace_size():
                  + 2 * slots * 3 * 128 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+
+
+def test_saved_buffer_size_and_validation():
+    # the backward workspace plus P in the forward's operand order (64 x 64 io elements per slot)
+    slots = 200 // 64 + 2 + 1
+    up = lambda b: (b + 255) // 256 * 256
+    st, nb = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
+    st2, ns = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_SAVED)
+    assert st == st2 == nat.GDN_OK and ns == nb + up(slots * 3 * 4096 * 2)
+    assert ws(problem(num_segments=2), nat.GDN_PASS_CHUNK_SAVED)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(precision=nat.GDN_PRECISION_FP32), nat.GDN_PASS_CHUNK_SAVED)[0] == nat.GDN_ERR_UNSUPPORTED
+    P = ctypes.c_void_p
+    lib = nat.load()
+    # gdn_chunk_fwd_save: q k v g beta S0 o S_final saved
+    f = [P(FAKE + (i << 30)) for i in range(9)]
+    f[5] = P(None)
+    assert lib.gdn_chunk_fwd_save(ctypes.byref(problem()), *f[:8], P(None), 0, None) == nat.GDN_ERR_WORKSPACE
+    assert lib.gdn_chunk_fwd_save(ctypes.byref(problem()), *f, 64, None) == nat.GDN_ERR_WORKSPACE
+    assert lib.gdn_chunk_fwd_save(ctypes.byref(problem(num_segments=4)), *f, 1 << 30, None) == nat.GDN_ERR_UNSUPPORTED
+    bad = list(f)
+    bad[8] = P(FAKE + (2 << 30) + 4096)  # saved inside v
+    assert lib.gdn_chunk_fwd_save(ctypes.byref(problem()), *bad, 1 << 30, None) == nat.GDN_ERR_ALIAS
+    z = [P(None)] * 9
+    assert lib.gdn_chunk_fwd_save(ctypes.byref(problem()), *z, 0, None) == nat.GDN_ERR_NULL
+    # gdn_chunk_bwd_saved: q k v g beta dO dS_final dq dk dv dg dbeta dS0 saved
+    b = [P(FAKE + (i << 30)) for i in range(14)]
+    b[6] = P(None)
+    b[12] = P(None)
+    assert lib.gdn_chunk_bwd_saved(ctypes.byref(problem()), *b[:13], P(None), 0, None) == nat.GDN_ERR_WORKSPACE
+    bad = list(b)
+    bad[9] = P(FAKE + (5 << 30) + 64)  # dv inside dO
+    assert lib.gdn_chunk_bwd_saved(ctypes.byref(problem()), *bad, 1 << 30, None) == nat.GDN_ERR_ALIAS
+    assert lib.gdn_chunk_bwd_saved(ctypes.byref(problem(chunk=32)), *b, 1 << 30, None) == nat.GDN_ERR_UNSUPPORTED
 
 
 def test_recurrent_backward_needs_workspace():
