@@ -629,224 +629,234 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   sdot_acc = wave_sum(sdot_acc);
   if (lane == 0) sdot[w] = sdot_acc;
 
-  // ---------------- 64 x 64 and 64 x d_k stages ----------------
-  E* const dQKt = U + GL::bQKt;
-  E* const dKKt = U + GL::bKKt;
-  E* const dWr = U + GL::bWr;
-  E* const Qr = U + GL::bQr;
-  E* const dTb = U + GL::bTb;
-  E* const Xt = U + GL::bXt;
-  // Q rows for the last stage (its operand Q^T, read transposed), loaded now and
-  // staged once dW is no longer needed (rows past the chunk's end read zeros).
-  constexpr int NQV = 64 * (DK / EPV) / 512;
-  u32x4_t qpre[NQV];
-#pragma unroll
-  for (int i = 0; i < NQV; ++i) {
-    const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-    qpre[i] = bload16(rq, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
-  }
-  // dW rows; dQK = dP o D (stored transposed)
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
-    store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, -dWT[s], lane);  // dW^T block (a, b)
-  }
-  {  // zero the 16x16 blocks no owner writes: above the diagonal in dT^T, below it
-     // in dQK^T and dKK^T (16-byte stores)
-    constexpr int VR = 16 / EPV, NZ = 3 * 6 * 16 * VR;
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int x = tid; x < NZ; x += 512) {
-      const int arr = x / (6 * 16 * VR), rem = x % (6 * 16 * VR);
-      const int blk = rem / (16 * VR), rr = (rem / VR) % 16, cv = (rem % VR) * EPV;
-      const int bu = blk < 3 ? 0 : (blk < 5 ? 1 : 2), bl = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-      E* const base = arr == 0 ? dTb : (arr == 1 ? dQKt : dKKt);
-      const int rb = arr == 0 ? bu : bl, cb = arr == 0 ? bl : bu;
-      st16(base + (16 * rb + rr) * LDC + 16 * cb + cv, z);
+  {
+    // Lane-derived values are formed again from here on (through an opaque copy
+    // of the thread index), so that no address computed before the d_v loop stays
+    // live across it: kept live, they cost more registers than the 128 this
+    // kernel is held to, and their spill traffic outweighed the recomputation.
+    int tid_o = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // ---------------- 64 x 64 and 64 x d_k stages ----------------
+    E* const dQKt = U + GL::bQKt;
+    E* const dKKt = U + GL::bKKt;
+    E* const dWr = U + GL::bWr;
+    E* const Qr = U + GL::bQr;
+    E* const dTb = U + GL::bTb;
+    E* const Xt = U + GL::bXt;
+    // Q rows for the last stage (its operand Q^T, read transposed), loaded now and
+    // staged once dW is no longer needed (rows past the chunk's end read zeros).
+    constexpr int NQV = 64 * (DK / EPV) / 512;
+    u32x4_t qpre[NQV];
+  #pragma unroll
+    for (int i = 0; i < NQV; ++i) {
+      const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      qpre[i] = bload16(rq, (t * H * DK + cv) * static_cast<int>(sizeof(E)));
     }
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s < nlow) {
-      const int bi = lbi[s], bj = lbj[s];
-      const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
-      f32x4_t dqk;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dqk[r] = i0 + r >= j ? dP[s][r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
-      store_t<E>(dQKt + 16 * bj * LDC + 16 * bi, LDC, dqk, lane);
+    // dW rows; dQK = dP o D (stored transposed)
+  #pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+      store_t<E>(dWr + 16 * b * LDK + 16 * a, LDK, -dWT[s], lane);  // dW^T block (a, b)
     }
-  }
-  __syncthreads();
-  // dT^T = diag(beta) dT1^T + diag(beta Gamma) (K dW^T), strictly lower part of dT.
-  // dKb^T = dW^T T (the last use of dW; kept in registers for the final stage).
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s < nlow) {
-      const int bi = lbi[s], bj = lbj[s];
-      f32x4_t acc = zero4();
-      tile_mma<Op, DK>(acc, Ks + 16 * bj * LDK, LDK, dWr + 16 * bi * LDK, LDK, lane);
-      const int j0 = 16 * bj + 4 * (lane >> 4), i = 16 * bi + (lane & 15);
-      f32x4_t dt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dt[r] = i > j0 + r ? bet[j0 + r] * dT1T[s][r] + bg[j0 + r] * acc[r] : 0.f;
-      store_t<E>(dTb + 16 * bi * LDC + 16 * bj, LDC, dt, lane);
-    }
-  }
-  f32x4_t dKbT[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
-    dKbT[s] = zero4();
-    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
-      dKbT[s] = Op::mma(Op::frag_tr(dWr + 16 * a, LDK, lane, ks * KS),
-                        Op::frag_tr(Tm + 16 * b, LDC, lane, ks * KS), dKbT[s]);
-  }
-  __syncthreads();
-  // X = dT T^T (all 16 blocks, two per wave), stored transposed.  The Q rows go
-  // where dW was.
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
-    f32x4_t acc = zero4();
-    const int kb = bk < bj ? bk : bj;
-    for (int ks = 0; ks < (16 * (kb + 1) + KS - 1) / KS; ++ks)
-      acc = Op::mma(Op::frag(dTb + 16 * bk * LDC, LDC, lane, ks * KS),
-                    Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
-    store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
-  }
-#pragma unroll
-  for (int i = 0; i < NQV; ++i) {
-    const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
-    st16(Qr + t * LDK + cv, qpre[i]);
-  }
-  __syncthreads();
-  // dA = strict_lower(-T^T X); QK and KK formed again; dbeta, dKK (stored
-  // transposed), dD = dP o QK; dDD row and column sums.
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s < nlow) {
-      const int bi = lbi[s], bj = lbj[s];
-      f32x4_t qk = zero4(), kkb = zero4();
-      tile_mma<Op, DK>(qk, Qr + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-      tile_mma<Op, DK>(kkb, Ks + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
-      f32x4_t acc = zero4();
-      for (int ks = (16 * bi) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag_tr(Tm + 16 * bi, LDC, lane, ks * KS),
-                      Op::frag(Xt + 16 * bj * LDC, LDC, lane, ks * KS), acc);
-      const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
-      f32x4_t dkk, dd;
-      float rows[4], colp = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        const bool lo = i > j;
-        const float d = i >= j ? exp2f(fminf(gam[i] - gam[j], 0.f)) : 0.f;
-        const float da = lo ? -acc[r] : 0.f;
-        const float b_i = bet[i];
-        const float kk = kkb[r];
-        rows[r] = da * kk * d;                 // dbeta_i
-        dkk[r] = da * b_i * d;                 // dKK
-        const float dd0 = i >= j ? dP[s][r] * qk[r] : 0.f;  // dD = dP o QK
-        dd[r] = (dd0 + da * b_i * kk) * d;     // dD o D
-        colp += dd[r];
+    {  // zero the 16x16 blocks no owner writes: above the diagonal in dT^T, below it
+       // in dQK^T and dKK^T (16-byte stores)
+      constexpr int VR = 16 / EPV, NZ = 3 * 6 * 16 * VR;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      for (int x = tid; x < NZ; x += 512) {
+        const int arr = x / (6 * 16 * VR), rem = x % (6 * 16 * VR);
+        const int blk = rem / (16 * VR), rr = (rem / VR) % 16, cv = (rem % VR) * EPV;
+        const int bu = blk < 3 ? 0 : (blk < 5 ? 1 : 2), bl = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        E* const base = arr == 0 ? dTb : (arr == 1 ? dQKt : dKKt);
+        const int rb = arr == 0 ? bu : bl, cb = arr == 0 ? bl : bu;
+        st16(base + (16 * rb + rr) * LDC + 16 * cb + cv, z);
       }
-      store_t<E>(dKKt + 16 * bj * LDC + 16 * bi, LDC, dkk, lane);
-      // row sums over the 16 lanes of a group; column sums over the four groups
-      float rs[4], rd[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rs[r] = sum_in_group(rows[r]);
-        rd[r] = sum_in_group(dd[r]);
+    }
+  #pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nlow) {
+        const int bi = lbi[s], bj = lbj[s];
+        const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
+        f32x4_t dqk;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dqk[r] = i0 + r >= j ? dP[s][r] * exp2f(fminf(gam[i0 + r] - gam[j], 0.f)) : 0.f;
+        store_t<E>(dQKt + 16 * bj * LDC + 16 * bi, LDC, dqk, lane);
       }
-      colp = sum_groups(colp);
-      if ((lane & 15) == 0) {
-#pragma unroll
+    }
+    __syncthreads();
+    // dT^T = diag(beta) dT1^T + diag(beta Gamma) (K dW^T), strictly lower part of dT.
+    // dKb^T = dW^T T (the last use of dW; kept in registers for the final stage).
+  #pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nlow) {
+        const int bi = lbi[s], bj = lbj[s];
+        f32x4_t acc = zero4();
+        tile_mma<Op, DK>(acc, Ks + 16 * bj * LDK, LDK, dWr + 16 * bi * LDK, LDK, lane);
+        const int j0 = 16 * bj + 4 * (lane >> 4), i = 16 * bi + (lane & 15);
+        f32x4_t dt;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dt[r] = i > j0 + r ? bet[j0 + r] * dT1T[s][r] + bg[j0 + r] * acc[r] : 0.f;
+        store_t<E>(dTb + 16 * bi * LDC + 16 * bj, LDC, dt, lane);
+      }
+    }
+    f32x4_t dKbT[NKS];
+  #pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+      dKbT[s] = zero4();
+      for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+        dKbT[s] = Op::mma(Op::frag_tr(dWr + 16 * a, LDK, lane, ks * KS),
+                          Op::frag_tr(Tm + 16 * b, LDC, lane, ks * KS), dKbT[s]);
+    }
+    __syncthreads();
+    // X = dT T^T (all 16 blocks, two per wave), stored transposed.  The Q rows go
+    // where dW was.
+  #pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int idx = w + 8 * s, bk = idx >> 2, bj = idx & 3;
+      f32x4_t acc = zero4();
+      const int kb = bk < bj ? bk : bj;
+      for (int ks = 0; ks < (16 * (kb + 1) + KS - 1) / KS; ++ks)
+        acc = Op::mma(Op::frag(dTb + 16 * bk * LDC, LDC, lane, ks * KS),
+                      Op::frag(Tm + 16 * bj * LDC, LDC, lane, ks * KS), acc);
+      store_t<E>(Xt + 16 * bj * LDC + 16 * bk, LDC, acc, lane);
+    }
+  #pragma unroll
+    for (int i = 0; i < NQV; ++i) {
+      const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      st16(Qr + t * LDK + cv, qpre[i]);
+    }
+    __syncthreads();
+    // dA = strict_lower(-T^T X); QK and KK formed again; dbeta, dKK (stored
+    // transposed), dD = dP o QK; dDD row and column sums.
+  #pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nlow) {
+        const int bi = lbi[s], bj = lbj[s];
+        f32x4_t qk = zero4(), kkb = zero4();
+        tile_mma<Op, DK>(qk, Qr + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+        tile_mma<Op, DK>(kkb, Ks + 16 * bi * LDK, LDK, Ks + 16 * bj * LDK, LDK, lane);
+        f32x4_t acc = zero4();
+        for (int ks = (16 * bi) / KS; ks < 64 / KS; ++ks)
+          acc = Op::mma(Op::frag_tr(Tm + 16 * bi, LDC, lane, ks * KS),
+                        Op::frag(Xt + 16 * bj * LDC, LDC, lane, ks * KS), acc);
+        const int i0 = 16 * bi + 4 * (lane >> 4), j = 16 * bj + (lane & 15);
+        f32x4_t dkk, dd;
+        float rows[4], colp = 0.f;
+  #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pb[w * 64 + i0 + r] += rs[r];
-          pg[w * 64 + i0 + r] += rd[r];
+          const int i = i0 + r;
+          const bool lo = i > j;
+          const float d = i >= j ? exp2f(fminf(gam[i] - gam[j], 0.f)) : 0.f;
+          const float da = lo ? -acc[r] : 0.f;
+          const float b_i = bet[i];
+          const float kk = kkb[r];
+          rows[r] = da * kk * d;                 // dbeta_i
+          dkk[r] = da * b_i * d;                 // dKK
+          const float dd0 = i >= j ? dP[s][r] * qk[r] : 0.f;  // dD = dP o QK
+          dd[r] = (dd0 + da * b_i * kk) * d;     // dD o D
+          colp += dd[r];
         }
+        store_t<E>(dKKt + 16 * bj * LDC + 16 * bi, LDC, dkk, lane);
+        // row sums over the 16 lanes of a group; column sums over the four groups
+        float rs[4], rd[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rs[r] = sum_in_group(rows[r]);
+          rd[r] = sum_in_group(dd[r]);
+        }
+        colp = sum_groups(colp);
+        if ((lane & 15) == 0) {
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pb[w * 64 + i0 + r] += rs[r];
+            pg[w * 64 + i0 + r] += rd[r];
+          }
+        }
+        if (lane < 16) pg[w * 64 + j] -= colp;
       }
-      if (lane < 16) pg[w * 64 + j] -= colp;
     }
-  }
-  __syncthreads();
-  // dq^T, dk^T blocks (a: d_k, b: tokens) and the per-token terms they carry
-  float pn_acc = 0.f;
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
-    const int t = 16 * b + (lane & 15), d0 = 16 * a + 4 * (lane >> 4);
-    // dq^T = Gamma o (dOs S_c^T)^T + K^T dQK^T
-    const f32x4_t q6 = dQ6T[s] * Gam[t];
-    f32x4_t dqa = q6;
-    for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
-      dqa = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
-                    Op::frag_tr(dQKt + 16 * b, LDC, lane, ks * KS), dqa);
-    // dk^T = decay o dK~^T + Q^T dQK + K^T (dKK + dKK^T) + (beta Gamma) o dKb^T;
-    // dKK is strictly lower, so only token blocks >= b of dKK and <= b of dKK^T
-    // reach column block b
-    f32x4_t dka = zero4();
-    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
-      dka = Op::mma(Op::frag_tr(Qr + 16 * a, LDK, lane, ks * KS),
-                    Op::frag(dQKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
-    for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
-      dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
-                    Op::frag(dKKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
-    for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
-      dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
-                    Op::frag_tr(dKKt + 16 * b, LDC, lane, ks * KS), dka);
-    const float dct = dec[t], bgt = bg[t];
-    float qd = 0.f, rk = 0.f, tj = 0.f;
-    const f32x4_t krow = wide4<E>(Ks + t * LDK + d0), qrow = wide4<E>(Qr + t * LDK + d0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float kv = krow[r];
-      qd += qrow[r] * q6[r];
-      rk += dKbT[s][r] * kv;
-      tj += dKtT[s][r] * dct * kv;
-      dka[r] += dct * dKtT[s][r] + bgt * dKbT[s][r];
+    __syncthreads();
+    // dq^T, dk^T blocks (a: d_k, b: tokens) and the per-token terms they carry
+    float pn_acc = 0.f;
+  #pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int idx = w + 8 * s, a = idx >> 2, b = idx & 3;
+      const int t = 16 * b + (lane & 15), d0 = 16 * a + 4 * (lane >> 4);
+      // dq^T = Gamma o (dOs S_c^T)^T + K^T dQK^T
+      const f32x4_t q6 = dQ6T[s] * Gam[t];
+      f32x4_t dqa = q6;
+      for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
+        dqa = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                      Op::frag_tr(dQKt + 16 * b, LDC, lane, ks * KS), dqa);
+      // dk^T = decay o dK~^T + Q^T dQK + K^T (dKK + dKK^T) + (beta Gamma) o dKb^T;
+      // dKK is strictly lower, so only token blocks >= b of dKK and <= b of dKK^T
+      // reach column block b
+      f32x4_t dka = zero4();
+      for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+        dka = Op::mma(Op::frag_tr(Qr + 16 * a, LDK, lane, ks * KS),
+                      Op::frag(dQKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
+      for (int ks = (16 * b) / KS; ks < 64 / KS; ++ks)
+        dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                      Op::frag(dKKt + 16 * b * LDC, LDC, lane, ks * KS), dka);
+      for (int ks = 0; ks < (16 * (b + 1) + KS - 1) / KS; ++ks)
+        dka = Op::mma(Op::frag_tr(Ks + 16 * a, LDK, lane, ks * KS),
+                      Op::frag_tr(dKKt + 16 * b, LDC, lane, ks * KS), dka);
+      const float dct = dec[t], bgt = bg[t];
+      float qd = 0.f, rk = 0.f, tj = 0.f;
+      const f32x4_t krow = wide4<E>(Ks + t * LDK + d0), qrow = wide4<E>(Qr + t * LDK + d0);
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float kv = krow[r];
+        qd += qrow[r] * q6[r];
+        rk += dKbT[s][r] * kv;
+        tj += dKtT[s][r] * dct * kv;
+        dka[r] += dct * dKtT[s][r] + bgt * dKbT[s][r];
+      }
+      qd = sum_groups(qd);
+      rk = sum_groups(rk);
+      tj = sum_groups(tj);
+      if (lane < 16) {
+        pg[w * 64 + t] += qd + bet[t] * Gam[t] * rk - tj;
+        pb[w * 64 + t] += Gam[t] * rk;
+        pn_acc += tj;
+      }
+      {
+        const int off = (t * H * DK + d0) * static_cast<int>(sizeof(E));
+        buffer_store4<E>(rdq, off, dqa[0], dqa[1], dqa[2], dqa[3]);
+        buffer_store4<E>(rdk, off, dka[0], dka[1], dka[2], dka[3]);
+      }
     }
-    qd = sum_groups(qd);
-    rk = sum_groups(rk);
-    tj = sum_groups(tj);
-    if (lane < 16) {
-      pg[w * 64 + t] += qd + bet[t] * Gam[t] * rk - tj;
-      pb[w * 64 + t] += Gam[t] * rk;
-      pn_acc += tj;
-    }
-    {
-      const int off = (t * H * DK + d0) * static_cast<int>(sizeof(E));
-      buffer_store4<E>(rdq, off, dqa[0], dqa[1], dqa[2], dqa[3]);
-      buffer_store4<E>(rdk, off, dka[0], dka[1], dka[2], dka[3]);
-    }
-  }
-  pn_acc = wave_sum(pn_acc);
-  if (lane == 0) pn[w] = pn_acc;
-  __syncthreads();
-  if (w == 0) {
-    float db = 0.f, dgm = 0.f;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      db += pb[x * 64 + lane];
-      dgm += pg[x * 64 + lane];
-    }
-    if (lane == 63) {
-      float sd = 0.f, sn = 0.f;
-#pragma unroll
+    pn_acc = wave_sum(pn_acc);
+    if (lane == 0) pn[w] = pn_acc;
+    __syncthreads();
+    if (w == 0) {
+      float db = 0.f, dgm = 0.f;
+  #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        sd += sdot[x];
-        sn += pn[x];
+        db += pb[x * 64 + lane];
+        dgm += pg[x * 64 + lane];
       }
-      dgm += Gam[63] * sd + sn;
-    }
-    // dg_t = sum of dgamma_u over u >= t: a forward scan of the reversed lanes
-    const float rev = __shfl(dgm, 63 - lane, 64);
-    const float sc = wave_inclusive_scan(rev, lane);
-    const float dgt = __shfl(sc, 63 - lane, 64);
-    if (lane < nv) {
-      p.dg[(row0 + lane) * H + h] = dgt;
-      p.dbeta[(row0 + lane) * H + h] = db;
+      if (lane == 63) {
+        float sd = 0.f, sn = 0.f;
+  #pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          sd += sdot[x];
+          sn += pn[x];
+        }
+        dgm += Gam[63] * sd + sn;
+      }
+      // dg_t = sum of dgamma_u over u >= t: a forward scan of the reversed lanes
+      const float rev = __shfl(dgm, 63 - lane, 64);
+      const float sc = wave_inclusive_scan(rev, lane);
+      const float dgt = __shfl(sc, 63 - lane, 64);
+      if (lane < nv) {
+        p.dg[(row0 + lane) * H + h] = dgt;
+        p.dbeta[(row0 + lane) * H + h] = db;
+      }
     }
   }
 }
