@@ -99,6 +99,19 @@ __device__ __forceinline__ f32x4_t ld4f<float>(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
 
+// Eight values to eight consecutive operand elements (16-byte aligned): one
+// 16-byte store for bf16 (round to nearest even), two for fp32.
+template <typename EL>
+__device__ __forceinline__ void store8(EL* dst, const float (&v)[8]) {
+  if constexpr (sizeof(EL) == 2) {
+    const uint4 u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    *reinterpret_cast<uint4*>(dst) = u;
+  } else {
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
 template <int DK, typename E>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   extern __shared__ __align__(16) char smp[];
   E* const ks = reinterpret_cast<E*>(smp + PL::kK);      // [64][DK] keys (swizzled)
   E* const qs = reinterpret_cast<E*>(smp + PL::kQ);      // [64][DK] queries (swizzled)
-  float* const gs = reinterpret_cast<float*>(smp + PL::kG);  // [64][DK] g, then gamma (swizzled by 4)
+  float* const gs = reinterpret_cast<float*>(smp + PL::kG);  // [64][DK] g, then gamma log2(e) (swizzled by 4)
   float* const As = reinterpret_cast<float*>(smp + PL::kA);  // [64][64] A; beta_i at (i, i)
   float* const Ts = reinterpret_cast<float*>(smp + PL::kT);  // [64][65] T = (I + A)^-1 (after the outputs)
   float* const Ms = reinterpret_cast<float*>(smp + PL::kM);  // [4][16][17] block products of the solve
@@ -166,10 +179,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     if (tid < 64) As[tid * 64 + tid] = tid < nr ? bv : 0.f;
   }
   __syncthreads();
-  if (tid < DK) {  // channel tid: its 64 values are read at once, summed in registers
+  if (tid < DK) {  // channel tid: its 64 values are read at once, summed in registers (log2 units)
     float col[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) col[i] = gs[gidx(i, tid)];
+    for (int i = 0; i < 64; ++i) col[i] = gs[gidx(i, tid)] * chunk::kLog2e;
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
@@ -183,21 +196,32 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   // last row r = 16 bj + 15 of block bj: exp(gamma_i - gamma_j) =
   // exp(gamma_i - gamma_r) exp(gamma_r - gamma_j) channel by channel, both factors
   // <= 1 (j <= r < i), so A and P there are fp32 MFMA products of decayed rows;
-  // waves 0-5 take one such block each.  The diagonal blocks (pairs j <= i inside
-  // a block) are summed pair by pair, one exponential per channel, by all threads.
+  // waves 0-5 take one such block each.  A lane reads four consecutive channels of
+  // its rows at once and feeds them to four products (in the product of k-step
+  // (k0, e) the lanes of group g hold channel k0 + 4 g + e, in both operands).
+  // The diagonal blocks (pairs j <= i inside a block) are summed pair by pair, one
+  // exponential per channel: every thread takes one of the first 512 pairs whole
+  // and an eighth of a channel range of one of the last 32, whose sixteen parts are
+  // added within a DPP row.
   if (wave < 6) {
     const int bi = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;  // (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
     const int bj = wave < 3 ? 0 : wave < 5 ? 1 : 2;
     const int ia = 16 * bi + (lane & 15), jb = 16 * bj + (lane & 15), r = 16 * bj + 15;
     f32x4_t accA = zero4(), accP = zero4();
-#pragma unroll 4
-    for (int k0 = 0; k0 < DK; k0 += 4) {
-      const int ch = k0 + (lane >> 4);
-      const float gr = gs[gidx(r, ch)];
-      const float ei = __expf(gs[gidx(ia, ch)] - gr);
-      const float bk = IoT<E>::ld(ks + kidx(jb, ch)) * __expf(gr - gs[gidx(jb, ch)]);
-      accA = __builtin_amdgcn_mfma_f32_16x16x4f32(IoT<E>::ld(ks + kidx(ia, ch)) * ei, bk, accA, 0, 0, 0);
-      accP = __builtin_amdgcn_mfma_f32_16x16x4f32(IoT<E>::ld(qs + kidx(ia, ch)) * ei, bk, accP, 0, 0, 0);
+#pragma unroll 2
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+      const int ch = k0 + 4 * (lane >> 4);
+      const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gs + gidx(r, ch));
+      const f32x4_t gi = *reinterpret_cast<const f32x4_t*>(gs + gidx(ia, ch));
+      const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(gs + gidx(jb, ch));
+      const f32x4_t ki = ld4f<E>(ks + kidx(ia, ch)), qi = ld4f<E>(qs + kidx(ia, ch)), kj = ld4f<E>(ks + kidx(jb, ch));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ei = __builtin_amdgcn_exp2f(gi[e] - gr[e]);
+        const float bk = kj[e] * __builtin_amdgcn_exp2f(gr[e] - gj[e]);
+        accA = __builtin_amdgcn_mfma_f32_16x16x4f32(ki[e] * ei, bk, accA, 0, 0, 0);
+        accP = __builtin_amdgcn_mfma_f32_16x16x4f32(qi[e] * ei, bk, accP, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -206,51 +230,104 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
       rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
     }
   }
-  // waves 6-7 (no MFMA block) take pairs 0..127 and the 32 past 511
-  for (int t = tid >= 384 ? tid - 384 : tid + 128; t < 4 * 136; t += 512) {
-    const int b = t / 136, tl = t % 136;
-    int il = static_cast<int>((sqrtf(8.f * tl + 1.f) - 1.f) * 0.5f);
-    if (il * (il + 1) / 2 > tl) --il;
-    if ((il + 1) * (il + 2) / 2 <= tl) ++il;
-    const int i = 16 * b + il, j = 16 * b + tl - il * (il + 1) / 2;
-    float a = 0.f, sc = 0.f;
+  {
+    // pair tl of diagonal block b: row il, column jl <= il inside the block
+    auto pair_of = [](int t, int& i, int& j) {
+      const int b = t / 136, tl = t % 136;
+      int il = static_cast<int>((sqrtf(8.f * tl + 1.f) - 1.f) * 0.5f);
+      if (il * (il + 1) / 2 > tl) --il;
+      if ((il + 1) * (il + 2) / 2 <= tl) ++il;
+      i = 16 * b + il;
+      j = 16 * b + tl - il * (il + 1) / 2;
+    };
+    // channels [c0, c0 + NCH) of pair (i, j): A and P sums
+    auto pair_sums = [&](int i, int j, int c0, int nch, float& a, float& sc) {
+      a = 0.f;
+      sc = 0.f;
 #pragma unroll 4
-    for (int ch = 0; ch < DK; ch += 4) {
-      const f32x4_t k4i = ld4f<E>(ks + kidx(i, ch));
-      const f32x4_t k4j = ld4f<E>(ks + kidx(j, ch));
-      const f32x4_t q4i = ld4f<E>(qs + kidx(i, ch));
-      const f32x4_t g4i = *reinterpret_cast<const f32x4_t*>(gs + gidx(i, ch));
-      const f32x4_t g4j = *reinterpret_cast<const f32x4_t*>(gs + gidx(j, ch));
+      for (int ch = c0; ch < c0 + nch; ch += 4) {
+        const f32x4_t k4i = ld4f<E>(ks + kidx(i, ch));
+        const f32x4_t k4j = ld4f<E>(ks + kidx(j, ch));
+        const f32x4_t q4i = ld4f<E>(qs + kidx(i, ch));
+        const f32x4_t g4i = *reinterpret_cast<const f32x4_t*>(gs + gidx(i, ch));
+        const f32x4_t g4j = *reinterpret_cast<const f32x4_t*>(gs + gidx(j, ch));
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float kd = k4j[x] * __expf(g4i[x] - g4j[x]);
-        a = fmaf(k4i[x], kd, a);
-        sc = fmaf(q4i[x], kd, sc);
+        for (int x = 0; x < 4; ++x) {
+          const float kd = k4j[x] * __builtin_amdgcn_exp2f(g4i[x] - g4j[x]);
+          a = fmaf(k4i[x], kd, a);
+          sc = fmaf(q4i[x], kd, sc);
+        }
       }
-    }
+    };
+    // waves 6-7 (no MFMA block) take pairs 0..127, waves 0-5 pairs 128..511
+    int i, j;
+    float a, sc;
+    pair_of(tid >= 384 ? tid - 384 : tid + 128, i, j);
+    pair_sums(i, j, 0, DK, a, sc);
     if (j < i) As[i * 64 + j] = As[i * 64 + i] * a;
     rec[R::kP + i * 64 + j] = Op::cvt(sc);
+    // pairs 512..543: sixteen threads (one DPP row) per pair, DK / 16 channels each
+    pair_of(512 + (tid >> 4), i, j);
+    pair_sums(i, j, (DK / 16) * (tid & 15), DK / 16, a, sc);
+    a += dpp_f32<0x111, 0xf>(a);  // row_shr:1 .. 8: lane 15 of the row ends with the row's sum
+    sc += dpp_f32<0x111, 0xf>(sc);
+    a += dpp_f32<0x112, 0xf>(a);
+    sc += dpp_f32<0x112, 0xf>(sc);
+    a += dpp_f32<0x114, 0xf>(a);
+    sc += dpp_f32<0x114, 0xf>(sc);
+    a += dpp_f32<0x118, 0xf>(a);
+    sc += dpp_f32<0x118, 0xf>(sc);
+    if ((tid & 15) == 15) {
+      if (j < i) As[i * 64 + j] = As[i * 64 + i] * a;
+      rec[R::kP + i * 64 + j] = Op::cvt(sc);
+    }
   }
-  for (int x = tid; x < 64 * 64; x += 512) {
-    const int i = x / 64, j = x % 64;
-    if (j > i) rec[R::kP + x] = Op::cvt(0.f);
+  // P above the diagonal: eight zeros per 16-byte store where all eight columns
+  // lie above it, single zeros in the group that holds the diagonal
+  {
+    const int i = tid >> 3, jb = 8 * (tid & 7);
+    if (jb > i) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      store8<EL>(rec + R::kP + i * 64 + jb, z);
+    } else if (jb + 7 > i) {
+      for (int j = i + 1; j < jb + 8; ++j) rec[R::kP + i * 64 + j] = Op::cvt(0.f);
+    }
   }
 
   // the record's K o Gamma, Q o Gamma, decayed keys and Gamma_n (K, Q and gamma
   // are dead afterwards: T and the block products take their place)
   {
     const int rl = nr - 1;
-    for (int x = tid; x < 64 * DK; x += 512) {
-      const int i = x / DK, ch = x % DK;
-      const float e = __expf(gs[gidx(i, ch)]);
-      rec[R::kKG + x] = Op::cvt(IoT<E>::ld(ks + kidx(i, ch)) * e);
-      rec[R::kQG + x] = Op::cvt(IoT<E>::ld(qs + kidx(i, ch)) * e);
+    // eight consecutive channels of one row per thread and pass
+    for (int x = tid; x < 8 * DK; x += 512) {
+      const int i = x / (DK / 8), ch = 8 * (x % (DK / 8));
+      const f32x4_t k0 = ld4f<E>(ks + kidx(i, ch)), k1 = ld4f<E>(ks + kidx(i, ch + 4));
+      const f32x4_t q0 = ld4f<E>(qs + kidx(i, ch)), q1 = ld4f<E>(qs + kidx(i, ch + 4));
+      const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gs + gidx(i, ch));
+      const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gs + gidx(i, ch + 4));
+      float kv[8], qv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float e0 = __builtin_amdgcn_exp2f(g0[e]), e1 = __builtin_amdgcn_exp2f(g1[e]);
+        kv[e] = k0[e] * e0;
+        kv[e + 4] = k1[e] * e1;
+        qv[e] = q0[e] * e0;
+        qv[e + 4] = q1[e] * e1;
+      }
+      store8<EL>(rec + R::kKG + i * DK + ch, kv);
+      store8<EL>(rec + R::kQG + i * DK + ch, qv);
     }
-    for (int x = tid; x < 64 * DK; x += 512) {
-      const int ch = x / 64, i = x % 64;
-      rec[R::kKDt + x] = Op::cvt(IoT<E>::ld(ks + kidx(i, ch)) * __expf(gs[gidx(rl, ch)] - gs[gidx(i, ch)]));
+    // decayed keys, transposed: eight consecutive rows of one channel per thread and pass
+    for (int x = tid; x < 8 * DK; x += 512) {
+      const int ch = x >> 3, i0 = 8 * (x & 7);
+      const float gl = gs[gidx(rl, ch)];
+      float dv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dv[e] = IoT<E>::ld(ks + kidx(i0 + e, ch)) * __builtin_amdgcn_exp2f(gl - gs[gidx(i0 + e, ch)]);
+      store8<EL>(rec + R::kKDt + ch * 64 + i0, dv);
     }
-    if (tid < DK) reinterpret_cast<float*>(recb + R::kGnByte)[tid] = __expf(gs[gidx(rl, tid)]);
+    if (tid < DK) reinterpret_cast<float*>(recb + R::kGnByte)[tid] = __builtin_amdgcn_exp2f(gs[gidx(rl, tid)]);
   }
   __syncthreads();
   for (int x = tid; x < 64 * 64; x += 512) {
