@@ -120,8 +120,11 @@ size_t gate_slot_bytes(const gdn_problem* p, const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
+// Per-chunk states and state gradients of the backward, in the products' operand
+// type (bf16 for bf16 products, fp32 for fp32 products: every use of them in the
+// gradient kernel is as an operand of that type).
 size_t state_slot_bytes(const gdn_problem* p, const Checked& c) {
-  return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * sizeof(float);
+  return static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * c.ce;
 }
 
 size_t kda_rec_region(const gdn_problem* p, const Checked& c) {
@@ -150,23 +153,23 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
     // T (64 x 64), T diag(beta) (packed), the decays and P (64 x 64) per (chunk
-    // slot, head), then the fp32 state before and the state gradient after every
-    // chunk, [slot][H][Dk][Dv] each
+    // slot, head), then the state before and the state gradient after every chunk,
+    // [slot][H][Dk][Dv] each in the operand type
     return 2 * t_slot_bytes(p, c) + packed_slot_bytes(p, c) + gate_slot_bytes(p, c) + 2 * state_slot_bytes(p, c);
   }
   return 0;
 }
 
 // The backward's buffer: per (chunk slot, head) T, T diag(beta) (packed), the
-// decays and P row-major; the fp32 state before and the state gradient after
-// every chunk; then (for the forward that keeps them) P in operand order.
+// decays and P row-major; the state before and the state gradient after every
+// chunk (operand type); then (for the forward that keeps them) P in operand order.
 struct BwdLayout {
   char* tws;
   char* tbws;
   float* gws;
   char* prws;
-  float* states;
-  float* dstates;
+  char* states;
+  char* dstates;
   char* pws;
 };
 BwdLayout bwd_layout(const gdn_problem* p, const Checked& c, void* ws) {
@@ -178,8 +181,8 @@ BwdLayout bwd_layout(const gdn_problem* p, const Checked& c, void* ws) {
   l.tbws = b + tb;
   l.gws = reinterpret_cast<float*>(b + tb + pb);
   l.prws = b + tb + pb + gb;
-  l.states = reinterpret_cast<float*>(l.prws + tb);
-  l.dstates = reinterpret_cast<float*>(l.prws + tb + sb);
+  l.states = l.prws + tb;
+  l.dstates = l.prws + tb + sb;
   l.pws = l.prws + tb + 2 * sb;
   return l;
 }

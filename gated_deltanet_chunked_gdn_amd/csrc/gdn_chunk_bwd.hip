@@ -52,6 +52,17 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, int off) {
 }
 // An offset every buffer range check rejects.
 constexpr int kNoLoadB = 0x7ffffff0;
+// Four consecutive elements of type E (bf16 or fp32) at byte offset `off`, widened to fp32.
+template <typename E>
+__device__ __forceinline__ float4 bload4e(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (sizeof(E) == 2) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return float4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                  __uint_as_float(u[1] & 0xffff0000u)};
+  } else {
+    return __builtin_bit_cast(float4, bload16(r, off));
+  }
+}
 
 template <typename E>
 __device__ __forceinline__ u32x4_t ld16(const E* p) {
@@ -297,12 +308,14 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 
   for (int c = nch - 1; c >= 0; --c) {
     {  // dS_{c+1}, the gradient of the state after chunk c
-      const auto rd = buffer_rsrc(p.dstates + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv, DK * Dv * 4);
+      const auto rd = buffer_rsrc(static_cast<E*>(p.dstates) + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv,
+                                  DK * Dv * static_cast<int>(sizeof(E)));
 #pragma unroll
       for (int sr = 0; sr < SRB; ++sr) {
         const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) buffer_store1(rd, ((i + r) * Dv + j0 + j) * 4, dS[sr][r]);
+        for (int r = 0; r < 4; ++r)
+          buffer_store1e<E>(rd, ((i + r) * Dv + j0 + j) * static_cast<int>(sizeof(E)), dS[sr][r]);
       }
     }
     // ---- stage K, Q, T, P (rows), dOs^T of this tile and the gates; load chunk c - 1 ----
@@ -446,8 +459,8 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   const int nv = static_cast<int>(len - c0 < 64 ? len - c0 : 64);
   const int64_t slot = bos / 64 + n + c;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const float* Sg = p.states + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
-  const float* dSg = p.dstates + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+  const E* Sg = static_cast<const E*>(p.states) + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+  const E* dSg = static_cast<const E*>(p.dstates) + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
 
   // Global operands of one d_v tile (V and dO rows, S_c and dS_{c+1}), loaded into
   // registers one tile ahead of their use.
@@ -465,13 +478,13 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
   const auto rv = buffer_rsrc(v + (row0 * H + h) * Dv, rowb);
   const auto rdo = buffer_rsrc(dO + (row0 * H + h) * Dv, rowb);
   const auto rdv = buffer_rsrc(dvo + (row0 * H + h) * Dv, rowb);
-  const auto rs = buffer_rsrc(Sg, DK * Dv * 4);
+  const auto rs = buffer_rsrc(Sg, DK * Dv * static_cast<int>(sizeof(E)));
   const int rowk = ((nv - 1) * H * DK + DK) * static_cast<int>(sizeof(E));
   const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rowk);
   const auto rk = buffer_rsrc(k + (row0 * H + h) * DK, rowk);
   const auto rdq = buffer_rsrc(dq + (row0 * H + h) * DK, rowk);
   const auto rdk = buffer_rsrc(dk + (row0 * H + h) * DK, rowk);
-  const auto rds = buffer_rsrc(dSg, DK * Dv * 4);
+  const auto rds = buffer_rsrc(dSg, DK * Dv * static_cast<int>(sizeof(E)));
   auto load_tile = [&](TileLd& L, int v0) {
 #pragma unroll
     for (int ix = 0; ix < NVX; ++ix) {
@@ -484,9 +497,9 @@ __attribute__((amdgpu_waves_per_eu(DK == 64 && sizeof(typename Op::elem) == 2 ? 
 #pragma unroll
     for (int ix = 0; ix < NSX; ++ix) {
       const int x = tid + 512 * ix, i = x / (DVT / 4), cv = (x % (DVT / 4)) * 4;
-      const int off = x < DK * (DVT / 4) && v0 + cv < Dv ? (i * Dv + v0 + cv) * 4 : kNoLoadB;
-      L.sv[ix] = __builtin_bit_cast(float4, bload16(rs, off));
-      L.dv[ix] = __builtin_bit_cast(float4, bload16(rds, off));
+      const int off = x < DK * (DVT / 4) && v0 + cv < Dv ? (i * Dv + v0 + cv) * static_cast<int>(sizeof(E)) : kNoLoadB;
+      L.sv[ix] = bload4e<E>(rs, off);
+      L.dv[ix] = bload4e<E>(rds, off);
     }
   };
 

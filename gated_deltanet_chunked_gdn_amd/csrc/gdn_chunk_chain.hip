@@ -203,13 +203,15 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 
         const bool active = c < nch;  // (only the optional state stores look at it)
         const uint16_t* Ks = sm.Ks[u];
         const float* Gs = sm.Gs[u];
-        if (STATES) {  // S_c, the state before chunk c, for the backward
-          const auto rs = buffer_rsrc(p.states + ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
-                                      active ? DK * Dv * 4 : 0);
+        if (STATES) {  // S_c, the state before chunk c, for the backward (bf16: its operand type there)
+          const auto rs = buffer_rsrc(static_cast<uint16_t*>(p.states) +
+                                          ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
+                                      active ? DK * Dv * 2 : 0);
 #pragma unroll
           for (int i = 0; i < HB; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) buffer_store1(rs, (tau(hh * HB + i, lg, r) * Dv + j0 + lr) * 4, S[i][r]);
+            for (int r = 0; r < 4; ++r)
+              buffer_store1e<uint16_t>(rs, (tau(hh * HB + i, lg, r) * Dv + j0 + lr) * 2, S[i][r]);
         }
         // ---- interval A: partial Z = K[:, half] S[half] (token rows in tau order) ----
         bf16x8_t ka[HS][4];

@@ -94,6 +94,15 @@ __device__ __forceinline__ void buffer_store4<float>(__amdgpu_buffer_rsrc_t r, i
 __device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, int off, float a) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
 }
+// One value as an element of type E (bf16 rounded to nearest even, or fp32) at byte
+// offset `off`.
+template <typename E>
+__device__ __forceinline__ void buffer_store1e(__amdgpu_buffer_rsrc_t r, int off, float a) {
+  if constexpr (sizeof(E) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a), r, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
+}
 
 }  // namespace chunk
 }  // namespace gdn

@@ -552,7 +552,8 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(FwdParams p) {
         const float* Gs = sm.Gs[u];
         // phase 1
         if (STATES) {  // S_c, the state before chunk c, kept for the backward
-          const auto rs = buffer_rsrc(p.states + ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
+          const auto rs = buffer_rsrc(static_cast<float*>(p.states) +
+                                          ((slot0 + clampc(c)) * H + h) * static_cast<int64_t>(DK) * Dv,
                                       active ? DK * Dv * 4 : 0);
 #pragma unroll
           for (int x = 0; x < DPW; ++x) {

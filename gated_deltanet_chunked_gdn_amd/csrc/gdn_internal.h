@@ -53,7 +53,8 @@ struct FwdParams {
   float* seg_out;      // [G][N][H][Dk][ncol] end states, or nullptr
   int32_t final_to_sfinal;  // segment G - 1 writes S_final (layout [N][H][Dk][Dv])
   float* seg_ws;       // G > 1: ends, starts ([G][N][H][Dk][Dv] each), maps ([G][N][H][Dk][Dk])
-  float* states;       // or nullptr: S_c before every chunk, [chunk slot][H][Dk][Dv] fp32
+  void* states;        // or nullptr: S_c before every chunk, [chunk slot][H][Dk][Dv] in the
+                       // operand type (bf16 for bf16 products, fp32 for fp32 products)
 };
 
 enum : int32_t { kStartS0 = 0, kStartZero = 1, kStartIdentity = 2, kStartCarry = 3 };
@@ -98,8 +99,8 @@ struct BwdParams {
   float* dS0;             // or nullptr (not wanted)
   const void* tws;        // T of every chunk slot (io element type, 64 x 64)
   const void* prws;       // P of every chunk slot, row-major (io element type, 64 x 64)
-  const float* states;    // S_c before every chunk, [slot][H][Dk][Dv]
-  float* dstates;         // dS_{c+1} after every chunk, [slot][H][Dk][Dv]
+  const void* states;     // S_c before every chunk, [slot][H][Dk][Dv], operand type (as FwdParams)
+  void* dstates;          // dS_{c+1} after every chunk, [slot][H][Dk][Dv], operand type
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -198,8 +198,9 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* problem, const void* q, cons
  *   in : q, k, v, g, beta, S0 (NULL = zero), dO, dS_final (NULL = zero)
  *   out: dq, dk, dv (io dtype), dg, dbeta (fp32), dS0 (fp32; NULL = not wanted)
  * num_segments must be 1.  Workspace: GDN_PASS_CHUNK_BWD (T, T diag(beta), the
- * decays and the causal score P of every chunk, and the fp32 state before and
- * its gradient after every chunk). */
+ * decays and the causal score P of every chunk, and the state before and its
+ * gradient after every chunk, held in the products' operand type: bf16 for bf16
+ * io, fp32 for fp32 io, the type in which the gradient products consume them). */
 gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
                          const void* v, const float* g, const float* beta, const float* S0,
                          const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
@@ -213,8 +214,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem* problem, const void* q, const void* 
  *
  * gdn_chunk_fwd_save computes exactly what gdn_chunk_fwd computes (o, S_final;
  * the same arithmetic, so bit-identical results) and also fills `saved` with
- * T, T diag(beta), the decays and the causal score P of every chunk and the fp32
- * state before every chunk.  gdn_chunk_bwd_saved then runs only the reverse
+ * T, T diag(beta), the decays and the causal score P of every chunk and the state
+ * before every chunk (in the operand type, as for gdn_chunk_bwd).  gdn_chunk_bwd_saved then runs only the reverse
  * passes of gdn_chunk_bwd and gives bit-identical gradients, provided q, k, v, g,
  * beta, S0 and the problem are the same as in the gdn_chunk_fwd_save call and
  * `saved` was not modified in between (neither is checked: other contents give

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
@@ -195,14 +195,19 @@ def test_backward_entry_validates():
 
 def test_backward_workspace_size():
     # T (64 x 64), the T diag(beta) record (3072 io elements), the decays and P (64 x 64),
-    # each rounded up to 256 bytes, then fp32 states before and state gradients after
-    # every chunk slot; slots = rows // 64 + N + 1
+    # each rounded up to 256 bytes, then the states before and state gradients after
+    # every chunk slot in the products' operand type (bf16 here, fp32 for fp32 io);
+    # slots = rows // 64 + N + 1
     slots = 200 // 64 + 2 + 1
     up = lambda b: (b + 255) // 256 * 256
     st, n = ws(problem(Dv=96), nat.GDN_PASS_CHUNK_BWD)
     assert st == nat.GDN_OK
     assert n == (2 * up(slots * 3 * 4096 * 2) + up(slots * 3 * 3072 * 2) + up(slots * 3 * 128 * 4)
-                 + 2 * slots * 3 * 128 * 96 * 4)
+                 + 2 * slots * 3 * 128 * 96 * 2)
+    st, n = ws(problem(io_dtype=nat.GDN_FP32, Dk=64, Dv=96), nat.GDN_PASS_CHUNK_BWD)
+    assert st == nat.GDN_OK
+    assert n == (2 * up(slots * 3 * 4096 * 4) + up(slots * 3 * 3072 * 4) + up(slots * 3 * 128 * 4)
+                 + 2 * slots * 3 * 64 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
 
