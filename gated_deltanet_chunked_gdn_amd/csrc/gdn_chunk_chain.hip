@@ -34,6 +34,8 @@
 //                      straight into operand fragments;
 //   waves 4-5:         stage K, the v tile (transposed, fp32), T diag(beta) and the
 //                      decays of chunk c + 1 into the LDS ring and load chunk c + 3.
+// A pass without outputs (the backward's state pass, the segment maps) has four
+// waves, the state and staging waves, and no hand-off buffers.
 // Two workgroup barriers per chunk: X (the partial Z exchanged) and Y (end of step);
 // the output and staging work is spread over both intervals.  (Waves are placed on
 // the SIMDs round robin: each state wave shares its SIMD with a staging wave.)
@@ -81,7 +83,9 @@ __device__ __forceinline__ int ksw(int t) {
 template <int DK>
 __device__ __forceinline__ int kpos(int t, int u) { return t * DK + 8 * (u ^ ksw<DK>(t)); }
 
-template <int DK>
+// LDS of the state pass; without outputs (OUT false) there are no output waves and
+// no hand-off buffers for them.
+template <int DK, bool OUT>
 struct ChainSmem {
   static constexpr int LDV = 64 + 4;  // rows of the transposed v tile
   static constexpr int NKS = DK / 32;
@@ -89,9 +93,9 @@ struct ChainSmem {
   alignas(16) float Vt[2][16 * LDV];            // the v tile, transposed (fp32)
   alignas(16) float Gs[2][128];                 // Gamma, exp(gamma_n - gamma)
   alignas(16) bf16x8_t Tb[2][6][64];            // T diag(beta) operand fragments
-  alignas(16) bf16x8_t hand[3][NKS][64];        // S_c operand fragments (ring of 3: S_c is
-                                                // written in step c - 1, read in step c + 1)
-  alignas(16) f32x4_t handE[2][4][64];          // E_c (fp32, accumulator layout)
+  alignas(16) bf16x8_t hand[OUT ? 3 : 1][OUT ? NKS : 1][OUT ? 64 : 1];  // S_c operand fragments (ring of 3:
+                                                // S_c is written in step c - 1, read in step c + 1)
+  alignas(16) f32x4_t handE[OUT ? 2 : 1][OUT ? 4 : 1][OUT ? 64 : 1];    // E_c (fp32, accumulator layout)
   alignas(16) f32x4_t zx[2][4][64];             // partial Z of each state wave
 };
 
@@ -101,7 +105,7 @@ struct ChainSmem {
 template <int DK, bool STATES, bool OUT>
 __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 4 : 1))) void chunk_chain_kernel(
     FwdParams p) {
-  using SM = ChainSmem<DK>;
+  using SM = ChainSmem<DK, OUT>;
   constexpr int LDV = SM::LDV;
   constexpr int NKS = DK / 32;  // reduction steps over d_k
   constexpr int HS = NKS / 2;   // ... over the half of d_k a state wave holds
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 
 #pragma unroll
     for (int i = 0; i < HS; ++i) {
       Sf[i] = pack_pair(S[2 * i], S[2 * i + 1]);
-      sm.hand[0][hh * HS + i][lane] = Sf[i];
+      if (OUT) sm.hand[0][hh * HS + i][lane] = Sf[i];
     }
     __syncthreads();  // chunk 0 staged
     int c0 = 0;
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 
         // decayed E as the B operand of the update; E (fp32) to the output wave
         auto ed_of = [&](int mb) { return E[mb] * f32x4_t{d4[mb].x, d4[mb].y, d4[mb].z, d4[mb].w}; };
         const bf16x8_t Edf0 = pack_pair(ed_of(0), ed_of(1));
-        if (hh == 0) {
+        if (OUT && hh == 0) {
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) sm.handE[u][mb][lane] = E[mb];
         }
@@ -316,115 +320,117 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(DK == 64 ? 
 #pragma unroll
         for (int i = 0; i < HS; ++i) {
           Sf[i] = pack_pair(S[2 * i], S[2 * i + 1]);
-          sm.hand[(c + 1) % 3][hh * HS + i][lane] = Sf[i];  // S_{c+1}, for the output wave
+          if (OUT) sm.hand[(c + 1) % 3][hh * HS + i][lane] = Sf[i];  // S_{c+1}, for the output wave
         }
         __syncthreads();  // Y: end of step
       }
       c0 += 2;
     } while (c0 < nsteps);
     write_state();
-  } else if (w < 4) {
-    // ================= output waves: token row blocks 2 ow, 2 ow + 1 =================
-    if (nch == 0) return;
-    const int ow = w - 2;
-    // Q rows 16 nb + j (B operand of S^T Q^T), P rows 16 nb + j in the operand
-    // order the preparation kernel stores (fragment (nb, s) of 64 lanes), Gamma.
-    struct OutSet {
-      bf16x8_t qf[2][NKS];
-      bf16x8_t pf[2][2];  // [block][reduction step], step 1 only for blocks 2-3
-      float gq[2];
-    };
-    OutSet os[2];
-    auto load_q = [&](OutSet& st, int c) {
-      if (!OUT) return;
-      const int nv = chunk_rows(c);
-      const int64_t row0 = row0_of(c);
-      const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * 2);
+  } else if (OUT && w < 4) {
+    if constexpr (OUT) {  // (compiled only where the pass has outputs)
+      // ================= output waves: token row blocks 2 ow, 2 ow + 1 =================
+      if (nch == 0) return;
+      const int ow = w - 2;
+      // Q rows 16 nb + j (B operand of S^T Q^T), P rows 16 nb + j in the operand
+      // order the preparation kernel stores (fragment (nb, s) of 64 lanes), Gamma.
+      struct OutSet {
+        bf16x8_t qf[2][NKS];
+        bf16x8_t pf[2][2];  // [block][reduction step], step 1 only for blocks 2-3
+        float gq[2];
+      };
+      OutSet os[2];
+      auto load_q = [&](OutSet& st, int c) {
+        if (!OUT) return;
+        const int nv = chunk_rows(c);
+        const int64_t row0 = row0_of(c);
+        const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, ((nv - 1) * H * DK + DK) * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-          st.qf[i][s] = __builtin_bit_cast(
-              bf16x8_t, buf_load16(rq, ((16 * (2 * ow + i) + lr) * H * DK + 32 * s + 8 * lg) * 2));
-    };
-    auto load_p = [&](OutSet& st, int c) {
-      if (!OUT) return;
-      const int64_t sh = (slot0 + c) * H + h;
-      const auto rp = buffer_rsrc(pw + sh * 4096, 4096 * 2);
+          for (int s = 0; s < NKS; ++s)
+            st.qf[i][s] = __builtin_bit_cast(
+                bf16x8_t, buf_load16(rq, ((16 * (2 * ow + i) + lr) * H * DK + 32 * s + 8 * lg) * 2));
+      };
+      auto load_p = [&](OutSet& st, int c) {
+        if (!OUT) return;
+        const int64_t sh = (slot0 + c) * H + h;
+        const auto rp = buffer_rsrc(pw + sh * 4096, 4096 * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          if (s == 0 || ow == 1)
-            st.pf[i][s] = __builtin_bit_cast(bf16x8_t, buf_load16(rp, (((2 * ow + i) * 2 + s) * 64 + lane) * 16));
-      const auto rg = buffer_rsrc(gw + sh * 128, 256);
+          for (int s = 0; s < 2; ++s)
+            if (s == 0 || ow == 1)
+              st.pf[i][s] = __builtin_bit_cast(bf16x8_t, buf_load16(rp, (((2 * ow + i) * 2 + s) * 64 + lane) * 16));
+        const auto rg = buffer_rsrc(gw + sh * 128, 256);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) st.gq[i] = buf_load1(rg, (16 * (2 * ow + i) + lr) * 4);
-    };
-    // Output of chunk c in two parts: Y^T = S_c^T Q^T (interval A of step c + 1),
-    // then E_c^T P^T and the store (interval B of step c + 1).
-    f32x4_t y[2];
-    auto part_y = [&](int c, const OutSet& st) {
-      bf16x8_t sf[NKS];
+        for (int i = 0; i < 2; ++i) st.gq[i] = buf_load1(rg, (16 * (2 * ow + i) + lr) * 4);
+      };
+      // Output of chunk c in two parts: Y^T = S_c^T Q^T (interval A of step c + 1),
+      // then E_c^T P^T and the store (interval B of step c + 1).
+      f32x4_t y[2];
+      auto part_y = [&](int c, const OutSet& st) {
+        bf16x8_t sf[NKS];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) sf[s] = sm.hand[c % 3][s][lane];
+        for (int s = 0; s < NKS; ++s) sf[s] = sm.hand[c % 3][s][lane];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        y[i] = zero4();
+        for (int i = 0; i < 2; ++i) {
+          y[i] = zero4();
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) y[i] = mma(sf[s], st.qf[i][s], y[i]);
-      }
-    };
-    auto part_pe = [&](int c, int ue, OutSet& st) {
-      const bf16x8_t ef0 = pack_pair(sm.handE[ue][0][lane], sm.handE[ue][1][lane]);
-      bf16x8_t ef1 = ef0;
-      if (ow == 1) ef1 = pack_pair(sm.handE[ue][2][lane], sm.handE[ue][3][lane]);
-      const int cc = clampc(c), nv = chunk_rows(cc);
-      const auto ro = buffer_rsrc(o + (row0_of(cc) * H + h) * Dv + j0,
-                                  store_o && c < nch ? ((nv - 1) * H * Dv + 16) * 2 : 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f32x4_t pe = mma(ef0, st.pf[i][0], zero4());
-        if (ow == 1) pe = mma(ef1, st.pf[i][1], pe);
-        const float gt = st.gq[i];
-        buffer_store4<uint16_t>(ro, ((16 * (2 * ow + i) + lr) * H * Dv + 4 * lg) * 2,
-                                p.scale * (gt * y[i][0] + pe[0]), p.scale * (gt * y[i][1] + pe[1]),
-                                p.scale * (gt * y[i][2] + pe[2]), p.scale * (gt * y[i][3] + pe[3]));
-      }
-    };
-    load_q(os[0], 0);
-    load_p(os[0], 0);
-    load_q(os[1], clampc(1));
-    load_p(os[1], clampc(1));
-    __syncthreads();
-    int c0 = 0;
-    do {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = c0 + u;
-        // interval A of step c: Y^T of chunk c - 1, then Q of chunk c + 1
-        if (OUT && c > 0) {
-          part_y(c - 1, os[u ^ 1]);
-          load_q(os[u ^ 1], clampc(c + 1));
+          for (int s = 0; s < NKS; ++s) y[i] = mma(sf[s], st.qf[i][s], y[i]);
         }
-        __syncthreads();  // X
-        // interval B: the rest of chunk c - 1's output, then P and Gamma of chunk c + 1
-        if (OUT && c > 0) {
-          part_pe(c - 1, u ^ 1, os[u ^ 1]);
-          load_p(os[u ^ 1], clampc(c + 1));
+      };
+      auto part_pe = [&](int c, int ue, OutSet& st) {
+        const bf16x8_t ef0 = pack_pair(sm.handE[ue][0][lane], sm.handE[ue][1][lane]);
+        bf16x8_t ef1 = ef0;
+        if (ow == 1) ef1 = pack_pair(sm.handE[ue][2][lane], sm.handE[ue][3][lane]);
+        const int cc = clampc(c), nv = chunk_rows(cc);
+        const auto ro = buffer_rsrc(o + (row0_of(cc) * H + h) * Dv + j0,
+                                    store_o && c < nch ? ((nv - 1) * H * Dv + 16) * 2 : 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x4_t pe = mma(ef0, st.pf[i][0], zero4());
+          if (ow == 1) pe = mma(ef1, st.pf[i][1], pe);
+          const float gt = st.gq[i];
+          buffer_store4<uint16_t>(ro, ((16 * (2 * ow + i) + lr) * H * Dv + 4 * lg) * 2,
+                                  p.scale * (gt * y[i][0] + pe[0]), p.scale * (gt * y[i][1] + pe[1]),
+                                  p.scale * (gt * y[i][2] + pe[2]), p.scale * (gt * y[i][3] + pe[3]));
         }
-        __syncthreads();  // Y: S_c and E_c handed over
+      };
+      load_q(os[0], 0);
+      load_p(os[0], 0);
+      load_q(os[1], clampc(1));
+      load_p(os[1], clampc(1));
+      __syncthreads();
+      int c0 = 0;
+      do {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = c0 + u;
+          // interval A of step c: Y^T of chunk c - 1, then Q of chunk c + 1
+          if (OUT && c > 0) {
+            part_y(c - 1, os[u ^ 1]);
+            load_q(os[u ^ 1], clampc(c + 1));
+          }
+          __syncthreads();  // X
+          // interval B: the rest of chunk c - 1's output, then P and Gamma of chunk c + 1
+          if (OUT && c > 0) {
+            part_pe(c - 1, u ^ 1, os[u ^ 1]);
+            load_p(os[u ^ 1], clampc(c + 1));
+          }
+          __syncthreads();  // Y: S_c and E_c handed over
+        }
+        c0 += 2;
+      } while (c0 < nsteps);
+      if (OUT) {  // the last step's chunk
+        part_y(nsteps - 1, os[1]);
+        part_pe(nsteps - 1, 1, os[1]);
       }
-      c0 += 2;
-    } while (c0 < nsteps);
-    if (OUT) {  // the last step's chunk
-      part_y(nsteps - 1, os[1]);
-      part_pe(nsteps - 1, 1, os[1]);
     }
   } else {
     // ================= loader waves =================
     if (nch == 0) return;
-    const int lt = tid - 256;               // 0..127
+    const int lt = tid - (OUT ? 256 : 128);  // 0..127
     constexpr int KVR = DK / 8;             // 16-byte vectors per K row
     constexpr int NKV = 64 * KVR / 128;     // K vectors per loader thread
     struct LoadSet {
@@ -530,7 +536,7 @@ int cu_count_chain() {
 
 template <int DK, bool STATES, bool OUT>
 hipError_t launch_chain_t(const FwdParams& q, hipStream_t s) {
-  constexpr size_t need = sizeof(ChainSmem<DK>);
+  constexpr size_t need = sizeof(ChainSmem<DK, OUT>);
   static_assert(DK == 64 || DK == 128, "K swizzle defined for 8 or 16 pieces per row");
   static_assert(need <= 160 * 1024, "LDS budget exceeded");
   // A grid with fewer than two workgroups per compute unit asks for more than half
@@ -541,7 +547,8 @@ hipError_t launch_chain_t(const FwdParams& q, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(384), smem, s, q);
+  // (without outputs: the two state waves and the two loader waves only)
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(OUT ? 384 : 256), smem, s, q);
   return hipGetLastError();
 }
 
