@@ -164,14 +164,16 @@ struct DStateSmem {
   E Qs[64 * LDK];   // Q rows
   E Tm[64 * LDC];   // T rows
   E Pr[64 * LDC];   // P rows (from the preparation kernel)
-  E dB[16 * LDB];   // [ dOs^T | dE^T ] of this tile
-  E dU[16 * LDB];   // [ (diag(Gamma) dOs)^T | (-diag(beta Gamma) T^T dE)^T ] of this tile
-  E dSt[16 * LDK];  // dS^T of this tile
+  E dB[2][16 * LDB];   // [ dOs^T | dE^T ] of each of the two tiles
+  E dU[2][16 * LDB];   // [ (diag(Gamma) dOs)^T | (-diag(beta Gamma) T^T dE)^T ] of each tile
+  E dSt[2][16 * LDK];  // dS^T of each tile
   float Gam[64], dec[64], bg[64];
 };
 
+// Two 16-column tiles of d_v per workgroup: waves 0-3 take the first, waves 4-7 the
+// second, and all eight stage the chunk's K, Q, T and P once for both.
 template <int DK, typename Op>
-__global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void chunk_dstate_kernel(BwdParams p) {
   using E = typename Op::elem;
   using SM = DStateSmem<DK, Op>;
   constexpr int LDK = SM::LDK, LDC = SM::LDC, LDB = SM::LDB, KS = Op::KSTEP;
@@ -185,34 +187,41 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   const E* __restrict__ prw = static_cast<const E*>(p.prws);
   const E* __restrict__ tws = static_cast<const E*>(p.tws);
 
-  const int H = p.H, Dv = p.Dv, NT = Dv / 16;
+  const int H = p.H, Dv = p.Dv, NT = Dv / 16, NP = (NT + 1) / 2;
   const int NB = gridDim.x, L = blockIdx.x;
   const int vb = (NB % 8 == 0) ? (L % 8) * (NB / 8) + L / 8 : L;  // tiles of a head share an XCD
-  const int tile = vb % NT, nh = vb / NT, h = nh % H, n = nh / H;
-  const int j0 = tile * 16;
+  const int tp = vb % NP, nh = vb / NP, h = nh % H, n = nh / H;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wt = w >> 2, wl = w & 3;  // this wave's tile of the pair, its wave within the tile
+  const int tile = 2 * tp + wt;
+  const bool tile_ok = tile < NT;     // (an odd count of tiles leaves the last pair's second empty)
+  const int j0 = (tile_ok ? tile : NT - 1) * 16;
+  E* const dB = sm.dB[wt];
+  E* const dU = sm.dU[wt];
+  E* const dSt = sm.dSt[wt];
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
   const int nch = static_cast<int>((len + 63) / 64);
   const int64_t slot0 = bos / 64 + n;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t nhS = (static_cast<int64_t>(n) * H + h) * DK;
 
   f32x4_t dS[SRB];
 #pragma unroll
   for (int sr = 0; sr < SRB; ++sr) {
-    const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+    const int i = 16 * (wl * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = p.dS_final ? p.dS_final[(nhS + i + r) * Dv + j0 + j] : 0.f;
     dS[sr] = f32x4_t{x[0], x[1], x[2], x[3]};
-    store4<E>(sm.dSt + j * LDK + i, x[0], x[1], x[2], x[3]);
+    store4<E>(dSt + j * LDK + i, x[0], x[1], x[2], x[3]);
   }
 
   // The global operands of chunk c - 1 (K, Q, T, dOs, the gates) are loaded into
   // registers while chunk c is processed, and staged into LDS at the start of
   // the next step: the load latency hides behind the products.
-  constexpr int NSV = 64 * (DK / EPV) / 256;  // K (and Q) vectors per thread
-  constexpr int NTV = 64 * 64 / EPV / 256;    // T vectors per thread
+  constexpr int NSV = 64 * (DK / EPV) / 512;  // K (and Q) vectors per thread
+  constexpr int NTV = 64 * 64 / EPV / 512;    // T vectors per thread
+  static_assert(NSV * 512 == 64 * (DK / EPV) && NTV * 512 == 64 * 64 / EPV, "whole vectors per thread");
   // Loads go through buffer resources bounded to the chunk's valid rows, so rows
   // past its end read as zeros without a branch or a select (either would make
   // the wave wait for every load in flight at that point), and the lane offsets
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   constexpr int ES = static_cast<int>(sizeof(E));
   struct Pre {
     u32x4_t kv[NSV], qv[NSV], tv[NTV], pv[NTV];
-    u32x4_t dor;  // four dO values of row tid / 4 (raw io elements)
+    u32x4_t dor;  // four dO values of this wave's tile, row (tid % 256) / 4 (raw io elements)
     float gv, bv;
   };
   auto load_pre = [&](Pre& pr, int c) {
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     const auto rq = buffer_rsrc(q + (row0 * H + h) * DK, rowk);
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
-      const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
       pr.kv[i] = bload16(rk, (t * H * DK + cv) * ES);
       pr.qv[i] = bload16(rq, (t * H * DK + cv) * ES);
     }
@@ -239,12 +248,12 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     const auto rp = buffer_rsrc(prw + ((slot0 + c) * H + h) * 4096, 4096 * ES);
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
-      const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+      const int x = tid + 512 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
       pr.tv[i] = bload16(rt, (t * 64 + cv) * ES);
       pr.pv[i] = bload16(rp, (t * 64 + cv) * ES);
     }
     {
-      const int t = tid >> 2, cq = (tid & 3) * 4;
+      const int t = (tid & 255) >> 2, cq = (tid & 3) * 4;
       const auto ro = buffer_rsrc(dO + (row0 * H + h) * Dv + j0, ((nv - 1) * H * Dv + 16) * ES);
       if constexpr (sizeof(E) == 2) {
         const auto u = __builtin_amdgcn_raw_buffer_load_b64(ro, (t * H * Dv + cq) * ES, 0, 0);
@@ -263,13 +272,13 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   auto stage_pre = [&](const Pre& pr) {
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
-      const int x = tid + 256 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
+      const int x = tid + 512 * i, t = x / (DK / EPV), cv = (x % (DK / EPV)) * EPV;
       st16(sm.Ks + t * LDK + cv, pr.kv[i]);
       st16(sm.Qs + t * LDK + cv, pr.qv[i]);
     }
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
-      const int x = tid + 256 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
+      const int x = tid + 512 * i, t = x / (64 / EPV), cv = (x % (64 / EPV)) * EPV;
       st16(sm.Tm + t * LDC + cv, pr.tv[i]);
       st16(sm.Pr + t * LDC + cv, pr.pv[i]);
     }
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       sm.bg[lane] = pr.bv * G;
     }
     {
-      const int t = tid >> 2, cq = (tid & 3) * 4;
+      const int t = (tid & 255) >> 2, cq = (tid & 3) * 4;
       const float Gt = __shfl(G, t, 64);
       float dov[4];
       if constexpr (sizeof(E) == 2) {
@@ -298,8 +307,8 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = dov[e];
-        sm.dB[(cq + e) * LDB + t] = Op::cvt(p.scale * x);
-        sm.dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * x);
+        dB[(cq + e) * LDB + t] = Op::cvt(p.scale * x);
+        dU[(cq + e) * LDB + t] = Op::cvt(p.scale * Gt * x);
       }
     }
   };
@@ -309,10 +318,10 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
   for (int c = nch - 1; c >= 0; --c) {
     {  // dS_{c+1}, the gradient of the state after chunk c
       const auto rd = buffer_rsrc(static_cast<E*>(p.dstates) + ((slot0 + c) * H + h) * static_cast<int64_t>(DK) * Dv,
-                                  DK * Dv * static_cast<int>(sizeof(E)));
+                                  tile_ok ? DK * Dv * static_cast<int>(sizeof(E)) : 0);
 #pragma unroll
       for (int sr = 0; sr < SRB; ++sr) {
-        const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+        const int i = 16 * (wl * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           buffer_store1e<E>(rd, ((i + r) * Dv + j0 + j) * static_cast<int>(sizeof(E)), dS[sr][r]);
@@ -323,27 +332,27 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
     if (c > 0) load_pre(pre, c - 1);
     __syncthreads();
 
-    // ---- dE = diag(decay) K dS + P^T dOs, token block w ----
+    // ---- dE = diag(decay) K dS + P^T dOs, token block wl of this wave's tile ----
     {
       f32x4_t acc = zero4();
-      tile_mma<Op, DK>(acc, sm.Ks + 16 * w * LDK, LDK, sm.dSt, LDK, lane);
+      tile_mma<Op, DK>(acc, sm.Ks + 16 * wl * LDK, LDK, dSt, LDK, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= sm.dec[16 * w + 4 * (lane >> 4) + r];
-      for (int ks = (16 * w) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag_tr(sm.Pr + 16 * w, LDC, lane, ks * KS), Op::frag(sm.dB, LDB, lane, ks * KS), acc);
-      store_t<E>(sm.dB + 64 + 16 * w, LDB, acc, lane);
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.dec[16 * wl + 4 * (lane >> 4) + r];
+      for (int ks = (16 * wl) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag_tr(sm.Pr + 16 * wl, LDC, lane, ks * KS), Op::frag(dB, LDB, lane, ks * KS), acc);
+      store_t<E>(dB + 64 + 16 * wl, LDB, acc, lane);
     }
     __syncthreads();
 
-    // ---- F = T^T dE (token block w; T is lower triangular), scaled to -beta Gamma F ----
+    // ---- F = T^T dE (token block wl; T is lower triangular), scaled to -beta Gamma F ----
     // (-W^T dE = K^T diag(-beta Gamma) T^T dE, so W itself is never formed)
     {
       f32x4_t acc = zero4();
-      for (int ks = (16 * w) / KS; ks < 64 / KS; ++ks)
-        acc = Op::mma(Op::frag_tr(sm.Tm + 16 * w, LDC, lane, ks * KS), Op::frag(sm.dB + 64, LDB, lane, ks * KS), acc);
+      for (int ks = (16 * wl) / KS; ks < 64 / KS; ++ks)
+        acc = Op::mma(Op::frag_tr(sm.Tm + 16 * wl, LDC, lane, ks * KS), Op::frag(dB + 64, LDB, lane, ks * KS), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= -sm.bg[16 * w + 4 * (lane >> 4) + r];
-      store_t<E>(sm.dU + 64 + 16 * w, LDB, acc, lane);
+      for (int r = 0; r < 4; ++r) acc[r] *= -sm.bg[16 * wl + 4 * (lane >> 4) + r];
+      store_t<E>(dU + 64 + 16 * wl, LDB, acc, lane);
     }
     __syncthreads();
 
@@ -352,25 +361,25 @@ __global__ __launch_bounds__(256) void chunk_dstate_kernel(BwdParams p) {
       const float gn = sm.Gam[63];
 #pragma unroll
       for (int sr = 0; sr < SRB; ++sr) {
-        const int rb = w * SRB + sr;
+        const int rb = wl * SRB + sr;
         f32x4_t acc = dS[sr] * gn;
 #pragma unroll
         for (int ks = 0; ks < 64 / KS; ++ks)
-          acc = Op::mma(Op::frag_tr(sm.Qs + 16 * rb, LDK, lane, ks * KS), Op::frag(sm.dU, LDB, lane, ks * KS), acc);
+          acc = Op::mma(Op::frag_tr(sm.Qs + 16 * rb, LDK, lane, ks * KS), Op::frag(dU, LDB, lane, ks * KS), acc);
 #pragma unroll
         for (int ks = 0; ks < 64 / KS; ++ks)
-          acc = Op::mma(Op::frag_tr(sm.Ks + 16 * rb, LDK, lane, ks * KS), Op::frag(sm.dU + 64, LDB, lane, ks * KS),
+          acc = Op::mma(Op::frag_tr(sm.Ks + 16 * rb, LDK, lane, ks * KS), Op::frag(dU + 64, LDB, lane, ks * KS),
                         acc);
         dS[sr] = acc;
-        store_t<E>(sm.dSt + 16 * rb, LDK, acc, lane);
+        store_t<E>(dSt + 16 * rb, LDK, acc, lane);
       }
     }
     __syncthreads();
   }
-  if (p.dS0) {
+  if (p.dS0 && tile_ok) {
 #pragma unroll
     for (int sr = 0; sr < SRB; ++sr) {
-      const int i = 16 * (w * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
+      const int i = 16 * (wl * SRB + sr) + 4 * (lane >> 4), j = lane & 15;
 #pragma unroll
       for (int r = 0; r < 4; ++r) p.dS0[(nhS + i + r) * Dv + j0 + j] = dS[sr][r];
     }
@@ -887,7 +896,7 @@ hipError_t launch_bwd_t(const BwdParams& b, hipStream_t s) {
   if (e != hipSuccess) return e;
   auto dstate = chunk_dstate_kernel<DK, Op>;
   auto grad = chunk_grad_kernel<DK, Op>;
-  hipLaunchKernelGGL(dstate, dim3(b.N * b.H * (b.Dv / 16)), dim3(256), ds_smem, s, b);
+  hipLaunchKernelGGL(dstate, dim3(b.N * b.H * ((b.Dv / 16 + 1) / 2)), dim3(512), ds_smem, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (b.max_chunks == 0) return hipSuccess;
   hipLaunchKernelGGL(grad, dim3(b.max_chunks, b.H, b.N), dim3(512), gr_smem, s, b);
