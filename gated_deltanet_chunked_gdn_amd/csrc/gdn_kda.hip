@@ -99,6 +99,17 @@ __device__ __forceinline__ f32x4_t ld4f<float>(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
 
+// The diagonal 16x16 blocks of A and P factor through their first row r:
+// exp(gamma_i - gamma_j) = exp(gamma_i - gamma_r) exp(gamma_r - gamma_j) for
+// r <= j <= i, the first factor <= 1 and the second >= 1 but at most the block's
+// own decay from row r to row r + 15.  While no channel decays by more than
+// 2^kMaxBlockDrop across any diagonal block (log2 units), both factors and their
+// products with the keys and queries stay far inside fp32 and the blocks are MFMA
+// products like the others; a chunk with a steeper block takes the exact
+// pair-by-pair sums instead.  The flag lives in an unused entry above A's diagonal.
+constexpr float kMaxBlockDrop = 100.f;
+constexpr int kSteepAt = 63;  // A's entry (0, 63)
+
 // Eight values to eight consecutive operand elements (16-byte aligned): one
 // 16-byte store for bf16 (round to nearest even), two for fp32.
 template <typename EL>
@@ -177,20 +188,25 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
       *reinterpret_cast<u32x4_t*>(gs + gidx(i, ch + 4)) = ok ? gr[u][1] : z;
     }
     if (tid < 64) As[tid * 64 + tid] = tid < nr ? bv : 0.f;
+    if (tid == 0) As[kSteepAt] = 0.f;
   }
   __syncthreads();
   if (tid < DK) {  // channel tid: its 64 values are read at once, summed in registers (log2 units)
     float col[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) col[i] = gs[gidx(i, tid)] * chunk::kLog2e;
-    float acc = 0.f;
+    float acc = 0.f, first = 0.f, drop = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       acc += col[i];
       gs[gidx(i, tid)] = acc;
+      if (i % 16 == 0) first = acc;
+      if (i % 16 == 15) drop = fmaxf(drop, first - acc);
     }
+    if (drop > kMaxBlockDrop) As[kSteepAt] = 1.f;  // (every writer stores the same value)
   }
   __syncthreads();
+  const bool steep = As[kSteepAt] != 0.f;  // uniform over the workgroup
 
   // A and P.  Below the 16x16 diagonal blocks, block (bi, bj) factors through the
   // last row r = 16 bj + 15 of block bj: exp(gamma_i - gamma_j) =
@@ -199,19 +215,19 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   // waves 0-5 take one such block each.  A lane reads four consecutive channels of
   // its rows at once and feeds them to four products (in the product of k-step
   // (k0, e) the lanes of group g hold channel k0 + 4 g + e, in both operands).
-  // The diagonal blocks (pairs j <= i inside a block) are summed pair by pair, one
-  // exponential per channel: every thread takes one of the first 512 pairs whole
-  // and an eighth of a channel range of one of the last 32, whose sixteen parts are
-  // added within a DPP row.
-  if (wave < 6) {
-    const int bi = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;  // (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
-    const int bj = wave < 3 ? 0 : wave < 5 ? 1 : 2;
-    const int ia = 16 * bi + (lane & 15), jb = 16 * bj + (lane & 15), r = 16 * bj + 15;
-    f32x4_t accA = zero4(), accP = zero4();
+  // The diagonal blocks go the same way through their first row (waves 6 and 7,
+  // two blocks each) unless the chunk is steep; then they are summed pair by pair,
+  // one exponential per channel: every thread takes one of the first 512 pairs
+  // whole and an eighth of a channel range of one of the last 32, whose sixteen
+  // parts are added within a DPP row.
+  // rows ia (A operand) and jb (B operand) of this lane, both decayed to row rr
+  auto decayed_product = [&](int ia, int jb, int rr, f32x4_t& accA, f32x4_t& accP) {
+    accA = zero4();
+    accP = zero4();
 #pragma unroll 2
     for (int k0 = 0; k0 < DK; k0 += 16) {
       const int ch = k0 + 4 * (lane >> 4);
-      const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gs + gidx(r, ch));
+      const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gs + gidx(rr, ch));
       const f32x4_t gi = *reinterpret_cast<const f32x4_t*>(gs + gidx(ia, ch));
       const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(gs + gidx(jb, ch));
       const f32x4_t ki = ld4f<E>(ks + kidx(ia, ch)), qi = ld4f<E>(qs + kidx(ia, ch)), kj = ld4f<E>(ks + kidx(jb, ch));
@@ -223,14 +239,33 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         accP = __builtin_amdgcn_mfma_f32_16x16x4f32(qi[e] * ei, bk, accP, 0, 0, 0);
       }
     }
+  };
+  if (wave < 6) {
+    const int bi = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;  // (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
+    const int bj = wave < 3 ? 0 : wave < 5 ? 1 : 2;
+    f32x4_t accA, accP;
+    decayed_product(16 * bi + (lane & 15), 16 * bj + (lane & 15), 16 * bj + 15, accA, accP);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int i = 16 * bi + 4 * (lane >> 4) + q4, j = 16 * bj + (lane & 15);
       As[i * 64 + j] = As[i * 64 + i] * accA[q4];
       rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
     }
+  } else if (!steep) {
+#pragma unroll 1
+    for (int x = 0; x < 2; ++x) {
+      const int b = 2 * (wave - 6) + x;
+      f32x4_t accA, accP;
+      decayed_product(16 * b + (lane & 15), 16 * b + (lane & 15), 16 * b, accA, accP);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int i = 16 * b + 4 * (lane >> 4) + q4, j = 16 * b + (lane & 15);
+        if (j < i) As[i * 64 + j] = As[i * 64 + i] * accA[q4];
+        if (j <= i) rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
+      }
+    }
   }
-  {
+  if (steep) {
     // pair tl of diagonal block b: row il, column jl <= il inside the block
     auto pair_of = [](int t, int& i, int& j) {
       const int b = t / 136, tl = t % 136;

@@ -73,17 +73,30 @@ def test_kda_matches_oracle(w):
     _check(d, _run(d, to_device(d)), _oracle(d), w.name)
 
 
-@pytest.mark.parametrize("kind", ["strong", "slow"])
+@pytest.mark.parametrize("kind", ["strong", "slow", "steep", "bounded"])
 def test_kda_decay_extremes(kind):
+    # The preparation forms the diagonal 16x16 blocks of A and P as products through
+    # their first row while no channel decays by more than 2^-100 across one block,
+    # and pair by pair otherwise: "steep" takes the pair-by-pair path in every chunk,
+    # "bounded" (up to ~2^-87 per block) never does, "strong" mixes both.
     w = Workload(f"kda_{kind}", 1, 260, 2, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel",
                  s0_std=0.1, seed=55)
     d = generate(w)
     rng = np.random.default_rng(56)
+    shape = d["q"].shape
     if kind == "strong":
         # per-channel log-decays down to -5 per token: exp(gamma) underflows within a chunk
-        d["g"] = (-5.0 / (1.0 + np.exp(-rng.standard_normal(d["q"].shape)))).astype(np.float32)
+        d["g"] = (-5.0 / (1.0 + np.exp(-rng.standard_normal(shape)))).astype(np.float32)
+    elif kind == "steep":
+        # channel 0 of every head decays by 7 per token: 105 nats across a block
+        g = -4.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+        g[..., 0] = -7.0
+        d["g"] = g.astype(np.float32)
+    elif kind == "bounded":
+        # at most 4 per token: at most 60 nats (87 in log2) across a block
+        d["g"] = (-4.0 / (1.0 + np.exp(-3.0 * rng.standard_normal(shape)))).astype(np.float32)
     else:
-        d["g"] = (-1e-3 * rng.random(d["q"].shape)).astype(np.float32)
+        d["g"] = (-1e-3 * rng.random(shape)).astype(np.float32)
     _check(d, _run(d, to_device(d)), _oracle(d), w.name)
 
 
