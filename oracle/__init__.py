@@ -9,7 +9,8 @@ float64 numpy (the normalisation and the
 gate formulas written out; pinned in tests/test_oracle_pins.py).
 
 ``kda_fwd`` is the same recurrence with one decay per key channel (numpy,
-float64; pinned in tests/test_oracle_kda_pins.py).
+float64) and ``kda_bwd`` its reverse mode (pinned in tests/test_oracle_kda_pins.py
+and tests/test_oracle_kda_bwd_pins.py).
 
 ``fwd`` / ``bwd`` wrap ``liboracle.so`` (built from ``gdn_oracle.c`` with gcc):
 the plain token-by-token recurrence of the Day-1 page ("Research Sprint Day 1",
@@ -213,19 +214,9 @@ def epilogue(o, z, weight=None, eps=1e-6):
     return o / rms * w * (z / (1.0 + np.exp(-z)))
 
 
-def kda_fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0):
-    """Gated delta rule with a per-key-channel decay, token by token, in float64.
-
-    The update of "Research Sprint Day 1" ("The GDN update") with the scalar
-    forget factor replaced by a diagonal one: g holds one log-decay per (token,
-    head, key channel), the gate layout of the cuLA issue #126 page ("Minimal
-    public reproduction", g shaped like q).  Per token, with a = exp(g_t) of
-    length Dk:
-        S <- diag(a) S,  r = S^T k_t,  e = beta_t (v_t - r),  S <- S + k_t e^T,
-        o_t = scale S^T q_t.
-    Shapes: q, k, g (B, T, H, Dk) or packed (Ttot, H, Dk); v (..., H, Dv);
-    beta (..., H); S0 / S_final (N, H, Dk, Dv).  Returns (o, S_final) in float64.
-    """
+def _kda_unpack(q, k, v, g, beta, cu_seqlens):
+    """Float64 copies flattened to (Ttot, H, .) rows, the sequence offsets and the
+    leading shape of the outputs (dense (B, T) or packed (Ttot,))."""
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     if g.shape != q.shape:
         raise ValueError("g must be shaped like q (one log-decay per key channel)")
@@ -245,8 +236,25 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0):
     H, Dk = q.shape[-2:]
     Dv = v.shape[-1]
     q, k, g = (x.reshape(-1, H, Dk) for x in (q, k, g))
-    v = v.reshape(-1, H, Dv)
-    beta = beta.reshape(-1, H)
+    return q, k, v.reshape(-1, H, Dv), g, beta.reshape(-1, H), cu, lead
+
+
+def kda_fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0):
+    """Gated delta rule with a per-key-channel decay, token by token, in float64.
+
+    The update of "Research Sprint Day 1" ("The GDN update") with the scalar
+    forget factor replaced by a diagonal one: g holds one log-decay per (token,
+    head, key channel), the gate layout of the cuLA issue #126 page ("Minimal
+    public reproduction", g shaped like q).  Per token, with a = exp(g_t) of
+    length Dk:
+        S <- diag(a) S,  r = S^T k_t,  e = beta_t (v_t - r),  S <- S + k_t e^T,
+        o_t = scale S^T q_t.
+    Shapes: q, k, g (B, T, H, Dk) or packed (Ttot, H, Dk); v (..., H, Dv);
+    beta (..., H); S0 / S_final (N, H, Dk, Dv).  Returns (o, S_final) in float64.
+    """
+    q, k, v, g, beta, cu, lead = _kda_unpack(q, k, v, g, beta, cu_seqlens)
+    H, Dk = q.shape[-2:]
+    Dv = v.shape[-1]
     N = len(cu) - 1
     S0 = _f64(S0)
     if S0 is not None and S0.shape != (N, H, Dk, Dv):
@@ -263,3 +271,68 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens=None, S0=None, scale=1.0):
             o[t] = scale * np.einsum("hkv,hk->hv", S, q[t])      # read after the write
         Sf[n] = S
     return o.reshape(lead + (H, Dv)), Sf
+
+
+def kda_bwd(q, k, v, g, beta, dO, cu_seqlens=None, S0=None, dS_final=None, scale=1.0):
+    """Reverse mode of ``kda_fwd``, token by token, in float64.
+
+    Gradients of L = <o, dO> + <S_final, dS_final> with respect to q, k, v, the
+    per-channel log-decays g, beta and S0.  The forward states S_0 .. S_L of each
+    sequence are kept, then the steps of ``kda_fwd`` are undone last to first
+    (the same forget / read / write / read order of "Research Sprint Day 1",
+    "The GDN update", with the forget factor diagonal over key channels):
+        o_t = scale S_t^T q_t     ->  dS += scale q_t do_t^T,  dq_t = scale S_t do_t
+        S_t = S' + k_t e^T        ->  dk_t = dS e,  de = dS^T k_t
+        e = beta_t (v_t - r)      ->  dv_t = beta_t de,  dbeta_t = <de, v_t - r>,
+                                      dr = -beta_t de
+        r = S'^T k_t              ->  dS' = dS + k_t dr^T,  dk_t += S' dr
+        S' = diag(a) S_{t-1}      ->  dg_t = a o rowsum(dS' o S_{t-1}),
+                                      dS_{t-1} = diag(a) dS'
+    with a = exp(g_t).  Shapes as ``kda_fwd``; dg has g's shape.  Returns a dict
+    dq, dk, dv, dg, dbeta, dS0.
+    """
+    q, k, v, g, beta, cu, lead = _kda_unpack(q, k, v, g, beta, cu_seqlens)
+    H, Dk = q.shape[-2:]
+    Dv = v.shape[-1]
+    N = len(cu) - 1
+    dO = _f64(dO).reshape(-1, H, Dv)
+    S0 = _f64(S0)
+    dSf = _f64(dS_final)
+    for name, x in (("S0", S0), ("dS_final", dSf)):
+        if x is not None and x.shape != (N, H, Dk, Dv):
+            raise ValueError(f"{name} must be {(N, H, Dk, Dv)}")
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "dg": np.zeros_like(g), "dbeta": np.zeros_like(beta), "dS0": np.zeros((N, H, Dk, Dv))}
+    for n in range(N):
+        t0, t1 = cu[n], cu[n + 1]
+        S = np.zeros((H, Dk, Dv)) if S0 is None else S0[n].copy()
+        states = [S.copy()]
+        for t in range(t0, t1):
+            S *= np.exp(g[t])[:, :, None]
+            r = np.einsum("hkv,hk->hv", S, k[t])
+            S += k[t][:, :, None] * (beta[t][:, None] * (v[t] - r))[:, None, :]
+            states.append(S.copy())
+        dS = np.zeros((H, Dk, Dv)) if dSf is None else dSf[n].copy()
+        for t in range(t1 - 1, t0 - 1, -1):
+            a = np.exp(g[t])
+            Sprev = states[t - t0]
+            Sp = a[:, :, None] * Sprev                                   # S'
+            r = np.einsum("hkv,hk->hv", Sp, k[t])
+            e = beta[t][:, None] * (v[t] - r)
+            Scur = states[t - t0 + 1]
+            dS += scale * q[t][:, :, None] * dO[t][:, None, :]
+            out["dq"][t] = scale * np.einsum("hkv,hv->hk", Scur, dO[t])
+            dk = np.einsum("hkv,hv->hk", dS, e)
+            de = np.einsum("hkv,hk->hv", dS, k[t])
+            out["dv"][t] = beta[t][:, None] * de
+            out["dbeta"][t] = np.einsum("hv,hv->h", de, v[t] - r)
+            dr = -beta[t][:, None] * de
+            dS += k[t][:, :, None] * dr[:, None, :]
+            out["dk"][t] = dk + np.einsum("hkv,hv->hk", Sp, dr)
+            out["dg"][t] = a * np.einsum("hkv,hkv->hk", dS, Sprev)
+            dS *= a[:, :, None]
+        out["dS0"][n] = dS
+    for name in ("dq", "dk", "dv", "dg"):
+        out[name] = out[name].reshape(lead + out[name].shape[1:])
+    out["dbeta"] = out["dbeta"].reshape(lead + (H,))
+    return out
