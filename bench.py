@@ -73,7 +73,7 @@ def event_times(call, n_calls, warmup, stream):
     return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
 
-EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda", "kda_segment_split", "policy")
+EXTRAS = ("bwd", "segment_split", "prologue", "epilogue", "kda", "kda_bwd", "kda_segment_split", "policy")
 
 
 def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRAS):
@@ -225,6 +225,27 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
         out["kda"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3, "tokens_per_s": w.B * w.T / float(kt.mean()),
                       "alg_bytes_per_launch": nb, "alg_GBps": nb / float(kt.mean()) / 1e9,
                       "kernels": "kda_prep_kernel + kda_state_kernel"}
+    if "kda_bwd" in which:
+        # backward of the per-key-channel-decay pass (gdn_kda_chunk_bwd) on the same shape
+        w = WORKLOADS["kda_bf16"]
+        d = generate(w)
+        t = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+        t.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta")})
+        del d
+        rng = np.random.default_rng(11)
+        t["dO"] = torch.from_numpy(rng.standard_normal((w.B, w.T, w.H, w.Dv), dtype=np.float32)).to(dev).to(
+            torch.bfloat16)
+        kt = event_times(lambda i: gdn.kda_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"],
+                                                     scale=w.scale, want_dS0=False), steps, warmup, stream)
+        th = w.B * w.T * w.H
+        # q, k, v, dO read and dq, dk, dv written (bf16); g read and dg written (Dk fp32 per
+        # token-head); beta read and dbeta written
+        nb = th * ((2 * w.Dk + 2 * w.Dv) * 2 + (2 * w.Dk + w.Dv) * 2 + 2 * (w.Dk * 4 + 4))
+        out["kda_bwd"] = {"workload": w.name, "ms_mean": float(kt.mean()) * 1e3,
+                          "tokens_per_s": w.B * w.T / float(kt.mean()), "alg_bytes_per_launch": nb,
+                          "alg_GBps": nb / float(kt.mean()) / 1e9,
+                          "kernels": "kda_prep_kernel + kda_state_kernel (states) + kda_dstate_kernel + kda_grad_kernel"}
+        del t
     if "policy" in which:
         # latency, workspace and peak device memory of one forward call per precision
         # policy on the same bf16 inputs (the metric shape, B=4 T=4096 H=8 d=128):

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gdn_abi.cpp", "gdn_noalloc.cpp", "gdn_chunk_fwd.hip", "gdn_chunk_chain.hip", "gdn_chunk_bwd.hip", "gdn_recurrent.hip", "gdn_prologue.hip",
-           "gdn_epilogue.hip", "gdn_kda.hip", "gdn_copy.hip"]
+           "gdn_epilogue.hip", "gdn_kda.hip", "gdn_kda_bwd.hip", "gdn_copy.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]

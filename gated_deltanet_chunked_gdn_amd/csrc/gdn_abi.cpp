@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "gdn_internal.h"
+#include "gdn_kda_common.h"
 
 namespace {
 
@@ -41,7 +42,7 @@ struct Checked {
   size_t ce = 4;         // bytes per element of the per-chunk records (the product operand type)
 };
 
-enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd, KdaFwd };
+enum class Kind { ChunkFwd, ChunkBwd, RecFwd, RecBwd, KdaFwd, KdaBwd };
 
 gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (!p) return GDN_ERR_NULL;
@@ -53,7 +54,8 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
   if (p->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (p->precision != GDN_PRECISION_IO && p->precision != GDN_PRECISION_FP32) return GDN_ERR_UNSUPPORTED;
   const bool fp32_policy_bf16 = p->precision == GDN_PRECISION_FP32 && p->io_dtype == GDN_BF16;
-  if (fp32_policy_bf16 && (kind == Kind::ChunkBwd || kind == Kind::KdaFwd)) return GDN_ERR_UNSUPPORTED;
+  if (fp32_policy_bf16 && (kind == Kind::ChunkBwd || kind == Kind::KdaFwd || kind == Kind::KdaBwd))
+    return GDN_ERR_UNSUPPORTED;
   const bool chunked = kind == Kind::ChunkFwd || kind == Kind::ChunkBwd;
   if (chunked) {
     const int G = p->num_segments;
@@ -69,6 +71,12 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
     // one state-kernel launch has up to G * N * H * (max(Dk, Dv) / 16) blocks
     if (static_cast<int64_t>(G) * p->num_seqs * p->H * (std::max(p->Dk, p->Dv) / 16) > INT32_MAX)
       return GDN_ERR_UNSUPPORTED;
+  }
+  if (kind == Kind::KdaBwd) {
+    if (p->num_segments != 1) return GDN_ERR_UNSUPPORTED;
+    // one chunk of one head's rows is addressed with 32-bit byte offsets
+    if (static_cast<int64_t>(64) * p->H * std::max(p->Dk, p->Dv) * 4 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(p->num_seqs) * p->H * (p->Dv / 16) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   }
   if (kind == Kind::RecBwd && static_cast<size_t>(2) * p->Dk * (p->Dv + 1) * 4 +
                                       (2 * gdn::kRecBlock * p->Dk + 2 * gdn::kRecBlock + 8) * 4 >
@@ -132,6 +140,17 @@ size_t kda_rec_region(const gdn_problem* p, const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
+// The KDA backward's fp32 copies of T, Ab and P, and its fp32 per-chunk states
+// and state gradients.
+size_t kda_aux_region(const gdn_problem* p, const Checked& c) {
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda::Aux::kFloats * 4;
+  return (b + 255) / 256 * 256;
+}
+size_t kda_state_region(const gdn_problem* p, const Checked& c) {
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * 4;
+  return (b + 255) / 256 * 256;
+}
+
 size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::RecBwd)
     return gdn::recurrent_bwd_ws_floats(c.N, p->H, p->Dk, p->Dv, c.max_len) * sizeof(float);
@@ -149,6 +168,12 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
     // one record per (chunk slot, head), then (num_segments > 1) the fp32 segment
     // end states, start states and maps
     return kda_rec_region(p, c) + gdn::segment_ws_bytes(p->num_segments, c.N, p->H, p->Dk, p->Dv);
+  }
+  if (kind == Kind::KdaBwd) {
+    if (c.N == 0) return 0;
+    // the forward's records, then T, Ab and P in fp32, then the state before and
+    // the state gradient after every chunk (fp32)
+    return kda_rec_region(p, c) + kda_aux_region(p, c) + 2 * kda_state_region(p, c);
   }
   if (kind == Kind::ChunkBwd) {
     if (c.N == 0) return 0;
@@ -275,6 +300,7 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int32_t pass, size_t* bytes)
     case GDN_PASS_RECURRENT_BWD: kind = Kind::RecBwd; break;
     case GDN_PASS_KDA_FWD: kind = Kind::KdaFwd; break;
     case GDN_PASS_CHUNK_SAVED: kind = Kind::ChunkBwd; break;
+    case GDN_PASS_KDA_BWD: kind = Kind::KdaBwd; break;
     default: return GDN_ERR_UNSUPPORTED;
   }
   Checked c;
@@ -343,6 +369,54 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   kp.G = p->num_segments;
   kp.seg_ws = kp.G > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kda_rec_region(p, c)) : nullptr;
   return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_kda_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* S0, const void* dO,
+                             const float* dS_final, void* dq, void* dk, void* dv, float* dg,
+                             float* dbeta, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::KdaBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, nk * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false},
+                      {dO, nv * c.io, 16, true}, {dS_final, ns * 4, 4, false}},
+                     {{dq, nk * c.io, 16, true}, {dk, nk * c.io, 16, true}, {dv, nv * c.io, 16, true},
+                      {dg, nk * 4, 4, true}, {dbeta, ng * 4, 4, true}, {dS0, ns * 4, 4, false},
+                      {workspace, ws_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::KdaBwd, c);
+  if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* const wsb = static_cast<char*>(workspace);
+  const size_t rb = kda_rec_region(p, c), ab = kda_aux_region(p, c), sb = kda_state_region(p, c);
+  float* const aux = reinterpret_cast<float*>(wsb + rb);
+  float* const states = reinterpret_cast<float*>(wsb + rb + ab);
+  float* const dstates = reinterpret_cast<float*>(wsb + rb + ab + sb);
+  gdn::KdaParams kp{};
+  kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = nullptr; kp.S_final = nullptr;
+  kp.ws = workspace;
+  kp.seq = seq_info(p);
+  kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
+  kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  kp.scale = p->scale;
+  kp.G = 1;
+  kp.aux = aux;
+  kp.states = states;
+  st = hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, s));
+  if (st != GDN_OK) return st;
+  gdn::KdaBwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
+  bp.rec = workspace; bp.aux = aux; bp.states = states; bp.dstates = dstates;
+  bp.seq = seq_info(p);
+  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv;
+  bp.max_chunks = kp.max_chunks;
+  bp.scale = p->scale;
+  return hip_status(gdn::launch_kda_bwd(bp, p->Dk, c.bf16, s));
 }
 
 // The reverse passes of the backward on a filled buffer.

@@ -215,6 +215,11 @@ struct KdaParams {
   float* seg_out;           // [G][N][H][Dk][ncol] end states, or nullptr
   int32_t final_to_sfinal;  // segment G - 1 writes S_final
   float* seg_ws;            // G > 1: end states, start states, maps (segment_ws_bytes)
+  // For the backward (nullptr otherwise): the prep kernel also writes T, Ab and P
+  // in fp32 (kda::Aux floats per (chunk slot, head)); the state kernel writes the
+  // state before every chunk, fp32 [slot][H][Dk][Dv].
+  float* aux;
+  float* states;
 };
 // Per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma, Q o Gamma
 // and (K o exp(gamma_n - gamma))^T (64 x Dk each) in the io element type (the
@@ -223,6 +228,34 @@ inline size_t kda_rec_bytes(int Dk, bool bf16) {
   return (8192 + 3 * 64 * static_cast<size_t>(Dk)) * (bf16 ? 2 : 4) + 4 * static_cast<size_t>(Dk);
 }
 hipError_t launch_kda_fwd(const KdaParams& p, int Dk, bool bf16, hipStream_t s);
+// Backward of the per-key-channel-decay pass on records, aux matrices and per-chunk
+// states already written (launch_kda_fwd with aux and states set): the reverse
+// state-gradient pass (dS after every chunk into dstates, fp32 [slot][H][Dk][Dv];
+// dS0) and the per-chunk gradient kernel.
+struct KdaBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const void* dO;
+  const float* dS_final;  // [N, H, Dk, Dv] or nullptr (zero)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;              // [rows][H][Dk]
+  float* dbeta;           // [rows][H]
+  float* dS0;             // [N, H, Dk, Dv] or nullptr
+  const void* rec;        // the forward's records
+  const float* aux;
+  const float* states;
+  float* dstates;
+  SeqInfo seq;
+  int32_t N, H, Dv;
+  int32_t max_chunks;
+  float scale;
+};
+hipError_t launch_kda_bwd(const KdaBwdParams& p, int Dk, bool bf16, hipStream_t s);
 // Start states of segments 1 .. G - 1 composed in fp32 from the segments' end
 // states b (ends, from zero; segment 0 from S0) and transition maps M (maps):
 // starts[s + 1] = M_s starts[s] + b_s, starts[1] = ends[0].  Layouts [G][N][H][Dk][Dv]

@@ -34,6 +34,7 @@
 #include "gdn_chunk_common.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_kda_common.h"
 
 namespace gdn {
 namespace {
@@ -41,21 +42,8 @@ namespace {
 using chunk::seq_range;
 using chunk::u32x4_t;
 
-// One (chunk slot, head) record: five matrices in the MFMA operand type EL
-// (bf16 for bf16 io, fp32 for fp32 io; element offsets below), then Gamma_n as
-// DK floats at byte kGnByte.
 template <int DK, typename EL>
-struct KdaRec {
-  static constexpr int kTb = 0;               // T diag(beta), 64 x 64, zero above the diagonal
-  static constexpr int kP = 4096;             // P, 64 x 64, zero above the diagonal
-  static constexpr int kKG = 8192;            // K o Gamma, 64 x DK
-  static constexpr int kQG = kKG + 64 * DK;   // Q o Gamma, 64 x DK
-  static constexpr int kKDt = kQG + 64 * DK;  // (K o exp(gamma_n - gamma))^T, DK x 64
-  static constexpr int kElems = kKDt + 64 * DK;
-  static constexpr int kGnByte = kElems * static_cast<int>(sizeof(EL));
-  static constexpr int kBytes = kGnByte + DK * 4;
-  static_assert(kGnByte % 4096 == 0 && kBytes % 16 == 0, "record alignment");
-};
+using KdaRec = kda::Rec<DK, EL>;
 
 // LDS of the prep kernel (bytes): K and Q rows in the io element type, gamma in
 // fp32, A in fp32 (beta on its unused diagonal), all rows unpadded and swizzled
@@ -149,6 +137,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   const int64_t slot = bos / 64 + n + c;
   char* const recb = static_cast<char*>(p.ws) + (slot * p.H + h) * static_cast<int64_t>(R::kBytes);
   EL* const rec = reinterpret_cast<EL*>(recb);
+  float* const aux = p.aux ? p.aux + (slot * p.H + h) * static_cast<int64_t>(kda::Aux::kFloats) : nullptr;
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
 
@@ -250,6 +239,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
       const int i = 16 * bi + 4 * (lane >> 4) + q4, j = 16 * bj + (lane & 15);
       As[i * 64 + j] = As[i * 64 + i] * accA[q4];
       rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
+      if (aux) {
+        aux[kda::Aux::kAb + i * 64 + j] = accA[q4];
+        aux[kda::Aux::kP + i * 64 + j] = accP[q4];
+      }
     }
   } else if (!steep) {
 #pragma unroll 1
@@ -262,6 +255,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         const int i = 16 * b + 4 * (lane >> 4) + q4, j = 16 * b + (lane & 15);
         if (j < i) As[i * 64 + j] = As[i * 64 + i] * accA[q4];
         if (j <= i) rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
+        if (aux) {
+          aux[kda::Aux::kAb + i * 64 + j] = accA[q4];
+          aux[kda::Aux::kP + i * 64 + j] = accP[q4];
+        }
       }
     }
   }
@@ -301,6 +298,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     pair_sums(i, j, 0, DK, a, sc);
     if (j < i) As[i * 64 + j] = As[i * 64 + i] * a;
     rec[R::kP + i * 64 + j] = Op::cvt(sc);
+    if (aux) {
+      aux[kda::Aux::kAb + i * 64 + j] = a;
+      aux[kda::Aux::kP + i * 64 + j] = sc;
+    }
     // pairs 512..543: sixteen threads (one DPP row) per pair, DK / 16 channels each
     pair_of(512 + (tid >> 4), i, j);
     pair_sums(i, j, (DK / 16) * (tid & 15), DK / 16, a, sc);
@@ -315,6 +316,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     if ((tid & 15) == 15) {
       if (j < i) As[i * 64 + j] = As[i * 64 + i] * a;
       rec[R::kP + i * 64 + j] = Op::cvt(sc);
+      if (aux) {
+        aux[kda::Aux::kAb + i * 64 + j] = a;
+        aux[kda::Aux::kP + i * 64 + j] = sc;
+      }
     }
   }
   // P above the diagonal: eight zeros per 16-byte store where all eight columns
@@ -411,6 +416,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   for (int x = tid; x < 64 * 64; x += 512) {
     const int i = x / 64, j = x % 64;
     rec[R::kTb + x] = Op::cvt(Ts[i * 65 + j] * As[j * 64 + j]);
+    if (aux) aux[kda::Aux::kT + x] = Ts[i * 65 + j];
   }
 }
 
@@ -659,6 +665,13 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   for (int c = 0; c < nch; ++c) {
     const int64_t r0 = 64LL * (cb + c);
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
+    if (p.states) {  // the state before the chunk, for the backward (one segment)
+      float* const sc = p.states + ((bos / 64 + n + cb + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[(16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] = S[b][r];
+    }
     __syncthreads();
     __syncthreads();  // the record and the v tile of chunk c are in LDS
     float vcur[4];
@@ -749,7 +762,7 @@ hipError_t launch_kda_t(const KdaParams& p, hipStream_t s) {
   q.zero_u = 0;
   q.carry = nullptr;
   if (p.G == 1) {
-    q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = kOutAll;
+    q.seg_base = 0; q.nseg = 1; q.start_mode = kStartS0; q.write_o = p.o ? kOutAll : kOutNone;
     q.seg_out = nullptr; q.final_to_sfinal = 1;
     return run(q);
   }

@@ -10,6 +10,7 @@ built library every call raises ``GdnLibraryMissing``.
     q, k, g, beta = prologue(q_raw, k_raw, a, b, A_log=..., dt_bias=..., gate="gdn")
     y          = epilogue(o, z, weight=None, eps=1e-6)
     o, S_final = kda_chunk_fwd(q, k, v, g, beta, ...)   # g (B, T, H, Dk): per-channel decay
+    grads      = kda_chunk_bwd(q, k, v, g, beta, dO, ...)
 
 Shapes: q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H) fp32;
 S0 / S_final (N, H, Dk, Dv) fp32.  q, k, v share the io dtype (bf16 or fp32).
@@ -251,6 +252,39 @@ def kda_chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0
                                _ptr(S0), _ptr(o), _ptr(Sf), _ptr(ws), nws, _stream(q.device))
     nat.check(st, "gdn_kda_chunk_fwd")
     return o, Sf
+
+
+def kda_chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,
+                  scale: float = 1.0, want_dS0: bool = True):
+    """Backward of kda_chunk_fwd (g fp32, shaped like q).  Returns dict dq, dk,
+    dv, dg (shaped like g), dbeta, dS0."""
+    lib = nat.load()
+    _check_inputs(q, k, v, beta, beta)
+    if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
+        raise ValueError("g must be a float32 tensor shaped like q (one log-decay per key channel)")
+    _on_device(g, q.device, "g")
+    if not g.is_contiguous():
+        raise ValueError("g must be a contiguous GPU tensor")
+    _on_device(dO, q.device, "dO")
+    if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
+        raise ValueError("dO must be contiguous, shaped and typed like v")
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
+    dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final", q.device)
+    out = {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+        "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+        "dS0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_dS0 else None,
+    }
+    ws, nws = _workspace(prob, nat.GDN_PASS_KDA_BWD, q.device)
+    st = lib.gdn_kda_chunk_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                               _ptr(ws), nws, _stream(q.device))
+    nat.check(st, "gdn_kda_chunk_bwd")
+    return out
 
 
 def chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -104,8 +104,9 @@ typedef enum gdn_dtype { GDN_FP32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   GDN_PRECISION_FP32 every product in IEEE fp32 (fp32 MFMA) whatever the io
  *                      dtype: bf16 inputs are widened exactly, o is rounded to
  *                      bf16 once, the per-chunk workspace records are fp32.
- *                      gdn_chunk_fwd only (gdn_chunk_bwd and gdn_kda_chunk_fwd
- *                      with bf16 io return GDN_ERR_UNSUPPORTED for it). */
+ *                      gdn_chunk_fwd only (gdn_chunk_bwd, gdn_kda_chunk_fwd and
+ *                      gdn_kda_chunk_bwd with bf16 io return GDN_ERR_UNSUPPORTED
+ *                      for it). */
 typedef enum gdn_precision { GDN_PRECISION_IO = 0, GDN_PRECISION_FP32 = 1 } gdn_precision;
 
 typedef enum gdn_pass {
@@ -114,7 +115,8 @@ typedef enum gdn_pass {
   GDN_PASS_RECURRENT_FWD = 2,
   GDN_PASS_RECURRENT_BWD = 3,
   GDN_PASS_KDA_FWD = 4,
-  GDN_PASS_CHUNK_SAVED = 5  /* the buffer of gdn_chunk_fwd_save / gdn_chunk_bwd_saved */
+  GDN_PASS_CHUNK_SAVED = 5, /* the buffer of gdn_chunk_fwd_save / gdn_chunk_bwd_saved */
+  GDN_PASS_KDA_BWD = 6
 } gdn_pass;
 
 typedef struct gdn_problem {
@@ -277,6 +279,36 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const vo
                              const void* v, const float* g, const float* beta, const float* S0,
                              void* o, float* S_final, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* Reverse mode of gdn_kda_chunk_fwd: the gradients of
+ *   L = <o, dO> + <S_final, dS_final>
+ * with respect to q, k, v, the per-channel log-decays g, beta and S0, for the
+ * recurrence of gdn_kda_chunk_fwd (per token, a = exp(g_t) of length Dk:
+ * S <- diag(a) S, e = beta (v - S^T k), S <- S + k e^T, o = scale S^T q; the
+ * update of "Research Sprint Day 1", "The GDN update", with the diagonal forget
+ * factor of the cuLA issue #126 page's gate layout).
+ *   in : q, k, v, g, beta, S0 (NULL = zero) as gdn_kda_chunk_fwd; dO [B,T,H,Dv]
+ *        (io dtype); dS_final [N,H,Dk,Dv] fp32 or NULL (zero)
+ *   out: dq, dk [B,T,H,Dk] and dv [B,T,H,Dv] (io dtype); dg [B,T,H,Dk] fp32 (one
+ *        gradient per key channel); dbeta [B,T,H] fp32; dS0 [N,H,Dk,Dv] fp32
+ *        (NULL = not wanted)
+ * The forward's chunk preparation and state pass run again (no o is written);
+ * then a reverse pass over the chunks forms the state gradient after every
+ * chunk, and one workgroup per chunk forms its gradients.  Packed sequences as
+ * for gdn_kda_chunk_fwd; Dk 64 or 128, Dv a multiple of 16 up to 256, both io
+ * dtypes; num_segments must be 1 and precision GDN_PRECISION_IO.
+ * Precision: the forward part as gdn_kda_chunk_fwd; the reverse pass reads its
+ * chunk records (io element type) into fp32 products; the gradient kernel works
+ * in fp32 throughout (fp32 MFMA) from the inputs, fp32 copies of T, the key
+ * products and P, and the fp32 per-chunk states.
+ * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_BWD, ...): the forward's records,
+ * then per chunk and head 12288 floats (T, Ab, P) and the state before and its
+ * gradient after the chunk, Dk Dv floats each.  Errors as gdn_kda_chunk_fwd. */
+gdn_status gdn_kda_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, const float* S0,
+                             const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
+                             float* dg, float* dbeta, float* dS0, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Gate forms of gdn_prologue. */
 typedef enum {

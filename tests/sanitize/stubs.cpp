@@ -16,6 +16,7 @@ hipError_t launch_recurrent(const RecParams&, int, bool, hipStream_t) { ++g_laun
 hipError_t launch_prologue(const PrologueParams&, int, bool, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_epilogue(const EpilogueParams&, int, bool, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_kda_fwd(const KdaParams&, int, bool, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+hipError_t launch_kda_bwd(const KdaBwdParams&, int, bool, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 size_t recurrent_bwd_ws_floats(int N, int H, int Dk, int Dv, int64_t max_len) {
   return static_cast<size_t>(N) * H * (static_cast<size_t>(max_len) + 1) * (Dk + Dv);
 }

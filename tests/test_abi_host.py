@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
@@ -94,6 +94,7 @@ def test_precision_policy_scope():
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64, precision=fp32), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_OK
     assert ws(problem(precision=fp32), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(precision=fp32), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(precision=fp32), nat.GDN_PASS_RECURRENT_FWD)[0] == nat.GDN_OK
 
 
@@ -333,6 +334,42 @@ def test_kda_workspace_and_checks():
     assert call(problem(), o=FAKE + (3 << 30) + 2 * 100 * 3 * 128 * 4 - 16) == nat.GDN_ERR_ALIAS
     assert call(problem(num_segments=4)) == nat.GDN_ERR_WORKSPACE    # segments need the larger workspace
     assert call(problem(num_segments=5)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
+
+
+def test_kda_bwd_workspace_and_checks():
+    # the forward's records, then per (chunk slot, head) T, Ab and P in fp32 (3 x 64 x 64
+    # floats), then the state before and the state gradient after every chunk (Dk Dv fp32 each)
+    slots = 200 // 64 + 2 + 1
+    for Dk in (64, 128):
+        for io, size in ((nat.GDN_BF16, 2), (nat.GDN_FP32, 4)):
+            rec = (8192 + 3 * 64 * Dk) * size + 4 * Dk
+            aux = 3 * 4096 * 4
+            st = Dk * 128 * 4
+            want = slots * 3 * (rec + aux + 2 * st)
+            assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_BWD) == (nat.GDN_OK, want)
+    assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(Dk=96), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(Dv=24), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    P = ctypes.c_void_p
+    lib = nat.load()
+    # inputs q k v g beta dO at FAKE + 0..5 GiB; outputs dq dk dv dg dbeta at 8..12 GiB
+    GB = 1 << 30
+
+    def call(p, q=FAKE, g=FAKE + 3 * GB, dq=FAKE + 8 * GB, dg=FAKE + 11 * GB, wsp=None, nws=0):
+        return lib.gdn_kda_chunk_bwd(ctypes.byref(p), P(q), P(FAKE + GB), P(FAKE + 2 * GB), P(g),
+                                     P(FAKE + 4 * GB), None, P(FAKE + 5 * GB), None, P(dq), P(FAKE + 9 * GB),
+                                     P(FAKE + 10 * GB), P(dg), P(FAKE + 12 * GB), None, P(wsp), nws, None)
+
+    assert call(problem()) == nat.GDN_ERR_WORKSPACE
+    assert call(problem(), q=None) == nat.GDN_ERR_NULL
+    assert call(problem(), dg=None) == nat.GDN_ERR_NULL
+    assert call(problem(), g=FAKE + 3 * GB + 2) == nat.GDN_ERR_ALIGN
+    assert call(problem(), dq=FAKE + 4096) == nat.GDN_ERR_ALIAS
+    # dg spans B T H Dk floats: dq starting inside it aliases it
+    assert call(problem(), dq=FAKE + 11 * GB + 2 * 100 * 3 * 128 * 4 - 16) == nat.GDN_ERR_ALIAS
+    assert call(problem(num_segments=2)) == nat.GDN_ERR_UNSUPPORTED
+    assert call(problem(precision=nat.GDN_PRECISION_FP32)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
 
 
