@@ -22,14 +22,16 @@
 //   dg_s = sum_{i >= s} dgamma_i + dgamma_n  (the reverse cumulative sum of the chunk).
 // Every exponent formed is <= 0, so any decay strength is safe.
 //
-// Two kernels, both fp32 throughout (fp32 MFMA, 16x16x4):
+// Two kernels:
 //   kda_dstate_kernel -- one workgroup per (sequence, head, 16 value columns);
 //                        walks the chunks last to first on the forward's
-//                        records, storing dS' of every chunk.
+//                        records, storing dS' of every chunk (fp32).  Its
+//                        products take the records' operand type (bf16 MFMA
+//                        with fp32 accumulation for bf16 io, fp32 for fp32 io).
 //   kda_grad_kernel   -- one workgroup per (chunk, head, sequence), fully
-//                        parallel: the products above over 16-column tiles of
-//                        d_v, then the decay terms pair by pair and the
-//                        cumulative sum.
+//                        parallel, fp32 throughout (fp32 MFMA): the products
+//                        above over 16-column tiles of d_v, then the decay
+//                        terms pair by pair and the cumulative sum.
 #include <type_traits>
 
 #include "gdn_chunk_common.h"
@@ -47,61 +49,108 @@ __device__ __forceinline__ float ldf(const float* p) { return *p; }
 
 // acc += A(16 x K) B(K x 16) on fp32 MFMA.  `a` points at A(m, kq) and `b` at
 // B(kq, n) for this lane (m = n = lane % 16, kq = lane / 16); SA and SB are the
-// strides between consecutive k.  Up to four independent accumulation chains.
-template <int K, int SA, int SB, typename TA>
+// strides between consecutive k.  NA independent accumulation chains (NA = 1:
+// straight into acc, for products interleaved with others of their own).
+template <int K, int SA, int SB, int NA = 4, typename TA>
 __device__ __forceinline__ void mm(f32x4_t& acc, const TA* a, const float* b, float ascale = 1.f) {
   constexpr int NS = K / 4;
-  constexpr int NA = NS < 4 ? NS : 4;
-  static_assert(NS * 4 == K, "K must be a multiple of 4");
-  f32x4_t x[NA];
+  static_assert(NS * 4 == K && NS % NA == 0, "K must be a multiple of 4 NA");
+  if constexpr (NA == 1) {
 #pragma unroll
-  for (int j = 0; j < NA; ++j) x[j] = zero4();
+    for (int st = 0; st < NS; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ascale * ldf(a + 4 * st * SA), b[4 * st * SB], acc, 0, 0, 0);
+  } else {
+    f32x4_t x[NA];
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-    x[st % NA] = __builtin_amdgcn_mfma_f32_16x16x4f32(ascale * ldf(a + 4 * st * SA), b[4 * st * SB], x[st % NA],
-                                                      0, 0, 0);
+    for (int j = 0; j < NA; ++j) x[j] = zero4();
 #pragma unroll
-  for (int j = 0; j < NA; ++j) acc += x[j];
+    for (int st = 0; st < NS; ++st)
+      x[st % NA] = __builtin_amdgcn_mfma_f32_16x16x4f32(ascale * ldf(a + 4 * st * SA), b[4 * st * SB], x[st % NA],
+                                                        0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) acc += x[j];
+  }
+}
+
+// N consecutive values (N a multiple of 8, 16-byte aligned) widened to fp32:
+// 16-byte loads.
+template <int N>
+__device__ __forceinline__ void ld_row(const uint16_t* p, float (&out)[N]) {
+#pragma unroll
+  for (int u = 0; u < N / 8; ++u) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p + 8 * u);
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[8 * u + 2 * e] = __uint_as_float(w4[e] << 16);
+      out[8 * u + 2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void ld_row(const float* p, float (&out)[N]) {
+#pragma unroll
+  for (int u = 0; u < N / 4; ++u) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p + 4 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * u + e] = x[e];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// State-gradient pass.  LDS (bytes): the chunk's record as stored, then fp32
-// tiles with rows of 20 floats.
+// State-gradient pass.  LDS, in elements of the MFMA operand type EL: the chunk's
+// record with rows padded by 16 bytes, then the B-operand tiles stored transposed
+// (16 rows of the value tile, reduction index contiguous), then Gamma_n (fp32).
 template <int DK, typename EL>
 struct DsLds {
-  using R = kda::Rec<DK, EL>;
-  static constexpr int LT = 20;
-  static constexpr int kRec = 0;                    // record matrices and Gamma_n, as in global memory
-  static constexpr int kDo = R::kBytes;             // float [64][LT]: scale dO, rows past the chunk zero
-  static constexpr int kDs = kDo + 64 * LT * 4;     // float [DK][LT]: dS'
-  static constexpr int kDe = kDs + DK * LT * 4;     // float [64][LT]: dE
-  static constexpr int kF = kDe + 64 * LT * 4;      // float [64][LT]: F
-  static constexpr int kBytes = kF + 64 * LT * 4;
+  static constexpr int PAD = 16 / static_cast<int>(sizeof(EL));
+  static constexpr int L64 = 64 + PAD, LK = DK + PAD;
+  static constexpr int kTb = 0;                  // [64][L64] T diag(beta)
+  static constexpr int kP = kTb + 64 * L64;      // [64][L64] P
+  static constexpr int kKG = kP + 64 * L64;      // [64][LK] K o Gamma
+  static constexpr int kQG = kKG + 64 * LK;      // [64][LK] Q o Gamma
+  static constexpr int kKDt = kQG + 64 * LK;     // [DK][L64] decayed keys, transposed
+  static constexpr int kDoT = kKDt + DK * L64;   // [16][L64] (scale dO)^T
+  static constexpr int kDsT = kDoT + 16 * L64;   // [16][LK] dS'^T
+  static constexpr int kDeT = kDsT + 16 * LK;    // [16][L64] dE^T
+  static constexpr int kFT = kDeT + 16 * L64;    // [16][L64] -F^T
+  static constexpr int kElems = kFT + 16 * L64;
+  static constexpr int kGnByte = (kElems * static_cast<int>(sizeof(EL)) + 15) / 16 * 16;
+  static constexpr int kBytes = kGnByte + DK * 4;
 };
 
+// C tile (lane: rows 4 (lane / 16) + r of column lane % 16) stored transposed:
+// dst[lane % 16][4 (lane / 16) + r], four consecutive elements.
+template <typename EL>
+__device__ __forceinline__ void store_ct(EL* dst, int ld, const f32x4_t& c, int lane) {
+  chunk::store4<EL>(dst + (lane & 15) * ld + 4 * (lane >> 4), c[0], c[1], c[2], c[3]);
+}
+
 // Four waves: wave w forms rows 16 w .. 16 w + 15 of dE and F and holds the
-// state-gradient rows 16 (w + 4 b) + 4 (lane / 16) + r in accumulators.  The next
-// chunk's record and dO tile are loaded into registers while a chunk is
-// processed and written to LDS at the top of the next step.
+// state-gradient rows 16 (w + 4 b) + 4 (lane / 16) + r in fp32 accumulators.
+// The products take the record's operands as stored (bf16 for bf16 io, fp32 for
+// fp32 io), transposed ones through transposing LDS reads; dE, F and dS' are
+// rounded to that type as operands.  The next chunk's record and dO tile are
+// loaded into registers while a chunk is processed.
 template <int DK, typename E>
 __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
-  using EL = std::conditional_t<sizeof(E) == 2, uint16_t, float>;
+  using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
+  using EL = typename Op::elem;
   using R = kda::Rec<DK, EL>;
   using L = DsLds<DK, EL>;
-  constexpr int LT = L::LT;
-  constexpr int RB = DK / 64;                      // state row blocks per wave
-  constexpr int NVEC = R::kBytes / 16;             // record vectors
-  constexpr int NU = (NVEC + 255) / 256;           // record vectors per thread
+  constexpr int KS = Op::KSTEP;
+  constexpr int RB = DK / 64;                                  // state row blocks per wave
+  constexpr int EPV = 16 / static_cast<int>(sizeof(EL));       // record elements per vector
+  constexpr int NV = R::kGnByte / 16 / 256;                    // record vectors per thread
+  constexpr int U64 = 4096 / EPV / 256;                        // vectors of one 64 x 64 matrix
+  constexpr int UDK = 64 * DK / EPV / 256;                     // vectors of one 64 x DK matrix
+  static_assert(NV == 2 * U64 + 3 * UDK, "record layout");
   constexpr int VPR = 16 * static_cast<int>(sizeof(E)) / 16;  // dO vectors per tile row
-  constexpr int EPV = 16 / static_cast<int>(sizeof(E));
+  constexpr int EPVIO = 16 / static_cast<int>(sizeof(E));
   extern __shared__ __align__(16) char sds[];
-  const EL* const rs = reinterpret_cast<const EL*>(sds + L::kRec);
-  const float* const gn = reinterpret_cast<const float*>(sds + R::kGnByte);
-  float* const dos = reinterpret_cast<float*>(sds + L::kDo);
-  float* const dss = reinterpret_cast<float*>(sds + L::kDs);
-  float* const des = reinterpret_cast<float*>(sds + L::kDe);
-  float* const fs = reinterpret_cast<float*>(sds + L::kF);
-  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4, kq = g4;
+  EL* const sm = reinterpret_cast<EL*>(sds);
+  float* const gn = reinterpret_cast<float*>(sds + L::kGnByte);
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int ntile = p.Dv / 16;
   const int nb = gridDim.x, Lb = blockIdx.x;
@@ -124,75 +173,95 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
     for (int r = 0; r < 4; ++r)
       dS[b][r] = p.dS_final ? p.dS_final[(sbase + 16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] : 0.f;
 
-  // prefetch: the record of chunk c and the dO tile (rows past the sequence read
-  // as zeros through a buffer resource bounded to the chunk's rows)
-  f32x4_t pr[NU];
+  // prefetch: the record of chunk c (its five matrices as 16-byte vectors tid + 256 u,
+  // and Gamma_n) and the dO tile (rows past the sequence read as zeros through a
+  // buffer resource bounded to the chunk's rows)
+  f32x4_t pr[NV];
+  f32x4_t pg = zero4();
   f32x4_t pd = zero4();
   const int drow = tid / VPR < 64 ? tid / VPR : 63, dpart = tid % VPR;
   auto prefetch = [&](int c) {
     const char* rc = rec0 + c * rec_step;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int x = tid + 256 * u;
-      pr[u] = *reinterpret_cast<const f32x4_t*>(rc + 16 * (x < NVEC ? x : NVEC - 1));
-    }
+    for (int u = 0; u < NV; ++u) pr[u] = *reinterpret_cast<const f32x4_t*>(rc + 16 * (tid + 256 * u));
+    pg = *reinterpret_cast<const f32x4_t*>(rc + R::kGnByte + 16 * (tid < DK / 4 ? tid : 0));
     const int64_t r0 = 64LL * c;
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
     const auto rd = chunk::buffer_rsrc(dO + ((bos + r0) * p.H + h) * Dv + tile * 16,
                                        static_cast<int>(((nr - 1) * p.H * Dv + 16) * sizeof(E)));
     pd = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rd, (drow * p.H * Dv + dpart * EPV) * static_cast<int>(sizeof(E)), 0, 0));
+                                         rd, (drow * p.H * Dv + dpart * EPVIO) * static_cast<int>(sizeof(E)), 0, 0));
   };
   if (nch > 0) prefetch(nch - 1);
 
   for (int c = nch - 1; c >= 0; --c) {
     __syncthreads();  // every read of the previous chunk's LDS is done
+    // the record into padded rows (each u lies in one matrix)
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int x = tid + 256 * u;
-      if (x < NVEC) *reinterpret_cast<f32x4_t*>(sds + L::kRec + 16 * x) = pr[u];
+    for (int u = 0; u < NV; ++u) {
+      EL* dstp;
+      if (u < 2 * U64) {
+        const int f = EPV * (tid + 256 * (u < U64 ? u : u - U64));
+        dstp = sm + (u < U64 ? L::kTb : L::kP) + (f / 64) * L::L64 + f % 64;
+      } else if (u < 2 * U64 + 2 * UDK) {
+        const int f = EPV * (tid + 256 * (u < 2 * U64 + UDK ? u - 2 * U64 : u - 2 * U64 - UDK));
+        dstp = sm + (u < 2 * U64 + UDK ? L::kKG : L::kQG) + (f / DK) * L::LK + f % DK;
+      } else {
+        const int f = EPV * (tid + 256 * (u - 2 * U64 - 2 * UDK));
+        dstp = sm + L::kKDt + (f / 64) * L::L64 + f % 64;
+      }
+      *reinterpret_cast<f32x4_t*>(dstp) = pr[u];
     }
+    if (tid < DK / 4) *reinterpret_cast<f32x4_t*>(gn + 4 * tid) = pg;
+    // (scale dO)^T: row j of the tile supplies column j
     if (tid < 64 * VPR) {
-      float* dst = dos + drow * LT + dpart * EPV;
+      float x[EPVIO];
       if constexpr (sizeof(E) == 2) {
         const uint32_t* u = reinterpret_cast<const uint32_t*>(&pd);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dst[2 * e] = p.scale * __uint_as_float(u[e] << 16);
-          dst[2 * e + 1] = p.scale * __uint_as_float(u[e] & 0xffff0000u);
+          x[2 * e] = __uint_as_float(u[e] << 16);
+          x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = p.scale * pd[e];
+        for (int e = 0; e < 4; ++e) x[e] = pd[e];
       }
+#pragma unroll
+      for (int e = 0; e < EPVIO; ++e) sm[L::kDoT + (dpart * EPVIO + e) * L::L64 + drow] = Op::cvt(p.scale * x[e]);
     }
-    // dS' (the gradient after chunk c) to LDS and to the per-chunk buffer
+    // dS' (the gradient after chunk c): to the per-chunk buffer and, transposed, to LDS
     float* const dsg = p.dstates + ((slot0 + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
+    for (int b = 0; b < RB; ++b) {
+      const int rb = w + 4 * b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (w + 4 * b) + 4 * g4 + r;
-        dss[row * LT + col] = dS[b][r];
-        dsg[row * Dv + c0] = dS[b][r];
-      }
+      for (int r = 0; r < 4; ++r) dsg[(16 * rb + 4 * g4 + r) * Dv + c0] = dS[b][r];
+      store_ct<EL>(sm + L::kDsT + 16 * rb, L::LK, dS[b], lane);
+    }
     __syncthreads();
     if (c > 0) prefetch(c - 1);
     // dE = P^T dOs + Kb dS' (rows 16 w ..)
     {
       f32x4_t acc = zero4();
-      mm<64, 64, LT>(acc, rs + R::kP + kq * 64 + 16 * w + col, dos + kq * LT + col);
-      mm<DK, 64, LT>(acc, rs + R::kKDt + kq * 64 + 16 * w + col, dss + kq * LT + col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) des[(16 * w + 4 * g4 + r) * LT + col] = acc[r];
+      for (int k0 = 0; k0 < 64; k0 += KS)
+        acc = Op::mma(Op::frag_tr(sm + L::kP + 16 * w, L::L64, lane, k0), Op::frag(sm + L::kDoT, L::L64, lane, k0), acc);
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += KS)
+        acc = Op::mma(Op::frag_tr(sm + L::kKDt + 16 * w, L::L64, lane, k0), Op::frag(sm + L::kDsT, L::LK, lane, k0),
+                      acc);
+      store_ct<EL>(sm + L::kDeT + 16 * w, L::L64, acc, lane);
     }
     __syncthreads();
-    // F = (T diag(beta))^T dE
+    // -F = -(T diag(beta))^T dE
     {
       f32x4_t acc = zero4();
-      mm<64, 64, LT>(acc, rs + R::kTb + kq * 64 + 16 * w + col, des + kq * LT + col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) fs[(16 * w + 4 * g4 + r) * LT + col] = acc[r];
+      for (int k0 = 0; k0 < 64; k0 += KS)
+        acc = Op::mma(Op::frag_tr(sm + L::kTb + 16 * w, L::L64, lane, k0), Op::frag(sm + L::kDeT, L::L64, lane, k0),
+                      acc);
+      store_ct<EL>(sm + L::kFT + 16 * w, L::L64, -acc, lane);
     }
     __syncthreads();
     // dS <- diag(Gamma_n) dS' + Qd^T dOs - Kd^T F
@@ -201,10 +270,14 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
       const int rb = w + 4 * b;
 #pragma unroll
       for (int r = 0; r < 4; ++r) dS[b][r] *= gn[16 * rb + 4 * g4 + r];
-      mm<64, DK, LT>(dS[b], rs + R::kQG + kq * DK + 16 * rb + col, dos + kq * LT + col);
-      f32x4_t kf = zero4();
-      mm<64, DK, LT>(kf, rs + R::kKG + kq * DK + 16 * rb + col, fs + kq * LT + col);
-      dS[b] -= kf;
+#pragma unroll
+      for (int k0 = 0; k0 < 64; k0 += KS)
+        dS[b] = Op::mma(Op::frag_tr(sm + L::kQG + 16 * rb, L::LK, lane, k0), Op::frag(sm + L::kDoT, L::L64, lane, k0),
+                        dS[b]);
+#pragma unroll
+      for (int k0 = 0; k0 < 64; k0 += KS)
+        dS[b] = Op::mma(Op::frag_tr(sm + L::kKG + 16 * rb, L::LK, lane, k0), Op::frag(sm + L::kFT, L::L64, lane, k0),
+                        dS[b]);
     }
   }
   if (p.dS0) {
@@ -214,6 +287,10 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
       for (int r = 0; r < 4; ++r) p.dS0[(sbase + 16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] = dS[b][r];
   }
 }
+
+// Largest decay of one channel across a 16-row block (log2 units) for which the
+// gradient kernel forms the diagonal blocks' pair sums through a reference row.
+constexpr float kMaxBlockDropBwd = 100.f;
 
 // ---------------------------------------------------------------------------
 // Gradient kernel.  LDS in floats; rows of d_k + 4 (LK), 68 (L64) and 20 (LT)
@@ -246,18 +323,24 @@ struct GradLds {
   static constexpr int kGam = kK + 64 * LK;       // [64][LK] gamma (log2 units)
   static constexpr int kBe2 = kGam + 64 * LK;     // [64] beta
   static constexpr int kEndY = kBe2 + 64;
+  static constexpr int kDbA = kEndY;              // [64] sum_{j < i} dA_ij Ab_ij (read in phase Z)
+  static constexpr int kSteep = kDbA + 64;        // flag: some block decays by more than 2^kMaxBlockDropBwd
   static constexpr int kFloats = kEndV > kEndY ? kEndV : kEndY;
   static_assert(kBe * 4 <= 65536, "tile arrays within the immediate-offset range");
-  static_assert(3 * 64 * LK <= kFloats, "phase X dump must fit");
+  static_assert(3 * 64 * LK + DK <= kFloats, "phase X and Z arrays must fit");
+  static_assert(kSteep + 1 <= kFloats && kDbA >= 3 * 64 * LK + DK, "dbeta partials beside the phase Z arrays");
   static_assert(kFloats * 4 <= 160 * 1024, "LDS budget exceeded");
 };
 
 // Eight waves.  Phase V: per 16-column tile of d_v, waves 0-3 form R then E and
 // waves 4-7 dE then G (one 16-row block each), then every wave accumulates its
 // share of dA, dP (two 16x16 tiles each) and dKd, dQd, dKb (DK / 32 tiles each).
-// Phase X/Y: thread (i, cg) = (tid / 8, tid % 8) owns row i, channels
-// cg DK/8 .. + DK/8, for the elementwise terms and the pair sums.  Phase Z: thread
-// c < DK forms channel c's reverse cumulative sum.
+// Phase X/Y: wave w < DK / 16 owns channels 16 w .. 16 w + 15 (lane: one channel,
+// 16 rows) for the elementwise terms and the pair sums: pairs inside the diagonal
+// 16x16 blocks one exponential each, pairs across blocks as fp32 MFMA products of
+// rows decayed to a reference row between the blocks.  Phase Z: thread (i, cg) =
+// (tid / 8, tid % 8) stores row i's channels cg DK/8 .., thread c < DK forms
+// channel c's reverse cumulative sum.
 template <int DK, typename E>
 __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   using L = GradLds<DK>;
@@ -291,19 +374,31 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   float* const kd = sg + L::kKd;
   float* const kb = sg + L::kKb;
   {
+    // every load first (16-byte vectors), then the LDS stores
     const int64_t off = ((bos + r0 + rowc) * H + h) * DK + cg * CPT;
+    float kv[CPT], gv[CPT];
+    ld_row<CPT>(k + off, kv);
+    ld_row<CPT>(p.g + off, gv);
+    f32x4_t tv[2], pv4[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      tv[u] = *reinterpret_cast<const f32x4_t*>(aux + kda::Aux::kT + 4 * (tid + 512 * u));
+      pv4[u] = *reinterpret_cast<const f32x4_t*>(aux + kda::Aux::kP + 4 * (tid + 512 * u));
+    }
+    const float bt = p.beta[(bos + r0 + (lane < nr ? lane : nr - 1)) * H + h];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      const float kv = IoT<E>::ld(k + off + e), gv = p.g[off + e];
-      kd[ri * LK + cg * CPT + e] = ri < nr ? kv : 0.f;
-      kb[ri * LK + cg * CPT + e] = ri < nr ? gv * chunk::kLog2e : 0.f;
+      kd[ri * LK + cg * CPT + e] = ri < nr ? kv[e] : 0.f;
+      kb[ri * LK + cg * CPT + e] = ri < nr ? gv[e] * chunk::kLog2e : 0.f;
     }
-    for (int x = tid; x < 64 * 64; x += 512) {
-      const int i = x >> 6, j = x & 63;
-      sg[L::kT + i * L64 + j] = aux[kda::Aux::kT + x];
-      sg[L::kP + i * L64 + j] = j <= i ? aux[kda::Aux::kP + x] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int vx = tid + 512 * u, i = vx >> 4, j0 = 4 * (vx & 15);
+      *reinterpret_cast<f32x4_t*>(sg + L::kT + i * L64 + j0) = tv[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sg[L::kP + i * L64 + j0 + e] = j0 + e <= i ? pv4[u][e] : 0.f;
     }
-    if (tid < 64) sg[L::kBe + tid] = tid < nr ? p.beta[(bos + r0 + tid) * H + h] : 0.f;
+    if (tid < 64) sg[L::kBe + tid] = tid < nr ? bt : 0.f;
   }
   __syncthreads();
   if (tid < DK) {  // cumulative sum of channel tid over the chunk, in place (log2 units)
@@ -435,15 +530,15 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int ta = 2 * w + x, ti = ta >> 2, tj = ta & 3;
-      mm<16, 1, 1>(aA[x], gt + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
-      mm<16, 1, 1>(aP[x], dot + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
+      mm<16, 1, 1, 1>(aA[x], gt + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
+      mm<16, 1, 1, 1>(aP[x], dot + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
     }
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
       const int tk = NK * w + x, ti = tk / (DK / 16), tc = tk % (DK / 16);
-      mm<16, 1, 1>(aKd[x], gt + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq, be[16 * ti + col]);
-      mm<16, 1, 1>(aQd[x], dot + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq);
-      mm<16, 1, 1>(aKb[x], et + (16 * ti + col) * LT + kq, dst + (16 * tc + col) * LT + kq);
+      mm<16, 1, 1, 1>(aKd[x], gt + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq, be[16 * ti + col]);
+      mm<16, 1, 1, 1>(aQd[x], dot + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq);
+      mm<16, 1, 1, 1>(aKb[x], et + (16 * ti + col) * LT + kq, dst + (16 * tc + col) * LT + kq);
     }
     if (tid < 64) {
 #pragma unroll
@@ -456,28 +551,36 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   }
   __syncthreads();
 
-  // ---- phase X: dKd = -F S^T, dQd = dOs S^T, dKb = E dS'^T to the row threads --
-  float xKd[CPT], xQd[CPT], xKb[CPT];
+  // ---- phase X: dKd = -F S^T, dQd = dOs S^T, dKb = E dS'^T to their owners ----
+  // From here on wave w < DK / 16 owns channel c = 16 w + lane % 16 and rows
+  // 16 b + 4 (lane / 16) + r (b, r < 4): the element layout of an MFMA result
+  // tile, so the pair products below land on their owners.
+  constexpr int NCB = DK / 16;
+  const bool cw = w < NCB;
+  const int ch = 16 * (cw ? w : 0) + col;
+  float xKd[4][4], xQd[4][4], xKb[4][4];
   {
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
       const int tk = NK * w + x, ti = tk / (DK / 16), tc = tk % (DK / 16);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * ti + 4 * g4 + r, ch = 16 * tc + col;
-        sg[row * LK + ch] = -aKd[x][r];
-        sg[64 * LK + row * LK + ch] = aQd[x][r];
-        sg[2 * 64 * LK + row * LK + ch] = aKb[x][r];
+        const int row = 16 * ti + 4 * g4 + r, cc = 16 * tc + col;
+        sg[row * LK + cc] = -aKd[x][r];
+        sg[64 * LK + row * LK + cc] = aQd[x][r];
+        sg[2 * 64 * LK + row * LK + cc] = aKb[x][r];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int ch = cg * CPT + e;
-      xKd[e] = sg[ri * LK + ch];
-      xQd[e] = sg[64 * LK + ri * LK + ch];
-      xKb[e] = sg[2 * 64 * LK + ri * LK + ch];
-    }
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * b + 4 * g4 + r;
+        xKd[b][r] = sg[row * LK + ch];
+        xQd[b][r] = sg[64 * LK + row * LK + ch];
+        xKb[b][r] = sg[2 * 64 * LK + row * LK + ch];
+      }
     __syncthreads();
   }
 
@@ -498,133 +601,236 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
       dP[i * L64 + j] = aP[x][r];
     }
   }
+  f32x4_t abr0, abr1;  // Ab row ri, columns 8 cg .. 8 cg + 7
   {
     const int64_t off = ((bos + r0 + rowc) * H + h) * DK + cg * CPT;
+    float qv[CPT], kv[CPT], gv[CPT];
+    ld_row<CPT>(q + off, qv);
+    ld_row<CPT>(k + off, kv);
+    ld_row<CPT>(p.g + off, gv);
+    const float bt = p.beta[(bos + r0 + (lane < nr ? lane : nr - 1)) * H + h];
+    abr0 = *reinterpret_cast<const f32x4_t*>(aux + kda::Aux::kAb + ri * 64 + 8 * cg);
+    abr1 = *reinterpret_cast<const f32x4_t*>(aux + kda::Aux::kAb + ri * 64 + 8 * cg + 4);
+    const bool ok = ri < nr;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      const bool ok = ri < nr;
-      qs[ri * LK + cg * CPT + e] = ok ? IoT<E>::ld(q + off + e) : 0.f;
-      ks[ri * LK + cg * CPT + e] = ok ? IoT<E>::ld(k + off + e) : 0.f;
-      gs[ri * LK + cg * CPT + e] = ok ? p.g[off + e] * chunk::kLog2e : 0.f;
+      qs[ri * LK + cg * CPT + e] = ok ? qv[e] : 0.f;
+      ks[ri * LK + cg * CPT + e] = ok ? kv[e] : 0.f;
+      gs[ri * LK + cg * CPT + e] = ok ? gv[e] * chunk::kLog2e : 0.f;
     }
-    if (tid < 64) be2[tid] = tid < nr ? p.beta[(bos + r0 + tid) * H + h] : 0.f;
+    if (tid < 64) be2[tid] = tid < nr ? bt : 0.f;
+    if (tid == 0) sg[L::kSteep] = 0.f;
   }
   __syncthreads();
-  if (tid < DK) {
-    float acc = 0.f;
+  if (tid < DK) {  // gamma, and the largest decay of channel tid across one 16-row block
+    float acc = 0.f, first = 0.f, drop = 0.f;
     for (int i = 0; i < 64; ++i) {
       acc += gs[i * LK + tid];
       gs[i * LK + tid] = acc;
+      if (i % 16 == 0) first = acc;
+      if (i % 16 == 15) drop = fmaxf(drop, first - acc);
     }
+    if (drop > kMaxBlockDropBwd) sg[L::kSteep] = 1.f;  // (every writer stores the same value)
   }
   __syncthreads();
-  // dbeta (rows tid < 64): sum over d_v of G o R, plus sum_{j < i} dA_ij Ab_ij
-  if (tid < 64) {
-    float acc = dbv;
-    for (int j = 0; j < tid; ++j) acc = fmaf(dA[tid * L64 + j], aux[kda::Aux::kAb + tid * 64 + j], acc);
-    if (tid < nr) p.dbeta[(bos + r0 + tid) * H + h] = acc;
+  const bool steep = sg[L::kSteep] != 0.f;  // uniform over the workgroup
+  // dbeta's second term, sum_{j < i} dA_ij Ab_ij: eight threads per row i, eight
+  // columns each, added across the eight lanes (the rest comes in phase Z)
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = 8 * cg + e, j1 = j0 + 4;
+      part += j0 < ri ? dA[ri * L64 + j0] * abr0[e] : 0.f;
+      part += j1 < ri ? dA[ri * L64 + j1] * abr1[e] : 0.f;
+    }
+    part += __shfl_xor(part, 1, 64);
+    part += __shfl_xor(part, 2, 64);
+    part += __shfl_xor(part, 4, 64);
+    if (cg == 0) sg[L::kDbA + ri] = part;
   }
   const float gnl = tid < DK ? gs[63 * LK + tid] : 0.f;  // gamma_n of channel tid (phase Z)
-  float dgam[CPT], xx[CPT];
-  {
-    const float bi = be2[ri];
-    E* const dqo = static_cast<E*>(p.dq) + ((bos + r0 + ri) * H + h) * DK + cg * CPT;
-    E* const dko = static_cast<E*>(p.dk) + ((bos + r0 + ri) * H + h) * DK + cg * CPT;
-    // eight channels at a time
+  float dq[4][4], dk[4][4], dgam[4][4];
+  float xsum = 0.f;  // this lane's rows of sum_i (dKb o Kb)_i, channel ch
+  if (cw) {
+    const float gn = gs[63 * LK + ch];
+    // the elementwise terms of K o Gamma, Q o Gamma and the decayed keys
 #pragma unroll
-    for (int e0 = 0; e0 < CPT; e0 += 8) {
-      const int cb = cg * CPT + e0;
-      float gi[8], kv[8], qv[8], dq8[8], dk8[8];
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        gi[e] = gs[ri * LK + cb + e];
-        kv[e] = ks[ri * LK + cb + e];
-        qv[e] = qs[ri * LK + cb + e];
-        const float gn = gs[63 * LK + cb + e];
-        const float G = __builtin_amdgcn_exp2f(gi[e]), eb = __builtin_amdgcn_exp2f(gn - gi[e]);
-        dq8[e] = xQd[e0 + e] * G;
-        dk8[e] = xKd[e0 + e] * G + xKb[e0 + e] * eb;
-        xx[e0 + e] = xKb[e0 + e] * kv[e] * eb;
-        dgam[e0 + e] = (xKd[e0 + e] * kv[e] + xQd[e0 + e] * qv[e]) * G - xx[e0 + e];
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * b + 4 * g4 + r;
+        const float gi = gs[i * LK + ch], ki = ks[i * LK + ch], qi = qs[i * LK + ch];
+        const float G = __builtin_amdgcn_exp2f(gi), eb = __builtin_amdgcn_exp2f(gn - gi);
+        const float xx = xKb[b][r] * ki * eb;
+        dq[b][r] = xQd[b][r] * G;
+        dk[b][r] = xKd[b][r] * G + xKb[b][r] * eb;
+        dgam[b][r] = (xKd[b][r] * ki + xQd[b][r] * qi) * G - xx;
+        xsum += xx;
       }
-      // row side: j <= i
-      float aq[8], ak[8];
+    // Pair products through a reference row, on fp32 MFMA.  Row side (results on
+    // the rows i of block bi, sums over the rows j of block bj):
+    //   sum_j M_ij y_j exp(gamma_i - gamma_j) = exp(gamma_i - gamma_a) sum_j M_ij (y_j exp(gamma_a - gamma_j));
+    // column side (results on the rows j of block bj, sums over the rows i of bi):
+    //   sum_i M_ij x_i exp(gamma_i - gamma_j) = exp(gamma_c - gamma_j) sum_i M_ij (x_i exp(gamma_i - gamma_c)).
+    // Across blocks (bj < bi) a = 16 bj + 15 and c = 16 bi, so every factor is <= 1.
+    // Inside a diagonal block (bi = bj = b) a = 16 b and c = 16 b + 15: the inner
+    // factors are >= 1 but at most the block's own decay, which the steep flag
+    // bounds by 2^kMaxBlockDrop; steeper chunks take the pairs one by one below.
+    auto pairs = [&](int bi, int bj, int ra, int rc, bool diag) __attribute__((always_inline)) {
+      const float ga = gs[ra * LK + ch], gc = gs[rc * LK + ch];
+      f32x4_t p1 = zero4(), p2 = zero4(), p3 = zero4(), p4 = zero4();
+      const int im = 16 * bi + col;   // A row of the row side
+      const int jm = 16 * bj + col;   // A row of the column side
+      const float bim = be2[im];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) aq[e] = ak[e] = 0.f;
-      for (int j = 0; j <= ri; ++j) {
-        const float pij = dP[ri * L64 + j];
-        const float aij = j < ri ? bi * dA[ri * L64 + j] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = ks[j * LK + cb + e] * __builtin_amdgcn_exp2f(gi[e] - gs[j * LK + cb + e]);
-          aq[e] = fmaf(pij, t, aq[e]);
-          ak[e] = fmaf(aij, t, ak[e]);
+      for (int st = 0; st < 4; ++st) {
+        const int j = 16 * bj + 4 * st + g4;  // row side: k index
+        const int i = 16 * bi + 4 * st + g4;  // column side: k index
+        const float kr = ks[j * LK + ch] * __builtin_amdgcn_exp2f(ga - gs[j * LK + ch]);
+        float a1 = dP[im * L64 + j], a2 = bim * dA[im * L64 + j];
+        float a3 = dP[i * L64 + jm], a4 = be2[i] * dA[i * L64 + jm];
+        if (diag) {
+          a1 = j <= im ? a1 : 0.f;
+          a2 = j < im ? a2 : 0.f;
+          a3 = i >= jm ? a3 : 0.f;
+          a4 = i > jm ? a4 : 0.f;
         }
+        const float ec = __builtin_amdgcn_exp2f(gs[i * LK + ch] - gc);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, kr, p1, 0, 0, 0);
+        p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, kr, p2, 0, 0, 0);
+        p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, qs[i * LK + ch] * ec, p3, 0, 0, 0);
+        p4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4, ks[i * LK + ch] * ec, p4, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dq8[e] += aq[e];
-        dk8[e] += ak[e];
-        dgam[e0 + e] += qv[e] * aq[e] + kv[e] * ak[e];
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * bi + 4 * g4 + r, j = 16 * bj + 4 * g4 + r;
+        const float fi = __builtin_amdgcn_exp2f(gs[i * LK + ch] - ga);
+        const float fj = __builtin_amdgcn_exp2f(gc - gs[j * LK + ch]);
+        const float ki = ks[i * LK + ch], qi = qs[i * LK + ch], kj = ks[j * LK + ch];
+        dq[bi][r] += fi * p1[r];
+        dk[bi][r] += fi * p2[r];
+        dgam[bi][r] += fi * (qi * p1[r] + ki * p2[r]);
+        const float cs = fj * (p3[r] + p4[r]);
+        dk[bj][r] += cs;
+        dgam[bj][r] -= kj * cs;
       }
-      // column side: i' >= i
-      float bp[8], ba[8];
+    };
+    // (written out: every block index must be a compile-time constant, so that
+    // the per-block accumulators stay in registers)
+    pairs(1, 0, 15, 16, false);
+    pairs(2, 0, 15, 32, false);
+    pairs(3, 0, 15, 48, false);
+    pairs(2, 1, 31, 32, false);
+    pairs(3, 1, 31, 48, false);
+    pairs(3, 2, 47, 48, false);
+    if (!steep) {
+      pairs(0, 0, 0, 15, true);
+      pairs(1, 1, 16, 31, true);
+      pairs(2, 2, 32, 47, true);
+      pairs(3, 3, 48, 63, true);
+    } else {
+      // pairs inside the diagonal blocks one by one, one exponential each:
+      // exp(gamma_i - gamma_j) for j <= i (row side), exp(gamma_j - gamma_i) for j >= i
+      auto one_by_one = [&](int b) __attribute__((always_inline)) {
+        float gi[4], aq[4], ak1[4], bp[4], ba[4], bir[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bp[e] = ba[e] = 0.f;
-      for (int i2 = ri; i2 < 64; ++i2) {
-        const float pji = dP[i2 * L64 + ri];
-        const float aji = i2 > ri ? be2[i2] * dA[i2 * L64 + ri] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float d = __builtin_amdgcn_exp2f(gs[i2 * LK + cb + e] - gi[e]);
-          bp[e] = fmaf(pji, qs[i2 * LK + cb + e] * d, bp[e]);
-          ba[e] = fmaf(aji, ks[i2 * LK + cb + e] * d, ba[e]);
+        for (int r = 0; r < 4; ++r) {
+          gi[r] = gs[(16 * b + 4 * g4 + r) * LK + ch];
+          bir[r] = be2[16 * b + 4 * g4 + r];
+          aq[r] = ak1[r] = bp[r] = ba[r] = 0.f;
         }
-      }
+        for (int jj = 0; jj < 16; ++jj) {
+          const int j = 16 * b + jj;
+          const float kj = ks[j * LK + ch], qj = qs[j * LK + ch], gj = gs[j * LK + ch], bj = be2[j];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dk8[e] += bp[e] + ba[e];
-        dgam[e0 + e] -= kv[e] * (bp[e] + ba[e]);
-      }
-      if (ri < nr) {
-        if constexpr (sizeof(E) == 2) {
-          *reinterpret_cast<uint4*>(dqo + e0) = uint4{pack_bf16x2(dq8[0], dq8[1]), pack_bf16x2(dq8[2], dq8[3]),
-                                                      pack_bf16x2(dq8[4], dq8[5]), pack_bf16x2(dq8[6], dq8[7])};
-          *reinterpret_cast<uint4*>(dko + e0) = uint4{pack_bf16x2(dk8[0], dk8[1]), pack_bf16x2(dk8[2], dk8[3]),
-                                                      pack_bf16x2(dk8[4], dk8[5]), pack_bf16x2(dk8[6], dk8[7])};
-        } else {
-          *reinterpret_cast<f32x4_t*>(dqo + e0) = f32x4_t{dq8[0], dq8[1], dq8[2], dq8[3]};
-          *reinterpret_cast<f32x4_t*>(dqo + e0 + 4) = f32x4_t{dq8[4], dq8[5], dq8[6], dq8[7]};
-          *reinterpret_cast<f32x4_t*>(dko + e0) = f32x4_t{dk8[0], dk8[1], dk8[2], dk8[3]};
-          *reinterpret_cast<f32x4_t*>(dko + e0 + 4) = f32x4_t{dk8[4], dk8[5], dk8[6], dk8[7]};
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * b + 4 * g4 + r;
+            const float e = __builtin_amdgcn_exp2f(-fabsf(gi[r] - gj));
+            const float pij = dP[i * L64 + j], aij = dA[i * L64 + j];
+            const float pji = dP[j * L64 + i], aji = dA[j * L64 + i];
+            aq[r] = fmaf(j <= i ? pij : 0.f, kj * e, aq[r]);
+            ak1[r] = fmaf(j < i ? bir[r] * aij : 0.f, kj * e, ak1[r]);
+            bp[r] = fmaf(j >= i ? pji : 0.f, qj * e, bp[r]);
+            ba[r] = fmaf(j > i ? bj * aji : 0.f, kj * e, ba[r]);
+          }
         }
-      }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * b + 4 * g4 + r;
+          const float ki = ks[i * LK + ch], qi = qs[i * LK + ch];
+          dq[b][r] += aq[r];
+          dk[b][r] += ak1[r] + bp[r] + ba[r];
+          dgam[b][r] += qi * aq[r] + ki * (ak1[r] - bp[r] - ba[r]);
+        }
+      };
+      one_by_one(0);
+      one_by_one(1);
+      one_by_one(2);
+      one_by_one(3);
     }
   }
   __syncthreads();
 
-  // ---- phase Z: dg = reverse cumulative sum of dgamma, plus dgamma_n -----------
-  float* const dgs = sg;             // [64][LK] dgamma
-  float* const xs = sg + 64 * LK;    // [64][LK] dKb o Kb
+  // ---- phase Z: dq, dk stores; dg = reverse cumulative sum of dgamma, plus dgamma_n ----
+  float* const dqs = sg;               // [64][LK]
+  float* const dks = sg + 64 * LK;     // [64][LK]
+  float* const dgs = sg + 2 * 64 * LK; // [64][LK] dgamma
+  float* const xs = sg + 3 * 64 * LK;  // [DK] sum over the rows of dKb o Kb
+  // the four lanes of a channel (lane % 16 equal) hold its 64 rows between them
+  xsum += __shfl_xor(xsum, 16, 64);
+  xsum += __shfl_xor(xsum, 32, 64);
+  if (cw) {
 #pragma unroll
-  for (int e = 0; e < CPT; ++e) {
-    dgs[ri * LK + cg * CPT + e] = dgam[e];
-    xs[ri * LK + cg * CPT + e] = xx[e];
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * b + 4 * g4 + r;
+        dqs[i * LK + ch] = dq[b][r];
+        dks[i * LK + ch] = dk[b][r];
+        dgs[i * LK + ch] = dgam[b][r];
+      }
+    if (g4 == 0) xs[ch] = xsum;
   }
   __syncthreads();
+  if (ri < nr) {
+    E* const dqo = static_cast<E*>(p.dq) + ((bos + r0 + ri) * H + h) * DK + cg * CPT;
+    E* const dko = static_cast<E*>(p.dk) + ((bos + r0 + ri) * H + h) * DK + cg * CPT;
+#pragma unroll
+    for (int e0 = 0; e0 < CPT; e0 += 8) {
+      float a8[8], b8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a8[e] = dqs[ri * LK + cg * CPT + e0 + e];
+        b8[e] = dks[ri * LK + cg * CPT + e0 + e];
+      }
+      if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<uint4*>(dqo + e0) = uint4{pack_bf16x2(a8[0], a8[1]), pack_bf16x2(a8[2], a8[3]),
+                                                    pack_bf16x2(a8[4], a8[5]), pack_bf16x2(a8[6], a8[7])};
+        *reinterpret_cast<uint4*>(dko + e0) = uint4{pack_bf16x2(b8[0], b8[1]), pack_bf16x2(b8[2], b8[3]),
+                                                    pack_bf16x2(b8[4], b8[5]), pack_bf16x2(b8[6], b8[7])};
+      } else {
+        *reinterpret_cast<f32x4_t*>(dqo + e0) = f32x4_t{a8[0], a8[1], a8[2], a8[3]};
+        *reinterpret_cast<f32x4_t*>(dqo + e0 + 4) = f32x4_t{a8[4], a8[5], a8[6], a8[7]};
+        *reinterpret_cast<f32x4_t*>(dko + e0) = f32x4_t{b8[0], b8[1], b8[2], b8[3]};
+        *reinterpret_cast<f32x4_t*>(dko + e0 + 4) = f32x4_t{b8[4], b8[5], b8[6], b8[7]};
+      }
+    }
+  }
+  // dbeta (rows tid < 64): sum over d_v of G o R, plus the Ab term
+  if (tid < nr) p.dbeta[(bos + r0 + tid) * H + h] = dbv + sg[L::kDbA + tid];
   if (tid < DK) {
-    float acc = __builtin_amdgcn_exp2f(gnl) * dgn;
-    for (int i = 0; i < 64; ++i) acc += xs[i * LK + tid];
-    for (int s = 63; s >= 0; --s) {
-      acc += dgs[s * LK + tid];
-      if (s < nr) p.dg[((bos + r0 + s) * H + h) * DK + tid] = acc;
+    float acc = __builtin_amdgcn_exp2f(gnl) * dgn + xs[tid];
+    for (int s2 = 63; s2 >= 0; --s2) {
+      acc += dgs[s2 * LK + tid];
+      if (s2 < nr) p.dg[((bos + r0 + s2) * H + h) * DK + tid] = acc;
     }
   }
 }
 
 template <int DK, typename E>
 hipError_t launch_kda_bwd_t(const KdaBwdParams& p, hipStream_t s) {
-  using EL = std::conditional_t<sizeof(E) == 2, uint16_t, float>;
+  using EL = typename std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>::elem;
   constexpr size_t ds_smem = DsLds<DK, EL>::kBytes;
   constexpr size_t gr_smem = GradLds<DK>::kFloats * sizeof(float);
   static_assert(ds_smem <= 160 * 1024, "LDS budget exceeded");
