@@ -293,42 +293,48 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
 constexpr float kMaxBlockDropBwd = 100.f;
 
 // ---------------------------------------------------------------------------
-// Gradient kernel.  LDS in floats; rows of d_k + 4 (LK), 68 (L64) and 20 (LT)
-// floats.  Phase V (the d_v tiles) uses the first layout, the later phases reuse
-// the same memory.
+// Gradient kernel.  LDS in floats.  Row strides (in 4-byte banks, mod 64) are
+// picked for how each array is read by the MFMA lanes: 16 lanes along a row and
+// four k rows (stride = 16 mod 64: conflict free), or 16 rows and four k columns
+// (stride = 4 mod 64: conflict free); an array read both ways takes 20 mod 64
+// (conflict free one way, two-way the other).  Phase V (the d_v tiles) uses the
+// first layout, the later phases reuse the same memory.
 template <int DK>
 struct GradLds {
-  static constexpr int LK = DK + 4, L64 = 68, LT = 20;
+  static constexpr int LK = DK + 4;   // rows of d_k (read along rows: 4 mod 64)
+  static constexpr int LT = 20;       // the 16-column tiles (read both ways)
+  static constexpr int LTT = 84;      // T (read both ways)
+  static constexpr int LPP = 80;      // P (read transposed only: 16 mod 64)
+  static constexpr int LY = 84;       // dA, dP in phase Y (read both ways)
   // phase V: the per-tile arrays first (within 64 KiB: immediate LDS offsets)
   static constexpr int kSt = 0;                   // [DK][LT] S tile
   static constexpr int kDst = kSt + DK * LT;      // [DK][LT] dS' tile
   static constexpr int kV = kDst + DK * LT;       // [64][LT] V tile
   static constexpr int kDo = kV + 64 * LT;        // [64][LT] scale dO tile
   static constexpr int kR = kDo + 64 * LT;        // [64][LT] R
-  static constexpr int kBR = kR + 64 * LT;        // [64][LT] diag(beta) R
-  static constexpr int kE = kBR + 64 * LT;        // [64][LT] E
+  static constexpr int kE = kR + 64 * LT;         // [64][LT] E
   static constexpr int kDe = kE + 64 * LT;        // [64][LT] dE
   static constexpr int kG = kDe + 64 * LT;        // [64][LT] G = T^T dE
   static constexpr int kBe = kG + 64 * LT;        // [64] beta
   static constexpr int kKd = kBe + 64;            // [64][LK] K o Gamma
   static constexpr int kKb = kKd + 64 * LK;       // [64][LK] K o exp(gamma_n - gamma)
-  static constexpr int kT = kKb + 64 * LK;        // [64][L64] T
-  static constexpr int kP = kT + 64 * L64;        // [64][L64] P (zero above the diagonal)
-  static constexpr int kEndV = kP + 64 * L64;
+  static constexpr int kT = kKb + 64 * LK;        // [64][LTT] T
+  static constexpr int kP = kT + 64 * LTT;        // [64][LPP] P (zero above the diagonal)
+  static constexpr int kEndV = kP + 64 * LPP;
   // phase Y
-  static constexpr int kDA = 0;                   // [64][L64] dA = -G E^T
-  static constexpr int kDP = kDA + 64 * L64;      // [64][L64] dP = dOs E^T
-  static constexpr int kQ = kDP + 64 * L64;       // [64][LK] q
+  static constexpr int kDA = 0;                   // [64][LY] dA = -G E^T
+  static constexpr int kDP = kDA + 64 * LY;       // [64][LY] dP = dOs E^T
+  static constexpr int kQ = kDP + 64 * LY;        // [64][LK] q
   static constexpr int kK = kQ + 64 * LK;         // [64][LK] k
   static constexpr int kGam = kK + 64 * LK;       // [64][LK] gamma (log2 units)
   static constexpr int kBe2 = kGam + 64 * LK;     // [64] beta
   static constexpr int kEndY = kBe2 + 64;
   static constexpr int kDbA = kEndY;              // [64] sum_{j < i} dA_ij Ab_ij (read in phase Z)
   static constexpr int kSteep = kDbA + 64;        // flag: some block decays by more than 2^kMaxBlockDropBwd
-  static constexpr int kFloats = kEndV > kEndY ? kEndV : kEndY;
+  static constexpr int kFloats = kEndV > kSteep + 1 ? kEndV : kSteep + 1;
   static_assert(kBe * 4 <= 65536, "tile arrays within the immediate-offset range");
   static_assert(3 * 64 * LK + DK <= kFloats, "phase X and Z arrays must fit");
-  static_assert(kSteep + 1 <= kFloats && kDbA >= 3 * 64 * LK + DK, "dbeta partials beside the phase Z arrays");
+  static_assert(kDbA >= 3 * 64 * LK + DK, "dbeta partials beside the phase Z arrays");
   static_assert(kFloats * 4 <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -344,7 +350,7 @@ struct GradLds {
 template <int DK, typename E>
 __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   using L = GradLds<DK>;
-  constexpr int LK = L::LK, L64 = L::L64, LT = L::LT;
+  constexpr int LK = L::LK, LT = L::LT, LTT = L::LTT, LPP = L::LPP, LY = L::LY;
   constexpr int CPT = DK / 8;         // channels per thread in the row phases
   constexpr int NK = DK / 32;         // dKd / dQd / dKb tiles per wave
   constexpr int VPR = 16 * static_cast<int>(sizeof(E)) / 16;  // io vectors per tile row
@@ -394,9 +400,9 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vx = tid + 512 * u, i = vx >> 4, j0 = 4 * (vx & 15);
-      *reinterpret_cast<f32x4_t*>(sg + L::kT + i * L64 + j0) = tv[u];
+      *reinterpret_cast<f32x4_t*>(sg + L::kT + i * LTT + j0) = tv[u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sg[L::kP + i * L64 + j0 + e] = j0 + e <= i ? pv4[u][e] : 0.f;
+      for (int e = 0; e < 4; ++e) sg[L::kP + i * LPP + j0 + e] = j0 + e <= i ? pv4[u][e] : 0.f;
     }
     if (tid < 64) sg[L::kBe + tid] = tid < nr ? bt : 0.f;
   }
@@ -431,7 +437,6 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   float* const vt = sg + L::kV;
   float* const dot = sg + L::kDo;
   float* const rt = sg + L::kR;
-  float* const brt = sg + L::kBR;
   float* const et = sg + L::kE;
   float* const det = sg + L::kDe;
   float* const gt = sg + L::kG;
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
     }
     __syncthreads();
     if (t + 1 < ntile) prefetch(t + 1);
-    if (w < 4) {  // R = V - Kd S and diag(beta) R (rows 16 w ..)
+    if (w < 4) {  // R = V - Kd S (rows 16 w ..)
       f32x4_t acc = zero4();
       mm<DK, 1, LT>(acc, kd + (16 * w + col) * LK + kq, st + kq * LT + col);
 #pragma unroll
@@ -498,26 +503,31 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
         const int row = 16 * w + 4 * g4 + r;
         const float rv2 = vt[row * LT + col] - acc[r];
         rt[row * LT + col] = rv2;
-        brt[row * LT + col] = be[row] * rv2;
       }
     } else {  // dE = P^T dOs + Kb dS' (rows 16 (w - 4) ..)
       const int w4 = w - 4;
       f32x4_t acc = zero4();
-      mm<64, L64, LT>(acc, sg + L::kP + kq * L64 + 16 * w4 + col, dot + kq * LT + col);
+      mm<64, LPP, LT>(acc, sg + L::kP + kq * LPP + 16 * w4 + col, dot + kq * LT + col);
       mm<DK, 1, LT>(acc, kb + (16 * w4 + col) * LK + kq, dst + kq * LT + col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) det[(16 * w4 + 4 * g4 + r) * LT + col] = acc[r];
     }
     __syncthreads();
     if (w < 4) {  // E = T diag(beta) R
-      f32x4_t acc = zero4();
-      mm<64, 1, LT>(acc, sg + L::kT + (16 * w + col) * L64 + kq, brt + kq * LT + col);
+      f32x4_t acc = zero4(), x[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int j = 4 * st + kq;
+        x[st % 4] = __builtin_amdgcn_mfma_f32_16x16x4f32(sg[L::kT + (16 * w + col) * LTT + j], be[j] * rt[j * LT + col],
+                                                         x[st % 4], 0, 0, 0);
+      }
+      acc = (x[0] + x[1]) + (x[2] + x[3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) et[(16 * w + 4 * g4 + r) * LT + col] = acc[r];
     } else {  // G = T^T dE; dv = diag(beta) G
       const int w4 = w - 4;
       f32x4_t acc = zero4();
-      mm<64, L64, LT>(acc, sg + L::kT + kq * L64 + 16 * w4 + col, det + kq * LT + col);
+      mm<64, LTT, LT>(acc, sg + L::kT + kq * LTT + 16 * w4 + col, det + kq * LT + col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * w4 + 4 * g4 + r;
@@ -597,8 +607,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + 4 * g4 + r, j = 16 * tj + col;
-      dA[i * L64 + j] = -aA[x][r];
-      dP[i * L64 + j] = aP[x][r];
+      dA[i * LY + j] = -aA[x][r];
+      dP[i * LY + j] = aP[x][r];
     }
   }
   f32x4_t abr0, abr1;  // Ab row ri, columns 8 cg .. 8 cg + 7
@@ -641,8 +651,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j0 = 8 * cg + e, j1 = j0 + 4;
-      part += j0 < ri ? dA[ri * L64 + j0] * abr0[e] : 0.f;
-      part += j1 < ri ? dA[ri * L64 + j1] * abr1[e] : 0.f;
+      part += j0 < ri ? dA[ri * LY + j0] * abr0[e] : 0.f;
+      part += j1 < ri ? dA[ri * LY + j1] * abr1[e] : 0.f;
     }
     part += __shfl_xor(part, 1, 64);
     part += __shfl_xor(part, 2, 64);
@@ -688,8 +698,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
         const int j = 16 * bj + 4 * st + g4;  // row side: k index
         const int i = 16 * bi + 4 * st + g4;  // column side: k index
         const float kr = ks[j * LK + ch] * __builtin_amdgcn_exp2f(ga - gs[j * LK + ch]);
-        float a1 = dP[im * L64 + j], a2 = bim * dA[im * L64 + j];
-        float a3 = dP[i * L64 + jm], a4 = be2[i] * dA[i * L64 + jm];
+        float a1 = dP[im * LY + j], a2 = bim * dA[im * LY + j];
+        float a3 = dP[i * LY + jm], a4 = be2[i] * dA[i * LY + jm];
         if (diag) {
           a1 = j <= im ? a1 : 0.f;
           a2 = j < im ? a2 : 0.f;
@@ -747,8 +757,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * b + 4 * g4 + r;
             const float e = __builtin_amdgcn_exp2f(-fabsf(gi[r] - gj));
-            const float pij = dP[i * L64 + j], aij = dA[i * L64 + j];
-            const float pji = dP[j * L64 + i], aji = dA[j * L64 + i];
+            const float pij = dP[i * LY + j], aij = dA[i * LY + j];
+            const float pji = dP[j * LY + i], aji = dA[j * LY + i];
             aq[r] = fmaf(j <= i ? pij : 0.f, kj * e, aq[r]);
             ak1[r] = fmaf(j < i ? bir[r] * aij : 0.f, kj * e, ak1[r]);
             bp[r] = fmaf(j >= i ? pji : 0.f, qj * e, bp[r]);
