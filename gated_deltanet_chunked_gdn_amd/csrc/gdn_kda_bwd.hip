@@ -293,35 +293,38 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
 constexpr float kMaxBlockDropBwd = 100.f;
 
 // ---------------------------------------------------------------------------
-// Gradient kernel.  LDS in floats.  Row strides (in 4-byte banks, mod 64) are
-// picked for how each array is read by the MFMA lanes: 16 lanes along a row and
-// four k rows (stride = 16 mod 64: conflict free), or 16 rows and four k columns
-// (stride = 4 mod 64: conflict free); an array read both ways takes 20 mod 64
-// (conflict free one way, two-way the other).  Phase V (the d_v tiles) uses the
-// first layout, the later phases reuse the same memory.
+// Gradient kernel.  Phase V (the d_v tiles) keeps its operands in the MFMA
+// operand type EL (bf16 for bf16 io, fp32 for fp32 io) with rows padded by 16
+// bytes; the tiles are TW = 32 (bf16: one MFMA depth) or 16 (fp32) columns of d_v.
+template <int DK, typename EL>
+struct GradVLds {
+  static constexpr int ES = static_cast<int>(sizeof(EL));
+  static constexpr int PAD = 16 / ES;
+  static constexpr int TW = ES == 2 ? 32 : 16;
+  static constexpr int LT = TW + PAD, LKE = DK + PAD, L64E = 64 + PAD;
+  static constexpr int kSt = 0;                         // [DK][LT] S tile
+  static constexpr int kDst = kSt + DK * LT * ES;       // [DK][LT] dS' tile
+  static constexpr int kV = kDst + DK * LT * ES;        // [64][LT] V tile
+  static constexpr int kDo = kV + 64 * LT * ES;         // [64][LT] scale dO tile
+  static constexpr int kR = kDo + 64 * LT * ES;         // [64][LT] R
+  static constexpr int kE = kR + 64 * LT * ES;          // [64][LT] E
+  static constexpr int kDe = kE + 64 * LT * ES;         // [64][LT] dE
+  static constexpr int kG = kDe + 64 * LT * ES;         // [64][LT] G = T^T dE
+  static constexpr int kBe = kG + 64 * LT * ES;         // [64] beta (fp32)
+  static constexpr int kKd = kBe + 64 * 4;              // [64][LKE] K o Gamma
+  static constexpr int kKb = kKd + 64 * LKE * ES;       // [64][LKE] K o exp(gamma_n - gamma)
+  static constexpr int kT = kKb + 64 * LKE * ES;        // [64][L64E] T
+  static constexpr int kP = kT + 64 * L64E * ES;        // [64][L64E] P (zero above the diagonal)
+  static constexpr int kBytes = kP + 64 * L64E * ES;
+  static_assert(kBe % 16 == 0 && kKd % 16 == 0 && kT % 16 == 0, "16-byte aligned rows");
+};
+
+// The later phases, in floats (rows of d_k + 4, and 84 for dA and dP: read both
+// along rows and down columns).
 template <int DK>
 struct GradLds {
-  static constexpr int LK = DK + 4;   // rows of d_k (read along rows: 4 mod 64)
-  static constexpr int LT = 20;       // the 16-column tiles (read both ways)
-  static constexpr int LTT = 84;      // T (read both ways)
-  static constexpr int LPP = 80;      // P (read transposed only: 16 mod 64)
-  static constexpr int LY = 84;       // dA, dP in phase Y (read both ways)
-  // phase V: the per-tile arrays first (within 64 KiB: immediate LDS offsets)
-  static constexpr int kSt = 0;                   // [DK][LT] S tile
-  static constexpr int kDst = kSt + DK * LT;      // [DK][LT] dS' tile
-  static constexpr int kV = kDst + DK * LT;       // [64][LT] V tile
-  static constexpr int kDo = kV + 64 * LT;        // [64][LT] scale dO tile
-  static constexpr int kR = kDo + 64 * LT;        // [64][LT] R
-  static constexpr int kE = kR + 64 * LT;         // [64][LT] E
-  static constexpr int kDe = kE + 64 * LT;        // [64][LT] dE
-  static constexpr int kG = kDe + 64 * LT;        // [64][LT] G = T^T dE
-  static constexpr int kBe = kG + 64 * LT;        // [64] beta
-  static constexpr int kKd = kBe + 64;            // [64][LK] K o Gamma
-  static constexpr int kKb = kKd + 64 * LK;       // [64][LK] K o exp(gamma_n - gamma)
-  static constexpr int kT = kKb + 64 * LK;        // [64][LTT] T
-  static constexpr int kP = kT + 64 * LTT;        // [64][LPP] P (zero above the diagonal)
-  static constexpr int kEndV = kP + 64 * LPP;
-  // phase Y
+  static constexpr int LK = DK + 4;
+  static constexpr int LY = 84;
   static constexpr int kDA = 0;                   // [64][LY] dA = -G E^T
   static constexpr int kDP = kDA + 64 * LY;       // [64][LY] dP = dOs E^T
   static constexpr int kQ = kDP + 64 * LY;        // [64][LK] q
@@ -331,16 +334,20 @@ struct GradLds {
   static constexpr int kEndY = kBe2 + 64;
   static constexpr int kDbA = kEndY;              // [64] sum_{j < i} dA_ij Ab_ij (read in phase Z)
   static constexpr int kSteep = kDbA + 64;        // flag: some block decays by more than 2^kMaxBlockDropBwd
-  static constexpr int kFloats = kEndV > kSteep + 1 ? kEndV : kSteep + 1;
-  static_assert(kBe * 4 <= 65536, "tile arrays within the immediate-offset range");
-  static_assert(3 * 64 * LK + DK <= kFloats, "phase X and Z arrays must fit");
-  static_assert(kDbA >= 3 * 64 * LK + DK, "dbeta partials beside the phase Z arrays");
+  static constexpr int kDgn = kSteep + 4;         // [DK] sum over d_v of dS' o S (read in phase Z)
+  static constexpr int kFloats = kDgn + DK;
+  static_assert(3 * 64 * LK + DK <= kDbA, "phase X and Z arrays below the dbeta partials");
   static_assert(kFloats * 4 <= 160 * 1024, "LDS budget exceeded");
 };
+template <int DK, typename EL>
+constexpr size_t grad_smem_bytes() {
+  return GradVLds<DK, EL>::kBytes > GradLds<DK>::kFloats * 4 ? GradVLds<DK, EL>::kBytes
+                                                             : GradLds<DK>::kFloats * 4;
+}
 
-// Eight waves.  Phase V: per 16-column tile of d_v, waves 0-3 form R then E and
+// Eight waves.  Phase V: per TW-column tile of d_v, waves 0-3 form R then E and
 // waves 4-7 dE then G (one 16-row block each), then every wave accumulates its
-// share of dA, dP (two 16x16 tiles each) and dKd, dQd, dKb (DK / 32 tiles each).
+// share of dA, dP (two 16x16 tiles each) and G S^T, dQd, dKb (DK / 32 tiles each).
 // Phase X/Y: wave w < DK / 16 owns channels 16 w .. 16 w + 15 (lane: one channel,
 // 16 rows) for the elementwise terms and the pair sums: pairs inside the diagonal
 // 16x16 blocks one exponential each, pairs across blocks as fp32 MFMA products of
@@ -349,15 +356,24 @@ struct GradLds {
 // channel c's reverse cumulative sum.
 template <int DK, typename E>
 __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
+  using Op = std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>;
+  using EL = typename Op::elem;
+  using V = GradVLds<DK, EL>;
   using L = GradLds<DK>;
-  constexpr int LK = L::LK, LT = L::LT, LTT = L::LTT, LPP = L::LPP, LY = L::LY;
+  constexpr int LK = L::LK, LY = L::LY;
+  constexpr int TW = V::TW, LT = V::LT, LKE = V::LKE, L64E = V::L64E, KS = Op::KSTEP;
   constexpr int CPT = DK / 8;         // channels per thread in the row phases
-  constexpr int NK = DK / 32;         // dKd / dQd / dKb tiles per wave
-  constexpr int VPR = 16 * static_cast<int>(sizeof(E)) / 16;  // io vectors per tile row
-  constexpr int EPV = 16 / static_cast<int>(sizeof(E));
+  constexpr int NK = DK / 32;         // G S^T / dQd / dKb tiles per wave
+  constexpr int NB = TW / 16;         // 16-column blocks of a tile
+  constexpr int EPV = 16 / static_cast<int>(sizeof(E));    // io elements per vector
+  constexpr int VPR = TW / EPV;                            // io vectors per tile row
+  constexpr int SPR = TW / 4;                              // fp32 state vectors per tile row
+  constexpr int NSV = (DK * SPR + 511) / 512;              // state vectors per thread
+  static_assert(VPR * 64 <= 512 && (NSV == 1 || NSV * 512 == DK * SPR), "tile loads");
   extern __shared__ __align__(16) float sg[];
+  char* const sv = reinterpret_cast<char*>(sg);
   const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z, tid = threadIdx.x;
-  const int lane = tid & 63, col = lane & 15, g4 = lane >> 4, kq = g4;
+  const int lane = tid & 63, col = lane & 15, g4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   int64_t bos, len;
   seq_range(p.seq, n, bos, len);
@@ -376,11 +392,25 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   const int ri = tid >> 3, cg = tid & 7;   // row phases: row ri, channels cg CPT ..
   const int rowc = ri < nr ? ri : nr - 1;  // rows past the chunk load its last row and are zeroed
 
+  EL* const st = reinterpret_cast<EL*>(sv + V::kSt);
+  EL* const dst = reinterpret_cast<EL*>(sv + V::kDst);
+  EL* const vt = reinterpret_cast<EL*>(sv + V::kV);
+  EL* const dot = reinterpret_cast<EL*>(sv + V::kDo);
+  EL* const rt = reinterpret_cast<EL*>(sv + V::kR);
+  EL* const et = reinterpret_cast<EL*>(sv + V::kE);
+  EL* const det = reinterpret_cast<EL*>(sv + V::kDe);
+  EL* const gt = reinterpret_cast<EL*>(sv + V::kG);
+  float* const be = reinterpret_cast<float*>(sv + V::kBe);
+  EL* const kd = reinterpret_cast<EL*>(sv + V::kKd);
+  EL* const kb = reinterpret_cast<EL*>(sv + V::kKb);
+  EL* const tm = reinterpret_cast<EL*>(sv + V::kT);
+  EL* const pm = reinterpret_cast<EL*>(sv + V::kP);
+
   // ---- stage 0: gamma, K o Gamma, K o exp(gamma_n - gamma), T, P, beta --------
-  float* const kd = sg + L::kKd;
-  float* const kb = sg + L::kKb;
+  // (k and gamma pass through fp32 scratch at the start of LDS first)
   {
-    // every load first (16-byte vectors), then the LDS stores
+    float* const ksc = sg;               // [64][LK]
+    float* const gsc = sg + 64 * LK;     // [64][LK]
     const int64_t off = ((bos + r0 + rowc) * H + h) * DK + cg * CPT;
     float kv[CPT], gv[CPT];
     ld_row<CPT>(k + off, kv);
@@ -394,172 +424,224 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
     const float bt = p.beta[(bos + r0 + (lane < nr ? lane : nr - 1)) * H + h];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      kd[ri * LK + cg * CPT + e] = ri < nr ? kv[e] : 0.f;
-      kb[ri * LK + cg * CPT + e] = ri < nr ? gv[e] * chunk::kLog2e : 0.f;
+      ksc[ri * LK + cg * CPT + e] = ri < nr ? kv[e] : 0.f;
+      gsc[ri * LK + cg * CPT + e] = ri < nr ? gv[e] * chunk::kLog2e : 0.f;
+    }
+    __syncthreads();
+    if (tid < DK) {  // cumulative sum of channel tid over the chunk, in place (log2 units)
+      float acc = 0.f;
+      for (int i = 0; i < 64; ++i) {
+        acc += gsc[i * LK + tid];
+        gsc[i * LK + tid] = acc;
+      }
+    }
+    __syncthreads();
+    float gl[CPT];
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      kv[e] = ksc[ri * LK + cg * CPT + e];
+      gv[e] = gsc[ri * LK + cg * CPT + e];
+      gl[e] = gsc[63 * LK + cg * CPT + e];
+    }
+    __syncthreads();  // the scratch is dead from here on
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      kd[ri * LKE + cg * CPT + e] = Op::cvt(kv[e] * __builtin_amdgcn_exp2f(gv[e]));
+      kb[ri * LKE + cg * CPT + e] = Op::cvt(kv[e] * __builtin_amdgcn_exp2f(gl[e] - gv[e]));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vx = tid + 512 * u, i = vx >> 4, j0 = 4 * (vx & 15);
-      *reinterpret_cast<f32x4_t*>(sg + L::kT + i * LTT + j0) = tv[u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sg[L::kP + i * LPP + j0 + e] = j0 + e <= i ? pv4[u][e] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        tm[i * L64E + j0 + e] = Op::cvt(tv[u][e]);
+        pm[i * L64E + j0 + e] = Op::cvt(j0 + e <= i ? pv4[u][e] : 0.f);
+      }
     }
-    if (tid < 64) sg[L::kBe + tid] = tid < nr ? bt : 0.f;
-  }
-  __syncthreads();
-  if (tid < DK) {  // cumulative sum of channel tid over the chunk, in place (log2 units)
-    float acc = 0.f;
-    for (int i = 0; i < 64; ++i) {
-      acc += kb[i * LK + tid];
-      kb[i * LK + tid] = acc;
-    }
-  }
-  __syncthreads();
-  {
-    float kv[CPT], gv[CPT], gl[CPT];
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      kv[e] = kd[ri * LK + cg * CPT + e];
-      gv[e] = kb[ri * LK + cg * CPT + e];
-      gl[e] = kb[63 * LK + cg * CPT + e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      kd[ri * LK + cg * CPT + e] = kv[e] * __builtin_amdgcn_exp2f(gv[e]);
-      kb[ri * LK + cg * CPT + e] = kv[e] * __builtin_amdgcn_exp2f(gl[e] - gv[e]);
-    }
+    if (tid < 64) be[tid] = tid < nr ? bt : 0.f;
   }
 
   // ---- phase V: the d_v tiles ----------------------------------------------
-  float* const st = sg + L::kSt;
-  float* const dst = sg + L::kDst;
-  float* const vt = sg + L::kV;
-  float* const dot = sg + L::kDo;
-  float* const rt = sg + L::kR;
-  float* const et = sg + L::kE;
-  float* const det = sg + L::kDe;
-  float* const gt = sg + L::kG;
-  const float* const be = sg + L::kBe;
   f32x4_t aA[2], aP[2], aKd[NK], aQd[NK], aKb[NK];
 #pragma unroll
   for (int x = 0; x < 2; ++x) aA[x] = aP[x] = zero4();
 #pragma unroll
   for (int x = 0; x < NK; ++x) aKd[x] = aQd[x] = aKb[x] = zero4();
-  float dbv = 0.f;   // tid < 64: sum over d_v of G o R for row tid
-  float dgn = 0.f;   // tid < DK: sum over d_v of dS' o S for channel tid
+  float dbv = 0.f;       // tid < 64: sum over d_v of G o R for row tid
+  float dgp[NSV];        // sum over d_v of dS' o S, this thread's part of rows tid / SPR + (512 / SPR) u
+#pragma unroll
+  for (int u = 0; u < NSV; ++u) dgp[u] = 0.f;
 
-  // tile prefetch: S and dS' rows (four floats per vector), V and dO rows (io
+  // tile prefetch: S and dS' rows (four fp32 per vector), V and dO rows (io
   // vectors, bounded to the chunk's rows: past them the loads read zeros)
-  const bool sl = tid < DK * 4;
-  const int srow = sl ? tid >> 2 : 0, spart = tid & 3;
   const bool iol = tid < 64 * VPR;
   const int iorow = iol ? tid / VPR : 0, iopart = tid % VPR;
   const int vbytes = static_cast<int>(((nr - 1) * H * Dv + Dv) * sizeof(E));
   const auto rv = chunk::buffer_rsrc(v + ((bos + r0) * H + h) * Dv, vbytes);
   const auto rdo = chunk::buffer_rsrc(dO + ((bos + r0) * H + h) * Dv, vbytes);
-  f32x4_t ps = zero4(), pds = zero4(), pv = zero4(), pdo = zero4();
+  f32x4_t ps[NSV], pds[NSV], pv = zero4(), pdo = zero4();
+  // (d_v a multiple of 16: the last bf16 tile may hold 16 valid columns; the
+  // vectors past d_v load column v0 again and are staged as zeros)
   auto prefetch = [&](int t) {
-    const int v0 = 16 * t;
-    ps = *reinterpret_cast<const f32x4_t*>(Sg + srow * Dv + v0 + 4 * spart);
-    pds = *reinterpret_cast<const f32x4_t*>(dSg + srow * Dv + v0 + 4 * spart);
-    const int off = (iorow * H * Dv + v0 + iopart * EPV) * static_cast<int>(sizeof(E));
+    const int v0 = TW * t;
+#pragma unroll
+    for (int u = 0; u < NSV; ++u) {
+      const int x = tid + 512 * u, row = x < DK * SPR ? x / SPR : 0, part = x % SPR;
+      const int cv = v0 + 4 * part < Dv ? v0 + 4 * part : v0;
+      ps[u] = *reinterpret_cast<const f32x4_t*>(Sg + row * Dv + cv);
+      pds[u] = *reinterpret_cast<const f32x4_t*>(dSg + row * Dv + cv);
+    }
+    const int cv = v0 + iopart * EPV < Dv ? v0 + iopart * EPV : v0;
+    const int off = (iorow * H * Dv + cv) * static_cast<int>(sizeof(E));
     pv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     pdo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
   };
-  auto io_to_lds = [&](float* dstp, const f32x4_t& x, float mul) {
+  // EPV io values of a vector to EL in LDS, times mul
+  auto io_to_lds = [&](EL* dstp, const f32x4_t& x, float mul) {
     if constexpr (sizeof(E) == 2) {
       const uint32_t* u = reinterpret_cast<const uint32_t*>(&x);
+      float f[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dstp[2 * e] = mul * __uint_as_float(u[e] << 16);
-        dstp[2 * e + 1] = mul * __uint_as_float(u[e] & 0xffff0000u);
+        f[2 * e] = mul * __uint_as_float(u[e] << 16);
+        f[2 * e + 1] = mul * __uint_as_float(u[e] & 0xffff0000u);
       }
+      *reinterpret_cast<uint4*>(dstp) = uint4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                              pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dstp[e] = mul * x[e];
+      *reinterpret_cast<f32x4_t*>(dstp) = x * mul;
     }
   };
-  const int ntile = Dv / 16;
+  const int ntile = (Dv + TW - 1) / TW;
   prefetch(0);
   for (int t = 0; t < ntile; ++t) {
-    const int v0 = 16 * t;
+    const int v0 = TW * t;
     __syncthreads();  // the previous tile's reads are done (and stage 0's writes visible)
-    if (sl) {
-      *reinterpret_cast<f32x4_t*>(st + srow * LT + 4 * spart) = ps;
-      *reinterpret_cast<f32x4_t*>(dst + srow * LT + 4 * spart) = pds;
+#pragma unroll
+    for (int u = 0; u < NSV; ++u) {
+      const int x = tid + 512 * u, row = x / SPR, part = x % SPR;
+      if (x >= DK * SPR) continue;
+      const f32x4_t z = zero4();
+      const bool okc = v0 + 4 * part < Dv;
+      const f32x4_t a = okc ? ps[u] : z, b = okc ? pds[u] : z;
+      chunk::store4<EL>(st + row * LT + 4 * part, a[0], a[1], a[2], a[3]);
+      chunk::store4<EL>(dst + row * LT + 4 * part, b[0], b[1], b[2], b[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dgp[u] = fmaf(a[e], b[e], dgp[u]);
     }
     if (iol) {
-      io_to_lds(vt + iorow * LT + iopart * EPV, pv, 1.f);
-      io_to_lds(dot + iorow * LT + iopart * EPV, pdo, p.scale);
+      const bool okc = v0 + iopart * EPV < Dv;
+      io_to_lds(vt + iorow * LT + iopart * EPV, okc ? pv : zero4(), 1.f);
+      io_to_lds(dot + iorow * LT + iopart * EPV, okc ? pdo : zero4(), p.scale);
     }
     __syncthreads();
     if (t + 1 < ntile) prefetch(t + 1);
     if (w < 4) {  // R = V - Kd S (rows 16 w ..)
-      f32x4_t acc = zero4();
-      mm<DK, 1, LT>(acc, kd + (16 * w + col) * LK + kq, st + kq * LT + col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w + 4 * g4 + r;
-        const float rv2 = vt[row * LT + col] - acc[r];
-        rt[row * LT + col] = rv2;
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += KS)
+          acc = Op::mma(Op::frag(kd + 16 * w * LKE, LKE, lane, k0), Op::frag_tr(st + 16 * nb, LT, lane, k0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * w + 4 * g4 + r;
+          rt[row * LT + 16 * nb + col] = Op::cvt(Op::widen(vt[row * LT + 16 * nb + col]) - acc[r]);
+        }
       }
     } else {  // dE = P^T dOs + Kb dS' (rows 16 (w - 4) ..)
       const int w4 = w - 4;
-      f32x4_t acc = zero4();
-      mm<64, LPP, LT>(acc, sg + L::kP + kq * LPP + 16 * w4 + col, dot + kq * LT + col);
-      mm<DK, 1, LT>(acc, kb + (16 * w4 + col) * LK + kq, dst + kq * LT + col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) det[(16 * w4 + 4 * g4 + r) * LT + col] = acc[r];
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += KS)
+          acc = Op::mma(Op::frag_tr(pm + 16 * w4, L64E, lane, k0), Op::frag_tr(dot + 16 * nb, LT, lane, k0), acc);
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += KS)
+          acc = Op::mma(Op::frag(kb + 16 * w4 * LKE, LKE, lane, k0), Op::frag_tr(dst + 16 * nb, LT, lane, k0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) det[(16 * w4 + 4 * g4 + r) * LT + 16 * nb + col] = Op::cvt(acc[r]);
+      }
     }
     __syncthreads();
     if (w < 4) {  // E = T diag(beta) R
-      f32x4_t acc = zero4(), x[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const int j = 4 * st + kq;
-        x[st % 4] = __builtin_amdgcn_mfma_f32_16x16x4f32(sg[L::kT + (16 * w + col) * LTT + j], be[j] * rt[j * LT + col],
-                                                         x[st % 4], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += KS)
+          acc = Op::mma(Op::scale(Op::frag(tm + 16 * w * L64E, L64E, lane, k0), be, lane, k0),
+                        Op::frag_tr(rt + 16 * nb, LT, lane, k0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) et[(16 * w + 4 * g4 + r) * LT + 16 * nb + col] = Op::cvt(acc[r]);
       }
-      acc = (x[0] + x[1]) + (x[2] + x[3]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) et[(16 * w + 4 * g4 + r) * LT + col] = acc[r];
     } else {  // G = T^T dE; dv = diag(beta) G
       const int w4 = w - 4;
-      f32x4_t acc = zero4();
-      mm<64, LTT, LT>(acc, sg + L::kT + kq * LTT + 16 * w4 + col, det + kq * LT + col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w4 + 4 * g4 + r;
-        gt[row * LT + col] = acc[r];
-        if (row < nr) IoT<E>::st(static_cast<E*>(p.dv) + ((bos + r0 + row) * H + h) * Dv + v0 + col, be[row] * acc[r]);
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += KS)
+          acc = Op::mma(Op::frag_tr(tm + 16 * w4, L64E, lane, k0), Op::frag_tr(det + 16 * nb, LT, lane, k0), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * w4 + 4 * g4 + r;
+          gt[row * LT + 16 * nb + col] = Op::cvt(acc[r]);
+          if (row < nr && v0 + 16 * nb < Dv)
+            IoT<E>::st(static_cast<E*>(p.dv) + ((bos + r0 + row) * H + h) * Dv + v0 + 16 * nb + col,
+                       be[row] * acc[r]);
+        }
       }
     }
     __syncthreads();
-    // accumulations over this tile's 16 columns
+    // accumulations over this tile's TW columns
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int ta = 2 * w + x, ti = ta >> 2, tj = ta & 3;
-      mm<16, 1, 1, 1>(aA[x], gt + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
-      mm<16, 1, 1, 1>(aP[x], dot + (16 * ti + col) * LT + kq, et + (16 * tj + col) * LT + kq);
+#pragma unroll
+      for (int k0 = 0; k0 < TW; k0 += KS) {
+        const auto fe = Op::frag(et + 16 * tj * LT, LT, lane, k0);
+        aA[x] = Op::mma(Op::frag(gt + 16 * ti * LT, LT, lane, k0), fe, aA[x]);
+        aP[x] = Op::mma(Op::frag(dot + 16 * ti * LT, LT, lane, k0), fe, aP[x]);
+      }
     }
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
       const int tk = NK * w + x, ti = tk / (DK / 16), tc = tk % (DK / 16);
-      mm<16, 1, 1, 1>(aKd[x], gt + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq, be[16 * ti + col]);
-      mm<16, 1, 1, 1>(aQd[x], dot + (16 * ti + col) * LT + kq, st + (16 * tc + col) * LT + kq);
-      mm<16, 1, 1, 1>(aKb[x], et + (16 * ti + col) * LT + kq, dst + (16 * tc + col) * LT + kq);
+#pragma unroll
+      for (int k0 = 0; k0 < TW; k0 += KS) {
+        const auto fs = Op::frag(st + 16 * tc * LT, LT, lane, k0);
+        aKd[x] = Op::mma(Op::frag(gt + 16 * ti * LT, LT, lane, k0), fs, aKd[x]);
+        aQd[x] = Op::mma(Op::frag(dot + 16 * ti * LT, LT, lane, k0), fs, aQd[x]);
+        aKb[x] = Op::mma(Op::frag(et + 16 * ti * LT, LT, lane, k0), Op::frag(dst + 16 * tc * LT, LT, lane, k0),
+                         aKb[x]);
+      }
     }
     if (tid < 64) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dbv = fmaf(gt[tid * LT + j], rt[tid * LT + j], dbv);
-    }
-    if (tid < DK) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dgn = fmaf(dst[tid * LT + j], st[tid * LT + j], dgn);
+      for (int j = 0; j < TW; ++j) dbv = fmaf(Op::widen(gt[tid * LT + j]), Op::widen(rt[tid * LT + j]), dbv);
     }
   }
+  // dKd = -diag(beta) G S^T: the rows' beta, read before the tile memory is reused
+  float bkd[4];
+  {
+    const int ti = (NK * w) / (DK / 16);  // the same row block for every x of this wave
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bkd[r] = be[16 * ti + 4 * g4 + r];
+  }
+  // the four (bf16) or eight lanes of a state row hold its dS' o S partial sums
+#pragma unroll
+  for (int u = 0; u < NSV; ++u) {
+#pragma unroll
+    for (int sh = 1; sh < SPR; sh <<= 1) dgp[u] += __shfl_xor(dgp[u], sh, 64);
+  }
   __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NSV; ++u) {
+    const int x = tid + 512 * u;
+    if (x < DK * SPR && x % SPR == 0) sg[L::kDgn + x / SPR] = dgp[u];
+  }
 
   // ---- phase X: dKd = -F S^T, dQd = dOs S^T, dKb = E dS'^T to their owners ----
   // From here on wave w < DK / 16 owns channel c = 16 w + lane % 16 and rows
@@ -576,7 +658,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * ti + 4 * g4 + r, cc = 16 * tc + col;
-        sg[row * LK + cc] = -aKd[x][r];
+        sg[row * LK + cc] = -bkd[r] * aKd[x][r];
         sg[64 * LK + row * LK + cc] = aQd[x][r];
         sg[2 * 64 * LK + row * LK + cc] = aKb[x][r];
       }
@@ -830,7 +912,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   // dbeta (rows tid < 64): sum over d_v of G o R, plus the Ab term
   if (tid < nr) p.dbeta[(bos + r0 + tid) * H + h] = dbv + sg[L::kDbA + tid];
   if (tid < DK) {
-    float acc = __builtin_amdgcn_exp2f(gnl) * dgn + xs[tid];
+    float acc = __builtin_amdgcn_exp2f(gnl) * sg[L::kDgn + tid] + xs[tid];
     for (int s2 = 63; s2 >= 0; --s2) {
       acc += dgs[s2 * LK + tid];
       if (s2 < nr) p.dg[((bos + r0 + s2) * H + h) * DK + tid] = acc;
@@ -842,7 +924,8 @@ template <int DK, typename E>
 hipError_t launch_kda_bwd_t(const KdaBwdParams& p, hipStream_t s) {
   using EL = typename std::conditional_t<sizeof(E) == 2, OpBf16, OpF32>::elem;
   constexpr size_t ds_smem = DsLds<DK, EL>::kBytes;
-  constexpr size_t gr_smem = GradLds<DK>::kFloats * sizeof(float);
+  constexpr size_t gr_smem = grad_smem_bytes<DK, EL>();
+  static_assert(gr_smem <= 160 * 1024, "LDS budget exceeded");
   static_assert(ds_smem <= 160 * 1024, "LDS budget exceeded");
   auto ds = kda_dstate_kernel<DK, E>;
   auto gr = kda_grad_kernel<DK, E>;

@@ -78,6 +78,9 @@ CASES = [
              cu_seqlens=(0, 1, 65, 200), s0_std=0.1, scale=0.3, with_dO=True, seed=75),
     Workload("kdab_bf16_dk128_dv16_edges", 1, 130, 2, 128, 16, io="bf16", qk="iid", gate="gdn_channel",
              cu_seqlens=(0, 64, 65, 130), with_dO=True, seed=76),
+    # d_v = 48: one full 32-column tile of the bf16 gradient kernel and a half one
+    Workload("kdab_bf16_dk64_dv48", 2, 150, 2, 64, 48, io="bf16", qk="norm_both", gate="gdn_channel",
+             s0_std=0.1, with_dO=True, seed=80),
 ]
 
 
