@@ -43,6 +43,10 @@ def test_host_inputs_rejected(no_calls):
         ops.prologue(q, k, g, beta, A_log=torch.zeros(2), dt_bias=torch.zeros(2))
     with pytest.raises(ValueError):
         ops.epilogue(v, v.clone())
+    with pytest.raises(ValueError):
+        ops.kda_chunk_fwd(q, k, v, torch.zeros(q.shape), beta)
+    with pytest.raises(ValueError):
+        ops.kda_chunk_bwd(q, k, v, torch.zeros(q.shape), beta, v.clone())
 
 
 @pytest.mark.gpu
@@ -74,3 +78,12 @@ def test_host_tensor_in_any_slot_rejected(no_calls):
         ops.epilogue(v, v.clone(), weight=torch.ones(64))
     with pytest.raises(ValueError, match="z"):
         ops.epilogue(v, v.cpu())
+    gk = torch.zeros(q.shape, device=dev)
+    with pytest.raises(ValueError, match="g"):
+        ops.kda_chunk_bwd(q, k, v, gk.cpu(), beta, v.clone())
+    with pytest.raises(ValueError, match="dO"):
+        ops.kda_chunk_bwd(q, k, v, gk, beta, v.cpu())
+    with pytest.raises(ValueError, match="S0"):
+        ops.kda_chunk_bwd(q, k, v, gk, beta, v.clone(), S0=S0_host)
+    with pytest.raises(ValueError, match="dS_final"):
+        ops.kda_chunk_bwd(q, k, v, gk, beta, v.clone(), dS_final=S0_host)
