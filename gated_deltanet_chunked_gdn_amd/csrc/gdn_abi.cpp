@@ -140,14 +140,14 @@ size_t kda_rec_region(const gdn_problem* p, const Checked& c) {
   return (b + 255) / 256 * 256;
 }
 
-// The KDA backward's fp32 copies of T, Ab and P, and its fp32 per-chunk states
-// and state gradients.
+// The KDA backward's fp32 copies of T, Ab and P, and its per-chunk states and state
+// gradients in the operand type.
 size_t kda_aux_region(const gdn_problem* p, const Checked& c) {
   const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * gdn::kda::Aux::kFloats * 4;
   return (b + 255) / 256 * 256;
 }
 size_t kda_state_region(const gdn_problem* p, const Checked& c) {
-  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * 4;
+  const size_t b = static_cast<size_t>(gdn::chunk_slots(c.tokens, c.N)) * p->H * p->Dk * p->Dv * c.ce;
   return (b + 255) / 256 * 256;
 }
 
@@ -172,7 +172,7 @@ size_t workspace_bytes(const gdn_problem* p, Kind kind, const Checked& c) {
   if (kind == Kind::KdaBwd) {
     if (c.N == 0) return 0;
     // the forward's records, then T, Ab and P in fp32, then the state before and
-    // the state gradient after every chunk (fp32)
+    // the state gradient after every chunk (operand type)
     return kda_rec_region(p, c) + kda_aux_region(p, c) + 2 * kda_state_region(p, c);
   }
   if (kind == Kind::ChunkBwd) {
@@ -394,8 +394,8 @@ gdn_status gdn_kda_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
   char* const wsb = static_cast<char*>(workspace);
   const size_t rb = kda_rec_region(p, c), ab = kda_aux_region(p, c), sb = kda_state_region(p, c);
   float* const aux = reinterpret_cast<float*>(wsb + rb);
-  float* const states = reinterpret_cast<float*>(wsb + rb + ab);
-  float* const dstates = reinterpret_cast<float*>(wsb + rb + ab + sb);
+  char* const states = wsb + rb + ab;
+  char* const dstates = wsb + rb + ab + sb;
   gdn::KdaParams kp{};
   kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = nullptr; kp.S_final = nullptr;
   kp.ws = workspace;

@@ -217,9 +217,10 @@ struct KdaParams {
   float* seg_ws;            // G > 1: end states, start states, maps (segment_ws_bytes)
   // For the backward (nullptr otherwise): the prep kernel also writes T, Ab and P
   // in fp32 (kda::Aux floats per (chunk slot, head)); the state kernel writes the
-  // state before every chunk, fp32 [slot][H][Dk][Dv].
+  // state before every chunk, [slot][H][Dk][Dv] in the operand type (bf16 for bf16
+  // io, fp32 for fp32 io).
   float* aux;
-  float* states;
+  void* states;
 };
 // Per (chunk slot, head): T diag(beta) and P (64 x 64 each), K o Gamma, Q o Gamma
 // and (K o exp(gamma_n - gamma))^T (64 x Dk each) in the io element type (the
@@ -230,8 +231,8 @@ inline size_t kda_rec_bytes(int Dk, bool bf16) {
 hipError_t launch_kda_fwd(const KdaParams& p, int Dk, bool bf16, hipStream_t s);
 // Backward of the per-key-channel-decay pass on records, aux matrices and per-chunk
 // states already written (launch_kda_fwd with aux and states set): the reverse
-// state-gradient pass (dS after every chunk into dstates, fp32 [slot][H][Dk][Dv];
-// dS0) and the per-chunk gradient kernel.
+// state-gradient pass (dS after every chunk into dstates; dS0) and the per-chunk
+// gradient kernel.
 struct KdaBwdParams {
   const void* q;
   const void* k;
@@ -248,8 +249,8 @@ struct KdaBwdParams {
   float* dS0;             // [N, H, Dk, Dv] or nullptr
   const void* rec;        // the forward's records
   const float* aux;
-  const float* states;
-  float* dstates;
+  const void* states;     // [slot][H][Dk][Dv], operand type (as KdaParams::states)
+  void* dstates;          // dS after every chunk, [slot][H][Dk][Dv], operand type
   SeqInfo seq;
   int32_t N, H, Dv;
   int32_t max_chunks;

@@ -665,12 +665,12 @@ __global__ __launch_bounds__(512) void kda_state_kernel(KdaParams p) {
   for (int c = 0; c < nch; ++c) {
     const int64_t r0 = 64LL * (cb + c);
     const int nr = static_cast<int>(len - r0 < 64 ? len - r0 : 64);
-    if (p.states) {  // the state before the chunk, for the backward (one segment)
-      float* const sc = p.states + ((bos / 64 + n + cb + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
+    if (p.states) {  // the state before the chunk, for the backward (one segment; operand type)
+      EL* const sc = static_cast<EL*>(p.states) + ((bos / 64 + n + cb + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
 #pragma unroll
       for (int b = 0; b < RB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[(16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] = S[b][r];
+        for (int r = 0; r < 4; ++r) sc[(16 * (w + 4 * b) + 4 * g4 + r) * Dv + c0] = Op::cvt(S[b][r]);
     }
     __syncthreads();
     __syncthreads();  // the record and the v tile of chunk c are in LDS

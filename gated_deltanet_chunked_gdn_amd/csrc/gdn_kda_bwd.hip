@@ -230,13 +230,14 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
 #pragma unroll
       for (int e = 0; e < EPVIO; ++e) sm[L::kDoT + (dpart * EPVIO + e) * L::L64 + drow] = Op::cvt(p.scale * x[e]);
     }
-    // dS' (the gradient after chunk c): to the per-chunk buffer and, transposed, to LDS
-    float* const dsg = p.dstates + ((slot0 + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
+    // dS' (the gradient after chunk c): to the per-chunk buffer (operand type) and,
+    // transposed, to LDS
+    EL* const dsg = static_cast<EL*>(p.dstates) + ((slot0 + c) * p.H + h) * static_cast<int64_t>(DK) * Dv;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const int rb = w + 4 * b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dsg[(16 * rb + 4 * g4 + r) * Dv + c0] = dS[b][r];
+      for (int r = 0; r < 4; ++r) dsg[(16 * rb + 4 * g4 + r) * Dv + c0] = Op::cvt(dS[b][r]);
       store_ct<EL>(sm + L::kDsT + 16 * rb, L::LK, dS[b], lane);
     }
     __syncthreads();
@@ -367,7 +368,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   constexpr int NB = TW / 16;         // 16-column blocks of a tile
   constexpr int EPV = 16 / static_cast<int>(sizeof(E));    // io elements per vector
   constexpr int VPR = TW / EPV;                            // io vectors per tile row
-  constexpr int SPR = TW / 4;                              // fp32 state vectors per tile row
+  constexpr int EPS = 16 / static_cast<int>(sizeof(EL));   // state elements per vector
+  constexpr int SPR = TW / EPS;                            // state vectors per tile row
   constexpr int NSV = (DK * SPR + 511) / 512;              // state vectors per thread
   static_assert(VPR * 64 <= 512 && (NSV == 1 || NSV * 512 == DK * SPR), "tile loads");
   extern __shared__ __align__(16) float sg[];
@@ -383,8 +385,8 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   const int H = p.H, Dv = p.Dv;
   const int64_t slot = bos / 64 + n + c;
   const float* const aux = p.aux + (slot * H + h) * static_cast<int64_t>(kda::Aux::kFloats);
-  const float* const Sg = p.states + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
-  const float* const dSg = p.dstates + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+  const EL* const Sg = static_cast<const EL*>(p.states) + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
+  const EL* const dSg = static_cast<const EL*>(p.dstates) + (slot * H + h) * static_cast<int64_t>(DK) * Dv;
   const E* q = static_cast<const E*>(p.q);
   const E* k = static_cast<const E*>(p.k);
   const E* v = static_cast<const E*>(p.v);
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
   for (int u = 0; u < NSV; ++u) dgp[u] = 0.f;
 
-  // tile prefetch: S and dS' rows (four fp32 per vector), V and dO rows (io
+  // tile prefetch: S and dS' rows (operand-type vectors), V and dO rows (io
   // vectors, bounded to the chunk's rows: past them the loads read zeros)
   const bool iol = tid < 64 * VPR;
   const int iorow = iol ? tid / VPR : 0, iopart = tid % VPR;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int u = 0; u < NSV; ++u) {
       const int x = tid + 512 * u, row = x < DK * SPR ? x / SPR : 0, part = x % SPR;
-      const int cv = v0 + 4 * part < Dv ? v0 + 4 * part : v0;
+      const int cv = v0 + EPS * part < Dv ? v0 + EPS * part : v0;
       ps[u] = *reinterpret_cast<const f32x4_t*>(Sg + row * Dv + cv);
       pds[u] = *reinterpret_cast<const f32x4_t*>(dSg + row * Dv + cv);
     }
@@ -522,12 +524,22 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
       const int x = tid + 512 * u, row = x / SPR, part = x % SPR;
       if (x >= DK * SPR) continue;
       const f32x4_t z = zero4();
-      const bool okc = v0 + 4 * part < Dv;
+      const bool okc = v0 + EPS * part < Dv;
       const f32x4_t a = okc ? ps[u] : z, b = okc ? pds[u] : z;
-      chunk::store4<EL>(st + row * LT + 4 * part, a[0], a[1], a[2], a[3]);
-      chunk::store4<EL>(dst + row * LT + 4 * part, b[0], b[1], b[2], b[3]);
+      *reinterpret_cast<f32x4_t*>(st + row * LT + EPS * part) = a;   // EPS operand values, as stored
+      *reinterpret_cast<f32x4_t*>(dst + row * LT + EPS * part) = b;
+      if constexpr (sizeof(EL) == 2) {
+        const uint32_t* ua = reinterpret_cast<const uint32_t*>(&a);
+        const uint32_t* ub = reinterpret_cast<const uint32_t*>(&b);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dgp[u] = fmaf(a[e], b[e], dgp[u]);
+        for (int e = 0; e < 4; ++e) {
+          dgp[u] = fmaf(__uint_as_float(ua[e] << 16), __uint_as_float(ub[e] << 16), dgp[u]);
+          dgp[u] = fmaf(__uint_as_float(ua[e] & 0xffff0000u), __uint_as_float(ub[e] & 0xffff0000u), dgp[u]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dgp[u] = fmaf(a[e], b[e], dgp[u]);
+      }
     }
     if (iol) {
       const bool okc = v0 + iopart * EPV < Dv;
@@ -630,7 +642,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) bkd[r] = be[16 * ti + 4 * g4 + r];
   }
-  // the four (bf16) or eight lanes of a state row hold its dS' o S partial sums
+  // the SPR lanes of a state row hold its dS' o S partial sums
 #pragma unroll
   for (int u = 0; u < NSV; ++u) {
 #pragma unroll

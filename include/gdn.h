@@ -297,13 +297,15 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* problem, const void* q, const vo
  * chunk, and one workgroup per chunk forms its gradients.  Packed sequences as
  * for gdn_kda_chunk_fwd; Dk 64 or 128, Dv a multiple of 16 up to 256, both io
  * dtypes; num_segments must be 1 and precision GDN_PRECISION_IO.
- * Precision: the forward part as gdn_kda_chunk_fwd; the reverse pass reads its
- * chunk records (io element type) into fp32 products; the gradient kernel works
- * in fp32 throughout (fp32 MFMA) from the inputs, fp32 copies of T, the key
- * products and P, and the fp32 per-chunk states.
+ * Precision: decays, the inverse, the state and its gradient are fp32; the
+ * products take bf16 operands with fp32 accumulation for bf16 io (the records,
+ * the per-chunk states and state gradients, and the intermediate tiles rounded to
+ * bf16) and are IEEE fp32 for fp32 io; the pair sums through the per-channel
+ * decays are fp32 for both.
  * Workspace: gdn_workspace_size(..., GDN_PASS_KDA_BWD, ...): the forward's records,
- * then per chunk and head 12288 floats (T, Ab, P) and the state before and its
- * gradient after the chunk, Dk Dv floats each.  Errors as gdn_kda_chunk_fwd. */
+ * then per chunk and head 12288 floats (T, Ab, P in fp32) and the state before and
+ * its gradient after the chunk, Dk Dv values each in the io element type.  Errors
+ * as gdn_kda_chunk_fwd. */
 gdn_status gdn_kda_chunk_bwd(const gdn_problem* problem, const void* q, const void* k,
                              const void* v, const float* g, const float* beta, const float* S0,
                              const void* dO, const float* dS_final, void* dq, void* dk, void* dv,

@@ -339,13 +339,14 @@ def test_kda_workspace_and_checks():
 
 def test_kda_bwd_workspace_and_checks():
     # the forward's records, then per (chunk slot, head) T, Ab and P in fp32 (3 x 64 x 64
-    # floats), then the state before and the state gradient after every chunk (Dk Dv fp32 each)
+    # floats), then the state before and the state gradient after every chunk (Dk Dv values
+    # each, in the io element type)
     slots = 200 // 64 + 2 + 1
     for Dk in (64, 128):
         for io, size in ((nat.GDN_BF16, 2), (nat.GDN_FP32, 4)):
             rec = (8192 + 3 * 64 * Dk) * size + 4 * Dk
             aux = 3 * 4096 * 4
-            st = Dk * 128 * 4
+            st = Dk * 128 * size
             want = slots * 3 * (rec + aux + 2 * st)
             assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_BWD) == (nat.GDN_OK, want)
     assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
