@@ -245,7 +245,23 @@ def extra_measurements(gdn, generate, WORKLOADS, dev, steps, warmup, which=EXTRA
                           "tokens_per_s": w.B * w.T / float(kt.mean()), "alg_bytes_per_launch": nb,
                           "alg_GBps": nb / float(kt.mean()) / 1e9,
                           "kernels": "kda_prep_kernel + kda_state_kernel (states) + kda_dstate_kernel + kda_grad_kernel"}
-        del t
+        # a training step recomputing the forward's records and states in the
+        # backward, against one that keeps them (gdn_kda_chunk_fwd_save /
+        # gdn_kda_chunk_bwd_saved)
+        f_ms = float(event_times(lambda i: gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                             scale=w.scale), steps, warmup, stream).mean()) * 1e3
+        saved = gdn.kda_saved_buffer(t["q"], t["v"])
+        s_ms = float(event_times(lambda i: gdn.kda_chunk_fwd_save(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                                  scale=w.scale, saved=saved),
+                                 steps, warmup, stream).mean()) * 1e3
+        b_ms = float(event_times(lambda i: gdn.kda_chunk_bwd_saved(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"],
+                                                                   saved, scale=w.scale, want_dS0=False),
+                                 steps, warmup, stream).mean()) * 1e3
+        out["kda_bwd"]["recompute"] = {"fwd_ms": f_ms, "bwd_ms": out["kda_bwd"]["ms_mean"],
+                                       "step_ms": f_ms + out["kda_bwd"]["ms_mean"]}
+        out["kda_bwd"]["retain"] = {"fwd_save_ms": s_ms, "bwd_saved_ms": b_ms, "step_ms": s_ms + b_ms,
+                                    "saved_bytes": saved.numel()}
+        del t, saved
     if "policy" in which:
         # latency, workspace and peak device memory of one forward call per precision
         # policy on the same bf16 inputs (the metric shape, B=4 T=4096 H=8 d=128):

@@ -45,12 +45,13 @@ GDN_PASS_RECURRENT_BWD = 3
 GDN_PASS_KDA_FWD = 4
 GDN_PASS_CHUNK_SAVED = 5
 GDN_PASS_KDA_BWD = 6
+GDN_PASS_KDA_SAVED = 7
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_abi_version", "gdn_status_str", "gdn_workspace_size", "gdn_chunk_fwd",
             "gdn_chunk_bwd", "gdn_recurrent_ref", "gdn_prologue", "gdn_epilogue",
             "gdn_kda_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_device_copy", "gdn_chunk_fwd_save",
-            "gdn_chunk_bwd_saved", "gdn_kda_chunk_bwd")
+            "gdn_chunk_bwd_saved", "gdn_kda_chunk_bwd", "gdn_kda_chunk_fwd_save", "gdn_kda_chunk_bwd_saved")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -122,6 +123,10 @@ def load():
     lib.gdn_device_copy.restype = ctypes.c_int
     lib.gdn_kda_chunk_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.gdn_kda_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_kda_chunk_fwd_save.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_kda_chunk_fwd_save.restype = ctypes.c_int
+    lib.gdn_kda_chunk_bwd_saved.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_kda_chunk_bwd_saved.restype = ctypes.c_int
     _lib = lib
     return lib
 

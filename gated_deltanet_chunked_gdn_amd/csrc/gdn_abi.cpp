@@ -301,6 +301,7 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int32_t pass, size_t* bytes)
     case GDN_PASS_KDA_FWD: kind = Kind::KdaFwd; break;
     case GDN_PASS_CHUNK_SAVED: kind = Kind::ChunkBwd; break;
     case GDN_PASS_KDA_BWD: kind = Kind::KdaBwd; break;
+    case GDN_PASS_KDA_SAVED: kind = Kind::KdaBwd; break;
     default: return GDN_ERR_UNSUPPORTED;
   }
   Checked c;
@@ -371,6 +372,54 @@ gdn_status gdn_kda_chunk_fwd(const gdn_problem* p, const void* q, const void* k,
   return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, static_cast<hipStream_t>(stream)));
 }
 
+// The per-channel-decay backward's buffer: the forward's records, fp32 T, Ab and P,
+// and the state before and its gradient after every chunk (operand type).
+struct KdaBwdLayout {
+  void* rec;
+  float* aux;
+  char* states;
+  char* dstates;
+};
+KdaBwdLayout kda_bwd_layout(const gdn_problem* p, const Checked& c, void* ws) {
+  char* const b = static_cast<char*>(ws);
+  const size_t rb = kda_rec_region(p, c), ab = kda_aux_region(p, c), sb = kda_state_region(p, c);
+  return KdaBwdLayout{ws, reinterpret_cast<float*>(b + rb), b + rb + ab, b + rb + ab + sb};
+}
+
+// The forward part of the per-channel-decay backward: records, fp32 T, Ab and P, the
+// state before every chunk; o and S_final too when given.
+gdn_status kda_fwd_keep(const gdn_problem* p, const Checked& c, const KdaBwdLayout& l, const void* q,
+                        const void* k, const void* v, const float* g, const float* beta, const float* S0,
+                        void* o, float* S_final, hipStream_t s) {
+  gdn::KdaParams kp{};
+  kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = o; kp.S_final = S_final;
+  kp.ws = l.rec;
+  kp.seq = seq_info(p);
+  kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
+  kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  kp.scale = p->scale;
+  kp.G = 1;
+  kp.aux = l.aux;
+  kp.states = l.states;
+  return hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, s));
+}
+
+// The reverse passes of the per-channel-decay backward on a filled buffer.
+gdn_status kda_bwd_from(const gdn_problem* p, const Checked& c, const KdaBwdLayout& l, const void* q,
+                        const void* k, const void* v, const float* g, const float* beta, const void* dO,
+                        const float* dS_final, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dS0,
+                        hipStream_t s) {
+  gdn::KdaBwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
+  bp.rec = l.rec; bp.aux = l.aux; bp.states = l.states; bp.dstates = l.dstates;
+  bp.seq = seq_info(p);
+  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv;
+  bp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
+  bp.scale = p->scale;
+  return hip_status(gdn::launch_kda_bwd(bp, p->Dk, c.bf16, s));
+}
+
 gdn_status gdn_kda_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const float* S0, const void* dO,
                              const float* dS_final, void* dq, void* dk, void* dv, float* dg,
@@ -391,32 +440,53 @@ gdn_status gdn_kda_chunk_bwd(const gdn_problem* p, const void* q, const void* k,
   if (need && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
   if (c.N == 0) return GDN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* const wsb = static_cast<char*>(workspace);
-  const size_t rb = kda_rec_region(p, c), ab = kda_aux_region(p, c), sb = kda_state_region(p, c);
-  float* const aux = reinterpret_cast<float*>(wsb + rb);
-  char* const states = wsb + rb + ab;
-  char* const dstates = wsb + rb + ab + sb;
-  gdn::KdaParams kp{};
-  kp.q = q; kp.k = k; kp.v = v; kp.g = g; kp.beta = beta; kp.S0 = S0; kp.o = nullptr; kp.S_final = nullptr;
-  kp.ws = workspace;
-  kp.seq = seq_info(p);
-  kp.N = c.N; kp.H = p->H; kp.Dv = p->Dv;
-  kp.max_chunks = static_cast<int32_t>((c.max_len + 63) / 64);
-  kp.scale = p->scale;
-  kp.G = 1;
-  kp.aux = aux;
-  kp.states = states;
-  st = hip_status(gdn::launch_kda_fwd(kp, p->Dk, c.bf16, s));
+  const KdaBwdLayout l = kda_bwd_layout(p, c, workspace);
+  st = kda_fwd_keep(p, c, l, q, k, v, g, beta, S0, nullptr, nullptr, s);
   if (st != GDN_OK) return st;
-  gdn::KdaBwdParams bp{};
-  bp.q = q; bp.k = k; bp.v = v; bp.g = g; bp.beta = beta; bp.dO = dO; bp.dS_final = dS_final;
-  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
-  bp.rec = workspace; bp.aux = aux; bp.states = states; bp.dstates = dstates;
-  bp.seq = seq_info(p);
-  bp.N = c.N; bp.H = p->H; bp.Dv = p->Dv;
-  bp.max_chunks = kp.max_chunks;
-  bp.scale = p->scale;
-  return hip_status(gdn::launch_kda_bwd(bp, p->Dk, c.bf16, s));
+  return kda_bwd_from(p, c, l, q, k, v, g, beta, dO, dS_final, dq, dk, dv, dg, dbeta, dS0, s);
+}
+
+gdn_status gdn_kda_chunk_fwd_save(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, const float* S0, void* o,
+                                  float* S_final, void* saved, size_t saved_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::KdaBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, nk * 4, 4, true}, {beta, ng * 4, 4, true}, {S0, ns * 4, 4, false}},
+                     {{o, nv * c.io, 16, true}, {S_final, ns * 4, 4, false},
+                      {saved, saved_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::KdaBwd, c);
+  if (need && (!saved || saved_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  return kda_fwd_keep(p, c, kda_bwd_layout(p, c, saved), q, k, v, g, beta, S0, o, S_final,
+                      static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_kda_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const void* dO, const float* dS_final,
+                                   void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dS0,
+                                   void* saved, size_t saved_bytes, void* stream) {
+  Checked c;
+  gdn_status st = check_problem(p, Kind::KdaBwd, &c);
+  if (st != GDN_OK) return st;
+  const size_t nk = c.tokens * p->H * p->Dk, nv = c.tokens * p->H * p->Dv, ng = c.tokens * p->H;
+  const size_t ns = static_cast<size_t>(c.N) * p->H * p->Dk * p->Dv;
+  st = check_tensors({{q, nk * c.io, 16, true}, {k, nk * c.io, 16, true}, {v, nv * c.io, 16, true},
+                      {g, nk * 4, 4, true}, {beta, ng * 4, 4, true},
+                      {dO, nv * c.io, 16, true}, {dS_final, ns * 4, 4, false}},
+                     {{dq, nk * c.io, 16, true}, {dk, nk * c.io, 16, true}, {dv, nv * c.io, 16, true},
+                      {dg, nk * 4, 4, true}, {dbeta, ng * 4, 4, true}, {dS0, ns * 4, 4, false},
+                      {saved, saved_bytes, 16, false}});
+  if (st != GDN_OK) return st;
+  const size_t need = workspace_bytes(p, Kind::KdaBwd, c);
+  if (need && (!saved || saved_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (c.N == 0) return GDN_OK;
+  return kda_bwd_from(p, c, kda_bwd_layout(p, c, saved), q, k, v, g, beta, dO, dS_final, dq, dk, dv, dg, dbeta,
+                      dS0, static_cast<hipStream_t>(stream));
 }
 
 // The reverse passes of the backward on a filled buffer.

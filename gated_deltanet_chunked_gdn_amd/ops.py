@@ -11,6 +11,7 @@ built library every call raises ``GdnLibraryMissing``.
     y          = epilogue(o, z, weight=None, eps=1e-6)
     o, S_final = kda_chunk_fwd(q, k, v, g, beta, ...)   # g (B, T, H, Dk): per-channel decay
     grads      = kda_chunk_bwd(q, k, v, g, beta, dO, ...)
+    o, S_final, saved = kda_chunk_fwd_save(...); grads = kda_chunk_bwd_saved(..., saved)
 
 Shapes: q, k (B, T, H, Dk); v (B, T, H, Dv); g, beta (B, T, H) fp32;
 S0 / S_final (N, H, Dk, Dv) fp32.  q, k, v share the io dtype (bf16 or fp32).
@@ -259,12 +260,7 @@ def kda_chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,
     """Backward of kda_chunk_fwd (g fp32, shaped like q).  Returns dict dq, dk,
     dv, dg (shaped like g), dbeta, dS0."""
     lib = nat.load()
-    _check_inputs(q, k, v, beta, beta)
-    if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
-        raise ValueError("g must be a float32 tensor shaped like q (one log-decay per key channel)")
-    _on_device(g, q.device, "g")
-    if not g.is_contiguous():
-        raise ValueError("g must be a contiguous GPU tensor")
+    _kda_check(q, k, v, g, beta)
     _on_device(dO, q.device, "dO")
     if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
         raise ValueError("dO must be contiguous, shaped and typed like v")
@@ -284,6 +280,80 @@ def kda_chunk_bwd(q, k, v, g, beta, dO, S0=None, dS_final=None, cu_seqlens=None,
                                _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
                                _ptr(ws), nws, _stream(q.device))
     nat.check(st, "gdn_kda_chunk_bwd")
+    return out
+
+
+def _kda_check(q, k, v, g, beta):
+    _check_inputs(q, k, v, beta, beta)
+    if not isinstance(g, torch.Tensor) or g.dtype != torch.float32 or g.shape != q.shape:
+        raise ValueError("g must be a float32 tensor shaped like q (one log-decay per key channel)")
+    _on_device(g, q.device, "g")
+    if not g.is_contiguous():
+        raise ValueError("g must be a contiguous GPU tensor")
+
+
+def kda_saved_buffer(q, v, cu_seqlens=None):
+    """A uint8 device tensor of the size kda_chunk_fwd_save / kda_chunk_bwd_saved
+    need (gdn_workspace_size with GDN_PASS_KDA_SAVED; None if 0 bytes)."""
+    seqs = _seqlens(cu_seqlens, q.device)
+    return _workspace(make_problem(q, v, seqs, 1.0, 1), nat.GDN_PASS_KDA_SAVED, q.device)[0]
+
+
+def _kda_saved_arg(saved, q, v, seqs, device):
+    if saved is None:
+        return _workspace(make_problem(q, v, seqs, 1.0, 1), nat.GDN_PASS_KDA_SAVED, device)
+    _on_device(saved, device, "saved")
+    if not saved.is_contiguous():
+        raise ValueError("saved must be contiguous")
+    return saved, saved.numel() * saved.element_size()
+
+
+def kda_chunk_fwd_save(q, k, v, g, beta, S0=None, cu_seqlens=None, scale: float = 1.0, saved=None):
+    """gdn_kda_chunk_fwd_save: the per-channel-decay forward that also keeps what
+    the backward needs.  Returns (o, S_final, saved); pass ``saved`` to
+    kda_chunk_bwd_saved with the same inputs."""
+    lib = nat.load()
+    _kda_check(q, k, v, g, beta)
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    S0 = _fp32_state(S0, N, H, Dk, Dv, "S0", q.device)
+    o = torch.empty_like(v)
+    Sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    sv, nsv = _kda_saved_arg(saved, q, v, seqs, q.device)
+    st = lib.gdn_kda_chunk_fwd_save(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(S0), _ptr(o), _ptr(Sf), _ptr(sv), nsv, _stream(q.device))
+    nat.check(st, "gdn_kda_chunk_fwd_save")
+    return o, Sf, sv
+
+
+def kda_chunk_bwd_saved(q, k, v, g, beta, dO, saved, dS_final=None, cu_seqlens=None,
+                        scale: float = 1.0, want_dS0: bool = True):
+    """gdn_kda_chunk_bwd_saved: the per-channel-decay backward from a buffer
+    filled by kda_chunk_fwd_save with the same q, k, v, g, beta, S0 and
+    cu_seqlens.  Returns dict dq, dk, dv, dg, dbeta, dS0."""
+    lib = nat.load()
+    _kda_check(q, k, v, g, beta)
+    _on_device(dO, q.device, "dO")
+    if dO.dtype != v.dtype or dO.shape != v.shape or not dO.is_contiguous():
+        raise ValueError("dO must be contiguous, shaped and typed like v")
+    if saved is None:
+        raise ValueError("saved must be the buffer kda_chunk_fwd_save filled")
+    seqs = _seqlens(cu_seqlens, q.device)
+    prob = make_problem(q, v, seqs, scale, 1)
+    N, H, Dk, Dv = prob.num_seqs, prob.H, prob.Dk, prob.Dv
+    dS_final = _fp32_state(dS_final, N, H, Dk, Dv, "dS_final", q.device)
+    sv, nsv = _kda_saved_arg(saved, q, v, seqs, q.device)
+    out = {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+        "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+        "dS0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_dS0 else None,
+    }
+    st = lib.gdn_kda_chunk_bwd_saved(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                                     _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                                     _ptr(sv), nsv, _stream(q.device))
+    nat.check(st, "gdn_kda_chunk_bwd_saved")
     return out
 
 

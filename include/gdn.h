@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -116,7 +116,8 @@ typedef enum gdn_pass {
   GDN_PASS_RECURRENT_BWD = 3,
   GDN_PASS_KDA_FWD = 4,
   GDN_PASS_CHUNK_SAVED = 5, /* the buffer of gdn_chunk_fwd_save / gdn_chunk_bwd_saved */
-  GDN_PASS_KDA_BWD = 6
+  GDN_PASS_KDA_BWD = 6,
+  GDN_PASS_KDA_SAVED = 7    /* the buffer of gdn_kda_chunk_fwd_save / gdn_kda_chunk_bwd_saved */
 } gdn_pass;
 
 typedef struct gdn_problem {
@@ -311,6 +312,31 @@ gdn_status gdn_kda_chunk_bwd(const gdn_problem* problem, const void* q, const vo
                              const void* dO, const float* dS_final, void* dq, void* dk, void* dv,
                              float* dg, float* dbeta, float* dS0, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Training with retained states for the per-channel decay, as gdn_chunk_fwd_save /
+ * gdn_chunk_bwd_saved for the scalar gate (the fla issue #1550 page, "Proposed
+ * scope": retained or recomputed states).  gdn_kda_chunk_fwd_save computes exactly
+ * what gdn_kda_chunk_fwd computes with num_segments = 1 (o, S_final; bit-identical)
+ * and also fills `saved` with the chunk records, fp32 T, Ab and P, and the state
+ * before every chunk; gdn_kda_chunk_bwd_saved then runs only the reverse passes of
+ * gdn_kda_chunk_bwd and gives bit-identical gradients, provided q, k, v, g, beta, S0
+ * and the problem are those of the save call and `saved` was not modified in
+ * between (neither is checked: other contents give undefined gradients, not an
+ * error).  It writes the state gradients into `saved` as well.
+ *   saved: caller-allocated device buffer of gdn_workspace_size(problem,
+ *          GDN_PASS_KDA_SAVED) bytes (the gdn_kda_chunk_bwd workspace), 16-byte
+ *          aligned.
+ *   Supported and errors: as gdn_kda_chunk_bwd.  S0 is not an argument of
+ *   gdn_kda_chunk_bwd_saved (the saved states carry it); dS0 is still produced. */
+gdn_status gdn_kda_chunk_fwd_save(const gdn_problem* problem, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta, const float* S0,
+                                  void* o, float* S_final, void* saved, size_t saved_bytes,
+                                  void* stream);
+gdn_status gdn_kda_chunk_bwd_saved(const gdn_problem* problem, const void* q, const void* k,
+                                   const void* v, const float* g, const float* beta, const void* dO,
+                                   const float* dS_final, void* dq, void* dk, void* dv, float* dg,
+                                   float* dbeta, float* dS0, void* saved, size_t saved_bytes,
+                                   void* stream);
 
 /* Gate forms of gdn_prologue. */
 typedef enum {

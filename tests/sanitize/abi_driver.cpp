@@ -143,6 +143,15 @@ int main() {
   EXPECT(gdn_kda_chunk_bwd(&pb, fake(0), fake(1), fake(2), ffake(3), ffake(4), nullptr, fake(5), nullptr, fake(6),
                            fake(7), fake(8), ffake(9), ffake(10), nullptr, fake(11), kw - 16, nullptr) ==
          GDN_ERR_WORKSPACE);
+  size_t ks = 0;
+  EXPECT(gdn_workspace_size(&pb, GDN_PASS_KDA_SAVED, &ks) == GDN_OK && ks == kw);
+  EXPECT(gdn_kda_chunk_fwd_save(&pb, fake(0), fake(1), fake(2), ffake(3), ffake(4), nullptr, fake(5), ffake(6),
+                                fake(7), ks, nullptr) == GDN_ERR_HIP);
+  EXPECT(gdn_kda_chunk_bwd_saved(&pb, fake(0), fake(1), fake(2), ffake(3), ffake(4), fake(5), nullptr, fake(6),
+                                 fake(7), fake(8), ffake(9), ffake(10), ffake(12), fake(11), ks, nullptr) == GDN_ERR_HIP);
+  EXPECT(gdn_kda_chunk_bwd_saved(&pb, fake(0), fake(1), fake(2), ffake(3), ffake(4), fake(5), nullptr, fake(6),
+                                 fake(7), fake(8), ffake(9), ffake(10), ffake(12), fake(2), ks, nullptr) ==
+         GDN_ERR_ALIAS);
   gdn_problem pk2 = problem(2, 300, 3, 64, 128, GDN_BF16, 2);
   EXPECT(gdn_kda_chunk_bwd(&pk2, fake(0), fake(1), fake(2), ffake(3), ffake(4), nullptr, fake(5), nullptr, fake(6),
                            fake(7), fake(8), ffake(9), ffake(10), nullptr, fake(11), kw, nullptr) ==

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     for s in range(11):
         assert lib.gdn_status_str(s).decode() not in ("", "unknown status")
     assert lib.gdn_status_str(99).decode() == "unknown status"
@@ -349,6 +349,8 @@ def test_kda_bwd_workspace_and_checks():
             st = Dk * 128 * size
             want = slots * 3 * (rec + aux + 2 * st)
             assert ws(problem(Dk=Dk, io_dtype=io), nat.GDN_PASS_KDA_BWD) == (nat.GDN_OK, want)
+    # the retained-state pair uses the same buffer
+    assert ws(problem(), nat.GDN_PASS_KDA_SAVED) == ws(problem(), nat.GDN_PASS_KDA_BWD)
     assert ws(problem(num_segments=2), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(Dk=96), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(Dv=24), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
@@ -372,6 +374,23 @@ def test_kda_bwd_workspace_and_checks():
     assert call(problem(num_segments=2)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(precision=nat.GDN_PRECISION_FP32)) == nat.GDN_ERR_UNSUPPORTED
     assert call(problem(B=0, T=0, num_seqs=0)) == nat.GDN_OK   # nothing to do, nothing launched
+    # the retained-state pair: the same checks; a short buffer is refused
+    n = ws(problem(), nat.GDN_PASS_KDA_SAVED)[1]
+    assert lib.gdn_kda_chunk_fwd_save(ctypes.byref(problem()), P(FAKE), P(FAKE + GB), P(FAKE + 2 * GB),
+                                      P(FAKE + 3 * GB), P(FAKE + 4 * GB), None, P(FAKE + 8 * GB), None,
+                                      P(FAKE + 13 * GB), n - 16, None) == nat.GDN_ERR_WORKSPACE
+    assert lib.gdn_kda_chunk_fwd_save(ctypes.byref(problem(num_segments=4)), P(FAKE), P(FAKE + GB),
+                                      P(FAKE + 2 * GB), P(FAKE + 3 * GB), P(FAKE + 4 * GB), None,
+                                      P(FAKE + 8 * GB), None, P(FAKE + 13 * GB), n, None) == nat.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_kda_chunk_bwd_saved(ctypes.byref(problem()), P(FAKE), P(FAKE + GB), P(FAKE + 2 * GB),
+                                       P(FAKE + 3 * GB), P(FAKE + 4 * GB), P(FAKE + 5 * GB), None,
+                                       P(FAKE + 8 * GB), P(FAKE + 9 * GB), P(FAKE + 10 * GB), P(FAKE + 11 * GB),
+                                       P(FAKE + 12 * GB), None, P(FAKE + 13 * GB), n - 16, None) == nat.GDN_ERR_WORKSPACE
+    # the saved buffer may not overlap an output
+    assert lib.gdn_kda_chunk_bwd_saved(ctypes.byref(problem()), P(FAKE), P(FAKE + GB), P(FAKE + 2 * GB),
+                                       P(FAKE + 3 * GB), P(FAKE + 4 * GB), P(FAKE + 5 * GB), None,
+                                       P(FAKE + 8 * GB), P(FAKE + 9 * GB), P(FAKE + 10 * GB), P(FAKE + 11 * GB),
+                                       P(FAKE + 12 * GB), None, P(FAKE + 8 * GB + 4096), n, None) == nat.GDN_ERR_ALIAS
 
 
 def test_noalloc_entry_checks_before_any_launch():

@@ -149,3 +149,26 @@ def test_kda_bwd_full_length_equal_decays_is_the_scalar_gate_backward():
         e = rel_rms(x, y)
         print(f"equal decays, full length {name}: rel_rms against gdn_chunk_bwd {e:.2e}", flush=True)
         assert e <= 2 * BF16_TOL, name
+
+
+@pytest.mark.parametrize("w", [CASES[2], CASES[3]], ids=lambda w: w.name)
+def test_kda_retained_states_bit_identical(w):
+    # gdn_kda_chunk_fwd_save gives gdn_kda_chunk_fwd's outputs bit for bit, and
+    # gdn_kda_chunk_bwd_saved (twice on one buffer) gdn_kda_chunk_bwd's gradients
+    d = generate(w)
+    t = to_device(d)
+    cu = d["cu_seqlens"]
+    dsf = torch.from_numpy(_dsf(d, 9)).cuda()
+    o_ref, sf_ref = gdn.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t.get("S0"), cu_seqlens=cu,
+                                      scale=d["scale"])
+    g_ref = gdn.kda_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], S0=t.get("S0"), dS_final=dsf,
+                              cu_seqlens=cu, scale=d["scale"])
+    o, sf, saved = gdn.kda_chunk_fwd_save(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=t.get("S0"), cu_seqlens=cu,
+                                          scale=d["scale"])
+    for rep in range(2):
+        got = gdn.kda_chunk_bwd_saved(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dO"], saved, dS_final=dsf,
+                                      cu_seqlens=cu, scale=d["scale"])
+        torch.cuda.synchronize()
+        for name in GRADS:
+            assert torch.equal(got[name], g_ref[name]), (rep, name)
+    assert torch.equal(o, o_ref) and torch.equal(sf, sf_ref)
