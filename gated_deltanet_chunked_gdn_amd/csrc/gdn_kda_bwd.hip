@@ -311,7 +311,8 @@ struct GradVLds {
   static constexpr int kE = kR + 64 * LT * ES;          // [64][LT] E
   static constexpr int kDe = kE + 64 * LT * ES;         // [64][LT] dE
   static constexpr int kG = kDe + 64 * LT * ES;         // [64][LT] G = T^T dE
-  static constexpr int kBe = kG + 64 * LT * ES;         // [64] beta (fp32)
+  static constexpr int kDv = kG + 64 * LT * ES;         // [64][LT] dv = diag(beta) G (io type = EL)
+  static constexpr int kBe = kDv + 64 * LT * ES;        // [64] beta (fp32)
   static constexpr int kKd = kBe + 64 * 4;              // [64][LKE] K o Gamma
   static constexpr int kKb = kKd + 64 * LKE * ES;       // [64][LKE] K o exp(gamma_n - gamma)
   static constexpr int kT = kKb + 64 * LKE * ES;        // [64][L64E] T
@@ -372,6 +373,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   constexpr int SPR = TW / EPS;                            // state vectors per tile row
   constexpr int NSV = (DK * SPR + 511) / 512;              // state vectors per thread
   static_assert(VPR * 64 <= 512 && (NSV == 1 || NSV * 512 == DK * SPR), "tile loads");
+  static_assert(sizeof(E) == sizeof(EL), "dv is staged in the operand type, which is the io type");
   extern __shared__ __align__(16) float sg[];
   char* const sv = reinterpret_cast<char*>(sg);
   const int c = blockIdx.x, h = blockIdx.y, n = blockIdx.z, tid = threadIdx.x;
@@ -402,6 +404,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
   EL* const et = reinterpret_cast<EL*>(sv + V::kE);
   EL* const det = reinterpret_cast<EL*>(sv + V::kDe);
   EL* const gt = reinterpret_cast<EL*>(sv + V::kG);
+  EL* const dvt = reinterpret_cast<EL*>(sv + V::kDv);
   float* const be = reinterpret_cast<float*>(sv + V::kBe);
   EL* const kd = reinterpret_cast<EL*>(sv + V::kKd);
   EL* const kb = reinterpret_cast<EL*>(sv + V::kKb);
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) et[(16 * w + 4 * g4 + r) * LT + 16 * nb + col] = Op::cvt(acc[r]);
       }
-    } else {  // G = T^T dE; dv = diag(beta) G
+    } else {  // G = T^T dE; dv = diag(beta) G (to LDS, stored below)
       const int w4 = w - 4;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -600,13 +603,18 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * w4 + 4 * g4 + r;
           gt[row * LT + 16 * nb + col] = Op::cvt(acc[r]);
-          if (row < nr && v0 + 16 * nb < Dv)
-            IoT<E>::st(static_cast<E*>(p.dv) + ((bos + r0 + row) * H + h) * Dv + v0 + 16 * nb + col,
-                       be[row] * acc[r]);
+          dvt[row * LT + 16 * nb + col] = Op::cvt(be[row] * acc[r]);
         }
       }
     }
     __syncthreads();
+    // dv rows out of LDS as 16-byte vectors (rows and columns past the chunk and d_v stay)
+    if (tid < 64 * VPR) {
+      const int row = tid / VPR, part = tid % VPR;
+      if (row < nr && v0 + part * EPV < Dv)
+        *reinterpret_cast<uint4*>(static_cast<E*>(p.dv) + ((bos + r0 + row) * H + h) * Dv + v0 + part * EPV) =
+            *reinterpret_cast<const uint4*>(dvt + row * LT + part * EPV);
+    }
     // accumulations over this tile's TW columns
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
