@@ -61,7 +61,6 @@ gdn_status check_problem(const gdn_problem* p, Kind kind, Checked* c) {
     const int G = p->num_segments;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERR_UNSUPPORTED;
     if (kind == Kind::ChunkBwd && G != 1) return GDN_ERR_UNSUPPORTED;
-    if (kind == Kind::ChunkBwd && p->io_dtype == GDN_FP32 && p->Dk != 64) return GDN_ERR_UNSUPPORTED;
     // one chunk of one head's rows is addressed with 32-bit byte offsets
     if (static_cast<int64_t>(64) * p->H * std::max(p->Dk, p->Dv) * 4 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   }

@@ -911,6 +911,7 @@ hipError_t launch_chunk_bwd(const BwdParams& b, int Dk, bool bf16, hipStream_t s
     if (Dk == 128) return launch_bwd_t<128, OpBf16>(b, s);
   } else {
     if (Dk == 64) return launch_bwd_t<64, OpF32>(b, s);
+    if (Dk == 128) return launch_bwd_t<128, OpF32>(b, s);
   }
   return hipErrorInvalidValue;
 }

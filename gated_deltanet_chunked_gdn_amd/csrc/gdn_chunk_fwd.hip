@@ -903,6 +903,7 @@ hipError_t launch_chunk_fwd_states(const FwdParams& p, int Dk, bool bf16, hipStr
     if (Dk == 128) return launch_states_t<128, OpBf16, uint16_t>(p, s);
   } else {
     if (Dk == 64) return launch_states_t<64, OpF32, float>(p, s);
+    if (Dk == 128) return launch_states_t<128, OpF32, float>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -913,6 +914,7 @@ hipError_t launch_chunk_fwd_save(const FwdParams& p, int Dk, bool bf16, hipStrea
     if (Dk == 128) return launch_save_t<128, OpBf16, uint16_t>(p, s);
   } else {
     if (Dk == 64) return launch_save_t<64, OpF32, float>(p, s);
+    if (Dk == 128) return launch_save_t<128, OpF32, float>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -58,7 +58,7 @@
  *      io dtype GDN_BF16: bf16 MFMA operands with fp32 accumulation; the state,
  *        the decay factors, the triangular solve and all gradients' reductions
  *        are fp32; outputs are rounded to bf16 (round to nearest even) once.
- *  - Supported: Dk in {64, 128} (fp32 products: gdn_chunk_bwd Dk == 64 only);
+ *  - Supported: Dk in {64, 128};
  *    Dv a multiple of 16 with 16 <= Dv <= 256; chunk == 64; num_segments in
  *    {1, 2, 4, 8, 16}; N <= 65535.  The recurrent backward needs
  *    2 * Dk * (Dv + 1) * 4 bytes of LDS and so Dk * Dv <= 128 * 128.

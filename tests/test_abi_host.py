@@ -84,14 +84,14 @@ def test_problem_validation(kw, status):
 
 def test_precision_policy_scope():
     """IEEE fp32 products: the forward at both head sizes and io dtypes; the
-    backward only with fp32 io at Dk = 64; not the per-channel-decay forward with
-    bf16 io."""
+    backward with fp32 io at both head sizes; not the per-channel-decay passes
+    with bf16 io."""
     fp32 = nat.GDN_PRECISION_FP32
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128))[0] == nat.GDN_OK
     assert ws(problem(precision=fp32))[0] == nat.GDN_OK
     assert ws(problem(precision=fp32, Dk=64))[0] == nat.GDN_OK
     assert ws(problem(precision=fp32), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
-    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_OK
     assert ws(problem(io_dtype=nat.GDN_FP32, Dk=64, precision=fp32), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_OK
     assert ws(problem(precision=fp32), nat.GDN_PASS_KDA_FWD)[0] == nat.GDN_ERR_UNSUPPORTED
     assert ws(problem(precision=fp32), nat.GDN_PASS_KDA_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
@@ -210,7 +210,7 @@ def test_backward_workspace_size():
     assert n == (2 * up(slots * 3 * 4096 * 4) + up(slots * 3 * 3072 * 4) + up(slots * 3 * 128 * 4)
                  + 2 * slots * 3 * 64 * 96 * 4)
     assert ws(problem(num_segments=4), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
-    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_ERR_UNSUPPORTED
+    assert ws(problem(io_dtype=nat.GDN_FP32, Dk=128), nat.GDN_PASS_CHUNK_BWD)[0] == nat.GDN_OK
 
 
 def test_saved_buffer_size_and_validation():

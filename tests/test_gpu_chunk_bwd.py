@@ -116,6 +116,7 @@ CASES = [
     (2, 63, 2, 64, 32, "fp32", None, None, 0.25, "gdn", False),
     (1, 200, 3, 64, 64, "fp32", (0, 0, 37, 200), 0.3, 0.7, "bounded5", True),
     (2, 130, 2, 64, 16, "fp32", None, 0.2, 1.0, "gdn", True),
+    (1, 300, 2, 128, 64, "fp32", (0, 70, 70, 300), 0.2, 0.5, "gdn", True),
     (1, 65, 1, 128, 16, "bf16", None, None, 1.0, "gdn", False),
     (3, 100, 2, 128, 48, "bf16", None, 0.1, 128 ** -0.5, "gdn", True),
     (1, 300, 2, 64, 256, "bf16", (0, 64, 64, 129, 300), 0.2, 1.0, "softplus01", True),

@@ -25,6 +25,7 @@ CASES = [
     # (B, T, H, Dk, Dv, io, cu_seqlens, s0, gate, with dS_final)
     (1, 1, 1, 64, 64, "fp32", None, 0.5, "softplus01", True),
     (2, 130, 2, 64, 16, "fp32", None, 0.2, "gdn", True),
+    (1, 200, 2, 128, 32, "fp32", (0, 1, 65, 200), 0.2, "gdn", True),
     (1, 65, 1, 128, 16, "bf16", None, None, "gdn", False),
     (3, 100, 2, 128, 48, "bf16", None, 0.1, "gdn", True),
     (1, 300, 2, 64, 256, "bf16", (0, 64, 64, 129, 300), 0.2, "softplus01", True),
