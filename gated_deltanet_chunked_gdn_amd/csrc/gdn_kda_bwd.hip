@@ -44,34 +44,6 @@ namespace {
 
 using chunk::seq_range;
 
-__device__ __forceinline__ float ldf(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float ldf(const float* p) { return *p; }
-
-// acc += A(16 x K) B(K x 16) on fp32 MFMA.  `a` points at A(m, kq) and `b` at
-// B(kq, n) for this lane (m = n = lane % 16, kq = lane / 16); SA and SB are the
-// strides between consecutive k.  NA independent accumulation chains (NA = 1:
-// straight into acc, for products interleaved with others of their own).
-template <int K, int SA, int SB, int NA = 4, typename TA>
-__device__ __forceinline__ void mm(f32x4_t& acc, const TA* a, const float* b, float ascale = 1.f) {
-  constexpr int NS = K / 4;
-  static_assert(NS * 4 == K && NS % NA == 0, "K must be a multiple of 4 NA");
-  if constexpr (NA == 1) {
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ascale * ldf(a + 4 * st * SA), b[4 * st * SB], acc, 0, 0, 0);
-  } else {
-    f32x4_t x[NA];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) x[j] = zero4();
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-      x[st % NA] = __builtin_amdgcn_mfma_f32_16x16x4f32(ascale * ldf(a + 4 * st * SA), b[4 * st * SB], x[st % NA],
-                                                        0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) acc += x[j];
-  }
-}
-
 // N consecutive values (N a multiple of 8, 16-byte aligned) widened to fp32:
 // 16-byte loads.
 template <int N>
