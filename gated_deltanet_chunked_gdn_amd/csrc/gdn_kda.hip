@@ -87,14 +87,16 @@ __device__ __forceinline__ f32x4_t ld4f<float>(const float* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
 
-// The diagonal 16x16 blocks of A and P factor through their first row r:
-// exp(gamma_i - gamma_j) = exp(gamma_i - gamma_r) exp(gamma_r - gamma_j) for
-// r <= j <= i, the first factor <= 1 and the second >= 1 but at most the block's
-// own decay from row r to row r + 15.  While no channel decays by more than
-// 2^kMaxBlockDrop across any diagonal block (log2 units), both factors and their
-// products with the keys and queries stay far inside fp32 and the blocks are MFMA
-// products like the others; a chunk with a steeper block takes the exact
-// pair-by-pair sums instead.  The flag lives in an unused entry above A's diagonal.
+// The diagonal 16x16 blocks of A and P factor through their middle row m = 16 b + 8:
+// exp(gamma_i - gamma_j) = exp(gamma_i - gamma_m) exp(gamma_m - gamma_j) for any
+// rows i, j of the block, each factor between 2^-D and 2^D, D the larger of the
+// block's decays from its first row to m and from m to its last row.  While no
+// channel has D above kMaxBlockDrop in any diagonal block (log2 units), both
+// factors and their products with the keys and queries stay far inside fp32 and
+// the blocks are MFMA products like the others; a chunk with a steeper block takes
+// the exact pair-by-pair sums instead.  (Entries above the diagonal, which these
+// products also form, can reach 2^(2 D) and are never kept.)  The flag lives in an
+// unused entry above A's diagonal.
 constexpr float kMaxBlockDrop = 100.f;
 constexpr int kSteepAt = 63;  // A's entry (0, 63)
 
@@ -184,13 +186,17 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     float col[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) col[i] = gs[gidx(i, tid)] * chunk::kLog2e;
-    float acc = 0.f, first = 0.f, drop = 0.f;
+    float acc = 0.f, first = 0.f, mid = 0.f, drop = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       acc += col[i];
       gs[gidx(i, tid)] = acc;
       if (i % 16 == 0) first = acc;
-      if (i % 16 == 15) drop = fmaxf(drop, first - acc);
+      if (i % 16 == 8) {
+        mid = acc;
+        drop = fmaxf(drop, first - mid);
+      }
+      if (i % 16 == 15) drop = fmaxf(drop, mid - acc);
     }
     if (drop > kMaxBlockDrop) As[kSteepAt] = 1.f;  // (every writer stores the same value)
   }
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   // waves 0-5 take one such block each.  A lane reads four consecutive channels of
   // its rows at once and feeds them to four products (in the product of k-step
   // (k0, e) the lanes of group g hold channel k0 + 4 g + e, in both operands).
-  // The diagonal blocks go the same way through their first row (waves 6 and 7,
+  // The diagonal blocks go the same way through their middle row (waves 6 and 7,
   // two blocks each) unless the chunk is steep; then they are summed pair by pair,
   // one exponential per channel: every thread takes one of the first 512 pairs
   // whole and an eighth of a channel range of one of the last 32, whose sixteen
@@ -249,15 +255,15 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     for (int x = 0; x < 2; ++x) {
       const int b = 2 * (wave - 6) + x;
       f32x4_t accA, accP;
-      decayed_product(16 * b + (lane & 15), 16 * b + (lane & 15), 16 * b, accA, accP);
+      decayed_product(16 * b + (lane & 15), 16 * b + (lane & 15), 16 * b + 8, accA, accP);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int i = 16 * b + 4 * (lane >> 4) + q4, j = 16 * b + (lane & 15);
         if (j < i) As[i * 64 + j] = As[i * 64 + i] * accA[q4];
         if (j <= i) rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
         if (aux) {
-          aux[kda::Aux::kAb + i * 64 + j] = accA[q4];
-          aux[kda::Aux::kP + i * 64 + j] = accP[q4];
+          aux[kda::Aux::kAb + i * 64 + j] = j < i ? accA[q4] : 0.f;
+          aux[kda::Aux::kP + i * 64 + j] = j <= i ? accP[q4] : 0.f;
         }
       }
     }

@@ -261,8 +261,9 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(KdaBwdParams p) {
   }
 }
 
-// Largest decay of one channel across a 16-row block (log2 units) for which the
-// gradient kernel forms the diagonal blocks' pair sums through a reference row.
+// Largest decay of one channel from the first row of a 16-row block to its middle
+// row, or from there to its last row (log2 units), for which the gradient kernel
+// forms the diagonal blocks' pair sums through the middle row.
 constexpr float kMaxBlockDropBwd = 100.f;
 
 // ---------------------------------------------------------------------------
@@ -706,13 +707,17 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
     if (tid == 0) sg[L::kSteep] = 0.f;
   }
   __syncthreads();
-  if (tid < DK) {  // gamma, and the largest decay of channel tid across one 16-row block
-    float acc = 0.f, first = 0.f, drop = 0.f;
+  if (tid < DK) {  // gamma, and the largest decay of channel tid across one half of a 16-row block
+    float acc = 0.f, first = 0.f, mid = 0.f, drop = 0.f;
     for (int i = 0; i < 64; ++i) {
       acc += gs[i * LK + tid];
       gs[i * LK + tid] = acc;
       if (i % 16 == 0) first = acc;
-      if (i % 16 == 15) drop = fmaxf(drop, first - acc);
+      if (i % 16 == 8) {
+        mid = acc;
+        drop = fmaxf(drop, first - mid);
+      }
+      if (i % 16 == 15) drop = fmaxf(drop, mid - acc);
     }
     if (drop > kMaxBlockDropBwd) sg[L::kSteep] = 1.f;  // (every writer stores the same value)
   }
@@ -758,9 +763,10 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
     // column side (results on the rows j of block bj, sums over the rows i of bi):
     //   sum_i M_ij x_i exp(gamma_i - gamma_j) = exp(gamma_c - gamma_j) sum_i M_ij (x_i exp(gamma_i - gamma_c)).
     // Across blocks (bj < bi) a = 16 bj + 15 and c = 16 bi, so every factor is <= 1.
-    // Inside a diagonal block (bi = bj = b) a = 16 b and c = 16 b + 15: the inner
-    // factors are >= 1 but at most the block's own decay, which the steep flag
-    // bounds by 2^kMaxBlockDrop; steeper chunks take the pairs one by one below.
+    // Inside a diagonal block (bi = bj = b) a = c = 16 b + 8, the middle row: every
+    // factor lies between 2^-D and 2^D, D the larger decay from the block's first
+    // row to its middle row and from there to its last, which the steep flag bounds
+    // by kMaxBlockDropBwd (log2 units); steeper chunks take the pairs one by one below.
     auto pairs = [&](int bi, int bj, int ra, int rc, bool diag) __attribute__((always_inline)) {
       const float ga = gs[ra * LK + ch], gc = gs[rc * LK + ch];
       f32x4_t p1 = zero4(), p2 = zero4(), p3 = zero4(), p4 = zero4();
@@ -809,10 +815,10 @@ __global__ __launch_bounds__(512) void kda_grad_kernel(KdaBwdParams p) {
     pairs(3, 1, 31, 48, false);
     pairs(3, 2, 47, 48, false);
     if (!steep) {
-      pairs(0, 0, 0, 15, true);
-      pairs(1, 1, 16, 31, true);
-      pairs(2, 2, 32, 47, true);
-      pairs(3, 3, 48, 63, true);
+      pairs(0, 0, 8, 8, true);
+      pairs(1, 1, 24, 24, true);
+      pairs(2, 2, 40, 40, true);
+      pairs(3, 3, 56, 56, true);
     } else {
       // pairs inside the diagonal blocks one by one, one exponential each:
       // exp(gamma_i - gamma_j) for j <= i (row side), exp(gamma_j - gamma_i) for j >= i

@@ -76,21 +76,26 @@ def test_kda_matches_oracle(w):
 @pytest.mark.parametrize("kind", ["strong", "slow", "steep", "bounded"])
 def test_kda_decay_extremes(kind):
     # The preparation forms the diagonal 16x16 blocks of A and P as products through
-    # their first row while no channel decays by more than 2^-100 across one block,
-    # and pair by pair otherwise: "steep" takes the pair-by-pair path in every chunk,
-    # "bounded" (up to ~2^-87 per block) never does, "strong" mixes both.
+    # their middle row while no channel decays by more than 2^-100 across either half
+    # of a block, and pair by pair otherwise: "steep" takes the pair-by-pair path in
+    # every chunk, "bounded" (up to ~2^-87 per whole block) never does, "strong"
+    # mixes both (head 0 through the products, head 1 pair by pair).
     w = Workload(f"kda_{kind}", 1, 260, 2, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel",
                  s0_std=0.1, seed=55)
     d = generate(w)
     rng = np.random.default_rng(56)
     shape = d["q"].shape
     if kind == "strong":
-        # per-channel log-decays down to -5 per token: exp(gamma) underflows within a chunk
-        d["g"] = (-5.0 / (1.0 + np.exp(-rng.standard_normal(shape)))).astype(np.float32)
+        # per-channel log-decays down to -5 per token: exp(gamma) underflows within a
+        # chunk; channel 0 of head 1 decays by 12 per token (96 nats, 138.5 in log2,
+        # across half a block)
+        g = -5.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+        g[:, :, 1, 0] = -12.0
+        d["g"] = g.astype(np.float32)
     elif kind == "steep":
-        # channel 0 of every head decays by 7 per token: 105 nats across a block
+        # channel 0 of every head decays by 12 per token
         g = -4.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
-        g[..., 0] = -7.0
+        g[..., 0] = -12.0
         d["g"] = g.astype(np.float32)
     elif kind == "bounded":
         # at most 4 per token: at most 60 nats (87 in log2) across a block

@@ -99,9 +99,12 @@ def test_kda_bwd_decay_extremes(kind):
     rng = np.random.default_rng(78)
     shape = d["q"].shape
     if kind == "strong":
-        # per-channel log-decays down to -5 per token, one channel at -7
+        # per-channel log-decays down to -5 per token; channel 0 of head 1 at -12, so
+        # that head's chunks take the gradient kernel's pair-by-pair path (more than
+        # 2^100 across half a 16-row block) and head 0's the products through the
+        # middle row
         g = -5.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
-        g[..., 0] = -7.0
+        g[:, :, 1, 0] = -12.0
     else:
         g = -1e-3 * rng.random(shape)
     d["g"] = g.astype(np.float32)
