@@ -73,13 +73,15 @@ def test_kda_matches_oracle(w):
     _check(d, _run(d, to_device(d)), _oracle(d), w.name)
 
 
-@pytest.mark.parametrize("kind", ["strong", "slow", "steep", "bounded"])
+@pytest.mark.parametrize("kind", ["strong", "slow", "steep", "bounded", "edge"])
 def test_kda_decay_extremes(kind):
     # The preparation forms the diagonal 16x16 blocks of A and P as products through
     # their middle row while no channel decays by more than 2^-100 across either half
     # of a block, and pair by pair otherwise: "steep" takes the pair-by-pair path in
     # every chunk, "bounded" (up to ~2^-87 per whole block) never does, "strong"
-    # mixes both (head 0 through the products, head 1 pair by pair).
+    # mixes both (head 0 through the products, head 1 pair by pair); "edge" sits just
+    # inside the bound (factors up to ~2^98; the products' discarded entries above
+    # the diagonal overflow).
     w = Workload(f"kda_{kind}", 1, 260, 2, 128, 64, io="bf16", qk="norm_both", gate="gdn_channel",
                  s0_std=0.1, seed=55)
     d = generate(w)
@@ -96,6 +98,11 @@ def test_kda_decay_extremes(kind):
         # channel 0 of every head decays by 12 per token
         g = -4.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
         g[..., 0] = -12.0
+        d["g"] = g.astype(np.float32)
+    elif kind == "edge":
+        # channel 0 of every head decays by 8.5 per token: 68 nats (98.1 in log2) across half a block
+        g = -4.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+        g[..., 0] = -8.5
         d["g"] = g.astype(np.float32)
     elif kind == "bounded":
         # at most 4 per token: at most 60 nats (87 in log2) across a block

@@ -91,7 +91,7 @@ def test_kda_bwd_matches_oracle(w):
     _check(d, _run(d, to_device(d), dsf), _oracle(d, dsf), w.name)
 
 
-@pytest.mark.parametrize("kind", ["strong", "slow"])
+@pytest.mark.parametrize("kind", ["strong", "slow", "edge"])
 def test_kda_bwd_decay_extremes(kind):
     w = Workload(f"kdab_{kind}", 1, 200, 2, 128, 64, io="fp32", qk="norm_both", gate="gdn_channel",
                  s0_std=0.1, with_dO=True, seed=77)
@@ -105,6 +105,11 @@ def test_kda_bwd_decay_extremes(kind):
         # middle row
         g = -5.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
         g[:, :, 1, 0] = -12.0
+    elif kind == "edge":
+        # channel 0 of every head at -8.5 per token: 98.1 in log2 across half a 16-row
+        # block, just inside the bound of the products through the middle row
+        g = -4.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+        g[..., 0] = -8.5
     else:
         g = -1e-3 * rng.random(shape)
     d["g"] = g.astype(np.float32)
