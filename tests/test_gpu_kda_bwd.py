@@ -8,9 +8,9 @@ gradient separately: max_rel <= 3e-4 for fp32 io, rel_rms <= 8e-3 for bf16 io
 head sizes, ragged tails, packed sequences with an empty and a one-token
 sequence, an initial state and a final-state gradient, strong and slow decay,
 run-to-run determinism, every head of the 4 x 4096 x 8 x 128 training shape
-over its first 512 tokens, and at full length the reduction to the scalar-gate
-backward (equal decays on every channel; gdn_chunk_bwd is itself checked
-against the oracle).
+over its first 512 tokens, four of its (sequence, head) pairs over all 4096
+tokens, and at full length the reduction to the scalar-gate backward (equal
+decays on every channel; gdn_chunk_bwd is itself checked against the oracle).
 """
 import numpy as np
 import pytest
@@ -135,6 +135,29 @@ def test_kda_bwd_training_shape_heads_first_512_tokens():
                           seed=w.seed))
     d = truncate(d, 512)
     _check(d, _run(d, to_device(d), None), _oracle(d, None), "kda_bf16[:512]")
+
+
+def test_kda_bwd_training_shape_full_length_sampled_heads():
+    # the whole 4 x 4096 x 8 x 128 bf16 backward with per-channel gates in one call;
+    # (sequence, head) pairs are independent, so the oracle's reverse mode runs on
+    # four of them over all 4096 tokens (about a second each).  Heads 0 of sequence
+    # 2 and 6 of sequence 3 hold this workload's two chunks steeper than 2^100 across
+    # half a 16-row block (pair-by-pair sums) beside many just inside that bound.
+    w = WORKLOADS["kda_bf16"]
+    d = generate(Workload(w.name, w.B, w.T, w.H, w.Dk, w.Dv, io=w.io, qk=w.qk, gate=w.gate, with_dO=True,
+                          seed=w.seed))
+    got = _run(d, to_device(d), None)
+
+    def sl(x, n, h):
+        return np.ascontiguousarray(x[n:n + 1, :, h:h + 1])
+
+    for n, h in ((2, 0), (3, 6), (0, 3), (1, 5)):
+        ref = oracle.kda_bwd(*(sl(d[key], n, h) for key in ("q", "k", "v", "g", "beta", "dO")), scale=d["scale"])
+        for name in GRADS:
+            out = got[name][n, :, h] if name != "dS0" else got[name][n, h]
+            e = rel_rms(out, ref[name].reshape(out.shape))
+            print(f"kda_bf16 full length (n={n}, h={h}) {name}: rel_rms {e:.2e}", flush=True)
+            assert np.isfinite(out).all() and e <= BF16_TOL, (n, h, name)
 
 
 def test_kda_bwd_full_length_equal_decays_is_the_scalar_gate_backward():
