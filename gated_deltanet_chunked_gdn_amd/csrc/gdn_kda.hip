@@ -216,11 +216,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
   // whole and an eighth of a channel range of one of the last 32, whose sixteen
   // parts are added within a DPP row.
   // rows ia (A operand) and jb (B operand) of this lane, both decayed to row rr
-  auto decayed_product = [&](int ia, int jb, int rr, f32x4_t& accA, f32x4_t& accP) {
+  auto decayed_product = [&](int ia, int jb, int rr, f32x4_t& accA, f32x4_t& accP, int kb = 0, int ke = DK) {
     accA = zero4();
     accP = zero4();
 #pragma unroll 2
-    for (int k0 = 0; k0 < DK; k0 += 16) {
+    for (int k0 = kb; k0 < ke; k0 += 16) {
       const int ch = k0 + 4 * (lane >> 4);
       const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gs + gidx(rr, ch));
       const f32x4_t gi = *reinterpret_cast<const f32x4_t*>(gs + gidx(ia, ch));
@@ -235,6 +235,26 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
       }
     }
   };
+  // A diagonal block's results: A below the diagonal (beta_i on it), P on and below it.
+  auto store_diag = [&](int b, const f32x4_t& accA, const f32x4_t& accP) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i = 16 * b + 4 * (lane >> 4) + q4, j = 16 * b + (lane & 15);
+      if (j < i) As[i * 64 + j] = As[i * 64 + i] * accA[q4];
+      if (j <= i) rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
+      if (aux) {
+        aux[kda::Aux::kAb + i * 64 + j] = j < i ? accA[q4] : 0.f;
+        aux[kda::Aux::kP + i * 64 + j] = j <= i ? accP[q4] : 0.f;
+      }
+    }
+  };
+  // The MFMA work per SIMD (wave w runs on SIMD w % 4) is balanced at two and a
+  // half blocks: waves 0-5 take one block below the diagonal blocks each, wave 6
+  // diagonal block 0 and wave 7 block 2 whole, and blocks 1 and 3 are split by
+  // channel halves between waves 6 / 4 and 7 / 5.  The second halves' sums wait in
+  // A's unused upper blocks ((0,1), (0,2) for block 1; (1,2), (1,3) for block 3)
+  // until the barrier below, after which waves 6 and 7 add them to their own.
+  f32x4_t hA = zero4(), hP = zero4();  // waves 6, 7: first half of block 1 / 3
   if (wave < 6) {
     const int bi = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;  // (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
     const int bj = wave < 3 ? 0 : wave < 5 ? 1 : 2;
@@ -250,22 +270,34 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         aux[kda::Aux::kP + i * 64 + j] = accP[q4];
       }
     }
-  } else if (!steep) {
-#pragma unroll 1
-    for (int x = 0; x < 2; ++x) {
-      const int b = 2 * (wave - 6) + x;
-      f32x4_t accA, accP;
-      decayed_product(16 * b + (lane & 15), 16 * b + (lane & 15), 16 * b + 8, accA, accP);
+    if (wave >= 4 && !steep) {  // second channel half of diagonal block 1 (wave 4) or 3 (wave 5)
+      const int b = wave == 4 ? 1 : 3, rb = wave == 4 ? 0 : 1;
+      decayed_product(16 * b + (lane & 15), 16 * b + (lane & 15), 16 * b + 8, accA, accP, DK / 2, DK);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int i = 16 * b + 4 * (lane >> 4) + q4, j = 16 * b + (lane & 15);
-        if (j < i) As[i * 64 + j] = As[i * 64 + i] * accA[q4];
-        if (j <= i) rec[R::kP + i * 64 + j] = Op::cvt(accP[q4]);
-        if (aux) {
-          aux[kda::Aux::kAb + i * 64 + j] = j < i ? accA[q4] : 0.f;
-          aux[kda::Aux::kP + i * 64 + j] = j <= i ? accP[q4] : 0.f;
-        }
+        const int r = 16 * rb + 4 * (lane >> 4) + q4, cc = lane & 15;
+        As[r * 64 + 16 * (rb + 1) + cc] = accA[q4];
+        As[r * 64 + 16 * (rb + 2) + cc] = accP[q4];
       }
+    }
+  } else if (!steep) {
+    const int b0 = 2 * (wave - 6), b1 = b0 + 1;  // whole block b0, first half of block b1
+    f32x4_t accA, accP;
+    decayed_product(16 * b0 + (lane & 15), 16 * b0 + (lane & 15), 16 * b0 + 8, accA, accP);
+    store_diag(b0, accA, accP);
+    decayed_product(16 * b1 + (lane & 15), 16 * b1 + (lane & 15), 16 * b1 + 8, hA, hP, 0, DK / 2);
+  }
+  if (!steep) {
+    __syncthreads();  // the second halves of blocks 1 and 3 are in A's upper blocks
+    if (wave >= 6) {
+      const int b1 = 2 * (wave - 6) + 1, rb = wave - 6;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r = 16 * rb + 4 * (lane >> 4) + q4, cc = lane & 15;
+        hA[q4] += As[r * 64 + 16 * (rb + 1) + cc];
+        hP[q4] += As[r * 64 + 16 * (rb + 2) + cc];
+      }
+      store_diag(b1, hA, hP);
     }
   }
   if (steep) {
